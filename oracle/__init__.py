@@ -1,0 +1,175 @@
+"""FP64 CPU oracle for the KDA chunked forward -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It wraps ``kda_oracle.c`` (plain C,
+FP64, OpenMP over (sequence, head) pairs) through ctypes.  Nothing here is
+shared with, imported by, or imported from the GPU library.
+
+Functions follow the definitions written at the top of ``kda_oracle.c``: the
+token-serial KDA recurrence (the serving-side FP32 recurrence the training
+chunk path is compared against in xtuner PR #2301 "[Enhancement] Add opt-in
+FP32 KDA chunk computation", sections Problem and Validation) and an FP64 chunk
+form with exposed intermediates.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libkda_oracle.so")
+_lib = None
+
+# Deliberate-mistake switches (see kda_oracle.c); used only by the pin tests.
+PLANT = {
+    "no_decay": 1 << 0,
+    "delta_undecayed": 1 << 1,
+    "read_before_write": 1 << 2,
+    "transposed_read": 1 << 3,
+    "delta_sign": 1 << 4,
+    "no_beta": 1 << 5,
+    "no_reset": 1 << 6,
+    "no_l2norm": 1 << 7,
+    "no_softplus": 1 << 8,
+    "gate_sign": 1 << 9,
+    "no_scale": 1 << 10,
+    "outer_swap": 1 << 11,
+    "drop_carry_64": 1 << 12,
+}
+
+
+def build(force: bool = False) -> str:
+    """Compile kda_oracle.c into libkda_oracle.so next to it (gcc -O2 -fopenmp)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", _SRC, "-o", tmp, "-lm"]
+        )
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    lib = ctypes.CDLL(build())
+    dp = ctypes.POINTER(ctypes.c_double)
+    ip = ctypes.POINTER(ctypes.c_int32)
+    lib.kda_oracle_fwd.restype = ctypes.c_int
+    lib.kda_oracle_fwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, ip, ctypes.c_int, ctypes.c_int64,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_double, ctypes.c_double, ctypes.c_uint, dp]
+    lib.kda_oracle_chunked.restype = ctypes.c_int
+    lib.kda_oracle_chunked.argtypes = [dp, dp, dp, dp, dp, dp, dp, ip, ctypes.c_int, ctypes.c_int64,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_double, ctypes.c_double, ctypes.c_int, dp, dp]
+    lib.kda_oracle_prep.restype = None
+    lib.kda_oracle_prep.argtypes = [dp, dp, dp, dp, dp, dp, ctypes.c_int64, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_double, dp, dp, dp, dp]
+    lib.kda_oracle_num_chunks.restype = ctypes.c_int64
+    lib.kda_oracle_num_chunks.argtypes = [ip, ctypes.c_int, ctypes.c_int]
+    lib.kda_oracle_chunk_record_len.restype = ctypes.c_int64
+    lib.kda_oracle_chunk_record_len.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.kda_oracle_num_threads.restype = ctypes.c_int
+    lib.kda_oracle_num_threads.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a, ct=ctypes.c_double):
+    return a.ctypes.data_as(ctypes.POINTER(ct))
+
+
+def _check_shapes(q, k, v, f, b, A_log, dt_bias, cu):
+    T, H, d = q.shape
+    for x in (k, v, f):
+        assert x.shape == (T, H, d), x.shape
+    assert b.shape == (T, H) and A_log.shape == (H,) and dt_bias.shape == (H, d)
+    assert cu.ndim == 1 and cu[0] == 0 and cu[-1] == T
+    return T, H, d
+
+
+def kda_forward(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, scale=None, eps=1e-6,
+                heads=None, plant=0, out=None):
+    """Token-serial FP64 KDA forward.  Inputs are any real arrays (converted to
+    float64 exactly); returns out [T, H, d] float64.  ``heads=(lo, hi)`` limits
+    the computation to a head range (other heads' rows stay zero / as given)."""
+    lib = _load()
+    q, k, v, f_raw, b_raw, A_log, dt_bias = map(_f64, (q, k, v, f_raw, b_raw, A_log, dt_bias))
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    T, H, d = _check_shapes(q, k, v, f_raw, b_raw, A_log, dt_bias, cu)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    lo, hi = (0, H) if heads is None else heads
+    if out is None:
+        out = np.zeros((T, H, d), dtype=np.float64)
+    rc = lib.kda_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(f_raw), _ptr(b_raw), _ptr(A_log),
+                            _ptr(dt_bias), _ptr(cu, ctypes.c_int32), len(cu) - 1, T, H, d, lo, hi,
+                            float(scale), float(eps), int(plant), _ptr(out))
+    if rc != 0:
+        raise ValueError("kda_oracle_fwd rejected its arguments")
+    return out
+
+
+def kda_chunked(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, chunk=64, scale=None,
+                eps=1e-6, heads=None, records=False):
+    """FP64 chunk-form forward.  Returns out, or (out, rec) with rec a dict of
+    per-(chunk, head) intermediates shaped [num_chunks, H, ...]."""
+    lib = _load()
+    q, k, v, f_raw, b_raw, A_log, dt_bias = map(_f64, (q, k, v, f_raw, b_raw, A_log, dt_bias))
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    T, H, d = _check_shapes(q, k, v, f_raw, b_raw, A_log, dt_bias, cu)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    lo, hi = (0, H) if heads is None else heads
+    C = int(chunk)
+    out = np.zeros((T, H, d), dtype=np.float64)
+    rec = None
+    if records:
+        nc = lib.kda_oracle_num_chunks(_ptr(cu, ctypes.c_int32), len(cu) - 1, C)
+        RL = lib.kda_oracle_chunk_record_len(C, d)
+        rec = np.zeros((nc, H, RL), dtype=np.float64)
+    rc = lib.kda_oracle_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(f_raw), _ptr(b_raw), _ptr(A_log),
+                                _ptr(dt_bias), _ptr(cu, ctypes.c_int32), len(cu) - 1, T, H, d, lo,
+                                hi, float(scale), float(eps), C, _ptr(out),
+                                _ptr(rec) if rec is not None else None)
+    if rc != 0:
+        raise ValueError("kda_oracle_chunked rejected its arguments")
+    if not records:
+        return out
+    parts = {}
+    off = 0
+    for name, shape in (("G", (C, d)), ("beta", (C,)), ("A", (C, C)), ("P", (C, C)),
+                        ("W", (C, d)), ("U", (C, d)), ("Qt", (C, d)), ("Kb", (C, d)),
+                        ("Gamma", (d,)), ("S0", (d, d))):
+        n = int(np.prod(shape))
+        parts[name] = rec[:, :, off:off + n].reshape(rec.shape[:2] + shape)
+        off += n
+    return out, parts
+
+
+def kda_prep(q, k, f_raw, b_raw, A_log, dt_bias, eps=1e-6):
+    """Stage-one quantities: (q^, k^, g, beta) for every token-head, FP64."""
+    lib = _load()
+    q, k, f_raw, b_raw, A_log, dt_bias = map(_f64, (q, k, f_raw, b_raw, A_log, dt_bias))
+    T, H, d = q.shape
+    qn = np.empty_like(q)
+    kn = np.empty_like(k)
+    g = np.empty_like(f_raw)
+    beta = np.empty((T, H), dtype=np.float64)
+    lib.kda_oracle_prep(_ptr(q), _ptr(k), _ptr(f_raw), _ptr(b_raw), _ptr(A_log), _ptr(dt_bias),
+                        T, H, d, float(eps), _ptr(qn), _ptr(kn), _ptr(g), _ptr(beta))
+    return qn, kn, g, beta
+
+
+def num_threads() -> int:
+    return int(_load().kda_oracle_num_threads())

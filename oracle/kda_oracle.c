@@ -1,0 +1,400 @@
+/*
+ * kda_oracle.c -- CPU reference ("oracle") for the Kimi Delta Attention (KDA)
+ * chunked forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, obviously-correct FP64
+ * definition that the GPU library is checked against.  Only the test suite,
+ * the smoke check and the CPU-baseline leg of the benchmark may load it.  It
+ * shares no code, header, table or helper with the GPU library, and the GPU
+ * library never calls it.
+ *
+ * What is computed (per head h, per packed sequence, zero initial state):
+ *
+ *   q^_t = q_t / sqrt(|q_t|^2 + eps),  k^_t = k_t / sqrt(|k_t|^2 + eps)
+ *   g_t[c] = -exp(A_log[h]) * softplus(f_t[c] + dt_bias[h][c])
+ *   beta_t = sigmoid(b_t)
+ *   S_t  = Diag(exp(g_t)) S_{t-1}                  (d_k x d_v state)
+ *   S_t += beta_t k^_t (v_t - S_t^T k^_t)^T        (delta rule on the decayed S)
+ *   o_t  = scale * S_t^T q^_t                      (includes token t's own write)
+ *
+ * Sources.  The pages name KDA's chunked operator and its serving-side FP32
+ * token recurrence, packed variable-length inputs with per-document state
+ * isolation, FP32 A_log / dt_bias feeding a separately computed gate, a sigmoid
+ * beta, and q/k L2 normalisation ("promote Q/K/V before L2 normalization"):
+ *   - xtuner PR #2301 "[Enhancement] Add opt-in FP32 KDA chunk computation",
+ *     sections Problem, Change and Validation ("independent FP64 recurrence");
+ *   - xtuner PR #2153 "GLM-5.3-Flash F6.2: KDA correctness and FLA sequence
+ *     parallelism", KDA module description (fused_kda_gate outside the kernel,
+ *     use_beta_sigmoid_in_kernel, packed multi-document isolation).
+ * The pages do not print the equations; the recurrence above is the standard
+ * KDA / gated delta rule with per-channel (diagonal) decay.  Readings where the
+ * pages are silent: eps = 1e-6 is a parameter (tests also use 0); the output
+ * scale multiplies the read-out; softplus uses the exact stable form
+ * max(x,0) + log1p(exp(-|x|)) with no linear cut-over.
+ *
+ * Layouts (row-major, contiguous): q,k,v,f [T][H][d]; b [T][H]; A_log [H];
+ * dt_bias [H][d]; cu_seqlens [N+1] with cu[0]=0, cu[N]=T, non-decreasing.
+ *
+ * kda_oracle_chunked() is a second, independent FP64 implementation in chunk
+ * form (intra-chunk decay-weighted blocks, unit-lower-triangular solve by
+ * forward substitution, chunk-to-chunk state pass).  It exists to localise
+ * disagreements stage by stage and is itself pinned to the token recurrence by
+ * the tests.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Deliberate-mistake switches.  They exist only so the tests can show that
+ * each plausible mistake is caught by at least one pin; 0 means "no mistake".
+ */
+enum {
+  PLANT_NO_DECAY = 1u << 0,          /* skip S <- Diag(exp g) S                 */
+  PLANT_DELTA_UNDECAYED = 1u << 1,   /* delta reads S_{t-1} instead of decayed S */
+  PLANT_READ_BEFORE_WRITE = 1u << 2, /* o_t read before token t's write         */
+  PLANT_TRANSPOSED_READ = 1u << 3,   /* o = S q instead of S^T q                */
+  PLANT_DELTA_SIGN = 1u << 4,        /* v + S^T k instead of v - S^T k          */
+  PLANT_NO_BETA = 1u << 5,           /* beta forced to 1                        */
+  PLANT_NO_RESET = 1u << 6,          /* state carried across sequences          */
+  PLANT_NO_L2NORM = 1u << 7,         /* q, k used un-normalised                 */
+  PLANT_NO_SOFTPLUS = 1u << 8,       /* g = -exp(A_log) * x                     */
+  PLANT_GATE_SIGN = 1u << 9,         /* decay by exp(-g)                        */
+  PLANT_NO_SCALE = 1u << 10,         /* output scale dropped                    */
+  PLANT_OUTER_SWAP = 1u << 11,       /* write (v - S^T k) k^T, operands swapped */
+  PLANT_DROP_CARRY_64 = 1u << 12     /* state reset every 64 tokens             */
+};
+
+static double softplus(double x) {
+  /* softplus(x) = log(1 + e^x), in the overflow-free form. */
+  return fmax(x, 0.0) + log1p(exp(-fabs(x)));
+}
+
+static double sigmoid(double x) {
+  if (x >= 0) return 1.0 / (1.0 + exp(-x));
+  double e = exp(x);
+  return e / (1.0 + e);
+}
+
+/* L2-normalise one d-vector: y = x / sqrt(sum x^2 + eps). */
+static void l2norm(const double* x, int d, double eps, double* y) {
+  double ss = 0.0;
+  for (int c = 0; c < d; ++c) ss += x[c] * x[c];
+  double r = 1.0 / sqrt(ss + eps);
+  for (int c = 0; c < d; ++c) y[c] = x[c] * r;
+}
+
+/* Per-channel log-decay of one token-head: g[c] = -exp(A_log) softplus(f + dt_bias). */
+static void gate(const double* f, double A_log, const double* dtb, int d, unsigned plant,
+                 double* g) {
+  double lam = exp(A_log);
+  for (int c = 0; c < d; ++c) {
+    double x = f[c] + dtb[c];
+    double sp = (plant & PLANT_NO_SOFTPLUS) ? x : softplus(x);
+    /* lam == 0 (A_log = -inf) must give g = 0 exactly, whatever sp is. */
+    g[c] = (lam == 0.0) ? 0.0 : -lam * sp;
+  }
+}
+
+/* Stage 1 alone: normalised q, k, the log-decay g and beta for every token-head. */
+void kda_oracle_prep(const double* q, const double* k, const double* f, const double* b,
+                     const double* A_log, const double* dt_bias, int64_t T, int H, int d,
+                     double eps, double* qn, double* kn, double* g, double* beta) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    for (int h = 0; h < H; ++h) {
+      int64_t o = (t * H + h) * (int64_t)d;
+      l2norm(q + o, d, eps, qn + o);
+      l2norm(k + o, d, eps, kn + o);
+      gate(f + o, A_log[h], dt_bias + (int64_t)h * d, d, 0u, g + o);
+      beta[t * H + h] = sigmoid(b[t * H + h]);
+    }
+  }
+}
+
+/* Token-serial recurrence for heads [h_lo, h_hi).  out is [T][H][d]; rows of
+ * heads outside the range are left untouched.  Returns 0, or -1 on bad args. */
+int kda_oracle_fwd(const double* q, const double* k, const double* v, const double* f,
+                   const double* b, const double* A_log, const double* dt_bias,
+                   const int32_t* cu_seqlens, int N, int64_t T, int H, int d, int h_lo,
+                   int h_hi, double scale, double eps, unsigned plant, double* out) {
+  if (N < 1 || H < 1 || d < 1 || h_lo < 0 || h_hi > H || h_lo > h_hi) return -1;
+  if (cu_seqlens[0] != 0 || cu_seqlens[N] != T) return -1;
+  for (int n = 0; n < N; ++n)
+    if (cu_seqlens[n + 1] < cu_seqlens[n]) return -1;
+  const int nh = h_hi - h_lo;
+  /* With PLANT_NO_RESET the sequences of one head are walked in order with one
+   * state, so the parallel unit is the head; otherwise it is (sequence, head). */
+  const int64_t units = (plant & PLANT_NO_RESET) ? (int64_t)nh : (int64_t)N * nh;
+
+#pragma omp parallel
+  {
+    double* S = (double*)malloc(sizeof(double) * (size_t)d * d);
+    double* qn = (double*)malloc(sizeof(double) * (size_t)d);
+    double* kn = (double*)malloc(sizeof(double) * (size_t)d);
+    double* g = (double*)malloc(sizeof(double) * (size_t)d);
+    double* u = (double*)malloc(sizeof(double) * (size_t)d);
+    double* Sprev = (plant & PLANT_DELTA_UNDECAYED) ? (double*)malloc(sizeof(double) * (size_t)d * d)
+                                                    : NULL;
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t w = 0; w < units; ++w) {
+      int h, n_lo, n_hi;
+      if (plant & PLANT_NO_RESET) {
+        h = h_lo + (int)w; n_lo = 0; n_hi = N;
+      } else {
+        h = h_lo + (int)(w % nh); n_lo = (int)(w / nh); n_hi = n_lo + 1;
+      }
+      memset(S, 0, sizeof(double) * (size_t)d * d);
+      for (int n = n_lo; n < n_hi; ++n) {
+        if (!(plant & PLANT_NO_RESET)) memset(S, 0, sizeof(double) * (size_t)d * d);
+        for (int64_t t = cu_seqlens[n]; t < cu_seqlens[n + 1]; ++t) {
+          if ((plant & PLANT_DROP_CARRY_64) && ((t - cu_seqlens[n]) % 64) == 0)
+            memset(S, 0, sizeof(double) * (size_t)d * d);
+          const int64_t o = (t * H + h) * (int64_t)d;
+          if (plant & PLANT_NO_L2NORM) {
+            memcpy(qn, q + o, sizeof(double) * d);
+            memcpy(kn, k + o, sizeof(double) * d);
+          } else {
+            l2norm(q + o, d, eps, qn);
+            l2norm(k + o, d, eps, kn);
+          }
+          gate(f + o, A_log[h], dt_bias + (int64_t)h * d, d, plant, g);
+          double beta = (plant & PLANT_NO_BETA) ? 1.0 : sigmoid(b[t * H + h]);
+          if (Sprev) memcpy(Sprev, S, sizeof(double) * (size_t)d * d);
+          /* S <- Diag(exp(g)) S : row i of S (key channel i) scales by exp(g_i). */
+          if (!(plant & PLANT_NO_DECAY)) {
+            for (int i = 0; i < d; ++i) {
+              double e = (plant & PLANT_GATE_SIGN) ? exp(-g[i]) : exp(g[i]);
+              for (int j = 0; j < d; ++j) S[i * d + j] *= e;
+            }
+          }
+          double* o_t = out + o;
+          if (plant & PLANT_READ_BEFORE_WRITE) {
+            for (int j = 0; j < d; ++j) {
+              double acc = 0.0;
+              for (int i = 0; i < d; ++i) acc += S[i * d + j] * qn[i];
+              o_t[j] = ((plant & PLANT_NO_SCALE) ? 1.0 : scale) * acc;
+            }
+          }
+          /* u = v - S^T k  (S^T k)_j = sum_i S[i][j] k_i, on the decayed S. */
+          const double* Sd = Sprev ? Sprev : S;
+          for (int j = 0; j < d; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < d; ++i) acc += Sd[i * d + j] * kn[i];
+            u[j] = (plant & PLANT_DELTA_SIGN) ? v[o + j] + acc : v[o + j] - acc;
+          }
+          /* S += beta k u^T */
+          if (plant & PLANT_OUTER_SWAP) {
+            for (int i = 0; i < d; ++i)
+              for (int j = 0; j < d; ++j) S[i * d + j] += beta * u[i] * kn[j];
+          } else {
+            for (int i = 0; i < d; ++i) {
+              double bk = beta * kn[i];
+              for (int j = 0; j < d; ++j) S[i * d + j] += bk * u[j];
+            }
+          }
+          if (!(plant & PLANT_READ_BEFORE_WRITE)) {
+            /* o_t = scale S^T q */
+            for (int j = 0; j < d; ++j) {
+              double acc = 0.0;
+              if (plant & PLANT_TRANSPOSED_READ)
+                for (int i = 0; i < d; ++i) acc += S[j * d + i] * qn[i];
+              else
+                for (int i = 0; i < d; ++i) acc += S[i * d + j] * qn[i];
+              o_t[j] = ((plant & PLANT_NO_SCALE) ? 1.0 : scale) * acc;
+            }
+          }
+        }
+      }
+    }
+    free(S); free(qn); free(kn); free(g); free(u); free(Sprev);
+  }
+  return 0;
+}
+
+/* Number of chunks of size C over all sequences (chunks restart at each
+ * sequence start; a sequence of length L has ceil(L/C) chunks). */
+int64_t kda_oracle_num_chunks(const int32_t* cu_seqlens, int N, int C) {
+  int64_t nc = 0;
+  for (int n = 0; n < N; ++n) {
+    int64_t L = cu_seqlens[n + 1] - cu_seqlens[n];
+    nc += (L + C - 1) / C;
+  }
+  return nc;
+}
+
+/* Size in doubles of one (chunk, head) record written by kda_oracle_chunked. */
+int64_t kda_oracle_chunk_record_len(int C, int d) {
+  return (int64_t)C * d       /* G    */
+         + C                  /* beta */
+         + 2 * (int64_t)C * C /* A, P */
+         + 4 * (int64_t)C * d /* W, U, Qt, Kb */
+         + d                  /* Gamma */
+         + (int64_t)d * d;    /* S0   */
+}
+
+/* Chunk-form forward with chunk size C (chunks restart at each sequence
+ * start).  For a chunk of n <= C tokens entering with state S0:
+ *   G[r]   = sum_{j<=r} g_j                      (chunk-local prefix)
+ *   A[r,i] = beta_r sum_c k^_rc k^_ic exp(G_rc - G_ic),  i < r
+ *   P[r,i] = sum_c q^_rc k^_ic exp(G_rc - G_ic),         i <= r
+ *   (I + A) W = Diag(beta) (k^ * exp(G)),  (I + A) U = Diag(beta) V
+ *       (unit lower-triangular: forward substitution)
+ *   D = U - W S0
+ *   O = scale (Qt S0 + P D),  Qt = q^ * exp(G)
+ *   S_next = Diag(Gamma) S0 + Kb^T D,  Gamma = exp(G_{n-1}),  Kb = k^ * exp(G_{n-1} - G)
+ * This is the token recurrence re-associated: unrolling S over the chunk gives
+ * D_r = beta_r (v_r - S_r^-T k^_r) with S_r^- the decayed state before token r.
+ * If rec != NULL it receives, per chunk (sequence-major order) and head, the
+ * record [G, beta, A, P, W, U, Qt, Kb, Gamma, S0] with rows >= n zero. */
+int kda_oracle_chunked(const double* q, const double* k, const double* v, const double* f,
+                       const double* b, const double* A_log, const double* dt_bias,
+                       const int32_t* cu_seqlens, int N, int64_t T, int H, int d, int h_lo,
+                       int h_hi, double scale, double eps, int C, double* out, double* rec) {
+  if (N < 1 || H < 1 || d < 1 || C < 1 || h_lo < 0 || h_hi > H || h_lo > h_hi) return -1;
+  if (cu_seqlens[0] != 0 || cu_seqlens[N] != T) return -1;
+  for (int n = 0; n < N; ++n)
+    if (cu_seqlens[n + 1] < cu_seqlens[n]) return -1;
+  const int nh = h_hi - h_lo;
+  const int64_t RL = kda_oracle_chunk_record_len(C, d);
+  /* first chunk index of each sequence */
+  int64_t* cfirst = (int64_t*)malloc(sizeof(int64_t) * (size_t)(N + 1));
+  cfirst[0] = 0;
+  for (int n = 0; n < N; ++n)
+    cfirst[n + 1] = cfirst[n] + (cu_seqlens[n + 1] - cu_seqlens[n] + C - 1) / C;
+
+#pragma omp parallel
+  {
+    const size_t Cd = (size_t)C * d, CC = (size_t)C * C, dd = (size_t)d * d;
+    double* S = (double*)malloc(sizeof(double) * dd);
+    double* Qn = (double*)malloc(sizeof(double) * Cd);
+    double* Kn = (double*)malloc(sizeof(double) * Cd);
+    double* G = (double*)malloc(sizeof(double) * Cd);
+    double* g = (double*)malloc(sizeof(double) * (size_t)d);
+    double* bet = (double*)malloc(sizeof(double) * (size_t)C);
+    double* A = (double*)malloc(sizeof(double) * CC);
+    double* P = (double*)malloc(sizeof(double) * CC);
+    double* W = (double*)malloc(sizeof(double) * Cd);
+    double* U = (double*)malloc(sizeof(double) * Cd);
+    double* Qt = (double*)malloc(sizeof(double) * Cd);
+    double* Kb = (double*)malloc(sizeof(double) * Cd);
+    double* Dl = (double*)malloc(sizeof(double) * Cd);
+    double* Gam = (double*)malloc(sizeof(double) * (size_t)d);
+    double* Sn = (double*)malloc(sizeof(double) * dd);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t w = 0; w < (int64_t)N * nh; ++w) {
+      const int h = h_lo + (int)(w % nh), n = (int)(w / nh);
+      const int64_t t0 = cu_seqlens[n], L = cu_seqlens[n + 1] - t0;
+      memset(S, 0, sizeof(double) * dd);
+      for (int64_t j = 0; j * C < L; ++j) {
+        const int64_t c0 = t0 + j * C;
+        const int nr = (int)((L - j * C) < C ? (L - j * C) : C);
+        memset(Qn, 0, sizeof(double) * Cd); memset(Kn, 0, sizeof(double) * Cd);
+        memset(G, 0, sizeof(double) * Cd); memset(bet, 0, sizeof(double) * C);
+        /* prep: normalised q, k; chunk-local prefix of the log-decay; beta */
+        for (int r = 0; r < nr; ++r) {
+          const int64_t o = ((c0 + r) * H + h) * (int64_t)d;
+          l2norm(q + o, d, eps, Qn + (size_t)r * d);
+          l2norm(k + o, d, eps, Kn + (size_t)r * d);
+          gate(f + o, A_log[h], dt_bias + (int64_t)h * d, d, 0u, g);
+          for (int c = 0; c < d; ++c)
+            G[(size_t)r * d + c] = (r ? G[(size_t)(r - 1) * d + c] : 0.0) + g[c];
+          bet[r] = sigmoid(b[(c0 + r) * H + h]);
+        }
+        /* decay-weighted blocks */
+        memset(A, 0, sizeof(double) * CC); memset(P, 0, sizeof(double) * CC);
+        for (int r = 0; r < nr; ++r)
+          for (int i = 0; i <= r; ++i) {
+            double sa = 0.0, sp = 0.0;
+            for (int c = 0; c < d; ++c) {
+              double e = exp(G[(size_t)r * d + c] - G[(size_t)i * d + c]);
+              double ke = Kn[(size_t)i * d + c] * e;
+              sa += Kn[(size_t)r * d + c] * ke;
+              sp += Qn[(size_t)r * d + c] * ke;
+            }
+            if (i < r) A[(size_t)r * C + i] = bet[r] * sa;
+            P[(size_t)r * C + i] = sp;
+          }
+        /* forward substitution: row r of (I + A) X = B gives
+         * X_r = B_r - sum_{i<r} A[r,i] X_i */
+        memset(W, 0, sizeof(double) * Cd); memset(U, 0, sizeof(double) * Cd);
+        for (int r = 0; r < nr; ++r) {
+          const int64_t o = ((c0 + r) * H + h) * (int64_t)d;
+          for (int c = 0; c < d; ++c) {
+            double xw = bet[r] * Kn[(size_t)r * d + c] * exp(G[(size_t)r * d + c]);
+            double xu = bet[r] * v[o + c];
+            for (int i = 0; i < r; ++i) {
+              xw -= A[(size_t)r * C + i] * W[(size_t)i * d + c];
+              xu -= A[(size_t)r * C + i] * U[(size_t)i * d + c];
+            }
+            W[(size_t)r * d + c] = xw;
+            U[(size_t)r * d + c] = xu;
+          }
+        }
+        memset(Qt, 0, sizeof(double) * Cd); memset(Kb, 0, sizeof(double) * Cd);
+        const double* Gl = G + (size_t)(nr - 1) * d;
+        for (int c = 0; c < d; ++c) Gam[c] = exp(Gl[c]);
+        for (int r = 0; r < nr; ++r)
+          for (int c = 0; c < d; ++c) {
+            Qt[(size_t)r * d + c] = Qn[(size_t)r * d + c] * exp(G[(size_t)r * d + c]);
+            Kb[(size_t)r * d + c] = Kn[(size_t)r * d + c] * exp(Gl[c] - G[(size_t)r * d + c]);
+          }
+        if (rec) {
+          double* R = rec + ((cfirst[n] + j) * H + h) * RL;
+          memcpy(R, G, sizeof(double) * Cd); R += Cd;
+          memcpy(R, bet, sizeof(double) * C); R += C;
+          memcpy(R, A, sizeof(double) * CC); R += CC;
+          memcpy(R, P, sizeof(double) * CC); R += CC;
+          memcpy(R, W, sizeof(double) * Cd); R += Cd;
+          memcpy(R, U, sizeof(double) * Cd); R += Cd;
+          memcpy(R, Qt, sizeof(double) * Cd); R += Cd;
+          memcpy(R, Kb, sizeof(double) * Cd); R += Cd;
+          memcpy(R, Gam, sizeof(double) * d); R += d;
+          memcpy(R, S, sizeof(double) * dd);
+        }
+        /* D = U - W S0 */
+        for (int r = 0; r < nr; ++r)
+          for (int jv = 0; jv < d; ++jv) {
+            double acc = 0.0;
+            for (int i = 0; i < d; ++i) acc += W[(size_t)r * d + i] * S[(size_t)i * d + jv];
+            Dl[(size_t)r * d + jv] = U[(size_t)r * d + jv] - acc;
+          }
+        /* O = scale (Qt S0 + P D) */
+        for (int r = 0; r < nr; ++r) {
+          double* o_t = out + ((c0 + r) * H + h) * (int64_t)d;
+          for (int jv = 0; jv < d; ++jv) {
+            double acc = 0.0;
+            for (int i = 0; i < d; ++i) acc += Qt[(size_t)r * d + i] * S[(size_t)i * d + jv];
+            for (int i = 0; i <= r; ++i) acc += P[(size_t)r * C + i] * Dl[(size_t)i * d + jv];
+            o_t[jv] = scale * acc;
+          }
+        }
+        /* S_next = Diag(Gamma) S0 + Kb^T D */
+        for (int i = 0; i < d; ++i)
+          for (int jv = 0; jv < d; ++jv) {
+            double acc = Gam[i] * S[(size_t)i * d + jv];
+            for (int r = 0; r < nr; ++r) acc += Kb[(size_t)r * d + i] * Dl[(size_t)r * d + jv];
+            Sn[(size_t)i * d + jv] = acc;
+          }
+        memcpy(S, Sn, sizeof(double) * dd);
+      }
+    }
+    free(S); free(Qn); free(Kn); free(G); free(g); free(bet); free(A); free(P);
+    free(W); free(U); free(Qt); free(Kb); free(Dl); free(Gam); free(Sn);
+  }
+  free(cfirst);
+  return 0;
+}
+
+/* Number of threads the OpenMP runtime will use (reported by the benchmark). */
+int kda_oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

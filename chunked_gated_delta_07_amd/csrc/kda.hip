@@ -1,0 +1,199 @@
+// kda.hip -- libkda: C ABI entry points (include/kda.h), argument checks,
+// workspace layout and kernel launches for the KDA chunked forward on gfx950.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kda.h"
+#include "kda_common.hpp"
+#include "kda_intra.hpp"
+#include "kda_scan.hpp"
+
+namespace kda {
+
+// ------------------------------------------------------------ chunk table
+// cfirst[n] = number of 64-token chunks in sequences 0..n-1 (chunks restart
+// at every sequence start: packed offsets, xtuner PR #2301 section Change).
+// One workgroup of 1024 threads; each thread owns a contiguous slice of
+// sequences.  Also writes cfirst[N] = total chunks.
+__global__ __launch_bounds__(1024) void kda_chunk_table_kernel(const int32_t* __restrict__ cu, int N,
+                                                                int32_t* __restrict__ cfirst) {
+  __shared__ int32_t part[1024];
+  const int tid = threadIdx.x;
+  const int per = (N + 1023) / 1024;
+  const int lo = min(N, tid * per), hi = min(N, lo + per);
+  int32_t s = 0;
+  for (int n = lo; n < hi; ++n) s += (cu[n + 1] - cu[n] + CHUNK - 1) / CHUNK;
+  part[tid] = s;
+  __syncthreads();
+  // inclusive scan over the 1024 partial sums (Hillis-Steele)
+  for (int off = 1; off < 1024; off <<= 1) {
+    int32_t x = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += x;
+    __syncthreads();
+  }
+  int32_t run = part[tid] - s;  // exclusive prefix of this thread's slice
+  for (int n = lo; n < hi; ++n) {
+    cfirst[n] = run;
+    run += (cu[n + 1] - cu[n] + CHUNK - 1) / CHUNK;
+  }
+  if (tid == 1023) cfirst[N] = part[1023];
+}
+
+// ------------------------------------------------------------ workspace
+// [cfirst: (N+1) int32, 256-aligned][gam: chunks*H*128 float][rec: chunks*H*REC MT]
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Upper bound on the number of chunks: each non-empty sequence of length L has
+// ceil(L/64) <= (L + 63)/64 chunks, at most min(N, T) sequences are non-empty.
+static inline int64_t max_chunks(int64_t T, int64_t N) {
+  const int64_t ne = N < T ? N : T;
+  return (T + 63 * ne) / 64;
+}
+
+struct WsLayout {
+  size_t off_cfirst, off_gam, off_rec, total;
+};
+
+static inline WsLayout ws_layout(int64_t T, int32_t N, int32_t H, uint32_t mode) {
+  const size_t mt = (mode & KDA_MODE_FP32_INTERMEDIATE) ? 4 : 2;
+  const int64_t C = max_chunks(T, N);
+  WsLayout L;
+  L.off_cfirst = 0;
+  L.off_gam = align256(sizeof(int32_t) * (size_t)(N + 1));
+  L.off_rec = L.off_gam + align256(sizeof(float) * (size_t)C * H * DH);
+  L.total = L.off_rec + align256(mt * (size_t)C * H * REC);
+  return L;
+}
+
+template <typename TA, typename MT, typename TO>
+static int launch_all(const void* q, const void* k, const void* v, const void* f, const void* b,
+                      const float* A_log, const float* dt_bias, const int32_t* cu, int32_t N,
+                      int64_t T, int32_t H, uint32_t mode, void* out, void* ws,
+                      hipStream_t stream, hipEvent_t const* ev) {
+  const WsLayout W = ws_layout(T, N, H, mode);
+  char* base = reinterpret_cast<char*>(ws);
+  int32_t* cfirst = reinterpret_cast<int32_t*>(base + W.off_cfirst);
+  float* gam = reinterpret_cast<float*>(base + W.off_gam);
+  void* rec = base + W.off_rec;
+  const int64_t C = max_chunks(T, N);
+
+  if (ev) (void)hipEventRecord(ev[0], stream);
+  hipLaunchKernelGGL(kda_chunk_table_kernel, dim3(1), dim3(1024), 0, stream, cu, (int)N, cfirst);
+  if (ev) (void)hipEventRecord(ev[1], stream);
+
+  IntraArgs ia;
+  ia.q = q; ia.k = k; ia.v = v; ia.f = f; ia.b = b;
+  ia.A_log = A_log; ia.dt_bias = dt_bias; ia.cu = cu; ia.cfirst = cfirst;
+  ia.N = N; ia.H = H; ia.eps = 1e-6f; ia.gam = gam; ia.rec = rec;
+  hipLaunchKernelGGL((kda_intra_kernel<TA, MT>), dim3((unsigned)C, (unsigned)H), dim3(256), 0, stream,
+                     ia);
+  if (ev) (void)hipEventRecord(ev[2], stream);
+
+  ScanArgs sa;
+  sa.cu = cu; sa.cfirst = cfirst; sa.N = N; sa.H = H;
+  sa.scale = 0.08838834764831845f;  // 1/sqrt(128)
+  sa.gam = gam; sa.rec = rec; sa.out = out;
+  const int64_t pairs = (int64_t)N * H;
+  const int64_t blocks = 32 * ((pairs + 7) / 8);
+  hipLaunchKernelGGL((kda_scan_kernel<MT, TO>), dim3((unsigned)blocks), dim3(256), 0, stream, sa);
+  if (ev) (void)hipEventRecord(ev[3], stream);
+  return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+static int dispatch(const void* q, const void* k, const void* v, const void* f, const void* b,
+                    const float* A_log, const float* dt_bias, const int32_t* cu, int32_t N,
+                    int64_t T, int32_t H, uint32_t mode, void* out, void* ws, hipStream_t s,
+                    hipEvent_t const* ev) {
+  const bool f32i = mode & KDA_MODE_FP32_INTERMEDIATE;
+  const bool a32 = mode & KDA_ACT_FP32;
+  const bool o32 = (mode & KDA_OUT_FP32) || a32;
+#define KDA_GO(TA, MT, TO) \
+  return launch_all<TA, MT, TO>(q, k, v, f, b, A_log, dt_bias, cu, N, T, H, mode, out, ws, s, ev)
+  if (!a32 && !f32i && !o32) KDA_GO(bf16, bf16, bf16);
+  if (!a32 && !f32i && o32) KDA_GO(bf16, bf16, float);
+  if (!a32 && f32i && !o32) KDA_GO(bf16, float, bf16);
+  if (!a32 && f32i && o32) KDA_GO(bf16, float, float);
+  if (a32 && !f32i) KDA_GO(float, bf16, float);
+  KDA_GO(float, float, float);
+#undef KDA_GO
+}
+
+}  // namespace kda
+
+// ================================================================ C ABI
+static int check_args(const void* q, const void* k, const void* v, const void* f, const void* b,
+                      const float* A_log, const float* dt_bias, const int32_t* cu, int32_t N,
+                      int64_t T, int32_t H, int32_t d, uint32_t mode, void* out, void* ws,
+                      size_t ws_bytes) {
+  if (mode & ~KDA_MODE_ALL_BITS) return KDA_ERR_INVALID_ARG;
+  if (N < 1 || T < 0 || H < 1) return KDA_ERR_INVALID_ARG;
+  if (d != kda::DH) return KDA_ERR_UNSUPPORTED;
+  if (T == 0) return KDA_OK;
+  if (!q || !k || !v || !f || !b || !A_log || !dt_bias || !cu || !out || !ws)
+    return KDA_ERR_INVALID_ARG;
+  if (T > (int64_t)INT32_MAX / 64 || (int64_t)N * H > (int64_t)INT32_MAX / 64)
+    return KDA_ERR_UNSUPPORTED;
+  if (ws_bytes < kda::ws_layout(T, N, H, mode).total) return KDA_ERR_WORKSPACE;
+  return KDA_OK;
+}
+
+extern "C" size_t kda_chunk_fwd_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t H,
+                                                int32_t d, uint32_t mode) {
+  if ((mode & ~KDA_MODE_ALL_BITS) || total_tokens < 0 || num_seqs < 1 || H < 1 || d != kda::DH)
+    return (size_t)-1;
+  if (total_tokens == 0) return 0;
+  return kda::ws_layout(total_tokens, num_seqs, H, mode).total;
+}
+
+extern "C" int kda_chunk_fwd_num_stages(uint32_t mode) {
+  (void)mode;
+  return 3;
+}
+
+static int fwd_impl(const void* q, const void* k, const void* v, const void* f_raw, const void* b_raw,
+                    const float* A_log, const float* dt_bias, const int32_t* cu, int32_t N, int64_t T,
+                    int32_t H, int32_t d, uint32_t mode, void* out, void* ws, size_t ws_bytes,
+                    void* stream, void* const* events, int32_t num_events) {
+  int st = check_args(q, k, v, f_raw, b_raw, A_log, dt_bias, cu, N, T, H, d, mode, out, ws, ws_bytes);
+  if (st != KDA_OK || T == 0) return st;
+  if (events && num_events != kda_chunk_fwd_num_stages(mode) + 1) return KDA_ERR_INVALID_ARG;
+  if (events)
+    for (int i = 0; i < num_events; ++i)
+      if (!events[i]) return KDA_ERR_INVALID_ARG;
+  (void)hipGetLastError();  // clear a stale error so the status reflects these launches
+  return kda::dispatch(q, k, v, f_raw, b_raw, A_log, dt_bias, cu, N, T, H, mode, out, ws,
+                       reinterpret_cast<hipStream_t>(stream),
+                       reinterpret_cast<hipEvent_t const*>(events));
+}
+
+extern "C" int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* f_raw,
+                             const void* b_raw, const float* A_log, const float* dt_bias,
+                             const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                             int32_t H, int32_t d, uint32_t mode, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return fwd_impl(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, num_seqs, total_tokens, H, d,
+                  mode, out, workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+extern "C" int kda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void* f_raw,
+                                   const void* b_raw, const float* A_log, const float* dt_bias,
+                                   const int32_t* cu_seqlens, int32_t num_seqs,
+                                   int64_t total_tokens, int32_t H, int32_t d, uint32_t mode,
+                                   void* out, void* workspace, size_t workspace_bytes, void* stream,
+                                   void* const* events, int32_t num_events) {
+  if (!events) return KDA_ERR_INVALID_ARG;
+  return fwd_impl(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, num_seqs, total_tokens, H, d,
+                  mode, out, workspace, workspace_bytes, stream, events, num_events);
+}
+
+extern "C" const char* kda_status_string(int status) {
+  switch (status) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    default: return "unknown";
+  }
+}

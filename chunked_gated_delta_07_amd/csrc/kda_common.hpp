@@ -1,0 +1,137 @@
+// kda_common.hpp -- device-side building blocks shared by the libkda kernels.
+//
+// gfx950 (CDNA4) only.  Wave size is 64.  Matrix products use the MFMA
+// instructions below; their lane layouts (checked on the hardware) are:
+//   v_mfma_f32_16x16x32_bf16 : A[m][k] in lane m%16 + 16*(k/8), element k%8;
+//                              B[k][n] in lane n + 16*(k/8); C[m][n] in lane
+//                              n + 16*(m/4), element m%4.
+//   v_mfma_f32_32x32x16_bf16 : A[m][k] in lane m + 32*(k/8); B[k][n] in lane
+//                              n + 32*(k/8); C[m][n] in lane n + 32*((m/4)%2),
+//                              element 4*(m/8) + m%4.
+//   v_mfma_f32_16x16x4f32    : A[m][k] in lane m + 16*k; B[k][n] in lane n + 16*k.
+//   v_mfma_f32_32x32x2f32    : A[m][k] in lane m + 32*k; B[k][n] in lane n + 32*k.
+// Any permutation of the contracted index k that is applied identically to A
+// and B leaves a product unchanged; the kernels use that to let every lane
+// read one contiguous run of memory per operand.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int CHUNK = 64;   // tokens per chunk
+constexpr int DH = 128;     // head dimension (d_k = d_v)
+constexpr int WAVE = 64;
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
+
+// Two consecutive elements -> float2.
+__device__ __forceinline__ f32x2 load2(const bf16* p) {
+  bf16x2 v = *reinterpret_cast<const bf16x2*>(p);
+  return f32x2{(float)v[0], (float)v[1]};
+}
+__device__ __forceinline__ f32x2 load2(const float* p) { return *reinterpret_cast<const f32x2*>(p); }
+
+__device__ __forceinline__ void store2(bf16* p, float a, float b) {
+  *reinterpret_cast<bf16x2*>(p) = bf16x2{(bf16)a, (bf16)b};
+}
+__device__ __forceinline__ void store2(float* p, float a, float b) {
+  *reinterpret_cast<f32x2*>(p) = f32x2{a, b};
+}
+__device__ __forceinline__ void store4(bf16* p, f32x4 v) {
+  *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+}
+__device__ __forceinline__ void store4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+
+// ---------------------------------------------------------------- MFMA tiles
+// A 16x16 output tile accumulated over K, for element type MT.  K-steps:
+// bf16 contracts 32 per instruction (8 per lane), f32 contracts 4 (1 per lane).
+template <typename MT> struct Mma16;
+
+template <> struct Mma16<bf16> {
+  static constexpr int KPI = 32;  // contracted elements per instruction
+  static constexpr int PER_LANE = 8;
+  typedef bf16x8 frag;
+  __device__ __forceinline__ static frag load(const bf16* p) {
+    return *reinterpret_cast<const bf16x8*>(p);
+  }
+  __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mma16<float> {
+  static constexpr int KPI = 4;
+  static constexpr int PER_LANE = 1;
+  typedef float frag;
+  __device__ __forceinline__ static frag load(const float* p) { return *p; }
+  __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// C[16][16] += A[16][K] * B[K][16] where A rows and B columns are both stored
+// as rows of K contiguous elements ("row-of-K" layout): A row m at a + m*lda,
+// B column n at b + n*ldb.  Lane l reads row (l%16) and contracts over the
+// K-range [g*K/4, (g+1)*K/4) with g = l/16, so every lane reads one
+// contiguous run from each operand.  K must be a multiple of 4*PER_LANE*...
+template <typename MT, int K>
+__device__ __forceinline__ f32x4 mma16_rows(const MT* a, int lda, const MT* b, int ldb, f32x4 c,
+                                            int lane) {
+  typedef Mma16<MT> M;
+  constexpr int KG = K / 4;                       // contracted range per lane group
+  constexpr int STEPS = KG / M::PER_LANE;         // instructions
+  const int r = lane & 15, g = lane >> 4;
+  const MT* pa = a + r * lda + g * KG;
+  const MT* pb = b + r * ldb + g * KG;
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s)
+    c = M::mma(M::load(pa + s * M::PER_LANE), M::load(pb + s * M::PER_LANE), c);
+  return c;
+}
+
+// 32x32 tiles for the state pass.
+template <typename MT> struct Mma32;
+template <> struct Mma32<bf16> {
+  static constexpr int PER_LANE = 8;
+  typedef bf16x8 frag;
+  __device__ __forceinline__ static frag load(const bf16* p) {
+    return *reinterpret_cast<const bf16x8*>(p);
+  }
+  __device__ __forceinline__ static f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mma32<float> {
+  static constexpr int PER_LANE = 1;
+  typedef float frag;
+  __device__ __forceinline__ static frag load(const float* p) { return *p; }
+  __device__ __forceinline__ static f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// Accumulator element e of a 32x32 tile holds row (row32(e, lane)), column lane%32.
+__device__ __forceinline__ int row32(int e, int lane) { return 8 * (e >> 2) + 4 * ((lane >> 5) & 1) + (e & 3); }
+
+// ---------------------------------------------------------------- math
+// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^{-|x|}).
+__device__ __forceinline__ float softplus_f(float x) {
+  return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x)));
+}
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+}  // namespace kda

@@ -1,0 +1,502 @@
+// kda_intra.hpp -- per-(chunk, head) kernel: gate/beta/L2-norm prep, the
+// decay-weighted intra-chunk blocks, the chunk solve, and the matrices the
+// state pass consumes.
+//
+// Chunk algebra (the token recurrence re-associated over a chunk of n <= 64
+// tokens; the chunked operator and its "chunk solve / state intermediates"
+// are those of xtuner PR #2301 "[Enhancement] Add opt-in FP32 KDA chunk
+// computation", sections Problem and Change):
+//   a_r[c]  = exp(g_r[c]) (per-token decay), Gam = prod_r a_r
+//   A[r,i]  = beta_r sum_c k^_rc k^_ic prod_{i<j<=r} a_j[c]      (i < r)
+//   P[r,i]  = sum_c q^_rc k^_ic prod_{i<j<=r} a_j[c]             (i <= r)
+//   T       = (I + A)^{-1}   (unit lower triangular)
+//   W       = T Diag(beta) (k^ * E),   E_r = prod_{j<=r} a_j
+//   U       = T Diag(beta) v
+//   Qt      = q^ * E,   Kb_r = k^_r * prod_{j>r} a_j
+// Every decay factor is a product of per-token decays over a token range, so
+// it lies in [0, 1] and never overflows, however strong the gate; the pages'
+// "fixed-layout FP32 gate prefix" (xtuner PR #2153, KDA module section) is
+// kept as an FP32 prefix, multiplicative here.
+//
+// Off-diagonal 16x16 blocks (row block R > column block I) are products
+// (k^_r * prod_{16R<j<=r} a_j) . (k^_i * prod_{i<j<=16R} a_j): both factors
+// <= 1, one MFMA tile each.  Inside a diagonal block the decay of each pair is
+// formed per pair and channel on the VALU and the channel sum is done by an
+// MFMA (one useful pair per output column).
+//
+// Layout choices: one workgroup (4 waves) per (chunk, head).  For the VALU
+// work each wave owns 16 token rows and each lane two adjacent channels, so
+// prefix/suffix products along tokens are plain register loops.  MFMA
+// operands are staged through LDS as rows of contiguous channels.
+#pragma once
+
+#include "kda_common.hpp"
+
+namespace kda {
+
+// Per-(chunk, head) record in the workspace, element type MT:
+//   W   [64][128]  row-major (token, key channel)
+//   Qt  [64][128]  row-major
+//   KbT [128][64]  transposed (key channel, token)
+//   UT  [128][64]  transposed (value channel, token)
+//   P   [64][64]   row-major (token, token)
+// plus Gam [128] float in a separate array.
+constexpr int OFF_W = 0;
+constexpr int OFF_QT = CHUNK * DH;
+constexpr int OFF_KBT = 2 * CHUNK * DH;
+constexpr int OFF_UT = 3 * CHUNK * DH;
+constexpr int OFF_P = 4 * CHUNK * DH;
+constexpr int REC = 4 * CHUNK * DH + CHUNK * CHUNK;
+
+struct IntraArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* f;
+  const void* b;
+  const float* A_log;
+  const float* dt_bias;
+  const int32_t* cu;
+  const int32_t* cfirst;  // [N+1] first chunk of each sequence; cfirst[N] = chunk count
+  int N;
+  int H;
+  float eps;
+  float* gam;  // [chunks][H][128]
+  void* rec;   // [chunks][H][REC] of MT
+};
+
+// Chunk c -> (first token, length).  cfirst is non-decreasing with cfirst[0]=0.
+__device__ __forceinline__ bool locate_chunk(const int32_t* __restrict__ cu,
+                                             const int32_t* __restrict__ cfirst, int N, int c,
+                                             int& t0, int& len) {
+  if (c >= cfirst[N]) return false;
+  int lo = 0, hi = N;  // cfirst[lo] <= c < cfirst[hi]
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (cfirst[mid] <= c) lo = mid; else hi = mid;
+  }
+  t0 = cu[lo] + (c - cfirst[lo]) * CHUNK;
+  len = min(CHUNK, cu[lo + 1] - t0);
+  return true;
+}
+
+// Diagonal-block pairs (u, i), 0 <= i < u < 16, ordered by i then u.
+__host__ __device__ constexpr int pair_first(int i) { return 15 * i - (i * (i - 1)) / 2; }
+__host__ __device__ constexpr int pair_i(int p) {
+  int i = 0;
+  while (i < 14 && pair_first(i + 1) <= p) ++i;
+  return i;
+}
+__host__ __device__ constexpr int pair_u(int p) { return pair_i(p) + 1 + (p - pair_first(pair_i(p))); }
+constexpr int NPAIR = 120;
+constexpr int NBATCH = 8;  // ceil(120 / 16)
+
+template <typename MT> struct IntraLds {
+  static constexpr int ROWL = sizeof(MT) == 2 ? 136 : 132;  // padded row of 128 channels
+  static constexpr int TL = sizeof(MT) == 2 ? 72 : 68;      // padded row of 64 tokens
+  static constexpr int AL = 68;                              // fp32 64x64 row
+  // fixed part
+  static constexpr int O_BETA = 0;                  // float[64]
+  static constexpr int O_RK = O_BETA + 256;         // float[64]
+  static constexpr int O_RQ = O_RK + 256;           // float[64]
+  static constexpr int O_TOT = O_RQ + 256;          // float[4][128] block decay products
+  static constexpr int O_A0 = O_TOT + 2048;         // float[4][128] first-row decay of each block
+  static constexpr int O_A = O_A0 + 2048;           // float[64][AL] strictly-lower A
+  static constexpr int O_U = O_A + 64 * AL * 4;     // union region
+  // union, phase 1: per wave private rows: raw k [16], raw q [16], pair vectors [16]
+  static constexpr int PRIV_ROWS = 48;
+  static constexpr int PRIV_BYTES = PRIV_ROWS * ROWL * (int)sizeof(MT);
+  // union, phase 2: cross-block operands: A-side rows (kL,qL for R=1..3) 96, B-side 96
+  static constexpr int X_ROWS = 192;
+  // union, phase 3: T (float [64][AL]), T-scaled operand (MT [64][TL]), transposed (MT [128][TL])
+  static constexpr int O_T = 0;
+  static constexpr int O_TS = O_T + 64 * AL * 4;
+  static constexpr int O_XT = O_TS + 64 * TL * (int)sizeof(MT);
+  static constexpr int U_P1 = 4 * PRIV_BYTES;
+  static constexpr int U_P2 = X_ROWS * ROWL * (int)sizeof(MT);
+  static constexpr int U_P3 = O_XT + 128 * TL * (int)sizeof(MT);
+  static constexpr int U_BYTES = U_P1 > U_P2 ? (U_P1 > U_P3 ? U_P1 : U_P3) : (U_P2 > U_P3 ? U_P2 : U_P3);
+  static constexpr int BYTES = O_U + U_BYTES;
+};
+
+// Index of cross-block combination (R, I), R > I, in 0..5.
+__device__ __forceinline__ constexpr int combo(int R, int I) { return (R * (R - 1)) / 2 + I; }
+
+template <typename TA, typename MT>
+__global__ __launch_bounds__(256) void kda_intra_kernel(IntraArgs p) {
+  typedef IntraLds<MT> L;
+  constexpr int ROWL = L::ROWL, TL = L::TL, AL = L::AL;
+  __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+  float* sBeta = reinterpret_cast<float*>(smem + L::O_BETA);
+  float* sRk = reinterpret_cast<float*>(smem + L::O_RK);
+  float* sRq = reinterpret_cast<float*>(smem + L::O_RQ);
+  float* sTot = reinterpret_cast<float*>(smem + L::O_TOT);
+  float* sA0 = reinterpret_cast<float*>(smem + L::O_A0);
+  float* sA = reinterpret_cast<float*>(smem + L::O_A);
+  char* sU = smem + L::O_U;
+
+  const int chunk = blockIdx.x, h = blockIdx.y;
+  int t0, len;
+  if (!locate_chunk(p.cu, p.cfirst, p.N, chunk, t0, len)) return;  // uniform over the block
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int H = p.H;
+  const int c0 = 2 * l;  // this lane's two channels: c0, c0 + 1
+  const TA* __restrict__ gq = reinterpret_cast<const TA*>(p.q);
+  const TA* __restrict__ gk = reinterpret_cast<const TA*>(p.k);
+  const TA* __restrict__ gv = reinterpret_cast<const TA*>(p.v);
+  const TA* __restrict__ gf = reinterpret_cast<const TA*>(p.f);
+  const TA* __restrict__ gb = reinterpret_cast<const TA*>(p.b);
+  const size_t rec_off = ((size_t)chunk * H + h) * REC;
+  MT* __restrict__ gW = reinterpret_cast<MT*>(p.rec) + rec_off + OFF_W;
+  MT* __restrict__ gQt = reinterpret_cast<MT*>(p.rec) + rec_off + OFF_QT;
+  MT* __restrict__ gKbT = reinterpret_cast<MT*>(p.rec) + rec_off + OFF_KBT;
+  MT* __restrict__ gUT = reinterpret_cast<MT*>(p.rec) + rec_off + OFF_UT;
+  MT* __restrict__ gP = reinterpret_cast<MT*>(p.rec) + rec_off + OFF_P;
+
+  // ------------------------------------------------------------ phase 1: prep
+  // Per lane: rows 16w..16w+15, channels c0, c0+1.  Rows past the chunk end
+  // hold q = k = v = 0 and decay 1, which makes every formula exact without
+  // special cases (they add nothing to any sum and do not decay the state).
+  const float lam = expf(p.A_log[h]);  // exp(-inf) = 0 gives g = 0 exactly
+  const f32x2 dtb = *reinterpret_cast<const f32x2*>(p.dt_bias + (size_t)h * DH + c0);
+  float qa[16][2], ka[16][2], aa[16][2];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int r = 16 * w + j;
+    if (r < len) {
+      const size_t o = ((size_t)(t0 + r) * H + h) * DH + c0;
+      f32x2 xq = load2(gq + o), xk = load2(gk + o), xf = load2(gf + o);
+      qa[j][0] = xq[0]; qa[j][1] = xq[1];
+      ka[j][0] = xk[0]; ka[j][1] = xk[1];
+      // g = -exp(A_log) softplus(f + dt_bias);  a = exp(g)
+      aa[j][0] = expf(-lam * softplus_f(xf[0] + dtb[0]));
+      aa[j][1] = expf(-lam * softplus_f(xf[1] + dtb[1]));
+    } else {
+      qa[j][0] = qa[j][1] = ka[j][0] = ka[j][1] = 0.0f;
+      aa[j][0] = aa[j][1] = 1.0f;
+    }
+  }
+  if (l < 16) {
+    const int r = 16 * w + l;
+    sBeta[r] = (r < len) ? sigmoid_f(to_f32(gb[(size_t)(t0 + r) * H + h])) : 0.0f;
+  }
+  // raw rows for the MFMA work inside the diagonal block
+  MT* priv = reinterpret_cast<MT*>(sU + w * L::PRIV_BYTES);
+  MT* pK = priv;               // rows 0..15
+  MT* pQ = priv + 16 * ROWL;   // rows 16..31
+  MT* pD = priv + 32 * ROWL;   // rows 32..47 (pair vectors)
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    store2(pK + j * ROWL + c0, ka[j][0], ka[j][1]);
+    store2(pQ + j * ROWL + c0, qa[j][0], qa[j][1]);
+  }
+  {
+    float t0c = 1.0f, t1c = 1.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) { t0c *= aa[j][0]; t1c *= aa[j][1]; }
+    sTot[w * DH + c0] = t0c; sTot[w * DH + c0 + 1] = t1c;
+    sA0[w * DH + c0] = aa[0][0]; sA0[w * DH + c0 + 1] = aa[0][1];
+  }
+  __syncthreads();
+
+  // Norms (sum of squares) and the plain q.k diagonal via MFMA on the raw rows.
+  {
+    f32x4 ckk = {0, 0, 0, 0}, cqq = {0, 0, 0, 0}, cqk = {0, 0, 0, 0};
+    ckk = mma16_rows<MT, DH>(pK, ROWL, pK, ROWL, ckk, l);
+    cqq = mma16_rows<MT, DH>(pQ, ROWL, pQ, ROWL, cqq, l);
+    cqk = mma16_rows<MT, DH>(pQ, ROWL, pK, ROWL, cqk, l);
+    const int n = l & 15, m0 = 4 * (l >> 4);
+    if (n >= m0 && n < m0 + 4) {
+      const int e = n - m0;
+      const int r = 16 * w + n;
+      const float rk = 1.0f / sqrtf(ckk[e] + p.eps);
+      const float rq = 1.0f / sqrtf(cqq[e] + p.eps);
+      sRk[r] = rk;
+      sRq[r] = rq;
+      gP[r * CHUNK + r] = from_f32<MT>(rq * rk * cqk[e]);  // P[r][r], decay 1
+    }
+  }
+  __syncthreads();
+
+  // Diagonal block: pair vectors kd_(u,i)[c] = k_i[c] prod_{i<j<=u} a_j[c],
+  // 16 per batch; MFMA k.kd and q.kd; keep the (u, column) entry.
+  {
+    float d0 = 1.0f, d1 = 1.0f;
+#pragma unroll
+    for (int bt = 0; bt < NBATCH; ++bt) {
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {
+        const int pp = 16 * bt + n;
+        if (pp < NPAIR) {
+          const int i = pair_i(pp), u = pair_u(pp);
+          if (u == i + 1) { d0 = aa[u][0]; d1 = aa[u][1]; }
+          else { d0 *= aa[u][0]; d1 *= aa[u][1]; }
+          store2(pD + n * ROWL + c0, ka[i][0] * d0, ka[i][1] * d1);
+        } else {
+          store2(pD + n * ROWL + c0, 0.0f, 0.0f);
+        }
+      }
+      __syncthreads();
+      f32x4 ca = {0, 0, 0, 0}, cp = {0, 0, 0, 0};
+      ca = mma16_rows<MT, DH>(pK, ROWL, pD, ROWL, ca, l);
+      cp = mma16_rows<MT, DH>(pQ, ROWL, pD, ROWL, cp, l);
+      {
+        const int n = l & 15, pp = 16 * bt + n;
+        if (pp < NPAIR) {
+          const int i = pair_i(pp), u = pair_u(pp);
+          const int m0 = 4 * (l >> 4);
+          if (u >= m0 && u < m0 + 4) {
+            const int e = u - m0;
+            const float va = e == 0 ? ca[0] : e == 1 ? ca[1] : e == 2 ? ca[2] : ca[3];
+            const float vp = e == 0 ? cp[0] : e == 1 ? cp[1] : e == 2 ? cp[2] : cp[3];
+            const int ru = 16 * w + u, ri = 16 * w + i;
+            sA[ru * AL + ri] = sBeta[ru] * sRk[ru] * sRk[ri] * va;
+            gP[ru * CHUNK + ri] = from_f32<MT>(sRq[ru] * sRk[ri] * vp);
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // ------------------------------------------------------- phase 2: cross-block
+  // Per channel: product of decays of the blocks before / after mine.
+  float pb[2] = {1.0f, 1.0f}, sa[2] = {1.0f, 1.0f};
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    if (x < w) { pb[0] *= sTot[x * DH + c0]; pb[1] *= sTot[x * DH + c0 + 1]; }
+    if (x > w) { sa[0] *= sTot[x * DH + c0]; sa[1] *= sTot[x * DH + c0 + 1]; }
+  }
+  {
+    // Qt = q^ * prod_{j<=r} a_j ;  KbT = (k^ * prod_{j>r} a_j)^T ; Gam
+    float e0 = pb[0], e1 = pb[1];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = 16 * w + j;
+      e0 *= aa[j][0]; e1 *= aa[j][1];
+      const float rq = sRq[r];
+      store2(gQt + r * DH + c0, qa[j][0] * rq * e0, qa[j][1] * rq * e1);
+    }
+    float s0 = sa[0], s1 = sa[1];
+    float kb0[16], kb1[16];
+#pragma unroll
+    for (int j = 15; j >= 0; --j) {
+      const float rk = sRk[16 * w + j];
+      kb0[j] = ka[j][0] * rk * s0;
+      kb1[j] = ka[j][1] * rk * s1;
+      s0 *= aa[j][0]; s1 *= aa[j][1];
+    }
+#pragma unroll
+    for (int j = 0; j < 16; j += 4) {
+      store4(gKbT + (size_t)c0 * CHUNK + 16 * w + j, f32x4{kb0[j], kb0[j + 1], kb0[j + 2], kb0[j + 3]});
+      store4(gKbT + (size_t)(c0 + 1) * CHUNK + 16 * w + j,
+             f32x4{kb1[j], kb1[j + 1], kb1[j + 2], kb1[j + 3]});
+    }
+    if (w == 0) {
+      float g0 = 1.0f, g1 = 1.0f;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) { g0 *= sTot[x * DH + c0]; g1 *= sTot[x * DH + c0 + 1]; }
+      *reinterpret_cast<f32x2*>(p.gam + ((size_t)chunk * H + h) * DH + c0) = f32x2{g0, g1};
+    }
+  }
+  // Cross-block operands.  A-side (rows of block R = w >= 1, reference = the
+  // block's first row): kL = k * prod_{16R<j<=r} a_j, qL likewise.  B-side
+  // (rows of block I = w for every R > w): kR = k * prod_{i<j<=16R} a_j.
+  MT* xA = reinterpret_cast<MT*>(sU);              // [3][32] rows: kL then qL of R=1..3
+  MT* xB = reinterpret_cast<MT*>(sU) + 96 * ROWL;  // [6][16] rows
+  if (w >= 1) {
+    float x0 = 1.0f, x1 = 1.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j > 0) { x0 *= aa[j][0]; x1 *= aa[j][1]; }
+      store2(xA + ((w - 1) * 32 + j) * ROWL + c0, ka[j][0] * x0, ka[j][1] * x1);
+      store2(xA + ((w - 1) * 32 + 16 + j) * ROWL + c0, qa[j][0] * x0, qa[j][1] * x1);
+    }
+  }
+  if (w <= 2) {
+    // suffix within my block, excluding the row itself
+    float ks0[16], ks1[16];
+    float s0 = 1.0f, s1 = 1.0f;
+#pragma unroll
+    for (int j = 15; j >= 0; --j) {
+      ks0[j] = ka[j][0] * s0; ks1[j] = ka[j][1] * s1;
+      s0 *= aa[j][0]; s1 *= aa[j][1];
+    }
+#pragma unroll
+    for (int R = 1; R < 4; ++R) {
+      if (R > w) {
+        // kappa = prod of whole blocks strictly between w and R, times the
+        // decay of the reference row 16R
+        float k0 = sA0[R * DH + c0], k1 = sA0[R * DH + c0 + 1];
+#pragma unroll
+        for (int x = 1; x < 4; ++x)
+          if (x > w && x < R) { k0 *= sTot[x * DH + c0]; k1 *= sTot[x * DH + c0 + 1]; }
+        MT* dst = xB + combo(R, w) * 16 * ROWL;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) store2(dst + j * ROWL + c0, ks0[j] * k0, ks1[j] * k1);
+      }
+    }
+  }
+  __syncthreads();
+  // 12 tile products (R, I, k|q), three per wave.
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    const int tp = 3 * w + t;  // 0..11
+    const int cmb = tp >> 1, isq = tp & 1;
+    const int R = cmb == 0 ? 1 : cmb <= 2 ? 2 : 3;
+    const int I = cmb - (R * (R - 1)) / 2;
+    f32x4 c = {0, 0, 0, 0};
+    c = mma16_rows<MT, DH>(xA + ((R - 1) * 32 + 16 * isq) * ROWL, ROWL, xB + cmb * 16 * ROWL, ROWL,
+                           c, l);
+    const int n = l & 15, m0 = 4 * (l >> 4);
+    const int ri = 16 * I + n;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ru = 16 * R + m0 + e;
+      if (isq) gP[ru * CHUNK + ri] = from_f32<MT>(sRq[ru] * sRk[ri] * c[e]);
+      else sA[ru * AL + ri] = sBeta[ru] * sRk[ru] * sRk[ri] * c[e];
+    }
+  }
+  // upper triangle of P is zero
+  for (int x = tid; x < CHUNK * CHUNK; x += 256) {
+    const int r = x >> 6, i = x & 63;
+    if (i > r) gP[x] = from_f32<MT>(0.0f);
+  }
+  __syncthreads();
+
+  // ------------------------------------------------- phase 3: T = (I + A)^{-1}
+  float* sT = reinterpret_cast<float*>(sU + L::O_T);
+  // diagonal blocks by forward substitution, one column per lane
+  if (l < 16) {
+    const int cc = l;
+    float t[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc = (r == cc) ? 1.0f : 0.0f;
+      const float* arow = sA + (16 * w + r) * AL + 16 * w;
+#pragma unroll
+      for (int i = 0; i < r; ++i) acc -= (i >= cc) ? arow[i] * t[i] : 0.0f;
+      t[r] = (r < cc) ? 0.0f : acc;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sT[(16 * w + r) * AL + 16 * w + cc] = t[r];
+  }
+  // blocks above the diagonal are zero
+  for (int x = tid; x < CHUNK * CHUNK; x += 256) {
+    const int r = x >> 6, i = x & 63;
+    if ((i >> 4) > (r >> 4)) sT[r * AL + i] = 0.0f;
+  }
+  __syncthreads();
+  // Off-diagonal blocks: T_RI = -T_RR sum_{J=I}^{R-1} A_RJ T_JI, by distance R-I.
+  // Lane: column cc = l%16, rows 4*(l/16)+e.
+  {
+    float* sY = reinterpret_cast<float*>(sU + L::O_TS);  // scratch [4 waves][16][17]
+    #pragma unroll 1
+    for (int dist = 1; dist < 4; ++dist) {
+      const int ntile = 4 - dist;  // tiles (I+dist, I), I = 0..ntile-1
+      const bool active = w < ntile;
+      const int I = w, R = w + dist;
+      const int cc = l & 15, m0 = 4 * (l >> 4);
+      float* y = sY + w * 16 * 17;
+      if (active) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rr = m0 + e;
+          float acc = 0.0f;
+          for (int J = I; J < R; ++J) {
+            const float* arow = sA + (16 * R + rr) * AL + 16 * J;
+            const float* tcol = sT + (16 * J) * AL + 16 * I + cc;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc += arow[j] * tcol[j * AL];
+          }
+          y[rr * 17 + cc] = acc;
+        }
+      }
+      __syncthreads();
+      if (active) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rr = m0 + e;
+          const float* trow = sT + (16 * R + rr) * AL + 16 * R;
+          float acc = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) acc += trow[j] * y[j * 17 + cc];
+          sT[(16 * R + rr) * AL + 16 * I + cc] = -acc;
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // ------------------------------------------------------ phase 4: W and U
+  MT* sTs = reinterpret_cast<MT*>(sU + L::O_TS);  // scaled T, row-major [64][TL]
+  MT* sXt = reinterpret_cast<MT*>(sU + L::O_XT);  // transposed operand [128][TL]
+  // W^T = (k^ * E)^T (T Diag(beta))^T  with k^ = k * rk folded into the T scale.
+  for (int x = tid; x < CHUNK * CHUNK; x += 256) {
+    const int r = x >> 6, i = x & 63;
+    sTs[r * TL + i] = from_f32<MT>(sT[r * AL + i] * sBeta[i] * sRk[i]);
+  }
+  {
+    float e0 = pb[0], e1 = pb[1];
+    float kg0[16], kg1[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      e0 *= aa[j][0]; e1 *= aa[j][1];
+      kg0[j] = ka[j][0] * e0; kg1[j] = ka[j][1] * e1;
+    }
+#pragma unroll
+    for (int j = 0; j < 16; j += 4) {
+      store4(sXt + c0 * TL + 16 * w + j, f32x4{kg0[j], kg0[j + 1], kg0[j + 2], kg0[j + 3]});
+      store4(sXt + (c0 + 1) * TL + 16 * w + j, f32x4{kg1[j], kg1[j + 1], kg1[j + 2], kg1[j + 3]});
+    }
+  }
+  __syncthreads();
+  // 32 output tiles of W^T: (channel block mt 0..7) x (token block nt 0..3); 8 per wave.
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int tile = 8 * w + t, mt = tile >> 2, nt = tile & 3;
+    f32x4 c = {0, 0, 0, 0};
+    c = mma16_rows<MT, CHUNK>(sXt + 16 * mt * TL, TL, sTs + 16 * nt * TL, TL, c, l);
+    // c[e] = W^T[16mt + 4(l/16) + e][16nt + l%16] = W[tok][ch..ch+3]
+    const int tok = 16 * nt + (l & 15), ch = 16 * mt + 4 * (l >> 4);
+    store4(gW + tok * DH + ch, c);
+  }
+  __syncthreads();
+  // U = (T Diag(beta)) v
+  for (int x = tid; x < CHUNK * CHUNK; x += 256) {
+    const int r = x >> 6, i = x & 63;
+    sTs[r * TL + i] = from_f32<MT>(sT[r * AL + i] * sBeta[i]);
+  }
+  {
+    float v0[16], v1[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = 16 * w + j;
+      if (r < len) {
+        f32x2 xv = load2(gv + ((size_t)(t0 + r) * H + h) * DH + c0);
+        v0[j] = xv[0]; v1[j] = xv[1];
+      } else {
+        v0[j] = v1[j] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; j += 4) {
+      store4(sXt + c0 * TL + 16 * w + j, f32x4{v0[j], v0[j + 1], v0[j + 2], v0[j + 3]});
+      store4(sXt + (c0 + 1) * TL + 16 * w + j, f32x4{v1[j], v1[j + 1], v1[j + 2], v1[j + 3]});
+    }
+  }
+  __syncthreads();
+  // 32 output tiles of U: (token block mt 0..3) x (value block nt 0..7)
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int tile = 8 * w + t, mt = tile >> 3, nt = tile & 7;
+    f32x4 c = {0, 0, 0, 0};
+    c = mma16_rows<MT, CHUNK>(sTs + 16 * mt * TL, TL, sXt + 16 * nt * TL, TL, c, l);
+    // c[e] = U[16mt + 4(l/16) + e][16nt + l%16] -> UT[dv][tok..tok+3]
+    const int dv = 16 * nt + (l & 15), tok = 16 * mt + 4 * (l >> 4);
+    store4(gUT + dv * CHUNK + tok, c);
+  }
+}
+
+}  // namespace kda

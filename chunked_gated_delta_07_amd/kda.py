@@ -1,0 +1,145 @@
+"""Thin ctypes binding over libkda (include/kda.h).
+
+Argument marshalling only: every step of the forward runs in the library's
+HIP kernels.  PyTorch provides device memory and the stream.  If the library
+is missing, every call raises; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_OK = 0
+KDA_ERR_INVALID_ARG = 1
+KDA_ERR_UNSUPPORTED = 2
+KDA_ERR_WORKSPACE = 3
+KDA_ERR_HIP = 4
+
+KDA_MODE_FP32_INTERMEDIATE = 0x1
+KDA_ACT_FP32 = 0x2
+KDA_OUT_FP32 = 0x4
+
+# Exported symbols, in declaration order of include/kda.h.
+SYMBOLS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_num_stages",
+           "kda_chunk_fwd_timed", "kda_status_string")
+
+_lib = None
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where} failed: {status_string(status)} ({status})")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libkda.so (built in-tree by __graft_entry__.build()).  Raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libkda.so not found at {path}; build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    vp = ctypes.c_void_p
+    lib.kda_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_chunk_fwd_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                                  ctypes.c_int32, ctypes.c_uint32]
+    fwd_args = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                ctypes.c_int32, ctypes.c_uint32, vp, vp, ctypes.c_size_t, vp]
+    lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd.argtypes = fwd_args
+    lib.kda_chunk_fwd_timed.restype = ctypes.c_int
+    lib.kda_chunk_fwd_timed.argtypes = fwd_args + [ctypes.POINTER(vp), ctypes.c_int32]
+    lib.kda_chunk_fwd_num_stages.restype = ctypes.c_int
+    lib.kda_chunk_fwd_num_stages.argtypes = [ctypes.c_uint32]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().kda_status_string(int(status)).decode()
+
+
+def workspace_bytes(total_tokens: int, num_seqs: int, H: int, d: int, mode: int) -> int:
+    n = load_library().kda_chunk_fwd_workspace_bytes(int(total_tokens), int(num_seqs), int(H),
+                                                     int(d), int(mode))
+    if n == ctypes.c_size_t(-1).value:
+        raise KdaError(KDA_ERR_INVALID_ARG, "kda_chunk_fwd_workspace_bytes")
+    return int(n)
+
+
+def num_stages(mode: int) -> int:
+    return int(load_library().kda_chunk_fwd_num_stages(int(mode)))
+
+
+def make_mode(fp32_intermediate: bool, act_fp32: bool = False, out_fp32: bool = False) -> int:
+    return ((KDA_MODE_FP32_INTERMEDIATE if fp32_intermediate else 0)
+            | (KDA_ACT_FP32 if act_fp32 else 0) | (KDA_OUT_FP32 if out_fp32 else 0))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def chunk_fwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, fp32_intermediate=False,
+              out_fp32=False, out=None, workspace=None, stream=None, events=None):
+    """KDA chunked forward through libkda.
+
+    q, k, v, f_raw: [T, H, 128] bfloat16 or float32 (one dtype for all);
+    b_raw: [T, H] same dtype; A_log: [H] float32; dt_bias: [H, 128] float32;
+    cu_seqlens: [N+1] int32.  All CUDA (HIP) tensors, contiguous.  Returns
+    out [T, H, 128] (activation dtype, or float32 when out_fp32).
+    ``events``: optional list of num_stages(mode)+1 torch.cuda.Event objects
+    recorded between the kernels (kda_chunk_fwd_timed)."""
+    import torch
+
+    lib = load_library()
+    act_fp32 = q.dtype == torch.float32
+    if not act_fp32 and q.dtype != torch.bfloat16:
+        raise TypeError("activations must be bfloat16 or float32")
+    for t in (k, v, f_raw, b_raw):
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, f_raw, b_raw must share one dtype")
+    if A_log.dtype != torch.float32 or dt_bias.dtype != torch.float32:
+        raise TypeError("A_log and dt_bias must be float32")
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    T, H, d = q.shape
+    for t in (q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens):
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("all tensors must be contiguous device tensors")
+    if k.shape != q.shape or v.shape != q.shape or f_raw.shape != q.shape:
+        raise ValueError("q, k, v, f_raw must have one shape [T, H, d]")
+    if b_raw.shape != (T, H) or A_log.shape != (H,) or dt_bias.shape != (H, d):
+        raise ValueError("b_raw [T,H], A_log [H], dt_bias [H,d] expected")
+    num_seqs = cu_seqlens.numel() - 1
+    mode = make_mode(fp32_intermediate, act_fp32, out_fp32)
+    out_dtype = torch.float32 if (out_fp32 or act_fp32) else q.dtype
+    if out is None:
+        out = torch.empty((T, H, d), dtype=out_dtype, device=q.device)
+    elif out.dtype != out_dtype or out.shape != (T, H, d) or not out.is_contiguous():
+        raise ValueError("out has the wrong dtype, shape or layout")
+    nbytes = workspace_bytes(T, max(num_seqs, 1), H, d, mode) if num_seqs >= 1 else 0
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(f_raw), _ptr(b_raw), _ptr(A_log), _ptr(dt_bias),
+            _ptr(cu_seqlens), num_seqs, T, H, d, mode, _ptr(out), _ptr(workspace),
+            workspace.numel(), sp)
+    if events is None:
+        st = lib.kda_chunk_fwd(*args)
+        where = "kda_chunk_fwd"
+    else:
+        arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+        st = lib.kda_chunk_fwd_timed(*args, arr, len(events))
+        where = "kda_chunk_fwd_timed"
+    if st != KDA_OK:
+        raise KdaError(st, where)
+    return out

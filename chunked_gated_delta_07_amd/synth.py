@@ -31,10 +31,12 @@ D_DEFAULT = 128
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16 (round to nearest, ties to even); return uint16 bits."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = x.view(np.uint32)
+    # finite values are at most 0xFF7FFFFF, so adding 0x8000 cannot wrap
+    bias = (u >> np.uint32(16)) & np.uint32(1)
+    bias += np.uint32(0x7FFF)
+    out = ((u + bias) >> np.uint32(16)).astype(np.uint16)
     nan = np.isnan(x)
-    out = rounded.astype(np.uint16)
     if nan.any():
         out[nan] = 0x7FC0
     return out

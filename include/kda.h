@@ -1,0 +1,131 @@
+/*
+ * kda.h -- C ABI of libkda, the MI355X (gfx950) Kimi Delta Attention (KDA)
+ * chunked forward.
+ *
+ * Operation (per head h and per packed sequence, zero initial state):
+ *   q^_t   = q_t / sqrt(|q_t|^2 + 1e-6),   k^_t likewise       (FP32 math)
+ *   g_t[c] = -exp(A_log[h]) * softplus(f_raw_t[c] + dt_bias[h][c])
+ *   beta_t = sigmoid(b_raw_t)
+ *   S_t    = Diag(exp(g_t)) S_{t-1};  S_t += beta_t k^_t (v_t - S_t^T k^_t)^T
+ *   out_t  = S_t^T q^_t / sqrt(d)
+ * computed in 64-token chunks (intra-chunk decay-weighted blocks, a
+ * unit-lower-triangular chunk solve, a chunk-to-chunk state pass, and an
+ * output combine).
+ *
+ * What the pages fix: the operator is the chunked KDA forward of xtuner PR
+ * #2153 "GLM-5.3-Flash F6.2: KDA correctness and FLA sequence parallelism"
+ * (KDA module section: gate computed outside the kernel from FP32 A_log and
+ * dt_bias, sigmoid beta, packed multi-document inputs, a fixed-layout FP32
+ * gate prefix); its two precision modes and the packed-offset interface come
+ * from xtuner PR #2301 "[Enhancement] Add opt-in FP32 KDA chunk computation"
+ * (section Change: promote Q/K/V before the L2 norm, keep normalised vectors
+ * and chunk solve / state intermediates in FP32, cast only the visible output
+ * back; no initial/final state).  The 64-head x 128-dim geometry is the one
+ * both pages measure.
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked "device" are device memory owned by the caller; the
+ *    library never frees or retains them.  All arrays are row-major,
+ *    contiguous and at least 16-byte aligned.
+ *  - Calls are asynchronous and ordered on `stream` (a hipStream_t; NULL is
+ *    the default stream).  The library performs no device allocation, no
+ *    host<->device copy and no synchronisation inside a call, so a call can
+ *    be captured into a HIP graph.
+ *  - Host-side argument errors are reported before anything is launched.
+ *  - Status codes are the KDA_* values below; kda_status_string() names them.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define KDA_API __attribute__((visibility("default")))
+#else
+#define KDA_API
+#endif
+
+/* Status codes. */
+#define KDA_OK 0
+#define KDA_ERR_INVALID_ARG 1 /* null pointer, H < 1, num_seqs < 1, T < 0, unknown mode bit */
+#define KDA_ERR_UNSUPPORTED 2 /* d != 128 (the only head dimension built)                 */
+#define KDA_ERR_WORKSPACE 3   /* workspace_bytes smaller than kda_chunk_fwd_workspace_bytes */
+#define KDA_ERR_HIP 4         /* a kernel launch failed (hipGetLastError)                 */
+
+/* Mode bits (bitwise OR).  Unknown bits are rejected.
+ * KDA_MODE_FP32_INTERMEDIATE: 0 = BF16 intermediates (normalised q/k, the
+ *   chunk-solve outputs W/U, the output-combine matrices and the state
+ *   snapshots used as matrix operands are bfloat16, accumulation is FP32);
+ *   1 = every intermediate and matrix product in FP32 (xtuner PR #2301,
+ *   section Change).  In both modes the gate, its chunk prefix, the
+ *   forward substitution and the running state are FP32.
+ * KDA_ACT_FP32: activation dtype of q, k, v, f_raw, b_raw: 0 = bfloat16,
+ *   1 = float32.
+ * KDA_OUT_FP32: dtype of out: 0 = the activation dtype, 1 = float32. */
+#define KDA_MODE_FP32_INTERMEDIATE 0x1u
+#define KDA_ACT_FP32 0x2u
+#define KDA_OUT_FP32 0x4u
+#define KDA_MODE_ALL_BITS 0x7u
+
+/* Bytes of caller-provided scratch that kda_chunk_fwd needs for this shape.
+ * Depends only on the arguments; monotone non-decreasing in total_tokens and
+ * num_seqs.  Returns 0 when total_tokens == 0, and (size_t)-1 when the
+ * arguments are invalid (negative sizes, d != 128, unknown mode bits). */
+KDA_API size_t kda_chunk_fwd_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t d,
+                                     uint32_t mode);
+
+/* KDA chunked forward over a packed batch.
+ *  q, k, v, f_raw : device, [total_tokens][H][d], activation dtype
+ *  b_raw          : device, [total_tokens][H], activation dtype (beta logits)
+ *  A_log          : device, [H], float32
+ *  dt_bias        : device, [H][d], float32
+ *  cu_seqlens     : device, [num_seqs + 1], int32; sequence n covers tokens
+ *                   [cu_seqlens[n], cu_seqlens[n+1]).  Preconditions (not
+ *                   checked, since checking would need a device read):
+ *                   cu_seqlens[0] = 0, non-decreasing, cu_seqlens[num_seqs] =
+ *                   total_tokens.  Empty sequences are allowed.  The state is
+ *                   zero at every sequence start and never crosses a
+ *                   boundary; no final state is returned.
+ *  num_seqs >= 1, total_tokens >= 0, H >= 1, d == 128.
+ *  out            : device, [total_tokens][H][d], dtype per KDA_OUT_FP32;
+ *                   every element is written.  Must not alias any input.
+ *  workspace      : device scratch of workspace_bytes >= the query above,
+ *                   256-byte aligned; contents on entry are ignored.
+ * total_tokens == 0 returns KDA_OK without launching anything (out and the
+ * inputs may then be NULL).  Two host threads may call concurrently only with
+ * distinct workspaces. */
+KDA_API int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* f_raw,
+                  const void* b_raw, const float* A_log, const float* dt_bias,
+                  const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens, int32_t H,
+                  int32_t d, uint32_t mode, void* out, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/* Number of kernels kda_chunk_fwd launches for this mode (the stages timed by
+ * kda_chunk_fwd_timed). */
+KDA_API int kda_chunk_fwd_num_stages(uint32_t mode);
+
+/* Same as kda_chunk_fwd, and additionally records events[i] (hipEvent_t,
+ * created by the caller) on `stream` before stage i and events[n] after the
+ * last stage, n = kda_chunk_fwd_num_stages(mode); num_events must be n + 1.
+ * Used by the benchmark to time each kernel on the stream it runs on. */
+KDA_API int kda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void* f_raw,
+                        const void* b_raw, const float* A_log, const float* dt_bias,
+                        const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                        int32_t H, int32_t d, uint32_t mode, void* out, void* workspace,
+                        size_t workspace_bytes, void* stream, void* const* events,
+                        int32_t num_events);
+
+/* Static, NUL-terminated name of a status code ("KDA_OK", ...; "unknown"
+ * for other values). */
+KDA_API const char* kda_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,71 @@
+"""Shared helpers for the GPU tests: move seeded inputs to the device, run the
+library through its C ABI, run the oracle on a subset of heads, compare."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from chunked_gated_delta_07_amd import synth
+
+# Tolerances on the whole output tensor (relative L2) and per element (max abs).
+TOL_FP32_REL = 1e-4
+TOL_FP32_MAXABS = 1e-3
+TOL_BF16_REL = 1e-2
+
+
+def to_device(inp: synth.KdaInputs, dev):
+    import torch
+
+    def t(a, bf16):
+        x = torch.from_numpy(np.ascontiguousarray(a))
+        if bf16:
+            x = x.view(torch.bfloat16)
+        return x.to(dev)
+
+    bf = inp.act == "bf16"
+    return [t(inp.q, bf), t(inp.k, bf), t(inp.v, bf), t(inp.f_raw, bf), t(inp.b_raw, bf),
+            t(inp.A_log, False), t(inp.dt_bias, False), t(inp.cu_seqlens, False)]
+
+
+def run_gpu(inp: synth.KdaInputs, fp32_intermediate: bool, out_fp32: bool, dev="cuda:0",
+            args=None, workspace=None):
+    import torch
+
+    from chunked_gated_delta_07_amd import kda
+
+    if args is None:
+        args = to_device(inp, dev)
+    out = kda.chunk_fwd(*args, fp32_intermediate=fp32_intermediate, out_fp32=out_fp32,
+                        workspace=workspace)
+    torch.cuda.synchronize()
+    return out
+
+
+def out_to_f64(out) -> np.ndarray:
+    import torch
+
+    return out.to(torch.float64).cpu().numpy()
+
+
+def oracle_heads(inp: synth.KdaInputs, heads, plant=0):
+    """FP64 oracle output for the given head indices only: [T, len(heads), d]."""
+    heads = np.asarray(heads)
+    conv = (lambda a: synth.bf16_bits_to_f32(a).astype(np.float64)) if inp.act == "bf16" else (
+        lambda a: a.astype(np.float64))
+    sub = dict(q=conv(inp.q[:, heads]), k=conv(inp.k[:, heads]), v=conv(inp.v[:, heads]),
+               f_raw=conv(inp.f_raw[:, heads]), b_raw=conv(inp.b_raw[:, heads]),
+               A_log=inp.A_log[heads].astype(np.float64),
+               dt_bias=inp.dt_bias[heads].astype(np.float64), cu_seqlens=inp.cu_seqlens)
+    return oracle.kda_forward(**sub, plant=plant)
+
+
+def rel_l2(a, b):
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def max_abs(a, b):
+    return float(np.max(np.abs(a - b))) if a.size else 0.0
+
+
+def bf16_round_f64(x: np.ndarray) -> np.ndarray:
+    return synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(x.astype(np.float32))).astype(np.float64)

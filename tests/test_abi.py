@@ -1,0 +1,99 @@
+"""The C-ABI library loads on a machine without a GPU, exports every symbol
+include/kda.h declares, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+LIB = os.path.join(ROOT, "chunked_gated_delta_07_amd", "libkda.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libkda.so not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return re.findall(r"KDA_API\s+[\w\s\*]+?\b(kda_\w+)\s*\(", src)
+
+
+def test_exports_match_header():
+    from chunked_gated_delta_07_amd import kda
+
+    decl = _declared()
+    assert decl and set(decl) == set(kda.SYMBOLS)
+    out = subprocess.check_output(["nm", "-D", "--defined-only", LIB], text=True)
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for name in decl:
+        assert name in exported, name
+    # nothing else with C linkage leaks out under the kda_ prefix
+    assert {n for n in exported if n.startswith("kda_")} == set(decl)
+    lib = ctypes.CDLL(LIB)
+    for name in decl:
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings():
+    from chunked_gated_delta_07_amd import kda
+
+    names = [kda.status_string(i) for i in range(5)]
+    assert names == ["KDA_OK", "KDA_ERR_INVALID_ARG", "KDA_ERR_UNSUPPORTED", "KDA_ERR_WORKSPACE",
+                     "KDA_ERR_HIP"]
+    assert kda.status_string(99) == "unknown"
+
+
+def _call(lib, *, N=1, T=10, H=64, d=128, mode=0, ptrs=True, ws_bytes=None):
+    p = ctypes.c_void_p(16) if ptrs else None  # never dereferenced: the checks fail first
+    if ws_bytes is None:
+        ws_bytes = 0
+    return lib.kda_chunk_fwd(p, p, p, p, p, p, p, p, N, T, H, d, mode, p, p, ws_bytes, None)
+
+
+def test_argument_errors_before_launch():
+    from chunked_gated_delta_07_amd import kda
+
+    lib = kda.load_library()
+    assert _call(lib, ptrs=False) == kda.KDA_ERR_INVALID_ARG          # null pointers
+    assert _call(lib, H=0) == kda.KDA_ERR_INVALID_ARG                 # H < 1
+    assert _call(lib, N=0) == kda.KDA_ERR_INVALID_ARG                 # num_seqs < 1
+    assert _call(lib, T=-1) == kda.KDA_ERR_INVALID_ARG                # negative T
+    assert _call(lib, mode=0x8) == kda.KDA_ERR_INVALID_ARG            # unknown mode bit
+    assert _call(lib, d=64) == kda.KDA_ERR_UNSUPPORTED                # d != 128
+    assert _call(lib, ws_bytes=1) == kda.KDA_ERR_WORKSPACE            # workspace too small
+    assert _call(lib, T=0, ptrs=False) == kda.KDA_OK                  # empty batch: no-op
+    # timed variant needs n+1 non-null events
+    p = ctypes.c_void_p(16)
+    ev = (ctypes.c_void_p * 2)(None, None)
+    n = kda.num_stages(0)
+    assert lib.kda_chunk_fwd_timed(p, p, p, p, p, p, p, p, 1, 10, 4, 128, 0, p, p, 1 << 40, None,
+                                   ev, 2) == kda.KDA_ERR_INVALID_ARG
+    assert n >= 1
+
+
+def test_workspace_query():
+    from chunked_gated_delta_07_amd import kda
+
+    assert kda.workspace_bytes(0, 1, 64, 128, 0) == 0
+    with pytest.raises(kda.KdaError):
+        kda.workspace_bytes(10, 1, 64, 64, 0)
+    with pytest.raises(kda.KdaError):
+        kda.workspace_bytes(10, 1, 64, 128, 0x10)
+    prev = 0
+    for T in (1, 63, 64, 65, 1000, 16384):
+        for N in (1, 2, 7):
+            if N > T:
+                continue
+            b = kda.workspace_bytes(T, N, 64, 128, 0)
+            b32 = kda.workspace_bytes(T, N, 64, 128, 1)
+            assert b > 0 and b32 > b and b % 256 == 0
+    for T in range(1, 400, 7):
+        b = kda.workspace_bytes(T, 3, 8, 128, 0)
+        assert b >= prev
+        prev = b
+    prev = 0
+    for N in range(1, 50):
+        b = kda.workspace_bytes(1000, N, 8, 128, 0)
+        assert b >= prev
+        prev = b

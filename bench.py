@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA chunked forward (libkda) on one MI355X.
+
+Workload: one sequence of 16384 tokens, 64 heads x 128 dims, bfloat16
+activations, synthetic seeded inputs (the 16K-token operator timing of xtuner
+PR #2301 "[Enhancement] Add opt-in FP32 KDA chunk computation", Validation).
+One step = one kda_chunk_fwd call over the whole batch (every kernel of the
+path).  The headline line times BF16-intermediate mode; FP32-intermediate mode
+is timed on the same inputs and reported alongside.
+
+Prints ONE JSON line.  --gpus above 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA chunk fwd tokens/s @H=64,d=128,16K tok; % of FLOP/HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_TFLOPS = 2500.0      # dense
+MFMA_FP32_TFLOPS = 157.3
+H200_CONTEXT_P50_US = {"bf16": 4050.976, "fp32": 7842.400}  # pages' H200 numbers (context only)
+
+# Algorithmic counts per token-head (d = 128, chunk 64), see the design doc.
+BYTES_IN_PER_TH = lambda s: (4 * 128 + 1) * s    # q, k, v, f_raw, b_raw
+BYTES_OUT_PER_TH = lambda s: 128 * s             # out
+FLOP_PER_TH = 139264                             # 3 d^2 + 1.5 C d + C d MACs, x2
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "chunked_gated_delta_07_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(name.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str, mode: str):
+    """HBM traffic per launch measured by rocprofv3 counters (committed in
+    profiles/), or None when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"counters_{kernel}_{workload}_{mode}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(T: int, budget_s: float):
+    """Time the FP64 oracle on the host cores on a bounded sample of the same
+    workload (all 16384 tokens, a subset of heads), scaled to tokens/s at H=64."""
+    import numpy as np
+
+    import oracle
+    from chunked_gated_delta_07_amd import synth
+
+    H_total = 64
+    probe = synth.make_inputs([0, 2048], H=1, d=128, act="bf16", seed=77)
+    t0 = time.perf_counter()
+    oracle.kda_forward(**probe.as_f64())
+    rate = 2048 / max(time.perf_counter() - t0, 1e-6)  # token-heads/s on one head
+    threads = oracle.num_threads()
+    # pick heads so the timed run is about budget_s (parallel over heads)
+    est_per_head = T / rate
+    nh = int(max(1, min(H_total, budget_s * min(threads, H_total) / max(est_per_head, 1e-6))))
+    inp = synth.make_inputs([0, T], H=nh, d=128, act="bf16", seed=1003)
+    f64 = inp.as_f64()
+    t0 = time.perf_counter()
+    oracle.kda_forward(**f64)
+    dt = time.perf_counter() - t0
+    return {"value": T * nh / H_total / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{T} tokens x {nh} of {H_total} heads (bf16 inputs, FP64 token-serial "
+                      f"recurrence, OpenMP over heads), {dt:.1f} s; scaled to 64 heads"}
+
+
+def copy_calibration(nbytes: int):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes}))
+
+
+def time_mode(args_dev, fp32: bool, steps: int, warmup: int):
+    import torch
+
+    from chunked_gated_delta_07_amd import kda
+
+    q = args_dev[0]
+    T, H, d = q.shape
+    mode = kda.make_mode(fp32, False, False)
+    ws = torch.empty(kda.workspace_bytes(T, args_dev[7].numel() - 1, H, d, mode),
+                     dtype=torch.uint8, device=q.device)
+    out = torch.empty((T, H, d), dtype=q.dtype, device=q.device)
+    stream = torch.cuda.current_stream()
+    nst = kda.num_stages(mode)
+    for _ in range(warmup):
+        kda.chunk_fwd(*args_dev, fp32_intermediate=fp32, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(steps)]
+    for e in evs:  # create the events outside the timed region
+        for x in e:
+            x.record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        kda.chunk_fwd(*args_dev, fp32_intermediate=fp32, out=out, workspace=ws, events=evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_step_us = [evs[i][0].elapsed_time(evs[i][nst]) * 1e3 for i in range(steps)]
+    stage_us = [[evs[i][s].elapsed_time(evs[i][s + 1]) * 1e3 for i in range(steps)] for s in range(nst)]
+    return {
+        "ms_per_step": wall * 1e3 / steps,
+        "p50_us": statistics.median(per_step_us),
+        "max_us": max(per_step_us),
+        "stage_avg_us": [sum(s) / len(s) for s in stage_us],
+    }
+
+
+def roofline_for(mode_name: str, T: int, H: int, res: dict, workload: str):
+    """Dominant kernel of the path (by measured time) against its roofline."""
+    names = ["chunk_table", "intra", "state_pass"]
+    st = res["stage_avg_us"]
+    dom = max(range(len(st)), key=lambda i: st[i])
+    act = 2  # bf16 activations
+    th = T * H
+    alg_bytes = {0: 4 * 2, 1: th * BYTES_IN_PER_TH(act), 2: th * BYTES_OUT_PER_TH(act)}[dom]
+    t = st[dom] * 1e-6
+    achieved = alg_bytes / t / 1e9
+    if mode_name == "bf16":
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        # FP32-intermediate mode: MFMA-FP32 bound by the algorithmic FLOP count
+        fl = th * FLOP_PER_TH / (res["p50_us"] * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(fl, 2), "peak": MFMA_FP32_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(fl / MFMA_FP32_TFLOPS, 4)}
+    roof["kernel"] = names[dom]
+    roof["kernel_avg_us"] = round(st[dom], 2)
+    roof["traffic"] = load_traffic(names[dom], workload, mode_name) if mode_name == "bf16" else None
+    # whole path against the HBM roofline (algorithmic bytes of the method)
+    path_bytes = th * (BYTES_IN_PER_TH(act) + BYTES_OUT_PER_TH(act))
+    path_gbs = path_bytes / (res["p50_us"] * 1e-6) / 1e9
+    roof["path_hbm_frac"] = round(path_gbs / HBM_PEAK_GBS, 4)
+    roof["path_mfma_bf16_frac"] = round(th * FLOP_PER_TH / (res["p50_us"] * 1e-6) / 1e12
+                                        / MFMA_BF16_TFLOPS, 4)
+    return roof
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--only-mode", choices=["bf16", "fp32"], default=None,
+                    help="time one precision mode only (for profiling runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="run only a device copy of BYTES bytes (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} requested; this build runs on one GPU only "
+              f"(no multi-GPU path), use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
+    import torch
+
+    from chunked_gated_delta_07_amd import kda, synth
+
+    kda.load_library()
+    cfg = synth.CONFIGS[3]
+    inp = synth.config_inputs(3)
+    T, H, d = inp.T, inp.H, inp.d
+    dev = torch.device("cuda:0")
+
+    def t(a, bf16):
+        x = torch.from_numpy(a)
+        return (x.view(torch.bfloat16) if bf16 else x).to(dev)
+
+    args_dev = [t(inp.q, True), t(inp.k, True), t(inp.v, True), t(inp.f_raw, True),
+                t(inp.b_raw, True), t(inp.A_log, False), t(inp.dt_bias, False),
+                t(inp.cu_seqlens, False)]
+    torch.cuda.synchronize()
+    modes = ["bf16", "fp32"] if args.only_mode is None else [args.only_mode]
+    res = {m: time_mode(args_dev, m == "fp32", args.steps, args.warmup) for m in modes}
+    head = modes[0]
+    r = res[head]
+    line = {
+        "metric": METRIC,
+        "value": round(T / (r["ms_per_step"] * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if head == "bf16" else "fp32",
+        "data": "synthetic",
+        "config": {"workload": cfg["name"], "tokens": T, "sequences": 1, "heads": H, "head_dim": d,
+                   "chunk": 64, "activations": "bf16",
+                   "intermediates": "bf16" if head == "bf16" else "fp32", "seq_len": T,
+                   "global_batch": 1, "parallelism": "none"},
+        "p50_us": round(r["p50_us"], 2),
+        "max_us": round(r["max_us"], 2),
+        "stage_avg_us": {n: round(x, 2) for n, x in
+                         zip(["chunk_table", "intra", "state_pass"], r["stage_avg_us"])},
+        "roofline": roofline_for(head, T, H, r, cfg["name"]),
+    }
+    for m in modes[1:]:
+        rm = res[m]
+        line[f"{m}_mode"] = {
+            "value": round(T / (rm["ms_per_step"] * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(rm["ms_per_step"], 4), "p50_us": round(rm["p50_us"], 2),
+            "max_us": round(rm["max_us"], 2),
+            "stage_avg_us": {n: round(x, 2) for n, x in
+                             zip(["chunk_table", "intra", "state_pass"], rm["stage_avg_us"])},
+            "roofline": roofline_for(m, T, H, rm, cfg["name"]),
+        }
+    line["context_h200_p50_us"] = H200_CONTEXT_P50_US
+    line["kernel_source_hash"] = kernel_source_hash()
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(T, args.cpu_budget_s)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

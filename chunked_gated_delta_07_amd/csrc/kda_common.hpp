@@ -87,19 +87,42 @@ template <> struct Mma16<float> {
 // as rows of K contiguous elements ("row-of-K" layout): A row m at a + m*lda,
 // B column n at b + n*ldb.  Lane l reads row (l%16) and contracts over the
 // K-range [g*K/4, (g+1)*K/4) with g = l/16, so every lane reads one
-// contiguous run from each operand.  K must be a multiple of 4*PER_LANE*...
+// contiguous run from each operand.
 template <typename MT, int K>
 __device__ __forceinline__ f32x4 mma16_rows(const MT* a, int lda, const MT* b, int ldb, f32x4 c,
                                             int lane) {
   typedef Mma16<MT> M;
   constexpr int KG = K / 4;                       // contracted range per lane group
-  constexpr int STEPS = KG / M::PER_LANE;         // instructions
   const int r = lane & 15, g = lane >> 4;
   const MT* pa = a + r * lda + g * KG;
   const MT* pb = b + r * ldb + g * KG;
+  if constexpr (M::PER_LANE == 8) {
 #pragma unroll
-  for (int s = 0; s < STEPS; ++s)
-    c = M::mma(M::load(pa + s * M::PER_LANE), M::load(pb + s * M::PER_LANE), c);
+    for (int s = 0; s < KG / 8; ++s) c = M::mma(M::load(pa + 8 * s), M::load(pb + 8 * s), c);
+  } else {
+    // fp32: one 16-byte read per operand feeds four instructions
+#pragma unroll 2
+    for (int s = 0; s < KG / 4; ++s) {
+      const f32x4 a4 = *reinterpret_cast<const f32x4*>(pa + 4 * s);
+      const f32x4 b4 = *reinterpret_cast<const f32x4*>(pb + 4 * s);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c = M::mma(a4[e], b4[e], c);
+    }
+  }
+  return c;
+}
+
+// fp32 C[16][16] += A[16][K] * B[K][16], A row-major (lda), B k-major
+// (B[k][n] at b + k*ldb + n).  K multiple of 4.
+template <int K>
+__device__ __forceinline__ f32x4 mma16_f32_kn(const float* a, int lda, const float* b, int ldb,
+                                              f32x4 c, int lane) {
+  constexpr int KG = K / 4;
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < KG; ++s)
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r * lda + g * KG + s], b[(g * KG + s) * ldb + r], c,
+                                             0, 0, 0);
   return c;
 }
 
@@ -128,10 +151,23 @@ template <> struct Mma32<float> {
 __device__ __forceinline__ int row32(int e, int lane) { return 8 * (e >> 2) + 4 * ((lane >> 5) & 1) + (e & 3); }
 
 // ---------------------------------------------------------------- math
-// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^{-|x|}).
-__device__ __forceinline__ float softplus_f(float x) {
-  return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x)));
+// Hardware base-2 exponential / logarithm (v_exp_f32 / v_log_f32, about 1 ulp).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+constexpr float LOG2E = 1.4426950408889634f;
+
+// Per-token decay a = exp(g), g = -lam * softplus(x), computed in base 2:
+//   softplus(x) log2(e) = max(x,0) log2(e) + log2(1 + 2^(-|x| log2 e)).
+// Only the absolute error of g matters (it is the relative error of a); the
+// log2(1 + t) form has absolute error ~1e-7 for every x.  lam = 0 gives a = 1.
+__device__ __forceinline__ float decay_from_gate(float x, float lam) {
+  const float t = exp2_hw(-fabsf(x) * LOG2E);
+  const float sp2 = fmaxf(x, 0.0f) * LOG2E + log2_hw(1.0f + t);
+  return exp2_hw(-lam * sp2);
 }
-__device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
+__device__ __forceinline__ float sigmoid_f(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + exp2_hw(-x * LOG2E));
+}
+__device__ __forceinline__ float rsqrt_hw(float x) { return __builtin_amdgcn_rsqf(x); }
 
 }  // namespace kda

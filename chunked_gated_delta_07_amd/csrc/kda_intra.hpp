@@ -34,19 +34,44 @@
 
 namespace kda {
 
-// Per-(chunk, head) record in the workspace, element type MT:
-//   W   [64][128]  row-major (token, key channel)
-//   Qt  [64][128]  row-major
-//   KbT [128][64]  transposed (key channel, token)
-//   UT  [128][64]  transposed (value channel, token)
-//   P   [64][64]   row-major (token, token)
-// plus Gam [128] float in a separate array.
+// Per-(chunk, head) record in the workspace, element type MT, holding
+//   W [64 tok][128 key ch], Qt [64][128], Kb^T [128 key ch][64 tok],
+//   U [64 tok][128 value ch], P [64][64]
+// plus Gam [128] float in a separate array.  Each matrix is stored in the
+// order in which the state pass reads it: one state-pass load instruction
+// (64 lanes x 16 bytes) covers 1 KB of contiguous memory.  The state pass uses
+// 32x32 MFMA tiles; lane L = 32 g + col holds tile row/column col and the
+// contracted-index half g (see kda_scan.hpp).  FE = elements per 16 bytes.
 constexpr int OFF_W = 0;
 constexpr int OFF_QT = CHUNK * DH;
 constexpr int OFF_KBT = 2 * CHUNK * DH;
 constexpr int OFF_UT = 3 * CHUNK * DH;
 constexpr int OFF_P = 4 * CHUNK * DH;
 constexpr int REC = 4 * CHUNK * DH + CHUNK * CHUNK;
+
+template <typename MT> struct Frag {
+  static constexpr int FE = 16 / (int)sizeof(MT);
+  // W / Qt element (token r, key channel c): A operand of [W;Qt] S0, contracted
+  // over key channels, half g = c/64.
+  __host__ __device__ static constexpr int a(int r, int c) {
+    return (((r >> 5) * (64 / FE) + (c & 63) / FE) * 64 + 32 * (c >> 6) + (r & 31)) * FE + (c & 63) % FE;
+  }
+  // Kb^T element (key channel c, token t): A operand of Kb^T D, contracted over
+  // tokens, half g = t/32.
+  __host__ __device__ static constexpr int kb(int c, int t) {
+    return (((c >> 5) * (32 / FE) + (t & 31) / FE) * 64 + 32 * (t >> 5) + (c & 31)) * FE + (t & 31) % FE;
+  }
+  // P element (token r, token i): A operand of P D, rows 32..63 -> waves 2,3.
+  __host__ __device__ static constexpr int pm(int r, int i) {
+    return (((r >> 5) * (32 / FE) + (i & 31) / FE) * 64 + 32 * (i >> 5) + (r & 31)) * FE + (i & 31) % FE;
+  }
+  // U element (token t, value channel v): lane (g, col = v%32) of wave t/32 in
+  // value block v/32 holds the 16 tokens 32w + 8e + 4g + i as q = 4e + i.
+  __host__ __device__ static constexpr int u(int t, int v) {
+    return ((((v >> 5) * 2 + (t >> 5)) * (16 / FE) + (4 * ((t & 31) >> 3) + (t & 3)) / FE) * 64 +
+            32 * ((t >> 2) & 1) + (v & 31)) * FE + (4 * ((t & 31) >> 3) + (t & 3)) % FE;
+  }
+};
 
 struct IntraArgs {
   const void* q;
@@ -123,7 +148,7 @@ template <typename MT> struct IntraLds {
 __device__ __forceinline__ constexpr int combo(int R, int I) { return (R * (R - 1)) / 2 + I; }
 
 template <typename TA, typename MT>
-__global__ __launch_bounds__(256) void kda_intra_kernel(IntraArgs p) {
+__global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
   typedef IntraLds<MT> L;
   constexpr int ROWL = L::ROWL, TL = L::TL, AL = L::AL;
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
@@ -158,30 +183,32 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(IntraArgs p) {
   // Per lane: rows 16w..16w+15, channels c0, c0+1.  Rows past the chunk end
   // hold q = k = v = 0 and decay 1, which makes every formula exact without
   // special cases (they add nothing to any sum and do not decay the state).
+  // All row loads are issued before any use (rows past the end re-read the
+  // chunk's first row and are masked), so their latencies overlap.
   const float lam = expf(p.A_log[h]);  // exp(-inf) = 0 gives g = 0 exactly
   const f32x2 dtb = *reinterpret_cast<const f32x2*>(p.dt_bias + (size_t)h * DH + c0);
   float qa[16][2], ka[16][2], aa[16][2];
+  {
+    f32x2 xq[16], xk[16], xf[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int r = 16 * w + j;
-    if (r < len) {
-      const size_t o = ((size_t)(t0 + r) * H + h) * DH + c0;
-      f32x2 xq = load2(gq + o), xk = load2(gk + o), xf = load2(gf + o);
-      qa[j][0] = xq[0]; qa[j][1] = xq[1];
-      ka[j][0] = xk[0]; ka[j][1] = xk[1];
-      // g = -exp(A_log) softplus(f + dt_bias);  a = exp(g)
-      aa[j][0] = expf(-lam * softplus_f(xf[0] + dtb[0]));
-      aa[j][1] = expf(-lam * softplus_f(xf[1] + dtb[1]));
-    } else {
-      qa[j][0] = qa[j][1] = ka[j][0] = ka[j][1] = 0.0f;
-      aa[j][0] = aa[j][1] = 1.0f;
+    for (int j = 0; j < 16; ++j) {
+      const int r = 16 * w + j;
+      const size_t o = ((size_t)(t0 + (r < len ? r : 0)) * H + h) * DH + c0;
+      xq[j] = load2(gq + o); xk[j] = load2(gk + o); xf[j] = load2(gf + o);
     }
+    float bl = 0.0f;
+    if (l < 16) bl = to_f32(gb[(size_t)(t0 + (16 * w + l < len ? 16 * w + l : 0)) * H + h]);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const bool ok = 16 * w + j < len;
+      qa[j][0] = ok ? xq[j][0] : 0.0f; qa[j][1] = ok ? xq[j][1] : 0.0f;
+      ka[j][0] = ok ? xk[j][0] : 0.0f; ka[j][1] = ok ? xk[j][1] : 0.0f;
+      aa[j][0] = ok ? decay_from_gate(xf[j][0] + dtb[0], lam) : 1.0f;
+      aa[j][1] = ok ? decay_from_gate(xf[j][1] + dtb[1], lam) : 1.0f;
+    }
+    if (l < 16) sBeta[16 * w + l] = (16 * w + l < len) ? sigmoid_f(bl) : 0.0f;
   }
-  if (l < 16) {
-    const int r = 16 * w + l;
-    sBeta[r] = (r < len) ? sigmoid_f(to_f32(gb[(size_t)(t0 + r) * H + h])) : 0.0f;
-  }
-  // raw rows for the MFMA work inside the diagonal block
+  // raw rows for the MFMA work inside the diagonal block (wave-private)
   MT* priv = reinterpret_cast<MT*>(sU + w * L::PRIV_BYTES);
   MT* pK = priv;               // rows 0..15
   MT* pQ = priv + 16 * ROWL;   // rows 16..31
@@ -198,7 +225,11 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(IntraArgs p) {
     sTot[w * DH + c0] = t0c; sTot[w * DH + c0 + 1] = t1c;
     sA0[w * DH + c0] = aa[0][0]; sA0[w * DH + c0 + 1] = aa[0][1];
   }
-  __syncthreads();
+  // From here to the end of the diagonal-block work each wave touches only
+  // its own rows: LDS traffic of one wave is processed in program order, so a
+  // compiler-level fence is all the ordering needed.
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
 
   // Norms (sum of squares) and the plain q.k diagonal via MFMA on the raw rows.
   {
@@ -210,14 +241,15 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(IntraArgs p) {
     if (n >= m0 && n < m0 + 4) {
       const int e = n - m0;
       const int r = 16 * w + n;
-      const float rk = 1.0f / sqrtf(ckk[e] + p.eps);
-      const float rq = 1.0f / sqrtf(cqq[e] + p.eps);
+      const float rk = rsqrt_hw(ckk[e] + p.eps);
+      const float rq = rsqrt_hw(cqq[e] + p.eps);
       sRk[r] = rk;
       sRq[r] = rq;
-      gP[r * CHUNK + r] = from_f32<MT>(rq * rk * cqk[e]);  // P[r][r], decay 1
+      gP[Frag<MT>::pm(r, r)] = from_f32<MT>(rq * rk * cqk[e]);  // P[r][r], decay 1
     }
   }
-  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
 
   // Diagonal block: pair vectors kd_(u,i)[c] = k_i[c] prod_{i<j<=u} a_j[c],
   // 16 per batch; MFMA k.kd and q.kd; keep the (u, column) entry.
@@ -237,7 +269,8 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(IntraArgs p) {
           store2(pD + n * ROWL + c0, 0.0f, 0.0f);
         }
       }
-      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
       f32x4 ca = {0, 0, 0, 0}, cp = {0, 0, 0, 0};
       ca = mma16_rows<MT, DH>(pK, ROWL, pD, ROWL, ca, l);
       cp = mma16_rows<MT, DH>(pQ, ROWL, pD, ROWL, cp, l);
@@ -252,13 +285,15 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(IntraArgs p) {
             const float vp = e == 0 ? cp[0] : e == 1 ? cp[1] : e == 2 ? cp[2] : cp[3];
             const int ru = 16 * w + u, ri = 16 * w + i;
             sA[ru * AL + ri] = sBeta[ru] * sRk[ru] * sRk[ri] * va;
-            gP[ru * CHUNK + ri] = from_f32<MT>(sRq[ru] * sRk[ri] * vp);
+            gP[Frag<MT>::pm(ru, ri)] = from_f32<MT>(sRq[ru] * sRk[ri] * vp);
           }
         }
       }
-      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
     }
   }
+  __syncthreads();
 
   // ------------------------------------------------------- phase 2: cross-block
   // Per channel: product of decays of the blocks before / after mine.
@@ -276,7 +311,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(IntraArgs p) {
       const int r = 16 * w + j;
       e0 *= aa[j][0]; e1 *= aa[j][1];
       const float rq = sRq[r];
-      store2(gQt + r * DH + c0, qa[j][0] * rq * e0, qa[j][1] * rq * e1);
+      store2(gQt + Frag<MT>::a(r, c0), qa[j][0] * rq * e0, qa[j][1] * rq * e1);
     }
     float s0 = sa[0], s1 = sa[1];
     float kb0[16], kb1[16];
@@ -289,8 +324,8 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(IntraArgs p) {
     }
 #pragma unroll
     for (int j = 0; j < 16; j += 4) {
-      store4(gKbT + (size_t)c0 * CHUNK + 16 * w + j, f32x4{kb0[j], kb0[j + 1], kb0[j + 2], kb0[j + 3]});
-      store4(gKbT + (size_t)(c0 + 1) * CHUNK + 16 * w + j,
+      store4(gKbT + Frag<MT>::kb(c0, 16 * w + j), f32x4{kb0[j], kb0[j + 1], kb0[j + 2], kb0[j + 3]});
+      store4(gKbT + Frag<MT>::kb(c0 + 1, 16 * w + j),
              f32x4{kb1[j], kb1[j + 1], kb1[j + 2], kb1[j + 3]});
     }
     if (w == 0) {
@@ -354,76 +389,107 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(IntraArgs p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int ru = 16 * R + m0 + e;
-      if (isq) gP[ru * CHUNK + ri] = from_f32<MT>(sRq[ru] * sRk[ri] * c[e]);
+      if (isq) gP[Frag<MT>::pm(ru, ri)] = from_f32<MT>(sRq[ru] * sRk[ri] * c[e]);
       else sA[ru * AL + ri] = sBeta[ru] * sRk[ru] * sRk[ri] * c[e];
     }
   }
   // upper triangle of P is zero
   for (int x = tid; x < CHUNK * CHUNK; x += 256) {
     const int r = x >> 6, i = x & 63;
-    if (i > r) gP[x] = from_f32<MT>(0.0f);
+    if (i > r) gP[Frag<MT>::pm(r, i)] = from_f32<MT>(0.0f);
   }
   __syncthreads();
 
   // ------------------------------------------------- phase 3: T = (I + A)^{-1}
+  // Forward substitution, blocked: 4x4 diagonal blocks explicitly, then
+  // 4x4-block substitution to the 16x16 diagonal blocks (one wave each), then
+  // 16x16-block substitution across waves with FP32 MFMA:
+  //   T_RI = -T_RR sum_{J=I}^{R-1} A_RJ T_JI.
   float* sT = reinterpret_cast<float*>(sU + L::O_T);
-  // diagonal blocks by forward substitution, one column per lane
-  if (l < 16) {
-    const int cc = l;
-    float t[16];
+  // values for the U product, loaded early so their latency hides under the solve
+  float v0[16], v1[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float acc = (r == cc) ? 1.0f : 0.0f;
-      const float* arow = sA + (16 * w + r) * AL + 16 * w;
-#pragma unroll
-      for (int i = 0; i < r; ++i) acc -= (i >= cc) ? arow[i] * t[i] : 0.0f;
-      t[r] = (r < cc) ? 0.0f : acc;
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sT[(16 * w + r) * AL + 16 * w + cc] = t[r];
+  for (int j = 0; j < 16; ++j) {
+    const int r = 16 * w + j;
+    const f32x2 xv = load2(gv + ((size_t)(t0 + (r < len ? r : 0)) * H + h) * DH + c0);
+    v0[j] = r < len ? xv[0] : 0.0f;
+    v1[j] = r < len ? xv[1] : 0.0f;
   }
-  // blocks above the diagonal are zero
-  for (int x = tid; x < CHUNK * CHUNK; x += 256) {
-    const int r = x >> 6, i = x & 63;
-    if ((i >> 4) > (r >> 4)) sT[r * AL + i] = 0.0f;
+  {
+    // (a) 4x4 diagonal blocks.  Lane: sub-block sb, row r4, column c4.
+    const int sb = l >> 4, r4 = (l >> 2) & 3, c4 = l & 3;
+    const int base = 16 * w + 4 * sb;
+    const float* ab = sA + base * AL + base;
+    const float n10 = ab[1 * AL + 0], n20 = ab[2 * AL + 0], n21 = ab[2 * AL + 1];
+    const float n30 = ab[3 * AL + 0], n31 = ab[3 * AL + 1], n32 = ab[3 * AL + 2];
+    // column c4 of the inverse: t_c = 1, t_i = -sum_{c<=j<i} n_ij t_j
+    float t0v = c4 == 0 ? 1.0f : 0.0f;
+    float t1v = c4 == 1 ? 1.0f : (c4 < 1 ? -n10 * t0v : 0.0f);
+    float t2v = c4 == 2 ? 1.0f : (c4 < 2 ? -(n20 * t0v + n21 * t1v) : 0.0f);
+    float t3v = c4 == 3 ? 1.0f : -(n30 * t0v + n31 * t1v + n32 * t2v);
+    const float mine = r4 == 0 ? t0v : r4 == 1 ? t1v : r4 == 2 ? t2v : t3v;
+    sT[(base + r4) * AL + base + c4] = mine;
+    // zero the rest of this wave's 16x16 diagonal block above the 4x4 diagonal
+    // and every block above the 16x16 diagonal
+    for (int x = l; x < 16 * 16; x += 64) {
+      const int rr = x >> 4, cc = x & 15;
+      if ((cc >> 2) > (rr >> 2)) sT[(16 * w + rr) * AL + 16 * w + cc] = 0.0f;
+    }
+    for (int x = tid; x < CHUNK * CHUNK; x += 256) {
+      const int rr = x >> 6, cc = x & 63;
+      if ((cc >> 4) > (rr >> 4)) sT[rr * AL + cc] = 0.0f;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // (b) 4x4-block substitution inside the 16x16 block, by block distance d.
+#pragma unroll
+    for (int d = 1; d < 4; ++d) {
+      if (l < 16 * (4 - d)) {
+        const int I4 = l >> 4, R4 = I4 + d, rr = (l >> 2) & 3, cc = l & 3;
+        const int rb = 16 * w + 4 * R4, cb = 16 * w + 4 * I4;
+        float y[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          float acc = 0.0f;
+          for (int J = I4; J < R4; ++J) {
+            const float* arow = sA + (rb + m) * AL + 16 * w + 4 * J;
+            const float* tcol = sT + (16 * w + 4 * J) * AL + cb + cc;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc += arow[j] * tcol[j * AL];
+          }
+          y[m] = acc;
+        }
+        const float* trr = sT + (rb + rr) * AL + rb;
+        sT[(rb + rr) * AL + cb + cc] = -(trr[0] * y[0] + trr[1] * y[1] + trr[2] * y[2] + trr[3] * y[3]);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    }
   }
   __syncthreads();
-  // Off-diagonal blocks: T_RI = -T_RR sum_{J=I}^{R-1} A_RJ T_JI, by distance R-I.
-  // Lane: column cc = l%16, rows 4*(l/16)+e.
   {
-    float* sY = reinterpret_cast<float*>(sU + L::O_TS);  // scratch [4 waves][16][17]
-    #pragma unroll 1
+    // (c) 16x16 blocks across waves, FP32 MFMA.  Y goes through a per-wave
+    // scratch tile so it can feed the second product as its B operand.
+    float* sY = reinterpret_cast<float*>(sU + L::O_TS) + w * 16 * 20;
+    const int nn = l & 15, m0 = 4 * (l >> 4);
+#pragma unroll
     for (int dist = 1; dist < 4; ++dist) {
-      const int ntile = 4 - dist;  // tiles (I+dist, I), I = 0..ntile-1
-      const bool active = w < ntile;
-      const int I = w, R = w + dist;
-      const int cc = l & 15, m0 = 4 * (l >> 4);
-      float* y = sY + w * 16 * 17;
-      if (active) {
+      if (w < 4 - dist) {
+        const int I = w, R = w + dist;
+        f32x4 y = {0, 0, 0, 0};
+        const float* a = sA + (16 * R) * AL + 16 * I;
+        const float* b = sT + (16 * I) * AL + 16 * I;
+        if (dist == 1) y = mma16_f32_kn<16>(a, AL, b, AL, y, l);
+        else if (dist == 2) y = mma16_f32_kn<32>(a, AL, b, AL, y, l);
+        else y = mma16_f32_kn<48>(a, AL, b, AL, y, l);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int rr = m0 + e;
-          float acc = 0.0f;
-          for (int J = I; J < R; ++J) {
-            const float* arow = sA + (16 * R + rr) * AL + 16 * J;
-            const float* tcol = sT + (16 * J) * AL + 16 * I + cc;
+        for (int e = 0; e < 4; ++e) sY[(m0 + e) * 20 + nn] = y[e];
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        f32x4 t = {0, 0, 0, 0};
+        t = mma16_f32_kn<16>(sT + (16 * R) * AL + 16 * R, AL, sY, 20, t, l);
 #pragma unroll
-            for (int j = 0; j < 16; ++j) acc += arow[j] * tcol[j * AL];
-          }
-          y[rr * 17 + cc] = acc;
-        }
-      }
-      __syncthreads();
-      if (active) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int rr = m0 + e;
-          const float* trow = sT + (16 * R + rr) * AL + 16 * R;
-          float acc = 0.0f;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) acc += trow[j] * y[j * 17 + cc];
-          sT[(16 * R + rr) * AL + 16 * I + cc] = -acc;
-        }
+        for (int e = 0; e < 4; ++e) sT[(16 * R + m0 + e) * AL + 16 * I + nn] = -t[e];
       }
       __syncthreads();
     }
@@ -460,7 +526,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(IntraArgs p) {
     c = mma16_rows<MT, CHUNK>(sXt + 16 * mt * TL, TL, sTs + 16 * nt * TL, TL, c, l);
     // c[e] = W^T[16mt + 4(l/16) + e][16nt + l%16] = W[tok][ch..ch+3]
     const int tok = 16 * nt + (l & 15), ch = 16 * mt + 4 * (l >> 4);
-    store4(gW + tok * DH + ch, c);
+    store4(gW + Frag<MT>::a(tok, ch), c);
   }
   __syncthreads();
   // U = (T Diag(beta)) v
@@ -469,17 +535,6 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(IntraArgs p) {
     sTs[r * TL + i] = from_f32<MT>(sT[r * AL + i] * sBeta[i]);
   }
   {
-    float v0[16], v1[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int r = 16 * w + j;
-      if (r < len) {
-        f32x2 xv = load2(gv + ((size_t)(t0 + r) * H + h) * DH + c0);
-        v0[j] = xv[0]; v1[j] = xv[1];
-      } else {
-        v0[j] = v1[j] = 0.0f;
-      }
-    }
 #pragma unroll
     for (int j = 0; j < 16; j += 4) {
       store4(sXt + c0 * TL + 16 * w + j, f32x4{v0[j], v0[j + 1], v0[j + 2], v0[j + 3]});
@@ -493,9 +548,9 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(IntraArgs p) {
     const int tile = 8 * w + t, mt = tile >> 3, nt = tile & 7;
     f32x4 c = {0, 0, 0, 0};
     c = mma16_rows<MT, CHUNK>(sTs + 16 * mt * TL, TL, sXt + 16 * nt * TL, TL, c, l);
-    // c[e] = U[16mt + 4(l/16) + e][16nt + l%16] -> UT[dv][tok..tok+3]
+    // c[e] = U[16mt + 4(l/16) + e][16nt + l%16]: four consecutive tokens
     const int dv = 16 * nt + (l & 15), tok = 16 * mt + 4 * (l >> 4);
-    store4(gUT + dv * CHUNK + tok, c);
+    store4(gUT + Frag<MT>::u(tok, dv), c);
   }
 }
 

@@ -16,6 +16,8 @@
 // 0,1 form W S0 (-> D), waves 2,3 form Qt S0 (-> output).
 #pragma once
 
+#include <type_traits>
+
 #include "kda_common.hpp"
 #include "kda_intra.hpp"
 
@@ -51,12 +53,138 @@ __device__ __forceinline__ void scan_unit(int bid, int& pair, int& vb) {
   pair = (slot >> 2) * 8 + xcd;
 }
 
+// Per-chunk operands of one lane, loaded one chunk ahead of their use.  The
+// record is stored in this kernel's read order (Frag in kda_intra.hpp), so
+// every load below is one contiguous 16-byte piece per lane and 1 KB per wave.
+// ROLE 0 (waves 0,1): W rows and U values; ROLE 1 (waves 2,3): Qt and P rows.
+template <typename MT, int ROLE> struct ScanOps {
+  static constexpr int FE = 16 / (int)sizeof(MT);
+  typedef typename std::conditional<sizeof(MT) == 2, bf16x8, f32x4>::type v16;
+  static constexpr int NX = ROLE == 0 ? 16 / FE : 32 / FE;
+  v16 a[64 / FE];   // W or Qt row: 64 key channels
+  v16 kb[32 / FE];  // Kb^T row: 32 tokens
+  v16 x[NX];        // U values (role 0) or P row (role 1)
+  f32x4 gm[4];      // Gam at the wave's 16 state rows
+};
+
+template <typename MT, int ROLE>
+__device__ __forceinline__ void scan_load(ScanOps<MT, ROLE>& o, const MT* __restrict__ R,
+                                          const float* __restrict__ gm, int wp, int w, int l,
+                                          int g, int vb) {
+  typedef ScanOps<MT, ROLE> O;
+  constexpr int FE = O::FE;
+  typedef typename O::v16 v16;
+  const MT* A = R + (ROLE == 0 ? OFF_W : OFF_QT) + wp * (64 / FE) * 64 * FE + l * FE;
+#pragma unroll
+  for (int s = 0; s < 64 / FE; ++s) o.a[s] = *reinterpret_cast<const v16*>(A + s * 64 * FE);
+  const MT* kb = R + OFF_KBT + w * (32 / FE) * 64 * FE + l * FE;
+#pragma unroll
+  for (int s = 0; s < 32 / FE; ++s) o.kb[s] = *reinterpret_cast<const v16*>(kb + s * 64 * FE);
+  const MT* x = ROLE == 0 ? R + OFF_UT + (vb * 2 + wp) * (16 / FE) * 64 * FE + l * FE
+                          : R + OFF_P + wp * (32 / FE) * 64 * FE + l * FE;
+#pragma unroll
+  for (int s = 0; s < O::NX; ++s) o.x[s] = *reinterpret_cast<const v16*>(x + s * 64 * FE);
+#pragma unroll
+  for (int e4 = 0; e4 < 4; ++e4) o.gm[e4] = *reinterpret_cast<const f32x4*>(gm + 32 * w + 8 * e4 + 4 * g);
+}
+
+// C += A B over NK contracted values per lane: A from register fragments, B
+// from LDS (contiguous NK values at pb), 16-byte LDS reads in both precisions.
+template <typename MT, int NK, typename V>
+__device__ __forceinline__ f32x16 mma32_frags(const V* afr, const MT* pb, f32x16 c) {
+  typedef Mma32<MT> M;
+  if constexpr (sizeof(MT) == 2) {
+#pragma unroll
+    for (int s = 0; s < NK / 8; ++s) c = M::mma(afr[s], *reinterpret_cast<const bf16x8*>(pb + 8 * s), c);
+  } else {
+#pragma unroll
+    for (int s = 0; s < NK / 4; ++s) {
+      const f32x4 b4 = *reinterpret_cast<const f32x4*>(pb + 4 * s);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c = M::mma(afr[s][e], b4[e], c);
+    }
+  }
+  return c;
+}
+template <typename V> __device__ __forceinline__ float val_at(const V* f, int q) {
+  constexpr int FE = sizeof(f[0][0]) == 2 ? 8 : 4;
+  return (float)f[q / FE][q % FE];
+}
+
+// The chunk loop of one wave.  ROLE 0 forms D = U - W S0 (and publishes it);
+// ROLE 1 forms the output rows.  Both update their 32 rows of the state.
+// Every wave runs the same number of barriers.
+template <typename MT, typename TO, int ROLE>
+__device__ __forceinline__ void scan_chunks(const ScanArgs& p, MT* sS, MT* sD, int h, int cbeg,
+                                            int cend, int tseq, int tend, int vb, int w, int l) {
+  typedef ScanLds<MT> L;
+  constexpr int SL = L::SL, DL = L::DL;
+  const int col = l & 31, g = l >> 5, wp = w & 1;
+  const int H = p.H;
+  const MT* __restrict__ rec = reinterpret_cast<const MT*>(p.rec);
+  TO* __restrict__ out = reinterpret_cast<TO*>(p.out);
+
+  // running state rows 32w.. (key), columns vb*32.. (value), FP32
+  f32x16 S;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) S[e] = 0.0f;
+
+  ScanOps<MT, ROLE> cur, nxt;
+  scan_load(cur, rec + ((size_t)cbeg * H + h) * REC, p.gam + ((size_t)cbeg * H + h) * DH, wp, w, l,
+            g, vb);
+  __syncthreads();  // zeroed S0 operand visible
+
+  for (int c = cbeg; c < cend; ++c) {
+    if (c + 1 < cend)
+      scan_load(nxt, rec + ((size_t)(c + 1) * H + h) * REC, p.gam + ((size_t)(c + 1) * H + h) * DH,
+                wp, w, l, g, vb);
+    const int ctok = tseq + (c - cbeg) * CHUNK;
+    const int len = min(CHUNK, tend - ctok);
+    // X = A S0, A = W rows (role 0) or Qt rows (role 1); 128 key channels
+    // contracted, lane group g covers channels [64g, 64g+64).
+    f32x16 X;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) X[e] = 0.0f;
+    X = mma32_frags<MT, 64>(cur.a, sS + col * SL + 64 * g, X);
+    if constexpr (ROLE == 0) {
+      // D = U - W S0 at tokens 32wp + row32(e), value column col
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        f32x4 d;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d[i] = val_at(cur.x, 4 * e4 + i) - X[4 * e4 + i];
+        store4(sD + col * DL + 32 * wp + 8 * e4 + 4 * g, d);
+      }
+    }
+    __syncthreads();  // D complete; every wave is done reading S0
+    if constexpr (ROLE == 1) {
+      // out = scale (Qt S0 + P D): rows 32wp.. of P, 64 tokens contracted
+      X = mma32_frags<MT, 32>(cur.x, sD + col * DL + 32 * g, X);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int tk = 32 * wp + row32(e, l);
+        if (tk < len)
+          out[((size_t)(ctok + tk) * H + h) * DH + DVB * vb + col] = from_f32<TO>(p.scale * X[e]);
+      }
+    }
+    // S_next = Diag(Gam) S0 + Kb^T D, rows 32w.. of Kb^T, 64 tokens contracted
+#pragma unroll
+    for (int e = 0; e < 16; ++e) S[e] *= cur.gm[e >> 2][e & 3];
+    S = mma32_frags<MT, 32>(cur.kb, sD + col * DL + 32 * g, S);
+    // operand copy of the new state, transposed: sS[value][key]
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4)
+      store4(sS + col * SL + 32 * w + 8 * e4 + 4 * g,
+             f32x4{S[4 * e4], S[4 * e4 + 1], S[4 * e4 + 2], S[4 * e4 + 3]});
+    cur = nxt;
+    __syncthreads();  // new S0 complete; D may be overwritten
+  }
+}
+
 template <typename MT, typename TO>
 __global__ __launch_bounds__(256) void kda_scan_kernel(ScanArgs p) {
   typedef ScanLds<MT> L;
-  typedef Mma32<MT> M;
-  constexpr int SL = L::SL, DL = L::DL;
-  constexpr int PL = M::PER_LANE;
+  constexpr int SL = L::SL;
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
   MT* sS = reinterpret_cast<MT*>(smem + L::O_S);  // S0^T [32 dv][SL]
   MT* sD = reinterpret_cast<MT*>(smem + L::O_D);  // D^T  [32 dv][DL]
@@ -68,80 +196,10 @@ __global__ __launch_bounds__(256) void kda_scan_kernel(ScanArgs p) {
   const int cbeg = p.cfirst[n], cend = p.cfirst[n + 1];
   if (cbeg == cend) return;
   const int tseq = p.cu[n], tend = p.cu[n + 1];
-
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int col = l & 31, g = l >> 5;  // MFMA column (value channel in block), lane group
-  const int H = p.H;
-  const MT* __restrict__ rec = reinterpret_cast<const MT*>(p.rec);
-  TO* __restrict__ out = reinterpret_cast<TO*>(p.out);
-
-  // running state rows 32w.. (key), columns vb*32.. (value), FP32
-  f32x16 S;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) S[e] = 0.0f;
   for (int x = tid; x < DVB * SL; x += 256) sS[x] = from_f32<MT>(0.0f);
-  __syncthreads();
-
-  for (int c = cbeg; c < cend; ++c) {
-    const MT* R = rec + ((size_t)c * H + h) * REC;
-    const int ctok = tseq + (c - cbeg) * CHUNK;
-    const int len = min(CHUNK, tend - ctok);
-    // X = A S0, A = W rows (waves 0,1) or Qt rows (waves 2,3); 128 key channels
-    // contracted, lane group g covers channels [64g, 64g+64).
-    const MT* A = R + (w < 2 ? OFF_W + (32 * w) * DH : OFF_QT + (32 * (w - 2)) * DH);
-    f32x16 X;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) X[e] = 0.0f;
-    {
-      const MT* pa = A + col * DH + 64 * g;
-      const MT* pb = sS + col * SL + 64 * g;
-#pragma unroll
-      for (int s = 0; s < 64 / PL; ++s) X = M::mma(M::load(pa + s * PL), M::load(pb + s * PL), X);
-    }
-    if (w < 2) {
-      // D = U - W S0 at tokens 32w + row32(e), value column col
-      const MT* ut = R + OFF_UT + (size_t)(DVB * vb + col) * CHUNK + 32 * w;
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int tk = 8 * e4 + 4 * g;
-        f32x4 d;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) d[i] = to_f32(ut[tk + i]) - X[4 * e4 + i];
-        store4(sD + col * DL + 32 * w + tk, d);
-      }
-    }
-    __syncthreads();
-    if (w >= 2) {
-      // out = scale (Qt S0 + P D): rows 32(w-2).. of P, 64 tokens contracted
-      const MT* pa = R + OFF_P + (32 * (w - 2) + col) * CHUNK + 32 * g;
-      const MT* pb = sD + col * DL + 32 * g;
-#pragma unroll
-      for (int s = 0; s < 32 / PL; ++s) X = M::mma(M::load(pa + s * PL), M::load(pb + s * PL), X);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int tk = 32 * (w - 2) + row32(e, l);
-        if (tk < len)
-          out[((size_t)(ctok + tk) * H + h) * DH + DVB * vb + col] = from_f32<TO>(p.scale * X[e]);
-      }
-    }
-    // S_next = Diag(Gam) S0 + Kb^T D, rows 32w.. of Kb^T, 64 tokens contracted
-    {
-      const float* gm = p.gam + ((size_t)c * H + h) * DH + 32 * w;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) S[e] *= gm[row32(e, l)];
-      const MT* pa = R + OFF_KBT + (32 * w + col) * CHUNK + 32 * g;
-      const MT* pb = sD + col * DL + 32 * g;
-#pragma unroll
-      for (int s = 0; s < 32 / PL; ++s) S = M::mma(M::load(pa + s * PL), M::load(pb + s * PL), S);
-      // operand copy of the new state, transposed: sS[value][key]
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int kr = 32 * w + 8 * e4 + 4 * g;
-        store4(sS + col * SL + kr, f32x4{S[4 * e4], S[4 * e4 + 1], S[4 * e4 + 2], S[4 * e4 + 3]});
-      }
-    }
-    __syncthreads();
-  }
+  if (w < 2) scan_chunks<MT, TO, 0>(p, sS, sD, h, cbeg, cend, tseq, tend, vb, w, l);
+  else scan_chunks<MT, TO, 1>(p, sS, sD, h, cbeg, cend, tseq, tend, vb, w, l);
 }
 
 }  // namespace kda

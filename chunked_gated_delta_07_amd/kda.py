@@ -137,6 +137,9 @@ def chunk_fwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, fp32_intermedia
         st = lib.kda_chunk_fwd(*args)
         where = "kda_chunk_fwd"
     else:
+        for e in events:  # torch creates the underlying hipEvent on first record
+            if not e.cuda_event:
+                e.record(stream)
         arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
         st = lib.kda_chunk_fwd_timed(*args, arr, len(events))
         where = "kda_chunk_fwd_timed"

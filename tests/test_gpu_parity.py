@@ -180,12 +180,27 @@ def test_intra_records_match_chunk_oracle():
     f64 = inp.as_f64()
     _, R = oracle.kda_chunked(**f64, chunk=64, records=True)
     assert nc == R["W"].shape[0]
+    # the library stores each matrix in its state pass's read order (the
+    # index maps below restate that order; FE = 4 float32 elements per 16 B)
+    FE = 4
+    r, c = np.meshgrid(np.arange(64), np.arange(128), indexing="ij")
+    ia = ((((r >> 5) * (64 // FE) + (c & 63) // FE) * 64 + 32 * (c >> 6) + (r & 31)) * FE
+          + (c & 63) % FE)
+    ch, t = np.meshgrid(np.arange(128), np.arange(64), indexing="ij")
+    ikb = ((((ch >> 5) * (32 // FE) + (t & 31) // FE) * 64 + 32 * (t >> 5) + (ch & 31)) * FE
+           + (t & 31) % FE)
+    q16 = 4 * ((r & 31) >> 3) + (r & 3)  # r: token, c: value channel
+    iu = (((((c >> 5) * 2 + (r >> 5)) * (16 // FE) + q16 // FE) * 64 + 32 * ((r >> 2) & 1)
+           + (c & 31)) * FE + q16 % FE)
+    rr, ii = np.meshgrid(np.arange(64), np.arange(64), indexing="ij")
+    ip = ((((rr >> 5) * (32 // FE) + (ii & 31) // FE) * 64 + 32 * (ii >> 5) + (rr & 31)) * FE
+          + (ii & 31) % FE)
     checks = {
-        "W": (rec[:, :, 0:8192].reshape(nc, H, 64, 128), R["W"]),
-        "Qt": (rec[:, :, 8192:16384].reshape(nc, H, 64, 128), R["Qt"]),
-        "KbT": (rec[:, :, 16384:24576].reshape(nc, H, 128, 64), np.swapaxes(R["Kb"], 2, 3)),
-        "UT": (rec[:, :, 24576:32768].reshape(nc, H, 128, 64), np.swapaxes(R["U"], 2, 3)),
-        "P": (rec[:, :, 32768:].reshape(nc, H, 64, 64), R["P"]),
+        "W": (rec[:, :, 0:8192][:, :, ia], R["W"]),
+        "Qt": (rec[:, :, 8192:16384][:, :, ia], R["Qt"]),
+        "KbT": (rec[:, :, 16384:24576][:, :, ikb], np.swapaxes(R["Kb"], 2, 3)),
+        "U": (rec[:, :, 24576:32768][:, :, iu], R["U"]),
+        "P": (rec[:, :, 32768:][:, :, ip], R["P"]),
         "Gam": (gam, R["Gamma"]),
     }
     for name, (got, ref) in checks.items():

@@ -111,73 +111,102 @@ template <typename V> __device__ __forceinline__ float val_at(const V* f, int q)
   return (float)f[q / FE][q % FE];
 }
 
-// The chunk loop of one wave.  ROLE 0 forms D = U - W S0 (and publishes it);
-// ROLE 1 forms the output rows.  Both update their 32 rows of the state.
-// Every wave runs the same number of barriers.
+// One chunk of the state pass for one wave.  ROLE 0 forms D = U - W S0 (and
+// publishes it); ROLE 1 forms the output rows.  Both update their 32 rows of
+// the running state S.  Two barriers per chunk, the same for every wave.
 template <typename MT, typename TO, int ROLE>
-__device__ __forceinline__ void scan_chunks(const ScanArgs& p, MT* sS, MT* sD, int h, int cbeg,
-                                            int cend, int tseq, int tend, int vb, int w, int l) {
+__device__ __forceinline__ void scan_step(const ScanArgs& p, const ScanOps<MT, ROLE>& cur, f32x16& S,
+                                          MT* sS, MT* sD, int h, int ctok, int len, int vb, int w,
+                                          int l) {
   typedef ScanLds<MT> L;
   constexpr int SL = L::SL, DL = L::DL;
   const int col = l & 31, g = l >> 5, wp = w & 1;
+  TO* __restrict__ out = reinterpret_cast<TO*>(p.out);
+  // X = A S0, A = W rows (role 0) or Qt rows (role 1); 128 key channels
+  // contracted, lane group g covers channels [64g, 64g+64).
+  f32x16 X;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) X[e] = 0.0f;
+  X = mma32_frags<MT, 64>(cur.a, sS + col * SL + 64 * g, X);
+  if constexpr (ROLE == 0) {
+    // D = U - W S0 at tokens 32wp + row32(e), value column col
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      f32x4 d;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d[i] = val_at(cur.x, 4 * e4 + i) - X[4 * e4 + i];
+      store4(sD + col * DL + 32 * wp + 8 * e4 + 4 * g, d);
+    }
+  }
+  __syncthreads();  // D complete; every wave is done reading S0
+  if constexpr (ROLE == 1) {
+    // out = scale (Qt S0 + P D): rows 32wp.. of P, 64 tokens contracted
+    X = mma32_frags<MT, 32>(cur.x, sD + col * DL + 32 * g, X);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int tk = 32 * wp + row32(e, l);
+      if (tk < len)
+        out[((size_t)(ctok + tk) * p.H + h) * DH + DVB * vb + col] = from_f32<TO>(p.scale * X[e]);
+    }
+  }
+  // S_next = Diag(Gam) S0 + Kb^T D, rows 32w.. of Kb^T, 64 tokens contracted
+#pragma unroll
+  for (int e = 0; e < 16; ++e) S[e] *= cur.gm[e >> 2][e & 3];
+  S = mma32_frags<MT, 32>(cur.kb, sD + col * DL + 32 * g, S);
+  // operand copy of the new state, transposed: sS[value][key]
+#pragma unroll
+  for (int e4 = 0; e4 < 4; ++e4)
+    store4(sS + col * SL + 32 * w + 8 * e4 + 4 * g,
+           f32x4{S[4 * e4], S[4 * e4 + 1], S[4 * e4 + 2], S[4 * e4 + 3]});
+  __syncthreads();  // new S0 complete; D may be overwritten
+}
+
+// The chunk loop of one wave: operands are loaded ahead into rotating register
+// sets (bf16: two chunks ahead, three sets; fp32: one chunk ahead, two sets).
+template <typename MT, typename TO, int ROLE>
+__device__ __forceinline__ void scan_chunks(const ScanArgs& p, MT* sS, MT* sD, int h, int cbeg,
+                                            int cend, int tseq, int tend, int vb, int w, int l) {
+  const int g = l >> 5, wp = w & 1;
   const int H = p.H;
   const MT* __restrict__ rec = reinterpret_cast<const MT*>(p.rec);
-  TO* __restrict__ out = reinterpret_cast<TO*>(p.out);
-
+  auto load = [&](ScanOps<MT, ROLE>& o, int c) {
+    scan_load(o, rec + ((size_t)c * H + h) * REC, p.gam + ((size_t)c * H + h) * DH, wp, w, l, g, vb);
+  };
+  auto step = [&](const ScanOps<MT, ROLE>& o, f32x16& S, int c) {
+    const int ctok = tseq + (c - cbeg) * CHUNK;
+    scan_step<MT, TO, ROLE>(p, o, S, sS, sD, h, ctok, min(CHUNK, tend - ctok), vb, w, l);
+  };
   // running state rows 32w.. (key), columns vb*32.. (value), FP32
   f32x16 S;
 #pragma unroll
   for (int e = 0; e < 16; ++e) S[e] = 0.0f;
-
-  ScanOps<MT, ROLE> cur, nxt;
-  scan_load(cur, rec + ((size_t)cbeg * H + h) * REC, p.gam + ((size_t)cbeg * H + h) * DH, wp, w, l,
-            g, vb);
+  ScanOps<MT, ROLE> o0, o1, o2;
+  load(o0, cbeg);
+  if constexpr (sizeof(MT) == 2) {
+    if (cbeg + 1 < cend) load(o1, cbeg + 1);
+  }
   __syncthreads();  // zeroed S0 operand visible
-
-  for (int c = cbeg; c < cend; ++c) {
-    if (c + 1 < cend)
-      scan_load(nxt, rec + ((size_t)(c + 1) * H + h) * REC, p.gam + ((size_t)(c + 1) * H + h) * DH,
-                wp, w, l, g, vb);
-    const int ctok = tseq + (c - cbeg) * CHUNK;
-    const int len = min(CHUNK, tend - ctok);
-    // X = A S0, A = W rows (role 0) or Qt rows (role 1); 128 key channels
-    // contracted, lane group g covers channels [64g, 64g+64).
-    f32x16 X;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) X[e] = 0.0f;
-    X = mma32_frags<MT, 64>(cur.a, sS + col * SL + 64 * g, X);
-    if constexpr (ROLE == 0) {
-      // D = U - W S0 at tokens 32wp + row32(e), value column col
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        f32x4 d;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) d[i] = val_at(cur.x, 4 * e4 + i) - X[4 * e4 + i];
-        store4(sD + col * DL + 32 * wp + 8 * e4 + 4 * g, d);
-      }
+  if constexpr (sizeof(MT) == 2) {
+    // two chunks in flight (three sets)
+    for (int c = cbeg; c < cend; c += 3) {
+      if (c + 2 < cend) load(o2, c + 2);
+      step(o0, S, c);
+      if (c + 1 >= cend) break;
+      if (c + 3 < cend) load(o0, c + 3);
+      step(o1, S, c + 1);
+      if (c + 2 >= cend) break;
+      if (c + 4 < cend) load(o1, c + 4);
+      step(o2, S, c + 2);
     }
-    __syncthreads();  // D complete; every wave is done reading S0
-    if constexpr (ROLE == 1) {
-      // out = scale (Qt S0 + P D): rows 32wp.. of P, 64 tokens contracted
-      X = mma32_frags<MT, 32>(cur.x, sD + col * DL + 32 * g, X);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int tk = 32 * wp + row32(e, l);
-        if (tk < len)
-          out[((size_t)(ctok + tk) * H + h) * DH + DVB * vb + col] = from_f32<TO>(p.scale * X[e]);
-      }
+  } else {
+    // FP32 operands are twice as large: one chunk in flight (two sets)
+    for (int c = cbeg; c < cend; c += 2) {
+      if (c + 1 < cend) load(o1, c + 1);
+      step(o0, S, c);
+      if (c + 1 >= cend) break;
+      if (c + 2 < cend) load(o0, c + 2);
+      step(o1, S, c + 1);
     }
-    // S_next = Diag(Gam) S0 + Kb^T D, rows 32w.. of Kb^T, 64 tokens contracted
-#pragma unroll
-    for (int e = 0; e < 16; ++e) S[e] *= cur.gm[e >> 2][e & 3];
-    S = mma32_frags<MT, 32>(cur.kb, sD + col * DL + 32 * g, S);
-    // operand copy of the new state, transposed: sS[value][key]
-#pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4)
-      store4(sS + col * SL + 32 * w + 8 * e4 + 4 * g,
-             f32x4{S[4 * e4], S[4 * e4 + 1], S[4 * e4 + 2], S[4 * e4 + 3]});
-    cur = nxt;
-    __syncthreads();  // new S0 complete; D may be overwritten
   }
 }
 

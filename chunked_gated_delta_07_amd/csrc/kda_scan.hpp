@@ -114,7 +114,7 @@ template <typename V> __device__ __forceinline__ float val_at(const V* f, int q)
 // One chunk of the state pass for one wave.  ROLE 0 forms D = U - W S0 (and
 // publishes it); ROLE 1 forms the output rows.  Both update their 32 rows of
 // the running state S.  Two barriers per chunk, the same for every wave.
-template <typename MT, typename TO, int ROLE>
+template <typename MT, typename TO, int ROLE, bool FULL>
 __device__ __forceinline__ void scan_step(const ScanArgs& p, const ScanOps<MT, ROLE>& cur, f32x16& S,
                                           MT* sS, MT* sD, int h, int ctok, int len, int vb, int w,
                                           int l) {
@@ -145,7 +145,9 @@ __device__ __forceinline__ void scan_step(const ScanArgs& p, const ScanOps<MT, R
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int tk = 32 * wp + row32(e, l);
-      if (tk < len)
+      // full chunks store without a branch, which keeps the memory-counter
+      // waits of the loop exact; only a sequence's last chunk is masked
+      if (FULL || tk < len)
         out[((size_t)(ctok + tk) * p.H + h) * DH + DVB * vb + col] = from_f32<TO>(p.scale * X[e]);
     }
   }
@@ -174,39 +176,62 @@ __device__ __forceinline__ void scan_chunks(const ScanArgs& p, MT* sS, MT* sD, i
   };
   auto step = [&](const ScanOps<MT, ROLE>& o, f32x16& S, int c) {
     const int ctok = tseq + (c - cbeg) * CHUNK;
-    scan_step<MT, TO, ROLE>(p, o, S, sS, sD, h, ctok, min(CHUNK, tend - ctok), vb, w, l);
+    scan_step<MT, TO, ROLE, true>(p, o, S, sS, sD, h, ctok, CHUNK, vb, w, l);
+  };
+  auto tail = [&](const ScanOps<MT, ROLE>& o, f32x16& S, int c) {
+    const int ctok = tseq + (c - cbeg) * CHUNK;
+    scan_step<MT, TO, ROLE, false>(p, o, S, sS, sD, h, ctok, tend - ctok, vb, w, l);
   };
   // running state rows 32w.. (key), columns vb*32.. (value), FP32
   f32x16 S;
 #pragma unroll
   for (int e = 0; e < 16; ++e) S[e] = 0.0f;
+  // Full chunks run in the main loop; a partial last chunk runs after it.
+  // Prefetch loads are unconditional (indices clamped to the last chunk), so
+  // every iteration issues the same memory operations and the compiler's
+  // memory-counter waits only cover the chunk being consumed.
+  const int cfull = cbeg + (tend - tseq) / CHUNK;  // chunks [cbeg, cfull) are full
+  const int clast = cend - 1;
   ScanOps<MT, ROLE> o0, o1, o2;
   load(o0, cbeg);
-  if constexpr (sizeof(MT) == 2) {
-    if (cbeg + 1 < cend) load(o1, cbeg + 1);
-  }
+  if constexpr (sizeof(MT) == 2) load(o1, min(cbeg + 1, clast));
   __syncthreads();  // zeroed S0 operand visible
+  int c = cbeg;
   if constexpr (sizeof(MT) == 2) {
-    // two chunks in flight (three sets)
-    for (int c = cbeg; c < cend; c += 3) {
-      if (c + 2 < cend) load(o2, c + 2);
+    // two chunks in flight (three sets); o0 holds chunk c, o1 chunk c+1
+    for (; c + 3 <= cfull; c += 3) {
+      load(o2, min(c + 2, clast));
       step(o0, S, c);
-      if (c + 1 >= cend) break;
-      if (c + 3 < cend) load(o0, c + 3);
+      load(o0, min(c + 3, clast));
       step(o1, S, c + 1);
-      if (c + 2 >= cend) break;
-      if (c + 4 < cend) load(o1, c + 4);
+      load(o1, min(c + 4, clast));
       step(o2, S, c + 2);
     }
+    // at most two full chunks and the partial chunk remain
+    if (c < cend) {
+      load(o2, min(c + 2, clast));
+      if (c < cfull) step(o0, S, c); else tail(o0, S, c);
+      ++c;
+    }
+    if (c < cend) {
+      if (c < cfull) step(o1, S, c); else tail(o1, S, c);
+      ++c;
+    }
+    if (c < cend) tail(o2, S, c);
   } else {
     // FP32 operands are twice as large: one chunk in flight (two sets)
-    for (int c = cbeg; c < cend; c += 2) {
-      if (c + 1 < cend) load(o1, c + 1);
+    for (; c + 2 <= cfull; c += 2) {
+      load(o1, min(c + 1, clast));
       step(o0, S, c);
-      if (c + 1 >= cend) break;
-      if (c + 2 < cend) load(o0, c + 2);
+      load(o0, min(c + 2, clast));
       step(o1, S, c + 1);
     }
+    if (c < cend) {
+      load(o1, min(c + 1, clast));
+      if (c < cfull) step(o0, S, c); else tail(o0, S, c);
+      ++c;
+    }
+    if (c < cend) tail(o1, S, c);
   }
 }
 

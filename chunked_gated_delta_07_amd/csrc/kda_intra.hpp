@@ -30,6 +30,8 @@
 // operands are staged through LDS as rows of contiguous channels.
 #pragma once
 
+#include <type_traits>
+
 #include "kda_common.hpp"
 
 namespace kda {
@@ -105,16 +107,20 @@ __device__ __forceinline__ bool locate_chunk(const int32_t* __restrict__ cu,
   return true;
 }
 
-// Diagonal-block pairs (u, i), 0 <= i < u < 16, ordered by i then u.
-__host__ __device__ constexpr int pair_first(int i) { return 15 * i - (i * (i - 1)) / 2; }
-__host__ __device__ constexpr int pair_i(int p) {
+// Pairs (u, i), i < u, inside one 8-row half of a 16-row diagonal block,
+// ordered by half, then i, then u (u, i are rows within the 16-row block).
+__host__ __device__ constexpr int pair8_first(int i) { return 7 * i - (i * (i - 1)) / 2; }
+__host__ __device__ constexpr int pair8_i(int q) {
   int i = 0;
-  while (i < 14 && pair_first(i + 1) <= p) ++i;
+  while (i < 6 && pair8_first(i + 1) <= q) ++i;
   return i;
 }
-__host__ __device__ constexpr int pair_u(int p) { return pair_i(p) + 1 + (p - pair_first(pair_i(p))); }
-constexpr int NPAIR = 120;
-constexpr int NBATCH = 8;  // ceil(120 / 16)
+__host__ __device__ constexpr int pair_i(int p) { return 8 * (p / 28) + pair8_i(p % 28); }
+__host__ __device__ constexpr int pair_u(int p) {
+  return 8 * (p / 28) + pair8_i(p % 28) + 1 + (p % 28 - pair8_first(pair8_i(p % 28)));
+}
+constexpr int NPAIR = 56;
+constexpr int NBATCH = 4;  // ceil(56 / 16)
 
 template <typename MT> struct IntraLds {
   static constexpr int ROWL = sizeof(MT) == 2 ? 136 : 132;  // padded row of 128 channels
@@ -251,7 +257,52 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   __builtin_amdgcn_wave_barrier();
 
-  // Diagonal block: pair vectors kd_(u,i)[c] = k_i[c] prod_{i<j<=u} a_j[c],
+  // Diagonal block, rows 8..15 x columns 0..7: factorised about row 8,
+  //   A[u][i] ~ (k_u prod_{8<j<=u} a_j) . (k_i prod_{i<j<=8} a_j),
+  // both factors <= 1.  X8 rows 0..7 hold the column factors, rows 8..15 the
+  // row factors of k (then of q for P); one MFMA tile each, block [8..15][0..7].
+  {
+    float x0 = 1.0f, x1 = 1.0f;
+    float ra0[8], ra1[8];
+#pragma unroll
+    for (int j = 8; j < 16; ++j) {
+      if (j > 8) { x0 *= aa[j][0]; x1 *= aa[j][1]; }
+      ra0[j - 8] = x0; ra1[j - 8] = x1;
+      store2(pD + j * ROWL + c0, ka[j][0] * x0, ka[j][1] * x1);
+    }
+    float y0 = aa[8][0], y1 = aa[8][1];
+#pragma unroll
+    for (int j = 7; j >= 0; --j) {
+      store2(pD + j * ROWL + c0, ka[j][0] * y0, ka[j][1] * y1);
+      y0 *= aa[j][0]; y1 *= aa[j][1];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    f32x4 ca = {0, 0, 0, 0};
+    ca = mma16_rows<MT, DH>(pD, ROWL, pD, ROWL, ca, l);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 8; j < 16; ++j) store2(pD + j * ROWL + c0, qa[j][0] * ra0[j - 8], qa[j][1] * ra1[j - 8]);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    f32x4 cp = {0, 0, 0, 0};
+    cp = mma16_rows<MT, DH>(pD, ROWL, pD, ROWL, cp, l);
+    const int n = l & 15, m0 = 4 * (l >> 4);
+    if (m0 >= 8 && n < 8) {
+      const int ri = 16 * w + n;
+      const float rki = sRk[ri];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ru = 16 * w + m0 + e;
+        sA[ru * AL + ri] = sBeta[ru] * sRk[ru] * rki * ca[e];
+        gP[Frag<MT>::pm(ru, ri)] = from_f32<MT>(sRq[ru] * rki * cp[e]);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
+  // Inside each 8-row half: pair vectors kd_(u,i)[c] = k_i[c] prod_{i<j<=u} a_j[c],
   // 16 per batch; MFMA k.kd and q.kd; keep the (u, column) entry.
   {
     float d0 = 1.0f, d1 = 1.0f;
@@ -393,10 +444,23 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
       else sA[ru * AL + ri] = sBeta[ru] * sRk[ru] * sRk[ri] * c[e];
     }
   }
-  // upper triangle of P is zero
-  for (int x = tid; x < CHUNK * CHUNK; x += 256) {
-    const int r = x >> 6, i = x & 63;
-    if (i > r) gP[Frag<MT>::pm(r, i)] = from_f32<MT>(0.0f);
+  // Upper triangle of P is zero.  In the stored order a 16-byte fragment holds
+  // FE consecutive columns of one row: fragments wholly above the diagonal are
+  // written as one vector, the one straddling it element by element.
+  {
+    constexpr int FE = Frag<MT>::FE;
+    typedef typename std::conditional<sizeof(MT) == 2, bf16x8, f32x4>::type v16;
+    for (int f = tid; f < CHUNK * CHUNK / FE; f += 256) {
+      const int r = f / (CHUNK / FE), i0 = (f % (CHUNK / FE)) * FE;
+      if (i0 > r) {
+        v16 z;
+#pragma unroll
+        for (int e = 0; e < FE; ++e) z[e] = from_f32<MT>(0.0f);
+        *reinterpret_cast<v16*>(gP + Frag<MT>::pm(r, i0)) = z;
+      } else {
+        for (int i = r + 1; i < i0 + FE; ++i) gP[Frag<MT>::pm(r, i)] = from_f32<MT>(0.0f);
+      }
+    }
   }
   __syncthreads();
 
@@ -498,10 +562,11 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
   // ------------------------------------------------------ phase 4: W and U
   MT* sTs = reinterpret_cast<MT*>(sU + L::O_TS);  // scaled T, row-major [64][TL]
   MT* sXt = reinterpret_cast<MT*>(sU + L::O_XT);  // transposed operand [128][TL]
-  // W^T = (k^ * E)^T (T Diag(beta))^T  with k^ = k * rk folded into the T scale.
+  // W = T (Diag(beta rk) (k * E)),  U = T (Diag(beta) v): the row scales go
+  // on the right-hand operands, T is converted once.
   for (int x = tid; x < CHUNK * CHUNK; x += 256) {
     const int r = x >> 6, i = x & 63;
-    sTs[r * TL + i] = from_f32<MT>(sT[r * AL + i] * sBeta[i] * sRk[i]);
+    sTs[r * TL + i] = from_f32<MT>(sT[r * AL + i]);
   }
   {
     float e0 = pb[0], e1 = pb[1];
@@ -509,7 +574,8 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       e0 *= aa[j][0]; e1 *= aa[j][1];
-      kg0[j] = ka[j][0] * e0; kg1[j] = ka[j][1] * e1;
+      const float sc = sBeta[16 * w + j] * sRk[16 * w + j];
+      kg0[j] = ka[j][0] * e0 * sc; kg1[j] = ka[j][1] * e1 * sc;
     }
 #pragma unroll
     for (int j = 0; j < 16; j += 4) {
@@ -529,12 +595,13 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
     store4(gW + Frag<MT>::a(tok, ch), c);
   }
   __syncthreads();
-  // U = (T Diag(beta)) v
-  for (int x = tid; x < CHUNK * CHUNK; x += 256) {
-    const int r = x >> 6, i = x & 63;
-    sTs[r * TL + i] = from_f32<MT>(sT[r * AL + i] * sBeta[i]);
-  }
+  // U = T (Diag(beta) v)
   {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float bj = sBeta[16 * w + j];
+      v0[j] *= bj; v1[j] *= bj;
+    }
 #pragma unroll
     for (int j = 0; j < 16; j += 4) {
       store4(sXt + c0 * TL + 16 * w + j, f32x4{v0[j], v0[j + 1], v0[j + 2], v0[j + 3]});

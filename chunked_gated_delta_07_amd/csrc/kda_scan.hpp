@@ -41,7 +41,9 @@ template <typename MT> struct ScanLds {
   static constexpr int DL = sizeof(MT) == 2 ? 72 : 68;    // D^T row: 64 tokens
   static constexpr int O_S = 0;
   static constexpr int O_D = O_S + DVB * SL * (int)sizeof(MT);
-  static constexpr int BYTES = O_D + DVB * DL * (int)sizeof(MT);
+  static constexpr int O_O = O_D + DVB * DL * (int)sizeof(MT);  // output tiles of waves 2,3
+  static constexpr int OT_BYTES = 32 * 32 * 4;                    // one tile, up to fp32
+  static constexpr int BYTES = O_O + (sizeof(MT) == 2 ? 2 * OT_BYTES : 0);
 };
 
 // Workgroup id -> (sequence*H + head, value block).  The four value blocks of
@@ -114,10 +116,14 @@ template <typename V> __device__ __forceinline__ float val_at(const V* f, int q)
 // One chunk of the state pass for one wave.  ROLE 0 forms D = U - W S0 (and
 // publishes it); ROLE 1 forms the output rows.  Both update their 32 rows of
 // the running state S.  Two barriers per chunk, the same for every wave.
-template <typename MT, typename TO, int ROLE, bool FULL>
+// `issue` sends the loads of a later chunk; each role issues them where it
+// would otherwise wait at a barrier (role 1 while role 0 forms D, role 0
+// while role 1 forms the output), so that the in-order load issue stays off
+// the step's dependency chain.
+template <typename MT, typename TO, int ROLE, bool FULL, typename Issue>
 __device__ __forceinline__ void scan_step(const ScanArgs& p, const ScanOps<MT, ROLE>& cur, f32x16& S,
                                           MT* sS, MT* sD, int h, int ctok, int len, int vb, int w,
-                                          int l) {
+                                          int l, Issue&& issue) {
   typedef ScanLds<MT> L;
   constexpr int SL = L::SL, DL = L::DL;
   const int col = l & 31, g = l >> 5, wp = w & 1;
@@ -137,18 +143,44 @@ __device__ __forceinline__ void scan_step(const ScanArgs& p, const ScanOps<MT, R
       for (int i = 0; i < 4; ++i) d[i] = val_at(cur.x, 4 * e4 + i) - X[4 * e4 + i];
       store4(sD + col * DL + 32 * wp + 8 * e4 + 4 * g, d);
     }
+  } else {
+    __builtin_amdgcn_sched_barrier(0);
+    issue();
+    __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();  // D complete; every wave is done reading S0
   if constexpr (ROLE == 1) {
     // out = scale (Qt S0 + P D): rows 32wp.. of P, 64 tokens contracted
     X = mma32_frags<MT, 32>(cur.x, sD + col * DL + 32 * g, X);
+    if constexpr (sizeof(MT) == 2) {
+      // The wave's 32x32 output tile goes through LDS (row = token) so the
+      // global stores are 16-byte pieces of 64-byte row segments.  (With
+      // fp32 operands the direct stores below measure faster.)
+      TO* so = reinterpret_cast<TO*>(reinterpret_cast<char*>(sS) + (L::O_O - L::O_S) +
+                                     wp * L::OT_BYTES);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int tk = 32 * wp + row32(e, l);
-      // full chunks store without a branch, which keeps the memory-counter
-      // waits of the loop exact; only a sequence's last chunk is masked
-      if (FULL || tk < len)
-        out[((size_t)(ctok + tk) * p.H + h) * DH + DVB * vb + col] = from_f32<TO>(p.scale * X[e]);
+      for (int e = 0; e < 16; ++e) so[row32(e, l) * 32 + col] = from_f32<TO>(p.scale * X[e]);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      constexpr int PE = 16 / (int)sizeof(TO);  // elements per 16-byte piece
+      typedef typename std::conditional<sizeof(TO) == 2, bf16x8, f32x4>::type vo;
+#pragma unroll
+      for (int k = 0; k < 32 * 32 / PE / 64; ++k) {
+        const int piece = k * 64 + l, row = piece / (32 / PE), c8 = (piece % (32 / PE)) * PE;
+        const int tk = 32 * wp + row;
+        // full chunks store without a branch, which keeps the memory-counter
+        // waits of the loop exact; only a sequence's last chunk is masked
+        if (FULL || tk < len)
+          *reinterpret_cast<vo*>(out + ((size_t)(ctok + tk) * p.H + h) * DH + DVB * vb + c8) =
+              *reinterpret_cast<const vo*>(so + row * 32 + c8);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int tk = 32 * wp + row32(e, l);
+        if (FULL || tk < len)
+          out[((size_t)(ctok + tk) * p.H + h) * DH + DVB * vb + col] = from_f32<TO>(p.scale * X[e]);
+      }
     }
   }
   // S_next = Diag(Gam) S0 + Kb^T D, rows 32w.. of Kb^T, 64 tokens contracted
@@ -160,6 +192,11 @@ __device__ __forceinline__ void scan_step(const ScanArgs& p, const ScanOps<MT, R
   for (int e4 = 0; e4 < 4; ++e4)
     store4(sS + col * SL + 32 * w + 8 * e4 + 4 * g,
            f32x4{S[4 * e4], S[4 * e4 + 1], S[4 * e4 + 2], S[4 * e4 + 3]});
+  if constexpr (ROLE == 0) {
+    __builtin_amdgcn_sched_barrier(0);
+    issue();
+    __builtin_amdgcn_sched_barrier(0);
+  }
   __syncthreads();  // new S0 complete; D may be overwritten
 }
 
@@ -174,14 +211,15 @@ __device__ __forceinline__ void scan_chunks(const ScanArgs& p, MT* sS, MT* sD, i
   auto load = [&](ScanOps<MT, ROLE>& o, int c) {
     scan_load(o, rec + ((size_t)c * H + h) * REC, p.gam + ((size_t)c * H + h) * DH, wp, w, l, g, vb);
   };
-  auto step = [&](const ScanOps<MT, ROLE>& o, f32x16& S, int c) {
+  auto step = [&](const ScanOps<MT, ROLE>& o, f32x16& S, int c, auto&& issue) {
     const int ctok = tseq + (c - cbeg) * CHUNK;
-    scan_step<MT, TO, ROLE, true>(p, o, S, sS, sD, h, ctok, CHUNK, vb, w, l);
+    scan_step<MT, TO, ROLE, true>(p, o, S, sS, sD, h, ctok, CHUNK, vb, w, l, issue);
   };
-  auto tail = [&](const ScanOps<MT, ROLE>& o, f32x16& S, int c) {
+  auto tail = [&](const ScanOps<MT, ROLE>& o, f32x16& S, int c, auto&& issue) {
     const int ctok = tseq + (c - cbeg) * CHUNK;
-    scan_step<MT, TO, ROLE, false>(p, o, S, sS, sD, h, ctok, tend - ctok, vb, w, l);
+    scan_step<MT, TO, ROLE, false>(p, o, S, sS, sD, h, ctok, tend - ctok, vb, w, l, issue);
   };
+  auto none = [] {};
   // running state rows 32w.. (key), columns vb*32.. (value), FP32
   f32x16 S;
 #pragma unroll
@@ -198,40 +236,35 @@ __device__ __forceinline__ void scan_chunks(const ScanArgs& p, MT* sS, MT* sD, i
   __syncthreads();  // zeroed S0 operand visible
   int c = cbeg;
   if constexpr (sizeof(MT) == 2) {
-    // two chunks in flight (three sets); o0 holds chunk c, o1 chunk c+1
+    // o0 holds chunk c, o1 chunk c+1; step c sends the loads of chunk c+2
     for (; c + 3 <= cfull; c += 3) {
-      load(o2, min(c + 2, clast));
-      step(o0, S, c);
-      load(o0, min(c + 3, clast));
-      step(o1, S, c + 1);
-      load(o1, min(c + 4, clast));
-      step(o2, S, c + 2);
+      step(o0, S, c, [&] { load(o2, min(c + 2, clast)); });
+      step(o1, S, c + 1, [&] { load(o0, min(c + 3, clast)); });
+      step(o2, S, c + 2, [&] { load(o1, min(c + 4, clast)); });
     }
     // at most two full chunks and the partial chunk remain
     if (c < cend) {
-      load(o2, min(c + 2, clast));
-      if (c < cfull) step(o0, S, c); else tail(o0, S, c);
+      auto nx = [&] { load(o2, min(c + 2, clast)); };
+      if (c < cfull) step(o0, S, c, nx); else tail(o0, S, c, nx);
       ++c;
     }
     if (c < cend) {
-      if (c < cfull) step(o1, S, c); else tail(o1, S, c);
+      if (c < cfull) step(o1, S, c, none); else tail(o1, S, c, none);
       ++c;
     }
-    if (c < cend) tail(o2, S, c);
+    if (c < cend) tail(o2, S, c, none);
   } else {
-    // FP32 operands are twice as large: one chunk in flight (two sets)
+    // FP32 operands are twice as large: two sets; step c sends chunk c+1
     for (; c + 2 <= cfull; c += 2) {
-      load(o1, min(c + 1, clast));
-      step(o0, S, c);
-      load(o0, min(c + 2, clast));
-      step(o1, S, c + 1);
+      step(o0, S, c, [&] { load(o1, min(c + 1, clast)); });
+      step(o1, S, c + 1, [&] { load(o0, min(c + 2, clast)); });
     }
     if (c < cend) {
-      load(o1, min(c + 1, clast));
-      if (c < cfull) step(o0, S, c); else tail(o0, S, c);
+      auto nx = [&] { load(o1, min(c + 1, clast)); };
+      if (c < cfull) step(o0, S, c, nx); else tail(o0, S, c, nx);
       ++c;
     }
-    if (c < cend) tail(o1, S, c);
+    if (c < cend) tail(o1, S, c, none);
   }
 }
 

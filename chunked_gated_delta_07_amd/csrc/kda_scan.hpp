@@ -41,9 +41,7 @@ template <typename MT> struct ScanLds {
   static constexpr int DL = sizeof(MT) == 2 ? 72 : 68;    // D^T row: 64 tokens
   static constexpr int O_S = 0;
   static constexpr int O_D = O_S + DVB * SL * (int)sizeof(MT);
-  static constexpr int O_O = O_D + DVB * DL * (int)sizeof(MT);  // output tiles of waves 2,3
-  static constexpr int OT_BYTES = 32 * 32 * 4;                    // one tile, up to fp32
-  static constexpr int BYTES = O_O + (sizeof(MT) == 2 ? 2 * OT_BYTES : 0);
+  static constexpr int BYTES = O_D + DVB * DL * (int)sizeof(MT);
 };
 
 // Workgroup id -> (sequence*H + head, value block).  The four value blocks of
@@ -76,18 +74,33 @@ __device__ __forceinline__ void scan_load(ScanOps<MT, ROLE>& o, const MT* __rest
   typedef ScanOps<MT, ROLE> O;
   constexpr int FE = O::FE;
   typedef typename O::v16 v16;
+  // The loads keep this order everywhere (the scheduling barriers stop the
+  // compiler from permuting them differently in the prologue and in the loop,
+  // which would make its memory-counter waits at the loop head conservative).
   const MT* A = R + (ROLE == 0 ? OFF_W : OFF_QT) + wp * (64 / FE) * 64 * FE + l * FE;
 #pragma unroll
-  for (int s = 0; s < 64 / FE; ++s) o.a[s] = *reinterpret_cast<const v16*>(A + s * 64 * FE);
+  for (int s = 0; s < 64 / FE; ++s) {
+    o.a[s] = *reinterpret_cast<const v16*>(A + s * 64 * FE);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   const MT* kb = R + OFF_KBT + w * (32 / FE) * 64 * FE + l * FE;
 #pragma unroll
-  for (int s = 0; s < 32 / FE; ++s) o.kb[s] = *reinterpret_cast<const v16*>(kb + s * 64 * FE);
+  for (int s = 0; s < 32 / FE; ++s) {
+    o.kb[s] = *reinterpret_cast<const v16*>(kb + s * 64 * FE);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   const MT* x = ROLE == 0 ? R + OFF_UT + (vb * 2 + wp) * (16 / FE) * 64 * FE + l * FE
                           : R + OFF_P + wp * (32 / FE) * 64 * FE + l * FE;
 #pragma unroll
-  for (int s = 0; s < O::NX; ++s) o.x[s] = *reinterpret_cast<const v16*>(x + s * 64 * FE);
+  for (int s = 0; s < O::NX; ++s) {
+    o.x[s] = *reinterpret_cast<const v16*>(x + s * 64 * FE);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
-  for (int e4 = 0; e4 < 4; ++e4) o.gm[e4] = *reinterpret_cast<const f32x4*>(gm + 32 * w + 8 * e4 + 4 * g);
+  for (int e4 = 0; e4 < 4; ++e4) {
+    o.gm[e4] = *reinterpret_cast<const f32x4*>(gm + 32 * w + 8 * e4 + 4 * g);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // C += A B over NK contracted values per lane: A from register fragments, B
@@ -108,6 +121,40 @@ __device__ __forceinline__ f32x16 mma32_frags(const V* afr, const MT* pb, f32x16
   }
   return c;
 }
+// C += A B with A read from LDS (contiguous NK values at pa) and B from
+// register fragments: the same MFMAs as mma32_frags with the operands
+// exchanged, so C comes out transposed.
+template <typename MT, int NK, typename V>
+__device__ __forceinline__ f32x16 mma32_lds_frags(const MT* pa, const V* bfr, f32x16 c) {
+  typedef Mma32<MT> M;
+  if constexpr (sizeof(MT) == 2) {
+#pragma unroll
+    for (int s = 0; s < NK / 8; ++s) c = M::mma(*reinterpret_cast<const bf16x8*>(pa + 8 * s), bfr[s], c);
+  } else {
+#pragma unroll
+    for (int s = 0; s < NK / 4; ++s) {
+      const f32x4 a4 = *reinterpret_cast<const f32x4*>(pa + 4 * s);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c = M::mma(a4[e], bfr[s][e], c);
+    }
+  }
+  return c;
+}
+// C += A B, both operands from register fragments (NK values per lane).
+template <typename MT, int NK, typename V>
+__device__ __forceinline__ f32x16 mma32_rr(const V* afr, const V* bfr, f32x16 c) {
+  typedef Mma32<MT> M;
+  if constexpr (sizeof(MT) == 2) {
+#pragma unroll
+    for (int s = 0; s < NK / 8; ++s) c = M::mma(afr[s], bfr[s], c);
+  } else {
+#pragma unroll
+    for (int s = 0; s < NK / 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c = M::mma(afr[s][e], bfr[s][e], c);
+  }
+  return c;
+}
 template <typename V> __device__ __forceinline__ float val_at(const V* f, int q) {
   constexpr int FE = sizeof(f[0][0]) == 2 ? 8 : 4;
   return (float)f[q / FE][q % FE];
@@ -119,7 +166,9 @@ template <typename V> __device__ __forceinline__ float val_at(const V* f, int q)
 // `issue` sends the loads of a later chunk; each role issues them where it
 // would otherwise wait at a barrier (role 1 while role 0 forms D, role 0
 // while role 1 forms the output), so that the in-order load issue stays off
-// the step's dependency chain.
+// the step's dependency chain.  With fp32 operands only one chunk is loaded
+// ahead, and role 0 issues at the start of the step so that the loads have a
+// whole step to arrive.
 template <typename MT, typename TO, int ROLE, bool FULL, typename Issue>
 __device__ __forceinline__ void scan_step(const ScanArgs& p, const ScanOps<MT, ROLE>& cur, f32x16& S,
                                           MT* sS, MT* sD, int h, int ctok, int len, int vb, int w,
@@ -128,13 +177,21 @@ __device__ __forceinline__ void scan_step(const ScanArgs& p, const ScanOps<MT, R
   constexpr int SL = L::SL, DL = L::DL;
   const int col = l & 31, g = l >> 5, wp = w & 1;
   TO* __restrict__ out = reinterpret_cast<TO*>(p.out);
-  // X = A S0, A = W rows (role 0) or Qt rows (role 1); 128 key channels
-  // contracted, lane group g covers channels [64g, 64g+64).
+  // Role 0: X = W S0 (rows = 32 tokens, columns = 32 values).  Role 1: the
+  // transposed product X = S0^T Qt^T (rows = values, columns = tokens), so
+  // that each lane ends up holding one token's run of value columns for the
+  // output store.  128 key channels contracted; lane group g covers channels
+  // [64g, 64g+64) in both forms.
   f32x16 X;
 #pragma unroll
   for (int e = 0; e < 16; ++e) X[e] = 0.0f;
-  X = mma32_frags<MT, 64>(cur.a, sS + col * SL + 64 * g, X);
+  constexpr bool EARLY = ROLE == 0 && sizeof(MT) == 4;
+  if constexpr (EARLY) {
+    issue();
+    __builtin_amdgcn_sched_barrier(0);
+  }
   if constexpr (ROLE == 0) {
+    X = mma32_frags<MT, 64>(cur.a, sS + col * SL + 64 * g, X);
     // D = U - W S0 at tokens 32wp + row32(e), value column col
 #pragma unroll
     for (int e4 = 0; e4 < 4; ++e4) {
@@ -144,55 +201,79 @@ __device__ __forceinline__ void scan_step(const ScanArgs& p, const ScanOps<MT, R
       store4(sD + col * DL + 32 * wp + 8 * e4 + 4 * g, d);
     }
   } else {
+    X = mma32_lds_frags<MT, 64>(sS + col * SL + 64 * g, cur.a, X);
+    // X is next used after the barrier; without this the compiler sinks the
+    // products below the load issue and the barrier, onto the critical path.
+    asm volatile("" : "+a"(X));
     __builtin_amdgcn_sched_barrier(0);
     issue();
     __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();  // D complete; every wave is done reading S0
+  // D^T fragments (lane: value column col, tokens 32g..32g+31): the A operand
+  // of the transposed P D product and the B operand of the state update.
+  typedef typename ScanOps<MT, ROLE>::v16 v16;
+  constexpr int FE = ScanOps<MT, ROLE>::FE;
+  v16 dfr[32 / FE];
+#pragma unroll
+  for (int s = 0; s < 32 / FE; ++s) dfr[s] = *reinterpret_cast<const v16*>(sD + col * DL + 32 * g + FE * s);
   if constexpr (ROLE == 1) {
-    // out = scale (Qt S0 + P D): rows 32wp.. of P, 64 tokens contracted
-    X = mma32_frags<MT, 32>(cur.x, sD + col * DL + 32 * g, X);
-    if constexpr (sizeof(MT) == 2) {
-      // The wave's 32x32 output tile goes through LDS (row = token) so the
-      // global stores are 16-byte pieces of 64-byte row segments.  (With
-      // fp32 operands the direct stores below measure faster.)
-      TO* so = reinterpret_cast<TO*>(reinterpret_cast<char*>(sS) + (L::O_O - L::O_S) +
-                                     wp * L::OT_BYTES);
+    // out^T = scale (S0^T Qt^T + D^T P^T): P rows 32wp.. are the columns
+    X = mma32_rr<MT, 32>(dfr, cur.x, X);
+    // Lane (col, g) holds token 32wp + col at values 8 e4 + 4g + (0..3).  One
+    // exchange between the lane halves per pair of e4 gives each lane the
+    // eight consecutive values 16 pr + 8g + (0..7), pr = 0, 1: 16-byte
+    // (bf16) or 32-byte (fp32) stores of whole 32-byte pieces.
+    typedef unsigned u32;
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int NW = (int)sizeof(TO);  // 32-bit words per four output values
+    u32 wd[4][NW];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) so[row32(e, l) * 32 + col] = from_f32<TO>(p.scale * X[e]);
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      constexpr int PE = 16 / (int)sizeof(TO);  // elements per 16-byte piece
-      typedef typename std::conditional<sizeof(TO) == 2, bf16x8, f32x4>::type vo;
+    for (int e4 = 0; e4 < 4; ++e4) {
+      if constexpr (sizeof(TO) == 2) {
 #pragma unroll
-      for (int k = 0; k < 32 * 32 / PE / 64; ++k) {
-        const int piece = k * 64 + l, row = piece / (32 / PE), c8 = (piece % (32 / PE)) * PE;
-        const int tk = 32 * wp + row;
-        // full chunks store without a branch, which keeps the memory-counter
-        // waits of the loop exact; only a sequence's last chunk is masked
-        if (FULL || tk < len)
-          *reinterpret_cast<vo*>(out + ((size_t)(ctok + tk) * p.H + h) * DH + DVB * vb + c8) =
-              *reinterpret_cast<const vo*>(so + row * 32 + c8);
+        for (int j = 0; j < 2; ++j)
+          wd[e4][j] = __builtin_bit_cast(u32, bf16x2{(bf16)(p.scale * X[4 * e4 + 2 * j]),
+                                                     (bf16)(p.scale * X[4 * e4 + 2 * j + 1])});
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wd[e4][j] = __builtin_bit_cast(u32, p.scale * X[4 * e4 + j]);
       }
-    } else {
+    }
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int tk = 32 * wp + row32(e, l);
-        if (FULL || tk < len)
-          out[((size_t)(ctok + tk) * p.H + h) * DH + DVB * vb + col] = from_f32<TO>(p.scale * X[e]);
+    for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+      for (int j = 0; j < NW; ++j) {
+        const auto r = __builtin_amdgcn_permlane32_swap(wd[2 * pr][j], wd[2 * pr + 1][j], false, false);
+        wd[2 * pr][j] = r[0];
+        wd[2 * pr + 1][j] = r[1];
+      }
+    const int tk = 32 * wp + col;
+    // full chunks store without a branch, which keeps the memory-counter
+    // waits of the loop exact; only a sequence's last chunk is masked
+    if (FULL || tk < len) {
+      u32x4* o = reinterpret_cast<u32x4*>(out + ((size_t)(ctok + tk) * p.H + h) * DH + DVB * vb + 8 * g);
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        if constexpr (sizeof(TO) == 2) {
+          o[2 * pr] = u32x4{wd[2 * pr][0], wd[2 * pr][1], wd[2 * pr + 1][0], wd[2 * pr + 1][1]};
+        } else {
+          o[4 * pr] = u32x4{wd[2 * pr][0], wd[2 * pr][1], wd[2 * pr][2], wd[2 * pr][3]};
+          o[4 * pr + 1] = u32x4{wd[2 * pr + 1][0], wd[2 * pr + 1][1], wd[2 * pr + 1][2], wd[2 * pr + 1][3]};
+        }
       }
     }
   }
   // S_next = Diag(Gam) S0 + Kb^T D, rows 32w.. of Kb^T, 64 tokens contracted
 #pragma unroll
   for (int e = 0; e < 16; ++e) S[e] *= cur.gm[e >> 2][e & 3];
-  S = mma32_frags<MT, 32>(cur.kb, sD + col * DL + 32 * g, S);
+  S = mma32_rr<MT, 32>(cur.kb, dfr, S);
   // operand copy of the new state, transposed: sS[value][key]
 #pragma unroll
   for (int e4 = 0; e4 < 4; ++e4)
     store4(sS + col * SL + 32 * w + 8 * e4 + 4 * g,
            f32x4{S[4 * e4], S[4 * e4 + 1], S[4 * e4 + 2], S[4 * e4 + 3]});
-  if constexpr (ROLE == 0) {
+  if constexpr (ROLE == 0 && !EARLY) {
     __builtin_amdgcn_sched_barrier(0);
     issue();
     __builtin_amdgcn_sched_barrier(0);

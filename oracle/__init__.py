@@ -39,6 +39,8 @@ PLANT = {
     "no_scale": 1 << 10,
     "outer_swap": 1 << 11,
     "drop_carry_64": 1 << 12,
+    "init_transposed": 1 << 13,
+    "final_early": 1 << 14,
 }
 
 
@@ -63,11 +65,12 @@ def _load():
     lib.kda_oracle_fwd.restype = ctypes.c_int
     lib.kda_oracle_fwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, ip, ctypes.c_int, ctypes.c_int64,
                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                   ctypes.c_double, ctypes.c_double, ctypes.c_uint, dp]
+                                   ctypes.c_double, ctypes.c_double, ctypes.c_uint, dp, dp, dp]
     lib.kda_oracle_chunked.restype = ctypes.c_int
     lib.kda_oracle_chunked.argtypes = [dp, dp, dp, dp, dp, dp, dp, ip, ctypes.c_int, ctypes.c_int64,
                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                       ctypes.c_double, ctypes.c_double, ctypes.c_int, dp, dp]
+                                       ctypes.c_double, ctypes.c_double, ctypes.c_int, dp, dp, dp,
+                                       dp]
     lib.kda_oracle_prep.restype = None
     lib.kda_oracle_prep.argtypes = [dp, dp, dp, dp, dp, dp, ctypes.c_int64, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_double, dp, dp, dp, dp]
@@ -98,11 +101,22 @@ def _check_shapes(q, k, v, f, b, A_log, dt_bias, cu):
     return T, H, d
 
 
+def _states(initial_state, return_final_state, N, H, d):
+    init = None
+    if initial_state is not None:
+        init = _f64(initial_state)
+        assert init.shape == (N, H, d, d), init.shape
+    fin = np.zeros((N, H, d, d), dtype=np.float64) if return_final_state else None
+    return init, fin
+
+
 def kda_forward(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, scale=None, eps=1e-6,
-                heads=None, plant=0, out=None):
+                heads=None, plant=0, out=None, initial_state=None, return_final_state=False):
     """Token-serial FP64 KDA forward.  Inputs are any real arrays (converted to
     float64 exactly); returns out [T, H, d] float64.  ``heads=(lo, hi)`` limits
-    the computation to a head range (other heads' rows stay zero / as given)."""
+    the computation to a head range (other heads' rows stay zero / as given).
+    ``initial_state`` [N, H, d, d] (key, value) starts each sequence from the
+    given state; with ``return_final_state`` the result is (out, final_state)."""
     lib = _load()
     q, k, v, f_raw, b_raw, A_log, dt_bias = map(_f64, (q, k, v, f_raw, b_raw, A_log, dt_bias))
     cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
@@ -112,18 +126,22 @@ def kda_forward(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, scale=None, e
     lo, hi = (0, H) if heads is None else heads
     if out is None:
         out = np.zeros((T, H, d), dtype=np.float64)
+    init, fin = _states(initial_state, return_final_state, len(cu) - 1, H, d)
     rc = lib.kda_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(f_raw), _ptr(b_raw), _ptr(A_log),
                             _ptr(dt_bias), _ptr(cu, ctypes.c_int32), len(cu) - 1, T, H, d, lo, hi,
-                            float(scale), float(eps), int(plant), _ptr(out))
+                            float(scale), float(eps), int(plant),
+                            _ptr(init) if init is not None else None,
+                            _ptr(fin) if fin is not None else None, _ptr(out))
     if rc != 0:
         raise ValueError("kda_oracle_fwd rejected its arguments")
-    return out
+    return (out, fin) if return_final_state else out
 
 
 def kda_chunked(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, chunk=64, scale=None,
-                eps=1e-6, heads=None, records=False):
+                eps=1e-6, heads=None, records=False, initial_state=None, return_final_state=False):
     """FP64 chunk-form forward.  Returns out, or (out, rec) with rec a dict of
-    per-(chunk, head) intermediates shaped [num_chunks, H, ...]."""
+    per-(chunk, head) intermediates shaped [num_chunks, H, ...]; with
+    ``return_final_state`` the final state [N, H, d, d] is appended."""
     lib = _load()
     q, k, v, f_raw, b_raw, A_log, dt_bias = map(_f64, (q, k, v, f_raw, b_raw, A_log, dt_bias))
     cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
@@ -138,14 +156,17 @@ def kda_chunked(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, chunk=64, sca
         nc = lib.kda_oracle_num_chunks(_ptr(cu, ctypes.c_int32), len(cu) - 1, C)
         RL = lib.kda_oracle_chunk_record_len(C, d)
         rec = np.zeros((nc, H, RL), dtype=np.float64)
+    init, fin = _states(initial_state, return_final_state, len(cu) - 1, H, d)
     rc = lib.kda_oracle_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(f_raw), _ptr(b_raw), _ptr(A_log),
                                 _ptr(dt_bias), _ptr(cu, ctypes.c_int32), len(cu) - 1, T, H, d, lo,
-                                hi, float(scale), float(eps), C, _ptr(out),
+                                hi, float(scale), float(eps), C,
+                                _ptr(init) if init is not None else None,
+                                _ptr(fin) if fin is not None else None, _ptr(out),
                                 _ptr(rec) if rec is not None else None)
     if rc != 0:
         raise ValueError("kda_oracle_chunked rejected its arguments")
     if not records:
-        return out
+        return (out, fin) if return_final_state else out
     parts = {}
     off = 0
     for name, shape in (("G", (C, d)), ("beta", (C,)), ("A", (C, C)), ("P", (C, C)),
@@ -154,7 +175,7 @@ def kda_chunked(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, chunk=64, sca
         n = int(np.prod(shape))
         parts[name] = rec[:, :, off:off + n].reshape(rec.shape[:2] + shape)
         off += n
-    return out, parts
+    return (out, parts, fin) if return_final_state else (out, parts)
 
 
 def kda_prep(q, k, f_raw, b_raw, A_log, dt_bias, eps=1e-6):

@@ -8,7 +8,8 @@
  * shares no code, header, table or helper with the GPU library, and the GPU
  * library never calls it.
  *
- * What is computed (per head h, per packed sequence, zero initial state):
+ * What is computed (per head h, per packed sequence; the state starts at zero,
+ * or at a caller-given initial state):
  *
  *   q^_t = q_t / sqrt(|q_t|^2 + eps),  k^_t = k_t / sqrt(|k_t|^2 + eps)
  *   g_t[c] = -exp(A_log[h]) * softplus(f_t[c] + dt_bias[h][c])
@@ -34,6 +35,15 @@
  *
  * Layouts (row-major, contiguous): q,k,v,f [T][H][d]; b [T][H]; A_log [H];
  * dt_bias [H][d]; cu_seqlens [N+1] with cu[0]=0, cu[N]=T, non-decreasing.
+ *
+ * Initial / final state (optional, NULL = absent): S_init and S_final are
+ * [N][H][d_k][d_v], the state of sequence n, head h before its first token
+ * and after its last (for an empty sequence the final state is the initial
+ * one).  The wrapper on the pages leaves them out (PR #2301, section Change);
+ * PR #2153 (FLA sequence parallelism: contiguous shards that exchange their
+ * recurrent boundary states) is the use that needs them: running a sequence
+ * in two pieces, the second starting from the first one's final state, must
+ * give the same outputs as running it whole.
  *
  * kda_oracle_chunked() is a second, independent FP64 implementation in chunk
  * form (intra-chunk decay-weighted blocks, unit-lower-triangular solve by
@@ -66,7 +76,9 @@ enum {
   PLANT_GATE_SIGN = 1u << 9,         /* decay by exp(-g)                        */
   PLANT_NO_SCALE = 1u << 10,         /* output scale dropped                    */
   PLANT_OUTER_SWAP = 1u << 11,       /* write (v - S^T k) k^T, operands swapped */
-  PLANT_DROP_CARRY_64 = 1u << 12     /* state reset every 64 tokens             */
+  PLANT_DROP_CARRY_64 = 1u << 12,    /* state reset every 64 tokens             */
+  PLANT_INIT_TRANSPOSED = 1u << 13,  /* initial state read as S_init^T          */
+  PLANT_FINAL_EARLY = 1u << 14       /* final state taken before the last token */
 };
 
 static double softplus(double x) {
@@ -116,12 +128,29 @@ void kda_oracle_prep(const double* q, const double* k, const double* f, const do
   }
 }
 
+/* Start state of sequence n, head h: S_init's block, or zero. */
+static void load_init(double* S, const double* S_init, int n, int H, int h, int d,
+                      unsigned plant) {
+  const size_t dd = (size_t)d * d;
+  if (!S_init) { memset(S, 0, sizeof(double) * dd); return; }
+  const double* src = S_init + ((size_t)n * H + h) * dd;
+  if (plant & PLANT_INIT_TRANSPOSED) {
+    for (int i = 0; i < d; ++i)
+      for (int j = 0; j < d; ++j) S[(size_t)i * d + j] = src[(size_t)j * d + i];
+  } else {
+    memcpy(S, src, sizeof(double) * dd);
+  }
+}
+
 /* Token-serial recurrence for heads [h_lo, h_hi).  out is [T][H][d]; rows of
- * heads outside the range are left untouched.  Returns 0, or -1 on bad args. */
+ * heads outside the range are left untouched.  S_init / S_final: see the
+ * header (NULL = zero start / not returned; only the blocks of heads in range
+ * are read or written).  Returns 0, or -1 on bad args. */
 int kda_oracle_fwd(const double* q, const double* k, const double* v, const double* f,
                    const double* b, const double* A_log, const double* dt_bias,
                    const int32_t* cu_seqlens, int N, int64_t T, int H, int d, int h_lo,
-                   int h_hi, double scale, double eps, unsigned plant, double* out) {
+                   int h_hi, double scale, double eps, unsigned plant, const double* S_init,
+                   double* S_final, double* out) {
   if (N < 1 || H < 1 || d < 1 || h_lo < 0 || h_hi > H || h_lo > h_hi) return -1;
   if (cu_seqlens[0] != 0 || cu_seqlens[N] != T) return -1;
   for (int n = 0; n < N; ++n)
@@ -148,10 +177,13 @@ int kda_oracle_fwd(const double* q, const double* k, const double* v, const doub
       } else {
         h = h_lo + (int)(w % nh); n_lo = (int)(w / nh); n_hi = n_lo + 1;
       }
-      memset(S, 0, sizeof(double) * (size_t)d * d);
+      load_init(S, S_init, n_lo, H, h, d, plant);
       for (int n = n_lo; n < n_hi; ++n) {
-        if (!(plant & PLANT_NO_RESET)) memset(S, 0, sizeof(double) * (size_t)d * d);
+        if (!(plant & PLANT_NO_RESET)) load_init(S, S_init, n, H, h, d, plant);
+        double* fin = S_final ? S_final + ((size_t)n * H + h) * (size_t)d * d : NULL;
         for (int64_t t = cu_seqlens[n]; t < cu_seqlens[n + 1]; ++t) {
+          if (fin && (plant & PLANT_FINAL_EARLY) && t == cu_seqlens[n + 1] - 1)
+            memcpy(fin, S, sizeof(double) * (size_t)d * d);
           if ((plant & PLANT_DROP_CARRY_64) && ((t - cu_seqlens[n]) % 64) == 0)
             memset(S, 0, sizeof(double) * (size_t)d * d);
           const int64_t o = (t * H + h) * (int64_t)d;
@@ -209,6 +241,8 @@ int kda_oracle_fwd(const double* q, const double* k, const double* v, const doub
             }
           }
         }
+        if (fin && !((plant & PLANT_FINAL_EARLY) && cu_seqlens[n + 1] > cu_seqlens[n]))
+          memcpy(fin, S, sizeof(double) * (size_t)d * d);
       }
     }
     free(S); free(qn); free(kn); free(g); free(u); free(Sprev);
@@ -250,11 +284,13 @@ int64_t kda_oracle_chunk_record_len(int C, int d) {
  * This is the token recurrence re-associated: unrolling S over the chunk gives
  * D_r = beta_r (v_r - S_r^-T k^_r) with S_r^- the decayed state before token r.
  * If rec != NULL it receives, per chunk (sequence-major order) and head, the
- * record [G, beta, A, P, W, U, Qt, Kb, Gamma, S0] with rows >= n zero. */
+ * record [G, beta, A, P, W, U, Qt, Kb, Gamma, S0] with rows >= n zero.
+ * S_init / S_final as for kda_oracle_fwd. */
 int kda_oracle_chunked(const double* q, const double* k, const double* v, const double* f,
                        const double* b, const double* A_log, const double* dt_bias,
                        const int32_t* cu_seqlens, int N, int64_t T, int H, int d, int h_lo,
-                       int h_hi, double scale, double eps, int C, double* out, double* rec) {
+                       int h_hi, double scale, double eps, int C, const double* S_init,
+                       double* S_final, double* out, double* rec) {
   if (N < 1 || H < 1 || d < 1 || C < 1 || h_lo < 0 || h_hi > H || h_lo > h_hi) return -1;
   if (cu_seqlens[0] != 0 || cu_seqlens[N] != T) return -1;
   for (int n = 0; n < N; ++n)
@@ -289,7 +325,7 @@ int kda_oracle_chunked(const double* q, const double* k, const double* v, const 
     for (int64_t w = 0; w < (int64_t)N * nh; ++w) {
       const int h = h_lo + (int)(w % nh), n = (int)(w / nh);
       const int64_t t0 = cu_seqlens[n], L = cu_seqlens[n + 1] - t0;
-      memset(S, 0, sizeof(double) * dd);
+      load_init(S, S_init, n, H, h, d, 0u);
       for (int64_t j = 0; j * C < L; ++j) {
         const int64_t c0 = t0 + j * C;
         const int nr = (int)((L - j * C) < C ? (L - j * C) : C);
@@ -382,6 +418,7 @@ int kda_oracle_chunked(const double* q, const double* k, const double* v, const 
           }
         memcpy(S, Sn, sizeof(double) * dd);
       }
+      if (S_final) memcpy(S_final + ((size_t)n * H + h) * dd, S, sizeof(double) * dd);
     }
     free(S); free(Qn); free(Kn); free(G); free(g); free(bet); free(A); free(P);
     free(W); free(U); free(Qt); free(Kb); free(Dl); free(Gam); free(Sn);

@@ -245,9 +245,66 @@ def pin_chunked_agreement(fwd, chunks=(1, 4, 16, 64), gate_scales=(1.0, 1e-3, 4.
     return bool(ok)
 
 
+def pin_state_split(fwd):
+    """Running each sequence in two pieces, the second starting from the first
+    piece's final state, gives the whole run's outputs and final state; the
+    whole run itself starts from a given (random) initial state.  Packed: three
+    sequences with their own initial states, one of them empty (final state =
+    initial state)."""
+    cu = [0, 150, 150, 197]
+    T, H, d = 197, 2, 8
+    x = _rand_inputs(T, H, d, seed=71, cu=cu)
+    r = _rng(72)
+    S0 = 0.3 * r.standard_normal((3, H, d, d))
+    out, fin = fwd(**x, initial_state=S0, return_final_state=True)
+    ok = np.array_equal(fin[1], S0[1])
+    cut = {0: 70, 2: 150 + 31}  # split points inside sequences 0 and 2
+    for n, tc in cut.items():
+        a, b = cu[n], cu[n + 1]
+
+        def piece(lo, hi):
+            return {kk: (vv[lo:hi] if kk not in ("A_log", "dt_bias", "cu_seqlens") else vv)
+                    for kk, vv in x.items() if kk != "cu_seqlens"}
+        one = np.array([0, tc - a], dtype=np.int32)
+        two = np.array([0, b - tc], dtype=np.int32)
+        o1, f1 = fwd(**piece(a, tc), cu_seqlens=one, initial_state=S0[n:n + 1],
+                     return_final_state=True)
+        o2, f2 = fwd(**piece(tc, b), cu_seqlens=two, initial_state=f1, return_final_state=True)
+        ok &= _rel(np.concatenate([o1, o2]), out[a:b]) < 1e-12
+        ok &= _rel(f2[0], fin[n]) < 1e-12
+    return bool(ok)
+
+
+def pin_state_closed_form(fwd):
+    """No writes (beta = 0): the initial state only decays, with the closed-form
+    gate of pin_pure_decay (g = -lam ln 2 or -lam ln 4 per key channel), so
+    o_t = scale * (Diag(exp(t' g)) S_init)^T q^_t with t' = t + 1 tokens decayed,
+    and the final state is Diag(exp(T g)) S_init."""
+    T, d = 6, 6
+    r = _rng(75)
+    q = r.standard_normal((T, 1, d))
+    S0 = r.standard_normal((1, 1, d, d))
+    lam = 0.75
+    dtb = np.where(np.arange(d) % 2 == 0, 0.25, 0.25 + math.log(3)).reshape(1, d)
+    out, fin = fwd(q=q, k=r.standard_normal((T, 1, d)), v=r.standard_normal((T, 1, d)),
+                   f_raw=np.full((T, 1, d), -0.25), b_raw=np.full((T, 1), -np.inf),
+                   A_log=np.array([math.log(lam)]), dt_bias=dtb,
+                   cu_seqlens=np.array([0, T], dtype=np.int32), eps=0.0, initial_state=S0,
+                   return_final_state=True)
+    g = -lam * np.where(np.arange(d) % 2 == 0, math.log(2), math.log(4))
+    ok = True
+    for t in range(T):
+        St = np.exp(g * (t + 1))[:, None] * S0[0, 0]  # row i (key) scaled
+        qt = q[t, 0] / np.linalg.norm(q[t, 0])
+        ok &= np.allclose(out[t, 0], (St.T @ qt) / math.sqrt(d), rtol=1e-13, atol=1e-15)
+    ok &= np.allclose(fin[0, 0], np.exp(g * T)[:, None] * S0[0, 0], rtol=1e-13, atol=1e-15)
+    return bool(ok)
+
+
 FORWARD_PINS = [pin_golden_d1, pin_golden_d2, pin_single_token, pin_pure_decay, pin_long_memory,
                 pin_retrieval_orthonormal, pin_delta_on_decayed_state, pin_sequence_reset,
-                pin_causality, pin_linearity_in_v, pin_head_permutation, pin_chunked_agreement]
+                pin_causality, pin_linearity_in_v, pin_head_permutation, pin_chunked_agreement,
+                pin_state_split, pin_state_closed_form]
 
 
 @pytest.mark.parametrize("pin", FORWARD_PINS, ids=lambda p: p.__name__)
@@ -266,6 +323,18 @@ def test_planted_mistake_is_caught(plant):
 # --------------------------------------------------------------------------
 # Stage-one (prep) closed forms
 # --------------------------------------------------------------------------
+
+def test_chunked_form_carries_initial_and_final_state():
+    """The chunk-form oracle takes and returns the state like the recurrence
+    (chunk sizes that split the sequences at different places)."""
+    cu = [0, 100, 100, 163]
+    x = _rand_inputs(163, 2, 16, seed=81, cu=cu)
+    S0 = 0.5 * _rng(82).standard_normal((3, 2, 16, 16))
+    ref, fref = oracle.kda_forward(**x, initial_state=S0, return_final_state=True)
+    for C in (1, 16, 64):
+        out, fin = oracle.kda_chunked(**x, chunk=C, initial_state=S0, return_final_state=True)
+        assert _rel(out, ref) < 1e-12 and _rel(fin, fref) < 1e-12, C
+
 
 def test_prep_l2norm_closed_form():
     r = _rng(1)

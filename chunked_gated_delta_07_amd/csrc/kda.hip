@@ -66,11 +66,18 @@ static inline WsLayout ws_layout(int64_t T, int32_t N, int32_t H, uint32_t mode)
   return L;
 }
 
+// End states of an empty batch (every sequence empty): fin = init, or zero.
+__global__ __launch_bounds__(256) void kda_state_copy_kernel(const float* __restrict__ init,
+                                                             float* __restrict__ fin, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    fin[i] = init ? init[i] : 0.0f;
+}
+
 template <typename TA, typename MT, typename TO>
 static int launch_all(const void* q, const void* k, const void* v, const void* f, const void* b,
                       const float* A_log, const float* dt_bias, const int32_t* cu, int32_t N,
                       int64_t T, int32_t H, uint32_t mode, void* out, void* ws,
-                      hipStream_t stream, hipEvent_t const* ev) {
+                      const float* init, float* fin, hipStream_t stream, hipEvent_t const* ev) {
   const WsLayout W = ws_layout(T, N, H, mode);
   char* base = reinterpret_cast<char*>(ws);
   int32_t* cfirst = reinterpret_cast<int32_t*>(base + W.off_cfirst);
@@ -93,7 +100,7 @@ static int launch_all(const void* q, const void* k, const void* v, const void* f
   ScanArgs sa;
   sa.cu = cu; sa.cfirst = cfirst; sa.N = N; sa.H = H;
   sa.scale = 0.08838834764831845f;  // 1/sqrt(128)
-  sa.gam = gam; sa.rec = rec; sa.out = out;
+  sa.gam = gam; sa.rec = rec; sa.out = out; sa.init = init; sa.fin = fin;
   const int64_t pairs = (int64_t)N * H;
   const int64_t blocks = 32 * ((pairs + 7) / 8);
   hipLaunchKernelGGL((kda_scan_kernel<MT, TO>), dim3((unsigned)blocks), dim3(256), 0, stream, sa);
@@ -103,13 +110,14 @@ static int launch_all(const void* q, const void* k, const void* v, const void* f
 
 static int dispatch(const void* q, const void* k, const void* v, const void* f, const void* b,
                     const float* A_log, const float* dt_bias, const int32_t* cu, int32_t N,
-                    int64_t T, int32_t H, uint32_t mode, void* out, void* ws, hipStream_t s,
-                    hipEvent_t const* ev) {
+                    int64_t T, int32_t H, uint32_t mode, void* out, void* ws, const float* init,
+                    float* fin, hipStream_t s, hipEvent_t const* ev) {
   const bool f32i = mode & KDA_MODE_FP32_INTERMEDIATE;
   const bool a32 = mode & KDA_ACT_FP32;
   const bool o32 = (mode & KDA_OUT_FP32) || a32;
 #define KDA_GO(TA, MT, TO) \
-  return launch_all<TA, MT, TO>(q, k, v, f, b, A_log, dt_bias, cu, N, T, H, mode, out, ws, s, ev)
+  return launch_all<TA, MT, TO>(q, k, v, f, b, A_log, dt_bias, cu, N, T, H, mode, out, ws, init, \
+                                fin, s, ev)
   if (!a32 && !f32i && !o32) KDA_GO(bf16, bf16, bf16);
   if (!a32 && !f32i && o32) KDA_GO(bf16, bf16, float);
   if (!a32 && f32i && !o32) KDA_GO(bf16, float, bf16);
@@ -154,15 +162,25 @@ extern "C" int kda_chunk_fwd_num_stages(uint32_t mode) {
 static int fwd_impl(const void* q, const void* k, const void* v, const void* f_raw, const void* b_raw,
                     const float* A_log, const float* dt_bias, const int32_t* cu, int32_t N, int64_t T,
                     int32_t H, int32_t d, uint32_t mode, void* out, void* ws, size_t ws_bytes,
-                    void* stream, void* const* events, int32_t num_events) {
+                    const float* init, float* fin, void* stream, void* const* events,
+                    int32_t num_events) {
   int st = check_args(q, k, v, f_raw, b_raw, A_log, dt_bias, cu, N, T, H, d, mode, out, ws, ws_bytes);
-  if (st != KDA_OK || T == 0) return st;
+  if (st != KDA_OK) return st;
+  if (T == 0) {
+    if (!fin) return KDA_OK;
+    (void)hipGetLastError();
+    const int64_t n = (int64_t)N * H * kda::DH * kda::DH;
+    const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+    hipLaunchKernelGGL(kda::kda_state_copy_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), init, fin, n);
+    return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  }
   if (events && num_events != kda_chunk_fwd_num_stages(mode) + 1) return KDA_ERR_INVALID_ARG;
   if (events)
     for (int i = 0; i < num_events; ++i)
       if (!events[i]) return KDA_ERR_INVALID_ARG;
   (void)hipGetLastError();  // clear a stale error so the status reflects these launches
-  return kda::dispatch(q, k, v, f_raw, b_raw, A_log, dt_bias, cu, N, T, H, mode, out, ws,
+  return kda::dispatch(q, k, v, f_raw, b_raw, A_log, dt_bias, cu, N, T, H, mode, out, ws, init, fin,
                        reinterpret_cast<hipStream_t>(stream),
                        reinterpret_cast<hipEvent_t const*>(events));
 }
@@ -173,7 +191,18 @@ extern "C" int kda_chunk_fwd(const void* q, const void* k, const void* v, const 
                              int32_t H, int32_t d, uint32_t mode, void* out, void* workspace,
                              size_t workspace_bytes, void* stream) {
   return fwd_impl(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, num_seqs, total_tokens, H, d,
-                  mode, out, workspace, workspace_bytes, stream, nullptr, 0);
+                  mode, out, workspace, workspace_bytes, nullptr, nullptr, stream, nullptr, 0);
+}
+
+extern "C" int kda_chunk_fwd_state(const void* q, const void* k, const void* v, const void* f_raw,
+                                   const void* b_raw, const float* A_log, const float* dt_bias,
+                                   const int32_t* cu_seqlens, int32_t num_seqs,
+                                   int64_t total_tokens, int32_t H, int32_t d, uint32_t mode,
+                                   void* out, void* workspace, size_t workspace_bytes,
+                                   const float* initial_state, float* final_state, void* stream) {
+  return fwd_impl(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, num_seqs, total_tokens, H, d,
+                  mode, out, workspace, workspace_bytes, initial_state, final_state, stream,
+                  nullptr, 0);
 }
 
 extern "C" int kda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void* f_raw,
@@ -184,7 +213,8 @@ extern "C" int kda_chunk_fwd_timed(const void* q, const void* k, const void* v, 
                                    void* const* events, int32_t num_events) {
   if (!events) return KDA_ERR_INVALID_ARG;
   return fwd_impl(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, num_seqs, total_tokens, H, d,
-                  mode, out, workspace, workspace_bytes, stream, events, num_events);
+                  mode, out, workspace, workspace_bytes, nullptr, nullptr, stream, events,
+                  num_events);
 }
 
 extern "C" const char* kda_status_string(int status) {

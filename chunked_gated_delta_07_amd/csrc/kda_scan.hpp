@@ -32,6 +32,8 @@ struct ScanArgs {
   const float* gam;  // [chunks][H][128]
   const void* rec;   // [chunks][H][REC]
   void* out;         // [T][H][128]
+  const float* init; // [N][H][128 key][128 value] start states, or null (zero)
+  float* fin;        // [N][H][128][128] end states, or null (not written)
 };
 
 constexpr int DVB = 32;  // value channels per workgroup
@@ -283,9 +285,12 @@ __device__ __forceinline__ void scan_step(const ScanArgs& p, const ScanOps<MT, R
 
 // The chunk loop of one wave: operands are loaded ahead into rotating register
 // sets (bf16: two chunks ahead, three sets; fp32: one chunk ahead, two sets).
+// S (in/out): the wave's 32 state rows 32w.. (key) at value columns vb*32..
+// of this sequence, FP32; the LDS operand copy of its start value is in sS.
 template <typename MT, typename TO, int ROLE>
 __device__ __forceinline__ void scan_chunks(const ScanArgs& p, MT* sS, MT* sD, int h, int cbeg,
-                                            int cend, int tseq, int tend, int vb, int w, int l) {
+                                            int cend, int tseq, int tend, int vb, int w, int l,
+                                            f32x16& S) {
   const int g = l >> 5, wp = w & 1;
   const int H = p.H;
   const MT* __restrict__ rec = reinterpret_cast<const MT*>(p.rec);
@@ -301,10 +306,6 @@ __device__ __forceinline__ void scan_chunks(const ScanArgs& p, MT* sS, MT* sD, i
     scan_step<MT, TO, ROLE, false>(p, o, S, sS, sD, h, ctok, tend - ctok, vb, w, l, issue);
   };
   auto none = [] {};
-  // running state rows 32w.. (key), columns vb*32.. (value), FP32
-  f32x16 S;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) S[e] = 0.0f;
   // Full chunks run in the main loop; a partial last chunk runs after it.
   // Prefetch loads are unconditional (indices clamped to the last chunk), so
   // every iteration issues the same memory operations and the compiler's
@@ -314,7 +315,7 @@ __device__ __forceinline__ void scan_chunks(const ScanArgs& p, MT* sS, MT* sD, i
   ScanOps<MT, ROLE> o0, o1, o2;
   load(o0, cbeg);
   if constexpr (sizeof(MT) == 2) load(o1, min(cbeg + 1, clast));
-  __syncthreads();  // zeroed S0 operand visible
+  __syncthreads();  // start-state operand visible
   int c = cbeg;
   if constexpr (sizeof(MT) == 2) {
     // o0 holds chunk c, o1 chunk c+1; step c sends the loads of chunk c+2
@@ -362,12 +363,33 @@ __global__ __launch_bounds__(256) void kda_scan_kernel(ScanArgs p) {
   if (pair >= p.N * p.H) return;
   const int n = pair / p.H, h = pair - n * p.H;
   const int cbeg = p.cfirst[n], cend = p.cfirst[n + 1];
-  if (cbeg == cend) return;
   const int tseq = p.cu[n], tend = p.cu[n + 1];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  for (int x = tid; x < DVB * SL; x += 256) sS[x] = from_f32<MT>(0.0f);
-  if (w < 2) scan_chunks<MT, TO, 0>(p, sS, sD, h, cbeg, cend, tseq, tend, vb, w, l);
-  else scan_chunks<MT, TO, 1>(p, sS, sD, h, cbeg, cend, tseq, tend, vb, w, l);
+  const int col = l & 31, g = l >> 5;
+  // Lane (col, g) of wave w holds state entries (key 32w + row32(e), value
+  // 32vb + col); for each e the 32 lanes of a group touch 128 contiguous bytes.
+  const size_t sbase = (size_t)pair * DH * DH + (size_t)(32 * w) * DH + DVB * vb + col;
+  f32x16 S;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) S[e] = p.init ? p.init[sbase + (size_t)row32(e, l) * DH] : 0.0f;
+  if (cbeg == cend) {  // empty sequence: the end state is the start state
+    if (p.fin) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) p.fin[sbase + (size_t)row32(e, l) * DH] = S[e];
+    }
+    return;
+  }
+  // operand copy of the start state, transposed: sS[value][key]
+#pragma unroll
+  for (int e4 = 0; e4 < 4; ++e4)
+    store4(sS + col * SL + 32 * w + 8 * e4 + 4 * g,
+           f32x4{S[4 * e4], S[4 * e4 + 1], S[4 * e4 + 2], S[4 * e4 + 3]});
+  if (w < 2) scan_chunks<MT, TO, 0>(p, sS, sD, h, cbeg, cend, tseq, tend, vb, w, l, S);
+  else scan_chunks<MT, TO, 1>(p, sS, sD, h, cbeg, cend, tseq, tend, vb, w, l, S);
+  if (p.fin) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) p.fin[sbase + (size_t)row32(e, l) * DH] = S[e];
+  }
 }
 
 }  // namespace kda

@@ -23,8 +23,8 @@ KDA_ACT_FP32 = 0x2
 KDA_OUT_FP32 = 0x4
 
 # Exported symbols, in declaration order of include/kda.h.
-SYMBOLS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_num_stages",
-           "kda_chunk_fwd_timed", "kda_status_string")
+SYMBOLS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_state",
+           "kda_chunk_fwd_num_stages", "kda_chunk_fwd_timed", "kda_status_string")
 
 _lib = None
 
@@ -51,6 +51,8 @@ def load_library(path: str = LIB_PATH):
                 ctypes.c_int32, ctypes.c_uint32, vp, vp, ctypes.c_size_t, vp]
     lib.kda_chunk_fwd.restype = ctypes.c_int
     lib.kda_chunk_fwd.argtypes = fwd_args
+    lib.kda_chunk_fwd_state.restype = ctypes.c_int
+    lib.kda_chunk_fwd_state.argtypes = fwd_args[:-1] + [vp, vp, vp]
     lib.kda_chunk_fwd_timed.restype = ctypes.c_int
     lib.kda_chunk_fwd_timed.argtypes = fwd_args + [ctypes.POINTER(vp), ctypes.c_int32]
     lib.kda_chunk_fwd_num_stages.restype = ctypes.c_int
@@ -87,7 +89,8 @@ def _ptr(t):
 
 
 def chunk_fwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, fp32_intermediate=False,
-              out_fp32=False, out=None, workspace=None, stream=None, events=None):
+              out_fp32=False, out=None, workspace=None, stream=None, events=None,
+              initial_state=None, final_state=None, return_final_state=False):
     """KDA chunked forward through libkda.
 
     q, k, v, f_raw: [T, H, 128] bfloat16 or float32 (one dtype for all);
@@ -95,7 +98,11 @@ def chunk_fwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, fp32_intermedia
     cu_seqlens: [N+1] int32.  All CUDA (HIP) tensors, contiguous.  Returns
     out [T, H, 128] (activation dtype, or float32 when out_fp32).
     ``events``: optional list of num_stages(mode)+1 torch.cuda.Event objects
-    recorded between the kernels (kda_chunk_fwd_timed)."""
+    recorded between the kernels (kda_chunk_fwd_timed).
+    ``initial_state``: optional [N, H, 128, 128] float32 start states (key,
+    value); ``final_state`` (a tensor of that shape to fill, may be the
+    initial_state tensor) or ``return_final_state=True`` (allocated) selects
+    kda_chunk_fwd_state and makes the result (out, final_state)."""
     import torch
 
     lib = load_library()
@@ -133,6 +140,21 @@ def chunk_fwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, fp32_intermedia
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(f_raw), _ptr(b_raw), _ptr(A_log), _ptr(dt_bias),
             _ptr(cu_seqlens), num_seqs, T, H, d, mode, _ptr(out), _ptr(workspace),
             workspace.numel(), sp)
+    use_state = initial_state is not None or final_state is not None or return_final_state
+    if use_state:
+        if events is not None:
+            raise ValueError("events are not supported together with states")
+        sshape = (num_seqs, H, d, d)
+        for t in (initial_state, final_state):
+            if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != sshape
+                                  or not t.is_contiguous() or not t.is_cuda):
+                raise ValueError("states must be contiguous float32 [N, H, d, d] device tensors")
+        if final_state is None and return_final_state:
+            final_state = torch.empty(sshape, dtype=torch.float32, device=q.device)
+        st = lib.kda_chunk_fwd_state(*args[:-1], _ptr(initial_state), _ptr(final_state), sp)
+        if st != KDA_OK:
+            raise KdaError(st, "kda_chunk_fwd_state")
+        return (out, final_state) if final_state is not None else out
     if events is None:
         st = lib.kda_chunk_fwd(*args)
         where = "kda_chunk_fwd"

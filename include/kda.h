@@ -2,7 +2,8 @@
  * kda.h -- C ABI of libkda, the MI355X (gfx950) Kimi Delta Attention (KDA)
  * chunked forward.
  *
- * Operation (per head h and per packed sequence, zero initial state):
+ * Operation (per head h and per packed sequence; zero initial state except
+ * in kda_chunk_fwd_state):
  *   q^_t   = q_t / sqrt(|q_t|^2 + 1e-6),   k^_t likewise       (FP32 math)
  *   g_t[c] = -exp(A_log[h]) * softplus(f_raw_t[c] + dt_bias[h][c])
  *   beta_t = sigmoid(b_raw_t)
@@ -104,6 +105,30 @@ KDA_API int kda_chunk_fwd(const void* q, const void* k, const void* v, const voi
                   const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens, int32_t H,
                   int32_t d, uint32_t mode, void* out, void* workspace, size_t workspace_bytes,
                   void* stream);
+
+/* kda_chunk_fwd with a start state and an end state per sequence and head.
+ * The pages' wrapper has neither (xtuner PR #2301, section Change: "does not
+ * add initial/final state"); the sequence-parallel design of xtuner PR #2153
+ * (contiguous shards exchanging recurrent boundary states) is what needs
+ * them: a sequence run in two calls, the second starting from the first
+ * call's final state, gives the outputs of one call over the whole sequence.
+ *  initial_state : device, [num_seqs][H][d][d] float32, or NULL (zero start).
+ *                  Entry [n][h][i][j] is S[key i][value j] of sequence n,
+ *                  head h before its first token (out_t = S_t^T q^_t).
+ *  final_state   : device, [num_seqs][H][d][d] float32, or NULL (not written).
+ *                  Receives S after each sequence's last token; for an empty
+ *                  sequence it is the initial state (zero if NULL).  It may be
+ *                  the same array as initial_state (updated in place), and
+ *                  must not overlap any other argument.
+ * Everything else as for kda_chunk_fwd; with total_tokens == 0 and a
+ * final_state, final_state is still written (one small launch).  The running
+ * state is FP32 in both precision modes. */
+KDA_API int kda_chunk_fwd_state(const void* q, const void* k, const void* v, const void* f_raw,
+                        const void* b_raw, const float* A_log, const float* dt_bias,
+                        const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                        int32_t H, int32_t d, uint32_t mode, void* out, void* workspace,
+                        size_t workspace_bytes, const float* initial_state, float* final_state,
+                        void* stream);
 
 /* Number of kernels kda_chunk_fwd launches for this mode (the stages timed by
  * kda_chunk_fwd_timed). */

@@ -70,6 +70,15 @@ def test_argument_errors_before_launch():
     assert lib.kda_chunk_fwd_timed(p, p, p, p, p, p, p, p, 1, 10, 4, 128, 0, p, p, 1 << 40, None,
                                    ev, 2) == kda.KDA_ERR_INVALID_ARG
     assert n >= 1
+    # the state variant applies the same checks (states may be NULL)
+    st = lambda **kw: lib.kda_chunk_fwd_state(
+        *([kw.get("p", p)] * 8), kw.get("N", 1), kw.get("T", 10), 4, kw.get("d", 128), 0,
+        kw.get("p", p), kw.get("p", p), kw.get("ws", 1 << 40), None, None, None)
+    assert st(p=None) == kda.KDA_ERR_INVALID_ARG
+    assert st(N=0) == kda.KDA_ERR_INVALID_ARG
+    assert st(d=96) == kda.KDA_ERR_UNSUPPORTED
+    assert st(ws=1) == kda.KDA_ERR_WORKSPACE
+    assert st(T=0, p=None) == kda.KDA_OK  # no final state requested: nothing launched
 
 
 def test_workspace_query():

@@ -157,3 +157,40 @@ def test_split_handoff_16384_tokens(fp32):
           f"final={r_fin:.3e}; vs oracle out={r_or:.3e} final={r_orf:.3e}", flush=True)
     assert r_out <= _tol(fp32) and r_fin <= _tol(fp32)
     assert r_or <= _tol(fp32) and r_orf <= _tol(fp32)
+
+
+@pytest.mark.parametrize("fp32", [False, True], ids=["bf16", "fp32"])
+def test_segmented_scan_with_transition_matrices(fp32):
+    """The sequence-parallel scheme on one GPU: a 16384-token sequence cut into
+    four pieces (not at chunk multiples) that are processed side by side as one
+    packed batch.  Per piece r, S_end = M_r S_start + L_r with
+    M_r = prod over its chunks of (Diag(Gamma) - Kb^T W): L_r is the final state
+    from a zero start, M_r the final state with v = 0 from the identity (the
+    recurrence is affine in the state).  An exclusive prefix
+    S_in[r+1] = M_r S_in[r] + L_r (host, FP64) gives each piece its true start
+    state; a third packed call then reproduces one call over the whole
+    sequence."""
+    import torch
+
+    inp = synth.make_inputs([0, 16384], H=8, d=128, act="bf16", seed=91)
+    full = U.to_device(inp, "cuda:0")
+    out_whole, fin_whole = _run(full, fp32)
+    cuts = [0, 4000, 8192, 12001, 16384]
+    R = len(cuts) - 1
+    packed = list(full[:7]) + [torch.tensor(cuts, dtype=torch.int32, device="cuda:0")]
+    _, L = _run(packed, fp32)                                   # local end states
+    zero_v = list(packed)
+    zero_v[2] = torch.zeros_like(packed[2])
+    eye = torch.eye(128, device="cuda:0").expand(R, inp.H, 128, 128).contiguous()
+    _, M = _run(zero_v, fp32, init=eye)                         # transition matrices
+    Ld, Md = L.double().cpu(), M.double().cpu()
+    S_in = torch.zeros((R, inp.H, 128, 128), dtype=torch.float64)
+    for r in range(R - 1):
+        S_in[r + 1] = Md[r] @ S_in[r] + Ld[r]
+    out_seg, fin_seg = _run(packed, fp32, init=S_in.float().cuda())
+    r_out = U.rel_l2(out_seg.double().cpu().numpy(), out_whole.double().cpu().numpy())
+    r_fin = U.rel_l2(fin_seg[-1].double().cpu().numpy(), fin_whole[0].double().cpu().numpy())
+    r_end = U.rel_l2((Md[-1] @ S_in[-1] + Ld[-1]).numpy(), fin_whole[0].double().cpu().numpy())
+    print(f"[segmented] mode={'fp32' if fp32 else 'bf16'} out={r_out:.3e} final={r_fin:.3e} "
+          f"affine end={r_end:.3e}", flush=True)
+    assert r_out <= _tol(fp32) and r_fin <= _tol(fp32) and r_end <= _tol(fp32)

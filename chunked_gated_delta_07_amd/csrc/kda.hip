@@ -103,7 +103,10 @@ static int launch_all(const void* q, const void* k, const void* v, const void* f
   sa.gam = gam; sa.rec = rec; sa.out = out; sa.init = init; sa.fin = fin;
   const int64_t pairs = (int64_t)N * H;
   const int64_t blocks = 32 * ((pairs + 7) / 8);
-  hipLaunchKernelGGL((kda_scan_kernel<MT, TO>), dim3((unsigned)blocks), dim3(256), 0, stream, sa);
+  if constexpr (sizeof(MT) == 2)
+    hipLaunchKernelGGL((kda_scan_ring_kernel<TO>), dim3((unsigned)blocks), dim3(512), 0, stream, sa);
+  else
+    hipLaunchKernelGGL((kda_scan_kernel<MT, TO>), dim3((unsigned)blocks), dim3(256), 0, stream, sa);
   if (ev) (void)hipEventRecord(ev[3], stream);
   return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

@@ -150,6 +150,15 @@ template <typename MT> struct IntraLds {
   static constexpr int BYTES = O_U + U_BYTES;
 };
 
+// A pointer that is the same in every lane of the wave, moved to scalar
+// registers so that addressing from it is scalar arithmetic.
+template <typename T> __device__ __forceinline__ const T* wave_uniform(const T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
+}
+
 // Index of cross-block combination (R, I), R > I, in 0..5.
 __device__ __forceinline__ constexpr int combo(int R, int I) { return (R * (R - 1)) / 2 + I; }
 
@@ -194,23 +203,50 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
   const float lam = expf(p.A_log[h]);  // exp(-inf) = 0 gives g = 0 exactly
   const f32x2 dtb = *reinterpret_cast<const f32x2*>(p.dt_bias + (size_t)h * DH + c0);
   float qa[16][2], ka[16][2], aa[16][2];
+  // Full chunks (all but a sequence's last) load their rows from one
+  // wave-uniform base with scalar row offsets and need no masks.
+  const bool full = len == CHUNK;  // uniform over the block
+  const size_t rstride = (size_t)H * DH;  // elements from one token to the next
   {
     f32x2 xq[16], xk[16], xf[16];
+    if (full) {
+      const size_t wb = ((size_t)(t0 + 16 * w) * H + h) * DH;
+      const TA* bq = wave_uniform(gq + wb);
+      const TA* bk = wave_uniform(gk + wb);
+      const TA* bf = wave_uniform(gf + wb);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int r = 16 * w + j;
-      const size_t o = ((size_t)(t0 + (r < len ? r : 0)) * H + h) * DH + c0;
-      xq[j] = load2(gq + o); xk[j] = load2(gk + o); xf[j] = load2(gf + o);
+      for (int j = 0; j < 16; ++j) {
+        xq[j] = load2(bq + j * rstride + c0);
+        xk[j] = load2(bk + j * rstride + c0);
+        xf[j] = load2(bf + j * rstride + c0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = 16 * w + j;
+        const size_t o = ((size_t)(t0 + (r < len ? r : 0)) * H + h) * DH + c0;
+        xq[j] = load2(gq + o); xk[j] = load2(gk + o); xf[j] = load2(gf + o);
+      }
     }
     float bl = 0.0f;
     if (l < 16) bl = to_f32(gb[(size_t)(t0 + (16 * w + l < len ? 16 * w + l : 0)) * H + h]);
+    if (full) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const bool ok = 16 * w + j < len;
-      qa[j][0] = ok ? xq[j][0] : 0.0f; qa[j][1] = ok ? xq[j][1] : 0.0f;
-      ka[j][0] = ok ? xk[j][0] : 0.0f; ka[j][1] = ok ? xk[j][1] : 0.0f;
-      aa[j][0] = ok ? decay_from_gate(xf[j][0] + dtb[0], lam) : 1.0f;
-      aa[j][1] = ok ? decay_from_gate(xf[j][1] + dtb[1], lam) : 1.0f;
+      for (int j = 0; j < 16; ++j) {
+        qa[j][0] = xq[j][0]; qa[j][1] = xq[j][1];
+        ka[j][0] = xk[j][0]; ka[j][1] = xk[j][1];
+        aa[j][0] = decay_from_gate(xf[j][0] + dtb[0], lam);
+        aa[j][1] = decay_from_gate(xf[j][1] + dtb[1], lam);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const bool ok = 16 * w + j < len;
+        qa[j][0] = ok ? xq[j][0] : 0.0f; qa[j][1] = ok ? xq[j][1] : 0.0f;
+        ka[j][0] = ok ? xk[j][0] : 0.0f; ka[j][1] = ok ? xk[j][1] : 0.0f;
+        aa[j][0] = ok ? decay_from_gate(xf[j][0] + dtb[0], lam) : 1.0f;
+        aa[j][1] = ok ? decay_from_gate(xf[j][1] + dtb[1], lam) : 1.0f;
+      }
     }
     if (l < 16) sBeta[16 * w + l] = (16 * w + l < len) ? sigmoid_f(bl) : 0.0f;
   }
@@ -472,12 +508,22 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
   float* sT = reinterpret_cast<float*>(sU + L::O_T);
   // values for the U product, loaded early so their latency hides under the solve
   float v0[16], v1[16];
+  if (full) {
+    const TA* bv = wave_uniform(gv + ((size_t)(t0 + 16 * w) * H + h) * DH);
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int r = 16 * w + j;
-    const f32x2 xv = load2(gv + ((size_t)(t0 + (r < len ? r : 0)) * H + h) * DH + c0);
-    v0[j] = r < len ? xv[0] : 0.0f;
-    v1[j] = r < len ? xv[1] : 0.0f;
+    for (int j = 0; j < 16; ++j) {
+      const f32x2 xv = load2(bv + j * rstride + c0);
+      v0[j] = xv[0];
+      v1[j] = xv[1];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = 16 * w + j;
+      const f32x2 xv = load2(gv + ((size_t)(t0 + (r < len ? r : 0)) * H + h) * DH + c0);
+      v0[j] = r < len ? xv[0] : 0.0f;
+      v1[j] = r < len ? xv[1] : 0.0f;
+    }
   }
   {
     // (a) 4x4 diagonal blocks.  Lane: sub-block sb, row r4, column c4.

@@ -392,4 +392,255 @@ __global__ __launch_bounds__(256) void kda_scan_kernel(ScanArgs p) {
   }
 }
 
+// ===========================================================================
+// State pass with loader waves (bf16 intermediates).
+//
+// The state pass is bound by how fast one CU can bring in each chunk's
+// operands (about 60 KB per workgroup) while the compute waves also have to
+// issue those loads in order with their matrix work.  Here four extra waves do
+// nothing but copy each chunk's operands straight from global memory into a
+// two-slot LDS ring with 16-byte direct-to-LDS loads; the four compute waves
+// read their fragments from LDS.  The records are already in fragment order,
+// so every copy is 1 KB contiguous on both sides.
+//
+// Slot layout (bytes): W [0,16K) | Qt [16K,32K) | Kb^T [32K,48K) | U of this
+// value block [48K,52K) | P [52K,60K) | Gam [60K, 60K+512).  "Early" operands
+// (W, Qt, U) are read before the first barrier of a step, "late" ones (Kb^T,
+// P, Gam) after it.  In step c the loaders copy chunk c+1's early operands at
+// the start and its late operands after the first barrier, each into the slot
+// that chunk c-1 used; a loader waits for its own copies (memory counter)
+// right before the barrier that publishes them.  The barriers here are plain
+// s_barrier with explicit waits: a workgroup-scope fence would make every
+// loader wait for all of its copies in flight.
+constexpr int RG_W = 0, RG_QT = 16384, RG_KBT = 32768, RG_U = 49152, RG_P = 53248, RG_GM = 61440;
+constexpr int RG_SLOT = 61952;
+struct RingLds {
+  static constexpr int SL = 136, DL = 72;  // bf16 row lengths of S0^T and D^T
+  static constexpr int O_RING = 0;
+  static constexpr int O_S = 2 * RG_SLOT;
+  static constexpr int O_D = O_S + DVB * SL * 2;
+  static constexpr int BYTES = O_D + DVB * DL * 2;
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// One wave copies 1 KB: lane l's 16 bytes from src_wave + 16 l to
+// lds_wave + 16 l (lds_wave is uniform across the wave).
+__device__ __forceinline__ void copy_1k(const char* src_wave, char* lds_wave, int l) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)(src_wave + 16 * l), (lds_void_t*)lds_wave, 16, 0, 0);
+}
+
+// s_waitcnt immediates (gfx9 encoding): wait until at most n vector-memory
+// operations of this wave are outstanding / until LDS operations are done.
+template <int n> __device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
+
+// Workgroup barrier without a workgroup-scope fence.  Callers wait for what
+// they must publish (compute waves: their LDS writes; loaders: their copies).
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Loader wave lw (0..3): copies of chunk record rc (bytes) and gamma gc.
+constexpr int RG_EARLY_PER_LOADER = 9;  // 32 KB of W, Qt + 4 KB of U over 4 loaders
+constexpr int RG_LATE_MIN = 6;          // 24 KB of Kb^T, P over 4 loaders (+ Gam on loader 0)
+__device__ __forceinline__ void ring_copy_early(const char* rc, char* slot, int vb, int lw, int l) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) copy_1k(rc + (lw + 4 * k) * 1024, slot + RG_W + (lw + 4 * k) * 1024, l);
+  copy_1k(rc + 2 * OFF_UT + vb * 4096 + lw * 1024, slot + RG_U + lw * 1024, l);
+}
+__device__ __forceinline__ void ring_copy_late(const char* rc, const char* gc, char* slot, int lw, int l) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) copy_1k(rc + 2 * OFF_KBT + (lw + 4 * k) * 1024, slot + RG_KBT + (lw + 4 * k) * 1024, l);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) copy_1k(rc + 2 * OFF_P + (lw + 4 * k) * 1024, slot + RG_P + (lw + 4 * k) * 1024, l);
+  if (lw == 0 && l < 32) copy_1k(gc, slot + RG_GM, l);  // 512 bytes of Gam
+}
+
+// One chunk for one compute wave; operands come from ring slot `slot`.
+template <typename TO, int ROLE, bool FULL>
+__device__ __forceinline__ void ring_step(const ScanArgs& p, const char* slot, f32x16& S, bf16* sS,
+                                          bf16* sD, int h, int ctok, int len, int vb, int w, int l) {
+  typedef RingLds L;
+  constexpr int SL = L::SL, DL = L::DL;
+  const int col = l & 31, g = l >> 5, wp = w & 1;
+  TO* __restrict__ out = reinterpret_cast<TO*>(p.out);
+  auto frag = [&](int off) { return *reinterpret_cast<const bf16x8*>(slot + off + 16 * l); };
+  bf16x8 a[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) a[s] = frag((ROLE == 0 ? RG_W : RG_QT) + wp * 8192 + s * 1024);
+  f32x16 X;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) X[e] = 0.0f;
+  if constexpr (ROLE == 0) {
+    bf16x8 u[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) u[s] = frag(RG_U + wp * 2048 + s * 1024);
+    X = mma32_frags<bf16, 64>(a, sS + col * SL + 64 * g, X);
+    // D = U - W S0 at tokens 32wp + row32(e), value column col
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      f32x4 d;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d[i] = val_at(u, 4 * e4 + i) - X[4 * e4 + i];
+      store4(sD + col * DL + 32 * wp + 8 * e4 + 4 * g, d);
+    }
+  } else {
+    // transposed product S0^T Qt^T: rows = values, columns = tokens
+    X = mma32_lds_frags<bf16, 64>(sS + col * SL + 64 * g, a, X);
+  }
+  wait_lds();
+  ring_barrier();  // D complete; every wave is done reading S0
+  bf16x8 kb[4], dfr[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) kb[s] = frag(RG_KBT + w * 4096 + s * 1024);
+  const f32x4* gmp = reinterpret_cast<const f32x4*>(slot + RG_GM);
+  f32x4 gm[4];
+#pragma unroll
+  for (int e4 = 0; e4 < 4; ++e4) gm[e4] = gmp[(32 * w + 8 * e4 + 4 * g) / 4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) dfr[s] = *reinterpret_cast<const bf16x8*>(sD + col * DL + 32 * g + 8 * s);
+  if constexpr (ROLE == 1) {
+    bf16x8 pr[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) pr[s] = frag(RG_P + wp * 4096 + s * 1024);
+    X = mma32_rr<bf16, 32>(dfr, pr, X);
+    // lane (col, g): token 32wp + col, values 8 e4 + 4g + (0..3); one exchange
+    // between the lane halves per pair of e4 gives 8 consecutive values
+    typedef unsigned u32;
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int NW = (int)sizeof(TO);
+    u32 wd[4][NW];
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      if constexpr (sizeof(TO) == 2) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          wd[e4][j] = __builtin_bit_cast(u32, bf16x2{(bf16)(p.scale * X[4 * e4 + 2 * j]),
+                                                     (bf16)(p.scale * X[4 * e4 + 2 * j + 1])});
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wd[e4][j] = __builtin_bit_cast(u32, p.scale * X[4 * e4 + j]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int j = 0; j < NW; ++j) {
+        const auto r = __builtin_amdgcn_permlane32_swap(wd[2 * q][j], wd[2 * q + 1][j], false, false);
+        wd[2 * q][j] = r[0];
+        wd[2 * q + 1][j] = r[1];
+      }
+    const int tk = 32 * wp + col;
+    if (FULL || tk < len) {
+      u32x4* o = reinterpret_cast<u32x4*>(out + ((size_t)(ctok + tk) * p.H + h) * DH + DVB * vb + 8 * g);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        if constexpr (sizeof(TO) == 2) {
+          o[2 * q] = u32x4{wd[2 * q][0], wd[2 * q][1], wd[2 * q + 1][0], wd[2 * q + 1][1]};
+        } else {
+          o[4 * q] = u32x4{wd[2 * q][0], wd[2 * q][1], wd[2 * q][2], wd[2 * q][3]};
+          o[4 * q + 1] = u32x4{wd[2 * q + 1][0], wd[2 * q + 1][1], wd[2 * q + 1][2], wd[2 * q + 1][3]};
+        }
+      }
+    }
+  }
+  // S_next = Diag(Gam) S0 + Kb^T D
+#pragma unroll
+  for (int e = 0; e < 16; ++e) S[e] *= gm[e >> 2][e & 3];
+  S = mma32_rr<bf16, 32>(kb, dfr, S);
+#pragma unroll
+  for (int e4 = 0; e4 < 4; ++e4)
+    store4(sS + col * SL + 32 * w + 8 * e4 + 4 * g,
+           f32x4{S[4 * e4], S[4 * e4 + 1], S[4 * e4 + 2], S[4 * e4 + 3]});
+  wait_lds();
+  ring_barrier();  // new S0 complete; D may be overwritten
+}
+
+template <typename TO>
+__global__ __launch_bounds__(512) void kda_scan_ring_kernel(ScanArgs p) {
+  typedef RingLds L;
+  constexpr int SL = L::SL;
+  __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+  char* ring = smem + L::O_RING;
+  bf16* sS = reinterpret_cast<bf16*>(smem + L::O_S);
+  bf16* sD = reinterpret_cast<bf16*>(smem + L::O_D);
+
+  int pair, vb;
+  scan_unit(blockIdx.x, pair, vb);
+  if (pair >= p.N * p.H) return;
+  const int n = pair / p.H, h = pair - n * p.H;
+  const int cbeg = p.cfirst[n], cend = p.cfirst[n + 1];
+  const int tseq = p.cu[n], tend = p.cu[n + 1];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int col = l & 31, g = l >> 5;
+  const size_t sbase = (size_t)pair * DH * DH + (size_t)(32 * (w & 3)) * DH + DVB * vb + col;
+  const int H = p.H;
+  const char* recb = reinterpret_cast<const char*>(p.rec);
+  const char* gamb = reinterpret_cast<const char*>(p.gam);
+  auto rec_of = [&](int c) { return recb + ((size_t)c * H + h) * (size_t)REC * 2; };
+  auto gam_of = [&](int c) { return gamb + ((size_t)c * H + h) * DH * 4; };
+
+  if (w >= 4) {
+    // ------------------------------------------------------------ loaders
+    if (cbeg == cend) return;
+    const int lw = w - 4, clast = cend - 1;
+    ring_copy_early(rec_of(cbeg), ring, vb, lw, l);
+    ring_copy_late(rec_of(cbeg), gam_of(cbeg), ring, lw, l);
+    wait_vm<0>();
+    ring_barrier();  // chunk cbeg in slot 0; start state in sS
+    for (int c = cbeg; c < cend; ++c) {
+      const int nx = min(c + 1, clast);
+      char* nslot = ring + ((c - cbeg + 1) & 1) * RG_SLOT;
+      ring_copy_early(rec_of(nx), nslot, vb, lw, l);
+      wait_vm<RG_EARLY_PER_LOADER>();  // late operands of chunk c are in
+      ring_barrier();
+      ring_copy_late(rec_of(nx), gam_of(nx), nslot, lw, l);
+      wait_vm<RG_LATE_MIN>();  // early operands of chunk c+1 are in
+      ring_barrier();
+    }
+    wait_vm<0>();  // nothing left in flight when the wave ends
+    return;
+  }
+  // -------------------------------------------------------------- compute
+  f32x16 S;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) S[e] = p.init ? p.init[sbase + (size_t)row32(e, l) * DH] : 0.0f;
+  if (cbeg == cend) {
+    if (p.fin) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) p.fin[sbase + (size_t)row32(e, l) * DH] = S[e];
+    }
+    return;
+  }
+#pragma unroll
+  for (int e4 = 0; e4 < 4; ++e4)
+    store4(sS + col * SL + 32 * w + 8 * e4 + 4 * g,
+           f32x4{S[4 * e4], S[4 * e4 + 1], S[4 * e4 + 2], S[4 * e4 + 3]});
+  wait_lds();
+  ring_barrier();
+  const int cfull = cbeg + (tend - tseq) / CHUNK;
+  for (int c = cbeg; c < cend; ++c) {
+    const char* slot = ring + ((c - cbeg) & 1) * RG_SLOT;
+    const int ctok = tseq + (c - cbeg) * CHUNK;
+    if (c < cfull) {
+      if (w < 2) ring_step<TO, 0, true>(p, slot, S, sS, sD, h, ctok, CHUNK, vb, w, l);
+      else ring_step<TO, 1, true>(p, slot, S, sS, sD, h, ctok, CHUNK, vb, w, l);
+    } else {
+      if (w < 2) ring_step<TO, 0, false>(p, slot, S, sS, sD, h, ctok, tend - ctok, vb, w, l);
+      else ring_step<TO, 1, false>(p, slot, S, sS, sD, h, ctok, tend - ctok, vb, w, l);
+    }
+  }
+  if (p.fin) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) p.fin[sbase + (size_t)row32(e, l) * DH] = S[e];
+  }
+}
+
 }  // namespace kda

@@ -42,6 +42,11 @@ def load_library(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"libkda.so not found at {path}; build it with __graft_entry__.build()")
+    # torch ships its own HIP runtime; loading it first makes libkda bind to the
+    # same runtime instance (same soname) instead of a second one that would
+    # not share devices, streams or allocations with torch.
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(path)
     vp = ctypes.c_void_p
     lib.kda_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t

@@ -138,6 +138,52 @@ def time_mode(args_dev, fp32: bool, steps: int, warmup: int):
     }
 
 
+def time_decode(N: int, H: int, steps: int, warmup: int):
+    """One decode step of the token-serial path: N sequences x 1 token x H
+    heads, bf16 activations, FP32 states updated in place (kda_recurrent_fwd).
+    Timed with HIP events on the launch stream.  Algorithmic bytes per step:
+    the states read and written (2 x N H d^2 x 4 B) plus q, k, v, f_raw,
+    b_raw read and out written (bf16)."""
+    import numpy as np
+    import torch
+
+    from chunked_gated_delta_07_amd import kda, synth
+
+    d = 128
+    inp = synth.make_inputs(list(range(N + 1)), H=H, d=d, act="bf16", seed=4242)
+    dev = torch.device("cuda:0")
+
+    def t(a, bf16):
+        x = torch.from_numpy(np.ascontiguousarray(a))
+        return (x.view(torch.bfloat16) if bf16 else x).to(dev)
+
+    args = [t(inp.q, True), t(inp.k, True), t(inp.v, True), t(inp.f_raw, True), t(inp.b_raw, True),
+            t(inp.A_log, False), t(inp.dt_bias, False), t(inp.cu_seqlens, False)]
+    S = 0.5 * torch.randn((N, H, d, d), generator=torch.Generator().manual_seed(4243)).to(dev)
+    out = torch.empty((N, H, d), dtype=torch.bfloat16, device=dev)
+    for _ in range(warmup):
+        kda.recurrent_fwd(*args, out=out, initial_state=S, final_state=S)
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record(stream)
+        kda.recurrent_fwd(*args, out=out, initial_state=S, final_state=S)
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    p50 = statistics.median(us)
+    nbytes = 2 * N * H * d * d * 4 + N * H * (5 * d + 1) * 2
+    gbps = nbytes / (p50 * 1e-6) / 1e9
+    return {"workload": f"decode {N} seq x 1 token, H={H}, d={d}, bf16 act, fp32 state in place",
+            "entry_point": "kda_recurrent_fwd", "p50_us": round(p50, 2), "max_us": round(us[-1], 2),
+            "tokens_per_s": round(N / (p50 * 1e-6), 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBS, 4),
+                         "bytes_per_step": nbytes}}
+
+
 def roofline_for(mode_name: str, T: int, H: int, res: dict, workload: str):
     """Dominant kernel of the path (by measured time) against its roofline."""
     names = ["chunk_table", "intra", "state_pass"]
@@ -174,6 +220,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-step measurement of the token-serial path")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--only-mode", choices=["bf16", "fp32"], default=None,
                     help="time one precision mode only (for profiling runs)")
@@ -243,6 +291,8 @@ def main():
                              zip(["chunk_table", "intra", "state_pass"], rm["stage_avg_us"])},
             "roofline": roofline_for(m, T, H, rm, cfg["name"]),
         }
+    if not args.no_decode and args.only_mode is None:
+        line["decode"] = time_decode(256, H, max(args.steps, 10), max(args.warmup, 2))
     line["context_h200_p50_us"] = H200_CONTEXT_P50_US
     line["kernel_source_hash"] = kernel_source_hash()
     if not args.no_cpu_baseline:

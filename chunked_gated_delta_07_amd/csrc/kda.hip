@@ -7,6 +7,7 @@
 #include "kda_common.hpp"
 #include "kda_intra.hpp"
 #include "kda_scan.hpp"
+#include "kda_recurrent.hpp"
 
 namespace kda {
 
@@ -218,6 +219,43 @@ extern "C" int kda_chunk_fwd_timed(const void* q, const void* k, const void* v, 
   return fwd_impl(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, num_seqs, total_tokens, H, d,
                   mode, out, workspace, workspace_bytes, nullptr, nullptr, stream, events,
                   num_events);
+}
+
+extern "C" int kda_recurrent_fwd(const void* q, const void* k, const void* v, const void* f_raw,
+                                 const void* b_raw, const float* A_log, const float* dt_bias,
+                                 const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                                 int32_t H, int32_t d, uint32_t mode, void* out,
+                                 const float* initial_state, float* final_state, void* stream) {
+  if (mode & ~KDA_MODE_ALL_BITS) return KDA_ERR_INVALID_ARG;
+  if (num_seqs < 1 || total_tokens < 0 || H < 1) return KDA_ERR_INVALID_ARG;
+  if (d != kda::DH) return KDA_ERR_UNSUPPORTED;
+  if ((int64_t)num_seqs * H > (int64_t)INT32_MAX / 2) return KDA_ERR_UNSUPPORTED;
+  if (total_tokens == 0 && !final_state) return KDA_OK;
+  if (total_tokens > 0 && (!q || !k || !v || !f_raw || !b_raw || !A_log || !dt_bias || !out ||
+                           !cu_seqlens))
+    return KDA_ERR_INVALID_ARG;
+  kda::RecArgs ra;
+  ra.q = q; ra.k = k; ra.v = v; ra.f = f_raw; ra.b = b_raw; ra.A_log = A_log; ra.dt_bias = dt_bias;
+  ra.cu = cu_seqlens; ra.init = initial_state; ra.fin = final_state; ra.out = out;
+  ra.N = num_seqs; ra.H = H; ra.eps = 1e-6f; ra.scale = 0.08838834764831845f;  // 1/sqrt(128)
+  const bool a32 = mode & KDA_ACT_FP32;
+  const bool o32 = (mode & KDA_OUT_FP32) || a32;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const dim3 grid((unsigned)((int64_t)num_seqs * H)), block(128);
+  if (total_tokens == 0) {
+    const int64_t n = (int64_t)num_seqs * H * kda::DH * kda::DH;
+    const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+    hipLaunchKernelGGL(kda::kda_state_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       initial_state, final_state, n);
+  } else if (!a32 && !o32) {
+    hipLaunchKernelGGL((kda::kda_recurrent_kernel<kda::bf16, kda::bf16>), grid, block, 0, s, ra);
+  } else if (!a32) {
+    hipLaunchKernelGGL((kda::kda_recurrent_kernel<kda::bf16, float>), grid, block, 0, s, ra);
+  } else {
+    hipLaunchKernelGGL((kda::kda_recurrent_kernel<float, float>), grid, block, 0, s, ra);
+  }
+  return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 extern "C" const char* kda_status_string(int status) {

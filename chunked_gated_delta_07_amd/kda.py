@@ -24,7 +24,8 @@ KDA_OUT_FP32 = 0x4
 
 # Exported symbols, in declaration order of include/kda.h.
 SYMBOLS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_state",
-           "kda_chunk_fwd_num_stages", "kda_chunk_fwd_timed", "kda_status_string")
+           "kda_recurrent_fwd", "kda_chunk_fwd_num_stages", "kda_chunk_fwd_timed",
+           "kda_status_string")
 
 _lib = None
 
@@ -58,6 +59,10 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd.argtypes = fwd_args
     lib.kda_chunk_fwd_state.restype = ctypes.c_int
     lib.kda_chunk_fwd_state.argtypes = fwd_args[:-1] + [vp, vp, vp]
+    lib.kda_recurrent_fwd.restype = ctypes.c_int
+    lib.kda_recurrent_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32,
+                                      ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_uint32, vp, vp, vp, vp]
     lib.kda_chunk_fwd_timed.restype = ctypes.c_int
     lib.kda_chunk_fwd_timed.argtypes = fwd_args + [ctypes.POINTER(vp), ctypes.c_int32]
     lib.kda_chunk_fwd_num_stages.restype = ctypes.c_int
@@ -173,3 +178,55 @@ def chunk_fwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, fp32_intermedia
     if st != KDA_OK:
         raise KdaError(st, where)
     return out
+
+
+def recurrent_fwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, out_fp32=False, out=None,
+                  initial_state=None, final_state=None, return_final_state=False, stream=None):
+    """Token-serial KDA forward through libkda (kda_recurrent_fwd): FP32 state,
+    one token at a time; for decode steps and short sequences.  Tensors as for
+    chunk_fwd; returns out, or (out, final_state) when a final state is asked
+    for (``final_state`` tensor to fill, or ``return_final_state=True``)."""
+    import torch
+
+    lib = load_library()
+    act_fp32 = q.dtype == torch.float32
+    if not act_fp32 and q.dtype != torch.bfloat16:
+        raise TypeError("activations must be bfloat16 or float32")
+    for t in (k, v, f_raw, b_raw):
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, f_raw, b_raw must share one dtype")
+    if A_log.dtype != torch.float32 or dt_bias.dtype != torch.float32:
+        raise TypeError("A_log and dt_bias must be float32")
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    T, H, d = q.shape
+    for t in (q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens):
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("all tensors must be contiguous device tensors")
+    if k.shape != q.shape or v.shape != q.shape or f_raw.shape != q.shape:
+        raise ValueError("q, k, v, f_raw must have one shape [T, H, d]")
+    if b_raw.shape != (T, H) or A_log.shape != (H,) or dt_bias.shape != (H, d):
+        raise ValueError("b_raw [T,H], A_log [H], dt_bias [H,d] expected")
+    num_seqs = cu_seqlens.numel() - 1
+    mode = make_mode(False, act_fp32, out_fp32)
+    out_dtype = torch.float32 if (out_fp32 or act_fp32) else q.dtype
+    if out is None:
+        out = torch.empty((T, H, d), dtype=out_dtype, device=q.device)
+    elif out.dtype != out_dtype or out.shape != (T, H, d) or not out.is_contiguous():
+        raise ValueError("out has the wrong dtype, shape or layout")
+    sshape = (num_seqs, H, d, d)
+    for t in (initial_state, final_state):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != sshape
+                              or not t.is_contiguous() or not t.is_cuda):
+            raise ValueError("states must be contiguous float32 [N, H, d, d] device tensors")
+    if final_state is None and return_final_state:
+        final_state = torch.empty(sshape, dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = lib.kda_recurrent_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(f_raw), _ptr(b_raw), _ptr(A_log),
+                               _ptr(dt_bias), _ptr(cu_seqlens), num_seqs, T, H, d, mode, _ptr(out),
+                               _ptr(initial_state), _ptr(final_state),
+                               ctypes.c_void_p(stream.cuda_stream))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_recurrent_fwd")
+    return (out, final_state) if final_state is not None else out

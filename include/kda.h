@@ -130,6 +130,28 @@ KDA_API int kda_chunk_fwd_state(const void* q, const void* k, const void* v, con
                         size_t workspace_bytes, const float* initial_state, float* final_state,
                         void* stream);
 
+/* Token-serial KDA forward: the same operator as kda_chunk_fwd_state, taken
+ * one token at a time with the state in FP32 (the serving-side FP32
+ * recurrence that xtuner PR #2301 validates its chunked path against,
+ * sections Problem and Validation).  Meant for decode steps and short
+ * sequences (work per token is sequential); long prefills belong to the
+ * chunked path.  Arguments as for kda_chunk_fwd_state, except:
+ *  - no workspace;
+ *  - mode: KDA_ACT_FP32 and KDA_OUT_FP32 as usual; KDA_MODE_FP32_INTERMEDIATE
+ *    is accepted and changes nothing (all intermediates are FP32);
+ *  - with total_tokens == 0 and a final_state, final_state receives the
+ *    initial state (zero if NULL) and no other pointer is read;
+ *  - initial_state / final_state ([num_seqs][H][d][d] float32, NULL
+ *    allowed) may be the same array: each state entry is read before the
+ *    first token and written after the last by the same thread.
+ * Returns KDA_OK without launching when total_tokens == 0 and final_state is
+ * NULL. */
+KDA_API int kda_recurrent_fwd(const void* q, const void* k, const void* v, const void* f_raw,
+                      const void* b_raw, const float* A_log, const float* dt_bias,
+                      const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                      int32_t H, int32_t d, uint32_t mode, void* out,
+                      const float* initial_state, float* final_state, void* stream);
+
 /* Number of kernels kda_chunk_fwd launches for this mode (the stages timed by
  * kda_chunk_fwd_timed). */
 KDA_API int kda_chunk_fwd_num_stages(uint32_t mode);

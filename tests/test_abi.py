@@ -79,6 +79,16 @@ def test_argument_errors_before_launch():
     assert st(d=96) == kda.KDA_ERR_UNSUPPORTED
     assert st(ws=1) == kda.KDA_ERR_WORKSPACE
     assert st(T=0, p=None) == kda.KDA_OK  # no final state requested: nothing launched
+    # the token-serial entry point checks the same before launching
+    rc = lambda **kw: lib.kda_recurrent_fwd(
+        *([kw.get("p", p)] * 8), kw.get("N", 1), kw.get("T", 10), kw.get("H", 4), kw.get("d", 128),
+        kw.get("mode", 0), kw.get("p", p), None, None, None)
+    assert rc(p=None) == kda.KDA_ERR_INVALID_ARG
+    assert rc(N=0) == kda.KDA_ERR_INVALID_ARG
+    assert rc(H=0) == kda.KDA_ERR_INVALID_ARG
+    assert rc(mode=0x10) == kda.KDA_ERR_INVALID_ARG
+    assert rc(d=64) == kda.KDA_ERR_UNSUPPORTED
+    assert rc(T=0, p=None) == kda.KDA_OK  # nothing to compute or copy
 
 
 def test_workspace_query():

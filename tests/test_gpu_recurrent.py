@@ -1,0 +1,135 @@
+"""GPU parity of the token-serial path (kda_recurrent_fwd, FP32 state) against
+the FP64 oracle, and its agreement with the chunked path on the same inputs.
+
+Tolerances: FP32 output rel. L2 <= 1e-4 and max abs <= 1e-3 (as for the
+chunked FP32 mode); final state rel. L2 <= 1e-4; bf16 output against the
+oracle rounded to bf16 <= 2^-8 (a few last-bit flips).
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+sys.path.insert(0, os.path.dirname(__file__))
+import kda_testutil as U  # noqa: E402
+
+import oracle  # noqa: E402
+from chunked_gated_delta_07_amd import synth  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from chunked_gated_delta_07_amd import kda
+
+    kda.load_library()
+    yield
+
+
+def _state(seed, N, H, scale=0.5):
+    return (scale * np.random.default_rng(seed).standard_normal((N, H, 128, 128))).astype(np.float32)
+
+
+def _rec(args, **kw):
+    import torch
+
+    from chunked_gated_delta_07_amd import kda
+
+    res = kda.recurrent_fwd(*args, **kw)
+    torch.cuda.synchronize()
+    return res
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp32"])
+def test_recurrent_packed_with_states(act):
+    import torch
+
+    cu = [0, 1, 40, 40, 107]
+    inp = synth.make_inputs(cu, H=3, d=128, act=act, seed=33)
+    S0 = _state(34, len(cu) - 1, 3)
+    out, fin = _rec(U.to_device(inp, "cuda:0"), out_fp32=True, initial_state=torch.from_numpy(S0).cuda(),
+                    return_final_state=True)
+    ref, fref = oracle.kda_forward(**inp.as_f64(), initial_state=S0.astype(np.float64),
+                                   return_final_state=True)
+    o, f = out.double().cpu().numpy(), fin.double().cpu().numpy()
+    ro, ma, rf = U.rel_l2(o, ref), U.max_abs(o, ref), U.rel_l2(f, fref)
+    print(f"[recurrent packed {act}] out rel={ro:.3e} max_abs={ma:.3e} final rel={rf:.3e}", flush=True)
+    assert ro <= U.TOL_FP32_REL and ma <= U.TOL_FP32_MAXABS and rf <= U.TOL_FP32_REL
+    assert np.array_equal(f[2], S0[2].astype(np.float64))  # empty sequence
+
+
+def test_recurrent_decode_batch():
+    """One token per sequence (a decode step) for 64 sequences x 8 heads."""
+    import torch
+
+    N, H = 64, 8
+    inp = synth.make_inputs(list(range(N + 1)), H=H, d=128, act="bf16", seed=35)
+    S0 = _state(36, N, H)
+    out, fin = _rec(U.to_device(inp, "cuda:0"), out_fp32=True, initial_state=torch.from_numpy(S0).cuda(),
+                    return_final_state=True)
+    ref, fref = oracle.kda_forward(**inp.as_f64(), initial_state=S0.astype(np.float64),
+                                   return_final_state=True)
+    ro = U.rel_l2(out.double().cpu().numpy(), ref)
+    rf = U.rel_l2(fin.double().cpu().numpy(), fref)
+    print(f"[recurrent decode] out rel={ro:.3e} final rel={rf:.3e}", flush=True)
+    assert ro <= U.TOL_FP32_REL and rf <= U.TOL_FP32_REL
+
+
+def test_recurrent_bf16_output():
+    inp = synth.config_inputs(1)
+    out = _rec(U.to_device(inp, "cuda:0"))
+    ref = U.bf16_round_f64(oracle.kda_forward(**inp.as_f64()))
+    rel = U.rel_l2(out.double().cpu().numpy(), ref)
+    print(f"[recurrent bf16 out] rel vs rounded oracle={rel:.3e}", flush=True)
+    assert rel <= 2 ** -8
+
+
+def test_recurrent_agrees_with_chunked_2048_tokens():
+    """Same inputs through the token loop and the chunked FP32 path (64 heads,
+    2048 tokens); both are also checked against the oracle on two heads."""
+    import torch
+
+    from chunked_gated_delta_07_amd import kda
+
+    inp = synth.config_inputs(2)
+    args = U.to_device(inp, "cuda:0")
+    o_rec, f_rec = _rec(args, out_fp32=True, return_final_state=True)
+    o_chk, f_chk = kda.chunk_fwd(*args, fp32_intermediate=True, out_fp32=True,
+                                 return_final_state=True)
+    torch.cuda.synchronize()
+    a, b = o_rec.double().cpu().numpy(), o_chk.double().cpu().numpy()
+    r_out, r_fin = U.rel_l2(a, b), U.rel_l2(f_rec.double().cpu().numpy(), f_chk.double().cpu().numpy())
+    heads = [3, 44]
+    ref = U.oracle_heads(inp, heads)
+    r_or = U.rel_l2(a[:, heads], ref)
+    print(f"[recurrent vs chunked 2048] out={r_out:.3e} final={r_fin:.3e}; vs oracle {r_or:.3e}",
+          flush=True)
+    assert r_out <= U.TOL_FP32_REL and r_fin <= U.TOL_FP32_REL and r_or <= U.TOL_FP32_REL
+
+
+def test_recurrent_in_place_and_empty():
+    import torch
+
+    from chunked_gated_delta_07_amd import kda
+
+    inp = synth.make_inputs([0, 50, 77], H=2, d=128, act="bf16", seed=37)
+    args = U.to_device(inp, "cuda:0")
+    S0 = torch.from_numpy(_state(38, 2, 2)).cuda()
+    out_a, fin_a = _rec(args, initial_state=S0, return_final_state=True)
+    S1 = S0.clone()
+    out_b, _ = _rec(args, initial_state=S1, final_state=S1)
+    assert torch.equal(out_a, out_b) and torch.equal(fin_a, S1)
+    dev = "cuda:0"
+    e = torch.empty((0, 2, 128), dtype=torch.bfloat16, device=dev)
+    empty = (e, e, e, e, torch.empty((0, 2), dtype=torch.bfloat16, device=dev),
+             torch.zeros(2, device=dev), torch.zeros((2, 128), device=dev),
+             torch.zeros(3, dtype=torch.int32, device=dev))
+    S2 = torch.from_numpy(_state(39, 2, 2)).cuda()
+    _, fin = kda.recurrent_fwd(*empty, initial_state=S2, return_final_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(fin, S2)

@@ -184,6 +184,44 @@ def time_decode(N: int, H: int, steps: int, warmup: int):
                          "bytes_per_step": nbytes}}
 
 
+def time_graph(args_dev, fp32: bool, replays: int = 50, warmup: int = 10):
+    """p50 / max of HIP-graph replays of one kda_chunk_fwd (the way the pages
+    time their kernels), events on the replay stream."""
+    import torch
+
+    from chunked_gated_delta_07_amd import kda
+
+    q = args_dev[0]
+    T, H, d = q.shape
+    mode = kda.make_mode(fp32, False, False)
+    ws = torch.empty(kda.workspace_bytes(T, args_dev[7].numel() - 1, H, d, mode),
+                     dtype=torch.uint8, device=q.device)
+    out = torch.empty((T, H, d), dtype=q.dtype, device=q.device)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        kda.chunk_fwd(*args_dev, fp32_intermediate=fp32, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        kda.chunk_fwd(*args_dev, fp32_intermediate=fp32, out=out, workspace=ws)
+    for _ in range(warmup):
+        g.replay()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(replays)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    return {"replays": replays, "p50_us": round(statistics.median(us), 2), "max_us": round(us[-1], 2),
+            "tokens_per_s": round(T / (statistics.median(us) * 1e-6), 1)}
+
+
 def roofline_for(mode_name: str, T: int, H: int, res: dict, workload: str):
     """Dominant kernel of the path (by measured time) against its roofline."""
     names = ["chunk_table", "intra", "state_pass"]
@@ -256,6 +294,7 @@ def main():
     torch.cuda.synchronize()
     modes = ["bf16", "fp32"] if args.only_mode is None else [args.only_mode]
     res = {m: time_mode(args_dev, m == "fp32", args.steps, args.warmup) for m in modes}
+    graph = {m: time_graph(args_dev, m == "fp32") for m in modes} if args.only_mode is None else {}
     head = modes[0]
     r = res[head]
     line = {
@@ -281,6 +320,8 @@ def main():
                          zip(["chunk_table", "intra", "state_pass"], r["stage_avg_us"])},
         "roofline": roofline_for(head, T, H, r, cfg["name"]),
     }
+    if head in graph:
+        line["graph_replay"] = graph[head]
     for m in modes[1:]:
         rm = res[m]
         line[f"{m}_mode"] = {
@@ -291,6 +332,8 @@ def main():
                              zip(["chunk_table", "intra", "state_pass"], rm["stage_avg_us"])},
             "roofline": roofline_for(m, T, H, rm, cfg["name"]),
         }
+        if m in graph:
+            line[f"{m}_mode"]["graph_replay"] = graph[m]
     if not args.no_decode and args.only_mode is None:
         line["decode"] = time_decode(256, H, max(args.steps, 10), max(args.warmup, 2))
     line["context_h200_p50_us"] = H200_CONTEXT_P50_US

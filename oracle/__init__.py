@@ -42,6 +42,11 @@ PLANT = {
     "init_transposed": 1 << 13,
     "final_early": 1 << 14,
 }
+# Deliberate mistakes of the short convolution (kda_oracle_short_conv).
+CONV_PLANT = {
+    "conv_no_reset": 1 << 15,
+    "conv_taps_reversed": 1 << 16,
+}
 
 
 def build(force: bool = False) -> str:
@@ -78,6 +83,10 @@ def _load():
     lib.kda_oracle_num_chunks.argtypes = [ip, ctypes.c_int, ctypes.c_int]
     lib.kda_oracle_chunk_record_len.restype = ctypes.c_int64
     lib.kda_oracle_chunk_record_len.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.kda_oracle_short_conv.restype = ctypes.c_int
+    lib.kda_oracle_short_conv.argtypes = [dp, ip, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                          ctypes.c_int, dp, dp, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_uint]
     lib.kda_oracle_num_threads.restype = ctypes.c_int
     lib.kda_oracle_num_threads.argtypes = []
     _lib = lib
@@ -190,6 +199,26 @@ def kda_prep(q, k, f_raw, b_raw, A_log, dt_bias, eps=1e-6):
     lib.kda_oracle_prep(_ptr(q), _ptr(k), _ptr(f_raw), _ptr(b_raw), _ptr(A_log), _ptr(dt_bias),
                         T, H, d, float(eps), _ptr(qn), _ptr(kn), _ptr(g), _ptr(beta))
     return qn, kn, g, beta
+
+
+def short_conv(x, cu_seqlens, weight, bias=None, silu=True, round_bf16=False, plant=0):
+    """Short causal convolution of one activation tensor x [T, H, d] (FP64
+    result): y_t = act(bias + sum_i weight[:, i] x_{t-K+1+i}), zero history at
+    every sequence start, act = SiLU or identity, optionally rounded to
+    bfloat16.  weight is [H*d, K] (last tap = current token), bias [H*d]."""
+    lib = _load()
+    y = _f64(x).copy()
+    T, H, d = y.shape
+    w = _f64(weight).reshape(H * d, -1)
+    K = w.shape[1]
+    b = None if bias is None else _f64(bias).reshape(H * d)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    rc = lib.kda_oracle_short_conv(_ptr(y), _ptr(cu, ctypes.c_int32), len(cu) - 1, T, H, d, _ptr(w),
+                                   _ptr(b) if b is not None else None, K, int(bool(silu)),
+                                   int(bool(round_bf16)), int(plant))
+    if rc != 0:
+        raise ValueError("kda_oracle_short_conv rejected its arguments")
+    return y
 
 
 def num_threads() -> int:

@@ -78,7 +78,9 @@ enum {
   PLANT_OUTER_SWAP = 1u << 11,       /* write (v - S^T k) k^T, operands swapped */
   PLANT_DROP_CARRY_64 = 1u << 12,    /* state reset every 64 tokens             */
   PLANT_INIT_TRANSPOSED = 1u << 13,  /* initial state read as S_init^T          */
-  PLANT_FINAL_EARLY = 1u << 14       /* final state taken before the last token */
+  PLANT_FINAL_EARLY = 1u << 14,      /* final state taken before the last token */
+  PLANT_CONV_NO_RESET = 1u << 15,    /* convolution history crosses sequences   */
+  PLANT_CONV_TAPS_REVERSED = 1u << 16 /* taps applied in reverse order           */
 };
 
 static double softplus(double x) {
@@ -424,6 +426,55 @@ int kda_oracle_chunked(const double* q, const double* k, const double* v, const 
     free(W); free(U); free(Qt); free(Kb); free(Dl); free(Gam); free(Sn);
   }
   free(cfirst);
+  return 0;
+}
+
+/* Round to the nearest bfloat16 value (8 significant bits), ties to even, in
+ * one step from the double value (no intermediate float rounding). */
+static double round_bf16(double x) {
+  if (x == 0.0 || !isfinite(x)) return x;
+  int e;
+  const double m = frexp(x, &e);          /* x = m 2^e, 0.5 <= |m| < 1 */
+  const double r = nearbyint(ldexp(m, 8)); /* 8 significant bits, ties to even */
+  return ldexp(r, e - 8);
+}
+
+/* Short causal convolution on one activation tensor, in place (the
+ * "KDAShortConvolution" in front of the KDA core, xtuner PR #2153, KDA
+ * module description: separate q/k/v causal convolutions whose forward keeps
+ * the activation dtype):
+ *   y_t[c] = act(bias[c] + sum_{i<K} w[c][i] x_{t-K+1+i}[c])
+ * with x_s = 0 for s before the start of t's sequence (no history crosses a
+ * sequence boundary), act = SiLU (x sigmoid(x)) when silu != 0, else the
+ * identity, and, when round_bf16 != 0, y rounded to bfloat16 (the activation
+ * dtype).  x is [T][H][d]; w is [H*d][K] (tap K-1 multiplies the current
+ * token); bias is [H*d] or NULL.  Returns 0, or -1 on bad args. */
+int kda_oracle_short_conv(double* x, const int32_t* cu_seqlens, int N, int64_t T, int H, int d,
+                          const double* w, const double* bias, int K, int silu, int round_to_bf16,
+                          unsigned plant) {
+  if (N < 1 || H < 1 || d < 1 || K < 1) return -1;
+  if (cu_seqlens[0] != 0 || cu_seqlens[N] != T) return -1;
+  const int64_t HD = (int64_t)H * d;
+#pragma omp parallel for schedule(static)
+  for (int64_t ch = 0; ch < HD; ++ch) {
+    double* hist = (double*)malloc(sizeof(double) * (size_t)K);
+    for (int n = 0; n < N; ++n) {
+      if (!(plant & PLANT_CONV_NO_RESET) || n == 0)
+        for (int i = 0; i < K; ++i) hist[i] = 0.0;  /* hist[K-1] = current token */
+      for (int64_t t = cu_seqlens[n]; t < cu_seqlens[n + 1]; ++t) {
+        for (int i = 0; i + 1 < K; ++i) hist[i] = hist[i + 1];
+        hist[K - 1] = x[t * HD + ch];
+        double acc = bias ? bias[ch] : 0.0;
+        for (int i = 0; i < K; ++i) {
+          const int tap = (plant & PLANT_CONV_TAPS_REVERSED) ? K - 1 - i : i;
+          acc += w[ch * K + tap] * hist[i];
+        }
+        if (silu) acc = acc / (1.0 + exp(-acc));
+        x[t * HD + ch] = round_to_bf16 ? round_bf16(acc) : acc;
+      }
+    }
+    free(hist);
+  }
   return 0;
 }
 

@@ -78,7 +78,8 @@ template <typename TA, typename MT, typename TO>
 static int launch_all(const void* q, const void* k, const void* v, const void* f, const void* b,
                       const float* A_log, const float* dt_bias, const int32_t* cu, int32_t N,
                       int64_t T, int32_t H, uint32_t mode, void* out, void* ws,
-                      const float* init, float* fin, hipStream_t stream, hipEvent_t const* ev) {
+                      const float* init, float* fin, const float* conv_w, const float* conv_b,
+                      int conv_silu, hipStream_t stream, hipEvent_t const* ev) {
   const WsLayout W = ws_layout(T, N, H, mode);
   char* base = reinterpret_cast<char*>(ws);
   int32_t* cfirst = reinterpret_cast<int32_t*>(base + W.off_cfirst);
@@ -94,8 +95,13 @@ static int launch_all(const void* q, const void* k, const void* v, const void* f
   ia.q = q; ia.k = k; ia.v = v; ia.f = f; ia.b = b;
   ia.A_log = A_log; ia.dt_bias = dt_bias; ia.cu = cu; ia.cfirst = cfirst;
   ia.N = N; ia.H = H; ia.eps = 1e-6f; ia.gam = gam; ia.rec = rec;
-  hipLaunchKernelGGL((kda_intra_kernel<TA, MT>), dim3((unsigned)C, (unsigned)H), dim3(256), 0, stream,
-                     ia);
+  ia.conv_w = conv_w; ia.conv_b = conv_b; ia.conv_silu = conv_silu;
+  if (conv_w)
+    hipLaunchKernelGGL((kda_intra_kernel<TA, MT, true>), dim3((unsigned)C, (unsigned)H), dim3(256), 0,
+                       stream, ia);
+  else
+    hipLaunchKernelGGL((kda_intra_kernel<TA, MT, false>), dim3((unsigned)C, (unsigned)H), dim3(256),
+                       0, stream, ia);
   if (ev) (void)hipEventRecord(ev[2], stream);
 
   ScanArgs sa;
@@ -115,13 +121,14 @@ static int launch_all(const void* q, const void* k, const void* v, const void* f
 static int dispatch(const void* q, const void* k, const void* v, const void* f, const void* b,
                     const float* A_log, const float* dt_bias, const int32_t* cu, int32_t N,
                     int64_t T, int32_t H, uint32_t mode, void* out, void* ws, const float* init,
-                    float* fin, hipStream_t s, hipEvent_t const* ev) {
+                    float* fin, const float* conv_w, const float* conv_b, int conv_silu,
+                    hipStream_t s, hipEvent_t const* ev) {
   const bool f32i = mode & KDA_MODE_FP32_INTERMEDIATE;
   const bool a32 = mode & KDA_ACT_FP32;
   const bool o32 = (mode & KDA_OUT_FP32) || a32;
 #define KDA_GO(TA, MT, TO) \
   return launch_all<TA, MT, TO>(q, k, v, f, b, A_log, dt_bias, cu, N, T, H, mode, out, ws, init, \
-                                fin, s, ev)
+                                fin, conv_w, conv_b, conv_silu, s, ev)
   if (!a32 && !f32i && !o32) KDA_GO(bf16, bf16, bf16);
   if (!a32 && !f32i && o32) KDA_GO(bf16, bf16, float);
   if (!a32 && f32i && !o32) KDA_GO(bf16, float, bf16);
@@ -166,8 +173,8 @@ extern "C" int kda_chunk_fwd_num_stages(uint32_t mode) {
 static int fwd_impl(const void* q, const void* k, const void* v, const void* f_raw, const void* b_raw,
                     const float* A_log, const float* dt_bias, const int32_t* cu, int32_t N, int64_t T,
                     int32_t H, int32_t d, uint32_t mode, void* out, void* ws, size_t ws_bytes,
-                    const float* init, float* fin, void* stream, void* const* events,
-                    int32_t num_events) {
+                    const float* init, float* fin, const float* conv_w, const float* conv_b,
+                    int conv_silu, void* stream, void* const* events, int32_t num_events) {
   int st = check_args(q, k, v, f_raw, b_raw, A_log, dt_bias, cu, N, T, H, d, mode, out, ws, ws_bytes);
   if (st != KDA_OK) return st;
   if (T == 0) {
@@ -185,7 +192,7 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* f_r
       if (!events[i]) return KDA_ERR_INVALID_ARG;
   (void)hipGetLastError();  // clear a stale error so the status reflects these launches
   return kda::dispatch(q, k, v, f_raw, b_raw, A_log, dt_bias, cu, N, T, H, mode, out, ws, init, fin,
-                       reinterpret_cast<hipStream_t>(stream),
+                       conv_w, conv_b, conv_silu, reinterpret_cast<hipStream_t>(stream),
                        reinterpret_cast<hipEvent_t const*>(events));
 }
 
@@ -195,7 +202,8 @@ extern "C" int kda_chunk_fwd(const void* q, const void* k, const void* v, const 
                              int32_t H, int32_t d, uint32_t mode, void* out, void* workspace,
                              size_t workspace_bytes, void* stream) {
   return fwd_impl(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, num_seqs, total_tokens, H, d,
-                  mode, out, workspace, workspace_bytes, nullptr, nullptr, stream, nullptr, 0);
+                  mode, out, workspace, workspace_bytes, nullptr, nullptr, nullptr, nullptr, 0, stream,
+                  nullptr, 0);
 }
 
 extern "C" int kda_chunk_fwd_state(const void* q, const void* k, const void* v, const void* f_raw,
@@ -205,8 +213,8 @@ extern "C" int kda_chunk_fwd_state(const void* q, const void* k, const void* v, 
                                    void* out, void* workspace, size_t workspace_bytes,
                                    const float* initial_state, float* final_state, void* stream) {
   return fwd_impl(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, num_seqs, total_tokens, H, d,
-                  mode, out, workspace, workspace_bytes, initial_state, final_state, stream,
-                  nullptr, 0);
+                  mode, out, workspace, workspace_bytes, initial_state, final_state, nullptr, nullptr, 0,
+                  stream, nullptr, 0);
 }
 
 extern "C" int kda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void* f_raw,
@@ -217,8 +225,21 @@ extern "C" int kda_chunk_fwd_timed(const void* q, const void* k, const void* v, 
                                    void* const* events, int32_t num_events) {
   if (!events) return KDA_ERR_INVALID_ARG;
   return fwd_impl(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, num_seqs, total_tokens, H, d,
-                  mode, out, workspace, workspace_bytes, nullptr, nullptr, stream, events,
-                  num_events);
+                  mode, out, workspace, workspace_bytes, nullptr, nullptr, nullptr, nullptr, 0, stream,
+                  events, num_events);
+}
+
+extern "C" int kda_chunk_fwd_conv(const void* q, const void* k, const void* v, const void* f_raw,
+                                  const void* b_raw, const float* A_log, const float* dt_bias,
+                                  const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                                  int32_t H, int32_t d, uint32_t mode, const float* conv_weight,
+                                  const float* conv_bias, int32_t conv_silu, void* out,
+                                  void* workspace, size_t workspace_bytes,
+                                  const float* initial_state, float* final_state, void* stream) {
+  if (total_tokens > 0 && !conv_weight) return KDA_ERR_INVALID_ARG;
+  return fwd_impl(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, num_seqs, total_tokens, H, d,
+                  mode, out, workspace, workspace_bytes, initial_state, final_state, conv_weight,
+                  conv_bias, conv_silu, stream, nullptr, 0);
 }
 
 extern "C" int kda_recurrent_fwd(const void* q, const void* k, const void* v, const void* f_raw,

@@ -90,19 +90,27 @@ struct IntraArgs {
   float eps;
   float* gam;  // [chunks][H][128]
   void* rec;   // [chunks][H][REC] of MT
+  // optional short causal convolution on q, k, v (used when the kernel's
+  // CONV parameter is set): weights [3][H*128][4] (tap 3 = current token),
+  // bias [3][H*128] or null, SiLU after it when conv_silu != 0
+  const float* conv_w;
+  const float* conv_b;
+  int conv_silu;
 };
 
-// Chunk c -> (first token, length).  cfirst is non-decreasing with cfirst[0]=0.
+// Chunk c -> (first token, length, first token of its sequence).  cfirst is
+// non-decreasing with cfirst[0]=0.
 __device__ __forceinline__ bool locate_chunk(const int32_t* __restrict__ cu,
                                              const int32_t* __restrict__ cfirst, int N, int c,
-                                             int& t0, int& len) {
+                                             int& t0, int& len, int& tseq) {
   if (c >= cfirst[N]) return false;
   int lo = 0, hi = N;  // cfirst[lo] <= c < cfirst[hi]
   while (hi - lo > 1) {
     int mid = (lo + hi) >> 1;
     if (cfirst[mid] <= c) lo = mid; else hi = mid;
   }
-  t0 = cu[lo] + (c - cfirst[lo]) * CHUNK;
+  tseq = cu[lo];
+  t0 = tseq + (c - cfirst[lo]) * CHUNK;
   len = min(CHUNK, cu[lo + 1] - t0);
   return true;
 }
@@ -159,10 +167,42 @@ template <typename T> __device__ __forceinline__ const T* wave_uniform(const T* 
   return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
 }
 
+// Short causal convolution (width 4) of a wave's 16 rows, channels c0 and
+// c0+1, in place: x[j] <- act(b + sum_i w[i] x[j-3+i]), rows before j = 0
+// taken from hist[0..2] (zero outside the sequence).  Computed from the last
+// row backwards so every row still reads raw inputs.  Weights and bias are
+// rounded to the activation dtype, products accumulate in FP32, the result is
+// rounded to the activation dtype (the convolution's forward keeps it).
+template <typename TA>
+__device__ __forceinline__ void conv16(f32x2 (&x)[16], const f32x2 (&hist)[3], const float* wt,
+                                       const float* bs, int c0, bool silu) {
+  float w[2][4], b[2];
+#pragma unroll
+  for (int ch = 0; ch < 2; ++ch) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[ch][i] = to_f32(from_f32<TA>(wt[(c0 + ch) * 4 + i]));
+    b[ch] = bs ? to_f32(from_f32<TA>(bs[c0 + ch])) : 0.0f;
+  }
+#pragma unroll
+  for (int j = 15; j >= 0; --j) {
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+      float acc = b[ch];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int src = j - 3 + i;
+        acc = fmaf(w[ch][i], src >= 0 ? x[src][ch] : hist[src + 3][ch], acc);
+      }
+      if (silu) acc *= sigmoid_f(acc);
+      x[j][ch] = to_f32(from_f32<TA>(acc));
+    }
+  }
+}
+
 // Index of cross-block combination (R, I), R > I, in 0..5.
 __device__ __forceinline__ constexpr int combo(int R, int I) { return (R * (R - 1)) / 2 + I; }
 
-template <typename TA, typename MT>
+template <typename TA, typename MT, bool CONV>
 __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
   typedef IntraLds<MT> L;
   constexpr int ROWL = L::ROWL, TL = L::TL, AL = L::AL;
@@ -176,8 +216,8 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
   char* sU = smem + L::O_U;
 
   const int chunk = blockIdx.x, h = blockIdx.y;
-  int t0, len;
-  if (!locate_chunk(p.cu, p.cfirst, p.N, chunk, t0, len)) return;  // uniform over the block
+  int t0, len, tseq;
+  if (!locate_chunk(p.cu, p.cfirst, p.N, chunk, t0, len, tseq)) return;  // uniform over the block
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int H = p.H;
@@ -207,6 +247,23 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
   // wave-uniform base with scalar row offsets and need no masks.
   const bool full = len == CHUNK;  // uniform over the block
   const size_t rstride = (size_t)H * DH;  // elements from one token to the next
+  // the three tokens before this wave's first row, for the convolution: zero
+  // before the sequence start (and past the chunk's end, where every row of
+  // this wave is masked anyway); reads stay inside the chunk or the sequence
+  auto conv_hist = [&](const TA* __restrict__ gx, f32x2 (&hx)[3]) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int tok = t0 + 16 * w - 3 + i;
+      const bool ok = tok >= tseq && tok < t0 + len;
+      const f32x2 x = load2(gx + ((size_t)(ok ? tok : t0) * H + h) * DH + c0);
+      hx[i] = ok ? x : f32x2{0.0f, 0.0f};
+    }
+  };
+  const size_t HDt = (size_t)H * DH;  // channels of one tensor
+  auto conv_w_of = [&](int tensor) { return p.conv_w + (tensor * HDt + (size_t)h * DH) * 4; };
+  auto conv_b_of = [&](int tensor) {
+    return p.conv_b ? p.conv_b + tensor * HDt + (size_t)h * DH : (const float*)nullptr;
+  };
   {
     f32x2 xq[16], xk[16], xf[16];
     if (full) {
@@ -227,6 +284,13 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
         const size_t o = ((size_t)(t0 + (r < len ? r : 0)) * H + h) * DH + c0;
         xq[j] = load2(gq + o); xk[j] = load2(gk + o); xf[j] = load2(gf + o);
       }
+    }
+    if constexpr (CONV) {
+      f32x2 hq[3], hk[3];
+      conv_hist(gq, hq);
+      conv_hist(gk, hk);
+      conv16<TA>(xq, hq, conv_w_of(0), conv_b_of(0), c0, p.conv_silu != 0);
+      conv16<TA>(xk, hk, conv_w_of(1), conv_b_of(1), c0, p.conv_silu != 0);
     }
     float bl = 0.0f;
     if (l < 16) bl = to_f32(gb[(size_t)(t0 + (16 * w + l < len ? 16 * w + l : 0)) * H + h]);
@@ -508,7 +572,22 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
   float* sT = reinterpret_cast<float*>(sU + L::O_T);
   // values for the U product, loaded early so their latency hides under the solve
   float v0[16], v1[16];
-  if (full) {
+  if constexpr (CONV) {
+    f32x2 xv[16], hv[3];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = 16 * w + j;
+      xv[j] = load2(gv + ((size_t)(t0 + (r < len ? r : 0)) * H + h) * DH + c0);
+    }
+    conv_hist(gv, hv);
+    conv16<TA>(xv, hv, conv_w_of(2), conv_b_of(2), c0, p.conv_silu != 0);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const bool ok = 16 * w + j < len;
+      v0[j] = ok ? xv[j][0] : 0.0f;
+      v1[j] = ok ? xv[j][1] : 0.0f;
+    }
+  } else if (full) {
     const TA* bv = wave_uniform(gv + ((size_t)(t0 + 16 * w) * H + h) * DH);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {

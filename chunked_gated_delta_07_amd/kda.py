@@ -24,8 +24,8 @@ KDA_OUT_FP32 = 0x4
 
 # Exported symbols, in declaration order of include/kda.h.
 SYMBOLS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_state",
-           "kda_recurrent_fwd", "kda_chunk_fwd_num_stages", "kda_chunk_fwd_timed",
-           "kda_status_string")
+           "kda_chunk_fwd_conv", "kda_recurrent_fwd", "kda_chunk_fwd_num_stages",
+           "kda_chunk_fwd_timed", "kda_status_string")
 
 _lib = None
 
@@ -59,6 +59,9 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd.argtypes = fwd_args
     lib.kda_chunk_fwd_state.restype = ctypes.c_int
     lib.kda_chunk_fwd_state.argtypes = fwd_args[:-1] + [vp, vp, vp]
+    lib.kda_chunk_fwd_conv.restype = ctypes.c_int
+    lib.kda_chunk_fwd_conv.argtypes = (fwd_args[:13] + [vp, vp, ctypes.c_int32] + fwd_args[13:16]
+                                       + [vp, vp, vp])
     lib.kda_recurrent_fwd.restype = ctypes.c_int
     lib.kda_recurrent_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32,
                                       ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
@@ -100,7 +103,8 @@ def _ptr(t):
 
 def chunk_fwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, fp32_intermediate=False,
               out_fp32=False, out=None, workspace=None, stream=None, events=None,
-              initial_state=None, final_state=None, return_final_state=False):
+              initial_state=None, final_state=None, return_final_state=False,
+              conv_weight=None, conv_bias=None, conv_silu=True):
     """KDA chunked forward through libkda.
 
     q, k, v, f_raw: [T, H, 128] bfloat16 or float32 (one dtype for all);
@@ -112,7 +116,10 @@ def chunk_fwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, fp32_intermedia
     ``initial_state``: optional [N, H, 128, 128] float32 start states (key,
     value); ``final_state`` (a tensor of that shape to fill, may be the
     initial_state tensor) or ``return_final_state=True`` (allocated) selects
-    kda_chunk_fwd_state and makes the result (out, final_state)."""
+    kda_chunk_fwd_state and makes the result (out, final_state).
+    ``conv_weight`` [3, H, 128, 4] float32 (optional ``conv_bias`` [3, H, 128],
+    ``conv_silu``) selects kda_chunk_fwd_conv: the short causal convolution on
+    q, k, v fused in front of the core."""
     import torch
 
     lib = load_library()
@@ -151,6 +158,29 @@ def chunk_fwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, fp32_intermedia
             _ptr(cu_seqlens), num_seqs, T, H, d, mode, _ptr(out), _ptr(workspace),
             workspace.numel(), sp)
     use_state = initial_state is not None or final_state is not None or return_final_state
+    if conv_weight is not None:
+        if events is not None:
+            raise ValueError("events are not supported together with the convolution")
+        if (conv_weight.dtype != torch.float32 or tuple(conv_weight.shape) != (3, H, d, 4)
+                or not conv_weight.is_contiguous() or not conv_weight.is_cuda):
+            raise ValueError("conv_weight must be a contiguous float32 [3, H, d, 4] device tensor")
+        if conv_bias is not None and (conv_bias.dtype != torch.float32
+                                      or tuple(conv_bias.shape) != (3, H, d)
+                                      or not conv_bias.is_contiguous() or not conv_bias.is_cuda):
+            raise ValueError("conv_bias must be a contiguous float32 [3, H, d] device tensor")
+        sshape = (num_seqs, H, d, d)
+        for t in (initial_state, final_state):
+            if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != sshape
+                                  or not t.is_contiguous() or not t.is_cuda):
+                raise ValueError("states must be contiguous float32 [N, H, d, d] device tensors")
+        if final_state is None and return_final_state:
+            final_state = torch.empty(sshape, dtype=torch.float32, device=q.device)
+        st = lib.kda_chunk_fwd_conv(*args[:13], _ptr(conv_weight), _ptr(conv_bias),
+                                    int(bool(conv_silu)), *args[13:16], _ptr(initial_state),
+                                    _ptr(final_state), sp)
+        if st != KDA_OK:
+            raise KdaError(st, "kda_chunk_fwd_conv")
+        return (out, final_state) if final_state is not None else out
     if use_state:
         if events is not None:
             raise ValueError("events are not supported together with states")

@@ -130,6 +130,31 @@ KDA_API int kda_chunk_fwd_state(const void* q, const void* k, const void* v, con
                         size_t workspace_bytes, const float* initial_state, float* final_state,
                         void* stream);
 
+/* kda_chunk_fwd_state with the short causal convolution in front of the core
+ * fused in: q, k and v each pass through their own depthwise causal
+ * convolution of width 4 (xtuner PR #2153, KDA module description: separate
+ * q/k/v causal convolutions; FP32 master parameters, forward in the
+ * activation dtype), optionally followed by SiLU:
+ *   x'_t[c] = act(bias[c] + sum_{i<4} w[c][i] x_{t-3+i}[c]),
+ * with zero history at every sequence start (no history input: a sequence
+ * split across calls needs its first 3 tokens' history, which this entry
+ * point does not take).
+ *  conv_weight : device, [3][H][d][4] float32 (tensor q, k, v; tap 3 is the
+ *                current token); required when total_tokens > 0.
+ *  conv_bias   : device, [3][H][d] float32, or NULL (no bias).
+ *  conv_silu   : nonzero applies SiLU (x * sigmoid(x)) after the convolution.
+ * Weights and bias are rounded to the activation dtype, products accumulate
+ * in FP32 and the convolution output is rounded to the activation dtype
+ * before the KDA core (L2 norm, gate, ...), as a separate convolution op in
+ * that dtype would do.  Everything else as for kda_chunk_fwd_state. */
+KDA_API int kda_chunk_fwd_conv(const void* q, const void* k, const void* v, const void* f_raw,
+                       const void* b_raw, const float* A_log, const float* dt_bias,
+                       const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                       int32_t H, int32_t d, uint32_t mode, const float* conv_weight,
+                       const float* conv_bias, int32_t conv_silu, void* out, void* workspace,
+                       size_t workspace_bytes, const float* initial_state, float* final_state,
+                       void* stream);
+
 /* Token-serial KDA forward: the same operator as kda_chunk_fwd_state, taken
  * one token at a time with the state in FP32 (the serving-side FP32
  * recurrence that xtuner PR #2301 validates its chunked path against,

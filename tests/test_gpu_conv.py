@@ -1,0 +1,134 @@
+"""GPU parity of kda_chunk_fwd_conv (short causal convolution on q, k, v fused
+in front of the core) against the oracle's convolution followed by its token
+recurrence.
+
+Tolerances: BF16 mode 1e-2; FP32 mode with float32 activations 1e-4 / 1e-3
+(max abs).  FP32 mode with bf16 activations: the convolution output is rounded
+to bf16 on both sides, from an FP32 value on the GPU and an FP64 value in the
+oracle, so a few elements round the other way (one bf16 step, 2^-8 relative);
+the bound there is 5e-4.  Weights and biases are drawn bf16-representable, so
+rounding them to the activation dtype changes nothing.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+sys.path.insert(0, os.path.dirname(__file__))
+import kda_testutil as U  # noqa: E402
+
+import oracle  # noqa: E402
+from chunked_gated_delta_07_amd import synth  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from chunked_gated_delta_07_amd import kda
+
+    kda.load_library()
+    yield
+
+
+def _bf16_exact(a):
+    return synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(a.astype(np.float32)))
+
+
+def _conv_params(H, seed):
+    r = np.random.default_rng(seed)
+    w = _bf16_exact(0.5 * r.standard_normal((3, H, 128, 4)))
+    b = _bf16_exact(0.1 * r.standard_normal((3, H, 128)))
+    return w, b
+
+
+def _oracle(inp, w, b, silu, init=None):
+    f64 = inp.as_f64()
+    H = inp.H
+    rnd = inp.act == "bf16"
+    for i, name in enumerate(("q", "k", "v")):
+        f64[name] = oracle.short_conv(f64[name], f64["cu_seqlens"], w[i].reshape(H * 128, 4),
+                                      bias=None if b is None else b[i].reshape(H * 128), silu=silu,
+                                      round_bf16=rnd)
+    if init is None:
+        return oracle.kda_forward(**f64), None
+    return oracle.kda_forward(**f64, initial_state=init.astype(np.float64), return_final_state=True)
+
+
+def _gpu_run(inp, w, b, silu, fp32, init=None):
+    import torch
+
+    from chunked_gated_delta_07_amd import kda
+
+    args = U.to_device(inp, "cuda:0")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    res = kda.chunk_fwd(*args, fp32_intermediate=fp32, out_fp32=True, conv_weight=dev(w),
+                        conv_bias=None if b is None else dev(b), conv_silu=silu,
+                        initial_state=None if init is None else dev(init),
+                        return_final_state=init is not None)
+    torch.cuda.synchronize()
+    if init is None:
+        return res.double().cpu().numpy(), None
+    return res[0].double().cpu().numpy(), res[1].double().cpu().numpy()
+
+
+@pytest.mark.parametrize("fp32", [False, True], ids=["bf16", "fp32"])
+def test_conv_packed_bf16_activations(fp32):
+    """Sequence starts inside chunks, a 2-token sequence, an empty one, and a
+    start state: the convolution history restarts at every sequence."""
+    cu = [0, 2, 67, 67, 200]
+    inp = synth.make_inputs(cu, H=3, d=128, act="bf16", seed=61)
+    w, b = _conv_params(3, 62)
+    S0 = (0.3 * np.random.default_rng(63).standard_normal((4, 3, 128, 128))).astype(np.float32)
+    out, fin = _gpu_run(inp, w, b, True, fp32, init=S0)
+    ref, fref = _oracle(inp, w, b, True, init=S0)
+    ro, rf = U.rel_l2(out, ref), U.rel_l2(fin, fref)
+    print(f"[conv bf16 act] mode={'fp32' if fp32 else 'bf16'} out rel={ro:.3e} final rel={rf:.3e}",
+          flush=True)
+    tol = 5e-4 if fp32 else U.TOL_BF16_REL
+    assert ro <= tol and rf <= tol
+
+
+def test_conv_fp32_activations_fp32_mode():
+    cu = [0, 130, 131, 250]
+    inp = synth.make_inputs(cu, H=2, d=128, act="fp32", seed=64)
+    w, b = _conv_params(2, 65)
+    out, _ = _gpu_run(inp, w, b, True, True)
+    ref, _ = _oracle(inp, w, b, True)
+    ro, ma = U.rel_l2(out, ref), U.max_abs(out, ref)
+    print(f"[conv fp32 act] out rel={ro:.3e} max_abs={ma:.3e}", flush=True)
+    assert ro <= U.TOL_FP32_REL and ma <= U.TOL_FP32_MAXABS
+
+
+def test_conv_without_silu_and_bias():
+    inp = synth.make_inputs([0, 100, 190], H=2, d=128, act="fp32", seed=66)
+    w, _ = _conv_params(2, 67)
+    out, _ = _gpu_run(inp, w, None, False, True)
+    ref, _ = _oracle(inp, w, None, False)
+    ro = U.rel_l2(out, ref)
+    print(f"[conv linear] out rel={ro:.3e}", flush=True)
+    assert ro <= U.TOL_FP32_REL
+
+
+@pytest.mark.parametrize("fp32", [False, True], ids=["bf16", "fp32"])
+def test_identity_conv_equals_plain_path(fp32):
+    """Taps (0, 0, 0, 1), no bias, no SiLU: the core sees the raw inputs."""
+    import torch
+
+    from chunked_gated_delta_07_amd import kda
+
+    inp = synth.config_inputs(1)
+    args = U.to_device(inp, "cuda:0")
+    w = np.zeros((3, inp.H, 128, 4), dtype=np.float32)
+    w[..., 3] = 1.0
+    a = kda.chunk_fwd(*args, fp32_intermediate=fp32, out_fp32=True)
+    c = kda.chunk_fwd(*args, fp32_intermediate=fp32, out_fp32=True,
+                      conv_weight=torch.from_numpy(w).cuda(), conv_silu=False)
+    torch.cuda.synchronize()
+    r = U.rel_l2(c.double().cpu().numpy(), a.double().cpu().numpy())
+    print(f"[identity conv] rel vs plain={r:.3e}", flush=True)
+    assert r <= 1e-6

@@ -222,6 +222,42 @@ def time_graph(args_dev, fp32: bool, replays: int = 50, warmup: int = 10):
             "tokens_per_s": round(T / (statistics.median(us) * 1e-6), 1)}
 
 
+def time_conv(args_dev, steps: int, warmup: int):
+    """kda_chunk_fwd_conv on the headline workload, BF16 intermediates: the
+    width-4 causal convolution on q, k, v (bias, SiLU) fused into the intra
+    kernel.  Step time from HIP events on the launch stream."""
+    import numpy as np
+    import torch
+
+    from chunked_gated_delta_07_amd import kda
+
+    q = args_dev[0]
+    T, H, d = q.shape
+    g = torch.Generator().manual_seed(4244)
+    w = (0.5 * torch.randn((3, H, d, 4), generator=g)).to(q.device)
+    b = (0.1 * torch.randn((3, H, d), generator=g)).to(q.device)
+    mode = kda.make_mode(False, False, False)
+    ws = torch.empty(kda.workspace_bytes(T, args_dev[7].numel() - 1, H, d, mode),
+                     dtype=torch.uint8, device=q.device)
+    out = torch.empty((T, H, d), dtype=q.dtype, device=q.device)
+    for _ in range(warmup):
+        kda.chunk_fwd(*args_dev, out=out, workspace=ws, conv_weight=w, conv_bias=b, conv_silu=True)
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, e in evs:
+        a.record(stream)
+        kda.chunk_fwd(*args_dev, out=out, workspace=ws, conv_weight=w, conv_bias=b, conv_silu=True)
+        e.record(stream)
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(e) * 1e3 for a, e in evs)
+    p50 = statistics.median(us)
+    return {"entry_point": "kda_chunk_fwd_conv", "workload": "headline + width-4 q/k/v conv, SiLU, bias",
+            "intermediates": "bf16", "p50_us": round(p50, 2), "max_us": round(us[-1], 2),
+            "tokens_per_s": round(T / (p50 * 1e-6), 1)}
+
+
 def roofline_for(mode_name: str, T: int, H: int, res: dict, workload: str):
     """Dominant kernel of the path (by measured time) against its roofline."""
     names = ["chunk_table", "intra", "state_pass"]
@@ -334,6 +370,8 @@ def main():
         }
         if m in graph:
             line[f"{m}_mode"]["graph_replay"] = graph[m]
+    if args.only_mode is None:
+        line["conv_fused"] = time_conv(args_dev, max(args.steps, 10), max(args.warmup, 2))
     if not args.no_decode and args.only_mode is None:
         line["decode"] = time_decode(256, H, max(args.steps, 10), max(args.warmup, 2))
     line["context_h200_p50_us"] = H200_CONTEXT_P50_US

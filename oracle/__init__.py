@@ -71,6 +71,11 @@ def _load():
     lib.kda_oracle_fwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, ip, ctypes.c_int, ctypes.c_int64,
                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_double, ctypes.c_double, ctypes.c_uint, dp, dp, dp]
+    lib.kda_oracle_fwd_rect.restype = ctypes.c_int
+    lib.kda_oracle_fwd_rect.argtypes = [dp, dp, dp, dp, dp, dp, dp, ip, ctypes.c_int,
+                                        ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                        ctypes.c_double, ctypes.c_uint, dp, dp, dp]
     lib.kda_oracle_chunked.restype = ctypes.c_int
     lib.kda_oracle_chunked.argtypes = [dp, dp, dp, dp, dp, dp, dp, ip, ctypes.c_int, ctypes.c_int64,
                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -108,6 +113,36 @@ def _check_shapes(q, k, v, f, b, A_log, dt_bias, cu):
     assert b.shape == (T, H) and A_log.shape == (H,) and dt_bias.shape == (H, d)
     assert cu.ndim == 1 and cu[0] == 0 and cu[-1] == T
     return T, H, d
+
+
+def kda_forward_rect(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, scale=None, eps=1e-6,
+                     plant=0, initial_state=None, return_final_state=False):
+    """Token-serial FP64 KDA forward with a rectangular state: q, k, f_raw
+    [T, H, dk], dt_bias [H, dk], v [T, H, dv]; returns out [T, H, dv] (and the
+    final state [N, H, dk, dv]).  scale defaults to 1/sqrt(dk)."""
+    lib = _load()
+    q, k, v, f_raw, b_raw, A_log, dt_bias = map(_f64, (q, k, v, f_raw, b_raw, A_log, dt_bias))
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    assert k.shape == q.shape and f_raw.shape == q.shape and v.shape == (T, H, dv)
+    assert b_raw.shape == (T, H) and A_log.shape == (H,) and dt_bias.shape == (H, dk)
+    N = len(cu) - 1
+    if scale is None:
+        scale = 1.0 / np.sqrt(dk)
+    out = np.zeros((T, H, dv), dtype=np.float64)
+    init = None if initial_state is None else _f64(initial_state)
+    if init is not None:
+        assert init.shape == (N, H, dk, dv), init.shape
+    fin = np.zeros((N, H, dk, dv), dtype=np.float64) if return_final_state else None
+    rc = lib.kda_oracle_fwd_rect(_ptr(q), _ptr(k), _ptr(v), _ptr(f_raw), _ptr(b_raw), _ptr(A_log),
+                                 _ptr(dt_bias), _ptr(cu, ctypes.c_int32), N, T, H, dk, dv, 0, H,
+                                 float(scale), float(eps), int(plant),
+                                 _ptr(init) if init is not None else None,
+                                 _ptr(fin) if fin is not None else None, _ptr(out))
+    if rc != 0:
+        raise ValueError("kda_oracle_fwd_rect rejected its arguments")
+    return (out, fin) if return_final_state else out
 
 
 def _states(initial_state, return_final_state, N, H, d):

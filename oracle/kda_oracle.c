@@ -130,30 +130,52 @@ void kda_oracle_prep(const double* q, const double* k, const double* f, const do
   }
 }
 
-/* Start state of sequence n, head h: S_init's block, or zero. */
-static void load_init(double* S, const double* S_init, int n, int H, int h, int d,
-                      unsigned plant) {
-  const size_t dd = (size_t)d * d;
+/* Start state of sequence n, head h (dk x dv): S_init's block, or zero.  The
+ * transposed plant reads a square block transposed. */
+static void load_init_rect(double* S, const double* S_init, int n, int H, int h, int dk, int dv,
+                           unsigned plant) {
+  const size_t dd = (size_t)dk * dv;
   if (!S_init) { memset(S, 0, sizeof(double) * dd); return; }
   const double* src = S_init + ((size_t)n * H + h) * dd;
-  if (plant & PLANT_INIT_TRANSPOSED) {
-    for (int i = 0; i < d; ++i)
-      for (int j = 0; j < d; ++j) S[(size_t)i * d + j] = src[(size_t)j * d + i];
+  if ((plant & PLANT_INIT_TRANSPOSED) && dk == dv) {
+    for (int i = 0; i < dk; ++i)
+      for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] = src[(size_t)j * dv + i];
   } else {
     memcpy(S, src, sizeof(double) * dd);
   }
+}
+static void load_init(double* S, const double* S_init, int n, int H, int h, int d,
+                      unsigned plant) {
+  load_init_rect(S, S_init, n, H, h, d, d, plant);
 }
 
 /* Token-serial recurrence for heads [h_lo, h_hi).  out is [T][H][d]; rows of
  * heads outside the range are left untouched.  S_init / S_final: see the
  * header (NULL = zero start / not returned; only the blocks of heads in range
  * are read or written).  Returns 0, or -1 on bad args. */
+int kda_oracle_fwd_rect(const double* q, const double* k, const double* v, const double* f,
+                        const double* b, const double* A_log, const double* dt_bias,
+                        const int32_t* cu_seqlens, int N, int64_t T, int H, int dk, int dv,
+                        int h_lo, int h_hi, double scale, double eps, unsigned plant,
+                        const double* S_init, double* S_final, double* out);
+
 int kda_oracle_fwd(const double* q, const double* k, const double* v, const double* f,
                    const double* b, const double* A_log, const double* dt_bias,
                    const int32_t* cu_seqlens, int N, int64_t T, int H, int d, int h_lo,
                    int h_hi, double scale, double eps, unsigned plant, const double* S_init,
                    double* S_final, double* out) {
-  if (N < 1 || H < 1 || d < 1 || h_lo < 0 || h_hi > H || h_lo > h_hi) return -1;
+  return kda_oracle_fwd_rect(q, k, v, f, b, A_log, dt_bias, cu_seqlens, N, T, H, d, d, h_lo, h_hi,
+                             scale, eps, plant, S_init, S_final, out);
+}
+
+/* The same with a rectangular state: q, k, f, dt_bias have dk channels, v
+ * and out dv channels, S and the states are dk x dv. */
+int kda_oracle_fwd_rect(const double* q, const double* k, const double* v, const double* f,
+                        const double* b, const double* A_log, const double* dt_bias,
+                        const int32_t* cu_seqlens, int N, int64_t T, int H, int dk, int dv,
+                        int h_lo, int h_hi, double scale, double eps, unsigned plant,
+                        const double* S_init, double* S_final, double* out) {
+  if (N < 1 || H < 1 || dk < 1 || dv < 1 || h_lo < 0 || h_hi > H || h_lo > h_hi) return -1;
   if (cu_seqlens[0] != 0 || cu_seqlens[N] != T) return -1;
   for (int n = 0; n < N; ++n)
     if (cu_seqlens[n + 1] < cu_seqlens[n]) return -1;
@@ -161,16 +183,17 @@ int kda_oracle_fwd(const double* q, const double* k, const double* v, const doub
   /* With PLANT_NO_RESET the sequences of one head are walked in order with one
    * state, so the parallel unit is the head; otherwise it is (sequence, head). */
   const int64_t units = (plant & PLANT_NO_RESET) ? (int64_t)nh : (int64_t)N * nh;
+  const size_t sz = (size_t)dk * dv;
+  const int square = dk == dv; /* the transposing plants only exist for square states */
 
 #pragma omp parallel
   {
-    double* S = (double*)malloc(sizeof(double) * (size_t)d * d);
-    double* qn = (double*)malloc(sizeof(double) * (size_t)d);
-    double* kn = (double*)malloc(sizeof(double) * (size_t)d);
-    double* g = (double*)malloc(sizeof(double) * (size_t)d);
-    double* u = (double*)malloc(sizeof(double) * (size_t)d);
-    double* Sprev = (plant & PLANT_DELTA_UNDECAYED) ? (double*)malloc(sizeof(double) * (size_t)d * d)
-                                                    : NULL;
+    double* S = (double*)malloc(sizeof(double) * sz);
+    double* qn = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* kn = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* g = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* u = (double*)malloc(sizeof(double) * (size_t)dv);
+    double* Sprev = (plant & PLANT_DELTA_UNDECAYED) ? (double*)malloc(sizeof(double) * sz) : NULL;
 #pragma omp for schedule(dynamic, 1)
     for (int64_t w = 0; w < units; ++w) {
       int h, n_lo, n_hi;
@@ -179,72 +202,73 @@ int kda_oracle_fwd(const double* q, const double* k, const double* v, const doub
       } else {
         h = h_lo + (int)(w % nh); n_lo = (int)(w / nh); n_hi = n_lo + 1;
       }
-      load_init(S, S_init, n_lo, H, h, d, plant);
+      load_init_rect(S, S_init, n_lo, H, h, dk, dv, plant);
       for (int n = n_lo; n < n_hi; ++n) {
-        if (!(plant & PLANT_NO_RESET)) load_init(S, S_init, n, H, h, d, plant);
-        double* fin = S_final ? S_final + ((size_t)n * H + h) * (size_t)d * d : NULL;
+        if (!(plant & PLANT_NO_RESET)) load_init_rect(S, S_init, n, H, h, dk, dv, plant);
+        double* fin = S_final ? S_final + ((size_t)n * H + h) * sz : NULL;
         for (int64_t t = cu_seqlens[n]; t < cu_seqlens[n + 1]; ++t) {
           if (fin && (plant & PLANT_FINAL_EARLY) && t == cu_seqlens[n + 1] - 1)
-            memcpy(fin, S, sizeof(double) * (size_t)d * d);
+            memcpy(fin, S, sizeof(double) * sz);
           if ((plant & PLANT_DROP_CARRY_64) && ((t - cu_seqlens[n]) % 64) == 0)
-            memset(S, 0, sizeof(double) * (size_t)d * d);
-          const int64_t o = (t * H + h) * (int64_t)d;
+            memset(S, 0, sizeof(double) * sz);
+          const int64_t ok_ = (t * H + h) * (int64_t)dk; /* q, k, f rows */
+          const int64_t ov = (t * H + h) * (int64_t)dv;  /* v, out rows */
           if (plant & PLANT_NO_L2NORM) {
-            memcpy(qn, q + o, sizeof(double) * d);
-            memcpy(kn, k + o, sizeof(double) * d);
+            memcpy(qn, q + ok_, sizeof(double) * dk);
+            memcpy(kn, k + ok_, sizeof(double) * dk);
           } else {
-            l2norm(q + o, d, eps, qn);
-            l2norm(k + o, d, eps, kn);
+            l2norm(q + ok_, dk, eps, qn);
+            l2norm(k + ok_, dk, eps, kn);
           }
-          gate(f + o, A_log[h], dt_bias + (int64_t)h * d, d, plant, g);
+          gate(f + ok_, A_log[h], dt_bias + (int64_t)h * dk, dk, plant, g);
           double beta = (plant & PLANT_NO_BETA) ? 1.0 : sigmoid(b[t * H + h]);
-          if (Sprev) memcpy(Sprev, S, sizeof(double) * (size_t)d * d);
+          if (Sprev) memcpy(Sprev, S, sizeof(double) * sz);
           /* S <- Diag(exp(g)) S : row i of S (key channel i) scales by exp(g_i). */
           if (!(plant & PLANT_NO_DECAY)) {
-            for (int i = 0; i < d; ++i) {
+            for (int i = 0; i < dk; ++i) {
               double e = (plant & PLANT_GATE_SIGN) ? exp(-g[i]) : exp(g[i]);
-              for (int j = 0; j < d; ++j) S[i * d + j] *= e;
+              for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= e;
             }
           }
-          double* o_t = out + o;
+          double* o_t = out + ov;
           if (plant & PLANT_READ_BEFORE_WRITE) {
-            for (int j = 0; j < d; ++j) {
+            for (int j = 0; j < dv; ++j) {
               double acc = 0.0;
-              for (int i = 0; i < d; ++i) acc += S[i * d + j] * qn[i];
+              for (int i = 0; i < dk; ++i) acc += S[(size_t)i * dv + j] * qn[i];
               o_t[j] = ((plant & PLANT_NO_SCALE) ? 1.0 : scale) * acc;
             }
           }
           /* u = v - S^T k  (S^T k)_j = sum_i S[i][j] k_i, on the decayed S. */
           const double* Sd = Sprev ? Sprev : S;
-          for (int j = 0; j < d; ++j) {
+          for (int j = 0; j < dv; ++j) {
             double acc = 0.0;
-            for (int i = 0; i < d; ++i) acc += Sd[i * d + j] * kn[i];
-            u[j] = (plant & PLANT_DELTA_SIGN) ? v[o + j] + acc : v[o + j] - acc;
+            for (int i = 0; i < dk; ++i) acc += Sd[(size_t)i * dv + j] * kn[i];
+            u[j] = (plant & PLANT_DELTA_SIGN) ? v[ov + j] + acc : v[ov + j] - acc;
           }
           /* S += beta k u^T */
-          if (plant & PLANT_OUTER_SWAP) {
-            for (int i = 0; i < d; ++i)
-              for (int j = 0; j < d; ++j) S[i * d + j] += beta * u[i] * kn[j];
+          if ((plant & PLANT_OUTER_SWAP) && square) {
+            for (int i = 0; i < dk; ++i)
+              for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] += beta * u[i] * kn[j];
           } else {
-            for (int i = 0; i < d; ++i) {
+            for (int i = 0; i < dk; ++i) {
               double bk = beta * kn[i];
-              for (int j = 0; j < d; ++j) S[i * d + j] += bk * u[j];
+              for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] += bk * u[j];
             }
           }
           if (!(plant & PLANT_READ_BEFORE_WRITE)) {
             /* o_t = scale S^T q */
-            for (int j = 0; j < d; ++j) {
+            for (int j = 0; j < dv; ++j) {
               double acc = 0.0;
-              if (plant & PLANT_TRANSPOSED_READ)
-                for (int i = 0; i < d; ++i) acc += S[j * d + i] * qn[i];
+              if ((plant & PLANT_TRANSPOSED_READ) && square)
+                for (int i = 0; i < dk; ++i) acc += S[(size_t)j * dv + i] * qn[i];
               else
-                for (int i = 0; i < d; ++i) acc += S[i * d + j] * qn[i];
+                for (int i = 0; i < dk; ++i) acc += S[(size_t)i * dv + j] * qn[i];
               o_t[j] = ((plant & PLANT_NO_SCALE) ? 1.0 : scale) * acc;
             }
           }
         }
         if (fin && !((plant & PLANT_FINAL_EARLY) && cu_seqlens[n + 1] > cu_seqlens[n]))
-          memcpy(fin, S, sizeof(double) * (size_t)d * d);
+          memcpy(fin, S, sizeof(double) * sz);
       }
     }
     free(S); free(qn); free(kn); free(g); free(u); free(Sprev);

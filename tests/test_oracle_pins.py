@@ -403,3 +403,67 @@ def test_chunk_records_consistent():
             assert np.allclose((np.eye(n) + A) @ rec["W"][c, h][:n], rhs, atol=1e-13)
             assert np.allclose(rec["Gamma"][c, h], np.exp(G[-1]), rtol=1e-14)
     assert np.allclose(rec["S0"][0], 0.0)
+
+
+# --------------------------------------------------------------------------
+# Rectangular state (d_k != d_v): reduced to the square recurrence by
+# zero-padding, which adds only exact zeros to every sum.
+# --------------------------------------------------------------------------
+
+def _rect_inputs(T, H, dk, dv, seed, cu):
+    r = _rng(seed)
+    return dict(q=r.standard_normal((T, H, dk)), k=r.standard_normal((T, H, dk)),
+                v=r.standard_normal((T, H, dv)), f_raw=r.standard_normal((T, H, dk)),
+                b_raw=r.standard_normal((T, H)), A_log=r.uniform(0, math.log(16), H),
+                dt_bias=0.5 * r.standard_normal((H, dk)), cu_seqlens=np.asarray(cu, dtype=np.int32))
+
+
+def _pad(a, n, axis=-1):
+    w = [(0, 0)] * a.ndim
+    w[axis] = (0, n - a.shape[axis])
+    return np.pad(a, w)
+
+
+def test_rect_pad_keys_to_square():
+    """dk = 16 < dv = 24 (the pages' failing rectangular case): padding q, k,
+    f_raw, dt_bias (and the start state's key rows) with zeros to 24 gives the
+    square recurrence the same outputs and final state."""
+    cu = [0, 5, 5, 40]
+    x = _rect_inputs(40, 2, 16, 24, 91, cu)
+    S0 = _rng(92).standard_normal((3, 2, 16, 24))
+    out, fin = oracle.kda_forward_rect(**x, scale=0.25, initial_state=S0, return_final_state=True)
+    sq = dict(x)
+    for key in ("q", "k", "f_raw"):
+        sq[key] = _pad(x[key], 24)
+    sq["dt_bias"] = _pad(x["dt_bias"], 24)
+    out2, fin2 = oracle.kda_forward(**sq, scale=0.25, initial_state=_pad(S0, 24, axis=2),
+                                    return_final_state=True)
+    assert np.allclose(out, out2, rtol=1e-14, atol=1e-15)
+    assert np.allclose(fin, fin2[:, :, :16, :], rtol=1e-14, atol=1e-15)
+    assert np.all(fin2[:, :, 16:, :] == 0.0)
+
+
+def test_rect_pad_values_to_square():
+    """dk = 32 > dv = 16: padding v (and the start state's value columns) with
+    zeros to 32 adds zero output columns and leaves the others unchanged."""
+    cu = [0, 33, 70]
+    x = _rect_inputs(70, 2, 32, 16, 93, cu)
+    S0 = _rng(94).standard_normal((2, 2, 32, 16))
+    out, fin = oracle.kda_forward_rect(**x, initial_state=S0, return_final_state=True)
+    sq = dict(x)
+    sq["v"] = _pad(x["v"], 32)
+    out2, fin2 = oracle.kda_forward(**sq, scale=1 / math.sqrt(32), initial_state=_pad(S0, 32, axis=3),
+                                    return_final_state=True)
+    assert np.allclose(out, out2[..., :16], rtol=1e-14, atol=1e-15)
+    assert np.all(out2[..., 16:] == 0.0)
+    assert np.allclose(fin, fin2[..., :16], rtol=1e-14, atol=1e-15)
+
+
+def test_rect_single_token_closed_form():
+    x = _rect_inputs(1, 3, 16, 24, 95, [0, 1])
+    out = oracle.kda_forward_rect(**x, eps=0.0)
+    for h in range(3):
+        qn = x["q"][0, h] / np.linalg.norm(x["q"][0, h])
+        kn = x["k"][0, h] / np.linalg.norm(x["k"][0, h])
+        beta = 1 / (1 + math.exp(-x["b_raw"][0, h]))
+        assert np.allclose(out[0, h], 0.25 * beta * (kn @ qn) * x["v"][0, h], rtol=1e-13, atol=1e-15)

@@ -242,41 +242,76 @@ extern "C" int kda_chunk_fwd_conv(const void* q, const void* k, const void* v, c
                   conv_bias, conv_silu, stream, nullptr, 0);
 }
 
-extern "C" int kda_recurrent_fwd(const void* q, const void* k, const void* v, const void* f_raw,
-                                 const void* b_raw, const float* A_log, const float* dt_bias,
-                                 const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
-                                 int32_t H, int32_t d, uint32_t mode, void* out,
-                                 const float* initial_state, float* final_state, void* stream) {
+template <int DK>
+static void launch_recurrent(const kda::RecArgs& ra, bool a32, bool o32, hipStream_t s) {
+  const int need = DK > ra.dv ? DK : ra.dv;
+  const dim3 grid((unsigned)((int64_t)ra.N * ra.H)), block((unsigned)(64 * ((need + 63) / 64)));
+  if (!a32 && !o32)
+    hipLaunchKernelGGL((kda::kda_recurrent_kernel<kda::bf16, kda::bf16, DK>), grid, block, 0, s, ra);
+  else if (!a32)
+    hipLaunchKernelGGL((kda::kda_recurrent_kernel<kda::bf16, float, DK>), grid, block, 0, s, ra);
+  else
+    hipLaunchKernelGGL((kda::kda_recurrent_kernel<float, float, DK>), grid, block, 0, s, ra);
+}
+
+static int recurrent_impl(const void* q, const void* k, const void* v, const void* f_raw,
+                          const void* b_raw, const float* A_log, const float* dt_bias,
+                          const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                          int32_t H, int32_t dk, int32_t dv, uint32_t mode, void* out,
+                          const float* initial_state, float* final_state, void* stream) {
   if (mode & ~KDA_MODE_ALL_BITS) return KDA_ERR_INVALID_ARG;
-  if (num_seqs < 1 || total_tokens < 0 || H < 1) return KDA_ERR_INVALID_ARG;
-  if (d != kda::DH) return KDA_ERR_UNSUPPORTED;
+  if (num_seqs < 1 || total_tokens < 0 || H < 1 || dk < 1 || dv < 1) return KDA_ERR_INVALID_ARG;
+  if ((dk != 16 && dk != 32 && dk != 64 && dk != 128) || dv > kda::rec_max_threads(dk))
+    return KDA_ERR_UNSUPPORTED;
   if ((int64_t)num_seqs * H > (int64_t)INT32_MAX / 2) return KDA_ERR_UNSUPPORTED;
   if (total_tokens == 0 && !final_state) return KDA_OK;
   if (total_tokens > 0 && (!q || !k || !v || !f_raw || !b_raw || !A_log || !dt_bias || !out ||
                            !cu_seqlens))
     return KDA_ERR_INVALID_ARG;
-  kda::RecArgs ra;
-  ra.q = q; ra.k = k; ra.v = v; ra.f = f_raw; ra.b = b_raw; ra.A_log = A_log; ra.dt_bias = dt_bias;
-  ra.cu = cu_seqlens; ra.init = initial_state; ra.fin = final_state; ra.out = out;
-  ra.N = num_seqs; ra.H = H; ra.eps = 1e-6f; ra.scale = 0.08838834764831845f;  // 1/sqrt(128)
-  const bool a32 = mode & KDA_ACT_FP32;
-  const bool o32 = (mode & KDA_OUT_FP32) || a32;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  const dim3 grid((unsigned)((int64_t)num_seqs * H)), block(128);
-  if (total_tokens == 0) {
-    const int64_t n = (int64_t)num_seqs * H * kda::DH * kda::DH;
+  if (total_tokens == 0) {  // final = initial state (zero if none)
+    const int64_t n = (int64_t)num_seqs * H * dk * dv;
     const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
     hipLaunchKernelGGL(kda::kda_state_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
                        initial_state, final_state, n);
-  } else if (!a32 && !o32) {
-    hipLaunchKernelGGL((kda::kda_recurrent_kernel<kda::bf16, kda::bf16>), grid, block, 0, s, ra);
-  } else if (!a32) {
-    hipLaunchKernelGGL((kda::kda_recurrent_kernel<kda::bf16, float>), grid, block, 0, s, ra);
-  } else {
-    hipLaunchKernelGGL((kda::kda_recurrent_kernel<float, float>), grid, block, 0, s, ra);
+    return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  }
+  kda::RecArgs ra;
+  ra.q = q; ra.k = k; ra.v = v; ra.f = f_raw; ra.b = b_raw; ra.A_log = A_log; ra.dt_bias = dt_bias;
+  ra.cu = cu_seqlens; ra.init = initial_state; ra.fin = final_state; ra.out = out;
+  ra.N = num_seqs; ra.H = H; ra.dv = dv; ra.eps = 1e-6f;
+  ra.scale = 1.0f / sqrtf((float)dk);
+  const bool a32 = mode & KDA_ACT_FP32;
+  const bool o32 = (mode & KDA_OUT_FP32) || a32;
+  switch (dk) {
+    case 16: launch_recurrent<16>(ra, a32, o32, s); break;
+    case 32: launch_recurrent<32>(ra, a32, o32, s); break;
+    case 64: launch_recurrent<64>(ra, a32, o32, s); break;
+    default: launch_recurrent<128>(ra, a32, o32, s); break;
   }
   return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+extern "C" int kda_recurrent_fwd(const void* q, const void* k, const void* v, const void* f_raw,
+                                 const void* b_raw, const float* A_log, const float* dt_bias,
+                                 const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                                 int32_t H, int32_t d, uint32_t mode, void* out,
+                                 const float* initial_state, float* final_state, void* stream) {
+  if (d != kda::DH) return d < 1 ? KDA_ERR_INVALID_ARG : KDA_ERR_UNSUPPORTED;
+  return recurrent_impl(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, num_seqs, total_tokens,
+                        H, d, d, mode, out, initial_state, final_state, stream);
+}
+
+extern "C" int kda_recurrent_fwd_rect(const void* q, const void* k, const void* v,
+                                      const void* f_raw, const void* b_raw, const float* A_log,
+                                      const float* dt_bias, const int32_t* cu_seqlens,
+                                      int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t dk,
+                                      int32_t dv, uint32_t mode, void* out,
+                                      const float* initial_state, float* final_state,
+                                      void* stream) {
+  return recurrent_impl(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, num_seqs, total_tokens,
+                        H, dk, dv, mode, out, initial_state, final_state, stream);
 }
 
 extern "C" const char* kda_status_string(int status) {

@@ -24,7 +24,8 @@ KDA_OUT_FP32 = 0x4
 
 # Exported symbols, in declaration order of include/kda.h.
 SYMBOLS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_state",
-           "kda_chunk_fwd_conv", "kda_recurrent_fwd", "kda_chunk_fwd_num_stages",
+           "kda_chunk_fwd_conv", "kda_recurrent_fwd", "kda_recurrent_fwd_rect",
+           "kda_chunk_fwd_num_stages",
            "kda_chunk_fwd_timed", "kda_status_string")
 
 _lib = None
@@ -66,6 +67,10 @@ def load_library(path: str = LIB_PATH):
     lib.kda_recurrent_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32,
                                       ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_uint32, vp, vp, vp, vp]
+    lib.kda_recurrent_fwd_rect.restype = ctypes.c_int
+    lib.kda_recurrent_fwd_rect.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32,
+                                           ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_uint32, vp, vp, vp, vp]
     lib.kda_chunk_fwd_timed.restype = ctypes.c_int
     lib.kda_chunk_fwd_timed.argtypes = fwd_args + [ctypes.POINTER(vp), ctypes.c_int32]
     lib.kda_chunk_fwd_num_stages.restype = ctypes.c_int
@@ -215,7 +220,9 @@ def recurrent_fwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, out_fp32=Fa
     """Token-serial KDA forward through libkda (kda_recurrent_fwd): FP32 state,
     one token at a time; for decode steps and short sequences.  Tensors as for
     chunk_fwd; returns out, or (out, final_state) when a final state is asked
-    for (``final_state`` tensor to fill, or ``return_final_state=True``)."""
+    for (``final_state`` tensor to fill, or ``return_final_state=True``).
+    q, k, f_raw [T, H, dk] with v [T, H, dv], dv != dk, select
+    kda_recurrent_fwd_rect (rectangular state [N, H, dk, dv])."""
     import torch
 
     lib = load_library()
@@ -229,22 +236,23 @@ def recurrent_fwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, out_fp32=Fa
         raise TypeError("A_log and dt_bias must be float32")
     if cu_seqlens.dtype != torch.int32:
         raise TypeError("cu_seqlens must be int32")
-    T, H, d = q.shape
+    T, H, dk = q.shape
+    dv = v.shape[2]
     for t in (q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens):
         if not t.is_contiguous() or not t.is_cuda:
             raise ValueError("all tensors must be contiguous device tensors")
-    if k.shape != q.shape or v.shape != q.shape or f_raw.shape != q.shape:
-        raise ValueError("q, k, v, f_raw must have one shape [T, H, d]")
-    if b_raw.shape != (T, H) or A_log.shape != (H,) or dt_bias.shape != (H, d):
-        raise ValueError("b_raw [T,H], A_log [H], dt_bias [H,d] expected")
+    if k.shape != q.shape or f_raw.shape != q.shape or v.shape != (T, H, dv):
+        raise ValueError("q, k, f_raw must be [T, H, dk] and v [T, H, dv]")
+    if b_raw.shape != (T, H) or A_log.shape != (H,) or dt_bias.shape != (H, dk):
+        raise ValueError("b_raw [T,H], A_log [H], dt_bias [H,dk] expected")
     num_seqs = cu_seqlens.numel() - 1
     mode = make_mode(False, act_fp32, out_fp32)
     out_dtype = torch.float32 if (out_fp32 or act_fp32) else q.dtype
     if out is None:
-        out = torch.empty((T, H, d), dtype=out_dtype, device=q.device)
-    elif out.dtype != out_dtype or out.shape != (T, H, d) or not out.is_contiguous():
+        out = torch.empty((T, H, dv), dtype=out_dtype, device=q.device)
+    elif out.dtype != out_dtype or out.shape != (T, H, dv) or not out.is_contiguous():
         raise ValueError("out has the wrong dtype, shape or layout")
-    sshape = (num_seqs, H, d, d)
+    sshape = (num_seqs, H, dk, dv)
     for t in (initial_state, final_state):
         if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != sshape
                               or not t.is_contiguous() or not t.is_cuda):
@@ -253,10 +261,14 @@ def recurrent_fwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, out_fp32=Fa
         final_state = torch.empty(sshape, dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    st = lib.kda_recurrent_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(f_raw), _ptr(b_raw), _ptr(A_log),
-                               _ptr(dt_bias), _ptr(cu_seqlens), num_seqs, T, H, d, mode, _ptr(out),
-                               _ptr(initial_state), _ptr(final_state),
-                               ctypes.c_void_p(stream.cuda_stream))
+    common = (_ptr(q), _ptr(k), _ptr(v), _ptr(f_raw), _ptr(b_raw), _ptr(A_log), _ptr(dt_bias),
+              _ptr(cu_seqlens), num_seqs, T, H)
+    tail = (mode, _ptr(out), _ptr(initial_state), _ptr(final_state),
+            ctypes.c_void_p(stream.cuda_stream))
+    if dk == dv:
+        st, where = lib.kda_recurrent_fwd(*common, dk, *tail), "kda_recurrent_fwd"
+    else:
+        st, where = lib.kda_recurrent_fwd_rect(*common, dk, dv, *tail), "kda_recurrent_fwd_rect"
     if st != KDA_OK:
-        raise KdaError(st, "kda_recurrent_fwd")
+        raise KdaError(st, where)
     return (out, final_state) if final_state is not None else out

@@ -177,6 +177,20 @@ KDA_API int kda_recurrent_fwd(const void* q, const void* k, const void* v, const
                       int32_t H, int32_t d, uint32_t mode, void* out,
                       const float* initial_state, float* final_state, void* stream);
 
+/* kda_recurrent_fwd with a rectangular state: dk key channels (q, k, f_raw
+ * [T][H][dk], dt_bias [H][dk]) and dv value channels (v, out [T][H][dv]);
+ * states [num_seqs][H][dk][dv]; the output scale is 1/sqrt(dk).  Supported:
+ * dk in {16, 32, 64, 128} (else KDA_ERR_UNSUPPORTED), 1 <= dv <= 512 for
+ * dk <= 64 and dv <= 128 for dk = 128 (larger: KDA_ERR_UNSUPPORTED).  The pages record the rectangular case dk = 16,
+ * dv = 24 failing to compile in their TileLang kernels (xtuner PR #2301,
+ * section Validation); here it runs on the token-serial path.  Everything
+ * else as for kda_recurrent_fwd. */
+KDA_API int kda_recurrent_fwd_rect(const void* q, const void* k, const void* v, const void* f_raw,
+                           const void* b_raw, const float* A_log, const float* dt_bias,
+                           const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                           int32_t H, int32_t dk, int32_t dv, uint32_t mode, void* out,
+                           const float* initial_state, float* final_state, void* stream);
+
 /* Number of kernels kda_chunk_fwd launches for this mode (the stages timed by
  * kda_chunk_fwd_timed). */
 KDA_API int kda_chunk_fwd_num_stages(uint32_t mode);

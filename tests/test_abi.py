@@ -89,6 +89,12 @@ def test_argument_errors_before_launch():
     assert rc(mode=0x10) == kda.KDA_ERR_INVALID_ARG
     assert rc(d=64) == kda.KDA_ERR_UNSUPPORTED
     assert rc(T=0, p=None) == kda.KDA_OK  # nothing to compute or copy
+    rr = lambda dk, dv: lib.kda_recurrent_fwd_rect(*([p] * 8), 1, 10, 4, dk, dv, 0, p, None, None,
+                                                   None)
+    assert rr(48, 24) == kda.KDA_ERR_UNSUPPORTED   # key length not built
+    assert rr(128, 200) == kda.KDA_ERR_UNSUPPORTED  # too many value channels for dk = 128
+    assert rr(16, 600) == kda.KDA_ERR_UNSUPPORTED
+    assert rr(16, 0) == kda.KDA_ERR_INVALID_ARG
 
 
 def test_workspace_query():

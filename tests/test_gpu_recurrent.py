@@ -133,3 +133,47 @@ def test_recurrent_in_place_and_empty():
     _, fin = kda.recurrent_fwd(*empty, initial_state=S2, return_final_state=True)
     torch.cuda.synchronize()
     assert torch.equal(fin, S2)
+
+
+def _rect_inputs(cu, H, dk, dv, seed, act):
+    r = np.random.default_rng(seed)
+    T = cu[-1]
+
+    def act_round(a):
+        a = a.astype(np.float32)
+        return synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(a)) if act == "bf16" else a
+    x = dict(q=act_round(r.standard_normal((T, H, dk))), k=act_round(r.standard_normal((T, H, dk))),
+             v=act_round(r.standard_normal((T, H, dv))), f_raw=act_round(r.standard_normal((T, H, dk))),
+             b_raw=act_round(r.standard_normal((T, H))),
+             A_log=r.uniform(0, np.log(16), H).astype(np.float32),
+             dt_bias=(0.5 * r.standard_normal((H, dk))).astype(np.float32),
+             cu_seqlens=np.asarray(cu, dtype=np.int32))
+    return x
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 24), (32, 16), (64, 100), (128, 64), (16, 512)])
+def test_recurrent_rectangular_state(dk, dv):
+    """Rectangular states (the pages' failing case is dk = 16, dv = 24), packed
+    sequences with start states, bf16 activations, against the FP64 oracle."""
+    import torch
+
+    from chunked_gated_delta_07_amd import kda
+
+    cu = [0, 3, 3, 70]
+    H = 2
+    x = _rect_inputs(cu, H, dk, dv, 100 + dk + dv, "bf16")
+    S0 = (0.5 * np.random.default_rng(7).standard_normal((3, H, dk, dv))).astype(np.float32)
+    dev = lambda a, bf: (torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16) if bf
+                         else torch.from_numpy(np.ascontiguousarray(a))).cuda()
+    args = [dev(x["q"], True), dev(x["k"], True), dev(x["v"], True), dev(x["f_raw"], True),
+            dev(x["b_raw"], True), dev(x["A_log"], False), dev(x["dt_bias"], False),
+            dev(x["cu_seqlens"], False)]
+    out, fin = kda.recurrent_fwd(*args, out_fp32=True, initial_state=dev(S0, False),
+                                 return_final_state=True)
+    torch.cuda.synchronize()
+    ref, fref = oracle.kda_forward_rect(**x, initial_state=S0.astype(np.float64),
+                                        return_final_state=True)
+    ro = U.rel_l2(out.double().cpu().numpy(), ref)
+    rf = U.rel_l2(fin.double().cpu().numpy(), fref)
+    print(f"[recurrent rect dk={dk} dv={dv}] out rel={ro:.3e} final rel={rf:.3e}", flush=True)
+    assert ro <= U.TOL_FP32_REL and rf <= U.TOL_FP32_REL

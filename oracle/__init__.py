@@ -42,6 +42,13 @@ PLANT = {
     "init_transposed": 1 << 13,
     "final_early": 1 << 14,
 }
+# Deliberate mistakes of the backward (kda_oracle_bwd_rect).
+BWD_PLANT = {
+    "bwd_beta_scale": 1 << 17,
+    "bwd_no_state_decay": 1 << 18,
+    "bwd_no_norm_proj": 1 << 19,
+    "bwd_gate_no_sigmoid": 1 << 20,
+}
 # Deliberate mistakes of the short convolution (kda_oracle_short_conv).
 CONV_PLANT = {
     "conv_no_reset": 1 << 15,
@@ -92,6 +99,11 @@ def _load():
     lib.kda_oracle_short_conv.argtypes = [dp, ip, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
                                           ctypes.c_int, dp, dp, ctypes.c_int, ctypes.c_int,
                                           ctypes.c_int, ctypes.c_uint]
+    lib.kda_oracle_bwd_rect.restype = ctypes.c_int
+    lib.kda_oracle_bwd_rect.argtypes = [dp, dp, dp, dp, dp, dp, dp, ip, ctypes.c_int,
+                                        ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_double, ctypes.c_double, ctypes.c_uint, dp, dp,
+                                        dp, dp, dp, dp, dp, dp, dp, dp, dp]
     lib.kda_oracle_num_threads.restype = ctypes.c_int
     lib.kda_oracle_num_threads.argtypes = []
     _lib = lib
@@ -254,6 +266,45 @@ def short_conv(x, cu_seqlens, weight, bias=None, silu=True, round_bf16=False, pl
     if rc != 0:
         raise ValueError("kda_oracle_short_conv rejected its arguments")
     return y
+
+
+def kda_backward(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, dout, scale=None, eps=1e-6,
+                 initial_state=None, dfinal_state=None, plant=0):
+    """FP64 vector-Jacobian product of the token recurrence (rectangular state
+    allowed: q, k, f_raw [T, H, dk], v and dout [T, H, dv]).  For the loss
+    L = <dout, out> + <dfinal_state, final_state> it returns a dict with dq,
+    dk, dv, df (= dL/df_raw), db (= dL/db_raw), dA_log [H], ddt_bias [H, dk]
+    and dinit [N, H, dk, dv] (dL/d initial state; zero start if none given)."""
+    lib = _load()
+    q, k, v, f_raw, b_raw, A_log, dt_bias, dout = map(
+        _f64, (q, k, v, f_raw, b_raw, A_log, dt_bias, dout))
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    assert k.shape == q.shape and f_raw.shape == q.shape and v.shape == (T, H, dv)
+    assert dout.shape == (T, H, dv)
+    assert b_raw.shape == (T, H) and A_log.shape == (H,) and dt_bias.shape == (H, dk)
+    N = len(cu) - 1
+    if scale is None:
+        scale = 1.0 / np.sqrt(dk)
+    init = None if initial_state is None else _f64(initial_state)
+    dfin = None if dfinal_state is None else _f64(dfinal_state)
+    for x in (init, dfin):
+        if x is not None:
+            assert x.shape == (N, H, dk, dv), x.shape
+    r = {"dq": np.zeros((T, H, dk)), "dk": np.zeros((T, H, dk)), "dv": np.zeros((T, H, dv)),
+         "df": np.zeros((T, H, dk)), "db": np.zeros((T, H)), "dA_log": np.zeros(H),
+         "ddt_bias": np.zeros((H, dk)), "dinit": np.zeros((N, H, dk, dv))}
+    opt = lambda x: _ptr(x) if x is not None else None
+    rc = lib.kda_oracle_bwd_rect(_ptr(q), _ptr(k), _ptr(v), _ptr(f_raw), _ptr(b_raw), _ptr(A_log),
+                                 _ptr(dt_bias), _ptr(cu, ctypes.c_int32), N, T, H, dk, dv,
+                                 float(scale), float(eps), int(plant), opt(init), _ptr(dout),
+                                 opt(dfin), _ptr(r["dq"]), _ptr(r["dk"]), _ptr(r["dv"]),
+                                 _ptr(r["df"]), _ptr(r["db"]), _ptr(r["dA_log"]),
+                                 _ptr(r["ddt_bias"]), _ptr(r["dinit"]))
+    if rc != 0:
+        raise ValueError("kda_oracle_bwd_rect rejected its arguments")
+    return r
 
 
 def num_threads() -> int:

@@ -80,7 +80,12 @@ enum {
   PLANT_INIT_TRANSPOSED = 1u << 13,  /* initial state read as S_init^T          */
   PLANT_FINAL_EARLY = 1u << 14,      /* final state taken before the last token */
   PLANT_CONV_NO_RESET = 1u << 15,    /* convolution history crosses sequences   */
-  PLANT_CONV_TAPS_REVERSED = 1u << 16 /* taps applied in reverse order           */
+  PLANT_CONV_TAPS_REVERSED = 1u << 16, /* taps applied in reverse order          */
+  /* mistakes of the backward (kda_oracle_bwd_rect) */
+  PLANT_BWD_BETA_SCALE = 1u << 17,   /* beta gradient scaled by 1.25            */
+  PLANT_BWD_NO_STATE_DECAY = 1u << 18, /* dS passed back without Diag(exp g)    */
+  PLANT_BWD_NO_NORM_PROJ = 1u << 19, /* dq = dq^ / |q|, radial term dropped      */
+  PLANT_BWD_GATE_NO_SIGMOID = 1u << 20 /* softplus' taken as 1                   */
 };
 
 static double softplus(double x) {
@@ -500,6 +505,196 @@ int kda_oracle_short_conv(double* x, const int32_t* cu_seqlens, int N, int64_t T
     free(hist);
   }
   return 0;
+}
+
+/* Vector-Jacobian product of the token recurrence above (reverse-mode
+ * differentiation of exactly the steps kda_oracle_fwd_rect takes; the pages
+ * check the chunked operator's gradients for q, k, v, the gate and beta
+ * against such an independent FP64 recurrence VJP: xtuner PR #2301, section
+ * Validation; PR #2153, KDA module description, for the gradients of the FP32
+ * A_log / dt_bias parameters and the initial state of a shard).
+ *
+ * Given dout = dL/dout [T][H][dv] and optionally dS_final = dL/dS_final
+ * [N][H][dk][dv], returns dL/d(input) for L = <dout, out> + <dS_final, S_final>:
+ *   dq, dk, df [T][H][dk];  dv [T][H][dv];  db [T][H];  dA_log [H];
+ *   ddt_bias [H][dk];  dS_init [N][H][dk][dv] (if non-NULL; the gradient of the
+ *   start state, whether S_init was given or the start was zero).
+ * Every output is overwritten.  Per token, in reverse order, with S_t stored
+ * by a forward sweep and Sd = Diag(a) S_{t-1}, u = v - Sd^T k^, a = exp(g):
+ *   dq^ = scale S_t dout_t;        dS += scale q^ dout_t^T
+ *   du = beta dS^T k^;             dbeta = k^^T dS u;   dk^ = beta dS u
+ *   dv = du;  dSd = dS - k^ du^T;  dk^ -= Sd du
+ *   da_i = sum_j dSd_ij S_{t-1,ij};  dS <- Diag(a) dSd;  dg = a * da
+ *   x = f + dt_bias:  dx = -exp(A_log) sigmoid(x) dg;  df = dx;  ddt_bias += dx
+ *   dA_log += sum_c dg_c g_c   (g is linear in exp(A_log))
+ *   db = dbeta beta (1 - beta)
+ *   dq = (dq^ - q^ (q^ . dq^)) / sqrt(|q|^2 + eps), dk likewise.
+ * Memory: the forward sweep keeps all states of one (sequence, head), i.e.
+ * (L+1) dk dv doubles per worker thread.  Returns 0, or -1 on bad args. */
+int kda_oracle_bwd_rect(const double* q, const double* k, const double* v, const double* f,
+                        const double* b, const double* A_log, const double* dt_bias,
+                        const int32_t* cu_seqlens, int N, int64_t T, int H, int dk, int dv,
+                        double scale, double eps, unsigned plant, const double* S_init,
+                        const double* dout, const double* dS_final, double* dq, double* dkk,
+                        double* dvv, double* df, double* db, double* dA_log, double* ddt_bias,
+                        double* dS_init) {
+  if (N < 1 || H < 1 || dk < 1 || dv < 1) return -1;
+  if (cu_seqlens[0] != 0 || cu_seqlens[N] != T) return -1;
+  for (int n = 0; n < N; ++n)
+    if (cu_seqlens[n + 1] < cu_seqlens[n]) return -1;
+  const int64_t units = (int64_t)N * H;
+  const size_t sz = (size_t)dk * dv;
+  /* per-unit partial parameter gradients, summed in a fixed order afterwards */
+  double* part = (double*)calloc((size_t)units * (dk + 1), sizeof(double));
+  if (!part) return -1;
+  int fail = 0;
+
+#pragma omp parallel
+  {
+    double* qn = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* kn = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* g = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* a = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* u = (double*)malloc(sizeof(double) * (size_t)dv);
+    double* du = (double*)malloc(sizeof(double) * (size_t)dv);
+    double* dqn = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* dkn = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* Sd = (double*)malloc(sizeof(double) * sz);
+    double* dS = (double*)malloc(sizeof(double) * sz);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t w = 0; w < units; ++w) {
+      const int n = (int)(w / H), h = (int)(w % H);
+      const int64_t t0 = cu_seqlens[n], L = cu_seqlens[n + 1] - t0;
+      double* St = (double*)malloc(sizeof(double) * sz * (size_t)(L + 1));
+      if (!St) {
+#pragma omp atomic write
+        fail = 1;
+        continue;
+      }
+      const double lam = exp(A_log[h]);
+      const double* dtb = dt_bias + (int64_t)h * dk;
+      /* forward sweep: St[s] = state after s tokens of the sequence */
+      load_init_rect(St, S_init, n, H, h, dk, dv, 0u);
+      for (int64_t s = 0; s < L; ++s) {
+        const int64_t t = t0 + s;
+        const int64_t ok_ = (t * H + h) * (int64_t)dk, ov = (t * H + h) * (int64_t)dv;
+        l2norm(q + ok_, dk, eps, qn);
+        l2norm(k + ok_, dk, eps, kn);
+        gate(f + ok_, A_log[h], dtb, dk, 0u, g);
+        const double beta = sigmoid(b[t * H + h]);
+        const double* Sp = St + sz * (size_t)s;
+        double* Sn = St + sz * (size_t)(s + 1);
+        for (int i = 0; i < dk; ++i) {
+          const double e = exp(g[i]);
+          for (int j = 0; j < dv; ++j) Sn[(size_t)i * dv + j] = e * Sp[(size_t)i * dv + j];
+        }
+        for (int j = 0; j < dv; ++j) {
+          double acc = 0.0;
+          for (int i = 0; i < dk; ++i) acc += Sn[(size_t)i * dv + j] * kn[i];
+          u[j] = v[ov + j] - acc;
+        }
+        for (int i = 0; i < dk; ++i)
+          for (int j = 0; j < dv; ++j) Sn[(size_t)i * dv + j] += beta * kn[i] * u[j];
+      }
+      /* reverse sweep */
+      if (dS_final) memcpy(dS, dS_final + ((size_t)n * H + h) * sz, sizeof(double) * sz);
+      else memset(dS, 0, sizeof(double) * sz);
+      double* pp = part + (size_t)w * (dk + 1);
+      for (int64_t s = L - 1; s >= 0; --s) {
+        const int64_t t = t0 + s;
+        const int64_t ok_ = (t * H + h) * (int64_t)dk, ov = (t * H + h) * (int64_t)dv;
+        double ssq = 0.0, ssk = 0.0;
+        for (int c = 0; c < dk; ++c) { ssq += q[ok_ + c] * q[ok_ + c]; ssk += k[ok_ + c] * k[ok_ + c]; }
+        const double rq = 1.0 / sqrt(ssq + eps), rk = 1.0 / sqrt(ssk + eps);
+        for (int c = 0; c < dk; ++c) { qn[c] = q[ok_ + c] * rq; kn[c] = k[ok_ + c] * rk; }
+        gate(f + ok_, A_log[h], dtb, dk, 0u, g);
+        for (int i = 0; i < dk; ++i) a[i] = exp(g[i]);
+        const double beta = sigmoid(b[t * H + h]);
+        const double* Sp = St + sz * (size_t)s;        /* S_{t-1} */
+        const double* Sc = St + sz * (size_t)(s + 1);  /* S_t     */
+        for (int i = 0; i < dk; ++i)
+          for (int j = 0; j < dv; ++j) Sd[(size_t)i * dv + j] = a[i] * Sp[(size_t)i * dv + j];
+        for (int j = 0; j < dv; ++j) {
+          double acc = 0.0;
+          for (int i = 0; i < dk; ++i) acc += Sd[(size_t)i * dv + j] * kn[i];
+          u[j] = v[ov + j] - acc;
+        }
+        const double* go = dout + ov;
+        /* o_t = scale S_t^T q^ */
+        for (int i = 0; i < dk; ++i) {
+          double acc = 0.0;
+          for (int j = 0; j < dv; ++j) acc += Sc[(size_t)i * dv + j] * go[j];
+          dqn[i] = scale * acc;
+          for (int j = 0; j < dv; ++j) dS[(size_t)i * dv + j] += scale * qn[i] * go[j];
+        }
+        /* S_t = Sd + beta k^ u^T */
+        double dbeta = 0.0;
+        for (int j = 0; j < dv; ++j) {
+          double acc = 0.0;
+          for (int i = 0; i < dk; ++i) acc += kn[i] * dS[(size_t)i * dv + j];
+          du[j] = beta * acc;
+          dbeta += acc * u[j];
+        }
+        for (int i = 0; i < dk; ++i) {
+          double acc = 0.0;
+          for (int j = 0; j < dv; ++j) acc += dS[(size_t)i * dv + j] * u[j];
+          dkn[i] = beta * acc;
+        }
+        /* u = v - Sd^T k^ */
+        for (int j = 0; j < dv; ++j) dvv[ov + j] = du[j];
+        for (int i = 0; i < dk; ++i) {
+          double acc = 0.0;
+          for (int j = 0; j < dv; ++j) {
+            dS[(size_t)i * dv + j] -= kn[i] * du[j];  /* now dSd */
+            acc += Sd[(size_t)i * dv + j] * du[j];
+          }
+          dkn[i] -= acc;
+        }
+        /* Sd = Diag(a) S_{t-1} */
+        for (int i = 0; i < dk; ++i) {
+          double da = 0.0;
+          for (int j = 0; j < dv; ++j) da += dS[(size_t)i * dv + j] * Sp[(size_t)i * dv + j];
+          if (!(plant & PLANT_BWD_NO_STATE_DECAY))
+            for (int j = 0; j < dv; ++j) dS[(size_t)i * dv + j] *= a[i];
+          const double dg = a[i] * da;
+          const double x = f[ok_ + i] + dtb[i];
+          const double sg = (plant & PLANT_BWD_GATE_NO_SIGMOID) ? 1.0 : sigmoid(x);
+          const double dx = (lam == 0.0) ? 0.0 : -lam * sg * dg;
+          df[ok_ + i] = dx;
+          pp[i] += dx;
+          pp[dk] += dg * g[i];
+        }
+        if (plant & PLANT_BWD_BETA_SCALE) dbeta *= 1.25;
+        db[t * H + h] = dbeta * beta * (1.0 - beta);
+        /* L2 normalisation */
+        double pq = 0.0, pk = 0.0;
+        for (int c = 0; c < dk; ++c) { pq += qn[c] * dqn[c]; pk += kn[c] * dkn[c]; }
+        if (plant & PLANT_BWD_NO_NORM_PROJ) pq = pk = 0.0;
+        for (int c = 0; c < dk; ++c) {
+          dq[ok_ + c] = rq * (dqn[c] - qn[c] * pq);
+          dkk[ok_ + c] = rk * (dkn[c] - kn[c] * pk);
+        }
+      }
+      if (dS_init) memcpy(dS_init + ((size_t)n * H + h) * sz, dS, sizeof(double) * sz);
+      free(St);
+    }
+    free(qn); free(kn); free(g); free(a); free(u); free(du); free(dqn); free(dkn); free(Sd);
+    free(dS);
+  }
+  if (!fail) {
+    for (int h = 0; h < H; ++h) {
+      dA_log[h] = 0.0;
+      for (int c = 0; c < dk; ++c) ddt_bias[(int64_t)h * dk + c] = 0.0;
+    }
+    for (int64_t w = 0; w < units; ++w) {
+      const int h = (int)(w % H);
+      const double* pp = part + (size_t)w * (dk + 1);
+      for (int c = 0; c < dk; ++c) ddt_bias[(int64_t)h * dk + c] += pp[c];
+      dA_log[h] += pp[dk];
+    }
+  }
+  free(part);
+  return fail ? -1 : 0;
 }
 
 /* Number of threads the OpenMP runtime will use (reported by the benchmark). */

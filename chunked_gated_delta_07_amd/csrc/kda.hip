@@ -8,6 +8,7 @@
 #include "kda_intra.hpp"
 #include "kda_scan.hpp"
 #include "kda_recurrent.hpp"
+#include "kda_bwd.hpp"
 
 namespace kda {
 
@@ -136,6 +137,93 @@ static int dispatch(const void* q, const void* k, const void* v, const void* f, 
   if (a32 && !f32i) KDA_GO(float, bf16, float);
   KDA_GO(float, float, float);
 #undef KDA_GO
+}
+
+
+// ------------------------------------------------------------ backward
+// Workspace of the backward, FP32 arrays per (chunk, head) after the chunk
+// table.  Arrays written by the last three kernels reuse ones whose readers
+// have finished: alpha/pi/rho take D/dD/dW, q^/k^ take S0, G takes dSn.
+struct BwdLayout {
+  size_t off_cfirst, off_gam, off_rec, off_t, off_bwt, off_s0, off_dsn, off_d, off_dd, off_dqt,
+      off_dkb, off_dw, off_dbw, off_dp, off_da, off_dgam, off_db1, off_rqk, off_pp, total;
+};
+
+static inline BwdLayout bwd_layout(int64_t T, int32_t N, int32_t H) {
+  const size_t CH = (size_t)max_chunks(T, N) * H;
+  BwdLayout L;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
+  L.off_cfirst = take(sizeof(int32_t) * (size_t)(N + 1));
+  L.off_gam = take(4 * CH * DH);
+  L.off_rec = take(4 * CH * REC);
+  L.off_t = take(4 * CH * SQM);
+  L.off_bwt = take(4 * CH * MAT);
+  L.off_s0 = take(4 * CH * STM);
+  L.off_dsn = take(4 * CH * STM);
+  L.off_d = take(4 * CH * MAT);
+  L.off_dd = take(4 * CH * MAT);
+  L.off_dqt = take(4 * CH * MAT);
+  L.off_dkb = take(4 * CH * MAT);
+  L.off_dw = take(4 * CH * MAT);
+  L.off_dbw = take(4 * CH * MAT);
+  L.off_dp = take(4 * CH * SQM);
+  L.off_da = take(4 * CH * SQM);
+  L.off_dgam = take(4 * CH * DH);
+  L.off_db1 = take(4 * CH * CHUNK);
+  L.off_rqk = take(4 * CH * 2 * CHUNK);
+  L.off_pp = take(4 * CH * PPART);
+  L.total = o;
+  return L;
+}
+
+template <typename TA, typename TG, typename TR>
+static int launch_bwd(const void* q, const void* k, const void* v, const void* f, const void* b,
+                      const float* A_log, const float* dt_bias, const int32_t* cu, int32_t N,
+                      int64_t T, int32_t H, const float* init, const void* dout, const float* dfin,
+                      void* dq, void* dk, void* dv, void* df, void* db, float* dA_log, float* ddt,
+                      float* dinit, void* ws, hipStream_t stream) {
+  const BwdLayout L = bwd_layout(T, N, H);
+  char* base = reinterpret_cast<char*>(ws);
+  auto fp = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
+  int32_t* cfirst = reinterpret_cast<int32_t*>(base + L.off_cfirst);
+  const int64_t C = max_chunks(T, N);
+  hipLaunchKernelGGL(kda_chunk_table_kernel, dim3(1), dim3(1024), 0, stream, cu, (int)N, cfirst);
+
+  IntraArgs ia;
+  ia.q = q; ia.k = k; ia.v = v; ia.f = f; ia.b = b;
+  ia.A_log = A_log; ia.dt_bias = dt_bias; ia.cu = cu; ia.cfirst = cfirst;
+  ia.N = N; ia.H = H; ia.eps = 1e-6f; ia.gam = fp(L.off_gam); ia.rec = fp(L.off_rec);
+  ia.conv_w = nullptr; ia.conv_b = nullptr; ia.conv_silu = 0;
+  ia.tmat = fp(L.off_t); ia.bwt = fp(L.off_bwt);
+  const dim3 gch((unsigned)C, (unsigned)H);
+  hipLaunchKernelGGL((kda_intra_kernel<TA, float, false, PlainRec<float>, true>), gch, dim3(256), 0,
+                     stream, ia);
+
+  BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.f = f; a.b = b; a.dout = dout;
+  a.A_log = A_log; a.dt_bias = dt_bias; a.cu = cu; a.cfirst = cfirst;
+  a.init = init; a.dfin = dfin; a.N = N; a.H = H; a.eps = 1e-6f;
+  a.scale = 0.08838834764831845f;  // 1/sqrt(128)
+  a.rec = fp(L.off_rec); a.gam = fp(L.off_gam); a.tmat = fp(L.off_t); a.bwt = fp(L.off_bwt);
+  a.s0 = fp(L.off_s0); a.dsn = fp(L.off_dsn); a.dmat = fp(L.off_d); a.ddmat = fp(L.off_dd);
+  a.dqt = fp(L.off_dqt); a.dkb = fp(L.off_dkb); a.dw = fp(L.off_dw); a.dbw = fp(L.off_dbw);
+  a.dpm = fp(L.off_dp); a.dam = fp(L.off_da); a.dgam = fp(L.off_dgam); a.db1 = fp(L.off_db1);
+  a.rqk = fp(L.off_rqk); a.ppart = fp(L.off_pp);
+  a.al = a.dmat; a.pi = a.ddmat; a.rho = a.dw;  // read-once arrays reused
+  a.qn = a.s0; a.kn = a.s0 + (size_t)C * H * MAT; a.g2 = a.dsn;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.df = df; a.db = db;
+  a.dinit = dinit; a.dA_log = dA_log; a.ddt_bias = ddt;
+  const int64_t pairs = (int64_t)N * H;
+  const dim3 gscan((unsigned)(32 * ((pairs + 7) / 8)));
+  hipLaunchKernelGGL(kda_bwd_fscan_kernel, gscan, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((kda_bwd_bscan_kernel<TG>), gscan, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((kda_bwd_jprod_kernel<TG>), gch, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((kda_bwd_tprod_kernel<TA, TR>), gch, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((kda_bwd_gate_kernel<TA>), gch, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((kda_bwd_final_kernel<TA, TR>), gch, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(kda_bwd_param_kernel, dim3((unsigned)H), dim3(DH), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 }  // namespace kda
@@ -312,6 +400,54 @@ extern "C" int kda_recurrent_fwd_rect(const void* q, const void* k, const void* 
                                       void* stream) {
   return recurrent_impl(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, num_seqs, total_tokens,
                         H, dk, dv, mode, out, initial_state, final_state, stream);
+}
+
+extern "C" size_t kda_chunk_bwd_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t H,
+                                                int32_t d, uint32_t mode) {
+  if ((mode & ~KDA_MODE_ALL_BITS) || total_tokens < 0 || num_seqs < 1 || H < 1 || d != kda::DH)
+    return (size_t)-1;
+  if (total_tokens == 0) return 0;
+  return kda::bwd_layout(total_tokens, num_seqs, H).total;
+}
+
+extern "C" int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* f_raw,
+                             const void* b_raw, const float* A_log, const float* dt_bias,
+                             const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                             int32_t H, int32_t d, uint32_t mode, const float* initial_state,
+                             const void* dout, const float* dfinal_state, void* dq, void* dk,
+                             void* dv, void* df_raw, void* db_raw, float* dA_log, float* ddt_bias,
+                             float* dinitial_state, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (mode & ~KDA_MODE_ALL_BITS) return KDA_ERR_INVALID_ARG;
+  if (num_seqs < 1 || total_tokens < 0 || H < 1) return KDA_ERR_INVALID_ARG;
+  if (d != kda::DH) return KDA_ERR_UNSUPPORTED;
+  if (!dA_log || !ddt_bias) return KDA_ERR_INVALID_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (total_tokens == 0) {
+    const int64_t n = (int64_t)num_seqs * H * kda::DH * kda::DH;
+    const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+    hipLaunchKernelGGL(kda::kda_bwd_empty_kernel, dim3((unsigned)(blocks > 0 ? blocks : 1)),
+                       dim3(256), 0, s, dfinal_state, dinitial_state, n, dA_log, ddt_bias, (int)H);
+    return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  }
+  if (!q || !k || !v || !f_raw || !b_raw || !A_log || !dt_bias || !cu_seqlens || !dout || !dq ||
+      !dk || !dv || !df_raw || !db_raw || !workspace)
+    return KDA_ERR_INVALID_ARG;
+  if (total_tokens > (int64_t)INT32_MAX / 64 || (int64_t)num_seqs * H > (int64_t)INT32_MAX / 64)
+    return KDA_ERR_UNSUPPORTED;
+  if (workspace_bytes < kda::bwd_layout(total_tokens, num_seqs, H).total) return KDA_ERR_WORKSPACE;
+  const bool a32 = mode & KDA_ACT_FP32;
+  const bool o32 = (mode & KDA_OUT_FP32) || a32;
+#define KDA_BWD(TA, TG, TR)                                                                      \
+  return kda::launch_bwd<TA, TG, TR>(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, num_seqs, \
+                                     total_tokens, H, initial_state, dout, dfinal_state, dq, dk, \
+                                     dv, df_raw, db_raw, dA_log, ddt_bias, dinitial_state,       \
+                                     workspace, s)
+  if (a32) KDA_BWD(float, float, float);
+  if (o32) KDA_BWD(kda::bf16, float, float);
+  KDA_BWD(kda::bf16, kda::bf16, kda::bf16);
+#undef KDA_BWD
 }
 
 extern "C" const char* kda_status_string(int status) {

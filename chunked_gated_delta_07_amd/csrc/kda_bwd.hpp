@@ -1,0 +1,817 @@
+// kda_bwd.hpp -- backward (vector-Jacobian product) of the KDA chunked forward,
+// recomputed in FP32.
+//
+// The pages' training path keeps "backward recomputation in FP32" and casts
+// only the input gradients back to the activation dtype; its gradients of q,
+// k, v, the gate and beta are checked against an independent FP64 recurrence
+// VJP (xtuner PR #2301, sections Change and Validation), and dt_bias gradients
+// are summed in FP32 (xtuner PR #2153, KDA module section).
+//
+// Notation (one chunk of n <= 64 tokens of one head, entering with state S0;
+// G = chunk-local prefix of g, E = exp(G), F_r = exp(G_last - G_r),
+// Gam = exp(G_last), Bw = Diag(beta)(k^ * E), Bu = Diag(beta) v):
+//   M[r,i] = sum_c k^_rc k^_ic exp(G_rc - G_ic) (i < r),  A = Diag(beta) M
+//   P[r,i] = sum_c q^_rc k^_ic exp(G_rc - G_ic) (i <= r)
+//   T = (I + A)^{-1},  W = T Bw,  U = T Bu,  Qt = q^ * E,  Kb = k^ * F
+//   D = U - W S0,  O = scale (Qt S0 + P D),  S_next = Diag(Gam) S0 + Kb^T D.
+// Given dO and dSn = dL/dS_next, reverse-mode differentiation of these steps:
+//   dD   = scale P^T dO + Kb dSn               (reverse state scan)
+//   dS0  = Diag(Gam) dSn + scale Qt^T dO - W^T dD
+//   dQt  = scale dO S0^T,   dP = scale dO D^T (i <= r),   dKb = D dSn^T,
+//   dW   = -dD S0^T,        dGam_c = sum_j dSn_cj S0_cj
+//   dBu  = T^T dD (dv = beta dBu),  dBw = T^T dW,  dT = dD Bu^T + dW Bw^T,
+//   dA   = -(T^T dT T^T) strictly lower,
+//   then through the decay-weighted sums with dA (for M, with beta) and dP:
+//   alpha_rc = sum_{i<r} dA_ri k^_ic e^{G_rc-G_ic},  pi_rc = sum_{i<=r} dP_ri k^_ic e^{..},
+//   rho_ic   = sum_{r>=i} (beta_r dA_ri k^_rc + dP_ri q^_rc) e^{G_rc-G_ic},
+//   dq^ = pi + dQt E;  dk^ = beta alpha + rho + beta dBw E + dKb F;
+//   dG  = beta k^ alpha + q^ pi - k^ rho + dQt Qt + beta dBw k^ E - dKb Kb
+//         (+ sum_r dKb Kb + dGam Gam on the chunk's last row),
+//   dbeta = sum_c (Bu dBu / beta + k^ alpha + dBw k^ E) (the first as v.dBu),
+//   dg = reverse prefix of dG; x = f + dt_bias: df = dx = -exp(A_log) sigmoid(x) dg,
+//   dA_log += sum dg g,  db = dbeta beta (1 - beta),
+//   dq = (dq^ - q^ (q^.dq^)) rq,  dk likewise.
+// Every exponential of a difference of G has a non-positive exponent
+// (diagonal blocks per element; off-diagonal 8x8 blocks factorised about the
+// first row of the row block), so no gate strength can overflow it.
+//
+// Kernel sequence (all intermediates FP32 in the workspace):
+//   1. kda_intra_kernel<.., PlainRec, BWD>: records W, Qt, Kb^T, U^T, P, Gam, T, Bw^T
+//   2. kda_bwd_fscan_kernel: S0 of every chunk and D           (per sequence, head, 32 values)
+//   3. kda_bwd_bscan_kernel: dSn of every chunk, dD, dS_init   (same, chunks in reverse)
+//   4. kda_bwd_jprod_kernel: dQt, dP, dKb, dW, dGam            (per chunk, head)
+//   5. kda_bwd_tprod_kernel: dv, dbeta part, dBw, dA          (per chunk, head)
+//   6. kda_bwd_gate_kernel:  q^, k^, G, alpha, pi, rho         (per chunk, head)
+//   7. kda_bwd_final_kernel: dq, dk, df, db, parameter parts   (per chunk, head)
+//   8. kda_bwd_param_kernel: dA_log, dt_bias gradient          (per head, fixed order)
+#pragma once
+
+#include "kda_common.hpp"
+#include "kda_intra.hpp"
+
+namespace kda {
+
+constexpr int MAT = CHUNK * DH;      // one [64][128] FP32 matrix
+constexpr int SQM = CHUNK * CHUNK;   // one [64][64] matrix
+constexpr int STM = DH * DH;         // one [128][128] state
+constexpr int PPART = 132;           // per-chunk parameter partials: dt_bias[128], A_log, pad
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* f;
+  const void* b;
+  const void* dout;        // [T][H][128], dtype of the forward's output
+  const float* A_log;
+  const float* dt_bias;
+  const int32_t* cu;
+  const int32_t* cfirst;
+  const float* init;       // [N][H][128][128] or null
+  const float* dfin;       // [N][H][128][128] or null
+  int N;
+  int H;
+  float eps;
+  float scale;
+  // workspace (FP32), per (chunk, head) unless noted
+  const float* rec;        // PlainRec record, REC floats
+  const float* gam;        // [128]
+  const float* tmat;       // T [64][64]
+  const float* bwt;        // Bw^T [128][64]
+  float* s0;               // state entering the chunk [128 key][128 value]
+  float* dsn;              // dL/d(state leaving the chunk) [128][128]
+  float* dmat;             // D [64][128]
+  float* ddmat;            // dD [64][128]
+  float* dqt;              // dQt [64][128]
+  float* dkb;              // dKb [64][128]
+  float* dw;               // dW [64][128]
+  float* dbw;              // dBw [64][128]
+  float* dpm;              // dP [64][64]
+  float* dam;              // dA [64][64]
+  float* dgam;             // dGam [128]
+  float* db1;              // v . dBu per row [64]
+  float* qn;               // q^ [64][128]
+  float* kn;               // k^ [64][128]
+  float* g2;               // G log2(e) [64][128]
+  float* rqk;              // [64] rq, [64] rk
+  float* al;               // alpha [64][128]
+  float* pi;               // pi [64][128]
+  float* rho;              // rho [64][128]
+  float* ppart;            // [PPART]
+  // outputs
+  void* dq;
+  void* dk;
+  void* dv;
+  void* df;
+  void* db;
+  float* dinit;            // [N][H][128][128] or null
+  float* dA_log;           // [H]
+  float* ddt_bias;         // [H][128]
+};
+
+// Blocks of the two state scans: four value blocks of 32 per (sequence, head)
+// pair, placed so that the four land on the same XCD (workgroups are dealt to
+// the 8 XCDs round-robin) and share the chunk records through its L2.
+__device__ __forceinline__ void scan_block(int bid, int& pair, int& vb) {
+  pair = (bid & 7) + 8 * (bid >> 5);
+  vb = (bid >> 3) & 3;
+}
+
+// ------------------------------------------------------------ 2. forward scan
+// S_next = Diag(Gam) S0 + Kb^T (U - W S0), value block [128][32] of S in LDS.
+__global__ __launch_bounds__(256) void kda_bwd_fscan_kernel(BwdArgs p) {
+  constexpr int LW = 132, LK = 68, LS = 36;
+  __shared__ __attribute__((aligned(16))) float sW[CHUNK * LW];
+  __shared__ __attribute__((aligned(16))) float sKbT[DH * LK];
+  __shared__ __attribute__((aligned(16))) float sS[DH * LS];
+  __shared__ __attribute__((aligned(16))) float sD[CHUNK * LS];
+  int pair, vb;
+  scan_block(blockIdx.x, pair, vb);
+  if (pair >= p.N * p.H) return;
+  const int n = pair / p.H, h = pair - n * p.H;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int v0 = 32 * vb;
+  for (int x = tid; x < DH * 32; x += 256) {
+    const int i = x >> 5, j = x & 31;
+    sS[i * LS + j] = p.init ? p.init[((size_t)pair * DH + i) * DH + v0 + j] : 0.0f;
+  }
+  const int c_lo = p.cfirst[n], c_hi = p.cfirst[n + 1];
+  __syncthreads();
+  for (int c = c_lo; c < c_hi; ++c) {
+    const size_t ch = (size_t)c * p.H + h;
+    const float* rec = p.rec + ch * REC;
+    float* snap = p.s0 + ch * STM;
+    for (int x = tid; x < DH * 8; x += 256) {
+      const int i = x >> 3, j4 = 4 * (x & 7);
+      store4(snap + i * DH + v0 + j4, *reinterpret_cast<const f32x4*>(sS + i * LS + j4));
+    }
+    for (int x = tid; x < CHUNK * 32; x += 256) {
+      const int r = x >> 5, c4 = 4 * (x & 31);
+      *reinterpret_cast<f32x4*>(sW + r * LW + c4) =
+          *reinterpret_cast<const f32x4*>(rec + OFF_W + r * DH + c4);
+    }
+    for (int x = tid; x < DH * 16; x += 256) {
+      const int i = x >> 4, t4 = 4 * (x & 15);
+      *reinterpret_cast<f32x4*>(sKbT + i * LK + t4) =
+          *reinterpret_cast<const f32x4*>(rec + OFF_KBT + i * CHUNK + t4);
+    }
+    __syncthreads();
+    // D = U - W S0: wave w owns token rows 16w..16w+15, both 16-column halves
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      f32x4 acc = {0, 0, 0, 0};
+      acc = mma16_f32_kn<DH>(sW + 16 * w * LW, LW, sS + 16 * cb, LS, acc, l);
+      const int j = 16 * cb + (l & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * w + 4 * (l >> 4) + e;
+        const float d = rec[OFF_UT + (v0 + j) * CHUNK + r] - acc[e];
+        sD[r * LS + j] = d;
+        p.dmat[ch * MAT + r * DH + v0 + j] = d;
+      }
+    }
+    __syncthreads();
+    // S_next = Diag(Gam) S0 + Kb^T D: wave w owns key rows 32w..32w+31
+    f32x4 ns[2][2];
+    const float* gam = p.gam + ch * DH;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      const int kb = 2 * w + kb2;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        f32x4 acc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * kb + 4 * (l >> 4) + e;
+          acc[e] = gam[i] * sS[i * LS + 16 * cb + (l & 15)];
+        }
+        ns[kb2][cb] = mma16_f32_kn<CHUNK>(sKbT + 16 * kb * LK, LK, sD + 16 * cb, LS, acc, l);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sS[(16 * (2 * w + kb2) + 4 * (l >> 4) + e) * LS + 16 * cb + (l & 15)] = ns[kb2][cb][e];
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------ 3. reverse scan
+// Chunks in reverse order: snapshot dSn, dD = scale P^T dO + Kb dSn,
+// dS0 = Diag(Gam) dSn + scale Qt^T dO - W^T dD.  Ends with dS_init.
+template <typename TG>
+__global__ __launch_bounds__(256) void kda_bwd_bscan_kernel(BwdArgs p) {
+  constexpr int LW = 132, LK = 68, LS = 36;
+  __shared__ __attribute__((aligned(16))) float sW[CHUNK * LW];
+  __shared__ __attribute__((aligned(16))) float sQt[CHUNK * LW];
+  __shared__ __attribute__((aligned(16))) float sKbT[DH * LK];
+  __shared__ __attribute__((aligned(16))) float sP[CHUNK * LK];
+  __shared__ __attribute__((aligned(16))) float sO[CHUNK * LS];
+  __shared__ __attribute__((aligned(16))) float sS[DH * LS];
+  __shared__ __attribute__((aligned(16))) float sD[CHUNK * LS];
+  int pair, vb;
+  scan_block(blockIdx.x, pair, vb);
+  if (pair >= p.N * p.H) return;
+  const int n = pair / p.H, h = pair - n * p.H;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int v0 = 32 * vb;
+  const TG* __restrict__ gO = reinterpret_cast<const TG*>(p.dout);
+  for (int x = tid; x < DH * 32; x += 256) {
+    const int i = x >> 5, j = x & 31;
+    sS[i * LS + j] = p.dfin ? p.dfin[((size_t)pair * DH + i) * DH + v0 + j] : 0.0f;
+  }
+  const int c_lo = p.cfirst[n], c_hi = p.cfirst[n + 1];
+  const int tseq = p.cu[n], tend = p.cu[n + 1];
+  __syncthreads();
+  for (int c = c_hi - 1; c >= c_lo; --c) {
+    const size_t ch = (size_t)c * p.H + h;
+    const float* rec = p.rec + ch * REC;
+    const int t0 = tseq + (c - c_lo) * CHUNK;
+    const int len = min(CHUNK, tend - t0);
+    float* snap = p.dsn + ch * STM;
+    for (int x = tid; x < DH * 8; x += 256) {
+      const int i = x >> 3, j4 = 4 * (x & 7);
+      store4(snap + i * DH + v0 + j4, *reinterpret_cast<const f32x4*>(sS + i * LS + j4));
+    }
+    for (int x = tid; x < CHUNK * 32; x += 256) {
+      const int r = x >> 5, c4 = 4 * (x & 31);
+      *reinterpret_cast<f32x4*>(sW + r * LW + c4) =
+          *reinterpret_cast<const f32x4*>(rec + OFF_W + r * DH + c4);
+      *reinterpret_cast<f32x4*>(sQt + r * LW + c4) =
+          *reinterpret_cast<const f32x4*>(rec + OFF_QT + r * DH + c4);
+    }
+    for (int x = tid; x < DH * 16; x += 256) {
+      const int i = x >> 4, t4 = 4 * (x & 15);
+      *reinterpret_cast<f32x4*>(sKbT + i * LK + t4) =
+          *reinterpret_cast<const f32x4*>(rec + OFF_KBT + i * CHUNK + t4);
+    }
+    for (int x = tid; x < CHUNK * 16; x += 256) {
+      const int r = x >> 4, i4 = 4 * (x & 15);
+      *reinterpret_cast<f32x4*>(sP + r * LK + i4) =
+          *reinterpret_cast<const f32x4*>(rec + OFF_P + r * CHUNK + i4);
+    }
+    for (int x = tid; x < CHUNK * 32; x += 256) {
+      const int r = x >> 5, j = x & 31;
+      sO[r * LS + j] = r < len ? p.scale * to_f32(gO[((size_t)(t0 + r) * p.H + h) * DH + v0 + j]) : 0.0f;
+    }
+    __syncthreads();
+    // dD = P^T (scale dO) + Kb dSn: wave w owns token rows 16w..16w+15
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      f32x4 acc = {0, 0, 0, 0};
+      acc = mma16_f32_tn<CHUNK>(sP + 16 * w, LK, sO + 16 * cb, LS, acc, l);
+      acc = mma16_f32_tn<DH>(sKbT + 16 * w, LK, sS + 16 * cb, LS, acc, l);
+      const int j = 16 * cb + (l & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * w + 4 * (l >> 4) + e;
+        sD[r * LS + j] = acc[e];
+        p.ddmat[ch * MAT + r * DH + v0 + j] = acc[e];
+      }
+    }
+    __syncthreads();
+    // dS0 = Diag(Gam) dSn + Qt^T (scale dO) - W^T dD: wave w owns key rows 32w..32w+31
+    f32x4 ns[2][2];
+    const float* gam = p.gam + ch * DH;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      const int kb = 2 * w + kb2;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        f32x4 acc, neg = {0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * kb + 4 * (l >> 4) + e;
+          acc[e] = gam[i] * sS[i * LS + 16 * cb + (l & 15)];
+        }
+        acc = mma16_f32_tn<CHUNK>(sQt + 16 * kb, LW, sO + 16 * cb, LS, acc, l);
+        neg = mma16_f32_tn<CHUNK>(sW + 16 * kb, LW, sD + 16 * cb, LS, neg, l);
+        ns[kb2][cb] = acc - neg;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sS[(16 * (2 * w + kb2) + 4 * (l >> 4) + e) * LS + 16 * cb + (l & 15)] = ns[kb2][cb][e];
+    __syncthreads();
+  }
+  if (p.dinit) {
+    for (int x = tid; x < DH * 8; x += 256) {
+      const int i = x >> 3, j4 = 4 * (x & 7);
+      store4(p.dinit + ((size_t)pair * DH + i) * DH + v0 + j4,
+             *reinterpret_cast<const f32x4*>(sS + i * LS + j4));
+    }
+  }
+}
+
+// Chunk -> (first token, length) for the per-(chunk, head) kernels.
+__device__ __forceinline__ bool bwd_chunk(const BwdArgs& p, int c, int& t0, int& len) {
+  int tseq;
+  return locate_chunk(p.cu, p.cfirst, p.N, c, t0, len, tseq);
+}
+
+// ------------------------------------------------------------ 4. products over values
+// dQt = scale dO S0^T, dP = scale dO D^T (i <= r), dKb = D dSn^T, dW = -dD S0^T,
+// dGam = rowsum(dSn * S0); contracted over the 128 value channels in four
+// slabs of 32.  Wave w owns token rows 16w..16w+15 of every output.
+template <typename TG>
+__global__ __launch_bounds__(256) void kda_bwd_jprod_kernel(BwdArgs p) {
+  constexpr int LS = 36;
+  __shared__ __attribute__((aligned(16))) float sO[CHUNK * LS];
+  __shared__ __attribute__((aligned(16))) float sDm[CHUNK * LS];
+  __shared__ __attribute__((aligned(16))) float sDD[CHUNK * LS];
+  __shared__ __attribute__((aligned(16))) float sS0[DH * LS];
+  __shared__ __attribute__((aligned(16))) float sDS[DH * LS];
+  const int c = blockIdx.x, h = blockIdx.y;
+  int t0, len;
+  if (!bwd_chunk(p, c, t0, len)) return;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const size_t ch = (size_t)c * p.H + h;
+  const TG* __restrict__ gO = reinterpret_cast<const TG*>(p.dout);
+  f32x4 aq[8], ak[8], aw[8], ap[4];
+#pragma unroll
+  for (int x = 0; x < 8; ++x) aq[x] = ak[x] = aw[x] = f32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int x = 0; x < 4; ++x) ap[x] = f32x4{0, 0, 0, 0};
+  float gacc = 0.0f;
+  for (int sl = 0; sl < 4; ++sl) {
+    const int v0 = 32 * sl;
+    __syncthreads();
+    for (int x = tid; x < CHUNK * 32; x += 256) {
+      const int r = x >> 5, j = x & 31;
+      sO[r * LS + j] = r < len ? p.scale * to_f32(gO[((size_t)(t0 + r) * p.H + h) * DH + v0 + j]) : 0.0f;
+    }
+    for (int x = tid; x < CHUNK * 8; x += 256) {
+      const int r = x >> 3, j4 = 4 * (x & 7);
+      *reinterpret_cast<f32x4*>(sDm + r * LS + j4) =
+          *reinterpret_cast<const f32x4*>(p.dmat + ch * MAT + r * DH + v0 + j4);
+      *reinterpret_cast<f32x4*>(sDD + r * LS + j4) =
+          *reinterpret_cast<const f32x4*>(p.ddmat + ch * MAT + r * DH + v0 + j4);
+    }
+    for (int x = tid; x < DH * 8; x += 256) {
+      const int i = x >> 3, j4 = 4 * (x & 7);
+      *reinterpret_cast<f32x4*>(sS0 + i * LS + j4) =
+          *reinterpret_cast<const f32x4*>(p.s0 + ch * STM + i * DH + v0 + j4);
+      *reinterpret_cast<f32x4*>(sDS + i * LS + j4) =
+          *reinterpret_cast<const f32x4*>(p.dsn + ch * STM + i * DH + v0 + j4);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+      aq[cb] = mma16_rows<float, 32>(sO + 16 * w * LS, LS, sS0 + 16 * cb * LS, LS, aq[cb], l);
+      ak[cb] = mma16_rows<float, 32>(sDm + 16 * w * LS, LS, sDS + 16 * cb * LS, LS, ak[cb], l);
+      aw[cb] = mma16_rows<float, 32>(sDD + 16 * w * LS, LS, sS0 + 16 * cb * LS, LS, aw[cb], l);
+    }
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib)
+      ap[ib] = mma16_rows<float, 32>(sO + 16 * w * LS, LS, sDm + 16 * ib * LS, LS, ap[ib], l);
+    if (tid < DH) {
+#pragma unroll 8
+      for (int j = 0; j < 32; ++j) gacc = fmaf(sDS[tid * LS + j], sS0[tid * LS + j], gacc);
+    }
+  }
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) {
+    const int col = 16 * cb + (l & 15);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * w + 4 * (l >> 4) + e;
+      p.dqt[ch * MAT + r * DH + col] = aq[cb][e];
+      p.dkb[ch * MAT + r * DH + col] = ak[cb][e];
+      p.dw[ch * MAT + r * DH + col] = -aw[cb][e];
+    }
+  }
+#pragma unroll
+  for (int ib = 0; ib < 4; ++ib) {
+    const int i = 16 * ib + (l & 15);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * w + 4 * (l >> 4) + e;
+      p.dpm[ch * SQM + r * CHUNK + i] = i <= r ? ap[ib][e] : 0.0f;
+    }
+  }
+  if (tid < DH) p.dgam[ch * DH + tid] = gacc;
+}
+
+// ------------------------------------------------------------ 5. products with T
+// dBu = T^T dD -> dv = beta dBu and db1 = v . dBu per row; dBw = T^T dW;
+// dT = dD Bu^T + dW Bw^T;  dA = -(T^T dT) T^T, strictly lower.
+template <typename TA, typename TR>
+__global__ __launch_bounds__(256) void kda_bwd_tprod_kernel(BwdArgs p) {
+  constexpr int LT = 68, LW = 132, LK = 68;
+  __shared__ __attribute__((aligned(16))) float sT[CHUNK * LT];
+  __shared__ __attribute__((aligned(16))) float sR1[CHUNK * LW];
+  __shared__ __attribute__((aligned(16))) float sR2[DH * LK];  // >= CHUNK * LW floats
+  __shared__ float sBeta[CHUNK];
+  static_assert(DH * LK >= CHUNK * LW && DH * LK >= 2 * CHUNK * LT, "region sizes");
+  const int c = blockIdx.x, h = blockIdx.y;
+  int t0, len;
+  if (!bwd_chunk(p, c, t0, len)) return;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const size_t ch = (size_t)c * p.H + h;
+  const TA* __restrict__ gv = reinterpret_cast<const TA*>(p.v);
+  const TA* __restrict__ gb = reinterpret_cast<const TA*>(p.b);
+  TR* __restrict__ gdv = reinterpret_cast<TR*>(p.dv);
+  // phase 1: T, dD, raw v
+  for (int x = tid; x < CHUNK * 16; x += 256) {
+    const int r = x >> 4, i4 = 4 * (x & 15);
+    *reinterpret_cast<f32x4*>(sT + r * LT + i4) =
+        *reinterpret_cast<const f32x4*>(p.tmat + ch * SQM + r * CHUNK + i4);
+  }
+  for (int x = tid; x < CHUNK * 32; x += 256) {
+    const int r = x >> 5, c4 = 4 * (x & 31);
+    *reinterpret_cast<f32x4*>(sR1 + r * LW + c4) =
+        *reinterpret_cast<const f32x4*>(p.ddmat + ch * MAT + r * DH + c4);
+  }
+  for (int x = tid; x < CHUNK * 64; x += 256) {
+    const int r = x >> 6, c2 = 2 * (x & 63);
+    const f32x2 vv = r < len ? load2(gv + ((size_t)(t0 + r) * p.H + h) * DH + c2) : f32x2{0, 0};
+    sR2[r * LW + c2] = vv[0];
+    sR2[r * LW + c2 + 1] = vv[1];
+  }
+  if (tid < CHUNK) sBeta[tid] = tid < len ? sigmoid_f(to_f32(gb[(size_t)(t0 + tid) * p.H + h])) : 0.0f;
+  __syncthreads();
+  // dBu rows i = 16w.. : dv = beta dBu, db1 = sum_j v dBu
+  {
+    float bsum[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+      f32x4 acc = {0, 0, 0, 0};
+      acc = mma16_f32_tn<CHUNK>(sT + 16 * w, LT, sR1 + 16 * cb, LW, acc, l);
+      const int j = 16 * cb + (l & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * w + 4 * (l >> 4) + e;
+        bsum[e] = fmaf(acc[e], sR2[i * LW + j], bsum[e]);
+        if (i < len) gdv[((size_t)(t0 + i) * p.H + h) * DH + j] = from_f32<TR>(sBeta[i] * acc[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) bsum[e] += __shfl_xor(bsum[e], m, 64);
+    }
+    if ((l & 15) == 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p.db1[ch * CHUNK + 16 * w + 4 * (l >> 4) + e] = bsum[e];
+    }
+  }
+  // dT = dD (beta v)^T: rows r = 16w.., columns i (scaled by beta_i afterwards)
+  f32x4 dt[4];
+#pragma unroll
+  for (int ib = 0; ib < 4; ++ib) {
+    f32x4 acc = {0, 0, 0, 0};
+    acc = mma16_rows<float, DH>(sR1 + 16 * w * LW, LW, sR2 + 16 * ib * LW, LW, acc, l);
+    const float bi = sBeta[16 * ib + (l & 15)];
+    dt[ib] = acc * bi;
+  }
+  __syncthreads();
+  // phase 2: dW, Bw^T
+  for (int x = tid; x < CHUNK * 32; x += 256) {
+    const int r = x >> 5, c4 = 4 * (x & 31);
+    *reinterpret_cast<f32x4*>(sR1 + r * LW + c4) =
+        *reinterpret_cast<const f32x4*>(p.dw + ch * MAT + r * DH + c4);
+  }
+  for (int x = tid; x < DH * 16; x += 256) {
+    const int i = x >> 4, t4 = 4 * (x & 15);
+    *reinterpret_cast<f32x4*>(sR2 + i * LK + t4) =
+        *reinterpret_cast<const f32x4*>(p.bwt + ch * DH * CHUNK + i * CHUNK + t4);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int ib = 0; ib < 4; ++ib)
+    dt[ib] = mma16_f32_kn<DH>(sR1 + 16 * w * LW, LW, sR2 + 16 * ib, LK, dt[ib], l);
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) {
+    f32x4 acc = {0, 0, 0, 0};
+    acc = mma16_f32_tn<CHUNK>(sT + 16 * w, LT, sR1 + 16 * cb, LW, acc, l);
+    const int col = 16 * cb + (l & 15);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p.dbw[ch * MAT + (16 * w + 4 * (l >> 4) + e) * DH + col] = acc[e];
+  }
+  __syncthreads();
+  // phase 3: X = T^T dT, dA = -X T^T (strictly lower)
+  float* sDT = sR2;
+  float* sX = sR2 + CHUNK * LT;
+#pragma unroll
+  for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sDT[(16 * w + 4 * (l >> 4) + e) * LT + 16 * ib + (l & 15)] = dt[ib][e];
+  __syncthreads();
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    f32x4 acc = {0, 0, 0, 0};
+    acc = mma16_f32_tn<CHUNK>(sT + 16 * w, LT, sDT + 16 * mb, LT, acc, l);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sX[(16 * w + 4 * (l >> 4) + e) * LT + 16 * mb + (l & 15)] = acc[e];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) {
+    f32x4 acc = {0, 0, 0, 0};
+    acc = mma16_rows<float, CHUNK>(sX + 16 * w * LT, LT, sT + 16 * jb * LT, LT, acc, l);
+    const int j = 16 * jb + (l & 15);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * w + 4 * (l >> 4) + e;
+      p.dam[ch * SQM + i * CHUNK + j] = j < i ? -acc[e] : 0.0f;
+    }
+  }
+}
+
+// Per-token-head prep of the backward, FP32: the log2-unit gate
+// g2 = g log2(e) = -exp(A_log) softplus(x) log2(e), x = f + dt_bias.
+__device__ __forceinline__ float gate_log2(float x, float lam) {
+  const float t = exp2_hw(-fabsf(x) * LOG2E);
+  return -lam * (fmaxf(x, 0.0f) * LOG2E + log2_hw(1.0f + t));
+}
+
+// ------------------------------------------------------------ 6. decay-weighted sums
+// Recomputes q^, k^ and G (stored for kernel 7), then
+//   waves 0-1 (one thread per channel): alpha, pi (sums over i <= r per row r)
+//   waves 2-3 (one thread per channel): rho (sums over r >= i per column i)
+// in 8x8 token blocks: off-diagonal blocks (R > I) factorised about row 8R,
+//   e^{G_r - G_i} = e^{G_r - G_8R} e^{G_8R - G_i}  (both exponents <= 0),
+// diagonal blocks per element.
+template <typename TA>
+__global__ __launch_bounds__(256) void kda_bwd_gate_kernel(BwdArgs p) {
+  __shared__ __attribute__((aligned(16))) float sQ[CHUNK * DH];
+  __shared__ __attribute__((aligned(16))) float sK[CHUNK * DH];
+  __shared__ __attribute__((aligned(16))) float sG[CHUNK * DH];
+  __shared__ __attribute__((aligned(16))) float sA[SQM];
+  __shared__ __attribute__((aligned(16))) float sP[SQM];
+  __shared__ float sBeta[CHUNK];
+  const int cidx = blockIdx.x, h = blockIdx.y;
+  int t0, len;
+  if (!bwd_chunk(p, cidx, t0, len)) return;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const size_t ch = (size_t)cidx * p.H + h;
+  const TA* __restrict__ gq = reinterpret_cast<const TA*>(p.q);
+  const TA* __restrict__ gk = reinterpret_cast<const TA*>(p.k);
+  const TA* __restrict__ gf = reinterpret_cast<const TA*>(p.f);
+  const TA* __restrict__ gb = reinterpret_cast<const TA*>(p.b);
+  const float lam = expf(p.A_log[h]);
+  const int c0 = 2 * l;
+  const f32x2 dtb = *reinterpret_cast<const f32x2*>(p.dt_bias + (size_t)h * DH + c0);
+  // prep: wave w rows 16w.., lane channels c0, c0+1; rows past the end are zero
+  // (q^ = k^ = 0, g = 0)
+  for (int j = 0; j < 16; ++j) {
+    const int r = 16 * w + j;
+    const bool ok = r < len;
+    const size_t o = ((size_t)(t0 + (ok ? r : 0)) * p.H + h) * DH + c0;
+    f32x2 qv = load2(gq + o), kv = load2(gk + o), fv = load2(gf + o);
+    if (!ok) qv = kv = fv = f32x2{0, 0};
+    const float sq = wave_sum(qv[0] * qv[0] + qv[1] * qv[1]);
+    const float sk = wave_sum(kv[0] * kv[0] + kv[1] * kv[1]);
+    const float rq = rsqrt_hw(sq + p.eps), rk = rsqrt_hw(sk + p.eps);
+    sQ[r * DH + c0] = qv[0] * rq; sQ[r * DH + c0 + 1] = qv[1] * rq;
+    sK[r * DH + c0] = kv[0] * rk; sK[r * DH + c0 + 1] = kv[1] * rk;
+    sG[r * DH + c0] = ok ? gate_log2(fv[0] + dtb[0], lam) : 0.0f;
+    sG[r * DH + c0 + 1] = ok ? gate_log2(fv[1] + dtb[1], lam) : 0.0f;
+    if (l == 0) {
+      sBeta[r] = ok ? sigmoid_f(to_f32(gb[(size_t)(t0 + r) * p.H + h])) : 0.0f;
+      p.rqk[ch * 2 * CHUNK + r] = rq;
+      p.rqk[ch * 2 * CHUNK + CHUNK + r] = rk;
+    }
+  }
+  __syncthreads();
+  if (tid < DH) {
+    float acc = 0.0f;
+    for (int r = 0; r < CHUNK; ++r) {
+      acc += sG[r * DH + tid];
+      sG[r * DH + tid] = acc;
+    }
+  } else {
+    for (int x = tid - DH; x < SQM / 4; x += 128) {
+      reinterpret_cast<f32x4*>(sA)[x] = reinterpret_cast<const f32x4*>(p.dam + ch * SQM)[x];
+      reinterpret_cast<f32x4*>(sP)[x] = reinterpret_cast<const f32x4*>(p.dpm + ch * SQM)[x];
+    }
+  }
+  __syncthreads();
+  for (int x = tid; x < MAT / 4; x += 256) {
+    reinterpret_cast<f32x4*>(p.qn + ch * MAT)[x] = reinterpret_cast<const f32x4*>(sQ)[x];
+    reinterpret_cast<f32x4*>(p.kn + ch * MAT)[x] = reinterpret_cast<const f32x4*>(sK)[x];
+    reinterpret_cast<f32x4*>(p.g2 + ch * MAT)[x] = reinterpret_cast<const f32x4*>(sG)[x];
+  }
+  const int c = tid & (DH - 1);
+  if (tid < DH) {
+    // rows: alpha_r = sum_{i<r} dA_ri k^_i e^{G_r-G_i}, pi_r = sum_{i<=r} dP_ri k^_i e^{..}
+    for (int R = 0; R < 8; ++R) {
+      const int m = 8 * R;
+      const float gm = sG[m * DH + c];
+      float ao[8], po[8];
+#pragma unroll
+      for (int a = 0; a < 8; ++a) ao[a] = po[a] = 0.0f;
+      for (int I = 0; I < R; ++I) {
+        float kt[8];
+#pragma unroll
+        for (int bb = 0; bb < 8; ++bb) {
+          const int i = 8 * I + bb;
+          kt[bb] = sK[i * DH + c] * exp2_hw(gm - sG[i * DH + c]);
+        }
+#pragma unroll
+        for (int a = 0; a < 8; ++a) {
+          const float* ar = sA + (m + a) * CHUNK + 8 * I;
+          const float* pr = sP + (m + a) * CHUNK + 8 * I;
+#pragma unroll
+          for (int bb = 0; bb < 8; ++bb) {
+            ao[a] = fmaf(ar[bb], kt[bb], ao[a]);
+            po[a] = fmaf(pr[bb], kt[bb], po[a]);
+          }
+        }
+      }
+#pragma unroll
+      for (int a = 0; a < 8; ++a) {
+        const int r = m + a;
+        const float gr = sG[r * DH + c];
+        const float fa = exp2_hw(gr - gm);
+        float al = ao[a] * fa, pv = po[a] * fa;
+#pragma unroll
+        for (int bb = 0; bb <= a; ++bb) {
+          const int i = m + bb;
+          const float kte = sK[i * DH + c] * exp2_hw(gr - sG[i * DH + c]);
+          al = fmaf(sA[r * CHUNK + i], kte, al);
+          pv = fmaf(sP[r * CHUNK + i], kte, pv);
+        }
+        p.al[ch * MAT + r * DH + c] = al;
+        p.pi[ch * MAT + r * DH + c] = pv;
+      }
+    }
+  } else {
+    // columns: rho_i = sum_{r>=i} (beta_r dA_ri k^_r + dP_ri q^_r) e^{G_r-G_i}
+    for (int I = 0; I < 8; ++I) {
+      float ro[8];
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb) ro[bb] = 0.0f;
+      for (int R = I + 1; R < 8; ++R) {
+        const int m = 8 * R;
+        const float gm = sG[m * DH + c];
+        float bk[8], qq[8], part[8];
+#pragma unroll
+        for (int a = 0; a < 8; ++a) {
+          const int r = m + a;
+          const float fa = exp2_hw(sG[r * DH + c] - gm);
+          bk[a] = sBeta[r] * sK[r * DH + c] * fa;
+          qq[a] = sQ[r * DH + c] * fa;
+        }
+#pragma unroll
+        for (int bb = 0; bb < 8; ++bb) part[bb] = 0.0f;
+#pragma unroll
+        for (int a = 0; a < 8; ++a) {
+          const float* ar = sA + (m + a) * CHUNK + 8 * I;
+          const float* pr = sP + (m + a) * CHUNK + 8 * I;
+#pragma unroll
+          for (int bb = 0; bb < 8; ++bb) part[bb] = fmaf(ar[bb], bk[a], fmaf(pr[bb], qq[a], part[bb]));
+        }
+#pragma unroll
+        for (int bb = 0; bb < 8; ++bb) {
+          const int i = 8 * I + bb;
+          ro[bb] = fmaf(exp2_hw(gm - sG[i * DH + c]), part[bb], ro[bb]);
+        }
+      }
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb) {
+        const int i = 8 * I + bb;
+        const float gi = sG[i * DH + c];
+        float rv = ro[bb];
+#pragma unroll
+        for (int a = bb; a < 8; ++a) {
+          const int r = 8 * I + a;
+          const float e = exp2_hw(sG[r * DH + c] - gi);
+          rv = fmaf(fmaf(sA[r * CHUNK + i], sBeta[r] * sK[r * DH + c], sP[r * CHUNK + i] * sQ[r * DH + c]), e, rv);
+        }
+        p.rho[ch * MAT + i * DH + c] = rv;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ 7. elementwise chain
+// Wave w: rows 16w..16w+15, lane channels c0, c0+1 for the row-local parts
+// (dq, dk, db and dG); then one thread per channel for the reverse prefix of
+// dG over the chunk's rows, df and the per-chunk parameter partials.
+template <typename TA, typename TR>
+__global__ __launch_bounds__(256) void kda_bwd_final_kernel(BwdArgs p) {
+  __shared__ __attribute__((aligned(16))) float sDG[CHUNK * DH];
+  __shared__ float sCol[4][DH];
+  __shared__ float sRed[DH];
+  const int cidx = blockIdx.x, h = blockIdx.y;
+  int t0, len;
+  if (!bwd_chunk(p, cidx, t0, len)) return;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const size_t ch = (size_t)cidx * p.H + h;
+  const TA* __restrict__ gf = reinterpret_cast<const TA*>(p.f);
+  const TA* __restrict__ gb = reinterpret_cast<const TA*>(p.b);
+  TR* __restrict__ gdq = reinterpret_cast<TR*>(p.dq);
+  TR* __restrict__ gdk = reinterpret_cast<TR*>(p.dk);
+  TR* __restrict__ gdf = reinterpret_cast<TR*>(p.df);
+  TR* __restrict__ gdb = reinterpret_cast<TR*>(p.db);
+  const int c0 = 2 * l;
+  const size_t mb = ch * MAT;
+  const f32x2 gL = load2(p.g2 + mb + (CHUNK - 1) * DH + c0);  // G_last (rows past the end keep it)
+  float col0 = 0.0f, col1 = 0.0f;
+  for (int j = 0; j < 16; ++j) {
+    const int r = 16 * w + j;
+    const size_t o = mb + r * DH + c0;
+    const f32x2 qn = load2(p.qn + o), kn = load2(p.kn + o), g2 = load2(p.g2 + o);
+    const f32x2 al = load2(p.al + o), pv = load2(p.pi + o), rh = load2(p.rho + o);
+    const f32x2 dqt = load2(p.dqt + o), dkb = load2(p.dkb + o), dbw = load2(p.dbw + o);
+    const bool ok = r < len;
+    const float beta = ok ? sigmoid_f(to_f32(gb[(size_t)(t0 + r) * p.H + h])) : 0.0f;
+    float dqn[2], dkn[2], sb = 0.0f;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const float E = exp2_hw(g2[x]), F = exp2_hw(gL[x] - g2[x]);
+      dqn[x] = pv[x] + dqt[x] * E;
+      dkn[x] = beta * al[x] + rh[x] + beta * dbw[x] * E + dkb[x] * F;
+      const float kbf = dkb[x] * kn[x] * F;
+      const float dG = beta * kn[x] * al[x] + qn[x] * pv[x] - kn[x] * rh[x] + dqt[x] * qn[x] * E +
+                       beta * dbw[x] * kn[x] * E - kbf;
+      sDG[r * DH + c0 + x] = ok ? dG : 0.0f;
+      if (ok) { if (x == 0) col0 += kbf; else col1 += kbf; }
+      sb += kn[x] * al[x] + dbw[x] * kn[x] * E;
+    }
+    const float s_b = wave_sum(sb);
+    const float s_q = wave_sum(qn[0] * dqn[0] + qn[1] * dqn[1]);
+    const float s_k = wave_sum(kn[0] * dkn[0] + kn[1] * dkn[1]);
+    if (ok) {
+      const float rq = p.rqk[ch * 2 * CHUNK + r], rk = p.rqk[ch * 2 * CHUNK + CHUNK + r];
+      const size_t go = ((size_t)(t0 + r) * p.H + h) * DH + c0;
+      store2(gdq + go, rq * (dqn[0] - qn[0] * s_q), rq * (dqn[1] - qn[1] * s_q));
+      store2(gdk + go, rk * (dkn[0] - kn[0] * s_k), rk * (dkn[1] - kn[1] * s_k));
+      if (l == 0) {
+        const float dbeta = p.db1[ch * CHUNK + r] + s_b;
+        gdb[(size_t)(t0 + r) * p.H + h] = from_f32<TR>(dbeta * beta * (1.0f - beta));
+      }
+    }
+  }
+  sCol[w][c0] = col0;
+  sCol[w][c0 + 1] = col1;
+  __syncthreads();
+  if (tid < DH) {
+    const int c = tid;
+    const float lam = expf(p.A_log[h]);
+    const float dtb = p.dt_bias[(size_t)h * DH + c];
+    const float gLc = p.g2[mb + (CHUNK - 1) * DH + c];
+    // the chunk's last row also carries d(G_last) from Kb and Gam
+    float acc = sCol[0][c] + sCol[1][c] + sCol[2][c] + sCol[3][c] +
+                p.dgam[ch * DH + c] * exp2_hw(gLc);
+    float pdt = 0.0f, pa = 0.0f;
+    for (int r = len - 1; r >= 0; --r) {
+      acc += sDG[r * DH + c];
+      const float x = to_f32(gf[((size_t)(t0 + r) * p.H + h) * DH + c]) + dtb;
+      const float dx = lam == 0.0f ? 0.0f : -lam * sigmoid_f(x) * acc;
+      gdf[((size_t)(t0 + r) * p.H + h) * DH + c] = from_f32<TR>(dx);
+      pdt += dx;
+      pa = fmaf(acc, gate_log2(x, lam) * (1.0f / LOG2E), pa);
+    }
+    p.ppart[ch * PPART + c] = pdt;
+    sRed[c] = pa;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float s = 0.0f;
+    for (int c = 0; c < DH; ++c) s += sRed[c];
+    p.ppart[ch * PPART + DH] = s;
+  }
+}
+
+// ------------------------------------------------------------ 8. parameter gradients
+// dt_bias and A_log gradients of head h: per-chunk partials summed in chunk
+// order (FP32, deterministic).
+__global__ __launch_bounds__(DH) void kda_bwd_param_kernel(BwdArgs p) {
+  const int h = blockIdx.x, c = threadIdx.x;
+  const int nch = p.cfirst[p.N];
+  float sdt = 0.0f, sa = 0.0f;
+  for (int k = 0; k < nch; ++k) {
+    const float* pp = p.ppart + ((size_t)k * p.H + h) * PPART;
+    sdt += pp[c];
+    if (c == 0) sa += pp[DH];
+  }
+  p.ddt_bias[(size_t)h * DH + c] = sdt;
+  if (c == 0) p.dA_log[h] = sa;
+}
+
+// Gradient outputs of an empty batch: dS_init = dS_final (or zero), dA_log
+// and the dt_bias gradient zero.
+__global__ __launch_bounds__(256) void kda_bwd_empty_kernel(const float* __restrict__ dfin,
+                                                            float* __restrict__ dinit, int64_t n,
+                                                            float* __restrict__ dA_log,
+                                                            float* __restrict__ ddt, int H) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  const int64_t i0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (dinit)
+    for (int64_t i = i0; i < n; i += stride) dinit[i] = dfin ? dfin[i] : 0.0f;
+  for (int64_t i = i0; i < (int64_t)H * DH; i += stride) ddt[i] = 0.0f;
+  for (int64_t i = i0; i < H; i += stride) dA_log[i] = 0.0f;
+}
+
+}  // namespace kda

@@ -126,6 +126,21 @@ __device__ __forceinline__ f32x4 mma16_f32_kn(const float* a, int lda, const flo
   return c;
 }
 
+// fp32 C[16][16] += A[16][K] * B[K][16] with A supplied transposed
+// (A[m][k] at at + k*ldat + m) and B k-major.  K multiple of 4.
+template <int K>
+__device__ __forceinline__ f32x4 mma16_f32_tn(const float* at, int ldat, const float* b, int ldb,
+                                              f32x4 c, int lane) {
+  constexpr int KG = K / 4;
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < KG; ++s) {
+    const int kk = g * KG + s;
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(at[kk * ldat + r], b[kk * ldb + r], c, 0, 0, 0);
+  }
+  return c;
+}
+
 // 32x32 tiles for the state pass.
 template <typename MT> struct Mma32;
 template <> struct Mma32<bf16> {
@@ -169,5 +184,12 @@ __device__ __forceinline__ float sigmoid_f(float x) {
   return __builtin_amdgcn_rcpf(1.0f + exp2_hw(-x * LOG2E));
 }
 __device__ __forceinline__ float rsqrt_hw(float x) { return __builtin_amdgcn_rsqf(x); }
+
+// Sum over the 64 lanes of a wave (every lane gets the total).
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
 
 }  // namespace kda

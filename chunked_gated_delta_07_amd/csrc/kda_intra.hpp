@@ -75,6 +75,18 @@ template <typename MT> struct Frag {
   }
 };
 
+// The same record in plain row-major order, for the backward pass (which
+// reads it as whole matrices): W [64][128], Qt [64][128], Kb^T [128][64],
+// U^T [128 value][64 tok], P [64][64].  Every group of stores the forward
+// makes (FE consecutive elements along one index) is contiguous here too.
+template <typename MT> struct PlainRec {
+  static constexpr int FE = 16 / (int)sizeof(MT);
+  __host__ __device__ static constexpr int a(int r, int c) { return r * DH + c; }
+  __host__ __device__ static constexpr int kb(int c, int t) { return c * CHUNK + t; }
+  __host__ __device__ static constexpr int pm(int r, int i) { return r * CHUNK + i; }
+  __host__ __device__ static constexpr int u(int t, int v) { return v * CHUNK + t; }
+};
+
 struct IntraArgs {
   const void* q;
   const void* k;
@@ -96,6 +108,10 @@ struct IntraArgs {
   const float* conv_w;
   const float* conv_b;
   int conv_silu;
+  // backward recomputation only (kernel parameter BWD): T = (I + A)^{-1}
+  // [chunks][H][64][64] and (Diag(beta) (k^ * E))^T [chunks][H][128][64], FP32
+  float* tmat;
+  float* bwt;
 };
 
 // Chunk c -> (first token, length, first token of its sequence).  cfirst is
@@ -202,7 +218,9 @@ __device__ __forceinline__ void conv16(f32x2 (&x)[16], const f32x2 (&hist)[3], c
 // Index of cross-block combination (R, I), R > I, in 0..5.
 __device__ __forceinline__ constexpr int combo(int R, int I) { return (R * (R - 1)) / 2 + I; }
 
-template <typename TA, typename MT, bool CONV>
+// LY: record layout (Frag for the forward's state pass, PlainRec for the
+// backward).  BWD: also store T and the W product's right-hand operand.
+template <typename TA, typename MT, bool CONV, typename LY = Frag<MT>, bool BWD = false>
 __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
   typedef IntraLds<MT> L;
   constexpr int ROWL = L::ROWL, TL = L::TL, AL = L::AL;
@@ -351,7 +369,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
       const float rq = rsqrt_hw(cqq[e] + p.eps);
       sRk[r] = rk;
       sRq[r] = rq;
-      gP[Frag<MT>::pm(r, r)] = from_f32<MT>(rq * rk * cqk[e]);  // P[r][r], decay 1
+      gP[LY::pm(r, r)] = from_f32<MT>(rq * rk * cqk[e]);  // P[r][r], decay 1
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -396,7 +414,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
       for (int e = 0; e < 4; ++e) {
         const int ru = 16 * w + m0 + e;
         sA[ru * AL + ri] = sBeta[ru] * sRk[ru] * rki * ca[e];
-        gP[Frag<MT>::pm(ru, ri)] = from_f32<MT>(sRq[ru] * rki * cp[e]);
+        gP[LY::pm(ru, ri)] = from_f32<MT>(sRq[ru] * rki * cp[e]);
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -436,7 +454,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
             const float vp = e == 0 ? cp[0] : e == 1 ? cp[1] : e == 2 ? cp[2] : cp[3];
             const int ru = 16 * w + u, ri = 16 * w + i;
             sA[ru * AL + ri] = sBeta[ru] * sRk[ru] * sRk[ri] * va;
-            gP[Frag<MT>::pm(ru, ri)] = from_f32<MT>(sRq[ru] * sRk[ri] * vp);
+            gP[LY::pm(ru, ri)] = from_f32<MT>(sRq[ru] * sRk[ri] * vp);
           }
         }
       }
@@ -462,7 +480,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
       const int r = 16 * w + j;
       e0 *= aa[j][0]; e1 *= aa[j][1];
       const float rq = sRq[r];
-      store2(gQt + Frag<MT>::a(r, c0), qa[j][0] * rq * e0, qa[j][1] * rq * e1);
+      store2(gQt + LY::a(r, c0), qa[j][0] * rq * e0, qa[j][1] * rq * e1);
     }
     float s0 = sa[0], s1 = sa[1];
     float kb0[16], kb1[16];
@@ -475,8 +493,8 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
     }
 #pragma unroll
     for (int j = 0; j < 16; j += 4) {
-      store4(gKbT + Frag<MT>::kb(c0, 16 * w + j), f32x4{kb0[j], kb0[j + 1], kb0[j + 2], kb0[j + 3]});
-      store4(gKbT + Frag<MT>::kb(c0 + 1, 16 * w + j),
+      store4(gKbT + LY::kb(c0, 16 * w + j), f32x4{kb0[j], kb0[j + 1], kb0[j + 2], kb0[j + 3]});
+      store4(gKbT + LY::kb(c0 + 1, 16 * w + j),
              f32x4{kb1[j], kb1[j + 1], kb1[j + 2], kb1[j + 3]});
     }
     if (w == 0) {
@@ -540,7 +558,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int ru = 16 * R + m0 + e;
-      if (isq) gP[Frag<MT>::pm(ru, ri)] = from_f32<MT>(sRq[ru] * sRk[ri] * c[e]);
+      if (isq) gP[LY::pm(ru, ri)] = from_f32<MT>(sRq[ru] * sRk[ri] * c[e]);
       else sA[ru * AL + ri] = sBeta[ru] * sRk[ru] * sRk[ri] * c[e];
     }
   }
@@ -548,7 +566,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
   // FE consecutive columns of one row: fragments wholly above the diagonal are
   // written as one vector, the one straddling it element by element.
   {
-    constexpr int FE = Frag<MT>::FE;
+    constexpr int FE = LY::FE;
     typedef typename std::conditional<sizeof(MT) == 2, bf16x8, f32x4>::type v16;
     for (int f = tid; f < CHUNK * CHUNK / FE; f += 256) {
       const int r = f / (CHUNK / FE), i0 = (f % (CHUNK / FE)) * FE;
@@ -556,9 +574,9 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
         v16 z;
 #pragma unroll
         for (int e = 0; e < FE; ++e) z[e] = from_f32<MT>(0.0f);
-        *reinterpret_cast<v16*>(gP + Frag<MT>::pm(r, i0)) = z;
+        *reinterpret_cast<v16*>(gP + LY::pm(r, i0)) = z;
       } else {
-        for (int i = r + 1; i < i0 + FE; ++i) gP[Frag<MT>::pm(r, i)] = from_f32<MT>(0.0f);
+        for (int i = r + 1; i < i0 + FE; ++i) gP[LY::pm(r, i)] = from_f32<MT>(0.0f);
       }
     }
   }
@@ -692,6 +710,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
   for (int x = tid; x < CHUNK * CHUNK; x += 256) {
     const int r = x >> 6, i = x & 63;
     sTs[r * TL + i] = from_f32<MT>(sT[r * AL + i]);
+    if constexpr (BWD) p.tmat[((size_t)chunk * H + h) * CHUNK * CHUNK + x] = sT[r * AL + i];
   }
   {
     float e0 = pb[0], e1 = pb[1];
@@ -706,6 +725,11 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
     for (int j = 0; j < 16; j += 4) {
       store4(sXt + c0 * TL + 16 * w + j, f32x4{kg0[j], kg0[j + 1], kg0[j + 2], kg0[j + 3]});
       store4(sXt + (c0 + 1) * TL + 16 * w + j, f32x4{kg1[j], kg1[j + 1], kg1[j + 2], kg1[j + 3]});
+      if constexpr (BWD) {
+        float* gb = p.bwt + ((size_t)chunk * H + h) * DH * CHUNK;
+        store4(gb + c0 * CHUNK + 16 * w + j, f32x4{kg0[j], kg0[j + 1], kg0[j + 2], kg0[j + 3]});
+        store4(gb + (c0 + 1) * CHUNK + 16 * w + j, f32x4{kg1[j], kg1[j + 1], kg1[j + 2], kg1[j + 3]});
+      }
     }
   }
   __syncthreads();
@@ -717,7 +741,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
     c = mma16_rows<MT, CHUNK>(sXt + 16 * mt * TL, TL, sTs + 16 * nt * TL, TL, c, l);
     // c[e] = W^T[16mt + 4(l/16) + e][16nt + l%16] = W[tok][ch..ch+3]
     const int tok = 16 * nt + (l & 15), ch = 16 * mt + 4 * (l >> 4);
-    store4(gW + Frag<MT>::a(tok, ch), c);
+    store4(gW + LY::a(tok, ch), c);
   }
   __syncthreads();
   // U = T (Diag(beta) v)
@@ -742,7 +766,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
     c = mma16_rows<MT, CHUNK>(sTs + 16 * mt * TL, TL, sXt + 16 * nt * TL, TL, c, l);
     // c[e] = U[16mt + 4(l/16) + e][16nt + l%16]: four consecutive tokens
     const int dv = 16 * nt + (l & 15), tok = 16 * mt + 4 * (l >> 4);
-    store4(gUT + Frag<MT>::u(tok, dv), c);
+    store4(gUT + LY::u(tok, dv), c);
   }
 }
 

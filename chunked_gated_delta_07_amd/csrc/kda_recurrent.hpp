@@ -42,12 +42,6 @@ struct RecArgs {
   float scale;
 };
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
-  return x;
-}
-
 // DK key channels (q, k, f, dt_bias rows; state rows), p.dv value channels
 // (v, out rows; state columns).  blockDim.x >= max(DK, dv), a multiple of 64,
 // at most rec_max_threads(DK): a 128-entry state column needs more than the

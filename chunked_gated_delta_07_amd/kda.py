@@ -25,7 +25,7 @@ KDA_OUT_FP32 = 0x4
 # Exported symbols, in declaration order of include/kda.h.
 SYMBOLS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_state",
            "kda_chunk_fwd_conv", "kda_recurrent_fwd", "kda_recurrent_fwd_rect",
-           "kda_chunk_fwd_num_stages",
+           "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_chunk_fwd_num_stages",
            "kda_chunk_fwd_timed", "kda_status_string")
 
 _lib = None
@@ -71,6 +71,12 @@ def load_library(path: str = LIB_PATH):
     lib.kda_recurrent_fwd_rect.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32,
                                            ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_int32, ctypes.c_uint32, vp, vp, vp, vp]
+    lib.kda_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_chunk_bwd_workspace_bytes.argtypes = lib.kda_chunk_fwd_workspace_bytes.argtypes
+    lib.kda_chunk_bwd.restype = ctypes.c_int
+    lib.kda_chunk_bwd.argtypes = ([vp] * 8 + [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_uint32]
+                                  + [vp] * 11 + [vp, ctypes.c_size_t, vp])
     lib.kda_chunk_fwd_timed.restype = ctypes.c_int
     lib.kda_chunk_fwd_timed.argtypes = fwd_args + [ctypes.POINTER(vp), ctypes.c_int32]
     lib.kda_chunk_fwd_num_stages.restype = ctypes.c_int
@@ -272,3 +278,82 @@ def recurrent_fwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, out_fp32=Fa
     if st != KDA_OK:
         raise KdaError(st, where)
     return (out, final_state) if final_state is not None else out
+
+
+def bwd_workspace_bytes(total_tokens: int, num_seqs: int, H: int, d: int, mode: int) -> int:
+    n = load_library().kda_chunk_bwd_workspace_bytes(int(total_tokens), int(num_seqs), int(H),
+                                                     int(d), int(mode))
+    if n == ctypes.c_size_t(-1).value:
+        raise KdaError(KDA_ERR_INVALID_ARG, "kda_chunk_bwd_workspace_bytes")
+    return int(n)
+
+
+def chunk_bwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, dout, out_fp32=False,
+              initial_state=None, dfinal_state=None, return_dinitial_state=False,
+              workspace=None, stream=None):
+    """Backward (vector-Jacobian product) of the KDA chunked forward through
+    libkda, recomputed in FP32 (kda_chunk_bwd).
+
+    Inputs as for chunk_fwd, plus dout [T, H, 128] = dL/dout in the forward's
+    output dtype (float32 when out_fp32 or float32 activations, else the
+    activation dtype) and optionally dfinal_state [N, H, 128, 128] float32.
+    Returns a dict: dq, dk, dv, df (= dL/df_raw), db (= dL/db_raw) in dout's
+    dtype, dA_log [H] and ddt_bias [H, 128] float32, and dinit [N, H, 128,
+    128] float32 when initial_state, dfinal_state or return_dinitial_state is
+    given (the gradient of the start state; zero start if none was given)."""
+    import torch
+
+    lib = load_library()
+    act_fp32 = q.dtype == torch.float32
+    if not act_fp32 and q.dtype != torch.bfloat16:
+        raise TypeError("activations must be bfloat16 or float32")
+    for t in (k, v, f_raw, b_raw):
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, f_raw, b_raw must share one dtype")
+    if A_log.dtype != torch.float32 or dt_bias.dtype != torch.float32:
+        raise TypeError("A_log and dt_bias must be float32")
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    T, H, d = q.shape
+    gdtype = torch.float32 if (out_fp32 or act_fp32) else q.dtype
+    if dout.dtype != gdtype or tuple(dout.shape) != (T, H, d):
+        raise ValueError("dout must have the forward output's dtype and shape")
+    for t in (q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, dout):
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("all tensors must be contiguous device tensors")
+    if k.shape != q.shape or v.shape != q.shape or f_raw.shape != q.shape:
+        raise ValueError("q, k, v, f_raw must have one shape [T, H, d]")
+    if b_raw.shape != (T, H) or A_log.shape != (H,) or dt_bias.shape != (H, d):
+        raise ValueError("b_raw [T,H], A_log [H], dt_bias [H,d] expected")
+    num_seqs = cu_seqlens.numel() - 1
+    sshape = (num_seqs, H, d, d)
+    for t in (initial_state, dfinal_state):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != sshape
+                              or not t.is_contiguous() or not t.is_cuda):
+            raise ValueError("states must be contiguous float32 [N, H, d, d] device tensors")
+    mode = make_mode(True, act_fp32, out_fp32)
+    dev = q.device
+    g = {"dq": torch.empty((T, H, d), dtype=gdtype, device=dev),
+         "dk": torch.empty((T, H, d), dtype=gdtype, device=dev),
+         "dv": torch.empty((T, H, d), dtype=gdtype, device=dev),
+         "df": torch.empty((T, H, d), dtype=gdtype, device=dev),
+         "db": torch.empty((T, H), dtype=gdtype, device=dev),
+         "dA_log": torch.empty((H,), dtype=torch.float32, device=dev),
+         "ddt_bias": torch.empty((H, d), dtype=torch.float32, device=dev)}
+    want_dinit = initial_state is not None or dfinal_state is not None or return_dinitial_state
+    if want_dinit:
+        g["dinit"] = torch.empty(sshape, dtype=torch.float32, device=dev)
+    nbytes = bwd_workspace_bytes(T, max(num_seqs, 1), H, d, mode) if num_seqs >= 1 else 0
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    st = lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(f_raw), _ptr(b_raw), _ptr(A_log),
+                           _ptr(dt_bias), _ptr(cu_seqlens), num_seqs, T, H, d, mode,
+                           _ptr(initial_state), _ptr(dout), _ptr(dfinal_state), _ptr(g["dq"]),
+                           _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["df"]), _ptr(g["db"]),
+                           _ptr(g["dA_log"]), _ptr(g["ddt_bias"]), _ptr(g.get("dinit")),
+                           _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream.cuda_stream))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_chunk_bwd")
+    return g

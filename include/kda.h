@@ -191,6 +191,45 @@ KDA_API int kda_recurrent_fwd_rect(const void* q, const void* k, const void* v, 
                            int32_t H, int32_t dk, int32_t dv, uint32_t mode, void* out,
                            const float* initial_state, float* final_state, void* stream);
 
+/* Workspace bytes needed by kda_chunk_bwd (same arguments and failure value
+ * as kda_chunk_fwd_workspace_bytes).  FP32 throughout: about 560 KB per
+ * (64-token chunk, head), e.g. 9.2 GB for 16384 tokens x 64 heads. */
+KDA_API size_t kda_chunk_bwd_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t H,
+                                     int32_t d, uint32_t mode);
+
+/* Backward (vector-Jacobian product) of kda_chunk_fwd_state, recomputed in
+ * FP32: the pages' training path keeps "backward recomputation in FP32" and
+ * casts the input gradients back to the activation dtype (xtuner PR #2301,
+ * section Change), checks the gradients of q, k, v, the gate and beta against
+ * an FP64 recurrence VJP (same PR, section Validation), and sums the dt_bias
+ * gradient in FP32 (xtuner PR #2153, KDA module section).
+ * For L = <dout, out> + <dfinal_state, final_state> of the forward with the
+ * same inputs, writes
+ *   dq, dk, dv, df_raw [T][H][d], db_raw [T][H]: dL/d(input), in dout's dtype;
+ *   dA_log [H], ddt_bias [H][d]: float32 (overwritten, not accumulated);
+ *   dinitial_state [num_seqs][H][d][d] float32 (NULL: not returned): dL/dS_0,
+ *   also when initial_state is NULL (the forward then started from zero).
+ * Arguments as for kda_chunk_fwd_state, plus:
+ *  - dout [T][H][d]: float32 when mode has KDA_OUT_FP32 or KDA_ACT_FP32 (then
+ *    the gradients are float32 too), else bfloat16 (gradients bfloat16);
+ *  - dfinal_state: NULL means zero;
+ *  - KDA_MODE_FP32_INTERMEDIATE is accepted and changes nothing (every
+ *    intermediate of the backward is FP32, whatever the forward used);
+ *  - workspace of kda_chunk_bwd_workspace_bytes bytes, caller-owned, 256-byte
+ *    aligned; its contents on return are unspecified.
+ * total_tokens == 0: only dA_log, ddt_bias (zeroed) and dinitial_state
+ * (= dfinal_state, or zero) are written; the other pointers are not read.
+ * No output may alias an input.  Asynchronous on `stream`, no allocation, no
+ * host synchronisation.  Errors as for kda_chunk_fwd (dA_log and ddt_bias
+ * are required). */
+KDA_API int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* f_raw,
+                  const void* b_raw, const float* A_log, const float* dt_bias,
+                  const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens, int32_t H,
+                  int32_t d, uint32_t mode, const float* initial_state, const void* dout,
+                  const float* dfinal_state, void* dq, void* dk, void* dv, void* df_raw,
+                  void* db_raw, float* dA_log, float* ddt_bias, float* dinitial_state,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* Number of kernels kda_chunk_fwd launches for this mode (the stages timed by
  * kda_chunk_fwd_timed). */
 KDA_API int kda_chunk_fwd_num_stages(uint32_t mode);

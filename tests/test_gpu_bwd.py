@@ -1,0 +1,174 @@
+"""GPU parity of kda_chunk_bwd (the FP32-recomputed backward) against the FP64
+oracle's vector-Jacobian product of the token recurrence.
+
+The pages check the chunked operator's input gradients against an independent
+FP64 recurrence VJP with packed lengths 37/28, a chunk boundary at 129 and the
+64-head x 128 geometry at 65 tokens, require every nonzero gradient within 2 %
+relative error, and plant a 25 % gradient scaling error that must fail
+(xtuner PR #2301, section Validation); FP32 budgets of 0.3 % (dq, dk, dv) and
+0.5 % (gate, beta) are quoted in xtuner PR #2153.  Bars here, relative L2 over
+each whole gradient tensor:
+  * FP32 gradients (FP32 activations, or bf16 activations with KDA_OUT_FP32):
+    1e-4 -- the forward's FP32 bar; the backward's arithmetic is FP32 with
+    sums of at most a few hundred terms per output, far below it;
+  * bf16 gradients: 2e-2, the pages' BF16 budget (rounding of a correct
+    result to bf16 alone costs ~2e-3).
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+sys.path.insert(0, os.path.dirname(__file__))
+import kda_testutil as U  # noqa: E402
+
+import oracle  # noqa: E402
+from chunked_gated_delta_07_amd import synth  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TOL_FP32 = 1e-4
+TOL_BF16 = 2e-2
+KEYS = ("dq", "dk", "dv", "df", "db", "dA_log", "ddt_bias")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from chunked_gated_delta_07_amd import kda
+
+    kda.load_library()
+    yield
+
+
+def _case(lens, H, act, seed, with_states=True, grad_fp32=True):
+    """Seeded inputs, dout (rounded to its dtype) and optional states."""
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    inp = synth.make_inputs(cu, H=H, act=act, seed=seed)
+    rng = np.random.default_rng(seed + 7)
+    T, N = int(cu[-1]), len(lens)
+    dout = rng.standard_normal((T, H, 128)).astype(np.float32)
+    if not grad_fp32:
+        dout = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(dout))
+    init = dfin = None
+    if with_states:
+        init = (0.3 * rng.standard_normal((N, H, 128, 128))).astype(np.float32)
+        dfin = rng.standard_normal((N, H, 128, 128)).astype(np.float32)
+    return inp, dout, init, dfin
+
+
+def _gpu_bwd(inp, dout, init, dfin, grad_fp32):
+    import torch
+
+    from chunked_gated_delta_07_amd import kda
+
+    dev = "cuda:0"
+    args = U.to_device(inp, dev)
+    dt = torch.float32 if (grad_fp32 or inp.act == "fp32") else torch.bfloat16
+    g = kda.chunk_bwd(*args, torch.from_numpy(dout).to(dev).to(dt), out_fp32=grad_fp32,
+                      initial_state=None if init is None else torch.from_numpy(init).to(dev),
+                      dfinal_state=None if dfin is None else torch.from_numpy(dfin).to(dev),
+                      return_dinitial_state=True)
+    torch.cuda.synchronize()
+    return {k: v.to(torch.float64).cpu().numpy() for k, v in g.items()}
+
+
+def _oracle_bwd(inp, dout, init, dfin, plant=0):
+    x = inp.as_f64()
+    return oracle.kda_backward(x["q"], x["k"], x["v"], x["f_raw"], x["b_raw"], x["A_log"],
+                               x["dt_bias"], x["cu_seqlens"], dout.astype(np.float64),
+                               initial_state=init, dfinal_state=dfin, plant=plant)
+
+
+def _errors(got, ref, keys=KEYS + ("dinit",)):
+    return {k: U.rel_l2(got[k], ref[k]) for k in keys if k in got}
+
+
+def _check(got, ref, tol, label):
+    errs = _errors(got, ref)
+    print(label, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    for k, e in errs.items():
+        assert np.all(np.isfinite(got[k])), (label, k)
+        assert e < tol, (label, k, e)
+    return errs
+
+
+@pytest.mark.parametrize("act", ["fp32", "bf16"])
+def test_bwd_parity_packed_37_28(act):
+    """The pages' packed lengths 37/28, with start states and a final-state
+    gradient; FP32 gradients."""
+    inp, dout, init, dfin = _case([37, 28], 4, act, seed=1)
+    _check(_gpu_bwd(inp, dout, init, dfin, True), _oracle_bwd(inp, dout, init, dfin), TOL_FP32,
+           f"37/28 {act}")
+
+
+def test_bwd_parity_chunk_boundary_129():
+    """129 tokens: chunks of 64, 64 and 1 (FP32 activations, zero start)."""
+    inp, dout, _, _ = _case([129], 4, "fp32", seed=2, with_states=False)
+    _check(_gpu_bwd(inp, dout, None, None, True), _oracle_bwd(inp, dout, None, None), TOL_FP32,
+           "129")
+
+
+def test_bwd_parity_ragged_multi_chunk():
+    """Several chunks per sequence, ragged tails, an empty and a one-token
+    sequence, with states."""
+    inp, dout, init, dfin = _case([300, 1, 0, 64, 130, 65], 3, "bf16", seed=3)
+    _check(_gpu_bwd(inp, dout, init, dfin, True), _oracle_bwd(inp, dout, init, dfin), TOL_FP32,
+           "ragged")
+
+
+def test_bwd_production_geometry_65_tokens():
+    """64 heads x 128 at 65 tokens (37/28), bf16 activations: FP32 gradients
+    to the FP32 bar and bf16 gradients to the pages' 2 % budget."""
+    inp, dout, init, dfin = _case([37, 28], 64, "bf16", seed=4, with_states=False, grad_fp32=False)
+    ref = _oracle_bwd(inp, dout, None, None)
+    _check(_gpu_bwd(inp, dout, None, None, True), ref, TOL_FP32, "H64 fp32-grad")
+    _check(_gpu_bwd(inp, dout, None, None, False), ref, TOL_BF16, "H64 bf16-grad")
+
+
+def test_bwd_planted_scale_error_fails():
+    """The pages' negative control: a 25 % scaling of one gradient (in the
+    oracle) is far outside the bar the GPU result meets."""
+    inp, dout, init, dfin = _case([37, 28], 2, "fp32", seed=5)
+    got = _gpu_bwd(inp, dout, init, dfin, True)
+    bad = _oracle_bwd(inp, dout, init, dfin, plant=oracle.BWD_PLANT["bwd_beta_scale"])
+    assert U.rel_l2(got["db"], bad["db"]) > 100 * TOL_FP32
+
+
+def test_bwd_strong_gates_and_special_values():
+    """Strong decay (A_log up to ln 64), saturated beta (b = +-inf) and a head
+    with the gate switched off (A_log = -inf)."""
+    inp, dout, init, dfin = _case([200, 70], 4, "fp32", seed=6)
+    inp.A_log[:] = np.array([np.log(64.0), -np.inf, 0.0, np.log(16.0)], dtype=np.float32)
+    inp.b_raw[5, 0] = np.inf
+    inp.b_raw[100, 2] = -np.inf
+    got = _gpu_bwd(inp, dout, init, dfin, True)
+    ref = _oracle_bwd(inp, dout, init, dfin)
+    _check(got, ref, TOL_FP32, "strong/special")
+    assert got["db"][5, 0] == 0.0 and got["db"][100, 2] == 0.0
+    assert np.all(got["df"][:, 1] == 0) and got["dA_log"][1] == 0.0
+
+
+def test_bwd_empty_batch_and_zero_dout():
+    import torch
+
+    from chunked_gated_delta_07_amd import kda
+
+    dev = "cuda:0"
+    # T = 0: dS_init = dS_final, parameter gradients zero
+    inp = synth.make_inputs(np.array([0, 0, 0], dtype=np.int32), H=2, act="bf16", seed=8)
+    args = U.to_device(inp, dev)
+    dfin = torch.randn(2, 2, 128, 128, device=dev)
+    g = kda.chunk_bwd(*args, torch.empty((0, 2, 128), dtype=torch.bfloat16, device=dev),
+                      dfinal_state=dfin)
+    torch.cuda.synchronize()
+    assert torch.equal(g["dinit"], dfin)
+    assert torch.all(g["dA_log"] == 0) and torch.all(g["ddt_bias"] == 0)
+    # zero output gradient and no final-state gradient: every gradient is zero
+    inp = synth.make_inputs(np.array([0, 90], dtype=np.int32), H=2, act="fp32", seed=9)
+    got = _gpu_bwd(inp, np.zeros((90, 2, 128), np.float32), None, None, True)
+    for k in KEYS:
+        assert np.all(got[k] == 0), k

@@ -258,6 +258,41 @@ def time_conv(args_dev, steps: int, warmup: int):
             "tokens_per_s": round(T / (p50 * 1e-6), 1)}
 
 
+def time_bwd(args_dev, steps: int, warmup: int):
+    """kda_chunk_bwd on the headline workload: the FP32-recomputed backward
+    with bf16 activations, bf16 output gradient and bf16 input gradients
+    (the pages' training path casts input gradients back to the activation
+    dtype), a random dout.  Step time from HIP events on the launch stream."""
+    import torch
+
+    from chunked_gated_delta_07_amd import kda
+
+    q = args_dev[0]
+    T, H, d = q.shape
+    g = torch.Generator().manual_seed(4245)
+    dout = torch.randn((T, H, d), generator=g).to(torch.bfloat16).to(q.device)
+    N = args_dev[7].numel() - 1
+    ws = torch.empty(kda.bwd_workspace_bytes(T, N, H, d, kda.make_mode(True)), dtype=torch.uint8,
+                     device=q.device)
+    for _ in range(warmup):
+        kda.chunk_bwd(*args_dev, dout, workspace=ws)
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, e in evs:
+        a.record(stream)
+        kda.chunk_bwd(*args_dev, dout, workspace=ws)
+        e.record(stream)
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(e) * 1e3 for a, e in evs)
+    p50 = statistics.median(us)
+    del ws
+    return {"entry_point": "kda_chunk_bwd", "workload": "headline, dout bf16, gradients bf16",
+            "intermediates": "fp32", "p50_us": round(p50, 2), "max_us": round(us[-1], 2),
+            "tokens_per_s": round(T / (p50 * 1e-6), 1)}
+
+
 def roofline_for(mode_name: str, T: int, H: int, res: dict, workload: str):
     """Dominant kernel of the path (by measured time) against its roofline."""
     names = ["chunk_table", "intra", "state_pass"]
@@ -296,6 +331,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode-step measurement of the token-serial path")
+    ap.add_argument("--no-bwd", action="store_true",
+                    help="skip the backward (kda_chunk_bwd) measurement")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--only-mode", choices=["bf16", "fp32"], default=None,
                     help="time one precision mode only (for profiling runs)")
@@ -372,6 +409,8 @@ def main():
             line[f"{m}_mode"]["graph_replay"] = graph[m]
     if args.only_mode is None:
         line["conv_fused"] = time_conv(args_dev, max(args.steps, 10), max(args.warmup, 2))
+    if not args.no_bwd and args.only_mode is None:
+        line["backward"] = time_bwd(args_dev, max(args.steps // 2, 5), max(args.warmup, 2))
     if not args.no_decode and args.only_mode is None:
         line["decode"] = time_decode(256, H, max(args.steps, 10), max(args.warmup, 2))
     line["context_h200_p50_us"] = H200_CONTEXT_P50_US

@@ -172,3 +172,31 @@ def test_bwd_empty_batch_and_zero_dout():
     got = _gpu_bwd(inp, np.zeros((90, 2, 128), np.float32), None, None, True)
     for k in KEYS:
         assert np.all(got[k] == 0), k
+
+
+def test_bwd_headline_size_sampled_heads():
+    """The benchmark's workload (16384 tokens x 64 heads, bf16 activations, one
+    call in the benchmark's launch configuration): heads 0 and 41 against the
+    oracle (heads are independent, so the oracle runs on those two alone)."""
+    import torch
+
+    inp = synth.config_inputs(3)
+    T, H = inp.T, inp.H
+    rng = np.random.default_rng(77)
+    dout = synth.bf16_bits_to_f32(
+        synth.f32_to_bf16_bits(rng.standard_normal((T, H, 128)).astype(np.float32)))
+    got32 = _gpu_bwd(inp, dout, None, None, True)
+    got16 = _gpu_bwd(inp, dout, None, None, False)
+    torch.cuda.empty_cache()
+    heads = np.array([0, 41])
+    x = inp.as_f64()
+    ref = oracle.kda_backward(x["q"][:, heads], x["k"][:, heads], x["v"][:, heads],
+                              x["f_raw"][:, heads], x["b_raw"][:, heads], x["A_log"][heads],
+                              x["dt_bias"][heads], x["cu_seqlens"],
+                              dout[:, heads].astype(np.float64))
+    for got, tol, lab in ((got32, TOL_FP32, "fp32-grad"), (got16, TOL_BF16, "bf16-grad")):
+        sub = {k: (got[k][:, heads] if k in ("dq", "dk", "dv", "df", "db") else got[k][heads])
+               for k in KEYS}
+        _check(sub, ref, tol, f"16384x64 {lab}")
+        for k in ("dq", "dk", "dv", "df", "db"):
+            assert np.all(np.isfinite(got[k])), k

@@ -117,75 +117,125 @@ __device__ __forceinline__ void scan_block(int bid, int& pair, int& vb) {
   vb = (bid >> 3) & 3;
 }
 
+// Both state scans keep every MFMA operand in LDS with its contracted index
+// contiguous ("rows of K", 16-byte reads feeding four FP32 MFMAs), transposing
+// where a record's stored order differs, and the state itself transposed
+// ([value][key]).  The next chunk's records are loaded into registers while
+// the second product of the current chunk runs, then written to LDS.
+constexpr int SL_LONG = 132;  // padded row of 128
+constexpr int SL_SHORT = 68;  // padded row of 64
+
+// Eight consecutive dout values of one row, scaled.
+__device__ __forceinline__ void load8_scaled(const bf16* p, float s, float (&o)[8]) {
+  const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = s * (float)v[e];
+}
+__device__ __forceinline__ void load8_scaled(const float* p, float s, float (&o)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { o[e] = s * a[e]; o[4 + e] = s * b[e]; }
+}
+
 // ------------------------------------------------------------ 2. forward scan
-// S_next = Diag(Gam) S0 + Kb^T (U - W S0), value block [128][32] of S in LDS.
+// Per chunk: snapshot S0; D = U - W S0; S_next = Diag(Gam) S0 + Kb^T D.
+// LDS: W [64][128] (rows of K over keys), Kb^T [128][64] (over tokens),
+// U^T block [32][64], S^T block [32 value][128 key], D^T [32][64], Gam.
 __global__ __launch_bounds__(256) void kda_bwd_fscan_kernel(BwdArgs p) {
-  constexpr int LW = 132, LK = 68, LS = 36;
-  __shared__ __attribute__((aligned(16))) float sW[CHUNK * LW];
-  __shared__ __attribute__((aligned(16))) float sKbT[DH * LK];
-  __shared__ __attribute__((aligned(16))) float sS[DH * LS];
-  __shared__ __attribute__((aligned(16))) float sD[CHUNK * LS];
+  constexpr int LL = SL_LONG, LS = SL_SHORT;
+  __shared__ __attribute__((aligned(16))) float sW[CHUNK * LL];
+  __shared__ __attribute__((aligned(16))) float sKbT[DH * LS];
+  __shared__ __attribute__((aligned(16))) float sUT[32 * LS];
+  __shared__ __attribute__((aligned(16))) float sST[32 * LL];
+  __shared__ __attribute__((aligned(16))) float sDT[32 * LS];
+  __shared__ __attribute__((aligned(16))) float sGam[DH];
   int pair, vb;
   scan_block(blockIdx.x, pair, vb);
   if (pair >= p.N * p.H) return;
   const int n = pair / p.H, h = pair - n * p.H;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int v0 = 32 * vb;
+  const int c_lo = p.cfirst[n], c_hi = p.cfirst[n + 1];
   for (int x = tid; x < DH * 32; x += 256) {
     const int i = x >> 5, j = x & 31;
-    sS[i * LS + j] = p.init ? p.init[((size_t)pair * DH + i) * DH + v0 + j] : 0.0f;
+    sST[j * LL + i] = p.init ? p.init[((size_t)pair * DH + i) * DH + v0 + j] : 0.0f;
   }
-  const int c_lo = p.cfirst[n], c_hi = p.cfirst[n + 1];
+  // register staging of one chunk's records: W 8, Kb^T 8, U^T 2 f32x4 per thread, Gam
+  f32x4 rW[8], rK[8], rU[2], rG;
+  auto fetch = [&](int c) {
+    const size_t ch = (size_t)c * p.H + h;
+    const float* rec = p.rec + ch * REC;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int x = tid + 256 * u;
+      rW[u] = *reinterpret_cast<const f32x4*>(rec + OFF_W + 4 * x);   // row x/32, cols 4(x%32)
+      rK[u] = *reinterpret_cast<const f32x4*>(rec + OFF_KBT + 4 * x); // row x/16, cols 4(x%16)
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int x = tid + 256 * u;  // U^T row v0 + x/16, tokens 4(x%16)
+      rU[u] = *reinterpret_cast<const f32x4*>(rec + OFF_UT + (v0 + (x >> 4)) * CHUNK + 4 * (x & 15));
+    }
+    if (tid < 32) rG = *reinterpret_cast<const f32x4*>(p.gam + ch * DH + 4 * tid);
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int x = tid + 256 * u;
+      *reinterpret_cast<f32x4*>(sW + (x >> 5) * LL + 4 * (x & 31)) = rW[u];
+      *reinterpret_cast<f32x4*>(sKbT + (x >> 4) * LS + 4 * (x & 15)) = rK[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int x = tid + 256 * u;
+      *reinterpret_cast<f32x4*>(sUT + (x >> 4) * LS + 4 * (x & 15)) = rU[u];
+    }
+    if (tid < 32) *reinterpret_cast<f32x4*>(sGam + 4 * tid) = rG;
+  };
+  if (c_lo < c_hi) {
+    fetch(c_lo);
+    stage();
+  }
   __syncthreads();
   for (int c = c_lo; c < c_hi; ++c) {
     const size_t ch = (size_t)c * p.H + h;
-    const float* rec = p.rec + ch * REC;
     float* snap = p.s0 + ch * STM;
-    for (int x = tid; x < DH * 8; x += 256) {
-      const int i = x >> 3, j4 = 4 * (x & 7);
-      store4(snap + i * DH + v0 + j4, *reinterpret_cast<const f32x4*>(sS + i * LS + j4));
+    for (int x = tid; x < DH * 32; x += 256) {
+      const int i = x >> 5, j = x & 31;
+      snap[i * DH + v0 + j] = sST[j * LL + i];
     }
-    for (int x = tid; x < CHUNK * 32; x += 256) {
-      const int r = x >> 5, c4 = 4 * (x & 31);
-      *reinterpret_cast<f32x4*>(sW + r * LW + c4) =
-          *reinterpret_cast<const f32x4*>(rec + OFF_W + r * DH + c4);
-    }
-    for (int x = tid; x < DH * 16; x += 256) {
-      const int i = x >> 4, t4 = 4 * (x & 15);
-      *reinterpret_cast<f32x4*>(sKbT + i * LK + t4) =
-          *reinterpret_cast<const f32x4*>(rec + OFF_KBT + i * CHUNK + t4);
-    }
-    __syncthreads();
-    // D = U - W S0: wave w owns token rows 16w..16w+15, both 16-column halves
+    // D[r][j] = U[r][j] - sum_c W[r][c] S[c][j]: wave w rows 16w.., both column halves
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       f32x4 acc = {0, 0, 0, 0};
-      acc = mma16_f32_kn<DH>(sW + 16 * w * LW, LW, sS + 16 * cb, LS, acc, l);
+      acc = mma16_rows<float, DH>(sW + 16 * w * LL, LL, sST + 16 * cb * LL, LL, acc, l);
       const int j = 16 * cb + (l & 15);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * w + 4 * (l >> 4) + e;
-        const float d = rec[OFF_UT + (v0 + j) * CHUNK + r] - acc[e];
-        sD[r * LS + j] = d;
+        const float d = sUT[j * LS + r] - acc[e];
+        sDT[j * LS + r] = d;
         p.dmat[ch * MAT + r * DH + v0 + j] = d;
       }
     }
     __syncthreads();
-    // S_next = Diag(Gam) S0 + Kb^T D: wave w owns key rows 32w..32w+31
+    const bool more = c + 1 < c_hi;
+    if (more) fetch(c + 1);
+    // S_next[i][j] = Gam_i S[i][j] + sum_r KbT[i][r] D[r][j]: wave w key rows 32w..32w+31
     f32x4 ns[2][2];
-    const float* gam = p.gam + ch * DH;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
       const int kb = 2 * w + kb2;
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
         f32x4 acc;
+        const int j = 16 * cb + (l & 15);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 16 * kb + 4 * (l >> 4) + e;
-          acc[e] = gam[i] * sS[i * LS + 16 * cb + (l & 15)];
+          acc[e] = sGam[i] * sST[j * LL + i];
         }
-        ns[kb2][cb] = mma16_f32_kn<CHUNK>(sKbT + 16 * kb * LK, LK, sD + 16 * cb, LS, acc, l);
+        ns[kb2][cb] = mma16_rows<float, CHUNK>(sKbT + 16 * kb * LS, LS, sDT + 16 * cb * LS, LS, acc, l);
       }
     }
     __syncthreads();
@@ -195,24 +245,29 @@ __global__ __launch_bounds__(256) void kda_bwd_fscan_kernel(BwdArgs p) {
       for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          sS[(16 * (2 * w + kb2) + 4 * (l >> 4) + e) * LS + 16 * cb + (l & 15)] = ns[kb2][cb][e];
+          sST[(16 * cb + (l & 15)) * LL + 16 * (2 * w + kb2) + 4 * (l >> 4) + e] = ns[kb2][cb][e];
+    if (more) stage();
     __syncthreads();
   }
 }
 
 // ------------------------------------------------------------ 3. reverse scan
-// Chunks in reverse order: snapshot dSn, dD = scale P^T dO + Kb dSn,
+// Chunks in reverse order: snapshot dSn; dD = scale P^T dO + Kb dSn;
 // dS0 = Diag(Gam) dSn + scale Qt^T dO - W^T dD.  Ends with dS_init.
+// LDS (rows of K): P^T [64 r][64 i], Kb [64 r][128 c], Qt^T [128 i][64 r],
+// W^T [128][64], (scale dO)^T block [32 j][64 r], dS^T block [32][128],
+// dD^T [32][64], Gam.
 template <typename TG>
 __global__ __launch_bounds__(256) void kda_bwd_bscan_kernel(BwdArgs p) {
-  constexpr int LW = 132, LK = 68, LS = 36;
-  __shared__ __attribute__((aligned(16))) float sW[CHUNK * LW];
-  __shared__ __attribute__((aligned(16))) float sQt[CHUNK * LW];
-  __shared__ __attribute__((aligned(16))) float sKbT[DH * LK];
-  __shared__ __attribute__((aligned(16))) float sP[CHUNK * LK];
-  __shared__ __attribute__((aligned(16))) float sO[CHUNK * LS];
-  __shared__ __attribute__((aligned(16))) float sS[DH * LS];
-  __shared__ __attribute__((aligned(16))) float sD[CHUNK * LS];
+  constexpr int LL = SL_LONG, LS = SL_SHORT;
+  __shared__ __attribute__((aligned(16))) float sPT[CHUNK * LS];
+  __shared__ __attribute__((aligned(16))) float sKb[CHUNK * LL];
+  __shared__ __attribute__((aligned(16))) float sQtT[DH * LS];
+  __shared__ __attribute__((aligned(16))) float sWT[DH * LS];
+  __shared__ __attribute__((aligned(16))) float sOT[32 * LS];
+  __shared__ __attribute__((aligned(16))) float sST[32 * LL];
+  __shared__ __attribute__((aligned(16))) float sDT[32 * LS];
+  __shared__ __attribute__((aligned(16))) float sGam[DH];
   int pair, vb;
   scan_block(blockIdx.x, pair, vb);
   if (pair >= p.N * p.H) return;
@@ -220,76 +275,114 @@ __global__ __launch_bounds__(256) void kda_bwd_bscan_kernel(BwdArgs p) {
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int v0 = 32 * vb;
   const TG* __restrict__ gO = reinterpret_cast<const TG*>(p.dout);
-  for (int x = tid; x < DH * 32; x += 256) {
-    const int i = x >> 5, j = x & 31;
-    sS[i * LS + j] = p.dfin ? p.dfin[((size_t)pair * DH + i) * DH + v0 + j] : 0.0f;
-  }
   const int c_lo = p.cfirst[n], c_hi = p.cfirst[n + 1];
   const int tseq = p.cu[n], tend = p.cu[n + 1];
+  for (int x = tid; x < DH * 32; x += 256) {
+    const int i = x >> 5, j = x & 31;
+    sST[j * LL + i] = p.dfin ? p.dfin[((size_t)pair * DH + i) * DH + v0 + j] : 0.0f;
+  }
+  // register staging: P 4, Kb^T 8, Qt 8, W 8 f32x4, dO 8 values, Gam
+  f32x4 rP[4], rK[8], rQ[8], rW[8], rG;
+  float rO[8];
+  auto fetch = [&](int c) {
+    const size_t ch = (size_t)c * p.H + h;
+    const float* rec = p.rec + ch * REC;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      rP[u] = *reinterpret_cast<const f32x4*>(rec + OFF_P + 4 * (tid + 256 * u));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int x = tid + 256 * u;
+      rK[u] = *reinterpret_cast<const f32x4*>(rec + OFF_KBT + 4 * x);
+      rQ[u] = *reinterpret_cast<const f32x4*>(rec + OFF_QT + 4 * x);
+      rW[u] = *reinterpret_cast<const f32x4*>(rec + OFF_W + 4 * x);
+    }
+    const int t0 = tseq + (c - c_lo) * CHUNK, len = min(CHUNK, tend - t0);
+    const int r = tid >> 2, j8 = 8 * (tid & 3);
+    if (r < len) {
+      load8_scaled(gO + ((size_t)(t0 + r) * p.H + h) * DH + v0 + j8, p.scale, rO);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rO[e] = 0.0f;
+    }
+    if (tid < 32) rG = *reinterpret_cast<const f32x4*>(p.gam + ch * DH + 4 * tid);
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {  // P row i = x/16, cols r = 4(x%16).. -> P^T[r][i]
+      const int x = tid + 256 * u, i = x >> 4, r4 = 4 * (x & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sPT[(r4 + e) * LS + i] = rP[u][e];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int x = tid + 256 * u;
+      {  // Kb^T row c = x/16, tokens 4(x%16).. -> Kb[t][c]
+        const int c = x >> 4, t4 = 4 * (x & 15);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sKb[(t4 + e) * LL + c] = rK[u][e];
+      }
+      {  // Qt / W row r = x/32, channels 4(x%32).. -> [channel][r]
+        const int r = x >> 5, c4 = 4 * (x & 31);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sQtT[(c4 + e) * LS + r] = rQ[u][e];
+          sWT[(c4 + e) * LS + r] = rW[u][e];
+        }
+      }
+    }
+    {
+      const int r = tid >> 2, j8 = 8 * (tid & 3);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sOT[(j8 + e) * LS + r] = rO[e];
+    }
+    if (tid < 32) *reinterpret_cast<f32x4*>(sGam + 4 * tid) = rG;
+  };
+  if (c_lo < c_hi) {
+    fetch(c_hi - 1);
+    stage();
+  }
   __syncthreads();
   for (int c = c_hi - 1; c >= c_lo; --c) {
     const size_t ch = (size_t)c * p.H + h;
-    const float* rec = p.rec + ch * REC;
-    const int t0 = tseq + (c - c_lo) * CHUNK;
-    const int len = min(CHUNK, tend - t0);
     float* snap = p.dsn + ch * STM;
-    for (int x = tid; x < DH * 8; x += 256) {
-      const int i = x >> 3, j4 = 4 * (x & 7);
-      store4(snap + i * DH + v0 + j4, *reinterpret_cast<const f32x4*>(sS + i * LS + j4));
+    for (int x = tid; x < DH * 32; x += 256) {
+      const int i = x >> 5, j = x & 31;
+      snap[i * DH + v0 + j] = sST[j * LL + i];
     }
-    for (int x = tid; x < CHUNK * 32; x += 256) {
-      const int r = x >> 5, c4 = 4 * (x & 31);
-      *reinterpret_cast<f32x4*>(sW + r * LW + c4) =
-          *reinterpret_cast<const f32x4*>(rec + OFF_W + r * DH + c4);
-      *reinterpret_cast<f32x4*>(sQt + r * LW + c4) =
-          *reinterpret_cast<const f32x4*>(rec + OFF_QT + r * DH + c4);
-    }
-    for (int x = tid; x < DH * 16; x += 256) {
-      const int i = x >> 4, t4 = 4 * (x & 15);
-      *reinterpret_cast<f32x4*>(sKbT + i * LK + t4) =
-          *reinterpret_cast<const f32x4*>(rec + OFF_KBT + i * CHUNK + t4);
-    }
-    for (int x = tid; x < CHUNK * 16; x += 256) {
-      const int r = x >> 4, i4 = 4 * (x & 15);
-      *reinterpret_cast<f32x4*>(sP + r * LK + i4) =
-          *reinterpret_cast<const f32x4*>(rec + OFF_P + r * CHUNK + i4);
-    }
-    for (int x = tid; x < CHUNK * 32; x += 256) {
-      const int r = x >> 5, j = x & 31;
-      sO[r * LS + j] = r < len ? p.scale * to_f32(gO[((size_t)(t0 + r) * p.H + h) * DH + v0 + j]) : 0.0f;
-    }
-    __syncthreads();
-    // dD = P^T (scale dO) + Kb dSn: wave w owns token rows 16w..16w+15
+    // dD[r][j] = sum_i P^T[r][i] dO^T[j][i] + sum_c Kb[r][c] dS^T[j][c]: wave w rows 16w..
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       f32x4 acc = {0, 0, 0, 0};
-      acc = mma16_f32_tn<CHUNK>(sP + 16 * w, LK, sO + 16 * cb, LS, acc, l);
-      acc = mma16_f32_tn<DH>(sKbT + 16 * w, LK, sS + 16 * cb, LS, acc, l);
+      acc = mma16_rows<float, CHUNK>(sPT + 16 * w * LS, LS, sOT + 16 * cb * LS, LS, acc, l);
+      acc = mma16_rows<float, DH>(sKb + 16 * w * LL, LL, sST + 16 * cb * LL, LL, acc, l);
       const int j = 16 * cb + (l & 15);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * w + 4 * (l >> 4) + e;
-        sD[r * LS + j] = acc[e];
+        sDT[j * LS + r] = acc[e];
         p.ddmat[ch * MAT + r * DH + v0 + j] = acc[e];
       }
     }
     __syncthreads();
-    // dS0 = Diag(Gam) dSn + Qt^T (scale dO) - W^T dD: wave w owns key rows 32w..32w+31
+    const bool more = c > c_lo;
+    if (more) fetch(c - 1);
+    // dS0[i][j] = Gam_i dSn[i][j] + sum_r Qt^T[i][r] dO^T[j][r] - sum_r W^T[i][r] dD^T[j][r]
     f32x4 ns[2][2];
-    const float* gam = p.gam + ch * DH;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
       const int kb = 2 * w + kb2;
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
         f32x4 acc, neg = {0, 0, 0, 0};
+        const int j = 16 * cb + (l & 15);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 16 * kb + 4 * (l >> 4) + e;
-          acc[e] = gam[i] * sS[i * LS + 16 * cb + (l & 15)];
+          acc[e] = sGam[i] * sST[j * LL + i];
         }
-        acc = mma16_f32_tn<CHUNK>(sQt + 16 * kb, LW, sO + 16 * cb, LS, acc, l);
-        neg = mma16_f32_tn<CHUNK>(sW + 16 * kb, LW, sD + 16 * cb, LS, neg, l);
+        acc = mma16_rows<float, CHUNK>(sQtT + 16 * kb * LS, LS, sOT + 16 * cb * LS, LS, acc, l);
+        neg = mma16_rows<float, CHUNK>(sWT + 16 * kb * LS, LS, sDT + 16 * cb * LS, LS, neg, l);
         ns[kb2][cb] = acc - neg;
       }
     }
@@ -300,14 +393,14 @@ __global__ __launch_bounds__(256) void kda_bwd_bscan_kernel(BwdArgs p) {
       for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          sS[(16 * (2 * w + kb2) + 4 * (l >> 4) + e) * LS + 16 * cb + (l & 15)] = ns[kb2][cb][e];
+          sST[(16 * cb + (l & 15)) * LL + 16 * (2 * w + kb2) + 4 * (l >> 4) + e] = ns[kb2][cb][e];
+    if (more) stage();
     __syncthreads();
   }
   if (p.dinit) {
-    for (int x = tid; x < DH * 8; x += 256) {
-      const int i = x >> 3, j4 = 4 * (x & 7);
-      store4(p.dinit + ((size_t)pair * DH + i) * DH + v0 + j4,
-             *reinterpret_cast<const f32x4*>(sS + i * LS + j4));
+    for (int x = tid; x < DH * 32; x += 256) {
+      const int i = x >> 5, j = x & 31;
+      p.dinit[((size_t)pair * DH + i) * DH + v0 + j] = sST[j * LL + i];
     }
   }
 }
@@ -323,7 +416,7 @@ __device__ __forceinline__ bool bwd_chunk(const BwdArgs& p, int c, int& t0, int&
 // dGam = rowsum(dSn * S0); contracted over the 128 value channels in four
 // slabs of 32.  Wave w owns token rows 16w..16w+15 of every output.
 template <typename TG>
-__global__ __launch_bounds__(256) void kda_bwd_jprod_kernel(BwdArgs p) {
+__global__ __launch_bounds__(256, 2) void kda_bwd_jprod_kernel(BwdArgs p) {
   constexpr int LS = 36;
   __shared__ __attribute__((aligned(16))) float sO[CHUNK * LS];
   __shared__ __attribute__((aligned(16))) float sDm[CHUNK * LS];
@@ -342,28 +435,54 @@ __global__ __launch_bounds__(256) void kda_bwd_jprod_kernel(BwdArgs p) {
 #pragma unroll
   for (int x = 0; x < 4; ++x) ap[x] = f32x4{0, 0, 0, 0};
   float gacc = 0.0f;
-  for (int sl = 0; sl < 4; ++sl) {
+  // slab sl + 1 is loaded into registers while slab sl is multiplied; dout
+  // stays in its own dtype (raw 16 or 32 bytes) until it is written to LDS
+  constexpr int OW = sizeof(TG) == 2 ? 1 : 2;
+  f32x4 rO[OW];
+  f32x4 rD[2], rDD[2], rS0[4], rDS[4];
+  auto fetch = [&](int sl) {
     const int v0 = 32 * sl;
-    __syncthreads();
-    for (int x = tid; x < CHUNK * 32; x += 256) {
-      const int r = x >> 5, j = x & 31;
-      sO[r * LS + j] = r < len ? p.scale * to_f32(gO[((size_t)(t0 + r) * p.H + h) * DH + v0 + j]) : 0.0f;
+    const int r = tid >> 2, j8 = 8 * (tid & 3);
+    const f32x4* src = reinterpret_cast<const f32x4*>(gO + ((size_t)(t0 + (r < len ? r : 0)) * p.H + h) * DH + v0 + j8);
+#pragma unroll
+    for (int u = 0; u < OW; ++u) rO[u] = r < len ? src[u] : f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int x = tid + 256 * u, rr = x >> 3, j4 = 4 * (x & 7);
+      rD[u] = *reinterpret_cast<const f32x4*>(p.dmat + ch * MAT + rr * DH + v0 + j4);
+      rDD[u] = *reinterpret_cast<const f32x4*>(p.ddmat + ch * MAT + rr * DH + v0 + j4);
     }
-    for (int x = tid; x < CHUNK * 8; x += 256) {
-      const int r = x >> 3, j4 = 4 * (x & 7);
-      *reinterpret_cast<f32x4*>(sDm + r * LS + j4) =
-          *reinterpret_cast<const f32x4*>(p.dmat + ch * MAT + r * DH + v0 + j4);
-      *reinterpret_cast<f32x4*>(sDD + r * LS + j4) =
-          *reinterpret_cast<const f32x4*>(p.ddmat + ch * MAT + r * DH + v0 + j4);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int x = tid + 256 * u, i = x >> 3, j4 = 4 * (x & 7);
+      rS0[u] = *reinterpret_cast<const f32x4*>(p.s0 + ch * STM + i * DH + v0 + j4);
+      rDS[u] = *reinterpret_cast<const f32x4*>(p.dsn + ch * STM + i * DH + v0 + j4);
     }
-    for (int x = tid; x < DH * 8; x += 256) {
-      const int i = x >> 3, j4 = 4 * (x & 7);
-      *reinterpret_cast<f32x4*>(sS0 + i * LS + j4) =
-          *reinterpret_cast<const f32x4*>(p.s0 + ch * STM + i * DH + v0 + j4);
-      *reinterpret_cast<f32x4*>(sDS + i * LS + j4) =
-          *reinterpret_cast<const f32x4*>(p.dsn + ch * STM + i * DH + v0 + j4);
+  };
+  auto stage = [&]() {
+    const int r = tid >> 2, j8 = 8 * (tid & 3);
+    float o[8];
+    load8_scaled(reinterpret_cast<const TG*>(rO), p.scale, o);  // from registers
+    store4(sO + r * LS + j8, f32x4{o[0], o[1], o[2], o[3]});
+    store4(sO + r * LS + j8 + 4, f32x4{o[4], o[5], o[6], o[7]});
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int x = tid + 256 * u, rr = x >> 3, j4 = 4 * (x & 7);
+      store4(sDm + rr * LS + j4, rD[u]);
+      store4(sDD + rr * LS + j4, rDD[u]);
     }
-    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int x = tid + 256 * u, i = x >> 3, j4 = 4 * (x & 7);
+      store4(sS0 + i * LS + j4, rS0[u]);
+      store4(sDS + i * LS + j4, rDS[u]);
+    }
+  };
+  fetch(0);
+  stage();
+  __syncthreads();
+  for (int sl = 0; sl < 4; ++sl) {
+    if (sl < 3) fetch(sl + 1);
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) {
       aq[cb] = mma16_rows<float, 32>(sO + 16 * w * LS, LS, sS0 + 16 * cb * LS, LS, aq[cb], l);
@@ -376,6 +495,11 @@ __global__ __launch_bounds__(256) void kda_bwd_jprod_kernel(BwdArgs p) {
     if (tid < DH) {
 #pragma unroll 8
       for (int j = 0; j < 32; ++j) gacc = fmaf(sDS[tid * LS + j], sS0[tid * LS + j], gacc);
+    }
+    __syncthreads();
+    if (sl < 3) {
+      stage();
+      __syncthreads();
     }
   }
 #pragma unroll
@@ -439,6 +563,14 @@ __global__ __launch_bounds__(256) void kda_bwd_tprod_kernel(BwdArgs p) {
   }
   if (tid < CHUNK) sBeta[tid] = tid < len ? sigmoid_f(to_f32(gb[(size_t)(t0 + tid) * p.H + h])) : 0.0f;
   __syncthreads();
+  // phase-2 operands (dW, Bw^T) are loaded into registers during phase 1
+  f32x4 rW[8], rB[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int x = tid + 256 * u;
+    rW[u] = *reinterpret_cast<const f32x4*>(p.dw + ch * MAT + 4 * x);
+    rB[u] = *reinterpret_cast<const f32x4*>(p.bwt + ch * DH * CHUNK + 4 * x);
+  }
   // dBu rows i = 16w.. : dv = beta dBu, db1 = sum_j v dBu
   {
     float bsum[4] = {0, 0, 0, 0};
@@ -474,16 +606,12 @@ __global__ __launch_bounds__(256) void kda_bwd_tprod_kernel(BwdArgs p) {
     dt[ib] = acc * bi;
   }
   __syncthreads();
-  // phase 2: dW, Bw^T
-  for (int x = tid; x < CHUNK * 32; x += 256) {
-    const int r = x >> 5, c4 = 4 * (x & 31);
-    *reinterpret_cast<f32x4*>(sR1 + r * LW + c4) =
-        *reinterpret_cast<const f32x4*>(p.dw + ch * MAT + r * DH + c4);
-  }
-  for (int x = tid; x < DH * 16; x += 256) {
-    const int i = x >> 4, t4 = 4 * (x & 15);
-    *reinterpret_cast<f32x4*>(sR2 + i * LK + t4) =
-        *reinterpret_cast<const f32x4*>(p.bwt + ch * DH * CHUNK + i * CHUNK + t4);
+  // phase 2: dW [64][128] -> sR1, Bw^T [128][64] -> sR2
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int x = tid + 256 * u;
+    *reinterpret_cast<f32x4*>(sR1 + (x >> 5) * LW + 4 * (x & 31)) = rW[u];
+    *reinterpret_cast<f32x4*>(sR2 + (x >> 4) * LK + 4 * (x & 15)) = rB[u];
   }
   __syncthreads();
 #pragma unroll
@@ -562,22 +690,33 @@ __global__ __launch_bounds__(256) void kda_bwd_gate_kernel(BwdArgs p) {
   const int c0 = 2 * l;
   const f32x2 dtb = *reinterpret_cast<const f32x2*>(p.dt_bias + (size_t)h * DH + c0);
   // prep: wave w rows 16w.., lane channels c0, c0+1; rows past the end are zero
-  // (q^ = k^ = 0, g = 0)
+  // (q^ = k^ = 0, g = 0).  All row loads are issued before any use.
+  f32x2 qv[16], kv[16], fv[16];
+  float bv[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int r = 16 * w + j;
+    const int rr = r < len ? r : 0;
+    const size_t o = ((size_t)(t0 + rr) * p.H + h) * DH + c0;
+    qv[j] = load2(gq + o);
+    kv[j] = load2(gk + o);
+    fv[j] = load2(gf + o);
+    bv[j] = to_f32(gb[(size_t)(t0 + rr) * p.H + h]);
+  }
+#pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int r = 16 * w + j;
     const bool ok = r < len;
-    const size_t o = ((size_t)(t0 + (ok ? r : 0)) * p.H + h) * DH + c0;
-    f32x2 qv = load2(gq + o), kv = load2(gk + o), fv = load2(gf + o);
-    if (!ok) qv = kv = fv = f32x2{0, 0};
-    const float sq = wave_sum(qv[0] * qv[0] + qv[1] * qv[1]);
-    const float sk = wave_sum(kv[0] * kv[0] + kv[1] * kv[1]);
+    if (!ok) qv[j] = kv[j] = fv[j] = f32x2{0, 0};
+    const float sq = wave_sum(qv[j][0] * qv[j][0] + qv[j][1] * qv[j][1]);
+    const float sk = wave_sum(kv[j][0] * kv[j][0] + kv[j][1] * kv[j][1]);
     const float rq = rsqrt_hw(sq + p.eps), rk = rsqrt_hw(sk + p.eps);
-    sQ[r * DH + c0] = qv[0] * rq; sQ[r * DH + c0 + 1] = qv[1] * rq;
-    sK[r * DH + c0] = kv[0] * rk; sK[r * DH + c0 + 1] = kv[1] * rk;
-    sG[r * DH + c0] = ok ? gate_log2(fv[0] + dtb[0], lam) : 0.0f;
-    sG[r * DH + c0 + 1] = ok ? gate_log2(fv[1] + dtb[1], lam) : 0.0f;
+    sQ[r * DH + c0] = qv[j][0] * rq; sQ[r * DH + c0 + 1] = qv[j][1] * rq;
+    sK[r * DH + c0] = kv[j][0] * rk; sK[r * DH + c0 + 1] = kv[j][1] * rk;
+    sG[r * DH + c0] = ok ? gate_log2(fv[j][0] + dtb[0], lam) : 0.0f;
+    sG[r * DH + c0 + 1] = ok ? gate_log2(fv[j][1] + dtb[1], lam) : 0.0f;
     if (l == 0) {
-      sBeta[r] = ok ? sigmoid_f(to_f32(gb[(size_t)(t0 + r) * p.H + h])) : 0.0f;
+      sBeta[r] = ok ? sigmoid_f(bv[j]) : 0.0f;
       p.rqk[ch * 2 * CHUNK + r] = rq;
       p.rqk[ch * 2 * CHUNK + CHUNK + r] = rk;
     }
@@ -695,14 +834,19 @@ __global__ __launch_bounds__(256) void kda_bwd_gate_kernel(BwdArgs p) {
 }
 
 // ------------------------------------------------------------ 7. elementwise chain
-// Wave w: rows 16w..16w+15, lane channels c0, c0+1 for the row-local parts
-// (dq, dk, db and dG); then one thread per channel for the reverse prefix of
-// dG over the chunk's rows, df and the per-chunk parameter partials.
+// Wave w: rows 16w..16w+15, lane channels c0, c0+1.  Row-local parts (dq, dk,
+// db, dG) row by row; dG and x = f + dt_bias go to LDS.  Then the reverse
+// prefix of dG over the chunk: inside the wave over its 16 rows from LDS,
+// across waves one carry (column totals of the later waves plus the last
+// row's d(G_last) terms), giving df and the per-chunk parameter partials.
 template <typename TA, typename TR>
 __global__ __launch_bounds__(256) void kda_bwd_final_kernel(BwdArgs p) {
   __shared__ __attribute__((aligned(16))) float sDG[CHUNK * DH];
+  __shared__ __attribute__((aligned(16))) float sX[CHUNK * DH];
+  __shared__ float sTot[4][DH];
   __shared__ float sCol[4][DH];
-  __shared__ float sRed[DH];
+  __shared__ float sPdt[4][DH];
+  __shared__ float sPa[4];
   const int cidx = blockIdx.x, h = blockIdx.y;
   int t0, len;
   if (!bwd_chunk(p, cidx, t0, len)) return;
@@ -716,29 +860,38 @@ __global__ __launch_bounds__(256) void kda_bwd_final_kernel(BwdArgs p) {
   TR* __restrict__ gdb = reinterpret_cast<TR*>(p.db);
   const int c0 = 2 * l;
   const size_t mb = ch * MAT;
+  const float lam = expf(p.A_log[h]);
+  const f32x2 dtb = *reinterpret_cast<const f32x2*>(p.dt_bias + (size_t)h * DH + c0);
   const f32x2 gL = load2(p.g2 + mb + (CHUNK - 1) * DH + c0);  // G_last (rows past the end keep it)
-  float col0 = 0.0f, col1 = 0.0f;
+  float tot0 = 0.0f, tot1 = 0.0f, col0 = 0.0f, col1 = 0.0f;
+#pragma unroll 2
   for (int j = 0; j < 16; ++j) {
     const int r = 16 * w + j;
+    const bool ok = r < len;
+    const int rr = ok ? r : 0;
     const size_t o = mb + r * DH + c0;
     const f32x2 qn = load2(p.qn + o), kn = load2(p.kn + o), g2 = load2(p.g2 + o);
     const f32x2 al = load2(p.al + o), pv = load2(p.pi + o), rh = load2(p.rho + o);
     const f32x2 dqt = load2(p.dqt + o), dkb = load2(p.dkb + o), dbw = load2(p.dbw + o);
-    const bool ok = r < len;
-    const float beta = ok ? sigmoid_f(to_f32(gb[(size_t)(t0 + r) * p.H + h])) : 0.0f;
-    float dqn[2], dkn[2], sb = 0.0f;
+    const f32x2 fv = load2(gf + ((size_t)(t0 + rr) * p.H + h) * DH + c0);
+    const float bv = to_f32(gb[(size_t)(t0 + rr) * p.H + h]);
+    const float beta = ok ? sigmoid_f(bv) : 0.0f;
+    float dqn[2], dkn[2], dG[2], kbf[2], sb = 0.0f;
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       const float E = exp2_hw(g2[x]), F = exp2_hw(gL[x] - g2[x]);
       dqn[x] = pv[x] + dqt[x] * E;
       dkn[x] = beta * al[x] + rh[x] + beta * dbw[x] * E + dkb[x] * F;
-      const float kbf = dkb[x] * kn[x] * F;
-      const float dG = beta * kn[x] * al[x] + qn[x] * pv[x] - kn[x] * rh[x] + dqt[x] * qn[x] * E +
-                       beta * dbw[x] * kn[x] * E - kbf;
-      sDG[r * DH + c0 + x] = ok ? dG : 0.0f;
-      if (ok) { if (x == 0) col0 += kbf; else col1 += kbf; }
+      kbf[x] = ok ? dkb[x] * kn[x] * F : 0.0f;
+      dG[x] = ok ? beta * kn[x] * al[x] + qn[x] * pv[x] - kn[x] * rh[x] + dqt[x] * qn[x] * E +
+                       beta * dbw[x] * kn[x] * E - kbf[x]
+                 : 0.0f;
       sb += kn[x] * al[x] + dbw[x] * kn[x] * E;
     }
+    tot0 += dG[0]; tot1 += dG[1];
+    col0 += kbf[0]; col1 += kbf[1];
+    *reinterpret_cast<f32x2*>(sDG + r * DH + c0) = f32x2{dG[0], dG[1]};
+    *reinterpret_cast<f32x2*>(sX + r * DH + c0) = fv + dtb;
     const float s_b = wave_sum(sb);
     const float s_q = wave_sum(qn[0] * dqn[0] + qn[1] * dqn[1]);
     const float s_k = wave_sum(kn[0] * dkn[0] + kn[1] * dkn[1]);
@@ -747,41 +900,46 @@ __global__ __launch_bounds__(256) void kda_bwd_final_kernel(BwdArgs p) {
       const size_t go = ((size_t)(t0 + r) * p.H + h) * DH + c0;
       store2(gdq + go, rq * (dqn[0] - qn[0] * s_q), rq * (dqn[1] - qn[1] * s_q));
       store2(gdk + go, rk * (dkn[0] - kn[0] * s_k), rk * (dkn[1] - kn[1] * s_k));
-      if (l == 0) {
-        const float dbeta = p.db1[ch * CHUNK + r] + s_b;
-        gdb[(size_t)(t0 + r) * p.H + h] = from_f32<TR>(dbeta * beta * (1.0f - beta));
-      }
+      if (l == 0)
+        gdb[(size_t)(t0 + r) * p.H + h] =
+            from_f32<TR>((p.db1[ch * CHUNK + r] + s_b) * beta * (1.0f - beta));
     }
   }
-  sCol[w][c0] = col0;
-  sCol[w][c0 + 1] = col1;
+  sTot[w][c0] = tot0; sTot[w][c0 + 1] = tot1;
+  sCol[w][c0] = col0; sCol[w][c0 + 1] = col1;
   __syncthreads();
-  if (tid < DH) {
-    const int c = tid;
-    const float lam = expf(p.A_log[h]);
-    const float dtb = p.dt_bias[(size_t)h * DH + c];
-    const float gLc = p.g2[mb + (CHUNK - 1) * DH + c];
-    // the chunk's last row also carries d(G_last) from Kb and Gam
-    float acc = sCol[0][c] + sCol[1][c] + sCol[2][c] + sCol[3][c] +
-                p.dgam[ch * DH + c] * exp2_hw(gLc);
-    float pdt = 0.0f, pa = 0.0f;
-    for (int r = len - 1; r >= 0; --r) {
-      acc += sDG[r * DH + c];
-      const float x = to_f32(gf[((size_t)(t0 + r) * p.H + h) * DH + c]) + dtb;
-      const float dx = lam == 0.0f ? 0.0f : -lam * sigmoid_f(x) * acc;
-      gdf[((size_t)(t0 + r) * p.H + h) * DH + c] = from_f32<TR>(dx);
-      pdt += dx;
-      pa = fmaf(acc, gate_log2(x, lam) * (1.0f / LOG2E), pa);
-    }
-    p.ppart[ch * PPART + c] = pdt;
-    sRed[c] = pa;
+  // dg_r = sum_{j >= r} dG_j plus, on every valid row, the last row's extra
+  // terms sum_r dKb k^ F + dGam Gam (they belong to G_last)
+  float carry[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int c = c0 + x;
+    float a = sCol[0][c] + sCol[1][c] + sCol[2][c] + sCol[3][c] + p.dgam[ch * DH + c] * exp2_hw(gL[x]);
+    for (int w2 = w + 1; w2 < 4; ++w2) a += sTot[w2][c];
+    carry[x] = a;
   }
+  float pdt0 = 0.0f, pdt1 = 0.0f, pa = 0.0f;
+  for (int j = 15; j >= 0; --j) {
+    const int r = 16 * w + j;
+    if (r >= len) continue;  // uniform over the wave
+    const f32x2 dg = *reinterpret_cast<const f32x2*>(sDG + r * DH + c0);
+    const f32x2 xx = *reinterpret_cast<const f32x2*>(sX + r * DH + c0);
+    carry[0] += dg[0];
+    carry[1] += dg[1];
+    const float dx0 = lam == 0.0f ? 0.0f : -lam * sigmoid_f(xx[0]) * carry[0];
+    const float dx1 = lam == 0.0f ? 0.0f : -lam * sigmoid_f(xx[1]) * carry[1];
+    pdt0 += dx0;
+    pdt1 += dx1;
+    pa = fmaf(carry[0], gate_log2(xx[0], lam) * (1.0f / LOG2E), pa);
+    pa = fmaf(carry[1], gate_log2(xx[1], lam) * (1.0f / LOG2E), pa);
+    store2(gdf + ((size_t)(t0 + r) * p.H + h) * DH + c0, dx0, dx1);
+  }
+  sPdt[w][c0] = pdt0; sPdt[w][c0 + 1] = pdt1;
+  pa = wave_sum(pa);
+  if (l == 0) sPa[w] = pa;
   __syncthreads();
-  if (tid == 0) {
-    float s = 0.0f;
-    for (int c = 0; c < DH; ++c) s += sRed[c];
-    p.ppart[ch * PPART + DH] = s;
-  }
+  if (tid < DH) p.ppart[ch * PPART + tid] = sPdt[0][tid] + sPdt[1][tid] + sPdt[2][tid] + sPdt[3][tid];
+  if (tid == 0) p.ppart[ch * PPART + DH] = sPa[0] + sPa[1] + sPa[2] + sPa[3];
 }
 
 // ------------------------------------------------------------ 8. parameter gradients

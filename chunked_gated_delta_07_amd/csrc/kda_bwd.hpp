@@ -36,7 +36,8 @@
 // first row of the row block), so no gate strength can overflow it.
 //
 // Kernel sequence (all intermediates FP32 in the workspace):
-//   1. kda_intra_kernel<.., PlainRec, BWD>: records W, Qt, Kb^T, U^T, P, Gam, T, Bw^T
+//   1. kda_intra_kernel<.., PlainRec, BWD>: records W, Qt^T, Kb^T, U^T, P^T, Gam, T, Bw^T,
+//      W^T, Kb
 //   2. kda_bwd_fscan_kernel: S0 of every chunk and D           (per sequence, head, 32 values)
 //   3. kda_bwd_bscan_kernel: dSn of every chunk, dD, dS_init   (same, chunks in reverse)
 //   4. kda_bwd_jprod_kernel: dQt, dP, dKb, dW, dGam            (per chunk, head)
@@ -78,6 +79,8 @@ struct BwdArgs {
   const float* gam;        // [128]
   const float* tmat;       // T [64][64]
   const float* bwt;        // Bw^T [128][64]
+  const float* wt;         // W^T [128][64]
+  const float* kbr;        // Kb [64][128]
   float* s0;               // state entering the chunk [128 key][128 value]
   float* dsn;              // dL/d(state leaving the chunk) [128][128]
   float* dmat;             // D [64][128]
@@ -288,14 +291,14 @@ __global__ __launch_bounds__(256) void kda_bwd_bscan_kernel(BwdArgs p) {
     const size_t ch = (size_t)c * p.H + h;
     const float* rec = p.rec + ch * REC;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 4; ++u)  // P^T [64 r][64 i]
       rP[u] = *reinterpret_cast<const f32x4*>(rec + OFF_P + 4 * (tid + 256 * u));
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int x = tid + 256 * u;
-      rK[u] = *reinterpret_cast<const f32x4*>(rec + OFF_KBT + 4 * x);
-      rQ[u] = *reinterpret_cast<const f32x4*>(rec + OFF_QT + 4 * x);
-      rW[u] = *reinterpret_cast<const f32x4*>(rec + OFF_W + 4 * x);
+      rK[u] = *reinterpret_cast<const f32x4*>(p.kbr + ch * MAT + 4 * x);        // Kb [64][128]
+      rQ[u] = *reinterpret_cast<const f32x4*>(rec + OFF_QT + 4 * x);            // Qt^T [128][64]
+      rW[u] = *reinterpret_cast<const f32x4*>(p.wt + ch * DH * CHUNK + 4 * x);  // W^T [128][64]
     }
     const int t0 = tseq + (c - c_lo) * CHUNK, len = min(CHUNK, tend - t0);
     const int r = tid >> 2, j8 = 8 * (tid & 3);
@@ -309,27 +312,16 @@ __global__ __launch_bounds__(256) void kda_bwd_bscan_kernel(BwdArgs p) {
   };
   auto stage = [&]() {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {  // P row i = x/16, cols r = 4(x%16).. -> P^T[r][i]
-      const int x = tid + 256 * u, i = x >> 4, r4 = 4 * (x & 15);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sPT[(r4 + e) * LS + i] = rP[u][e];
+    for (int u = 0; u < 4; ++u) {
+      const int x = tid + 256 * u;
+      *reinterpret_cast<f32x4*>(sPT + (x >> 4) * LS + 4 * (x & 15)) = rP[u];
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int x = tid + 256 * u;
-      {  // Kb^T row c = x/16, tokens 4(x%16).. -> Kb[t][c]
-        const int c = x >> 4, t4 = 4 * (x & 15);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sKb[(t4 + e) * LL + c] = rK[u][e];
-      }
-      {  // Qt / W row r = x/32, channels 4(x%32).. -> [channel][r]
-        const int r = x >> 5, c4 = 4 * (x & 31);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sQtT[(c4 + e) * LS + r] = rQ[u][e];
-          sWT[(c4 + e) * LS + r] = rW[u][e];
-        }
-      }
+      *reinterpret_cast<f32x4*>(sKb + (x >> 5) * LL + 4 * (x & 31)) = rK[u];
+      *reinterpret_cast<f32x4*>(sQtT + (x >> 4) * LS + 4 * (x & 15)) = rQ[u];
+      *reinterpret_cast<f32x4*>(sWT + (x >> 4) * LS + 4 * (x & 15)) = rW[u];
     }
     {
       const int r = tid >> 2, j8 = 8 * (tid & 3);
@@ -664,13 +656,13 @@ __device__ __forceinline__ float gate_log2(float x, float lam) {
 
 // ------------------------------------------------------------ 6. decay-weighted sums
 // Recomputes q^, k^ and G (stored for kernel 7), then
-//   waves 0-1 (one thread per channel): alpha, pi (sums over i <= r per row r)
-//   waves 2-3 (one thread per channel): rho (sums over r >= i per column i)
+//   waves 0-3 (one thread per channel): alpha, pi (sums over i <= r per row r)
+//   waves 4-7 (one thread per channel): rho (sums over r >= i per column i)
 // in 8x8 token blocks: off-diagonal blocks (R > I) factorised about row 8R,
 //   e^{G_r - G_i} = e^{G_r - G_8R} e^{G_8R - G_i}  (both exponents <= 0),
 // diagonal blocks per element.
 template <typename TA>
-__global__ __launch_bounds__(256) void kda_bwd_gate_kernel(BwdArgs p) {
+__global__ __launch_bounds__(512) void kda_bwd_gate_kernel(BwdArgs p) {
   __shared__ __attribute__((aligned(16))) float sQ[CHUNK * DH];
   __shared__ __attribute__((aligned(16))) float sK[CHUNK * DH];
   __shared__ __attribute__((aligned(16))) float sG[CHUNK * DH];
@@ -689,13 +681,13 @@ __global__ __launch_bounds__(256) void kda_bwd_gate_kernel(BwdArgs p) {
   const float lam = expf(p.A_log[h]);
   const int c0 = 2 * l;
   const f32x2 dtb = *reinterpret_cast<const f32x2*>(p.dt_bias + (size_t)h * DH + c0);
-  // prep: wave w rows 16w.., lane channels c0, c0+1; rows past the end are zero
-  // (q^ = k^ = 0, g = 0).  All row loads are issued before any use.
-  f32x2 qv[16], kv[16], fv[16];
-  float bv[16];
+  // prep: wave w (of 8) rows 8w..8w+7, lane channels c0, c0+1; rows past the
+  // end are zero (q^ = k^ = 0, g = 0).  All row loads are issued before any use.
+  f32x2 qv[8], kv[8], fv[8];
+  float bv[8];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int r = 16 * w + j;
+  for (int j = 0; j < 8; ++j) {
+    const int r = 8 * w + j;
     const int rr = r < len ? r : 0;
     const size_t o = ((size_t)(t0 + rr) * p.H + h) * DH + c0;
     qv[j] = load2(gq + o);
@@ -704,8 +696,8 @@ __global__ __launch_bounds__(256) void kda_bwd_gate_kernel(BwdArgs p) {
     bv[j] = to_f32(gb[(size_t)(t0 + rr) * p.H + h]);
   }
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int r = 16 * w + j;
+  for (int j = 0; j < 8; ++j) {
+    const int r = 8 * w + j;
     const bool ok = r < len;
     if (!ok) qv[j] = kv[j] = fv[j] = f32x2{0, 0};
     const float sq = wave_sum(qv[j][0] * qv[j][0] + qv[j][1] * qv[j][1]);
@@ -729,21 +721,26 @@ __global__ __launch_bounds__(256) void kda_bwd_gate_kernel(BwdArgs p) {
       sG[r * DH + tid] = acc;
     }
   } else {
-    for (int x = tid - DH; x < SQM / 4; x += 128) {
+    for (int x = tid - DH; x < SQM / 4; x += 384) {
       reinterpret_cast<f32x4*>(sA)[x] = reinterpret_cast<const f32x4*>(p.dam + ch * SQM)[x];
       reinterpret_cast<f32x4*>(sP)[x] = reinterpret_cast<const f32x4*>(p.dpm + ch * SQM)[x];
     }
   }
   __syncthreads();
-  for (int x = tid; x < MAT / 4; x += 256) {
+  for (int x = tid; x < MAT / 4; x += 512) {
     reinterpret_cast<f32x4*>(p.qn + ch * MAT)[x] = reinterpret_cast<const f32x4*>(sQ)[x];
     reinterpret_cast<f32x4*>(p.kn + ch * MAT)[x] = reinterpret_cast<const f32x4*>(sK)[x];
     reinterpret_cast<f32x4*>(p.g2 + ch * MAT)[x] = reinterpret_cast<const f32x4*>(sG)[x];
   }
-  const int c = tid & (DH - 1);
-  if (tid < DH) {
+  // Four roles of 128 threads (one per channel): rows of blocks {7,6,1,0},
+  // rows of {5,4,3,2}, columns of blocks {0,1,6,7}, columns of {2,3,4,5}
+  // (18 of the 36 block pairs each).
+  const int c = tid & (DH - 1), role = tid >> 7;
+  const int set = role & 1;
+  if (role < 2) {
     // rows: alpha_r = sum_{i<r} dA_ri k^_i e^{G_r-G_i}, pi_r = sum_{i<=r} dP_ri k^_i e^{..}
-    for (int R = 0; R < 8; ++R) {
+    for (int k4 = 0; k4 < 4; ++k4) {
+      const int R = set == 0 ? (k4 < 2 ? 7 - k4 : 3 - k4) : 5 - k4;
       const int m = 8 * R;
       const float gm = sG[m * DH + c];
       float ao[8], po[8];
@@ -786,7 +783,8 @@ __global__ __launch_bounds__(256) void kda_bwd_gate_kernel(BwdArgs p) {
     }
   } else {
     // columns: rho_i = sum_{r>=i} (beta_r dA_ri k^_r + dP_ri q^_r) e^{G_r-G_i}
-    for (int I = 0; I < 8; ++I) {
+    for (int k4 = 0; k4 < 4; ++k4) {
+      const int I = set == 0 ? (k4 < 2 ? k4 : 4 + k4) : 2 + k4;
       float ro[8];
 #pragma unroll
       for (int bb = 0; bb < 8; ++bb) ro[bb] = 0.0f;

@@ -53,11 +53,13 @@ constexpr int REC = 4 * CHUNK * DH + CHUNK * CHUNK;
 
 template <typename MT> struct Frag {
   static constexpr int FE = 16 / (int)sizeof(MT);
+  static constexpr bool TRANSPOSED_QT_P = false;
   // W / Qt element (token r, key channel c): A operand of [W;Qt] S0, contracted
   // over key channels, half g = c/64.
   __host__ __device__ static constexpr int a(int r, int c) {
     return (((r >> 5) * (64 / FE) + (c & 63) / FE) * 64 + 32 * (c >> 6) + (r & 31)) * FE + (c & 63) % FE;
   }
+  __host__ __device__ static constexpr int qt(int r, int c) { return a(r, c); }
   // Kb^T element (key channel c, token t): A operand of Kb^T D, contracted over
   // tokens, half g = t/32.
   __host__ __device__ static constexpr int kb(int c, int t) {
@@ -75,15 +77,17 @@ template <typename MT> struct Frag {
   }
 };
 
-// The same record in plain row-major order, for the backward pass (which
-// reads it as whole matrices): W [64][128], Qt [64][128], Kb^T [128][64],
-// U^T [128 value][64 tok], P [64][64].  Every group of stores the forward
-// makes (FE consecutive elements along one index) is contiguous here too.
+// The same record as whole matrices for the backward pass, each in the
+// orientation its consumer contracts over: W [64 tok][128 key], Qt^T
+// [128 key][64 tok], Kb^T [128][64], U^T [128 value][64 tok], P^T [64 i][64 r].
+// (The forward's own layout is Frag; there the Qt and P stores are vectors.)
 template <typename MT> struct PlainRec {
   static constexpr int FE = 16 / (int)sizeof(MT);
+  static constexpr bool TRANSPOSED_QT_P = true;
   __host__ __device__ static constexpr int a(int r, int c) { return r * DH + c; }
+  __host__ __device__ static constexpr int qt(int r, int c) { return c * CHUNK + r; }
   __host__ __device__ static constexpr int kb(int c, int t) { return c * CHUNK + t; }
-  __host__ __device__ static constexpr int pm(int r, int i) { return r * CHUNK + i; }
+  __host__ __device__ static constexpr int pm(int r, int i) { return i * CHUNK + r; }
   __host__ __device__ static constexpr int u(int t, int v) { return v * CHUNK + t; }
 };
 
@@ -112,6 +116,9 @@ struct IntraArgs {
   // [chunks][H][64][64] and (Diag(beta) (k^ * E))^T [chunks][H][128][64], FP32
   float* tmat;
   float* bwt;
+  // and W^T [128][64], Kb [64][128] (the backward's reverse state scan)
+  float* wt;
+  float* kbr;
 };
 
 // Chunk c -> (first token, length, first token of its sequence).  cfirst is
@@ -480,7 +487,12 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
       const int r = 16 * w + j;
       e0 *= aa[j][0]; e1 *= aa[j][1];
       const float rq = sRq[r];
-      store2(gQt + LY::a(r, c0), qa[j][0] * rq * e0, qa[j][1] * rq * e1);
+      if constexpr (LY::TRANSPOSED_QT_P) {
+        gQt[LY::qt(r, c0)] = from_f32<MT>(qa[j][0] * rq * e0);
+        gQt[LY::qt(r, c0 + 1)] = from_f32<MT>(qa[j][1] * rq * e1);
+      } else {
+        store2(gQt + LY::qt(r, c0), qa[j][0] * rq * e0, qa[j][1] * rq * e1);
+      }
     }
     float s0 = sa[0], s1 = sa[1];
     float kb0[16], kb1[16];
@@ -496,6 +508,11 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
       store4(gKbT + LY::kb(c0, 16 * w + j), f32x4{kb0[j], kb0[j + 1], kb0[j + 2], kb0[j + 3]});
       store4(gKbT + LY::kb(c0 + 1, 16 * w + j),
              f32x4{kb1[j], kb1[j + 1], kb1[j + 2], kb1[j + 3]});
+      if constexpr (BWD) {
+        float* gk = p.kbr + ((size_t)chunk * H + h) * CHUNK * DH;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) store2(gk + (16 * w + j + e) * DH + c0, kb0[j + e], kb1[j + e]);
+      }
     }
     if (w == 0) {
       float g0 = 1.0f, g1 = 1.0f;
@@ -562,10 +579,16 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
       else sA[ru * AL + ri] = sBeta[ru] * sRk[ru] * sRk[ri] * c[e];
     }
   }
-  // Upper triangle of P is zero.  In the stored order a 16-byte fragment holds
-  // FE consecutive columns of one row: fragments wholly above the diagonal are
-  // written as one vector, the one straddling it element by element.
-  {
+  // Upper triangle of P is zero.  In the forward's stored order a 16-byte
+  // fragment holds FE consecutive columns of one row: fragments wholly above
+  // the diagonal are written as one vector, the one straddling it element by
+  // element.  The transposed (backward) layout is zeroed element by element.
+  if constexpr (LY::TRANSPOSED_QT_P) {
+    for (int f = tid; f < CHUNK * CHUNK; f += 256) {
+      const int r = f & 63, i = f >> 6;  // consecutive threads: consecutive addresses
+      if (i > r) gP[LY::pm(r, i)] = from_f32<MT>(0.0f);
+    }
+  } else {
     constexpr int FE = LY::FE;
     typedef typename std::conditional<sizeof(MT) == 2, bf16x8, f32x4>::type v16;
     for (int f = tid; f < CHUNK * CHUNK / FE; f += 256) {
@@ -742,6 +765,11 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
     // c[e] = W^T[16mt + 4(l/16) + e][16nt + l%16] = W[tok][ch..ch+3]
     const int tok = 16 * nt + (l & 15), ch = 16 * mt + 4 * (l >> 4);
     store4(gW + LY::a(tok, ch), c);
+    if constexpr (BWD) {
+      float* gwt = p.wt + ((size_t)chunk * H + h) * DH * CHUNK;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) gwt[(ch + e) * CHUNK + tok] = c[e];
+    }
   }
   __syncthreads();
   // U = T (Diag(beta) v)

@@ -288,9 +288,16 @@ def time_bwd(args_dev, steps: int, warmup: int):
     us = sorted(a.elapsed_time(e) * 1e3 for a, e in evs)
     p50 = statistics.median(us)
     del ws
+    # algorithmic FLOP of a vector-Jacobian product: twice the forward's
+    # (every product of the forward has two adjoint products)
+    flop = 2 * FLOP_PER_TH * T * H
+    tflops = flop / (p50 * 1e-6) / 1e12
     return {"entry_point": "kda_chunk_bwd", "workload": "headline, dout bf16, gradients bf16",
             "intermediates": "fp32", "p50_us": round(p50, 2), "max_us": round(us[-1], 2),
-            "tokens_per_s": round(T / (p50 * 1e-6), 1)}
+            "tokens_per_s": round(T / (p50 * 1e-6), 1),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_FP32_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_FP32_TFLOPS, 4),
+                         "flop_per_token_head": 2 * FLOP_PER_TH}}
 
 
 def roofline_for(mode_name: str, T: int, H: int, res: dict, workload: str):

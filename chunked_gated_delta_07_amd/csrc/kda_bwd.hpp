@@ -159,9 +159,13 @@ __global__ __launch_bounds__(256) void kda_bwd_fscan_kernel(BwdArgs p) {
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int v0 = 32 * vb;
   const int c_lo = p.cfirst[n], c_hi = p.cfirst[n + 1];
+  // the state entering each chunk is snapshotted from registers as it is
+  // formed; the first one here
   for (int x = tid; x < DH * 32; x += 256) {
     const int i = x >> 5, j = x & 31;
-    sST[j * LL + i] = p.init ? p.init[((size_t)pair * DH + i) * DH + v0 + j] : 0.0f;
+    const float s0 = p.init ? p.init[((size_t)pair * DH + i) * DH + v0 + j] : 0.0f;
+    sST[j * LL + i] = s0;
+    if (c_lo < c_hi) p.s0[((size_t)c_lo * p.H + h) * STM + i * DH + v0 + j] = s0;
   }
   // register staging of one chunk's records: W 8, Kb^T 8, U^T 2 f32x4 per thread, Gam
   f32x4 rW[8], rK[8], rU[2], rG;
@@ -202,11 +206,6 @@ __global__ __launch_bounds__(256) void kda_bwd_fscan_kernel(BwdArgs p) {
   __syncthreads();
   for (int c = c_lo; c < c_hi; ++c) {
     const size_t ch = (size_t)c * p.H + h;
-    float* snap = p.s0 + ch * STM;
-    for (int x = tid; x < DH * 32; x += 256) {
-      const int i = x >> 5, j = x & 31;
-      snap[i * DH + v0 + j] = sST[j * LL + i];
-    }
     // D[r][j] = U[r][j] - sum_c W[r][c] S[c][j]: wave w rows 16w.., both column halves
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
@@ -239,6 +238,11 @@ __global__ __launch_bounds__(256) void kda_bwd_fscan_kernel(BwdArgs p) {
           acc[e] = sGam[i] * sST[j * LL + i];
         }
         ns[kb2][cb] = mma16_rows<float, CHUNK>(sKbT + 16 * kb * LS, LS, sDT + 16 * cb * LS, LS, acc, l);
+        if (more) {
+          float* snap = p.s0 + (ch + p.H) * STM;  // state entering chunk c + 1
+#pragma unroll
+          for (int e = 0; e < 4; ++e) snap[(16 * kb + 4 * (l >> 4) + e) * DH + v0 + j] = ns[kb2][cb][e];
+        }
       }
     }
     __syncthreads();
@@ -280,11 +284,15 @@ __global__ __launch_bounds__(256) void kda_bwd_bscan_kernel(BwdArgs p) {
   const TG* __restrict__ gO = reinterpret_cast<const TG*>(p.dout);
   const int c_lo = p.cfirst[n], c_hi = p.cfirst[n + 1];
   const int tseq = p.cu[n], tend = p.cu[n + 1];
+  // dSn of each chunk is snapshotted from registers as it is formed; the
+  // last chunk's (= dS_final) here
   for (int x = tid; x < DH * 32; x += 256) {
     const int i = x >> 5, j = x & 31;
-    sST[j * LL + i] = p.dfin ? p.dfin[((size_t)pair * DH + i) * DH + v0 + j] : 0.0f;
+    const float d = p.dfin ? p.dfin[((size_t)pair * DH + i) * DH + v0 + j] : 0.0f;
+    sST[j * LL + i] = d;
+    if (c_lo < c_hi) p.dsn[((size_t)(c_hi - 1) * p.H + h) * STM + i * DH + v0 + j] = d;
   }
-  // register staging: P 4, Kb^T 8, Qt 8, W 8 f32x4, dO 8 values, Gam
+  // register staging: P^T 4, Kb 8, Qt^T 8, W^T 8 f32x4, dO 8 values, Gam
   f32x4 rP[4], rK[8], rQ[8], rW[8], rG;
   float rO[8];
   auto fetch = [&](int c) {
@@ -337,11 +345,6 @@ __global__ __launch_bounds__(256) void kda_bwd_bscan_kernel(BwdArgs p) {
   __syncthreads();
   for (int c = c_hi - 1; c >= c_lo; --c) {
     const size_t ch = (size_t)c * p.H + h;
-    float* snap = p.dsn + ch * STM;
-    for (int x = tid; x < DH * 32; x += 256) {
-      const int i = x >> 5, j = x & 31;
-      snap[i * DH + v0 + j] = sST[j * LL + i];
-    }
     // dD[r][j] = sum_i P^T[r][i] dO^T[j][i] + sum_c Kb[r][c] dS^T[j][c]: wave w rows 16w..
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
@@ -376,6 +379,11 @@ __global__ __launch_bounds__(256) void kda_bwd_bscan_kernel(BwdArgs p) {
         acc = mma16_rows<float, CHUNK>(sQtT + 16 * kb * LS, LS, sOT + 16 * cb * LS, LS, acc, l);
         neg = mma16_rows<float, CHUNK>(sWT + 16 * kb * LS, LS, sDT + 16 * cb * LS, LS, neg, l);
         ns[kb2][cb] = acc - neg;
+        if (more) {
+          float* snap = p.dsn + (ch - p.H) * STM;  // dSn of chunk c - 1
+#pragma unroll
+          for (int e = 0; e < 4; ++e) snap[(16 * kb + 4 * (l >> 4) + e) * DH + v0 + j] = ns[kb2][cb][e];
+        }
       }
     }
     __syncthreads();

@@ -12,7 +12,13 @@ each whole gradient tensor:
     1e-4 -- the forward's FP32 bar; the backward's arithmetic is FP32 with
     sums of at most a few hundred terms per output, far below it;
   * bf16 gradients: 2e-2, the pages' BF16 budget (rounding of a correct
-    result to bf16 alone costs ~2e-3).
+    result to bf16 alone costs ~2e-3);
+  * the parameter gradients dA_log and dt_bias (FP32 sums over every token
+    and channel of a head): 1e-3.  Their terms cancel -- sum|term| / |sum| is
+    ~330 at 2048 tokens and ~670 at 8192 (it grows like sqrt(T)) -- so FP32
+    rounding of ~2e-7 per term becomes ~1e-4 of the sum at 64K tokens; the
+    pages' FP32 budget for the gate gradient is 0.5 % and their worst FP32
+    parameter-gradient error 0.374 % (xtuner PR #2153, KDA module section).
 """
 import os
 import sys
@@ -30,6 +36,8 @@ pytestmark = pytest.mark.gpu
 
 TOL_FP32 = 1e-4
 TOL_BF16 = 2e-2
+TOL_PARAM = 1e-3
+PARAMS = ("dA_log", "ddt_bias")
 KEYS = ("dq", "dk", "dv", "df", "db", "dA_log", "ddt_bias")
 
 
@@ -60,7 +68,9 @@ def _case(lens, H, act, seed, with_states=True, grad_fp32=True):
     return inp, dout, init, dfin
 
 
-def _gpu_bwd(inp, dout, init, dfin, grad_fp32):
+def _gpu_bwd(inp, dout, init, dfin, grad_fp32, heads=None):
+    """GPU gradients as float64 numpy; with ``heads`` only those heads are
+    copied back (per-head arrays keep their head axis)."""
     import torch
 
     from chunked_gated_delta_07_amd import kda
@@ -73,6 +83,10 @@ def _gpu_bwd(inp, dout, init, dfin, grad_fp32):
                       dfinal_state=None if dfin is None else torch.from_numpy(dfin).to(dev),
                       return_dinitial_state=True)
     torch.cuda.synchronize()
+    if heads is not None:
+        hd = torch.as_tensor(heads, device=dev)
+        g = {k: (v.index_select(0, hd) if k in ("dA_log", "ddt_bias") else v.index_select(1, hd))
+             for k, v in g.items()}
     return {k: v.to(torch.float64).cpu().numpy() for k, v in g.items()}
 
 
@@ -92,7 +106,7 @@ def _check(got, ref, tol, label):
     print(label, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
     for k, e in errs.items():
         assert np.all(np.isfinite(got[k])), (label, k)
-        assert e < tol, (label, k, e)
+        assert e < (max(tol, TOL_PARAM) if k in PARAMS else tol), (label, k, e)
     return errs
 
 
@@ -185,18 +199,38 @@ def test_bwd_headline_size_sampled_heads():
     rng = np.random.default_rng(77)
     dout = synth.bf16_bits_to_f32(
         synth.f32_to_bf16_bits(rng.standard_normal((T, H, 128)).astype(np.float32)))
-    got32 = _gpu_bwd(inp, dout, None, None, True)
-    got16 = _gpu_bwd(inp, dout, None, None, False)
-    torch.cuda.empty_cache()
     heads = np.array([0, 41])
+    got32 = _gpu_bwd(inp, dout, None, None, True, heads=heads)
+    got16 = _gpu_bwd(inp, dout, None, None, False, heads=heads)
+    torch.cuda.empty_cache()
     x = inp.as_f64()
     ref = oracle.kda_backward(x["q"][:, heads], x["k"][:, heads], x["v"][:, heads],
                               x["f_raw"][:, heads], x["b_raw"][:, heads], x["A_log"][heads],
                               x["dt_bias"][heads], x["cu_seqlens"],
                               dout[:, heads].astype(np.float64))
     for got, tol, lab in ((got32, TOL_FP32, "fp32-grad"), (got16, TOL_BF16, "bf16-grad")):
-        sub = {k: (got[k][:, heads] if k in ("dq", "dk", "dv", "df", "db") else got[k][heads])
-               for k in KEYS}
-        _check(sub, ref, tol, f"16384x64 {lab}")
-        for k in ("dq", "dk", "dv", "df", "db"):
-            assert np.all(np.isfinite(got[k])), k
+        got = {k: got[k] for k in KEYS}
+        _check(got, ref, tol, f"16384x64 {lab}")
+
+
+def test_bwd_ragged_65536_sampled_head():
+    """The ragged packed workload (lengths U{1..8192} totalling 65536 tokens,
+    64 heads, bf16): every sequence of head 23 against the oracle, FP32
+    gradients, with the final-state gradient of every sequence."""
+    import torch
+
+    inp = synth.config_inputs(4)
+    T, H = inp.T, inp.H
+    N = len(inp.cu_seqlens) - 1
+    rng = np.random.default_rng(78)
+    dout = rng.standard_normal((T, H, 128)).astype(np.float32)
+    dfin = rng.standard_normal((N, H, 128, 128)).astype(np.float32)
+    hd = np.array([23])
+    got = _gpu_bwd(inp, dout, None, dfin, True, heads=hd)
+    torch.cuda.empty_cache()
+    x = inp.as_f64()
+    ref = oracle.kda_backward(x["q"][:, hd], x["k"][:, hd], x["v"][:, hd], x["f_raw"][:, hd],
+                              x["b_raw"][:, hd], x["A_log"][hd], x["dt_bias"][hd], x["cu_seqlens"],
+                              dout[:, hd].astype(np.float64),
+                              dfinal_state=dfin[:, hd].astype(np.float64))
+    _check(got, ref, TOL_FP32, f"ragged 65536 ({N} seqs) head 23")

@@ -192,8 +192,8 @@ KDA_API int kda_recurrent_fwd_rect(const void* q, const void* k, const void* v, 
                            const float* initial_state, float* final_state, void* stream);
 
 /* Workspace bytes needed by kda_chunk_bwd (same arguments and failure value
- * as kda_chunk_fwd_workspace_bytes).  FP32 throughout: about 560 KB per
- * (64-token chunk, head), e.g. 9.2 GB for 16384 tokens x 64 heads. */
+ * as kda_chunk_fwd_workspace_bytes).  FP32 throughout: about 620 KB per
+ * (64-token chunk, head), e.g. 10.2 GB for 16384 tokens x 64 heads. */
 KDA_API size_t kda_chunk_bwd_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t H,
                                      int32_t d, uint32_t mode);
 

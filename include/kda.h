@@ -1,6 +1,6 @@
 /*
  * kda.h -- C ABI of libkda, the MI355X (gfx950) Kimi Delta Attention (KDA)
- * chunked forward.
+ * chunked forward, its token-serial form and its backward.
  *
  * Operation (per head h and per packed sequence; zero initial state except
  * in kda_chunk_fwd_state):

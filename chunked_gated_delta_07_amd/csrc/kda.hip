@@ -423,12 +423,22 @@ extern "C" int kda_chunk_bwd(const void* q, const void* k, const void* v, const 
                              void* dv, void* df_raw, void* db_raw, float* dA_log, float* ddt_bias,
                              float* dinitial_state, void* workspace, size_t workspace_bytes,
                              void* stream) {
+  // every host-side check comes before the first HIP call
   if (mode & ~KDA_MODE_ALL_BITS) return KDA_ERR_INVALID_ARG;
   if (num_seqs < 1 || total_tokens < 0 || H < 1) return KDA_ERR_INVALID_ARG;
   if (d != kda::DH) return KDA_ERR_UNSUPPORTED;
   if (!dA_log || !ddt_bias) return KDA_ERR_INVALID_ARG;
+  if (total_tokens > 0) {
+    if (!q || !k || !v || !f_raw || !b_raw || !A_log || !dt_bias || !cu_seqlens || !dout || !dq ||
+        !dk || !dv || !df_raw || !db_raw || !workspace)
+      return KDA_ERR_INVALID_ARG;
+    if (total_tokens > (int64_t)INT32_MAX / 64 || (int64_t)num_seqs * H > (int64_t)INT32_MAX / 64)
+      return KDA_ERR_UNSUPPORTED;
+    if (workspace_bytes < kda::bwd_layout(total_tokens, num_seqs, H).total)
+      return KDA_ERR_WORKSPACE;
+  }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  (void)hipGetLastError();
+  (void)hipGetLastError();  // clear a stale error so the status reflects these launches
   if (total_tokens == 0) {
     const int64_t n = (int64_t)num_seqs * H * kda::DH * kda::DH;
     const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
@@ -436,12 +446,6 @@ extern "C" int kda_chunk_bwd(const void* q, const void* k, const void* v, const 
                        dim3(256), 0, s, dfinal_state, dinitial_state, n, dA_log, ddt_bias, (int)H);
     return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
   }
-  if (!q || !k || !v || !f_raw || !b_raw || !A_log || !dt_bias || !cu_seqlens || !dout || !dq ||
-      !dk || !dv || !df_raw || !db_raw || !workspace)
-    return KDA_ERR_INVALID_ARG;
-  if (total_tokens > (int64_t)INT32_MAX / 64 || (int64_t)num_seqs * H > (int64_t)INT32_MAX / 64)
-    return KDA_ERR_UNSUPPORTED;
-  if (workspace_bytes < kda::bwd_layout(total_tokens, num_seqs, H).total) return KDA_ERR_WORKSPACE;
   const bool a32 = mode & KDA_ACT_FP32;
   const bool o32 = (mode & KDA_OUT_FP32) || a32;
 #define KDA_BWD(TA, TG, TR)                                                                      \

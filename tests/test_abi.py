@@ -97,6 +97,36 @@ def test_argument_errors_before_launch():
     assert rr(16, 0) == kda.KDA_ERR_INVALID_ARG
 
 
+def test_backward_argument_errors_before_launch():
+    """kda_chunk_bwd rejects bad arguments before any HIP call (this runs on a
+    machine without a GPU)."""
+    from chunked_gated_delta_07_amd import kda
+
+    lib = kda.load_library()
+    p = ctypes.c_void_p(16)  # never dereferenced: the checks fail first
+
+    def bw(N=1, T=10, H=4, d=128, mode=1, x=p, par=p, ws=1 << 40):
+        return lib.kda_chunk_bwd(*([x] * 8), N, T, H, d, mode, None, x, None, x, x, x, x, x, par,
+                                 par, None, x, ws, None)
+
+    assert bw(x=None) == kda.KDA_ERR_INVALID_ARG      # null input / output pointers
+    assert bw(par=None) == kda.KDA_ERR_INVALID_ARG    # parameter gradients are required
+    assert bw(N=0) == kda.KDA_ERR_INVALID_ARG
+    assert bw(H=0) == kda.KDA_ERR_INVALID_ARG
+    assert bw(T=-1) == kda.KDA_ERR_INVALID_ARG
+    assert bw(mode=0x8) == kda.KDA_ERR_INVALID_ARG
+    assert bw(d=64) == kda.KDA_ERR_UNSUPPORTED
+    assert bw(ws=1) == kda.KDA_ERR_WORKSPACE
+    assert bw(T=0, par=None) == kda.KDA_ERR_INVALID_ARG  # still required for an empty batch
+    assert kda.bwd_workspace_bytes(0, 1, 64, 128, 1) == 0
+    with pytest.raises(kda.KdaError):
+        kda.bwd_workspace_bytes(10, 1, 64, 96, 1)
+    b = [kda.bwd_workspace_bytes(T, 1, 64, 128, 1) for T in (1, 64, 65, 16384)]
+    assert b == sorted(b) and all(x % 256 == 0 for x in b)
+    # about 620 KB per (chunk, head): 16384 tokens x 64 heads = 256 x 64 chunk-heads
+    assert 600e3 < b[-1] / (256 * 64) < 660e3
+
+
 def test_workspace_query():
     from chunked_gated_delta_07_amd import kda
 

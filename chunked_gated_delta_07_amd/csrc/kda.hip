@@ -97,7 +97,7 @@ static int launch_all(const void* q, const void* k, const void* v, const void* f
   ia.A_log = A_log; ia.dt_bias = dt_bias; ia.cu = cu; ia.cfirst = cfirst;
   ia.N = N; ia.H = H; ia.eps = 1e-6f; ia.gam = gam; ia.rec = rec;
   ia.conv_w = conv_w; ia.conv_b = conv_b; ia.conv_silu = conv_silu;
-  ia.tmat = nullptr; ia.bwt = nullptr; ia.wt = nullptr; ia.kbr = nullptr;
+  ia.tmat = nullptr; ia.bw = nullptr; ia.wt = nullptr; ia.kbr = nullptr;
   if (conv_w)
     hipLaunchKernelGGL((kda_intra_kernel<TA, MT, true>), dim3((unsigned)C, (unsigned)H), dim3(256), 0,
                        stream, ia);
@@ -146,7 +146,7 @@ static int dispatch(const void* q, const void* k, const void* v, const void* f, 
 // table.  Arrays written by the last three kernels reuse ones whose readers
 // have finished: alpha/pi/rho take D/dD/dW, q^/k^ take S0, G takes dSn.
 struct BwdLayout {
-  size_t off_cfirst, off_gam, off_rec, off_t, off_bwt, off_wt, off_kbr, off_s0, off_dsn, off_d,
+  size_t off_cfirst, off_gam, off_rec, off_t, off_bw, off_wt, off_kbr, off_s0, off_dsn, off_d,
       off_dd, off_dqt, off_dkb, off_dw, off_dbw, off_dp, off_da, off_dgam, off_db1, off_rqk, off_pp,
       total;
 };
@@ -160,7 +160,7 @@ static inline BwdLayout bwd_layout(int64_t T, int32_t N, int32_t H) {
   L.off_gam = take(4 * CH * DH);
   L.off_rec = take(4 * CH * REC);
   L.off_t = take(4 * CH * SQM);
-  L.off_bwt = take(4 * CH * MAT);
+  L.off_bw = take(4 * CH * MAT);
   L.off_wt = take(4 * CH * MAT);
   L.off_kbr = take(4 * CH * MAT);
   L.off_s0 = take(4 * CH * STM);
@@ -199,7 +199,7 @@ static int launch_bwd(const void* q, const void* k, const void* v, const void* f
   ia.A_log = A_log; ia.dt_bias = dt_bias; ia.cu = cu; ia.cfirst = cfirst;
   ia.N = N; ia.H = H; ia.eps = 1e-6f; ia.gam = fp(L.off_gam); ia.rec = fp(L.off_rec);
   ia.conv_w = nullptr; ia.conv_b = nullptr; ia.conv_silu = 0;
-  ia.tmat = fp(L.off_t); ia.bwt = fp(L.off_bwt); ia.wt = fp(L.off_wt); ia.kbr = fp(L.off_kbr);
+  ia.tmat = fp(L.off_t); ia.bw = fp(L.off_bw); ia.wt = fp(L.off_wt); ia.kbr = fp(L.off_kbr);
   const dim3 gch((unsigned)C, (unsigned)H);
   hipLaunchKernelGGL((kda_intra_kernel<TA, float, false, PlainRec<float>, true>), gch, dim3(256), 0,
                      stream, ia);
@@ -209,7 +209,7 @@ static int launch_bwd(const void* q, const void* k, const void* v, const void* f
   a.A_log = A_log; a.dt_bias = dt_bias; a.cu = cu; a.cfirst = cfirst;
   a.init = init; a.dfin = dfin; a.N = N; a.H = H; a.eps = 1e-6f;
   a.scale = 0.08838834764831845f;  // 1/sqrt(128)
-  a.rec = fp(L.off_rec); a.gam = fp(L.off_gam); a.tmat = fp(L.off_t); a.bwt = fp(L.off_bwt);
+  a.rec = fp(L.off_rec); a.gam = fp(L.off_gam); a.tmat = fp(L.off_t); a.bw = fp(L.off_bw);
   a.wt = fp(L.off_wt); a.kbr = fp(L.off_kbr);
   a.s0 = fp(L.off_s0); a.dsn = fp(L.off_dsn); a.dmat = fp(L.off_d); a.ddmat = fp(L.off_dd);
   a.dqt = fp(L.off_dqt); a.dkb = fp(L.off_dkb); a.dw = fp(L.off_dw); a.dbw = fp(L.off_dbw);

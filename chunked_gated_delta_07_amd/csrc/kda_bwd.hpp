@@ -36,7 +36,7 @@
 // first row of the row block), so no gate strength can overflow it.
 //
 // Kernel sequence (all intermediates FP32 in the workspace):
-//   1. kda_intra_kernel<.., PlainRec, BWD>: records W, Qt^T, Kb^T, U^T, P^T, Gam, T, Bw^T,
+//   1. kda_intra_kernel<.., PlainRec, BWD>: records W, Qt^T, Kb^T, U^T, P^T, Gam, T, Bw,
 //      W^T, Kb
 //   2. kda_bwd_fscan_kernel: S0 of every chunk and D           (per sequence, head, 32 values)
 //   3. kda_bwd_bscan_kernel: dSn of every chunk, dD, dS_init   (same, chunks in reverse)
@@ -78,7 +78,7 @@ struct BwdArgs {
   const float* rec;        // PlainRec record, REC floats
   const float* gam;        // [128]
   const float* tmat;       // T [64][64]
-  const float* bwt;        // Bw^T [128][64]
+  const float* bw;         // Bw [64][128]
   const float* wt;         // W^T [128][64]
   const float* kbr;        // Kb [64][128]
   float* s0;               // state entering the chunk [128 key][128 value]
@@ -528,14 +528,48 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_jprod_kernel(BwdArgs p) {
 // ------------------------------------------------------------ 5. products with T
 // dBu = T^T dD -> dv = beta dBu and db1 = v . dBu per row; dBw = T^T dW;
 // dT = dD Bu^T + dW Bw^T;  dA = -(T^T dT) T^T, strictly lower.
+// LDS holds unpadded matrices whose 16-byte chunks are XOR-swizzled by row
+// (T [64][64], two [64][128] operands; 80 KB in all, two workgroups per CU).
+template <int LC>
+__device__ __forceinline__ int swz(int r, int c) {
+  return r * LC + ((((c >> 2) ^ (r & (LC / 4 - 1)))) << 2) + (c & 3);
+}
+// C[m][n] += sum_k A[m0+m][k] B[n0+n][k], both swizzled rows of K (16-byte reads)
+template <int LCA, int LCB, int K>
+__device__ __forceinline__ f32x4 mma16_rows_swz(const float* A, int m0, const float* B, int n0,
+                                                f32x4 c, int lane) {
+  constexpr int KG = K / 4;
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < KG / 4; ++s) {
+    const int k = g * KG + 4 * s;
+    const f32x4 a4 = *reinterpret_cast<const f32x4*>(A + swz<LCA>(m0 + r, k));
+    const f32x4 b4 = *reinterpret_cast<const f32x4*>(B + swz<LCB>(n0 + r, k));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[e], b4[e], c, 0, 0, 0);
+  }
+  return c;
+}
+// C[m][n] += sum_k At[k][m0+m] B[k][n0+n], both swizzled, k-major
+template <int LCA, int LCB, int K>
+__device__ __forceinline__ f32x4 mma16_tn_swz(const float* At, int m0, const float* B, int n0,
+                                              f32x4 c, int lane) {
+  constexpr int KG = K / 4;
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < KG; ++s) {
+    const int k = g * KG + s;
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(At[swz<LCA>(k, m0 + r)], B[swz<LCB>(k, n0 + r)], c, 0,
+                                             0, 0);
+  }
+  return c;
+}
+
 template <typename TA, typename TR>
-__global__ __launch_bounds__(256) void kda_bwd_tprod_kernel(BwdArgs p) {
-  constexpr int LT = 68, LW = 132, LK = 68;
-  __shared__ __attribute__((aligned(16))) float sT[CHUNK * LT];
-  __shared__ __attribute__((aligned(16))) float sR1[CHUNK * LW];
-  __shared__ __attribute__((aligned(16))) float sR2[DH * LK];  // >= CHUNK * LW floats
-  __shared__ float sBeta[CHUNK];
-  static_assert(DH * LK >= CHUNK * LW && DH * LK >= 2 * CHUNK * LT, "region sizes");
+__global__ __launch_bounds__(256, 2) void kda_bwd_tprod_kernel(BwdArgs p) {
+  __shared__ __attribute__((aligned(16))) float sT[CHUNK * CHUNK];
+  __shared__ __attribute__((aligned(16))) float sR1[CHUNK * DH];
+  __shared__ __attribute__((aligned(16))) float sR2[CHUNK * DH];
   const int c = blockIdx.x, h = blockIdx.y;
   int t0, len;
   if (!bwd_chunk(p, c, t0, len)) return;
@@ -544,46 +578,56 @@ __global__ __launch_bounds__(256) void kda_bwd_tprod_kernel(BwdArgs p) {
   const TA* __restrict__ gv = reinterpret_cast<const TA*>(p.v);
   const TA* __restrict__ gb = reinterpret_cast<const TA*>(p.b);
   TR* __restrict__ gdv = reinterpret_cast<TR*>(p.dv);
-  // phase 1: T, dD, raw v
-  for (int x = tid; x < CHUNK * 16; x += 256) {
-    const int r = x >> 4, i4 = 4 * (x & 15);
-    *reinterpret_cast<f32x4*>(sT + r * LT + i4) =
-        *reinterpret_cast<const f32x4*>(p.tmat + ch * SQM + r * CHUNK + i4);
+  auto beta_of = [&](int i) {
+    return i < len ? sigmoid_f(to_f32(gb[(size_t)(t0 + i) * p.H + h])) : 0.0f;
+  };
+  // phase 1: T, dD, raw v (rows past the end zero)
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int x = tid + 256 * u, r = x >> 4, i4 = 4 * (x & 15);
+    *reinterpret_cast<f32x4*>(sT + swz<CHUNK>(r, i4)) =
+        *reinterpret_cast<const f32x4*>(p.tmat + ch * SQM + 4 * x);
   }
-  for (int x = tid; x < CHUNK * 32; x += 256) {
-    const int r = x >> 5, c4 = 4 * (x & 31);
-    *reinterpret_cast<f32x4*>(sR1 + r * LW + c4) =
-        *reinterpret_cast<const f32x4*>(p.ddmat + ch * MAT + r * DH + c4);
-  }
-  for (int x = tid; x < CHUNK * 64; x += 256) {
-    const int r = x >> 6, c2 = 2 * (x & 63);
-    const f32x2 vv = r < len ? load2(gv + ((size_t)(t0 + r) * p.H + h) * DH + c2) : f32x2{0, 0};
-    sR2[r * LW + c2] = vv[0];
-    sR2[r * LW + c2 + 1] = vv[1];
-  }
-  if (tid < CHUNK) sBeta[tid] = tid < len ? sigmoid_f(to_f32(gb[(size_t)(t0 + tid) * p.H + h])) : 0.0f;
-  __syncthreads();
-  // phase-2 operands (dW, Bw^T) are loaded into registers during phase 1
-  f32x4 rW[8], rB[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    const int x = tid + 256 * u;
-    rW[u] = *reinterpret_cast<const f32x4*>(p.dw + ch * MAT + 4 * x);
-    rB[u] = *reinterpret_cast<const f32x4*>(p.bwt + ch * DH * CHUNK + 4 * x);
+    const int x = tid + 256 * u, r = x >> 5, c4 = 4 * (x & 31);
+    *reinterpret_cast<f32x4*>(sR1 + swz<DH>(r, c4)) =
+        *reinterpret_cast<const f32x4*>(p.ddmat + ch * MAT + 4 * x);
   }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int x = tid + 256 * u, r = x >> 4, c8 = 8 * (x & 15);
+    float vv[8];
+    if (r < len) {
+      load8_scaled(gv + ((size_t)(t0 + r) * p.H + h) * DH + c8, 1.0f, vv);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vv[e] = 0.0f;
+    }
+    *reinterpret_cast<f32x4*>(sR2 + swz<DH>(r, c8)) = f32x4{vv[0], vv[1], vv[2], vv[3]};
+    *reinterpret_cast<f32x4*>(sR2 + swz<DH>(r, c8 + 4)) = f32x4{vv[4], vv[5], vv[6], vv[7]};
+  }
+  // this lane's rows 16w + 4(l/16) + e (dv scale) and columns 16 ib + l%16 (dT scale)
+  float brow[4], bcol[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    brow[e] = beta_of(16 * w + 4 * (l >> 4) + e);
+    bcol[e] = beta_of(16 * e + (l & 15));
+  }
+  __syncthreads();
   // dBu rows i = 16w.. : dv = beta dBu, db1 = sum_j v dBu
   {
     float bsum[4] = {0, 0, 0, 0};
-#pragma unroll
+#pragma unroll 2
     for (int cb = 0; cb < 8; ++cb) {
       f32x4 acc = {0, 0, 0, 0};
-      acc = mma16_f32_tn<CHUNK>(sT + 16 * w, LT, sR1 + 16 * cb, LW, acc, l);
+      acc = mma16_tn_swz<CHUNK, DH, CHUNK>(sT, 16 * w, sR1, 16 * cb, acc, l);
       const int j = 16 * cb + (l & 15);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 16 * w + 4 * (l >> 4) + e;
-        bsum[e] = fmaf(acc[e], sR2[i * LW + j], bsum[e]);
-        if (i < len) gdv[((size_t)(t0 + i) * p.H + h) * DH + j] = from_f32<TR>(sBeta[i] * acc[e]);
+        bsum[e] = fmaf(acc[e], sR2[swz<DH>(i, j)], bsum[e]);
+        if (i < len) gdv[((size_t)(t0 + i) * p.H + h) * DH + j] = from_f32<TR>(brow[e] * acc[e]);
       }
     }
 #pragma unroll
@@ -601,51 +645,53 @@ __global__ __launch_bounds__(256) void kda_bwd_tprod_kernel(BwdArgs p) {
 #pragma unroll
   for (int ib = 0; ib < 4; ++ib) {
     f32x4 acc = {0, 0, 0, 0};
-    acc = mma16_rows<float, DH>(sR1 + 16 * w * LW, LW, sR2 + 16 * ib * LW, LW, acc, l);
-    const float bi = sBeta[16 * ib + (l & 15)];
-    dt[ib] = acc * bi;
+    acc = mma16_rows_swz<DH, DH, DH>(sR1, 16 * w, sR2, 16 * ib, acc, l);
+    dt[ib] = acc * bcol[ib];
   }
   __syncthreads();
-  // phase 2: dW [64][128] -> sR1, Bw^T [128][64] -> sR2
+  // phase 2: dW -> sR1, Bw -> sR2 (the other workgroup on the CU covers the latency)
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    const int x = tid + 256 * u;
-    *reinterpret_cast<f32x4*>(sR1 + (x >> 5) * LW + 4 * (x & 31)) = rW[u];
-    *reinterpret_cast<f32x4*>(sR2 + (x >> 4) * LK + 4 * (x & 15)) = rB[u];
+    const int x = tid + 256 * u, r = x >> 5, c4 = 4 * (x & 31);
+    *reinterpret_cast<f32x4*>(sR1 + swz<DH>(r, c4)) =
+        *reinterpret_cast<const f32x4*>(p.dw + ch * MAT + 4 * x);
+    *reinterpret_cast<f32x4*>(sR2 + swz<DH>(r, c4)) =
+        *reinterpret_cast<const f32x4*>(p.bw + ch * MAT + 4 * x);
   }
   __syncthreads();
+  // dT += dW Bw^T
 #pragma unroll
-  for (int ib = 0; ib < 4; ++ib)
-    dt[ib] = mma16_f32_kn<DH>(sR1 + 16 * w * LW, LW, sR2 + 16 * ib, LK, dt[ib], l);
-#pragma unroll
+  for (int ib = 0; ib < 4; ++ib) dt[ib] = mma16_rows_swz<DH, DH, DH>(sR1, 16 * w, sR2, 16 * ib, dt[ib], l);
+  // dBw = T^T dW
+#pragma unroll 2
   for (int cb = 0; cb < 8; ++cb) {
     f32x4 acc = {0, 0, 0, 0};
-    acc = mma16_f32_tn<CHUNK>(sT + 16 * w, LT, sR1 + 16 * cb, LW, acc, l);
+    acc = mma16_tn_swz<CHUNK, DH, CHUNK>(sT, 16 * w, sR1, 16 * cb, acc, l);
     const int col = 16 * cb + (l & 15);
 #pragma unroll
     for (int e = 0; e < 4; ++e) p.dbw[ch * MAT + (16 * w + 4 * (l >> 4) + e) * DH + col] = acc[e];
   }
   __syncthreads();
-  // phase 3: X = T^T dT, dA = -X T^T (strictly lower)
+  // phase 3: X = T^T dT, dA = -X T^T (strictly lower); dT and X in sR2
   float* sDT = sR2;
-  float* sX = sR2 + CHUNK * LT;
+  float* sX = sR2 + SQM;
 #pragma unroll
   for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sDT[(16 * w + 4 * (l >> 4) + e) * LT + 16 * ib + (l & 15)] = dt[ib][e];
+    for (int e = 0; e < 4; ++e) sDT[swz<CHUNK>(16 * w + 4 * (l >> 4) + e, 16 * ib + (l & 15))] = dt[ib][e];
   __syncthreads();
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     f32x4 acc = {0, 0, 0, 0};
-    acc = mma16_f32_tn<CHUNK>(sT + 16 * w, LT, sDT + 16 * mb, LT, acc, l);
+    acc = mma16_tn_swz<CHUNK, CHUNK, CHUNK>(sT, 16 * w, sDT, 16 * mb, acc, l);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sX[(16 * w + 4 * (l >> 4) + e) * LT + 16 * mb + (l & 15)] = acc[e];
+    for (int e = 0; e < 4; ++e) sX[swz<CHUNK>(16 * w + 4 * (l >> 4) + e, 16 * mb + (l & 15))] = acc[e];
   }
   __syncthreads();
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb) {
     f32x4 acc = {0, 0, 0, 0};
-    acc = mma16_rows<float, CHUNK>(sX + 16 * w * LT, LT, sT + 16 * jb * LT, LT, acc, l);
+    acc = mma16_rows_swz<CHUNK, CHUNK, CHUNK>(sX, 16 * w, sT, 16 * jb, acc, l);
     const int j = 16 * jb + (l & 15);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -841,14 +887,13 @@ __global__ __launch_bounds__(512) void kda_bwd_gate_kernel(BwdArgs p) {
 
 // ------------------------------------------------------------ 7. elementwise chain
 // Wave w: rows 16w..16w+15, lane channels c0, c0+1.  Row-local parts (dq, dk,
-// db, dG) row by row; dG and x = f + dt_bias go to LDS.  Then the reverse
+// db, dG) row by row; dG goes to LDS.  Then the reverse
 // prefix of dG over the chunk: inside the wave over its 16 rows from LDS,
 // across waves one carry (column totals of the later waves plus the last
 // row's d(G_last) terms), giving df and the per-chunk parameter partials.
 template <typename TA, typename TR>
 __global__ __launch_bounds__(256) void kda_bwd_final_kernel(BwdArgs p) {
   __shared__ __attribute__((aligned(16))) float sDG[CHUNK * DH];
-  __shared__ __attribute__((aligned(16))) float sX[CHUNK * DH];
   __shared__ float sTot[4][DH];
   __shared__ float sCol[4][DH];
   __shared__ float sPdt[4][DH];
@@ -879,7 +924,6 @@ __global__ __launch_bounds__(256) void kda_bwd_final_kernel(BwdArgs p) {
     const f32x2 qn = load2(p.qn + o), kn = load2(p.kn + o), g2 = load2(p.g2 + o);
     const f32x2 al = load2(p.al + o), pv = load2(p.pi + o), rh = load2(p.rho + o);
     const f32x2 dqt = load2(p.dqt + o), dkb = load2(p.dkb + o), dbw = load2(p.dbw + o);
-    const f32x2 fv = load2(gf + ((size_t)(t0 + rr) * p.H + h) * DH + c0);
     const float bv = to_f32(gb[(size_t)(t0 + rr) * p.H + h]);
     const float beta = ok ? sigmoid_f(bv) : 0.0f;
     float dqn[2], dkn[2], dG[2], kbf[2], sb = 0.0f;
@@ -897,7 +941,6 @@ __global__ __launch_bounds__(256) void kda_bwd_final_kernel(BwdArgs p) {
     tot0 += dG[0]; tot1 += dG[1];
     col0 += kbf[0]; col1 += kbf[1];
     *reinterpret_cast<f32x2*>(sDG + r * DH + c0) = f32x2{dG[0], dG[1]};
-    *reinterpret_cast<f32x2*>(sX + r * DH + c0) = fv + dtb;
     const float s_b = wave_sum(sb);
     const float s_q = wave_sum(qn[0] * dqn[0] + qn[1] * dqn[1]);
     const float s_k = wave_sum(kn[0] * dkn[0] + kn[1] * dkn[1]);
@@ -925,11 +968,19 @@ __global__ __launch_bounds__(256) void kda_bwd_final_kernel(BwdArgs p) {
     carry[x] = a;
   }
   float pdt0 = 0.0f, pdt1 = 0.0f, pa = 0.0f;
+  // x = f + dt_bias of the wave's 16 rows, loaded together (second read, cached)
+  f32x2 xs[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int r = 16 * w + j;
+    xs[j] = load2(gf + ((size_t)(t0 + (r < len ? r : 0)) * p.H + h) * DH + c0) + dtb;
+  }
+#pragma unroll
   for (int j = 15; j >= 0; --j) {
     const int r = 16 * w + j;
     if (r >= len) continue;  // uniform over the wave
     const f32x2 dg = *reinterpret_cast<const f32x2*>(sDG + r * DH + c0);
-    const f32x2 xx = *reinterpret_cast<const f32x2*>(sX + r * DH + c0);
+    const f32x2 xx = xs[j];
     carry[0] += dg[0];
     carry[1] += dg[1];
     const float dx0 = lam == 0.0f ? 0.0f : -lam * sigmoid_f(xx[0]) * carry[0];

@@ -113,9 +113,9 @@ struct IntraArgs {
   const float* conv_b;
   int conv_silu;
   // backward recomputation only (kernel parameter BWD): T = (I + A)^{-1}
-  // [chunks][H][64][64] and (Diag(beta) (k^ * E))^T [chunks][H][128][64], FP32
+  // [chunks][H][64][64] and Bw = Diag(beta) (k^ * E) [chunks][H][64][128], FP32
   float* tmat;
-  float* bwt;
+  float* bw;
   // and W^T [128][64], Kb [64][128] (the backward's reverse state scan)
   float* wt;
   float* kbr;
@@ -749,9 +749,9 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
       store4(sXt + c0 * TL + 16 * w + j, f32x4{kg0[j], kg0[j + 1], kg0[j + 2], kg0[j + 3]});
       store4(sXt + (c0 + 1) * TL + 16 * w + j, f32x4{kg1[j], kg1[j + 1], kg1[j + 2], kg1[j + 3]});
       if constexpr (BWD) {
-        float* gb = p.bwt + ((size_t)chunk * H + h) * DH * CHUNK;
-        store4(gb + c0 * CHUNK + 16 * w + j, f32x4{kg0[j], kg0[j + 1], kg0[j + 2], kg0[j + 3]});
-        store4(gb + (c0 + 1) * CHUNK + 16 * w + j, f32x4{kg1[j], kg1[j + 1], kg1[j + 2], kg1[j + 3]});
+        float* gb = p.bw + ((size_t)chunk * H + h) * CHUNK * DH;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) store2(gb + (16 * w + j + e) * DH + c0, kg0[j + e], kg1[j + e]);
       }
     }
   }

@@ -234,3 +234,36 @@ def test_bwd_ragged_65536_sampled_head():
                               dout[:, hd].astype(np.float64),
                               dfinal_state=dfin[:, hd].astype(np.float64))
     _check(got, ref, TOL_FP32, f"ragged 65536 ({N} seqs) head 23")
+
+
+def test_bwd_mode_bit_changes_nothing():
+    """KDA_MODE_FP32_INTERMEDIATE is accepted by kda_chunk_bwd and changes
+    nothing: the backward recomputes in FP32 whatever the forward used.
+    Called through the C ABI with the bit clear and set; bitwise equal."""
+    import ctypes
+
+    import torch
+
+    from chunked_gated_delta_07_amd import kda
+
+    inp, dout, init, dfin = _case([70, 30], 2, "bf16", seed=12, grad_fp32=False)
+    dev = "cuda:0"
+    args = U.to_device(inp, dev)
+    T, H, N = inp.T, inp.H, 2
+    lib = kda.load_library()
+    d = torch.from_numpy(dout).to(dev).to(torch.bfloat16)
+    ws = torch.empty(kda.bwd_workspace_bytes(T, N, H, 128, 1), dtype=torch.uint8, device=dev)
+    outs = []
+    for mode in (0, kda.KDA_MODE_FP32_INTERMEDIATE):
+        g = [torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev) for _ in range(4)]
+        g.append(torch.empty((T, H), dtype=torch.bfloat16, device=dev))
+        par = [torch.empty(H, device=dev), torch.empty((H, 128), device=dev)]
+        st = lib.kda_chunk_bwd(*[kda._ptr(a) for a in args], N, T, H, 128, mode, None, kda._ptr(d),
+                               None, *[kda._ptr(x) for x in g], *[kda._ptr(x) for x in par], None,
+                               kda._ptr(ws), ws.numel(),
+                               ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert st == kda.KDA_OK
+        torch.cuda.synchronize()
+        outs.append(g + par)
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)

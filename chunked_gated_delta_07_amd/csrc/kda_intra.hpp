@@ -157,6 +157,13 @@ template <typename MT> struct IntraLds {
   static constexpr int ROWL = sizeof(MT) == 2 ? 136 : 132;  // padded row of 128 channels
   static constexpr int TL = sizeof(MT) == 2 ? 72 : 68;      // padded row of 64 tokens
   static constexpr int AL = 68;                              // fp32 64x64 row
+  // FP32 operands take twice the bytes: their 128-channel contractions run as
+  // NP = 2 passes over 64-channel halves (lanes 32p..32p+31 hold channels
+  // 64p..64p+63) through half-width buffers of row stride ROWP, so the kernel
+  // fits two workgroups per CU like the bf16 one.
+  static constexpr int NP = sizeof(MT) == 2 ? 1 : 2;
+  static constexpr int ROWP = NP == 1 ? ROWL : 68;
+  static constexpr bool TS_ALIAS = sizeof(MT) == 4;  // FP32: the "scaled" T is T itself
   // fixed part
   static constexpr int O_BETA = 0;                  // float[64]
   static constexpr int O_RK = O_BETA + 256;         // float[64]
@@ -167,16 +174,19 @@ template <typename MT> struct IntraLds {
   static constexpr int O_U = O_A + 64 * AL * 4;     // union region
   // union, phase 1: per wave private rows: raw k [16], raw q [16], pair vectors [16]
   static constexpr int PRIV_ROWS = 48;
-  static constexpr int PRIV_BYTES = PRIV_ROWS * ROWL * (int)sizeof(MT);
+  static constexpr int PRIV_BYTES = PRIV_ROWS * ROWP * (int)sizeof(MT);
   // union, phase 2: cross-block operands: A-side rows (kL,qL for R=1..3) 96, B-side 96
   static constexpr int X_ROWS = 192;
-  // union, phase 3: T (float [64][AL]), T-scaled operand (MT [64][TL]), transposed (MT [128][TL])
+  // union, phase 3: T (float [64][AL]), T-scaled operand (MT [64][TL], or T itself),
+  // transposed operand (MT [128 / NP][TL])
   static constexpr int O_T = 0;
-  static constexpr int O_TS = O_T + 64 * AL * 4;
-  static constexpr int O_XT = O_TS + 64 * TL * (int)sizeof(MT);
+  static constexpr int O_TS = TS_ALIAS ? O_T : O_T + 64 * AL * 4;
+  static constexpr int O_XT = TS_ALIAS ? O_T + 64 * AL * 4 : O_TS + 64 * TL * (int)sizeof(MT);
   static constexpr int U_P1 = 4 * PRIV_BYTES;
-  static constexpr int U_P2 = X_ROWS * ROWL * (int)sizeof(MT);
-  static constexpr int U_P3 = O_XT + 128 * TL * (int)sizeof(MT);
+  static constexpr int U_P2 = X_ROWS * ROWP * (int)sizeof(MT);
+  static constexpr int U_P3 = O_XT + (128 / NP) * TL * (int)sizeof(MT);
+  // scratch of the 16x16 block substitution (phase 3, before W/U use O_XT)
+  static constexpr int O_SCR = TS_ALIAS ? O_XT : O_TS;
   static constexpr int U_BYTES = U_P1 > U_P2 ? (U_P1 > U_P3 ? U_P1 : U_P3) : (U_P2 > U_P3 ? U_P2 : U_P3);
   static constexpr int BYTES = O_U + U_BYTES;
 };
@@ -339,134 +349,295 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
     }
     if (l < 16) sBeta[16 * w + l] = (16 * w + l < len) ? sigmoid_f(bl) : 0.0f;
   }
-  // raw rows for the MFMA work inside the diagonal block (wave-private)
-  MT* priv = reinterpret_cast<MT*>(sU + w * L::PRIV_BYTES);
-  MT* pK = priv;               // rows 0..15
-  MT* pQ = priv + 16 * ROWL;   // rows 16..31
-  MT* pD = priv + 32 * ROWL;   // rows 32..47 (pair vectors)
+  if constexpr (L::NP == 2) {
+    // FP32: every product of the diagonal-block work in two passes over
+    // 64-channel halves.  The first pass parks its raw partial sums in sA (A
+    // entries in place, P entries in the unused upper triangle, transposed);
+    // the second adds its own, applies the norms (complete by then) and writes
+    // the final entries.  Every entry is read back by the lane that parked it.
+    constexpr int RP = L::ROWP;
+    MT* priv = reinterpret_cast<MT*>(sU + w * L::PRIV_BYTES);
+    MT* pK = priv;             // rows 0..15
+    MT* pQ = priv + 16 * RP;   // rows 16..31
+    MT* pD = priv + 32 * RP;   // rows 32..47 (pair vectors)
+    {
+      float t0c = 1.0f, t1c = 1.0f;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    store2(pK + j * ROWL + c0, ka[j][0], ka[j][1]);
-    store2(pQ + j * ROWL + c0, qa[j][0], qa[j][1]);
-  }
-  {
-    float t0c = 1.0f, t1c = 1.0f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) { t0c *= aa[j][0]; t1c *= aa[j][1]; }
-    sTot[w * DH + c0] = t0c; sTot[w * DH + c0 + 1] = t1c;
-    sA0[w * DH + c0] = aa[0][0]; sA0[w * DH + c0 + 1] = aa[0][1];
-  }
-  // From here to the end of the diagonal-block work each wave touches only
-  // its own rows: LDS traffic of one wave is processed in program order, so a
-  // compiler-level fence is all the ordering needed.
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-
-  // Norms (sum of squares) and the plain q.k diagonal via MFMA on the raw rows.
-  {
-    f32x4 ckk = {0, 0, 0, 0}, cqq = {0, 0, 0, 0}, cqk = {0, 0, 0, 0};
-    ckk = mma16_rows<MT, DH>(pK, ROWL, pK, ROWL, ckk, l);
-    cqq = mma16_rows<MT, DH>(pQ, ROWL, pQ, ROWL, cqq, l);
-    cqk = mma16_rows<MT, DH>(pQ, ROWL, pK, ROWL, cqk, l);
-    const int n = l & 15, m0 = 4 * (l >> 4);
-    if (n >= m0 && n < m0 + 4) {
-      const int e = n - m0;
-      const int r = 16 * w + n;
-      const float rk = rsqrt_hw(ckk[e] + p.eps);
-      const float rq = rsqrt_hw(cqq[e] + p.eps);
-      sRk[r] = rk;
-      sRq[r] = rq;
-      gP[LY::pm(r, r)] = from_f32<MT>(rq * rk * cqk[e]);  // P[r][r], decay 1
+      for (int j = 0; j < 16; ++j) { t0c *= aa[j][0]; t1c *= aa[j][1]; }
+      sTot[w * DH + c0] = t0c; sTot[w * DH + c0 + 1] = t1c;
+      sA0[w * DH + c0] = aa[0][0]; sA0[w * DH + c0 + 1] = aa[0][1];
     }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-
-  // Diagonal block, rows 8..15 x columns 0..7: factorised about row 8,
-  //   A[u][i] ~ (k_u prod_{8<j<=u} a_j) . (k_i prod_{i<j<=8} a_j),
-  // both factors <= 1.  X8 rows 0..7 hold the column factors, rows 8..15 the
-  // row factors of k (then of q for P); one MFMA tile each, block [8..15][0..7].
-  {
-    float x0 = 1.0f, x1 = 1.0f;
-    float ra0[8], ra1[8];
-#pragma unroll
-    for (int j = 8; j < 16; ++j) {
-      if (j > 8) { x0 *= aa[j][0]; x1 *= aa[j][1]; }
-      ra0[j - 8] = x0; ra1[j - 8] = x1;
-      store2(pD + j * ROWL + c0, ka[j][0] * x0, ka[j][1] * x1);
-    }
-    float y0 = aa[8][0], y1 = aa[8][1];
-#pragma unroll
-    for (int j = 7; j >= 0; --j) {
-      store2(pD + j * ROWL + c0, ka[j][0] * y0, ka[j][1] * y1);
-      y0 *= aa[j][0]; y1 *= aa[j][1];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    f32x4 ca = {0, 0, 0, 0};
-    ca = mma16_rows<MT, DH>(pD, ROWL, pD, ROWL, ca, l);
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int j = 8; j < 16; ++j) store2(pD + j * ROWL + c0, qa[j][0] * ra0[j - 8], qa[j][1] * ra1[j - 8]);
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    f32x4 cp = {0, 0, 0, 0};
-    cp = mma16_rows<MT, DH>(pD, ROWL, pD, ROWL, cp, l);
-    const int n = l & 15, m0 = 4 * (l >> 4);
-    if (m0 >= 8 && n < 8) {
-      const int ri = 16 * w + n;
-      const float rki = sRk[ri];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int ru = 16 * w + m0 + e;
-        sA[ru * AL + ri] = sBeta[ru] * sRk[ru] * rki * ca[e];
-        gP[LY::pm(ru, ri)] = from_f32<MT>(sRq[ru] * rki * cp[e]);
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-  }
-  // Inside each 8-row half: pair vectors kd_(u,i)[c] = k_i[c] prod_{i<j<=u} a_j[c],
-  // 16 per batch; MFMA k.kd and q.kd; keep the (u, column) entry.
-  {
-    float d0 = 1.0f, d1 = 1.0f;
-#pragma unroll
-    for (int bt = 0; bt < NBATCH; ++bt) {
-#pragma unroll
-      for (int n = 0; n < 16; ++n) {
-        const int pp = 16 * bt + n;
-        if (pp < NPAIR) {
-          const int i = pair_i(pp), u = pair_u(pp);
-          if (u == i + 1) { d0 = aa[u][0]; d1 = aa[u][1]; }
-          else { d0 *= aa[u][0]; d1 *= aa[u][1]; }
-          store2(pD + n * ROWL + c0, ka[i][0] * d0, ka[i][1] * d1);
-        } else {
-          store2(pD + n * ROWL + c0, 0.0f, 0.0f);
-        }
-      }
+    const int cl = c0 - 64 * (l >> 5);  // this lane's first channel inside its half
+    // each wave touches only its own rows: a compiler-level fence orders its LDS traffic
+    auto wsync = [] {
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
       __builtin_amdgcn_wave_barrier();
-      f32x4 ca = {0, 0, 0, 0}, cp = {0, 0, 0, 0};
-      ca = mma16_rows<MT, DH>(pK, ROWL, pD, ROWL, ca, l);
-      cp = mma16_rows<MT, DH>(pQ, ROWL, pD, ROWL, cp, l);
+    };
+    // entry (ru, ri), ri < ru, of A (va) and P (vp) in pass ps
+    auto entry = [&](int ps, int ru, int ri, float va, float vp) {
+      float* sa = sA + ru * AL + ri;
+      float* sp = sA + ri * AL + ru;
+      if (ps == 0) {
+        *sa = va;
+        *sp = vp;
+      } else {
+        va += *sa;
+        vp += *sp;
+        *sa = sBeta[ru] * sRk[ru] * sRk[ri] * va;
+        gP[LY::pm(ru, ri)] = from_f32<MT>(sRq[ru] * sRk[ri] * vp);
+      }
+    };
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+      const bool mine = (l >> 5) == ps;
+      // the decays pass through an empty asm per pass, so the compiler cannot
+      // form the products of both passes once and keep them all live
+      float la[16][2];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        la[j][0] = aa[j][0]; la[j][1] = aa[j][1];
+        asm volatile("" : "+v"(la[j][0]), "+v"(la[j][1]));
+      }
+      if (mine) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          store2(pK + j * RP + cl, ka[j][0], ka[j][1]);
+          store2(pQ + j * RP + cl, qa[j][0], qa[j][1]);
+        }
+      }
+      wsync();
+      // norms (sums of squares) and the plain q.k diagonal; the first pass
+      // parks its sums in sRk, sRq and the diagonal of sA
       {
-        const int n = l & 15, pp = 16 * bt + n;
-        if (pp < NPAIR) {
-          const int i = pair_i(pp), u = pair_u(pp);
-          const int m0 = 4 * (l >> 4);
-          if (u >= m0 && u < m0 + 4) {
-            const int e = u - m0;
-            const float va = e == 0 ? ca[0] : e == 1 ? ca[1] : e == 2 ? ca[2] : ca[3];
-            const float vp = e == 0 ? cp[0] : e == 1 ? cp[1] : e == 2 ? cp[2] : cp[3];
-            const int ru = 16 * w + u, ri = 16 * w + i;
-            sA[ru * AL + ri] = sBeta[ru] * sRk[ru] * sRk[ri] * va;
-            gP[LY::pm(ru, ri)] = from_f32<MT>(sRq[ru] * sRk[ri] * vp);
+        f32x4 ckk = {0, 0, 0, 0}, cqq = {0, 0, 0, 0}, cqk = {0, 0, 0, 0};
+        ckk = mma16_rows<MT, CHUNK>(pK, RP, pK, RP, ckk, l);
+        cqq = mma16_rows<MT, CHUNK>(pQ, RP, pQ, RP, cqq, l);
+        cqk = mma16_rows<MT, CHUNK>(pQ, RP, pK, RP, cqk, l);
+        const int n = l & 15, m0 = 4 * (l >> 4);
+        if (n >= m0 && n < m0 + 4) {
+          const int e = n - m0;
+          const int r = 16 * w + n;
+          const float vkk = e == 0 ? ckk[0] : e == 1 ? ckk[1] : e == 2 ? ckk[2] : ckk[3];
+          const float vqq = e == 0 ? cqq[0] : e == 1 ? cqq[1] : e == 2 ? cqq[2] : cqq[3];
+          const float vqk = e == 0 ? cqk[0] : e == 1 ? cqk[1] : e == 2 ? cqk[2] : cqk[3];
+          if (ps == 0) {
+            sRk[r] = vkk;
+            sRq[r] = vqq;
+            sA[r * AL + r] = vqk;
+          } else {
+            const float rk = rsqrt_hw(sRk[r] + vkk + p.eps);
+            const float rq = rsqrt_hw(sRq[r] + vqq + p.eps);
+            sRk[r] = rk;
+            sRq[r] = rq;
+            gP[LY::pm(r, r)] = from_f32<MT>(rq * rk * (sA[r * AL + r] + vqk));  // P[r][r], decay 1
           }
         }
       }
+      // diagonal block rows 8..15 x columns 0..7, factorised about row 8:
+      // k row factors (rows 8..15) and column factors (rows 0..7), then q row factors
+      float ra0[8], ra1[8];
+      if (mine) {
+        float x0 = 1.0f, x1 = 1.0f;
+#pragma unroll
+        for (int j = 8; j < 16; ++j) {
+          if (j > 8) { x0 *= la[j][0]; x1 *= la[j][1]; }
+          ra0[j - 8] = x0; ra1[j - 8] = x1;
+          store2(pD + j * RP + cl, ka[j][0] * x0, ka[j][1] * x1);
+        }
+        float y0 = la[8][0], y1 = la[8][1];
+#pragma unroll
+        for (int j = 7; j >= 0; --j) {
+          store2(pD + j * RP + cl, ka[j][0] * y0, ka[j][1] * y1);
+          y0 *= la[j][0]; y1 *= la[j][1];
+        }
+      }
+      wsync();
+      f32x4 c8a = {0, 0, 0, 0};
+      c8a = mma16_rows<MT, CHUNK>(pD, RP, pD, RP, c8a, l);
+      wsync();
+      if (mine) {
+#pragma unroll
+        for (int j = 8; j < 16; ++j) store2(pD + j * RP + cl, qa[j][0] * ra0[j - 8], qa[j][1] * ra1[j - 8]);
+      }
+      wsync();
+      f32x4 c8p = {0, 0, 0, 0};
+      c8p = mma16_rows<MT, CHUNK>(pD, RP, pD, RP, c8p, l);
+      {
+        const int n = l & 15, m0 = 4 * (l >> 4);
+        if (m0 >= 8 && n < 8) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) entry(ps, 16 * w + m0 + e, 16 * w + n, c8a[e], c8p[e]);
+        }
+      }
+      wsync();
+      // pair vectors inside each 8-row half, 16 per batch
+      float d0 = 1.0f, d1 = 1.0f;
+#pragma unroll
+      for (int bt = 0; bt < NBATCH; ++bt) {
+        if (mine) {
+#pragma unroll
+          for (int n = 0; n < 16; ++n) {
+            const int pp = 16 * bt + n;
+            if (pp < NPAIR) {
+              const int i = pair_i(pp), u = pair_u(pp);
+              if (u == i + 1) { d0 = la[u][0]; d1 = la[u][1]; }
+              else { d0 *= la[u][0]; d1 *= la[u][1]; }
+              store2(pD + n * RP + cl, ka[i][0] * d0, ka[i][1] * d1);
+            } else {
+              store2(pD + n * RP + cl, 0.0f, 0.0f);
+            }
+          }
+        }
+        wsync();
+        f32x4 ca = {0, 0, 0, 0}, cp = {0, 0, 0, 0};
+        ca = mma16_rows<MT, CHUNK>(pK, RP, pD, RP, ca, l);
+        cp = mma16_rows<MT, CHUNK>(pQ, RP, pD, RP, cp, l);
+        {
+          const int n = l & 15, pp = 16 * bt + n;
+          if (pp < NPAIR) {
+            const int i = pair_i(pp), u = pair_u(pp);
+            const int m0 = 4 * (l >> 4);
+            if (u >= m0 && u < m0 + 4) {
+              const int e = u - m0;
+              const float va = e == 0 ? ca[0] : e == 1 ? ca[1] : e == 2 ? ca[2] : ca[3];
+              const float vp = e == 0 ? cp[0] : e == 1 ? cp[1] : e == 2 ? cp[2] : cp[3];
+              entry(ps, 16 * w + u, 16 * w + i, va, vp);
+            }
+          }
+        }
+        wsync();
+      }
+    }
+  } else {
+    // raw rows for the MFMA work inside the diagonal block (wave-private)
+    MT* priv = reinterpret_cast<MT*>(sU + w * L::PRIV_BYTES);
+    MT* pK = priv;               // rows 0..15
+    MT* pQ = priv + 16 * ROWL;   // rows 16..31
+    MT* pD = priv + 32 * ROWL;   // rows 32..47 (pair vectors)
+  #pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      store2(pK + j * ROWL + c0, ka[j][0], ka[j][1]);
+      store2(pQ + j * ROWL + c0, qa[j][0], qa[j][1]);
+    }
+    {
+      float t0c = 1.0f, t1c = 1.0f;
+  #pragma unroll
+      for (int j = 0; j < 16; ++j) { t0c *= aa[j][0]; t1c *= aa[j][1]; }
+      sTot[w * DH + c0] = t0c; sTot[w * DH + c0 + 1] = t1c;
+      sA0[w * DH + c0] = aa[0][0]; sA0[w * DH + c0 + 1] = aa[0][1];
+    }
+    // From here to the end of the diagonal-block work each wave touches only
+    // its own rows: LDS traffic of one wave is processed in program order, so a
+    // compiler-level fence is all the ordering needed.
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+
+    // Norms (sum of squares) and the plain q.k diagonal via MFMA on the raw rows.
+    {
+      f32x4 ckk = {0, 0, 0, 0}, cqq = {0, 0, 0, 0}, cqk = {0, 0, 0, 0};
+      ckk = mma16_rows<MT, DH>(pK, ROWL, pK, ROWL, ckk, l);
+      cqq = mma16_rows<MT, DH>(pQ, ROWL, pQ, ROWL, cqq, l);
+      cqk = mma16_rows<MT, DH>(pQ, ROWL, pK, ROWL, cqk, l);
+      const int n = l & 15, m0 = 4 * (l >> 4);
+      if (n >= m0 && n < m0 + 4) {
+        const int e = n - m0;
+        const int r = 16 * w + n;
+        const float rk = rsqrt_hw(ckk[e] + p.eps);
+        const float rq = rsqrt_hw(cqq[e] + p.eps);
+        sRk[r] = rk;
+        sRq[r] = rq;
+        gP[LY::pm(r, r)] = from_f32<MT>(rq * rk * cqk[e]);  // P[r][r], decay 1
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+
+    // Diagonal block, rows 8..15 x columns 0..7: factorised about row 8,
+    //   A[u][i] ~ (k_u prod_{8<j<=u} a_j) . (k_i prod_{i<j<=8} a_j),
+    // both factors <= 1.  X8 rows 0..7 hold the column factors, rows 8..15 the
+    // row factors of k (then of q for P); one MFMA tile each, block [8..15][0..7].
+    {
+      float x0 = 1.0f, x1 = 1.0f;
+      float ra0[8], ra1[8];
+  #pragma unroll
+      for (int j = 8; j < 16; ++j) {
+        if (j > 8) { x0 *= aa[j][0]; x1 *= aa[j][1]; }
+        ra0[j - 8] = x0; ra1[j - 8] = x1;
+        store2(pD + j * ROWL + c0, ka[j][0] * x0, ka[j][1] * x1);
+      }
+      float y0 = aa[8][0], y1 = aa[8][1];
+  #pragma unroll
+      for (int j = 7; j >= 0; --j) {
+        store2(pD + j * ROWL + c0, ka[j][0] * y0, ka[j][1] * y1);
+        y0 *= aa[j][0]; y1 *= aa[j][1];
+      }
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
       __builtin_amdgcn_wave_barrier();
+      f32x4 ca = {0, 0, 0, 0};
+      ca = mma16_rows<MT, DH>(pD, ROWL, pD, ROWL, ca, l);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+  #pragma unroll
+      for (int j = 8; j < 16; ++j) store2(pD + j * ROWL + c0, qa[j][0] * ra0[j - 8], qa[j][1] * ra1[j - 8]);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      f32x4 cp = {0, 0, 0, 0};
+      cp = mma16_rows<MT, DH>(pD, ROWL, pD, ROWL, cp, l);
+      const int n = l & 15, m0 = 4 * (l >> 4);
+      if (m0 >= 8 && n < 8) {
+        const int ri = 16 * w + n;
+        const float rki = sRk[ri];
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ru = 16 * w + m0 + e;
+          sA[ru * AL + ri] = sBeta[ru] * sRk[ru] * rki * ca[e];
+          gP[LY::pm(ru, ri)] = from_f32<MT>(sRq[ru] * rki * cp[e]);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    }
+    // Inside each 8-row half: pair vectors kd_(u,i)[c] = k_i[c] prod_{i<j<=u} a_j[c],
+    // 16 per batch; MFMA k.kd and q.kd; keep the (u, column) entry.
+    {
+      float d0 = 1.0f, d1 = 1.0f;
+  #pragma unroll
+      for (int bt = 0; bt < NBATCH; ++bt) {
+  #pragma unroll
+        for (int n = 0; n < 16; ++n) {
+          const int pp = 16 * bt + n;
+          if (pp < NPAIR) {
+            const int i = pair_i(pp), u = pair_u(pp);
+            if (u == i + 1) { d0 = aa[u][0]; d1 = aa[u][1]; }
+            else { d0 *= aa[u][0]; d1 *= aa[u][1]; }
+            store2(pD + n * ROWL + c0, ka[i][0] * d0, ka[i][1] * d1);
+          } else {
+            store2(pD + n * ROWL + c0, 0.0f, 0.0f);
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        f32x4 ca = {0, 0, 0, 0}, cp = {0, 0, 0, 0};
+        ca = mma16_rows<MT, DH>(pK, ROWL, pD, ROWL, ca, l);
+        cp = mma16_rows<MT, DH>(pQ, ROWL, pD, ROWL, cp, l);
+        {
+          const int n = l & 15, pp = 16 * bt + n;
+          if (pp < NPAIR) {
+            const int i = pair_i(pp), u = pair_u(pp);
+            const int m0 = 4 * (l >> 4);
+            if (u >= m0 && u < m0 + 4) {
+              const int e = u - m0;
+              const float va = e == 0 ? ca[0] : e == 1 ? ca[1] : e == 2 ? ca[2] : ca[3];
+              const float vp = e == 0 ? cp[0] : e == 1 ? cp[1] : e == 2 ? cp[2] : cp[3];
+              const int ru = 16 * w + u, ri = 16 * w + i;
+              sA[ru * AL + ri] = sBeta[ru] * sRk[ru] * sRk[ri] * va;
+              gP[LY::pm(ru, ri)] = from_f32<MT>(sRq[ru] * sRk[ri] * vp);
+            }
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+      }
     }
   }
   __syncthreads();
@@ -524,59 +695,130 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
   // Cross-block operands.  A-side (rows of block R = w >= 1, reference = the
   // block's first row): kL = k * prod_{16R<j<=r} a_j, qL likewise.  B-side
   // (rows of block I = w for every R > w): kR = k * prod_{i<j<=16R} a_j.
-  MT* xA = reinterpret_cast<MT*>(sU);              // [3][32] rows: kL then qL of R=1..3
-  MT* xB = reinterpret_cast<MT*>(sU) + 96 * ROWL;  // [6][16] rows
-  if (w >= 1) {
-    float x0 = 1.0f, x1 = 1.0f;
+  if constexpr (L::NP == 2) {
+    // FP32: the same operands and products in two 64-channel passes
+    constexpr int RP = L::ROWP;
+    MT* xA = reinterpret_cast<MT*>(sU);            // [3][32] rows: kL then qL of R=1..3
+    MT* xB = reinterpret_cast<MT*>(sU) + 96 * RP;  // [6][16] rows
+    const int cl = c0 - 64 * (l >> 5);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (j > 0) { x0 *= aa[j][0]; x1 *= aa[j][1]; }
-      store2(xA + ((w - 1) * 32 + j) * ROWL + c0, ka[j][0] * x0, ka[j][1] * x1);
-      store2(xA + ((w - 1) * 32 + 16 + j) * ROWL + c0, qa[j][0] * x0, qa[j][1] * x1);
+    for (int ps = 0; ps < 2; ++ps) {
+      if ((l >> 5) == ps) {
+        if (w >= 1) {
+          float x0 = 1.0f, x1 = 1.0f;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            if (j > 0) { x0 *= aa[j][0]; x1 *= aa[j][1]; }
+            store2(xA + ((w - 1) * 32 + j) * RP + cl, ka[j][0] * x0, ka[j][1] * x1);
+            store2(xA + ((w - 1) * 32 + 16 + j) * RP + cl, qa[j][0] * x0, qa[j][1] * x1);
+          }
+        }
+        if (w <= 2) {
+          float ks0[16], ks1[16];
+          float s0 = 1.0f, s1 = 1.0f;
+#pragma unroll
+          for (int j = 15; j >= 0; --j) {
+            ks0[j] = ka[j][0] * s0; ks1[j] = ka[j][1] * s1;
+            s0 *= aa[j][0]; s1 *= aa[j][1];
+          }
+#pragma unroll
+          for (int R = 1; R < 4; ++R) {
+            if (R > w) {
+              float k0 = sA0[R * DH + c0], k1 = sA0[R * DH + c0 + 1];
+#pragma unroll
+              for (int x = 1; x < 4; ++x)
+                if (x > w && x < R) { k0 *= sTot[x * DH + c0]; k1 *= sTot[x * DH + c0 + 1]; }
+              MT* dst = xB + combo(R, w) * 16 * RP;
+#pragma unroll
+              for (int j = 0; j < 16; ++j) store2(dst + j * RP + cl, ks0[j] * k0, ks1[j] * k1);
+            }
+          }
+        }
+      }
+      __syncthreads();
+      // the first pass parks its partial sums (A in place, P transposed into
+      // the upper triangle of sA); the second adds its own and finalises
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        const int tp = 3 * w + t;  // 0..11
+        const int cmb = tp >> 1, isq = tp & 1;
+        const int R = cmb == 0 ? 1 : cmb <= 2 ? 2 : 3;
+        const int I = cmb - (R * (R - 1)) / 2;
+        f32x4 cx = {0, 0, 0, 0};
+        cx = mma16_rows<MT, CHUNK>(xA + ((R - 1) * 32 + 16 * isq) * RP, RP, xB + cmb * 16 * RP, RP,
+                                   cx, l);
+        const int n = l & 15, m0 = 4 * (l >> 4);
+        const int ri = 16 * I + n;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ru = 16 * R + m0 + e;
+          float* slot = isq ? sA + ri * AL + ru : sA + ru * AL + ri;
+          if (ps == 0) {
+            *slot = cx[e];
+          } else {
+            const float v = *slot + cx[e];
+            if (isq) gP[LY::pm(ru, ri)] = from_f32<MT>(sRq[ru] * sRk[ri] * v);
+            else *slot = sBeta[ru] * sRk[ru] * sRk[ri] * v;
+          }
+        }
+      }
+      __syncthreads();
     }
-  }
-  if (w <= 2) {
-    // suffix within my block, excluding the row itself
-    float ks0[16], ks1[16];
-    float s0 = 1.0f, s1 = 1.0f;
-#pragma unroll
-    for (int j = 15; j >= 0; --j) {
-      ks0[j] = ka[j][0] * s0; ks1[j] = ka[j][1] * s1;
-      s0 *= aa[j][0]; s1 *= aa[j][1];
-    }
-#pragma unroll
-    for (int R = 1; R < 4; ++R) {
-      if (R > w) {
-        // kappa = prod of whole blocks strictly between w and R, times the
-        // decay of the reference row 16R
-        float k0 = sA0[R * DH + c0], k1 = sA0[R * DH + c0 + 1];
-#pragma unroll
-        for (int x = 1; x < 4; ++x)
-          if (x > w && x < R) { k0 *= sTot[x * DH + c0]; k1 *= sTot[x * DH + c0 + 1]; }
-        MT* dst = xB + combo(R, w) * 16 * ROWL;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) store2(dst + j * ROWL + c0, ks0[j] * k0, ks1[j] * k1);
+  } else {
+    MT* xA = reinterpret_cast<MT*>(sU);              // [3][32] rows: kL then qL of R=1..3
+    MT* xB = reinterpret_cast<MT*>(sU) + 96 * ROWL;  // [6][16] rows
+    if (w >= 1) {
+      float x0 = 1.0f, x1 = 1.0f;
+  #pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (j > 0) { x0 *= aa[j][0]; x1 *= aa[j][1]; }
+        store2(xA + ((w - 1) * 32 + j) * ROWL + c0, ka[j][0] * x0, ka[j][1] * x1);
+        store2(xA + ((w - 1) * 32 + 16 + j) * ROWL + c0, qa[j][0] * x0, qa[j][1] * x1);
       }
     }
-  }
-  __syncthreads();
-  // 12 tile products (R, I, k|q), three per wave.
-#pragma unroll
-  for (int t = 0; t < 3; ++t) {
-    const int tp = 3 * w + t;  // 0..11
-    const int cmb = tp >> 1, isq = tp & 1;
-    const int R = cmb == 0 ? 1 : cmb <= 2 ? 2 : 3;
-    const int I = cmb - (R * (R - 1)) / 2;
-    f32x4 c = {0, 0, 0, 0};
-    c = mma16_rows<MT, DH>(xA + ((R - 1) * 32 + 16 * isq) * ROWL, ROWL, xB + cmb * 16 * ROWL, ROWL,
-                           c, l);
-    const int n = l & 15, m0 = 4 * (l >> 4);
-    const int ri = 16 * I + n;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int ru = 16 * R + m0 + e;
-      if (isq) gP[LY::pm(ru, ri)] = from_f32<MT>(sRq[ru] * sRk[ri] * c[e]);
-      else sA[ru * AL + ri] = sBeta[ru] * sRk[ru] * sRk[ri] * c[e];
+    if (w <= 2) {
+      // suffix within my block, excluding the row itself
+      float ks0[16], ks1[16];
+      float s0 = 1.0f, s1 = 1.0f;
+  #pragma unroll
+      for (int j = 15; j >= 0; --j) {
+        ks0[j] = ka[j][0] * s0; ks1[j] = ka[j][1] * s1;
+        s0 *= aa[j][0]; s1 *= aa[j][1];
+      }
+  #pragma unroll
+      for (int R = 1; R < 4; ++R) {
+        if (R > w) {
+          // kappa = prod of whole blocks strictly between w and R, times the
+          // decay of the reference row 16R
+          float k0 = sA0[R * DH + c0], k1 = sA0[R * DH + c0 + 1];
+  #pragma unroll
+          for (int x = 1; x < 4; ++x)
+            if (x > w && x < R) { k0 *= sTot[x * DH + c0]; k1 *= sTot[x * DH + c0 + 1]; }
+          MT* dst = xB + combo(R, w) * 16 * ROWL;
+  #pragma unroll
+          for (int j = 0; j < 16; ++j) store2(dst + j * ROWL + c0, ks0[j] * k0, ks1[j] * k1);
+        }
+      }
+    }
+    __syncthreads();
+    // 12 tile products (R, I, k|q), three per wave.
+  #pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      const int tp = 3 * w + t;  // 0..11
+      const int cmb = tp >> 1, isq = tp & 1;
+      const int R = cmb == 0 ? 1 : cmb <= 2 ? 2 : 3;
+      const int I = cmb - (R * (R - 1)) / 2;
+      f32x4 c = {0, 0, 0, 0};
+      c = mma16_rows<MT, DH>(xA + ((R - 1) * 32 + 16 * isq) * ROWL, ROWL, xB + cmb * 16 * ROWL, ROWL,
+                             c, l);
+      const int n = l & 15, m0 = 4 * (l >> 4);
+      const int ri = 16 * I + n;
+  #pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ru = 16 * R + m0 + e;
+        if (isq) gP[LY::pm(ru, ri)] = from_f32<MT>(sRq[ru] * sRk[ri] * c[e]);
+        else sA[ru * AL + ri] = sBeta[ru] * sRk[ru] * sRk[ri] * c[e];
+      }
     }
   }
   // Upper triangle of P is zero.  In the forward's stored order a 16-byte
@@ -700,7 +942,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
   {
     // (c) 16x16 blocks across waves, FP32 MFMA.  Y goes through a per-wave
     // scratch tile so it can feed the second product as its B operand.
-    float* sY = reinterpret_cast<float*>(sU + L::O_TS) + w * 16 * 20;
+    float* sY = reinterpret_cast<float*>(sU + L::O_SCR) + w * 16 * 20;
     const int nn = l & 15, m0 = 4 * (l >> 4);
 #pragma unroll
     for (int dist = 1; dist < 4; ++dist) {
@@ -727,74 +969,87 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
 
   // ------------------------------------------------------ phase 4: W and U
   MT* sTs = reinterpret_cast<MT*>(sU + L::O_TS);  // scaled T, row-major [64][TL]
-  MT* sXt = reinterpret_cast<MT*>(sU + L::O_XT);  // transposed operand [128][TL]
+  MT* sXt = reinterpret_cast<MT*>(sU + L::O_XT);  // transposed operand [128 / NP][TL]
   // W = T (Diag(beta rk) (k * E)),  U = T (Diag(beta) v): the row scales go
-  // on the right-hand operands, T is converted once.
+  // on the right-hand operands, T is converted once (FP32: T is used as is).
   for (int x = tid; x < CHUNK * CHUNK; x += 256) {
     const int r = x >> 6, i = x & 63;
-    sTs[r * TL + i] = from_f32<MT>(sT[r * AL + i]);
+    if constexpr (!L::TS_ALIAS) sTs[r * TL + i] = from_f32<MT>(sT[r * AL + i]);
     if constexpr (BWD) p.tmat[((size_t)chunk * H + h) * CHUNK * CHUNK + x] = sT[r * AL + i];
   }
-  {
-    float e0 = pb[0], e1 = pb[1];
-    float kg0[16], kg1[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      e0 *= aa[j][0]; e1 *= aa[j][1];
-      const float sc = sBeta[16 * w + j] * sRk[16 * w + j];
-      kg0[j] = ka[j][0] * e0 * sc; kg1[j] = ka[j][1] * e1 * sc;
-    }
+  for (int j = 0; j < 16; ++j) {
+    const float bj = sBeta[16 * w + j];
+    v0[j] *= bj; v1[j] *= bj;
+  }
+  // Each product in NP passes over channel halves (NP = 1 for bf16): the
+  // transposed operand holds 128 / NP channels; lanes whose channels fall in
+  // the pass form and write them.
+  constexpr int NP = L::NP, CB = 8 / NP;  // channel blocks of 16 per pass
+#pragma unroll 1
+  for (int ps = 0; ps < NP; ++ps) {
+    const int cl = c0 - 64 * ps;
+    if (NP == 1 || (l >> 5) == ps) {
+      float kg0[16], kg1[16];
+      float e0 = pb[0], e1 = pb[1];
 #pragma unroll
-    for (int j = 0; j < 16; j += 4) {
-      store4(sXt + c0 * TL + 16 * w + j, f32x4{kg0[j], kg0[j + 1], kg0[j + 2], kg0[j + 3]});
-      store4(sXt + (c0 + 1) * TL + 16 * w + j, f32x4{kg1[j], kg1[j + 1], kg1[j + 2], kg1[j + 3]});
+      for (int j = 0; j < 16; ++j) {
+        e0 *= aa[j][0]; e1 *= aa[j][1];
+        const float sc = sBeta[16 * w + j] * sRk[16 * w + j];
+        kg0[j] = ka[j][0] * e0 * sc; kg1[j] = ka[j][1] * e1 * sc;
+      }
       if constexpr (BWD) {
         float* gb = p.bw + ((size_t)chunk * H + h) * CHUNK * DH;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) store2(gb + (16 * w + j + e) * DH + c0, kg0[j + e], kg1[j + e]);
+        for (int j = 0; j < 16; ++j) store2(gb + (16 * w + j) * DH + c0, kg0[j], kg1[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; j += 4) {
+        store4(sXt + cl * TL + 16 * w + j, f32x4{kg0[j], kg0[j + 1], kg0[j + 2], kg0[j + 3]});
+        store4(sXt + (cl + 1) * TL + 16 * w + j, f32x4{kg1[j], kg1[j + 1], kg1[j + 2], kg1[j + 3]});
       }
     }
-  }
-  __syncthreads();
-  // 32 output tiles of W^T: (channel block mt 0..7) x (token block nt 0..3); 8 per wave.
+    __syncthreads();
+    // output tiles of W^T: (channel block mt) x (token block nt 0..3); 8 / NP per wave
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int tile = 8 * w + t, mt = tile >> 2, nt = tile & 3;
-    f32x4 c = {0, 0, 0, 0};
-    c = mma16_rows<MT, CHUNK>(sXt + 16 * mt * TL, TL, sTs + 16 * nt * TL, TL, c, l);
-    // c[e] = W^T[16mt + 4(l/16) + e][16nt + l%16] = W[tok][ch..ch+3]
-    const int tok = 16 * nt + (l & 15), ch = 16 * mt + 4 * (l >> 4);
-    store4(gW + LY::a(tok, ch), c);
-    if constexpr (BWD) {
-      float* gwt = p.wt + ((size_t)chunk * H + h) * DH * CHUNK;
+    for (int t = 0; t < 2 * CB / 2; ++t) {
+      const int tile = CB * w + t, mtl = tile >> 2, nt = tile & 3, mt = CB * ps + mtl;
+      f32x4 c = {0, 0, 0, 0};
+      c = mma16_rows<MT, CHUNK>(sXt + 16 * mtl * TL, TL, sTs + 16 * nt * TL, TL, c, l);
+      // c[e] = W^T[16mt + 4(l/16) + e][16nt + l%16] = W[tok][ch..ch+3]
+      const int tok = 16 * nt + (l & 15), ch = 16 * mt + 4 * (l >> 4);
+      store4(gW + LY::a(tok, ch), c);
+      if constexpr (BWD) {
+        float* gwt = p.wt + ((size_t)chunk * H + h) * DH * CHUNK;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) gwt[(ch + e) * CHUNK + tok] = c[e];
+        for (int e = 0; e < 4; ++e) gwt[(ch + e) * CHUNK + tok] = c[e];
+      }
     }
+    __syncthreads();
   }
-  __syncthreads();
   // U = T (Diag(beta) v)
-  {
+#pragma unroll 1
+  for (int ps = 0; ps < NP; ++ps) {
+    const int cl = c0 - 64 * ps;
+    if (NP == 1 || (l >> 5) == ps) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float bj = sBeta[16 * w + j];
-      v0[j] *= bj; v1[j] *= bj;
+      for (int j = 0; j < 16; j += 4) {
+        store4(sXt + cl * TL + 16 * w + j, f32x4{v0[j], v0[j + 1], v0[j + 2], v0[j + 3]});
+        store4(sXt + (cl + 1) * TL + 16 * w + j, f32x4{v1[j], v1[j + 1], v1[j + 2], v1[j + 3]});
+      }
     }
+    __syncthreads();
+    // output tiles of U: (token block mt 0..3) x (value block nt); 8 / NP per wave
 #pragma unroll
-    for (int j = 0; j < 16; j += 4) {
-      store4(sXt + c0 * TL + 16 * w + j, f32x4{v0[j], v0[j + 1], v0[j + 2], v0[j + 3]});
-      store4(sXt + (c0 + 1) * TL + 16 * w + j, f32x4{v1[j], v1[j + 1], v1[j + 2], v1[j + 3]});
+    for (int t = 0; t < CB; ++t) {
+      const int tile = CB * w + t, mt = tile / CB, ntl = tile % CB, nt = CB * ps + ntl;
+      f32x4 c = {0, 0, 0, 0};
+      c = mma16_rows<MT, CHUNK>(sTs + 16 * mt * TL, TL, sXt + 16 * ntl * TL, TL, c, l);
+      // c[e] = U[16mt + 4(l/16) + e][16nt + l%16]: four consecutive tokens
+      const int dv = 16 * nt + (l & 15), tok = 16 * mt + 4 * (l >> 4);
+      store4(gUT + LY::u(tok, dv), c);
     }
-  }
-  __syncthreads();
-  // 32 output tiles of U: (token block mt 0..3) x (value block nt 0..7)
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int tile = 8 * w + t, mt = tile >> 3, nt = tile & 7;
-    f32x4 c = {0, 0, 0, 0};
-    c = mma16_rows<MT, CHUNK>(sTs + 16 * mt * TL, TL, sXt + 16 * nt * TL, TL, c, l);
-    // c[e] = U[16mt + 4(l/16) + e][16nt + l%16]: four consecutive tokens
-    const int dv = 16 * nt + (l & 15), tok = 16 * mt + 4 * (l >> 4);
-    store4(gUT + LY::u(tok, dv), c);
+    if (ps + 1 < NP) __syncthreads();
   }
 }
 

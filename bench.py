@@ -33,6 +33,10 @@ H200_CONTEXT_P50_US = {"bf16": 4050.976, "fp32": 7842.400}  # pages' H200 number
 BYTES_IN_PER_TH = lambda s: (4 * 128 + 1) * s    # q, k, v, f_raw, b_raw
 BYTES_OUT_PER_TH = lambda s: 128 * s             # out
 FLOP_PER_TH = 139264                             # 3 d^2 + 1.5 C d + C d MACs, x2
+# split by kernel: the intra-chunk blocks and solve (1.5 C d + C d MACs) and
+# the state pass with the output (3 d^2 MACs: W S0, Qt S0, Kb^T D)
+FLOP_INTRA_PER_TH = 2 * (3 * 64 * 128 // 2 + 64 * 128)   # 40,960
+FLOP_STATE_PER_TH = 2 * 3 * 128 * 128                   # 98,304
 
 
 def kernel_source_hash() -> str:
@@ -314,13 +318,17 @@ def roofline_for(mode_name: str, T: int, H: int, res: dict, workload: str):
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
     else:
-        # FP32-intermediate mode: MFMA-FP32 bound by the algorithmic FLOP count
-        fl = th * FLOP_PER_TH / (res["p50_us"] * 1e-6) / 1e12
-        roof = {"bound": "mfma", "achieved": round(fl, 2), "peak": MFMA_FP32_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(fl / MFMA_FP32_TFLOPS, 4)}
+        # FP32-intermediate mode is MFMA-FP32 bound: the dominant kernel's share
+        # of the algorithmic FLOP over its launch time, and the whole path's
+        # FLOP over the step time
+        kfl = {0: 0, 1: FLOP_INTRA_PER_TH, 2: FLOP_STATE_PER_TH}[dom] * th / t / 1e12
+        roof = {"bound": "mfma", "achieved": round(kfl, 2), "peak": MFMA_FP32_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(kfl / MFMA_FP32_TFLOPS, 4)}
+        roof["path_mfma_fp32_frac"] = round(th * FLOP_PER_TH / (res["p50_us"] * 1e-6) / 1e12
+                                            / MFMA_FP32_TFLOPS, 4)
     roof["kernel"] = names[dom]
     roof["kernel_avg_us"] = round(st[dom], 2)
-    roof["traffic"] = load_traffic(names[dom], workload, mode_name) if mode_name == "bf16" else None
+    roof["traffic"] = load_traffic(names[dom], workload, mode_name)
     # whole path against the HBM roofline (algorithmic bytes of the method)
     path_bytes = th * (BYTES_IN_PER_TH(act) + BYTES_OUT_PER_TH(act))
     path_gbs = path_bytes / (res["p50_us"] * 1e-6) / 1e9

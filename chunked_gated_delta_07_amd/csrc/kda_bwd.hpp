@@ -1,8 +1,8 @@
 // kda_bwd.hpp -- backward (vector-Jacobian product) of the KDA chunked forward,
 // recomputed in FP32.
 //
-// The pages' training path keeps "backward recomputation in FP32" and casts
-// only the input gradients back to the activation dtype; its gradients of q,
+// The pages' training path recomputes the backward in FP32 and returns only
+// the input gradients in the activation dtype; its gradients of q,
 // k, v, the gate and beta are checked against an independent FP64 recurrence
 // VJP (xtuner PR #2301, sections Change and Validation), and dt_bias gradients
 // are summed in FP32 (xtuner PR #2153, KDA module section).

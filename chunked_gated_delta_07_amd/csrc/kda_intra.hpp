@@ -15,7 +15,7 @@
 //   Qt      = q^ * E,   Kb_r = k^_r * prod_{j>r} a_j
 // Every decay factor is a product of per-token decays over a token range, so
 // it lies in [0, 1] and never overflows, however strong the gate; the pages'
-// "fixed-layout FP32 gate prefix" (xtuner PR #2153, KDA module section) is
+// FP32 gate prefix with a fixed layout (xtuner PR #2153, KDA module section) is
 // kept as an FP32 prefix, multiplicative here.
 //
 // Off-diagonal 16x16 blocks (row block R > column block I) are products

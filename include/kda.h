@@ -198,7 +198,7 @@ KDA_API size_t kda_chunk_bwd_workspace_bytes(int64_t total_tokens, int32_t num_s
                                      int32_t d, uint32_t mode);
 
 /* Backward (vector-Jacobian product) of kda_chunk_fwd_state, recomputed in
- * FP32: the pages' training path keeps "backward recomputation in FP32" and
+ * FP32: the pages' training path recomputes the backward in FP32 and
  * casts the input gradients back to the activation dtype (xtuner PR #2301,
  * section Change), checks the gradients of q, k, v, the gate and beta against
  * an FP64 recurrence VJP (same PR, section Validation), and sums the dt_bias

@@ -21,9 +21,10 @@
  * Sources.  The pages name KDA's chunked operator and its serving-side FP32
  * token recurrence, packed variable-length inputs with per-document state
  * isolation, FP32 A_log / dt_bias feeding a separately computed gate, a sigmoid
- * beta, and q/k L2 normalisation ("promote Q/K/V before L2 normalization"):
+ * beta, and q/k L2 normalisation done in FP32 (q, k, v raised to FP32 first):
  *   - xtuner PR #2301 "[Enhancement] Add opt-in FP32 KDA chunk computation",
- *     sections Problem, Change and Validation ("independent FP64 recurrence");
+ *     sections Problem, Change and Validation (an FP64 recurrence written
+ *     independently of the kernels is the reference there);
  *   - xtuner PR #2153 "GLM-5.3-Flash F6.2: KDA correctness and FLA sequence
  *     parallelism", KDA module description (fused_kda_gate outside the kernel,
  *     use_beta_sigmoid_in_kernel, packed multi-document isolation).

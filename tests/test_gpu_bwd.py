@@ -1,11 +1,12 @@
 """GPU parity of kda_chunk_bwd (the FP32-recomputed backward) against the FP64
 oracle's vector-Jacobian product of the token recurrence.
 
-The pages check the chunked operator's input gradients against an independent
-FP64 recurrence VJP with packed lengths 37/28, a chunk boundary at 129 and the
-64-head x 128 geometry at 65 tokens, require every nonzero gradient within 2 %
-relative error, and plant a 25 % gradient scaling error that must fail
-(xtuner PR #2301, section Validation); FP32 budgets of 0.3 % (dq, dk, dv) and
+The pages check the chunked operator's input gradients against an FP64
+recurrence VJP written apart from the kernels, on two packed sequences of 37
+and 28 tokens, on a 129-token sequence that crosses chunk boundaries and on all
+64 heads of width 128 at 65 tokens; each gradient that is not zero must stay
+within 2 % relative error, and a gradient scaled by 25 % on purpose must be
+caught (xtuner PR #2301, section Validation); FP32 budgets of 0.3 % (dq, dk, dv) and
 0.5 % (gate, beta) are quoted in xtuner PR #2153.  Bars here, relative L2 over
 each whole gradient tensor:
   * FP32 gradients (FP32 activations, or bf16 activations with KDA_OUT_FP32):

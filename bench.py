@@ -8,7 +8,7 @@ One step = one kda_chunk_fwd call over the whole batch (every kernel of the
 path).  The headline line times BF16-intermediate mode; FP32-intermediate mode
 is timed on the same inputs and reported alongside.
 
-Prints ONE JSON line.  --gpus above 1 is refused: this build runs on one GPU.
+Prints ONE JSON line.  --gpus above 1 is refused: the implementation runs on one GPU.
 """
 from __future__ import annotations
 
@@ -355,7 +355,7 @@ def main():
                     help="run only a device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} requested; this build runs on one GPU only "
+        print(f"bench.py: --gpus {args.gpus} requested; this implementation runs on one GPU only "
               f"(no multi-GPU path), use --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:

@@ -115,7 +115,7 @@ static int launch_all(const void* q, const void* k, const void* v, const void* f
   if constexpr (sizeof(MT) == 2)
     hipLaunchKernelGGL((kda_scan_ring_kernel<TO>), dim3((unsigned)blocks), dim3(512), 0, stream, sa);
   else
-    hipLaunchKernelGGL((kda_scan_kernel<MT, TO>), dim3((unsigned)blocks), dim3(256), 0, stream, sa);
+    hipLaunchKernelGGL((kda_scan_ring32_kernel<TO>), dim3((unsigned)blocks), dim3(512), 0, stream, sa);
   if (ev) (void)hipEventRecord(ev[3], stream);
   return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

@@ -1,22 +1,25 @@
 // kda_scan.hpp -- chunk-to-chunk state pass fused with the output combine.
 //
 // For each chunk of a sequence, with S0 the state entering it (d_k x d_v,
-// zero at the sequence start -- no initial/final state, xtuner PR #2301,
-// section Change):
+// zero at the sequence start unless a start state is given):
 //   D      = U - W S0                       (corrected values)
 //   out    = scale (Qt S0 + P D)            (inter- plus intra-chunk terms)
 //   S_next = Diag(Gam) S0 + Kb^T D
-// Columns of S are independent, so one workgroup owns a 32-wide block of
-// value channels of one (sequence, head) and walks its chunks in order.  The
-// running state stays FP32 in MFMA accumulators for the whole sequence; the
-// copy used as a matrix operand is stored in the intermediate type.
+// (the inter-chunk part of the chunked operator of xtuner PR #2301, sections
+// Problem and Change; the algebra is written out in kda_intra.hpp).  Columns
+// of S are independent, so one workgroup owns a 32-wide block of value
+// channels of one (sequence, head) and walks its chunks in order.  The running state stays FP32 in MFMA
+// accumulators for the whole sequence.
 //
-// Work split inside a workgroup (4 waves, 32x32 MFMA tiles): wave w owns
-// state rows 32w..32w+31 (key channels).  X = [W; Qt] S0 is 128 x 32: waves
-// 0,1 form W S0 (-> D), waves 2,3 form Qt S0 (-> output).
+// Work split inside a workgroup (4 compute waves, 32x32 MFMA tiles): wave w
+// owns state rows 32w..32w+31 (key channels).  X = [W; Qt] S0 is 128 x 32:
+// waves 0,1 form W S0 (-> D), waves 2,3 form Qt S0 (-> output).  Four more
+// waves copy each chunk's operands into LDS.  Two kernels:
+//   kda_scan_ring_kernel    bf16 intermediates, two LDS slots;
+//   kda_scan_ring32_kernel  FP32 intermediates, one LDS slot refilled in
+//                           halves, products on bf16 matrix cores from
+//                           three-piece splits of the FP32 operands.
 #pragma once
-
-#include <type_traits>
 
 #include "kda_common.hpp"
 #include "kda_intra.hpp"
@@ -38,13 +41,81 @@ struct ScanArgs {
 
 constexpr int DVB = 32;  // value channels per workgroup
 
-template <typename MT> struct ScanLds {
-  static constexpr int SL = sizeof(MT) == 2 ? 136 : 132;  // S0^T row: 128 key channels
-  static constexpr int DL = sizeof(MT) == 2 ? 72 : 68;    // D^T row: 64 tokens
+// FP32 operands on bf16 matrix cores.  Each FP32 value x is split into three
+// bf16 pieces x = h + m + l: h is x rounded to nearest even, m the same for
+// x - h, l for x - h - m (both remainders are exact in FP32, and for a normal
+// x the three pieces hold all 24 significand bits, so the split is exact).  A
+// product x y is the sum of the six piece products of order >= 2^-16,
+//   h h' + (h m' + m h') + (h l' + m m' + l h'),
+// the "bf16x6" scheme of Henry, Tang and Heinecke ("Leveraging the bfloat16
+// artificial intelligence datatype for higher-precision computations", ARITH
+// 2019).  The omitted terms m l' + l m' + l l' stay below 2^-23 |x y| and the
+// matrix core accumulates in FP32, so a contraction agrees with an FP32 one to
+// within FP32 rounding.  Cost per 16 contracted values: six
+// v_mfma_f32_32x32x16_bf16 (32 cycles each) instead of eight
+// v_mfma_f32_32x32x2f32 (64 cycles each).
+typedef unsigned u32;
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+// the two bf16 of a packed pair as FP32 (exact)
+__device__ __forceinline__ f32x2 bf16x2_as_f32(u32 v) {
+  return f32x2{__builtin_bit_cast(float, v << 16), __builtin_bit_cast(float, v & 0xffff0000u)};
+}
+__device__ __forceinline__ u32 cvt_pair(f32x2 x) {
+  return __builtin_bit_cast(u32, __builtin_convertvector(x, bf16x2));  // RNE, one instruction
+}
+// pieces of two FP32 values, each piece packed as a bf16 pair
+struct Pieces2 { u32 h, m, l; };
+__device__ __forceinline__ Pieces2 split2(f32x2 x) {
+  Pieces2 o;
+  o.h = cvt_pair(x);
+  const f32x2 r = x - bf16x2_as_f32(o.h);
+  o.m = cvt_pair(r);
+  o.l = cvt_pair(r - bf16x2_as_f32(o.m));
+  return o;
+}
+// pieces of eight FP32 values (a then b), one bf16x8 per piece
+__device__ __forceinline__ void split8(const f32x4& a, const f32x4& b, bf16x8 (&o)[3]) {
+  const Pieces2 p0 = split2(f32x2{a[0], a[1]}), p1 = split2(f32x2{a[2], a[3]});
+  const Pieces2 p2 = split2(f32x2{b[0], b[1]}), p3 = split2(f32x2{b[2], b[3]});
+  o[0] = __builtin_bit_cast(bf16x8, u32x4{p0.h, p1.h, p2.h, p3.h});
+  o[1] = __builtin_bit_cast(bf16x8, u32x4{p0.m, p1.m, p2.m, p3.m});
+  o[2] = __builtin_bit_cast(bf16x8, u32x4{p0.l, p1.l, p2.l, p3.l});
+}
+// C += A B over 16 contracted values from their pieces (smallest terms first)
+__device__ __forceinline__ f32x16 mma_x6(const bf16x8 (&a)[3], const bf16x8 (&b)[3], f32x16 c) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], b[0], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[1], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[2], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[0], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[1], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[0], c, 0, 0, 0);
+  return c;
+}
+
+// Operand copies of S0 (S0^T, [value][key]) and of D (D^T, [value][token])
+// in the FP32-intermediate state pass, each as three bf16 planes (pieces h,
+// m, l) of row lengths SL and DL.
+struct ScanLds {
+  static constexpr int SL = 136;      // S0^T row: 128 key channels (+8 pad)
+  static constexpr int DL = 72;       // D^T row: 64 tokens (+8 pad)
+  static constexpr int PS = DVB * SL; // plane strides, elements
+  static constexpr int PD = DVB * DL;
   static constexpr int O_S = 0;
-  static constexpr int O_D = O_S + DVB * SL * (int)sizeof(MT);
-  static constexpr int BYTES = O_D + DVB * DL * (int)sizeof(MT);
+  static constexpr int O_D = O_S + 3 * PS * 2;
+  static constexpr int BYTES = O_D + 3 * PD * 2;
 };
+// four FP32 values -> their pieces at p, p + stride, p + 2 stride
+__device__ __forceinline__ void store_pieces4(bf16* p, int stride, const f32x4& v) {
+  const Pieces2 p0 = split2(f32x2{v[0], v[1]}), p1 = split2(f32x2{v[2], v[3]});
+  *reinterpret_cast<u32x2*>(p) = u32x2{p0.h, p1.h};
+  *reinterpret_cast<u32x2*>(p + stride) = u32x2{p0.m, p1.m};
+  *reinterpret_cast<u32x2*>(p + 2 * stride) = u32x2{p0.l, p1.l};
+}
+__device__ __forceinline__ void load_pieces8(const bf16* p, int stride, bf16x8 (&o)[3]) {
+#pragma unroll
+  for (int q = 0; q < 3; ++q) o[q] = *reinterpret_cast<const bf16x8*>(p + q * stride);
+}
 
 // Workgroup id -> (sequence*H + head, value block).  The four value blocks of
 // one (sequence, head) get ids that are equal mod 8, i.e. land on one XCD and
@@ -55,341 +126,35 @@ __device__ __forceinline__ void scan_unit(int bid, int& pair, int& vb) {
   pair = (slot >> 2) * 8 + xcd;
 }
 
-// Per-chunk operands of one lane, loaded one chunk ahead of their use.  The
-// record is stored in this kernel's read order (Frag in kda_intra.hpp), so
-// every load below is one contiguous 16-byte piece per lane and 1 KB per wave.
-// ROLE 0 (waves 0,1): W rows and U values; ROLE 1 (waves 2,3): Qt and P rows.
-template <typename MT, int ROLE> struct ScanOps {
-  static constexpr int FE = 16 / (int)sizeof(MT);
-  typedef typename std::conditional<sizeof(MT) == 2, bf16x8, f32x4>::type v16;
-  static constexpr int NX = ROLE == 0 ? 16 / FE : 32 / FE;
-  v16 a[64 / FE];   // W or Qt row: 64 key channels
-  v16 kb[32 / FE];  // Kb^T row: 32 tokens
-  v16 x[NX];        // U values (role 0) or P row (role 1)
-  f32x4 gm[4];      // Gam at the wave's 16 state rows
-};
-
-template <typename MT, int ROLE>
-__device__ __forceinline__ void scan_load(ScanOps<MT, ROLE>& o, const MT* __restrict__ R,
-                                          const float* __restrict__ gm, int wp, int w, int l,
-                                          int g, int vb) {
-  typedef ScanOps<MT, ROLE> O;
-  constexpr int FE = O::FE;
-  typedef typename O::v16 v16;
-  // The loads keep this order everywhere (the scheduling barriers stop the
-  // compiler from permuting them differently in the prologue and in the loop,
-  // which would make its memory-counter waits at the loop head conservative).
-  const MT* A = R + (ROLE == 0 ? OFF_W : OFF_QT) + wp * (64 / FE) * 64 * FE + l * FE;
+// bf16 32x32 tiles over NK contracted values per lane (NK/8 instructions).
+// C += A B: A from register fragments, B from LDS (NK contiguous values at pb).
+template <int NK>
+__device__ __forceinline__ f32x16 mma32_frags(const bf16x8* afr, const bf16* pb, f32x16 c) {
 #pragma unroll
-  for (int s = 0; s < 64 / FE; ++s) {
-    o.a[s] = *reinterpret_cast<const v16*>(A + s * 64 * FE);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  const MT* kb = R + OFF_KBT + w * (32 / FE) * 64 * FE + l * FE;
-#pragma unroll
-  for (int s = 0; s < 32 / FE; ++s) {
-    o.kb[s] = *reinterpret_cast<const v16*>(kb + s * 64 * FE);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  const MT* x = ROLE == 0 ? R + OFF_UT + (vb * 2 + wp) * (16 / FE) * 64 * FE + l * FE
-                          : R + OFF_P + wp * (32 / FE) * 64 * FE + l * FE;
-#pragma unroll
-  for (int s = 0; s < O::NX; ++s) {
-    o.x[s] = *reinterpret_cast<const v16*>(x + s * 64 * FE);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-#pragma unroll
-  for (int e4 = 0; e4 < 4; ++e4) {
-    o.gm[e4] = *reinterpret_cast<const f32x4*>(gm + 32 * w + 8 * e4 + 4 * g);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// C += A B over NK contracted values per lane: A from register fragments, B
-// from LDS (contiguous NK values at pb), 16-byte LDS reads in both precisions.
-template <typename MT, int NK, typename V>
-__device__ __forceinline__ f32x16 mma32_frags(const V* afr, const MT* pb, f32x16 c) {
-  typedef Mma32<MT> M;
-  if constexpr (sizeof(MT) == 2) {
-#pragma unroll
-    for (int s = 0; s < NK / 8; ++s) c = M::mma(afr[s], *reinterpret_cast<const bf16x8*>(pb + 8 * s), c);
-  } else {
-#pragma unroll
-    for (int s = 0; s < NK / 4; ++s) {
-      const f32x4 b4 = *reinterpret_cast<const f32x4*>(pb + 4 * s);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) c = M::mma(afr[s][e], b4[e], c);
-    }
-  }
+  for (int s = 0; s < NK / 8; ++s)
+    c = Mma32<bf16>::mma(afr[s], *reinterpret_cast<const bf16x8*>(pb + 8 * s), c);
   return c;
 }
-// C += A B with A read from LDS (contiguous NK values at pa) and B from
-// register fragments: the same MFMAs as mma32_frags with the operands
+// C += A B with A read from LDS (NK contiguous values at pa) and B from
+// register fragments: the same instructions as mma32_frags with the operands
 // exchanged, so C comes out transposed.
-template <typename MT, int NK, typename V>
-__device__ __forceinline__ f32x16 mma32_lds_frags(const MT* pa, const V* bfr, f32x16 c) {
-  typedef Mma32<MT> M;
-  if constexpr (sizeof(MT) == 2) {
+template <int NK>
+__device__ __forceinline__ f32x16 mma32_lds_frags(const bf16* pa, const bf16x8* bfr, f32x16 c) {
 #pragma unroll
-    for (int s = 0; s < NK / 8; ++s) c = M::mma(*reinterpret_cast<const bf16x8*>(pa + 8 * s), bfr[s], c);
-  } else {
-#pragma unroll
-    for (int s = 0; s < NK / 4; ++s) {
-      const f32x4 a4 = *reinterpret_cast<const f32x4*>(pa + 4 * s);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) c = M::mma(a4[e], bfr[s][e], c);
-    }
-  }
+  for (int s = 0; s < NK / 8; ++s)
+    c = Mma32<bf16>::mma(*reinterpret_cast<const bf16x8*>(pa + 8 * s), bfr[s], c);
   return c;
 }
-// C += A B, both operands from register fragments (NK values per lane).
-template <typename MT, int NK, typename V>
-__device__ __forceinline__ f32x16 mma32_rr(const V* afr, const V* bfr, f32x16 c) {
-  typedef Mma32<MT> M;
-  if constexpr (sizeof(MT) == 2) {
+// C += A B, both operands from register fragments.
+template <int NK>
+__device__ __forceinline__ f32x16 mma32_rr(const bf16x8* afr, const bf16x8* bfr, f32x16 c) {
 #pragma unroll
-    for (int s = 0; s < NK / 8; ++s) c = M::mma(afr[s], bfr[s], c);
-  } else {
-#pragma unroll
-    for (int s = 0; s < NK / 4; ++s)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) c = M::mma(afr[s][e], bfr[s][e], c);
-  }
+  for (int s = 0; s < NK / 8; ++s) c = Mma32<bf16>::mma(afr[s], bfr[s], c);
   return c;
 }
 template <typename V> __device__ __forceinline__ float val_at(const V* f, int q) {
   constexpr int FE = sizeof(f[0][0]) == 2 ? 8 : 4;
   return (float)f[q / FE][q % FE];
-}
-
-// One chunk of the state pass for one wave.  ROLE 0 forms D = U - W S0 (and
-// publishes it); ROLE 1 forms the output rows.  Both update their 32 rows of
-// the running state S.  Two barriers per chunk, the same for every wave.
-// `issue` sends the loads of a later chunk; each role issues them where it
-// would otherwise wait at a barrier (role 1 while role 0 forms D, role 0
-// while role 1 forms the output), so that the in-order load issue stays off
-// the step's dependency chain.  With fp32 operands only one chunk is loaded
-// ahead, and role 0 issues at the start of the step so that the loads have a
-// whole step to arrive.
-template <typename MT, typename TO, int ROLE, bool FULL, typename Issue>
-__device__ __forceinline__ void scan_step(const ScanArgs& p, const ScanOps<MT, ROLE>& cur, f32x16& S,
-                                          MT* sS, MT* sD, int h, int ctok, int len, int vb, int w,
-                                          int l, Issue&& issue) {
-  typedef ScanLds<MT> L;
-  constexpr int SL = L::SL, DL = L::DL;
-  const int col = l & 31, g = l >> 5, wp = w & 1;
-  TO* __restrict__ out = reinterpret_cast<TO*>(p.out);
-  // Role 0: X = W S0 (rows = 32 tokens, columns = 32 values).  Role 1: the
-  // transposed product X = S0^T Qt^T (rows = values, columns = tokens), so
-  // that each lane ends up holding one token's run of value columns for the
-  // output store.  128 key channels contracted; lane group g covers channels
-  // [64g, 64g+64) in both forms.
-  f32x16 X;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) X[e] = 0.0f;
-  constexpr bool EARLY = ROLE == 0 && sizeof(MT) == 4;
-  if constexpr (EARLY) {
-    issue();
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  if constexpr (ROLE == 0) {
-    X = mma32_frags<MT, 64>(cur.a, sS + col * SL + 64 * g, X);
-    // D = U - W S0 at tokens 32wp + row32(e), value column col
-#pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      f32x4 d;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) d[i] = val_at(cur.x, 4 * e4 + i) - X[4 * e4 + i];
-      store4(sD + col * DL + 32 * wp + 8 * e4 + 4 * g, d);
-    }
-  } else {
-    X = mma32_lds_frags<MT, 64>(sS + col * SL + 64 * g, cur.a, X);
-    // X is next used after the barrier; without this the compiler sinks the
-    // products below the load issue and the barrier, onto the critical path.
-    asm volatile("" : "+a"(X));
-    __builtin_amdgcn_sched_barrier(0);
-    issue();
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  __syncthreads();  // D complete; every wave is done reading S0
-  // D^T fragments (lane: value column col, tokens 32g..32g+31): the A operand
-  // of the transposed P D product and the B operand of the state update.
-  typedef typename ScanOps<MT, ROLE>::v16 v16;
-  constexpr int FE = ScanOps<MT, ROLE>::FE;
-  v16 dfr[32 / FE];
-#pragma unroll
-  for (int s = 0; s < 32 / FE; ++s) dfr[s] = *reinterpret_cast<const v16*>(sD + col * DL + 32 * g + FE * s);
-  if constexpr (ROLE == 1) {
-    // out^T = scale (S0^T Qt^T + D^T P^T): P rows 32wp.. are the columns
-    X = mma32_rr<MT, 32>(dfr, cur.x, X);
-    // Lane (col, g) holds token 32wp + col at values 8 e4 + 4g + (0..3).  One
-    // exchange between the lane halves per pair of e4 gives each lane the
-    // eight consecutive values 16 pr + 8g + (0..7), pr = 0, 1: 16-byte
-    // (bf16) or 32-byte (fp32) stores of whole 32-byte pieces.
-    typedef unsigned u32;
-    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-    constexpr int NW = (int)sizeof(TO);  // 32-bit words per four output values
-    u32 wd[4][NW];
-#pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      if constexpr (sizeof(TO) == 2) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          wd[e4][j] = __builtin_bit_cast(u32, bf16x2{(bf16)(p.scale * X[4 * e4 + 2 * j]),
-                                                     (bf16)(p.scale * X[4 * e4 + 2 * j + 1])});
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) wd[e4][j] = __builtin_bit_cast(u32, p.scale * X[4 * e4 + j]);
-      }
-    }
-#pragma unroll
-    for (int pr = 0; pr < 2; ++pr)
-#pragma unroll
-      for (int j = 0; j < NW; ++j) {
-        const auto r = __builtin_amdgcn_permlane32_swap(wd[2 * pr][j], wd[2 * pr + 1][j], false, false);
-        wd[2 * pr][j] = r[0];
-        wd[2 * pr + 1][j] = r[1];
-      }
-    const int tk = 32 * wp + col;
-    // full chunks store without a branch, which keeps the memory-counter
-    // waits of the loop exact; only a sequence's last chunk is masked
-    if (FULL || tk < len) {
-      u32x4* o = reinterpret_cast<u32x4*>(out + ((size_t)(ctok + tk) * p.H + h) * DH + DVB * vb + 8 * g);
-#pragma unroll
-      for (int pr = 0; pr < 2; ++pr) {
-        if constexpr (sizeof(TO) == 2) {
-          o[2 * pr] = u32x4{wd[2 * pr][0], wd[2 * pr][1], wd[2 * pr + 1][0], wd[2 * pr + 1][1]};
-        } else {
-          o[4 * pr] = u32x4{wd[2 * pr][0], wd[2 * pr][1], wd[2 * pr][2], wd[2 * pr][3]};
-          o[4 * pr + 1] = u32x4{wd[2 * pr + 1][0], wd[2 * pr + 1][1], wd[2 * pr + 1][2], wd[2 * pr + 1][3]};
-        }
-      }
-    }
-  }
-  // S_next = Diag(Gam) S0 + Kb^T D, rows 32w.. of Kb^T, 64 tokens contracted
-#pragma unroll
-  for (int e = 0; e < 16; ++e) S[e] *= cur.gm[e >> 2][e & 3];
-  S = mma32_rr<MT, 32>(cur.kb, dfr, S);
-  // operand copy of the new state, transposed: sS[value][key]
-#pragma unroll
-  for (int e4 = 0; e4 < 4; ++e4)
-    store4(sS + col * SL + 32 * w + 8 * e4 + 4 * g,
-           f32x4{S[4 * e4], S[4 * e4 + 1], S[4 * e4 + 2], S[4 * e4 + 3]});
-  if constexpr (ROLE == 0 && !EARLY) {
-    __builtin_amdgcn_sched_barrier(0);
-    issue();
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  __syncthreads();  // new S0 complete; D may be overwritten
-}
-
-// The chunk loop of one wave: operands are loaded ahead into rotating register
-// sets (bf16: two chunks ahead, three sets; fp32: one chunk ahead, two sets).
-// S (in/out): the wave's 32 state rows 32w.. (key) at value columns vb*32..
-// of this sequence, FP32; the LDS operand copy of its start value is in sS.
-template <typename MT, typename TO, int ROLE>
-__device__ __forceinline__ void scan_chunks(const ScanArgs& p, MT* sS, MT* sD, int h, int cbeg,
-                                            int cend, int tseq, int tend, int vb, int w, int l,
-                                            f32x16& S) {
-  const int g = l >> 5, wp = w & 1;
-  const int H = p.H;
-  const MT* __restrict__ rec = reinterpret_cast<const MT*>(p.rec);
-  auto load = [&](ScanOps<MT, ROLE>& o, int c) {
-    scan_load(o, rec + ((size_t)c * H + h) * REC, p.gam + ((size_t)c * H + h) * DH, wp, w, l, g, vb);
-  };
-  auto step = [&](const ScanOps<MT, ROLE>& o, f32x16& S, int c, auto&& issue) {
-    const int ctok = tseq + (c - cbeg) * CHUNK;
-    scan_step<MT, TO, ROLE, true>(p, o, S, sS, sD, h, ctok, CHUNK, vb, w, l, issue);
-  };
-  auto tail = [&](const ScanOps<MT, ROLE>& o, f32x16& S, int c, auto&& issue) {
-    const int ctok = tseq + (c - cbeg) * CHUNK;
-    scan_step<MT, TO, ROLE, false>(p, o, S, sS, sD, h, ctok, tend - ctok, vb, w, l, issue);
-  };
-  auto none = [] {};
-  // Full chunks run in the main loop; a partial last chunk runs after it.
-  // Prefetch loads are unconditional (indices clamped to the last chunk), so
-  // every iteration issues the same memory operations and the compiler's
-  // memory-counter waits only cover the chunk being consumed.
-  const int cfull = cbeg + (tend - tseq) / CHUNK;  // chunks [cbeg, cfull) are full
-  const int clast = cend - 1;
-  ScanOps<MT, ROLE> o0, o1, o2;
-  load(o0, cbeg);
-  if constexpr (sizeof(MT) == 2) load(o1, min(cbeg + 1, clast));
-  __syncthreads();  // start-state operand visible
-  int c = cbeg;
-  if constexpr (sizeof(MT) == 2) {
-    // o0 holds chunk c, o1 chunk c+1; step c sends the loads of chunk c+2
-    for (; c + 3 <= cfull; c += 3) {
-      step(o0, S, c, [&] { load(o2, min(c + 2, clast)); });
-      step(o1, S, c + 1, [&] { load(o0, min(c + 3, clast)); });
-      step(o2, S, c + 2, [&] { load(o1, min(c + 4, clast)); });
-    }
-    // at most two full chunks and the partial chunk remain
-    if (c < cend) {
-      auto nx = [&] { load(o2, min(c + 2, clast)); };
-      if (c < cfull) step(o0, S, c, nx); else tail(o0, S, c, nx);
-      ++c;
-    }
-    if (c < cend) {
-      if (c < cfull) step(o1, S, c, none); else tail(o1, S, c, none);
-      ++c;
-    }
-    if (c < cend) tail(o2, S, c, none);
-  } else {
-    // FP32 operands are twice as large: two sets; step c sends chunk c+1
-    for (; c + 2 <= cfull; c += 2) {
-      step(o0, S, c, [&] { load(o1, min(c + 1, clast)); });
-      step(o1, S, c + 1, [&] { load(o0, min(c + 2, clast)); });
-    }
-    if (c < cend) {
-      auto nx = [&] { load(o1, min(c + 1, clast)); };
-      if (c < cfull) step(o0, S, c, nx); else tail(o0, S, c, nx);
-      ++c;
-    }
-    if (c < cend) tail(o1, S, c, none);
-  }
-}
-
-template <typename MT, typename TO>
-__global__ __launch_bounds__(256) void kda_scan_kernel(ScanArgs p) {
-  typedef ScanLds<MT> L;
-  constexpr int SL = L::SL;
-  __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
-  MT* sS = reinterpret_cast<MT*>(smem + L::O_S);  // S0^T [32 dv][SL]
-  MT* sD = reinterpret_cast<MT*>(smem + L::O_D);  // D^T  [32 dv][DL]
-
-  int pair, vb;
-  scan_unit(blockIdx.x, pair, vb);
-  if (pair >= p.N * p.H) return;
-  const int n = pair / p.H, h = pair - n * p.H;
-  const int cbeg = p.cfirst[n], cend = p.cfirst[n + 1];
-  const int tseq = p.cu[n], tend = p.cu[n + 1];
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int col = l & 31, g = l >> 5;
-  // Lane (col, g) of wave w holds state entries (key 32w + row32(e), value
-  // 32vb + col); for each e the 32 lanes of a group touch 128 contiguous bytes.
-  const size_t sbase = (size_t)pair * DH * DH + (size_t)(32 * w) * DH + DVB * vb + col;
-  f32x16 S;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) S[e] = p.init ? p.init[sbase + (size_t)row32(e, l) * DH] : 0.0f;
-  if (cbeg == cend) {  // empty sequence: the end state is the start state
-    if (p.fin) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) p.fin[sbase + (size_t)row32(e, l) * DH] = S[e];
-    }
-    return;
-  }
-  // operand copy of the start state, transposed: sS[value][key]
-#pragma unroll
-  for (int e4 = 0; e4 < 4; ++e4)
-    store4(sS + col * SL + 32 * w + 8 * e4 + 4 * g,
-           f32x4{S[4 * e4], S[4 * e4 + 1], S[4 * e4 + 2], S[4 * e4 + 3]});
-  if (w < 2) scan_chunks<MT, TO, 0>(p, sS, sD, h, cbeg, cend, tseq, tend, vb, w, l, S);
-  else scan_chunks<MT, TO, 1>(p, sS, sD, h, cbeg, cend, tseq, tend, vb, w, l, S);
-  if (p.fin) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) p.fin[sbase + (size_t)row32(e, l) * DH] = S[e];
-  }
 }
 
 // ===========================================================================
@@ -482,7 +247,7 @@ __device__ __forceinline__ void ring_step(const ScanArgs& p, const char* slot, f
     bf16x8 u[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) u[s] = frag(RG_U + wp * 2048 + s * 1024);
-    X = mma32_frags<bf16, 64>(a, sS + col * SL + 64 * g, X);
+    X = mma32_frags<64>(a, sS + col * SL + 64 * g, X);
     // D = U - W S0 at tokens 32wp + row32(e), value column col
 #pragma unroll
     for (int e4 = 0; e4 < 4; ++e4) {
@@ -493,7 +258,7 @@ __device__ __forceinline__ void ring_step(const ScanArgs& p, const char* slot, f
     }
   } else {
     // transposed product S0^T Qt^T: rows = values, columns = tokens
-    X = mma32_lds_frags<bf16, 64>(sS + col * SL + 64 * g, a, X);
+    X = mma32_lds_frags<64>(sS + col * SL + 64 * g, a, X);
   }
   wait_lds();
   ring_barrier();  // D complete; every wave is done reading S0
@@ -510,7 +275,7 @@ __device__ __forceinline__ void ring_step(const ScanArgs& p, const char* slot, f
     bf16x8 pr[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) pr[s] = frag(RG_P + wp * 4096 + s * 1024);
-    X = mma32_rr<bf16, 32>(dfr, pr, X);
+    X = mma32_rr<32>(dfr, pr, X);
     // lane (col, g): token 32wp + col, values 8 e4 + 4g + (0..3); one exchange
     // between the lane halves per pair of e4 gives 8 consecutive values
     typedef unsigned u32;
@@ -554,7 +319,7 @@ __device__ __forceinline__ void ring_step(const ScanArgs& p, const char* slot, f
   // S_next = Diag(Gam) S0 + Kb^T D
 #pragma unroll
   for (int e = 0; e < 16; ++e) S[e] *= gm[e >> 2][e & 3];
-  S = mma32_rr<bf16, 32>(kb, dfr, S);
+  S = mma32_rr<32>(kb, dfr, S);
 #pragma unroll
   for (int e4 = 0; e4 < 4; ++e4)
     store4(sS + col * SL + 32 * w + 8 * e4 + 4 * g,
@@ -635,6 +400,235 @@ __global__ __launch_bounds__(512) void kda_scan_ring_kernel(ScanArgs p) {
     } else {
       if (w < 2) ring_step<TO, 0, false>(p, slot, S, sS, sD, h, ctok, tend - ctok, vb, w, l);
       else ring_step<TO, 1, false>(p, slot, S, sS, sD, h, ctok, tend - ctok, vb, w, l);
+    }
+  }
+  if (p.fin) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) p.fin[sbase + (size_t)row32(e, l) * DH] = S[e];
+  }
+}
+
+// ===========================================================================
+// State pass with loader waves, FP32 intermediates.
+//
+// The same division of labour as above, with one LDS slot: a chunk's FP32
+// operands (120.5 KB) and the pieces of S0 and D (39 KB) fill the 160 KB of a
+// CU, so there is no second slot.  The slot is refilled in halves instead:
+// the early operands (W, Qt, U; read before the first barrier of a step) of
+// chunk c+1 are copied while the compute waves work on chunk c's late
+// operands (Kb^T, P, Gam), and those of chunk c+1 while the compute waves
+// work on chunk c+1's early ones.  Each copy has half a step to land and each
+// loader waits for all of its copies before the barrier that publishes them.
+// The compute waves hold no prefetched operands in registers, which leaves
+// the register file to the splitting of the operands into bf16 pieces.
+//
+// Slot layout (bytes): W [0,32K) | Qt [32K,64K) | Kb^T [64K,96K) | U of this
+// value block [96K,104K) | P [104K,120K) | Gam [120K, 120K+512).
+constexpr int RF_W = 0, RF_QT = 32768, RF_KBT = 65536, RF_U = 98304, RF_P = 106496, RF_GM = 122880;
+constexpr int RF_SLOT = 123392;
+struct Ring32Lds {
+  static constexpr int SL = ScanLds::SL, DL = ScanLds::DL, PS = ScanLds::PS, PD = ScanLds::PD;
+  static constexpr int O_SLOT = 0;
+  static constexpr int O_S = RF_SLOT;               // S0^T pieces [3][32][SL]
+  static constexpr int O_D = O_S + 3 * PS * 2;      // D^T pieces  [3][32][DL]
+  static constexpr int BYTES = O_D + 3 * PD * 2;
+};
+static_assert(Ring32Lds::BYTES <= 160 * 1024, "one slot plus the pieces fit in a CU's LDS");
+
+// Loader wave lw (0..3).  rc: chunk record (bytes, FP32 elements), gc: Gam.
+__device__ __forceinline__ void ring32_copy_early(const char* rc, char* slot, int vb, int lw, int l) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k)  // W and Qt: 64 KB, adjacent in the record and in the slot
+    copy_1k(rc + (lw + 4 * k) * 1024, slot + RF_W + (lw + 4 * k) * 1024, l);
+#pragma unroll
+  for (int k = 0; k < 2; ++k)  // U columns of value block vb: 8 KB
+    copy_1k(rc + 4 * OFF_UT + vb * 8192 + (lw + 4 * k) * 1024, slot + RF_U + (lw + 4 * k) * 1024, l);
+}
+__device__ __forceinline__ void ring32_copy_late(const char* rc, const char* gc, char* slot, int lw,
+                                                 int l) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k)  // Kb^T: 32 KB
+    copy_1k(rc + 4 * OFF_KBT + (lw + 4 * k) * 1024, slot + RF_KBT + (lw + 4 * k) * 1024, l);
+#pragma unroll
+  for (int k = 0; k < 4; ++k)  // P: 16 KB
+    copy_1k(rc + 4 * OFF_P + (lw + 4 * k) * 1024, slot + RF_P + (lw + 4 * k) * 1024, l);
+  if (lw == 0 && l < 32) copy_1k(gc, slot + RF_GM, l);  // 512 bytes of Gam
+}
+
+// One chunk for one compute wave of the FP32 ring; every FP32 fragment is
+// one 16-byte LDS read per lane from the slot, split into pieces as it is used.
+template <typename TO, int ROLE, bool FULL>
+__device__ __forceinline__ void ring32_step(const ScanArgs& p, const char* slot, f32x16& S,
+                                            bf16* sS, bf16* sD, int h, int ctok, int len, int vb,
+                                            int w, int l) {
+  typedef Ring32Lds L;
+  constexpr int SL = L::SL, DL = L::DL, PS = L::PS, PD = L::PD;
+  const int col = l & 31, g = l >> 5, wp = w & 1;
+  TO* __restrict__ out = reinterpret_cast<TO*>(p.out);
+  auto frag = [&](int off) { return *reinterpret_cast<const f32x4*>(slot + off + 16 * l); };
+  f32x16 X;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) X[e] = 0.0f;
+  // X = W S0 (role 0) or S0^T Qt^T (role 1); fragments 2s, 2s+1 of the row
+  // pair with S0^T entries 64g + 8s .. 64g + 8s + 7
+  const int abase = (ROLE == 0 ? RF_W : RF_QT) + wp * 16384;
+  const bf16* ps = sS + col * SL + 64 * g;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    bf16x8 ra[3], rb[3];
+    split8(frag(abase + 2 * s * 1024), frag(abase + (2 * s + 1) * 1024), ra);
+    load_pieces8(ps + 8 * s, PS, rb);
+    X = ROLE == 0 ? mma_x6(ra, rb, X) : mma_x6(rb, ra, X);
+  }
+  if constexpr (ROLE == 0) {
+    // D = U - W S0 at tokens 32wp + row32(e), value column col
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const f32x4 u = frag(RF_U + wp * 4096 + e4 * 1024);
+      store_pieces4(sD + col * DL + 32 * wp + 8 * e4 + 4 * g, PD,
+                    f32x4{u[0] - X[4 * e4], u[1] - X[4 * e4 + 1], u[2] - X[4 * e4 + 2],
+                          u[3] - X[4 * e4 + 3]});
+    }
+  }
+  wait_lds();
+  ring_barrier();  // D complete; every wave is done reading S0 and the early operands
+  bf16x8 dp[4][3];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) load_pieces8(sD + col * DL + 32 * g + 8 * s, PD, dp[s]);
+  if constexpr (ROLE == 1) {
+    // out^T = scale (S0^T Qt^T + D^T P^T): P rows 32wp.. are the columns
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 rp[3];
+      split8(frag(RF_P + wp * 8192 + 2 * s * 1024), frag(RF_P + wp * 8192 + (2 * s + 1) * 1024), rp);
+      X = mma_x6(dp[s], rp, X);
+    }
+    constexpr int NW = (int)sizeof(TO);  // 32-bit words per four output values
+    u32 wd[4][NW];
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      if constexpr (sizeof(TO) == 2) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          wd[e4][j] = __builtin_bit_cast(u32, bf16x2{(bf16)(p.scale * X[4 * e4 + 2 * j]),
+                                                     (bf16)(p.scale * X[4 * e4 + 2 * j + 1])});
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wd[e4][j] = __builtin_bit_cast(u32, p.scale * X[4 * e4 + j]);
+      }
+    }
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+      for (int j = 0; j < NW; ++j) {
+        const auto r = __builtin_amdgcn_permlane32_swap(wd[2 * pr][j], wd[2 * pr + 1][j], false, false);
+        wd[2 * pr][j] = r[0];
+        wd[2 * pr + 1][j] = r[1];
+      }
+    const int tk = 32 * wp + col;
+    if (FULL || tk < len) {
+      u32x4* o = reinterpret_cast<u32x4*>(out + ((size_t)(ctok + tk) * p.H + h) * DH + DVB * vb + 8 * g);
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        if constexpr (sizeof(TO) == 2) {
+          o[2 * pr] = u32x4{wd[2 * pr][0], wd[2 * pr][1], wd[2 * pr + 1][0], wd[2 * pr + 1][1]};
+        } else {
+          o[4 * pr] = u32x4{wd[2 * pr][0], wd[2 * pr][1], wd[2 * pr][2], wd[2 * pr][3]};
+          o[4 * pr + 1] = u32x4{wd[2 * pr + 1][0], wd[2 * pr + 1][1], wd[2 * pr + 1][2], wd[2 * pr + 1][3]};
+        }
+      }
+    }
+  }
+  // S_next = Diag(Gam) S0 + Kb^T D, rows 32w.. of Kb^T, 64 tokens contracted
+  const f32x4* gmp = reinterpret_cast<const f32x4*>(slot + RF_GM);
+#pragma unroll
+  for (int e4 = 0; e4 < 4; ++e4) {
+    const f32x4 gm = gmp[(32 * w + 8 * e4 + 4 * g) / 4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) S[4 * e4 + i] *= gm[i];
+  }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    bf16x8 rk[3];
+    split8(frag(RF_KBT + w * 8192 + 2 * s * 1024), frag(RF_KBT + w * 8192 + (2 * s + 1) * 1024), rk);
+    S = mma_x6(rk, dp[s], S);
+  }
+#pragma unroll
+  for (int e4 = 0; e4 < 4; ++e4)
+    store_pieces4(sS + col * SL + 32 * w + 8 * e4 + 4 * g, PS,
+                  f32x4{S[4 * e4], S[4 * e4 + 1], S[4 * e4 + 2], S[4 * e4 + 3]});
+  wait_lds();
+  ring_barrier();  // new S0 complete; D and the late operands may be overwritten
+}
+
+template <typename TO>
+__global__ __launch_bounds__(512) void kda_scan_ring32_kernel(ScanArgs p) {
+  typedef Ring32Lds L;
+  __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+  char* slot = smem + L::O_SLOT;
+  bf16* sS = reinterpret_cast<bf16*>(smem + L::O_S);
+  bf16* sD = reinterpret_cast<bf16*>(smem + L::O_D);
+
+  int pair, vb;
+  scan_unit(blockIdx.x, pair, vb);
+  if (pair >= p.N * p.H) return;
+  const int n = pair / p.H, h = pair - n * p.H;
+  const int cbeg = p.cfirst[n], cend = p.cfirst[n + 1];
+  const int tseq = p.cu[n], tend = p.cu[n + 1];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int col = l & 31, g = l >> 5;
+  const int H = p.H;
+  const char* recb = reinterpret_cast<const char*>(p.rec);
+  const char* gamb = reinterpret_cast<const char*>(p.gam);
+  auto rec_of = [&](int c) { return recb + ((size_t)c * H + h) * (size_t)REC * 4; };
+  auto gam_of = [&](int c) { return gamb + ((size_t)c * H + h) * DH * 4; };
+
+  if (w >= 4) {
+    // ------------------------------------------------------------ loaders
+    // Barriers: one after the prologue, two per chunk -- the same sequence as
+    // the compute waves.
+    if (cbeg == cend) return;
+    const int lw = w - 4, clast = cend - 1;
+    ring32_copy_early(rec_of(cbeg), slot, vb, lw, l);
+    wait_vm<0>();
+    ring_barrier();  // early operands of chunk cbeg in; start state in sS
+    for (int c = cbeg; c < cend; ++c) {
+      ring32_copy_late(rec_of(c), gam_of(c), slot, lw, l);
+      wait_vm<0>();
+      ring_barrier();  // late operands of chunk c in; early ones consumed
+      ring32_copy_early(rec_of(min(c + 1, clast)), slot, vb, lw, l);
+      wait_vm<0>();
+      ring_barrier();  // early operands of chunk c+1 in; late ones of c consumed
+    }
+    return;
+  }
+  // -------------------------------------------------------------- compute
+  const size_t sbase = (size_t)pair * DH * DH + (size_t)(32 * w) * DH + DVB * vb + col;
+  f32x16 S;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) S[e] = p.init ? p.init[sbase + (size_t)row32(e, l) * DH] : 0.0f;
+  if (cbeg == cend) {
+    if (p.fin) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) p.fin[sbase + (size_t)row32(e, l) * DH] = S[e];
+    }
+    return;
+  }
+#pragma unroll
+  for (int e4 = 0; e4 < 4; ++e4)
+    store_pieces4(sS + col * L::SL + 32 * w + 8 * e4 + 4 * g, L::PS,
+                  f32x4{S[4 * e4], S[4 * e4 + 1], S[4 * e4 + 2], S[4 * e4 + 3]});
+  wait_lds();
+  ring_barrier();
+  const int cfull = cbeg + (tend - tseq) / CHUNK;
+  for (int c = cbeg; c < cend; ++c) {
+    const int ctok = tseq + (c - cbeg) * CHUNK;
+    if (c < cfull) {
+      if (w < 2) ring32_step<TO, 0, true>(p, slot, S, sS, sD, h, ctok, CHUNK, vb, w, l);
+      else ring32_step<TO, 1, true>(p, slot, S, sS, sD, h, ctok, CHUNK, vb, w, l);
+    } else {
+      if (w < 2) ring32_step<TO, 0, false>(p, slot, S, sS, sD, h, ctok, tend - ctok, vb, w, l);
+      else ring32_step<TO, 1, false>(p, slot, S, sS, sD, h, ctok, tend - ctok, vb, w, l);
     }
   }
   if (p.fin) {

@@ -37,6 +37,15 @@ FLOP_PER_TH = 139264                             # 3 d^2 + 1.5 C d + C d MACs, x
 # the state pass with the output (3 d^2 MACs: W S0, Qt S0, Kb^T D)
 FLOP_INTRA_PER_TH = 2 * (3 * 64 * 128 // 2 + 64 * 128)   # 40,960
 FLOP_STATE_PER_TH = 2 * 3 * 128 * 128                   # 98,304
+# transcendentals per token-head on the path: the gate's softplus (exp, log)
+# and decay (exp) per channel, beta's sigmoid (exp, reciprocal) and the two
+# rsqrt of the norms; decay products inside a chunk are multiplications
+TRANS_PER_TH = 3 * 128 + 2 + 2                          # 388
+# quarter-rate transcendental VALU: 256 CUs x 4 SIMDs x 16 lanes / 4 x 2.4 GHz
+VALU_TRANS_PER_S = 256 * 4 * 16 / 4 * 2.4e9             # 9.83e12
+# the FP32-intermediate state pass forms every FP32 product from six bf16
+# matrix-core products (three-piece split): its peak is the bf16 one / 6
+SPLIT_PASSES = 6
 
 
 def kernel_source_hash() -> str:
@@ -326,6 +335,12 @@ def roofline_for(mode_name: str, T: int, H: int, res: dict, workload: str):
                 "unit": "TFLOP/s", "frac": round(kfl / MFMA_FP32_TFLOPS, 4)}
         roof["path_mfma_fp32_frac"] = round(th * FLOP_PER_TH / (res["p50_us"] * 1e-6) / 1e12
                                             / MFMA_FP32_TFLOPS, 4)
+        # the state pass runs its FP32 products as six bf16 matrix-core passes
+        sfl = FLOP_STATE_PER_TH * th / (st[2] * 1e-6) / 1e12
+        speak = MFMA_BF16_TFLOPS / SPLIT_PASSES
+        roof["state_pass_split"] = {"achieved": round(sfl, 2), "peak": round(speak, 1),
+                                    "unit": "TFLOP/s", "frac": round(sfl / speak, 4),
+                                    "passes": SPLIT_PASSES, "kernel_avg_us": round(st[2], 2)}
     roof["kernel"] = names[dom]
     roof["kernel_avg_us"] = round(st[dom], 2)
     roof["traffic"] = load_traffic(names[dom], workload, mode_name)
@@ -335,6 +350,15 @@ def roofline_for(mode_name: str, T: int, H: int, res: dict, workload: str):
     roof["path_hbm_frac"] = round(path_gbs / HBM_PEAK_GBS, 4)
     roof["path_mfma_bf16_frac"] = round(th * FLOP_PER_TH / (res["p50_us"] * 1e-6) / 1e12
                                         / MFMA_BF16_TFLOPS, 4)
+    # the path's lower bounds in time (whole step) and the step against the largest
+    bounds = {"hbm": path_bytes / (HBM_PEAK_GBS * 1e9) * 1e6,
+              "mfma_bf16": th * FLOP_PER_TH / (MFMA_BF16_TFLOPS * 1e12) * 1e6,
+              "mfma_fp32": th * FLOP_PER_TH / (MFMA_FP32_TFLOPS * 1e12) * 1e6,
+              "valu_transcendental": th * TRANS_PER_TH / VALU_TRANS_PER_S * 1e6}
+    if mode_name == "bf16":
+        del bounds["mfma_fp32"]
+    roof["path_bounds_us"] = {k: round(v, 1) for k, v in bounds.items()}
+    roof["path_frac_vs_max_bound"] = round(max(bounds.values()) / res["p50_us"], 4)
     return roof
 
 

@@ -62,9 +62,13 @@ extern "C" {
  * KDA_MODE_FP32_INTERMEDIATE: 0 = BF16 intermediates (normalised q/k, the
  *   chunk-solve outputs W/U, the output-combine matrices and the state
  *   snapshots used as matrix operands are bfloat16, accumulation is FP32);
- *   1 = every intermediate and matrix product in FP32 (xtuner PR #2301,
- *   section Change).  In both modes the gate, its chunk prefix, the
- *   forward substitution and the running state are FP32.
+ *   1 = every intermediate stored in FP32 and every matrix product
+ *   FP32-accurate (xtuner PR #2301, section Change): FP32 matrix cores in
+ *   the intra-chunk kernel; in the state pass bf16 matrix cores on a
+ *   three-piece bf16 split of each FP32 operand, six piece products per
+ *   product, FP32 accumulation (omitted terms below 2^-23 of the product).
+ *   In both modes the gate, its chunk prefix, the forward substitution and
+ *   the running state are FP32.
  * KDA_ACT_FP32: activation dtype of q, k, v, f_raw, b_raw: 0 = bfloat16,
  *   1 = float32.
  * KDA_OUT_FP32: dtype of out: 0 = the activation dtype, 1 = float32. */

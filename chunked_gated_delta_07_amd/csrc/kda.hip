@@ -221,8 +221,8 @@ static int launch_bwd(const void* q, const void* k, const void* v, const void* f
   a.dinit = dinit; a.dA_log = dA_log; a.ddt_bias = ddt;
   const int64_t pairs = (int64_t)N * H;
   const dim3 gscan((unsigned)(32 * ((pairs + 7) / 8)));
-  hipLaunchKernelGGL(kda_bwd_fscan_kernel, gscan, dim3(256), 0, stream, a);
-  hipLaunchKernelGGL((kda_bwd_bscan_kernel<TG>), gscan, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(kda_bwd_fscan_kernel, gscan, dim3(SCAN_THREADS), 0, stream, a);
+  hipLaunchKernelGGL((kda_bwd_bscan_kernel<TG>), gscan, dim3(SCAN_THREADS), 0, stream, a);
   hipLaunchKernelGGL((kda_bwd_jprod_kernel<TG>), gch, dim3(256), 0, stream, a);
   hipLaunchKernelGGL((kda_bwd_tprod_kernel<TA, TR>), gch, dim3(256), 0, stream, a);
   hipLaunchKernelGGL((kda_bwd_gate_kernel<TA>), gch, dim3(512), 0, stream, a);

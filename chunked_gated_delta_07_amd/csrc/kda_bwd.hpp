@@ -140,12 +140,28 @@ __device__ __forceinline__ void load8_scaled(const float* p, float s, float (&o)
   for (int e = 0; e < 4; ++e) { o[e] = s * a[e]; o[4 + e] = s * b[e]; }
 }
 
+// Four consecutive dout values of one row, scaled.
+__device__ __forceinline__ void load4_scaled(const bf16* p, float s, float (&o)[4]) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = s * (float)v[e];
+}
+__device__ __forceinline__ void load4_scaled(const float* p, float s, float (&o)[4]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = s * a[e];
+}
+
 // ------------------------------------------------------------ 2. forward scan
 // Per chunk: snapshot S0; D = U - W S0; S_next = Diag(Gam) S0 + Kb^T D.
 // LDS: W [64][128] (rows of K over keys), Kb^T [128][64] (over tokens),
 // U^T block [32][64], S^T block [32 value][128 key], D^T [32][64], Gam.
-__global__ __launch_bounds__(256) void kda_bwd_fscan_kernel(BwdArgs p) {
-  constexpr int LL = SL_LONG, LS = SL_SHORT;
+// Eight waves (two per SIMD, so one wave's LDS and barrier waits overlap the
+// other's matrix work): D tiles (16 tokens x 16 values) one per wave, state
+// tiles (16 keys x 16 values) two per wave.
+constexpr int SCAN_THREADS = 512;
+__global__ __launch_bounds__(SCAN_THREADS) void kda_bwd_fscan_kernel(BwdArgs p) {
+  constexpr int LL = SL_LONG, LS = SL_SHORT, NT = SCAN_THREADS;
   __shared__ __attribute__((aligned(16))) float sW[CHUNK * LL];
   __shared__ __attribute__((aligned(16))) float sKbT[DH * LS];
   __shared__ __attribute__((aligned(16))) float sUT[32 * LS];
@@ -161,42 +177,36 @@ __global__ __launch_bounds__(256) void kda_bwd_fscan_kernel(BwdArgs p) {
   const int c_lo = p.cfirst[n], c_hi = p.cfirst[n + 1];
   // the state entering each chunk is snapshotted from registers as it is
   // formed; the first one here
-  for (int x = tid; x < DH * 32; x += 256) {
+  for (int x = tid; x < DH * 32; x += NT) {
     const int i = x >> 5, j = x & 31;
     const float s0 = p.init ? p.init[((size_t)pair * DH + i) * DH + v0 + j] : 0.0f;
     sST[j * LL + i] = s0;
     if (c_lo < c_hi) p.s0[((size_t)c_lo * p.H + h) * STM + i * DH + v0 + j] = s0;
   }
-  // register staging of one chunk's records: W 8, Kb^T 8, U^T 2 f32x4 per thread, Gam
-  f32x4 rW[8], rK[8], rU[2], rG;
+  // register staging of one chunk's records: W 4, Kb^T 4, U^T 1 f32x4 per thread, Gam
+  constexpr int NR = CHUNK * DH / 4 / NT;  // f32x4 of a 64 x 128 matrix per thread
+  f32x4 rW[NR], rK[NR], rU, rG;
   auto fetch = [&](int c) {
     const size_t ch = (size_t)c * p.H + h;
     const float* rec = p.rec + ch * REC;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int x = tid + 256 * u;
+    for (int u = 0; u < NR; ++u) {
+      const int x = tid + NT * u;
       rW[u] = *reinterpret_cast<const f32x4*>(rec + OFF_W + 4 * x);   // row x/32, cols 4(x%32)
       rK[u] = *reinterpret_cast<const f32x4*>(rec + OFF_KBT + 4 * x); // row x/16, cols 4(x%16)
     }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int x = tid + 256 * u;  // U^T row v0 + x/16, tokens 4(x%16)
-      rU[u] = *reinterpret_cast<const f32x4*>(rec + OFF_UT + (v0 + (x >> 4)) * CHUNK + 4 * (x & 15));
-    }
+    // U^T row v0 + tid/16, tokens 4(tid%16)
+    rU = *reinterpret_cast<const f32x4*>(rec + OFF_UT + (v0 + (tid >> 4)) * CHUNK + 4 * (tid & 15));
     if (tid < 32) rG = *reinterpret_cast<const f32x4*>(p.gam + ch * DH + 4 * tid);
   };
   auto stage = [&]() {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int x = tid + 256 * u;
+    for (int u = 0; u < NR; ++u) {
+      const int x = tid + NT * u;
       *reinterpret_cast<f32x4*>(sW + (x >> 5) * LL + 4 * (x & 31)) = rW[u];
       *reinterpret_cast<f32x4*>(sKbT + (x >> 4) * LS + 4 * (x & 15)) = rK[u];
     }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int x = tid + 256 * u;
-      *reinterpret_cast<f32x4*>(sUT + (x >> 4) * LS + 4 * (x & 15)) = rU[u];
-    }
+    *reinterpret_cast<f32x4*>(sUT + (tid >> 4) * LS + 4 * (tid & 15)) = rU;
     if (tid < 32) *reinterpret_cast<f32x4*>(sGam + 4 * tid) = rG;
   };
   if (c_lo < c_hi) {
@@ -204,17 +214,17 @@ __global__ __launch_bounds__(256) void kda_bwd_fscan_kernel(BwdArgs p) {
     stage();
   }
   __syncthreads();
+  const int rb = w & 3, cbw = w >> 2;  // this wave's D tile
   for (int c = c_lo; c < c_hi; ++c) {
     const size_t ch = (size_t)c * p.H + h;
-    // D[r][j] = U[r][j] - sum_c W[r][c] S[c][j]: wave w rows 16w.., both column halves
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    // D[r][j] = U[r][j] - sum_c W[r][c] S[c][j]: rows 16 rb.., values 16 cbw..
+    {
       f32x4 acc = {0, 0, 0, 0};
-      acc = mma16_rows<float, DH>(sW + 16 * w * LL, LL, sST + 16 * cb * LL, LL, acc, l);
-      const int j = 16 * cb + (l & 15);
+      acc = mma16_rows<float, DH>(sW + 16 * rb * LL, LL, sST + 16 * cbw * LL, LL, acc, l);
+      const int j = 16 * cbw + (l & 15);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 16 * w + 4 * (l >> 4) + e;
+        const int r = 16 * rb + 4 * (l >> 4) + e;
         const float d = sUT[j * LS + r] - acc[e];
         sDT[j * LS + r] = d;
         p.dmat[ch * MAT + r * DH + v0 + j] = d;
@@ -223,36 +233,30 @@ __global__ __launch_bounds__(256) void kda_bwd_fscan_kernel(BwdArgs p) {
     __syncthreads();
     const bool more = c + 1 < c_hi;
     if (more) fetch(c + 1);
-    // S_next[i][j] = Gam_i S[i][j] + sum_r KbT[i][r] D[r][j]: wave w key rows 32w..32w+31
-    f32x4 ns[2][2];
+    // S_next[i][j] = Gam_i S[i][j] + sum_r KbT[i][r] D[r][j]: key rows 16w..16w+15
+    f32x4 ns[2];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      const int kb = 2 * w + kb2;
+    for (int cb = 0; cb < 2; ++cb) {
+      f32x4 acc;
+      const int j = 16 * cb + (l & 15);
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        f32x4 acc;
-        const int j = 16 * cb + (l & 15);
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * w + 4 * (l >> 4) + e;
+        acc[e] = sGam[i] * sST[j * LL + i];
+      }
+      ns[cb] = mma16_rows<float, CHUNK>(sKbT + 16 * w * LS, LS, sDT + 16 * cb * LS, LS, acc, l);
+      if (more) {
+        float* snap = p.s0 + (ch + p.H) * STM;  // state entering chunk c + 1
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 16 * kb + 4 * (l >> 4) + e;
-          acc[e] = sGam[i] * sST[j * LL + i];
-        }
-        ns[kb2][cb] = mma16_rows<float, CHUNK>(sKbT + 16 * kb * LS, LS, sDT + 16 * cb * LS, LS, acc, l);
-        if (more) {
-          float* snap = p.s0 + (ch + p.H) * STM;  // state entering chunk c + 1
-#pragma unroll
-          for (int e = 0; e < 4; ++e) snap[(16 * kb + 4 * (l >> 4) + e) * DH + v0 + j] = ns[kb2][cb][e];
-        }
+        for (int e = 0; e < 4; ++e) snap[(16 * w + 4 * (l >> 4) + e) * DH + v0 + j] = ns[cb][e];
       }
     }
     __syncthreads();
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
+    for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          sST[(16 * cb + (l & 15)) * LL + 16 * (2 * w + kb2) + 4 * (l >> 4) + e] = ns[kb2][cb][e];
+      for (int e = 0; e < 4; ++e)
+        sST[(16 * cb + (l & 15)) * LL + 16 * w + 4 * (l >> 4) + e] = ns[cb][e];
     if (more) stage();
     __syncthreads();
   }
@@ -263,10 +267,11 @@ __global__ __launch_bounds__(256) void kda_bwd_fscan_kernel(BwdArgs p) {
 // dS0 = Diag(Gam) dSn + scale Qt^T dO - W^T dD.  Ends with dS_init.
 // LDS (rows of K): P^T [64 r][64 i], Kb [64 r][128 c], Qt^T [128 i][64 r],
 // W^T [128][64], (scale dO)^T block [32 j][64 r], dS^T block [32][128],
-// dD^T [32][64], Gam.
+// dD^T [32][64], Gam.  Eight waves as in the forward scan: dD tiles one per
+// wave, dS0 tiles two per wave.
 template <typename TG>
-__global__ __launch_bounds__(256) void kda_bwd_bscan_kernel(BwdArgs p) {
-  constexpr int LL = SL_LONG, LS = SL_SHORT;
+__global__ __launch_bounds__(SCAN_THREADS) void kda_bwd_bscan_kernel(BwdArgs p) {
+  constexpr int LL = SL_LONG, LS = SL_SHORT, NT = SCAN_THREADS;
   __shared__ __attribute__((aligned(16))) float sPT[CHUNK * LS];
   __shared__ __attribute__((aligned(16))) float sKb[CHUNK * LL];
   __shared__ __attribute__((aligned(16))) float sQtT[DH * LS];
@@ -286,55 +291,57 @@ __global__ __launch_bounds__(256) void kda_bwd_bscan_kernel(BwdArgs p) {
   const int tseq = p.cu[n], tend = p.cu[n + 1];
   // dSn of each chunk is snapshotted from registers as it is formed; the
   // last chunk's (= dS_final) here
-  for (int x = tid; x < DH * 32; x += 256) {
+  for (int x = tid; x < DH * 32; x += NT) {
     const int i = x >> 5, j = x & 31;
     const float d = p.dfin ? p.dfin[((size_t)pair * DH + i) * DH + v0 + j] : 0.0f;
     sST[j * LL + i] = d;
     if (c_lo < c_hi) p.dsn[((size_t)(c_hi - 1) * p.H + h) * STM + i * DH + v0 + j] = d;
   }
-  // register staging: P^T 4, Kb 8, Qt^T 8, W^T 8 f32x4, dO 8 values, Gam
-  f32x4 rP[4], rK[8], rQ[8], rW[8], rG;
-  float rO[8];
+  // register staging: P^T 2, Kb 4, Qt^T 4, W^T 4 f32x4, dO 4 values, Gam
+  constexpr int NR = CHUNK * DH / 4 / NT;  // f32x4 of a 64 x 128 matrix per thread
+  constexpr int NRP = CHUNK * CHUNK / 4 / NT;
+  f32x4 rP[NRP], rK[NR], rQ[NR], rW[NR], rG;
+  float rO[4];
   auto fetch = [&](int c) {
     const size_t ch = (size_t)c * p.H + h;
     const float* rec = p.rec + ch * REC;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)  // P^T [64 r][64 i]
-      rP[u] = *reinterpret_cast<const f32x4*>(rec + OFF_P + 4 * (tid + 256 * u));
+    for (int u = 0; u < NRP; ++u)  // P^T [64 r][64 i]
+      rP[u] = *reinterpret_cast<const f32x4*>(rec + OFF_P + 4 * (tid + NT * u));
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int x = tid + 256 * u;
+    for (int u = 0; u < NR; ++u) {
+      const int x = tid + NT * u;
       rK[u] = *reinterpret_cast<const f32x4*>(p.kbr + ch * MAT + 4 * x);        // Kb [64][128]
       rQ[u] = *reinterpret_cast<const f32x4*>(rec + OFF_QT + 4 * x);            // Qt^T [128][64]
       rW[u] = *reinterpret_cast<const f32x4*>(p.wt + ch * DH * CHUNK + 4 * x);  // W^T [128][64]
     }
     const int t0 = tseq + (c - c_lo) * CHUNK, len = min(CHUNK, tend - t0);
-    const int r = tid >> 2, j8 = 8 * (tid & 3);
+    const int r = tid >> 3, j4 = 4 * (tid & 7);
     if (r < len) {
-      load8_scaled(gO + ((size_t)(t0 + r) * p.H + h) * DH + v0 + j8, p.scale, rO);
+      load4_scaled(gO + ((size_t)(t0 + r) * p.H + h) * DH + v0 + j4, p.scale, rO);
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) rO[e] = 0.0f;
+      for (int e = 0; e < 4; ++e) rO[e] = 0.0f;
     }
     if (tid < 32) rG = *reinterpret_cast<const f32x4*>(p.gam + ch * DH + 4 * tid);
   };
   auto stage = [&]() {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int x = tid + 256 * u;
+    for (int u = 0; u < NRP; ++u) {
+      const int x = tid + NT * u;
       *reinterpret_cast<f32x4*>(sPT + (x >> 4) * LS + 4 * (x & 15)) = rP[u];
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int x = tid + 256 * u;
+    for (int u = 0; u < NR; ++u) {
+      const int x = tid + NT * u;
       *reinterpret_cast<f32x4*>(sKb + (x >> 5) * LL + 4 * (x & 31)) = rK[u];
       *reinterpret_cast<f32x4*>(sQtT + (x >> 4) * LS + 4 * (x & 15)) = rQ[u];
       *reinterpret_cast<f32x4*>(sWT + (x >> 4) * LS + 4 * (x & 15)) = rW[u];
     }
     {
-      const int r = tid >> 2, j8 = 8 * (tid & 3);
+      const int r = tid >> 3, j4 = 4 * (tid & 7);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sOT[(j8 + e) * LS + r] = rO[e];
+      for (int e = 0; e < 4; ++e) sOT[(j4 + e) * LS + r] = rO[e];
     }
     if (tid < 32) *reinterpret_cast<f32x4*>(sGam + 4 * tid) = rG;
   };
@@ -343,18 +350,18 @@ __global__ __launch_bounds__(256) void kda_bwd_bscan_kernel(BwdArgs p) {
     stage();
   }
   __syncthreads();
+  const int rb = w & 3, cbw = w >> 2;  // this wave's dD tile
   for (int c = c_hi - 1; c >= c_lo; --c) {
     const size_t ch = (size_t)c * p.H + h;
-    // dD[r][j] = sum_i P^T[r][i] dO^T[j][i] + sum_c Kb[r][c] dS^T[j][c]: wave w rows 16w..
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    // dD[r][j] = sum_i P^T[r][i] dO^T[j][i] + sum_c Kb[r][c] dS^T[j][c]: rows 16 rb.., values 16 cbw..
+    {
       f32x4 acc = {0, 0, 0, 0};
-      acc = mma16_rows<float, CHUNK>(sPT + 16 * w * LS, LS, sOT + 16 * cb * LS, LS, acc, l);
-      acc = mma16_rows<float, DH>(sKb + 16 * w * LL, LL, sST + 16 * cb * LL, LL, acc, l);
-      const int j = 16 * cb + (l & 15);
+      acc = mma16_rows<float, CHUNK>(sPT + 16 * rb * LS, LS, sOT + 16 * cbw * LS, LS, acc, l);
+      acc = mma16_rows<float, DH>(sKb + 16 * rb * LL, LL, sST + 16 * cbw * LL, LL, acc, l);
+      const int j = 16 * cbw + (l & 15);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 16 * w + 4 * (l >> 4) + e;
+        const int r = 16 * rb + 4 * (l >> 4) + e;
         sDT[j * LS + r] = acc[e];
         p.ddmat[ch * MAT + r * DH + v0 + j] = acc[e];
       }
@@ -362,43 +369,38 @@ __global__ __launch_bounds__(256) void kda_bwd_bscan_kernel(BwdArgs p) {
     __syncthreads();
     const bool more = c > c_lo;
     if (more) fetch(c - 1);
-    // dS0[i][j] = Gam_i dSn[i][j] + sum_r Qt^T[i][r] dO^T[j][r] - sum_r W^T[i][r] dD^T[j][r]
-    f32x4 ns[2][2];
+    // dS0[i][j] = Gam_i dSn[i][j] + sum_r Qt^T[i][r] dO^T[j][r] - sum_r W^T[i][r] dD^T[j][r]:
+    // key rows 16w..16w+15
+    f32x4 ns[2];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      const int kb = 2 * w + kb2;
+    for (int cb = 0; cb < 2; ++cb) {
+      f32x4 acc, neg = {0, 0, 0, 0};
+      const int j = 16 * cb + (l & 15);
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        f32x4 acc, neg = {0, 0, 0, 0};
-        const int j = 16 * cb + (l & 15);
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * w + 4 * (l >> 4) + e;
+        acc[e] = sGam[i] * sST[j * LL + i];
+      }
+      acc = mma16_rows<float, CHUNK>(sQtT + 16 * w * LS, LS, sOT + 16 * cb * LS, LS, acc, l);
+      neg = mma16_rows<float, CHUNK>(sWT + 16 * w * LS, LS, sDT + 16 * cb * LS, LS, neg, l);
+      ns[cb] = acc - neg;
+      if (more) {
+        float* snap = p.dsn + (ch - p.H) * STM;  // dSn of chunk c - 1
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 16 * kb + 4 * (l >> 4) + e;
-          acc[e] = sGam[i] * sST[j * LL + i];
-        }
-        acc = mma16_rows<float, CHUNK>(sQtT + 16 * kb * LS, LS, sOT + 16 * cb * LS, LS, acc, l);
-        neg = mma16_rows<float, CHUNK>(sWT + 16 * kb * LS, LS, sDT + 16 * cb * LS, LS, neg, l);
-        ns[kb2][cb] = acc - neg;
-        if (more) {
-          float* snap = p.dsn + (ch - p.H) * STM;  // dSn of chunk c - 1
-#pragma unroll
-          for (int e = 0; e < 4; ++e) snap[(16 * kb + 4 * (l >> 4) + e) * DH + v0 + j] = ns[kb2][cb][e];
-        }
+        for (int e = 0; e < 4; ++e) snap[(16 * w + 4 * (l >> 4) + e) * DH + v0 + j] = ns[cb][e];
       }
     }
     __syncthreads();
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
+    for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          sST[(16 * cb + (l & 15)) * LL + 16 * (2 * w + kb2) + 4 * (l >> 4) + e] = ns[kb2][cb][e];
+      for (int e = 0; e < 4; ++e)
+        sST[(16 * cb + (l & 15)) * LL + 16 * w + 4 * (l >> 4) + e] = ns[cb][e];
     if (more) stage();
     __syncthreads();
   }
   if (p.dinit) {
-    for (int x = tid; x < DH * 32; x += 256) {
+    for (int x = tid; x < DH * 32; x += NT) {
       const int i = x >> 5, j = x & 31;
       p.dinit[((size_t)pair * DH + i) * DH + v0 + j] = sST[j * LL + i];
     }

@@ -455,8 +455,49 @@ __device__ __forceinline__ void ring32_copy_late(const char* rc, const char* gc,
   if (lw == 0 && l < 32) copy_1k(gc, slot + RF_GM, l);  // 512 bytes of Gam
 }
 
-// One chunk for one compute wave of the FP32 ring; every FP32 fragment is
-// one 16-byte LDS read per lane from the slot, split into pieces as it is used.
+// Software-pipelined six-product step: C += (record operand) x (other operand)
+// over 16 contracted values from their pieces r and o, while the split of the
+// next step's record fragments (na, nb -> nr) runs on the VALU between the six
+// matrix-core products.  The products of one step accumulate into one tile, so
+// each waits for the previous; the wave issues the independent split
+// instructions in those gaps instead of after the sixth product.  The
+// scheduling barriers pin that order.  REC_A: the record operand is A (rows of
+// the product), else B.  Terms are summed smallest first, as in mma_x6.
+template <bool REC_A>
+__device__ __forceinline__ f32x16 mma_x6_pipe(const bf16x8 (&r)[3], const bf16x8 (&o)[3], f32x16 c,
+                                              bool next, const f32x4& na, const f32x4& nb,
+                                              bf16x8 (&nr)[3]) {
+  auto mm = [&](const bf16x8& x, const bf16x8& y) {
+    c = REC_A ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, c, 0, 0, 0)
+              : __builtin_amdgcn_mfma_f32_32x32x16_bf16(y, x, c, 0, 0, 0);
+  };
+  Pieces2 p0{}, p1{}, p2{}, p3{};
+  mm(r[2], o[0]);
+  if (next) p0 = split2(f32x2{na[0], na[1]});
+  __builtin_amdgcn_sched_barrier(0);
+  mm(r[1], o[1]);
+  if (next) p1 = split2(f32x2{na[2], na[3]});
+  __builtin_amdgcn_sched_barrier(0);
+  mm(r[0], o[2]);
+  if (next) p2 = split2(f32x2{nb[0], nb[1]});
+  __builtin_amdgcn_sched_barrier(0);
+  mm(r[1], o[0]);
+  if (next) p3 = split2(f32x2{nb[2], nb[3]});
+  __builtin_amdgcn_sched_barrier(0);
+  mm(r[0], o[1]);
+  if (next) {
+    nr[0] = __builtin_bit_cast(bf16x8, u32x4{p0.h, p1.h, p2.h, p3.h});
+    nr[1] = __builtin_bit_cast(bf16x8, u32x4{p0.m, p1.m, p2.m, p3.m});
+    nr[2] = __builtin_bit_cast(bf16x8, u32x4{p0.l, p1.l, p2.l, p3.l});
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  mm(r[0], o[0]);
+  return c;
+}
+
+// One chunk for one compute wave of the FP32 ring.  Every FP32 record fragment
+// is one 16-byte LDS read per lane from the slot, issued two steps before its
+// products, and split into pieces during the previous step's products.
 template <typename TO, int ROLE, bool FULL>
 __device__ __forceinline__ void ring32_step(const ScanArgs& p, const char* slot, f32x16& S,
                                             bf16* sS, bf16* sD, int h, int ctok, int len, int vb,
@@ -471,38 +512,89 @@ __device__ __forceinline__ void ring32_step(const ScanArgs& p, const char* slot,
   for (int e = 0; e < 16; ++e) X[e] = 0.0f;
   // X = W S0 (role 0) or S0^T Qt^T (role 1); fragments 2s, 2s+1 of the row
   // pair with S0^T entries 64g + 8s .. 64g + 8s + 7
-  const int abase = (ROLE == 0 ? RF_W : RF_QT) + wp * 16384;
-  const bf16* ps = sS + col * SL + 64 * g;
+  {
+    const int abase = (ROLE == 0 ? RF_W : RF_QT) + wp * 16384;
+    const bf16* ps = sS + col * SL + 64 * g;
+    f32x4 raw[8][2];
+    bf16x8 rr[8][3], oo[8][3];
+    raw[0][0] = frag(abase);
+    raw[0][1] = frag(abase + 1024);
+    raw[1][0] = frag(abase + 2048);
+    raw[1][1] = frag(abase + 3072);
+    load_pieces8(ps, PS, oo[0]);
+    f32x4 u[4];
+    if constexpr (ROLE == 0) {
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    bf16x8 ra[3], rb[3];
-    split8(frag(abase + 2 * s * 1024), frag(abase + (2 * s + 1) * 1024), ra);
-    load_pieces8(ps + 8 * s, PS, rb);
-    X = ROLE == 0 ? mma_x6(ra, rb, X) : mma_x6(rb, ra, X);
-  }
-  if constexpr (ROLE == 0) {
-    // D = U - W S0 at tokens 32wp + row32(e), value column col
+      for (int e4 = 0; e4 < 4; ++e4) u[e4] = frag(RF_U + wp * 4096 + e4 * 1024);
+    }
+    split8(raw[0][0], raw[0][1], rr[0]);
 #pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      const f32x4 u = frag(RF_U + wp * 4096 + e4 * 1024);
-      store_pieces4(sD + col * DL + 32 * wp + 8 * e4 + 4 * g, PD,
-                    f32x4{u[0] - X[4 * e4], u[1] - X[4 * e4 + 1], u[2] - X[4 * e4 + 2],
-                          u[3] - X[4 * e4 + 3]});
+    for (int s = 0; s < 8; ++s) {
+      if (s + 2 < 8) {
+        raw[s + 2][0] = frag(abase + 2 * (s + 2) * 1024);
+        raw[s + 2][1] = frag(abase + (2 * (s + 2) + 1) * 1024);
+      }
+      if (s + 1 < 8) load_pieces8(ps + 8 * (s + 1), PS, oo[s + 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      const int sn = s + 1 < 8 ? s + 1 : s;
+      X = mma_x6_pipe<ROLE == 0>(rr[s], oo[s], X, s + 1 < 8, raw[sn][0], raw[sn][1], rr[sn]);
+    }
+    if constexpr (ROLE == 0) {
+      // D = U - W S0 at tokens 32wp + row32(e), value column col
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4)
+        store_pieces4(sD + col * DL + 32 * wp + 8 * e4 + 4 * g, PD,
+                      f32x4{u[e4][0] - X[4 * e4], u[e4][1] - X[4 * e4 + 1],
+                            u[e4][2] - X[4 * e4 + 2], u[e4][3] - X[4 * e4 + 3]});
     }
   }
   wait_lds();
   ring_barrier();  // D complete; every wave is done reading S0 and the early operands
+  // Phase 2, one pipelined sequence of steps: role 1 runs D^T P^T into X
+  // (steps 0..3) and then Kb^T D into S (steps 4..7); role 0 only the latter.
+  constexpr int FIRST = ROLE == 1 ? 0 : 4;
   bf16x8 dp[4][3];
+  f32x4 raw[8][2];
+  bf16x8 rr[8][3];
+  auto rec_off = [&](int s, int half) {
+    return s < 4 ? RF_P + wp * 8192 + (2 * s + half) * 1024
+                 : RF_KBT + w * 8192 + (2 * (s - 4) + half) * 1024;
+  };
+#pragma unroll
+  for (int s = FIRST; s < 8 && s < FIRST + 2; ++s) {
+    raw[s][0] = frag(rec_off(s, 0));
+    raw[s][1] = frag(rec_off(s, 1));
+  }
 #pragma unroll
   for (int s = 0; s < 4; ++s) load_pieces8(sD + col * DL + 32 * g + 8 * s, PD, dp[s]);
-  if constexpr (ROLE == 1) {
-    // out^T = scale (S0^T Qt^T + D^T P^T): P rows 32wp.. are the columns
+  // Diag(Gam) S0 first: the state tile is free until the Kb^T products
+  const f32x4* gmp = reinterpret_cast<const f32x4*>(slot + RF_GM);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8 rp[3];
-      split8(frag(RF_P + wp * 8192 + 2 * s * 1024), frag(RF_P + wp * 8192 + (2 * s + 1) * 1024), rp);
-      X = mma_x6(dp[s], rp, X);
+  for (int e4 = 0; e4 < 4; ++e4) {
+    const f32x4 gm = gmp[(32 * w + 8 * e4 + 4 * g) / 4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) S[4 * e4 + i] *= gm[i];
+  }
+  split8(raw[FIRST][0], raw[FIRST][1], rr[FIRST]);
+#pragma unroll
+  for (int s = FIRST; s < 8; ++s) {
+    if (s + 2 < 8) {
+      raw[s + 2][0] = frag(rec_off(s + 2, 0));
+      raw[s + 2][1] = frag(rec_off(s + 2, 1));
     }
+    __builtin_amdgcn_sched_barrier(0);
+    const int sn = s + 1 < 8 ? s + 1 : s;
+    if (s < 4)  // out^T += D^T P^T: P rows 32wp.. are the columns
+      X = mma_x6_pipe<false>(rr[s], dp[s], X, true, raw[sn][0], raw[sn][1], rr[sn]);
+    else  // S_next = Diag(Gam) S0 + Kb^T D, rows 32w.. of Kb^T, 64 tokens contracted
+      S = mma_x6_pipe<true>(rr[s], dp[s - 4], S, s + 1 < 8, raw[sn][0], raw[sn][1], rr[sn]);
+  }
+#pragma unroll
+  for (int e4 = 0; e4 < 4; ++e4)
+    store_pieces4(sS + col * SL + 32 * w + 8 * e4 + 4 * g, PS,
+                  f32x4{S[4 * e4], S[4 * e4 + 1], S[4 * e4 + 2], S[4 * e4 + 3]});
+  if constexpr (ROLE == 1) {
+    // output of this chunk while the state pieces are written
     constexpr int NW = (int)sizeof(TO);  // 32-bit words per four output values
     u32 wd[4][NW];
 #pragma unroll
@@ -539,24 +631,6 @@ __device__ __forceinline__ void ring32_step(const ScanArgs& p, const char* slot,
       }
     }
   }
-  // S_next = Diag(Gam) S0 + Kb^T D, rows 32w.. of Kb^T, 64 tokens contracted
-  const f32x4* gmp = reinterpret_cast<const f32x4*>(slot + RF_GM);
-#pragma unroll
-  for (int e4 = 0; e4 < 4; ++e4) {
-    const f32x4 gm = gmp[(32 * w + 8 * e4 + 4 * g) / 4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) S[4 * e4 + i] *= gm[i];
-  }
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    bf16x8 rk[3];
-    split8(frag(RF_KBT + w * 8192 + 2 * s * 1024), frag(RF_KBT + w * 8192 + (2 * s + 1) * 1024), rk);
-    S = mma_x6(rk, dp[s], S);
-  }
-#pragma unroll
-  for (int e4 = 0; e4 < 4; ++e4)
-    store_pieces4(sS + col * SL + 32 * w + 8 * e4 + 4 * g, PS,
-                  f32x4{S[4 * e4], S[4 * e4 + 1], S[4 * e4 + 2], S[4 * e4 + 3]});
   wait_lds();
   ring_barrier();  // new S0 complete; D and the late operands may be overwritten
 }

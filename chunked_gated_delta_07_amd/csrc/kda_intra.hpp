@@ -470,44 +470,88 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
         }
       }
       wsync();
-      // pair vectors inside each 8-row half, 16 per batch
-      float d0 = 1.0f, d1 = 1.0f;
+    }
+    // Pairs (u, i), i < u, inside each 8-row half: the channel sums on the
+    // VALU.  Each lane forms its two channels' share of
+    //   A[u][i] ~ k_u . (k_i prod_{i<j<=u} a_j),   P[u][i] ~ q_u . (same),
+    // 16 pairs (32 values) per batch, then the wave sums them: two exchanges
+    // between lane halves and rows halve the values, three DPP steps inside a
+    // row halve them further, and a last one adds lanes l and l^1.  The norms
+    // are complete by now, so the entries are written in their final form.
+    {
+      auto as_u = [](float x) { return __builtin_bit_cast(uint32_t, x); };
+      auto as_f = [](uint32_t x) { return __builtin_bit_cast(float, x); };
+      // partner value through DPP (row_mirror 0x140, row_half_mirror 0x141,
+      // quad_perm xor 2 0x4E, quad_perm xor 1 0xB1)
+      auto dpp = [&](float x, auto ctrl) {
+        return as_f((uint32_t)__builtin_amdgcn_mov_dpp((int)as_u(x), decltype(ctrl)::value, 0xF, 0xF, false));
+      };
+      // which of the two exchanged values this lane sums: the swap leaves
+      // either value in either half, so a tag goes through the same exchange
+      const auto t32 = __builtin_amdgcn_permlane32_swap(as_u(0.0f), as_u(1.0f), false, false);
+      const int h32 = as_f(t32[0]) + as_f(t32[1]) > 0.5f;
+      const auto t16 = __builtin_amdgcn_permlane16_swap(as_u(0.0f), as_u(1.0f), false, false);
+      const int h16 = as_f(t16[0]) + as_f(t16[1]) > 0.5f;
+      const bool b3 = (l >> 3) & 1, b2 = (l >> 2) & 1, b1 = (l >> 1) & 1;
+      float kd0 = 0.0f, kd1 = 0.0f;
 #pragma unroll
       for (int bt = 0; bt < NBATCH; ++bt) {
-        if (mine) {
+        float v[32];
 #pragma unroll
-          for (int n = 0; n < 16; ++n) {
-            const int pp = 16 * bt + n;
-            if (pp < NPAIR) {
-              const int i = pair_i(pp), u = pair_u(pp);
-              if (u == i + 1) { d0 = la[u][0]; d1 = la[u][1]; }
-              else { d0 *= la[u][0]; d1 *= la[u][1]; }
-              store2(pD + n * RP + cl, ka[i][0] * d0, ka[i][1] * d1);
-            } else {
-              store2(pD + n * RP + cl, 0.0f, 0.0f);
-            }
-          }
-        }
-        wsync();
-        f32x4 ca = {0, 0, 0, 0}, cp = {0, 0, 0, 0};
-        ca = mma16_rows<MT, CHUNK>(pK, RP, pD, RP, ca, l);
-        cp = mma16_rows<MT, CHUNK>(pQ, RP, pD, RP, cp, l);
-        {
-          const int n = l & 15, pp = 16 * bt + n;
+        for (int n = 0; n < 16; ++n) {
+          const int pp = 16 * bt + n;
           if (pp < NPAIR) {
             const int i = pair_i(pp), u = pair_u(pp);
-            const int m0 = 4 * (l >> 4);
-            if (u >= m0 && u < m0 + 4) {
-              const int e = u - m0;
-              const float va = e == 0 ? ca[0] : e == 1 ? ca[1] : e == 2 ? ca[2] : ca[3];
-              const float vp = e == 0 ? cp[0] : e == 1 ? cp[1] : e == 2 ? cp[2] : cp[3];
-              entry(ps, 16 * w + u, 16 * w + i, va, vp);
-            }
+            if (u == i + 1) { kd0 = ka[i][0] * aa[u][0]; kd1 = ka[i][1] * aa[u][1]; }
+            else { kd0 *= aa[u][0]; kd1 *= aa[u][1]; }
+            v[2 * n] = fmaf(ka[u][0], kd0, ka[u][1] * kd1);
+            v[2 * n + 1] = fmaf(qa[u][0], kd0, qa[u][1] * kd1);
+          } else {
+            v[2 * n] = 0.0f;
+            v[2 * n + 1] = 0.0f;
           }
         }
-        wsync();
+        // value index bit 4 <-> lane halves, bit 3 <-> rows of 16
+        float v1[16], v2[8], v3[4], v4[2];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const auto r = __builtin_amdgcn_permlane32_swap(as_u(v[k]), as_u(v[k + 16]), false, false);
+          v1[k] = as_f(r[0]) + as_f(r[1]);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const auto r = __builtin_amdgcn_permlane16_swap(as_u(v1[k]), as_u(v1[k + 8]), false, false);
+          v2[k] = as_f(r[0]) + as_f(r[1]);
+        }
+        // bits 2, 1, 0 <-> lane bits 3, 2, 1 (partners inside the row)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float keep = b3 ? v2[k + 4] : v2[k], send = b3 ? v2[k] : v2[k + 4];
+          v3[k] = keep + dpp(send, std::integral_constant<int, 0x140>{});
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const float keep = b2 ? v3[k + 2] : v3[k], send = b2 ? v3[k] : v3[k + 2];
+          v4[k] = keep + dpp(send, std::integral_constant<int, 0x141>{});
+        }
+        float tot;
+        {
+          const float keep = b1 ? v4[1] : v4[0], send = b1 ? v4[0] : v4[1];
+          tot = keep + dpp(send, std::integral_constant<int, 0x4E>{});
+        }
+        tot += dpp(tot, std::integral_constant<int, 0xB1>{});
+        // value 2n + ap, n = 8 h32 + 4 h16 + 2 b3 + b2, ap = b1 (0: A, 1: P)
+        if ((l & 1) == 0) {
+          const int pp = 16 * bt + 8 * h32 + 4 * h16 + 2 * b3 + b2;
+          if (pp < NPAIR) {
+            const int ru = 16 * w + pair_u(pp), ri = 16 * w + pair_i(pp);
+            if (b1) gP[LY::pm(ru, ri)] = from_f32<MT>(sRq[ru] * sRk[ri] * tot);
+            else sA[ru * AL + ri] = sBeta[ru] * sRk[ru] * sRk[ri] * tot;
+          }
+        }
       }
     }
+    wsync();
   } else {
     // raw rows for the MFMA work inside the diagonal block (wave-private)
     MT* priv = reinterpret_cast<MT*>(sU + w * L::PRIV_BYTES);

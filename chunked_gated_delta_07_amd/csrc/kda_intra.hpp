@@ -232,6 +232,60 @@ __device__ __forceinline__ void conv16(f32x2 (&x)[16], const f32x2 (&hist)[3], c
   }
 }
 
+// Sums over the 64 lanes of a wave of N (32 or 64) values, each lane holding
+// one partial of every value.  Exchanges between the lane halves
+// (v_permlane32_swap) and between rows of 16 lanes (v_permlane16_swap) halve
+// the values twice; DPP steps inside a row (mirror, half mirror, quad xor 2)
+// halve them further, each pairing lanes that hold the same values so far.
+// Lane l ends with the total of value
+//   N = 64: 32 h32 + 16 h16 + (l & 15)
+//   N = 32: 16 h32 + 8 h16 + ((l & 15) >> 1)   (lanes l and l^1 alike)
+// where h32, h16 (wave_swap_sides) tell which of the two values each swap
+// left in this lane.
+struct SwapSides { int h32, h16; };
+__device__ __forceinline__ uint32_t f2u(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float u2f(uint32_t x) { return __builtin_bit_cast(float, x); }
+__device__ __forceinline__ SwapSides wave_swap_sides() {
+  // a tag goes through the same exchanges as the values
+  const auto t32 = __builtin_amdgcn_permlane32_swap(f2u(0.0f), f2u(1.0f), false, false);
+  const auto t16 = __builtin_amdgcn_permlane16_swap(f2u(0.0f), f2u(1.0f), false, false);
+  return SwapSides{u2f(t32[0]) + u2f(t32[1]) > 0.5f, u2f(t16[0]) + u2f(t16[1]) > 0.5f};
+}
+template <int CTRL> __device__ __forceinline__ float dpp_f(float x) {
+  return u2f((uint32_t)__builtin_amdgcn_mov_dpp((int)f2u(x), CTRL, 0xF, 0xF, false));
+}
+// one DPP halving step: keep value hi (bit set) or lo, add the partner's copy
+template <int CTRL> __device__ __forceinline__ float dpp_halve(float lo, float hi, bool bit) {
+  return (bit ? hi : lo) + dpp_f<CTRL>(bit ? lo : hi);
+}
+template <int N> __device__ __forceinline__ float wave_sum_many(const float (&v)[N], int l) {
+  static_assert(N == 32 || N == 64, "32 or 64 values");
+  constexpr int DPP_MIRROR = 0x140, DPP_HALF_MIRROR = 0x141, DPP_XOR2 = 0x4E, DPP_XOR1 = 0xB1;
+  float v1[N / 2], v2[N / 4], v3[N / 8], v4[N / 16];
+#pragma unroll
+  for (int k = 0; k < N / 2; ++k) {
+    const auto r = __builtin_amdgcn_permlane32_swap(f2u(v[k]), f2u(v[k + N / 2]), false, false);
+    v1[k] = u2f(r[0]) + u2f(r[1]);
+  }
+#pragma unroll
+  for (int k = 0; k < N / 4; ++k) {
+    const auto r = __builtin_amdgcn_permlane16_swap(f2u(v1[k]), f2u(v1[k + N / 4]), false, false);
+    v2[k] = u2f(r[0]) + u2f(r[1]);
+  }
+  const bool b3 = (l >> 3) & 1, b2 = (l >> 2) & 1, b1 = (l >> 1) & 1, b0 = l & 1;
+#pragma unroll
+  for (int k = 0; k < N / 8; ++k) v3[k] = dpp_halve<DPP_MIRROR>(v2[k], v2[k + N / 8], b3);
+#pragma unroll
+  for (int k = 0; k < N / 16; ++k) v4[k] = dpp_halve<DPP_HALF_MIRROR>(v3[k], v3[k + N / 16], b2);
+  if constexpr (N == 64) {
+    const float v5[2] = {dpp_halve<DPP_XOR2>(v4[0], v4[2], b1), dpp_halve<DPP_XOR2>(v4[1], v4[3], b1)};
+    return dpp_halve<DPP_XOR1>(v5[0], v5[1], b0);
+  } else {
+    const float t = dpp_halve<DPP_XOR2>(v4[0], v4[1], b1);
+    return t + dpp_f<DPP_XOR1>(t);
+  }
+}
+
 // Index of cross-block combination (R, I), R > I, in 0..5.
 __device__ __forceinline__ constexpr int combo(int R, int I) { return (R * (R - 1)) / 2 + I; }
 
@@ -350,16 +404,18 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
     if (l < 16) sBeta[16 * w + l] = (16 * w + l < len) ? sigmoid_f(bl) : 0.0f;
   }
   if constexpr (L::NP == 2) {
-    // FP32: every product of the diagonal-block work in two passes over
-    // 64-channel halves.  The first pass parks its raw partial sums in sA (A
-    // entries in place, P entries in the unused upper triangle, transposed);
-    // the second adds its own, applies the norms (complete by then) and writes
-    // the final entries.  Every entry is read back by the lane that parked it.
+    // FP32: the norms, the q.k diagonal and the pairs inside each 8-row half
+    // are channel sums on the VALU (each lane holds two channels of every row
+    // of its wave), summed over the wave; FP32 matrix tiles there would use one
+    // entry in sixteen.  The 8 x 8 cross-half block stays on the matrix cores,
+    // in two passes over 64-channel halves: the first pass parks its raw
+    // partial sums in sA (A entries in place, P entries in the unused upper
+    // triangle, transposed); the second adds its own, applies the norms and
+    // writes the final entries.  Every entry is read back by the lane that
+    // parked it.
     constexpr int RP = L::ROWP;
     MT* priv = reinterpret_cast<MT*>(sU + w * L::PRIV_BYTES);
-    MT* pK = priv;             // rows 0..15
-    MT* pQ = priv + 16 * RP;   // rows 16..31
-    MT* pD = priv + 32 * RP;   // rows 32..47 (pair vectors)
+    MT* pD = priv + 32 * RP;   // rows 32..47 (factor rows of the 8 x 8 block)
     {
       float t0c = 1.0f, t1c = 1.0f;
 #pragma unroll
@@ -387,6 +443,34 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
         gP[LY::pm(ru, ri)] = from_f32<MT>(sRq[ru] * sRk[ri] * vp);
       }
     };
+    // norms (sums of squares) and the plain q.k diagonal on the VALU: 48
+    // channel sums over this wave's rows, value 16 t + row for t = 0 (k.k),
+    // 1 (q.q), 2 (q.k); the raw sums go to sRk, sRq and the diagonal of sA
+    {
+      float v[64];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        v[j] = fmaf(ka[j][0], ka[j][0], ka[j][1] * ka[j][1]);
+        v[16 + j] = fmaf(qa[j][0], qa[j][0], qa[j][1] * qa[j][1]);
+        v[32 + j] = fmaf(qa[j][0], ka[j][0], qa[j][1] * ka[j][1]);
+        v[48 + j] = 0.0f;
+      }
+      const float tot = wave_sum_many<64>(v, l);
+      const SwapSides sd = wave_swap_sides();
+      const int t = 2 * sd.h32 + sd.h16, r = 16 * w + (l & 15);
+      if (t == 0) sRk[r] = tot;
+      else if (t == 1) sRq[r] = tot;
+      else if (t == 2) sA[r * AL + r] = tot;
+      wsync();
+      if (l < 16) {
+        const float rk = rsqrt_hw(sRk[r] + p.eps);
+        const float rq = rsqrt_hw(sRq[r] + p.eps);
+        sRk[r] = rk;
+        sRq[r] = rq;
+        gP[LY::pm(r, r)] = from_f32<MT>(rq * rk * sA[r * AL + r]);  // P[r][r], decay 1
+      }
+      wsync();
+    }
 #pragma unroll
     for (int ps = 0; ps < 2; ++ps) {
       const bool mine = (l >> 5) == ps;
@@ -397,41 +481,6 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
       for (int j = 0; j < 16; ++j) {
         la[j][0] = aa[j][0]; la[j][1] = aa[j][1];
         asm volatile("" : "+v"(la[j][0]), "+v"(la[j][1]));
-      }
-      if (mine) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          store2(pK + j * RP + cl, ka[j][0], ka[j][1]);
-          store2(pQ + j * RP + cl, qa[j][0], qa[j][1]);
-        }
-      }
-      wsync();
-      // norms (sums of squares) and the plain q.k diagonal; the first pass
-      // parks its sums in sRk, sRq and the diagonal of sA
-      {
-        f32x4 ckk = {0, 0, 0, 0}, cqq = {0, 0, 0, 0}, cqk = {0, 0, 0, 0};
-        ckk = mma16_rows<MT, CHUNK>(pK, RP, pK, RP, ckk, l);
-        cqq = mma16_rows<MT, CHUNK>(pQ, RP, pQ, RP, cqq, l);
-        cqk = mma16_rows<MT, CHUNK>(pQ, RP, pK, RP, cqk, l);
-        const int n = l & 15, m0 = 4 * (l >> 4);
-        if (n >= m0 && n < m0 + 4) {
-          const int e = n - m0;
-          const int r = 16 * w + n;
-          const float vkk = e == 0 ? ckk[0] : e == 1 ? ckk[1] : e == 2 ? ckk[2] : ckk[3];
-          const float vqq = e == 0 ? cqq[0] : e == 1 ? cqq[1] : e == 2 ? cqq[2] : cqq[3];
-          const float vqk = e == 0 ? cqk[0] : e == 1 ? cqk[1] : e == 2 ? cqk[2] : cqk[3];
-          if (ps == 0) {
-            sRk[r] = vkk;
-            sRq[r] = vqq;
-            sA[r * AL + r] = vqk;
-          } else {
-            const float rk = rsqrt_hw(sRk[r] + vkk + p.eps);
-            const float rq = rsqrt_hw(sRq[r] + vqq + p.eps);
-            sRk[r] = rk;
-            sRq[r] = rq;
-            gP[LY::pm(r, r)] = from_f32<MT>(rq * rk * (sA[r * AL + r] + vqk));  // P[r][r], decay 1
-          }
-        }
       }
       // diagonal block rows 8..15 x columns 0..7, factorised about row 8:
       // k row factors (rows 8..15) and column factors (rows 0..7), then q row factors
@@ -474,25 +523,11 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
     // Pairs (u, i), i < u, inside each 8-row half: the channel sums on the
     // VALU.  Each lane forms its two channels' share of
     //   A[u][i] ~ k_u . (k_i prod_{i<j<=u} a_j),   P[u][i] ~ q_u . (same),
-    // 16 pairs (32 values) per batch, then the wave sums them: two exchanges
-    // between lane halves and rows halve the values, three DPP steps inside a
-    // row halve them further, and a last one adds lanes l and l^1.  The norms
-    // are complete by now, so the entries are written in their final form.
+    // 16 pairs (32 values) per batch, and the wave sums them.  The norms are
+    // complete by now, so the entries are written in their final form.
     {
-      auto as_u = [](float x) { return __builtin_bit_cast(uint32_t, x); };
-      auto as_f = [](uint32_t x) { return __builtin_bit_cast(float, x); };
-      // partner value through DPP (row_mirror 0x140, row_half_mirror 0x141,
-      // quad_perm xor 2 0x4E, quad_perm xor 1 0xB1)
-      auto dpp = [&](float x, auto ctrl) {
-        return as_f((uint32_t)__builtin_amdgcn_mov_dpp((int)as_u(x), decltype(ctrl)::value, 0xF, 0xF, false));
-      };
-      // which of the two exchanged values this lane sums: the swap leaves
-      // either value in either half, so a tag goes through the same exchange
-      const auto t32 = __builtin_amdgcn_permlane32_swap(as_u(0.0f), as_u(1.0f), false, false);
-      const int h32 = as_f(t32[0]) + as_f(t32[1]) > 0.5f;
-      const auto t16 = __builtin_amdgcn_permlane16_swap(as_u(0.0f), as_u(1.0f), false, false);
-      const int h16 = as_f(t16[0]) + as_f(t16[1]) > 0.5f;
-      const bool b3 = (l >> 3) & 1, b2 = (l >> 2) & 1, b1 = (l >> 1) & 1;
+      const SwapSides sd = wave_swap_sides();
+      const int b3 = (l >> 3) & 1, b2 = (l >> 2) & 1, b1 = (l >> 1) & 1;
       float kd0 = 0.0f, kd1 = 0.0f;
 #pragma unroll
       for (int bt = 0; bt < NBATCH; ++bt) {
@@ -511,38 +546,10 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
             v[2 * n + 1] = 0.0f;
           }
         }
-        // value index bit 4 <-> lane halves, bit 3 <-> rows of 16
-        float v1[16], v2[8], v3[4], v4[2];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          const auto r = __builtin_amdgcn_permlane32_swap(as_u(v[k]), as_u(v[k + 16]), false, false);
-          v1[k] = as_f(r[0]) + as_f(r[1]);
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const auto r = __builtin_amdgcn_permlane16_swap(as_u(v1[k]), as_u(v1[k + 8]), false, false);
-          v2[k] = as_f(r[0]) + as_f(r[1]);
-        }
-        // bits 2, 1, 0 <-> lane bits 3, 2, 1 (partners inside the row)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float keep = b3 ? v2[k + 4] : v2[k], send = b3 ? v2[k] : v2[k + 4];
-          v3[k] = keep + dpp(send, std::integral_constant<int, 0x140>{});
-        }
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const float keep = b2 ? v3[k + 2] : v3[k], send = b2 ? v3[k] : v3[k + 2];
-          v4[k] = keep + dpp(send, std::integral_constant<int, 0x141>{});
-        }
-        float tot;
-        {
-          const float keep = b1 ? v4[1] : v4[0], send = b1 ? v4[0] : v4[1];
-          tot = keep + dpp(send, std::integral_constant<int, 0x4E>{});
-        }
-        tot += dpp(tot, std::integral_constant<int, 0xB1>{});
+        const float tot = wave_sum_many<32>(v, l);
         // value 2n + ap, n = 8 h32 + 4 h16 + 2 b3 + b2, ap = b1 (0: A, 1: P)
         if ((l & 1) == 0) {
-          const int pp = 16 * bt + 8 * h32 + 4 * h16 + 2 * b3 + b2;
+          const int pp = 16 * bt + 8 * sd.h32 + 4 * sd.h16 + 2 * b3 + b2;
           if (pp < NPAIR) {
             const int ru = 16 * w + pair_u(pp), ri = 16 * w + pair_i(pp);
             if (b1) gP[LY::pm(ru, ri)] = from_f32<MT>(sRq[ru] * sRk[ri] * tot);

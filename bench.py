@@ -313,6 +313,49 @@ def time_bwd(args_dev, steps: int, warmup: int):
                          "flop_per_token_head": 2 * FLOP_PER_TH}}
 
 
+def measured_peaks():
+    """What this machine delivers against the datasheet peaks: a timed 1 GiB device
+    copy (2 GiB moved) and the matrix-core microbenchmarks of libkda_peaks."""
+    import torch
+
+    from chunked_gated_delta_07_amd import peaks
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    del src, dst
+    out = {"hbm_copy_gbs": round(2 * n / statistics.median(ts) / 1e9, 1)}
+    out.update(peaks.measure())
+    out["datasheet"] = {"hbm_gbs": HBM_PEAK_GBS, "mfma_bf16_tflops": MFMA_BF16_TFLOPS,
+                        "mfma_fp32_tflops": MFMA_FP32_TFLOPS}
+    out["measured_frac_of_datasheet"] = {
+        "hbm": round(out["hbm_copy_gbs"] / HBM_PEAK_GBS, 4),
+        "mfma_bf16": round(out["mfma_bf16_tflops"] / MFMA_BF16_TFLOPS, 4),
+        "mfma_fp32": round(out["mfma_fp32_tflops"] / MFMA_FP32_TFLOPS, 4)}
+    return out
+
+
+def add_measured_fracs(roof: dict, mp: dict):
+    """The roofline fraction against the measured peak as well (the datasheet
+    one stays in `frac`)."""
+    key = {"GB/s": "hbm_copy_gbs"}.get(roof["unit"])
+    if key is None:
+        key = "mfma_fp32_tflops" if roof["peak"] == MFMA_FP32_TFLOPS else "mfma_bf16_tflops"
+    roof["measured_peak"] = mp[key]
+    roof["frac_of_measured_peak"] = round(roof["achieved"] / mp[key], 4)
+
+
 def roofline_for(mode_name: str, T: int, H: int, res: dict, workload: str):
     """Dominant kernel of the path (by measured time) against its roofline."""
     names = ["chunk_table", "intra", "state_pass"]
@@ -373,6 +416,8 @@ def main():
     ap.add_argument("--no-bwd", action="store_true",
                     help="skip the backward (kda_chunk_bwd) measurement")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured-peak microbenchmarks (HBM copy, matrix cores)")
     ap.add_argument("--only-mode", choices=["bf16", "fp32"], default=None,
                     help="time one precision mode only (for profiling runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -452,6 +497,15 @@ def main():
         line["backward"] = time_bwd(args_dev, max(args.steps // 2, 5), max(args.warmup, 2))
     if not args.no_decode and args.only_mode is None:
         line["decode"] = time_decode(256, H, max(args.steps, 10), max(args.warmup, 2))
+    if not args.no_peaks:
+        mp = measured_peaks()
+        line["measured_peaks"] = mp
+        add_measured_fracs(line["roofline"], mp)
+        for m in modes[1:]:
+            add_measured_fracs(line[f"{m}_mode"]["roofline"], mp)
+        for leg in ("backward", "decode"):
+            if leg in line:
+                add_measured_fracs(line[leg]["roofline"], mp)
     line["context_h200_p50_us"] = H200_CONTEXT_P50_US
     line["kernel_source_hash"] = kernel_source_hash()
     if not args.no_cpu_baseline:

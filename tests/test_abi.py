@@ -152,3 +152,28 @@ def test_workspace_query():
         b = kda.workspace_bytes(1000, N, 8, 128, 0)
         assert b >= prev
         prev = b
+
+
+PEAKS_HEADER = os.path.join(ROOT, "include", "kda_peaks.h")
+PEAKS_LIB = os.path.join(ROOT, "chunked_gated_delta_07_amd", "libkda_peaks.so")
+
+
+@pytest.mark.skipif(not os.path.exists(PEAKS_LIB), reason="libkda_peaks.so not built")
+def test_peaks_exports_and_argument_errors():
+    """The microbenchmark library exports exactly what its header declares and
+    rejects bad arguments before any launch (so this runs without a GPU)."""
+    from chunked_gated_delta_07_amd import peaks
+
+    decl = re.findall(r"KDA_PEAKS_API\s+[\w\s\*]+?\b(kda_\w+)\s*\(", open(PEAKS_HEADER).read())
+    assert decl and set(decl) == set(peaks.SYMBOLS)
+    out = subprocess.check_output(["nm", "-D", "--defined-only", PEAKS_LIB], text=True)
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    assert {n for n in exported if n.startswith("kda_")} == set(decl)
+    lib = peaks.load_library()
+    sink = ctypes.c_void_p(16)  # never dereferenced: the checks fail first
+    assert lib.kda_peaks_probe(9, 10, 1, 64, sink, None) == 1      # unknown kind
+    assert lib.kda_peaks_probe(-1, 10, 1, 64, sink, None) == 1
+    assert lib.kda_peaks_probe(0, 0, 1, 64, sink, None) == 1       # iters < 1
+    assert lib.kda_peaks_probe(0, 10, 0, 64, sink, None) == 1      # blocks < 1
+    assert lib.kda_peaks_probe(0, 10, 1, 100, sink, None) == 1     # threads not 64..512 pow2
+    assert lib.kda_peaks_probe(0, 10, 1, 64, None, None) == 1      # null sink

@@ -6,7 +6,7 @@ import ctypes
 import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda_peaks.so")
-SYMBOLS = ("kda_peaks_probe",)
+SYMBOLS = ("kda_peaks_probe", "kda_peaks_copy")
 MFMA_BF16, MFMA_FP32, CHAIN_BF16, CHAIN_BF16_VALU, VALU = range(5)
 # FLOP per wave and loop iteration of each kind
 FLOP_PER_ITER = {MFMA_BF16: 4 * 32 * 32 * 16 * 2, MFMA_FP32: 4 * 16 * 16 * 4 * 2,
@@ -26,6 +26,9 @@ def load_library(path: str = LIB_PATH):
     lib.kda_peaks_probe.restype = ctypes.c_int
     lib.kda_peaks_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_void_p, ctypes.c_void_p]
+    lib.kda_peaks_copy.restype = ctypes.c_int
+    lib.kda_peaks_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                   ctypes.c_void_p]
     _lib = lib
     return lib
 
@@ -54,6 +57,34 @@ def time_probe(kind: int, iters: int, blocks: int, threads: int, repeats: int = 
     if not bool(torch.isfinite(sink).all()):
         raise RuntimeError("kda_peaks_probe produced non-finite values")
     return statistics.median(times)
+
+
+def copy_gbs(nbytes: int = 1 << 30, blocks: int = 256 * 8, repeats: int = 5) -> float:
+    """HBM GB/s of the streaming copy kernel (2 x nbytes moved per launch, median)."""
+    import statistics
+
+    import torch
+
+    lib = load_library()
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    times = []
+    for r in range(repeats + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        st = lib.kda_peaks_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                nbytes, blocks, sp)
+        e1.record(stream)
+        if st != 0:
+            raise RuntimeError(f"kda_peaks_copy failed with status {st}")
+        torch.cuda.synchronize()
+        if r:
+            times.append(e0.elapsed_time(e1) * 1e-3)
+    if not bool(torch.equal(src[:: 1 << 20], dst[:: 1 << 20])):
+        raise RuntimeError("kda_peaks_copy: copy mismatch")
+    return 2 * nbytes / statistics.median(times) / 1e9
 
 
 def measure(cus: int = 256, iters: int = 20000) -> dict:

@@ -64,6 +64,26 @@ __global__ __launch_bounds__(512) void kda_peaks_kernel(int iters, float* __rest
   sink[(size_t)blockIdx.x * blockDim.x + tid] = out;
 }
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void kda_peaks_copy_kernel(const u32x4* __restrict__ src,
+                                                             u32x4* __restrict__ dst, size_t n) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  // four independent 16-byte loads in flight per thread, then their stores
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const u32x4 a = __builtin_nontemporal_load(src + i);
+    const u32x4 b = __builtin_nontemporal_load(src + i + stride);
+    const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
+    const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
+    __builtin_nontemporal_store(a, dst + i);
+    __builtin_nontemporal_store(b, dst + i + stride);
+    __builtin_nontemporal_store(c, dst + i + 2 * stride);
+    __builtin_nontemporal_store(d, dst + i + 3 * stride);
+  }
+  for (; i < n; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
 template <int KIND>
 int launch(int iters, int blocks, int threads, float* sink, hipStream_t stream) {
   hipLaunchKernelGGL((kda_peaks_kernel<KIND>), dim3((unsigned)blocks), dim3((unsigned)threads), 0,
@@ -86,4 +106,14 @@ extern "C" KDA_PEAKS_API int kda_peaks_probe(int kind, int iters, int blocks, in
     case KDA_PEAK_VALU: return launch<KDA_PEAK_VALU>(iters, blocks, threads, sink, stream);
     default: return 1;
   }
+}
+
+extern "C" KDA_PEAKS_API int kda_peaks_copy(const void* src, void* dst, size_t bytes, int blocks,
+                                            hipStream_t stream) {
+  if (src == nullptr || dst == nullptr || blocks < 1 || bytes % 16 != 0) return 1;
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16 != 0) return 1;
+  if (bytes == 0) return 0;
+  hipLaunchKernelGGL(kda_peaks_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<const u32x4*>(src), reinterpret_cast<u32x4*>(dst), bytes / 16);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
 }

@@ -7,7 +7,7 @@
  * be read against both, and time whether a wave's own vector (VALU) work
  * overlaps its dependent matrix-core products.
  *
- * One entry point.  Asynchronous on `stream`; the caller times it (events on
+ * kda_peaks_probe: asynchronous on `stream`; the caller times it (events on
  * the same stream).  Every thread writes one float of `sink` (a value derived
  * from its results, so the work cannot be removed): sink must hold
  * blocks * threads floats of device memory owned by the caller.
@@ -42,6 +42,15 @@ enum {
 
 KDA_PEAKS_API int kda_peaks_probe(int kind, int iters, int blocks, int threads, float* sink,
                                   hipStream_t stream);
+
+/* Streaming device copy of `bytes` bytes from src to dst (device memory owned
+ * by the caller, not overlapping): 16-byte non-temporal loads and stores, a
+ * grid-stride loop over `blocks` workgroups of 256 threads.  Measures the HBM
+ * bandwidth a plain copy reaches (2 x bytes moved).  Returns 0 on success, 1
+ * if a pointer is null or not 16-byte aligned, bytes is not a multiple of 16
+ * or blocks < 1, 4 for a launch error. */
+KDA_PEAKS_API int kda_peaks_copy(const void* src, void* dst, size_t bytes, int blocks,
+                                 hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -177,3 +177,9 @@ def test_peaks_exports_and_argument_errors():
     assert lib.kda_peaks_probe(0, 10, 0, 64, sink, None) == 1      # blocks < 1
     assert lib.kda_peaks_probe(0, 10, 1, 100, sink, None) == 1     # threads not 64..512 pow2
     assert lib.kda_peaks_probe(0, 10, 1, 64, None, None) == 1      # null sink
+    p16 = ctypes.c_void_p(16)
+    assert lib.kda_peaks_copy(None, p16, 16, 1, None) == 1        # null source
+    assert lib.kda_peaks_copy(p16, ctypes.c_void_p(24), 16, 1, None) == 1  # misaligned
+    assert lib.kda_peaks_copy(p16, p16, 24, 1, None) == 1         # bytes not a multiple of 16
+    assert lib.kda_peaks_copy(p16, p16, 16, 0, None) == 1         # blocks < 1
+    assert lib.kda_peaks_copy(p16, p16, 0, 1, None) == 0          # nothing to copy: no launch

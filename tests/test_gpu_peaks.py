@@ -1,5 +1,5 @@
-"""The matrix-core microbenchmarks run and report plausible figures: measured
-peaks within (20 %, 105 %] of the datasheet ones, per-iteration cycle counts of
+"""The matrix-core microbenchmarks and the streaming copy run and report
+plausible figures: measured peaks within (20 %, 105 %] of the datasheet ones, per-iteration cycle counts of
 the dependent chain and of the VALU block near their issue costs."""
 import pytest
 
@@ -20,3 +20,12 @@ def test_measured_peaks_plausible():
     assert cyc["mfma_chain"] >= 30.0 and cyc["valu_8fma"] >= 30.0
     assert cyc["both"] >= max(cyc["mfma_chain"], cyc["valu_8fma"]) * 0.95
     assert -0.2 <= m["chain_overlap"]["overlap_frac"] <= 1.2
+
+
+def test_streaming_copy_plausible():
+    from chunked_gated_delta_07_amd import peaks
+
+    print("peaks: copy_gbs(256 MiB)", flush=True)
+    gbs = peaks.copy_gbs(1 << 28, repeats=3)
+    print(gbs, flush=True)
+    assert 0.2 * 8000.0 < gbs <= 1.05 * 8000.0

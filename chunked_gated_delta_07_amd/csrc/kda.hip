@@ -89,7 +89,9 @@ static int launch_all(const void* q, const void* k, const void* v, const void* f
   const int64_t C = max_chunks(T, N);
 
   if (ev) (void)hipEventRecord(ev[0], stream);
-  hipLaunchKernelGGL(kda_chunk_table_kernel, dim3(1), dim3(1024), 0, stream, cu, (int)N, cfirst);
+  // a single sequence needs no table: its chunk c starts at token 64 c
+  if (N == 1) cfirst = nullptr;
+  else hipLaunchKernelGGL(kda_chunk_table_kernel, dim3(1), dim3(1024), 0, stream, cu, (int)N, cfirst);
   if (ev) (void)hipEventRecord(ev[1], stream);
 
   IntraArgs ia;

@@ -100,7 +100,7 @@ struct IntraArgs {
   const float* A_log;
   const float* dt_bias;
   const int32_t* cu;
-  const int32_t* cfirst;  // [N+1] first chunk of each sequence; cfirst[N] = chunk count
+  const int32_t* cfirst;  // [N+1] first chunk of each sequence; cfirst[N] = chunk count; null for N = 1
   int N;
   int H;
   float eps;
@@ -121,11 +121,31 @@ struct IntraArgs {
   float* kbr;
 };
 
+// Chunks [cbeg, cend) of sequence n.  A null cfirst means a single sequence
+// (N = 1): its chunks are 0 .. ceil(length / 64) - 1 and no table is built.
+__device__ __forceinline__ void chunk_range(const int32_t* __restrict__ cu,
+                                            const int32_t* __restrict__ cfirst, int n, int& cbeg,
+                                            int& cend) {
+  if (cfirst == nullptr) {
+    cbeg = 0;
+    cend = (cu[1] - cu[0] + CHUNK - 1) / CHUNK;
+  } else {
+    cbeg = cfirst[n];
+    cend = cfirst[n + 1];
+  }
+}
+
 // Chunk c -> (first token, length, first token of its sequence).  cfirst is
-// non-decreasing with cfirst[0]=0.
+// non-decreasing with cfirst[0]=0, or null for a single sequence.
 __device__ __forceinline__ bool locate_chunk(const int32_t* __restrict__ cu,
                                              const int32_t* __restrict__ cfirst, int N, int c,
                                              int& t0, int& len, int& tseq) {
+  if (cfirst == nullptr) {
+    tseq = cu[0];
+    t0 = tseq + c * CHUNK;
+    len = min(CHUNK, cu[1] - t0);
+    return len > 0;
+  }
   if (c >= cfirst[N]) return false;
   int lo = 0, hi = N;  // cfirst[lo] <= c < cfirst[hi]
   while (hi - lo > 1) {

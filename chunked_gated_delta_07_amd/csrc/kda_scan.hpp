@@ -28,7 +28,7 @@ namespace kda {
 
 struct ScanArgs {
   const int32_t* cu;
-  const int32_t* cfirst;
+  const int32_t* cfirst;  // [N+1] first chunk of each sequence, or null for N = 1
   int N;
   int H;
   float scale;
@@ -341,7 +341,8 @@ __global__ __launch_bounds__(512) void kda_scan_ring_kernel(ScanArgs p) {
   scan_unit(blockIdx.x, pair, vb);
   if (pair >= p.N * p.H) return;
   const int n = pair / p.H, h = pair - n * p.H;
-  const int cbeg = p.cfirst[n], cend = p.cfirst[n + 1];
+  int cbeg, cend;
+  chunk_range(p.cu, p.cfirst, n, cbeg, cend);
   const int tseq = p.cu[n], tend = p.cu[n + 1];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int col = l & 31, g = l >> 5;
@@ -647,7 +648,8 @@ __global__ __launch_bounds__(512) void kda_scan_ring32_kernel(ScanArgs p) {
   scan_unit(blockIdx.x, pair, vb);
   if (pair >= p.N * p.H) return;
   const int n = pair / p.H, h = pair - n * p.H;
-  const int cbeg = p.cfirst[n], cend = p.cfirst[n + 1];
+  int cbeg, cend;
+  chunk_range(p.cu, p.cfirst, n, cbeg, cend);
   const int tseq = p.cu[n], tend = p.cu[n + 1];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int col = l & 31, g = l >> 5;

@@ -29,7 +29,8 @@ MFMA_BF16_TFLOPS = 2500.0      # dense
 MFMA_FP32_TFLOPS = 157.3
 H200_CONTEXT_P50_US = {"bf16": 4050.976, "fp32": 7842.400}  # pages' H200 numbers (context only)
 
-# Algorithmic counts per token-head (d = 128, chunk 64), see the design doc.
+# Algorithmic counts per token-head (d = 128, chunk 64): what the method must
+# read and write (its inputs and output) and the products it must form.
 BYTES_IN_PER_TH = lambda s: (4 * 128 + 1) * s    # q, k, v, f_raw, b_raw
 BYTES_OUT_PER_TH = lambda s: 128 * s             # out
 FLOP_PER_TH = 139264                             # 3 d^2 + 1.5 C d + C d MACs, x2

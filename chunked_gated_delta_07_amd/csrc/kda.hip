@@ -87,6 +87,7 @@ static int launch_all(const void* q, const void* k, const void* v, const void* f
   float* gam = reinterpret_cast<float*>(base + W.off_gam);
   void* rec = base + W.off_rec;
   const int64_t C = max_chunks(T, N);
+  if (C * H > 0x7fffffff) return KDA_ERR_UNSUPPORTED;  // one grid dimension of chunks x heads
 
   if (ev) (void)hipEventRecord(ev[0], stream);
   // a single sequence needs no table: its chunk c starts at token 64 c
@@ -101,10 +102,10 @@ static int launch_all(const void* q, const void* k, const void* v, const void* f
   ia.conv_w = conv_w; ia.conv_b = conv_b; ia.conv_silu = conv_silu;
   ia.tmat = nullptr; ia.bw = nullptr; ia.wt = nullptr; ia.kbr = nullptr;
   if (conv_w)
-    hipLaunchKernelGGL((kda_intra_kernel<TA, MT, true>), dim3((unsigned)C, (unsigned)H), dim3(256), 0,
+    hipLaunchKernelGGL((kda_intra_kernel<TA, MT, true>), dim3((unsigned)(C * H)), dim3(256), 0,
                        stream, ia);
   else
-    hipLaunchKernelGGL((kda_intra_kernel<TA, MT, false>), dim3((unsigned)C, (unsigned)H), dim3(256),
+    hipLaunchKernelGGL((kda_intra_kernel<TA, MT, false>), dim3((unsigned)(C * H)), dim3(256),
                        0, stream, ia);
   if (ev) (void)hipEventRecord(ev[2], stream);
 

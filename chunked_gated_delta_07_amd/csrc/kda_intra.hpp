@@ -324,7 +324,20 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
   float* sA = reinterpret_cast<float*>(smem + L::O_A);
   char* sU = smem + L::O_U;
 
-  const int chunk = blockIdx.x, h = blockIdx.y;
+  // Forward: a 1-D grid of chunks x heads, chunk-major with the last chunk
+  // first, so that the records the state pass reads first (every head's first
+  // chunks) are the most recently written ones, still in the memory-side
+  // cache; consecutive workgroups read neighbouring heads of the same tokens.
+  // Backward recomputation: the (chunk, head) grid of the other kernels.
+  int chunk, h;
+  if constexpr (BWD) {
+    chunk = blockIdx.x;
+    h = blockIdx.y;
+  } else {
+    const unsigned nh = (unsigned)p.H;
+    chunk = (int)(gridDim.x / nh) - 1 - (int)(blockIdx.x / nh);
+    h = (int)(blockIdx.x % nh);
+  }
   int t0, len, tseq;
   if (!locate_chunk(p.cu, p.cfirst, p.N, chunk, t0, len, tseq)) return;  // uniform over the block
 

@@ -141,6 +141,29 @@ def test_deterministic_bitwise():
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+def test_single_sequence_without_chunk_table_matches_table_path():
+    """A single sequence is run without the chunk table (chunk c starts at token
+    64 c); the same tokens packed with an empty second sequence take the table
+    path.  Both map chunks to tokens alike, so the outputs and end states must
+    be bitwise equal, in both precision modes, for a ragged length."""
+    import torch
+
+    from chunked_gated_delta_07_amd import kda
+
+    inp = synth.make_inputs([0, 1000], H=8, d=128, act="bf16", seed=31)
+    args = U.to_device(inp, "cuda:0")
+    cu2 = torch.tensor([0, 1000, 1000], dtype=torch.int32, device="cuda:0")
+    for fp32 in (False, True):
+        a, fa = kda.chunk_fwd(*args, fp32_intermediate=fp32, out_fp32=True, return_final_state=True)
+        b, fb = kda.chunk_fwd(*args[:7], cu2, fp32_intermediate=fp32, out_fp32=True,
+                              return_final_state=True)
+        torch.cuda.synchronize()
+        print(f"[no-table vs table] mode={'fp32' if fp32 else 'bf16'}", flush=True)
+        assert torch.equal(a, b)
+        assert torch.equal(fa[0], fb[0])
+        assert torch.count_nonzero(fb[1]) == 0  # the empty sequence's end state = its zero start
+
+
 def test_negative_control_dropped_carry_fails():
     """A planted mistake (state reset every 64 tokens, planted in the oracle on
     the CPU) must be rejected by the same tolerance the real check passes."""

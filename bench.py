@@ -207,7 +207,7 @@ def time_graph(args_dev, fp32: bool, replays: int = 50, warmup: int = 10):
 
     q = args_dev[0]
     T, H, d = q.shape
-    mode = kda.make_mode(fp32, False, False)
+    mode = kda.make_mode(fp32, q.dtype == torch.float32, False)
     ws = torch.empty(kda.workspace_bytes(T, args_dev[7].numel() - 1, H, d, mode),
                      dtype=torch.uint8, device=q.device)
     out = torch.empty((T, H, d), dtype=q.dtype, device=q.device)
@@ -362,28 +362,48 @@ def add_measured_fracs(roof: dict, mp: dict):
 
 
 def roofline_for(mode_name: str, T: int, H: int, res: dict, workload: str):
-    """Dominant kernel of the path (by measured time) against its roofline."""
+    """Dominant kernel of the path (by measured time) against its roofline.
+
+    BF16 intermediates (HBM-bound): achieved = the path's algorithmic bytes
+    (1282 B per token-head: q, k, v, f_raw, b_raw read, out written, bf16)
+    for the T x H token-heads of one launch, over the dominant kernel's average
+    launch time.  FP32 intermediates (matrix-core bound): the dominant kernel's
+    share of the algorithmic FLOP over its launch time, against the peak of
+    the instructions it runs (intra: FP32 matrix cores and VALU, 157.3 TFLOP/s;
+    state pass: six bf16 products per FP32 product, 2500 / 6 TFLOP/s); the
+    whole step against the sum of both kernels' bounds (`path_frac`)."""
     names = ["chunk_table", "intra", "state_pass"]
     st = res["stage_avg_us"]
     dom = max(range(len(st)), key=lambda i: st[i])
     act = 2  # bf16 activations
     th = T * H
-    alg_bytes = {0: 4 * 2, 1: th * BYTES_IN_PER_TH(act), 2: th * BYTES_OUT_PER_TH(act)}[dom]
     t = st[dom] * 1e-6
-    achieved = alg_bytes / t / 1e9
+    path_bytes = th * (BYTES_IN_PER_TH(act) + BYTES_OUT_PER_TH(act))
     if mode_name == "bf16":
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+        achieved = path_bytes / t / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "alg_bytes_per_launch": path_bytes, "alg_bytes_per_token_head": 1282}
+        bound_us = path_bytes / (HBM_PEAK_GBS * 1e9) * 1e6
+        roof["path_bound_us"] = round(bound_us, 1)
+        roof["path_frac"] = round(bound_us / res["p50_us"], 4)
     else:
-        # FP32-intermediate mode is MFMA-FP32 bound: the dominant kernel's share
-        # of the algorithmic FLOP over its launch time, and the whole path's
-        # FLOP over the step time
-        kfl = {0: 0, 1: FLOP_INTRA_PER_TH, 2: FLOP_STATE_PER_TH}[dom] * th / t / 1e12
-        roof = {"bound": "mfma", "achieved": round(kfl, 2), "peak": MFMA_FP32_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(kfl / MFMA_FP32_TFLOPS, 4)}
-        roof["path_mfma_fp32_frac"] = round(th * FLOP_PER_TH / (res["p50_us"] * 1e-6) / 1e12
-                                            / MFMA_FP32_TFLOPS, 4)
-        # the state pass runs its FP32 products as six bf16 matrix-core passes
+        peak_of = {1: MFMA_FP32_TFLOPS, 2: MFMA_BF16_TFLOPS / SPLIT_PASSES}
+        flop_of = {1: FLOP_INTRA_PER_TH, 2: FLOP_STATE_PER_TH}
+        kpeak = peak_of.get(dom, MFMA_FP32_TFLOPS)
+        kfl = flop_of.get(dom, 0) * th / t / 1e12
+        roof = {"bound": "mfma", "achieved": round(kfl, 2), "peak": round(kpeak, 1),
+                "unit": "TFLOP/s", "frac": round(kfl / kpeak, 4),
+                "alg_flop_per_launch": flop_of.get(dom, 0) * th,
+                "alg_flop_per_token_head": flop_of.get(dom, 0)}
+        # split-aware bound of the whole step: each kernel's FLOP at the peak
+        # of the instructions it runs
+        b_intra = FLOP_INTRA_PER_TH * th / (MFMA_FP32_TFLOPS * 1e12) * 1e6
+        b_state = FLOP_STATE_PER_TH * th / (MFMA_BF16_TFLOPS / SPLIT_PASSES * 1e12) * 1e6
+        roof["path_bound_us"] = round(b_intra + b_state, 1)
+        roof["path_bound_parts_us"] = {"intra_fp32": round(b_intra, 1),
+                                       "state_pass_bf16x6": round(b_state, 1)}
+        roof["path_frac"] = round((b_intra + b_state) / res["p50_us"], 4)
         sfl = FLOP_STATE_PER_TH * th / (st[2] * 1e-6) / 1e12
         speak = MFMA_BF16_TFLOPS / SPLIT_PASSES
         roof["state_pass_split"] = {"achieved": round(sfl, 2), "peak": round(speak, 1),
@@ -392,22 +412,100 @@ def roofline_for(mode_name: str, T: int, H: int, res: dict, workload: str):
     roof["kernel"] = names[dom]
     roof["kernel_avg_us"] = round(st[dom], 2)
     roof["traffic"] = load_traffic(names[dom], workload, mode_name)
-    # whole path against the HBM roofline (algorithmic bytes of the method)
-    path_bytes = th * (BYTES_IN_PER_TH(act) + BYTES_OUT_PER_TH(act))
-    path_gbs = path_bytes / (res["p50_us"] * 1e-6) / 1e9
-    roof["path_hbm_frac"] = round(path_gbs / HBM_PEAK_GBS, 4)
-    roof["path_mfma_bf16_frac"] = round(th * FLOP_PER_TH / (res["p50_us"] * 1e-6) / 1e12
-                                        / MFMA_BF16_TFLOPS, 4)
+    roof["traffic_source"] = (
+        f"profiles/counters_{names[dom]}_{workload}_{mode_name}.json: rocprofv3 --pmc FETCH_SIZE "
+        f"and WRITE_SIZE of this kernel, scaled by a device-copy calibration; replayed, not "
+        f"measured in this run, and null when the kernel source differs from the counted one")
     # the path's lower bounds in time (whole step) and the step against the largest
     bounds = {"hbm": path_bytes / (HBM_PEAK_GBS * 1e9) * 1e6,
               "mfma_bf16": th * FLOP_PER_TH / (MFMA_BF16_TFLOPS * 1e12) * 1e6,
-              "mfma_fp32": th * FLOP_PER_TH / (MFMA_FP32_TFLOPS * 1e12) * 1e6,
               "valu_transcendental": th * TRANS_PER_TH / VALU_TRANS_PER_S * 1e6}
-    if mode_name == "bf16":
-        del bounds["mfma_fp32"]
+    if mode_name == "fp32":
+        bounds["mfma_split_aware"] = roof["path_bound_us"]
     roof["path_bounds_us"] = {k: round(v, 1) for k, v in bounds.items()}
     roof["path_frac_vs_max_bound"] = round(max(bounds.values()) / res["p50_us"], 4)
     return roof
+
+
+# The pages' H200 forward p50 (CUDA-graph replay, one sequence), by token
+# count and mode: context, not a target.
+H200_P50_BY_TOKENS = {129: {"bf16": 71.712, "fp32": 112.096},
+                      2048: {"bf16": 550.080, "fp32": 1039.648},
+                      16384: {"bf16": 4050.976, "fp32": 7842.400}}
+
+
+def cpu_oracle_timing(inp, heads, threads=None):
+    """Wall-clock of the FP64 oracle on the given heads of a workload (after
+    one warm-up call on a small piece), scaled to tokens/s at all heads."""
+    import oracle
+
+    f64 = inp.as_f64()
+    sub = {k: (v[:, heads] if k in ("q", "k", "v", "f_raw", "b_raw") else
+               v[heads] if k in ("A_log", "dt_bias") else v) for k, v in f64.items()}
+    full_threads = oracle.num_threads()
+    if threads:
+        oracle.set_num_threads(threads)
+    try:
+        used = oracle.num_threads()
+        t0 = time.perf_counter()
+        oracle.kda_forward(**sub)
+        dt = time.perf_counter() - t0
+    finally:
+        oracle.set_num_threads(full_threads)
+    return {"tokens_per_s": round(inp.T * len(heads) / inp.H / dt, 1), "cores": used,
+            "seconds": round(dt, 3),
+            "sample": f"{inp.T} tokens x {len(heads)} of {inp.H} heads; scaled to {inp.H} heads"}
+
+
+def time_configs(no_cpu: bool):
+    """Every workload of the parity/timing set: HIP-graph replay p50 / max of
+    one kda_chunk_fwd (10 warm-up, 50 timed replays, output in the activation
+    dtype), in each listed precision mode, plus the oracle on the host cores
+    (all cores; configs 0-2 also one core) on a bounded sample of heads."""
+    import numpy as np
+    import torch
+
+    from chunked_gated_delta_07_amd import synth
+
+    dev = torch.device("cuda:0")
+    out = {}
+    for i in range(5):
+        c = synth.CONFIGS[i]
+        inp = synth.config_inputs(i)
+        bf = inp.act == "bf16"
+
+        def t(a, is_act):
+            x = torch.from_numpy(np.ascontiguousarray(a))
+            return (x.view(torch.bfloat16) if (bf and is_act) else x).to(dev)
+
+        args_dev = [t(inp.q, True), t(inp.k, True), t(inp.v, True), t(inp.f_raw, True),
+                    t(inp.b_raw, True), t(inp.A_log, False), t(inp.dt_bias, False),
+                    t(inp.cu_seqlens, False)]
+        N = len(inp.cu_seqlens) - 1
+        lens = np.diff(inp.cu_seqlens)
+        rec = {"workload": c["name"], "tokens": inp.T, "sequences": N,
+               "longest_sequence": int(lens.max()), "activations": inp.act, "modes": {}}
+        for m in c["modes"] if i != 4 else ("bf16", "fp32"):
+            g = time_graph(args_dev, m == "fp32")
+            g["listed_mode"] = m in c["modes"]
+            h200 = H200_P50_BY_TOKENS.get(inp.T, {}).get(m) if N == 1 else None
+            if h200 is not None:
+                g["context_h200_p50_us"] = h200
+            rec["modes"][m] = g
+        del args_dev
+        torch.cuda.empty_cache()
+        if not no_cpu:
+            nh = {0: 64, 1: 64, 2: 16, 3: 4, 4: 4}[i]
+            heads = list(np.linspace(0, inp.H - 1, nh).astype(int))
+            rec["cpu_oracle"] = cpu_oracle_timing(inp, heads)
+            if i <= 2:
+                nh1 = {0: 16, 1: 64, 2: 2}[i]
+                rec["cpu_oracle_one_core"] = cpu_oracle_timing(
+                    inp, list(np.linspace(0, inp.H - 1, nh1).astype(int)), threads=1)
+        out[f"cfg{i}"] = rec
+        print(json.dumps({"config_timed": f"cfg{i}", "modes": {
+            m: v["p50_us"] for m, v in rec["modes"].items()}}), file=sys.stderr, flush=True)
+    return out
 
 
 def main():
@@ -425,6 +523,8 @@ def main():
                     help="skip the measured-peak microbenchmarks (HBM copy, matrix cores)")
     ap.add_argument("--only-mode", choices=["bf16", "fp32"], default=None,
                     help="time one precision mode only (for profiling runs)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-config graph-replay timings (configs 0-4)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="run only a device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -512,6 +612,10 @@ def main():
             if leg in line:
                 add_measured_fracs(line[leg]["roofline"], mp)
     line["context_h200_p50_us"] = H200_CONTEXT_P50_US
+    if not args.no_configs and args.only_mode is None:
+        del args_dev
+        torch.cuda.empty_cache()
+        line["configs"] = time_configs(args.no_cpu_baseline)
     line["kernel_source_hash"] = kernel_source_hash()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(T, args.cpu_budget_s)

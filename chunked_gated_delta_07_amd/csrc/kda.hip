@@ -42,6 +42,12 @@ __global__ __launch_bounds__(1024) void kda_chunk_table_kernel(const int32_t* __
   if (tid == 1023) cfirst[N] = part[1023];
 }
 
+// A dispatch counts each grid dimension in work-items with a 32-bit field:
+// blocks x threads must stay below 2^32 in every dimension.
+static inline bool grid_fits(int64_t blocks, int64_t threads) {
+  return blocks >= 0 && blocks * threads <= (int64_t)UINT32_MAX;
+}
+
 // ------------------------------------------------------------ workspace
 // [cfirst: (N+1) int32, 256-aligned][gam: chunks*H*128 float][rec: chunks*H*REC MT]
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -87,7 +93,6 @@ static int launch_all(const void* q, const void* k, const void* v, const void* f
   float* gam = reinterpret_cast<float*>(base + W.off_gam);
   void* rec = base + W.off_rec;
   const int64_t C = max_chunks(T, N);
-  if (C * H > 0x7fffffff) return KDA_ERR_UNSUPPORTED;  // one grid dimension of chunks x heads
 
   if (ev) (void)hipEventRecord(ev[0], stream);
   // a single sequence needs no table: its chunk c starts at token 64 c
@@ -101,24 +106,25 @@ static int launch_all(const void* q, const void* k, const void* v, const void* f
   ia.N = N; ia.H = H; ia.eps = 1e-6f; ia.gam = gam; ia.rec = rec;
   ia.conv_w = conv_w; ia.conv_b = conv_b; ia.conv_silu = conv_silu;
   ia.tmat = nullptr; ia.bw = nullptr; ia.wt = nullptr; ia.kbr = nullptr;
+  const dim3 gintra((unsigned)H, (unsigned)C);  // heads x chunks (sizes checked by the caller)
   if (conv_w)
-    hipLaunchKernelGGL((kda_intra_kernel<TA, MT, true>), dim3((unsigned)(C * H)), dim3(256), 0,
-                       stream, ia);
+    hipLaunchKernelGGL((kda_intra_kernel<TA, MT, true>), gintra, dim3(256), 0, stream, ia);
   else
-    hipLaunchKernelGGL((kda_intra_kernel<TA, MT, false>), dim3((unsigned)(C * H)), dim3(256),
-                       0, stream, ia);
+    hipLaunchKernelGGL((kda_intra_kernel<TA, MT, false>), gintra, dim3(256), 0, stream, ia);
   if (ev) (void)hipEventRecord(ev[2], stream);
 
   ScanArgs sa;
   sa.cu = cu; sa.cfirst = cfirst; sa.N = N; sa.H = H;
   sa.scale = 0.08838834764831845f;  // 1/sqrt(128)
   sa.gam = gam; sa.rec = rec; sa.out = out; sa.init = init; sa.fin = fin;
+  // 32 workgroups (four value blocks of eight (sequence, head) pairs) per
+  // grid row; workgroup id = x + 32 y
   const int64_t pairs = (int64_t)N * H;
-  const int64_t blocks = 32 * ((pairs + 7) / 8);
+  const dim3 gscan(32, (unsigned)((pairs + 7) / 8));
   if constexpr (sizeof(MT) == 2)
-    hipLaunchKernelGGL((kda_scan_ring_kernel<TO>), dim3((unsigned)blocks), dim3(512), 0, stream, sa);
+    hipLaunchKernelGGL((kda_scan_ring_kernel<TO>), gscan, dim3(512), 0, stream, sa);
   else
-    hipLaunchKernelGGL((kda_scan_ring32_kernel<TO>), dim3((unsigned)blocks), dim3(512), 0, stream, sa);
+    hipLaunchKernelGGL((kda_scan_ring32_kernel<TO>), gscan, dim3(512), 0, stream, sa);
   if (ev) (void)hipEventRecord(ev[3], stream);
   return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
@@ -223,7 +229,7 @@ static int launch_bwd(const void* q, const void* k, const void* v, const void* f
   a.dq = dq; a.dk = dk; a.dv = dv; a.df = df; a.db = db;
   a.dinit = dinit; a.dA_log = dA_log; a.ddt_bias = ddt;
   const int64_t pairs = (int64_t)N * H;
-  const dim3 gscan((unsigned)(32 * ((pairs + 7) / 8)));
+  const dim3 gscan(32, (unsigned)((pairs + 7) / 8));  // workgroup id = x + 32 y
   hipLaunchKernelGGL(kda_bwd_fscan_kernel, gscan, dim3(SCAN_THREADS), 0, stream, a);
   hipLaunchKernelGGL((kda_bwd_bscan_kernel<TG>), gscan, dim3(SCAN_THREADS), 0, stream, a);
   hipLaunchKernelGGL((kda_bwd_jprod_kernel<TG>), gch, dim3(256), 0, stream, a);
@@ -248,6 +254,10 @@ static int check_args(const void* q, const void* k, const void* v, const void* f
   if (!q || !k || !v || !f || !b || !A_log || !dt_bias || !cu || !out || !ws)
     return KDA_ERR_INVALID_ARG;
   if (T > (int64_t)INT32_MAX / 64 || (int64_t)N * H > (int64_t)INT32_MAX / 64)
+    return KDA_ERR_UNSUPPORTED;
+  // grids: intra (H x 256 threads, chunks), state pass (32 x 512, N H / 8)
+  if (!kda::grid_fits(H, 256) || !kda::grid_fits(kda::max_chunks(T, N), 1) ||
+      !kda::grid_fits(((int64_t)N * H + 7) / 8, 1))
     return KDA_ERR_UNSUPPORTED;
   if (ws_bytes < kda::ws_layout(T, N, H, mode).total) return KDA_ERR_WORKSPACE;
   return KDA_OK;
@@ -359,7 +369,10 @@ static int recurrent_impl(const void* q, const void* k, const void* v, const voi
   if (num_seqs < 1 || total_tokens < 0 || H < 1 || dk < 1 || dv < 1) return KDA_ERR_INVALID_ARG;
   if ((dk != 16 && dk != 32 && dk != 64 && dk != 128) || dv > kda::rec_max_threads(dk))
     return KDA_ERR_UNSUPPORTED;
-  if ((int64_t)num_seqs * H > (int64_t)INT32_MAX / 2) return KDA_ERR_UNSUPPORTED;
+  // one workgroup of up to 512 threads per (sequence, head), one grid dimension
+  if ((int64_t)num_seqs * H > (int64_t)INT32_MAX / 2 ||
+      !kda::grid_fits((int64_t)num_seqs * H, 64 * (((dk > dv ? dk : dv) + 63) / 64)))
+    return KDA_ERR_UNSUPPORTED;
   if (total_tokens == 0 && !final_state) return KDA_OK;
   if (total_tokens > 0 && (!q || !k || !v || !f_raw || !b_raw || !A_log || !dt_bias || !out ||
                            !cu_seqlens))
@@ -436,6 +449,10 @@ extern "C" int kda_chunk_bwd(const void* q, const void* k, const void* v, const 
         !dk || !dv || !df_raw || !db_raw || !workspace)
       return KDA_ERR_INVALID_ARG;
     if (total_tokens > (int64_t)INT32_MAX / 64 || (int64_t)num_seqs * H > (int64_t)INT32_MAX / 64)
+      return KDA_ERR_UNSUPPORTED;
+    // grids: (chunks x up to 512 threads, H) per chunk; (32 x 512, N H / 8) scans
+    if (!kda::grid_fits(kda::max_chunks(total_tokens, num_seqs), 512) ||
+        !kda::grid_fits(((int64_t)num_seqs * H + 7) / 8, 1))
       return KDA_ERR_UNSUPPORTED;
     if (workspace_bytes < kda::bwd_layout(total_tokens, num_seqs, H).total)
       return KDA_ERR_WORKSPACE;

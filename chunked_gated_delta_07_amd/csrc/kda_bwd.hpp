@@ -169,7 +169,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_bwd_fscan_kernel(BwdArgs p) 
   __shared__ __attribute__((aligned(16))) float sDT[32 * LS];
   __shared__ __attribute__((aligned(16))) float sGam[DH];
   int pair, vb;
-  scan_block(blockIdx.x, pair, vb);
+  scan_block(blockIdx.x + 32 * blockIdx.y, pair, vb);  // grid (32, pairs / 8)
   if (pair >= p.N * p.H) return;
   const int n = pair / p.H, h = pair - n * p.H;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_bwd_bscan_kernel(BwdArgs p) 
   __shared__ __attribute__((aligned(16))) float sDT[32 * LS];
   __shared__ __attribute__((aligned(16))) float sGam[DH];
   int pair, vb;
-  scan_block(blockIdx.x, pair, vb);
+  scan_block(blockIdx.x + 32 * blockIdx.y, pair, vb);  // grid (32, pairs / 8)
   if (pair >= p.N * p.H) return;
   const int n = pair / p.H, h = pair - n * p.H;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;

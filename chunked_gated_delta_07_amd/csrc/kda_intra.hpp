@@ -324,7 +324,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
   float* sA = reinterpret_cast<float*>(smem + L::O_A);
   char* sU = smem + L::O_U;
 
-  // Forward: a 1-D grid of chunks x heads, chunk-major with the last chunk
+  // Forward: a grid of heads x chunks, chunk-major with the last chunk
   // first, so that the records the state pass reads first (every head's first
   // chunks) are the most recently written ones, still in the memory-side
   // cache; consecutive workgroups read neighbouring heads of the same tokens.
@@ -334,9 +334,9 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
     chunk = blockIdx.x;
     h = blockIdx.y;
   } else {
-    const unsigned nh = (unsigned)p.H;
-    chunk = (int)(gridDim.x / nh) - 1 - (int)(blockIdx.x / nh);
-    h = (int)(blockIdx.x % nh);
+    // grid (H, chunks): x = head, y = chunk counted from the last
+    chunk = (int)gridDim.y - 1 - (int)blockIdx.y;
+    h = (int)blockIdx.x;
   }
   int t0, len, tseq;
   if (!locate_chunk(p.cu, p.cfirst, p.N, chunk, t0, len, tseq)) return;  // uniform over the block

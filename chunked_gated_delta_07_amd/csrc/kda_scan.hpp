@@ -338,7 +338,7 @@ __global__ __launch_bounds__(512) void kda_scan_ring_kernel(ScanArgs p) {
   bf16* sD = reinterpret_cast<bf16*>(smem + L::O_D);
 
   int pair, vb;
-  scan_unit(blockIdx.x, pair, vb);
+  scan_unit(blockIdx.x + 32 * blockIdx.y, pair, vb);  // grid (32, pairs / 8)
   if (pair >= p.N * p.H) return;
   const int n = pair / p.H, h = pair - n * p.H;
   int cbeg, cend;
@@ -645,7 +645,7 @@ __global__ __launch_bounds__(512) void kda_scan_ring32_kernel(ScanArgs p) {
   bf16* sD = reinterpret_cast<bf16*>(smem + L::O_D);
 
   int pair, vb;
-  scan_unit(blockIdx.x, pair, vb);
+  scan_unit(blockIdx.x + 32 * blockIdx.y, pair, vb);  // grid (32, pairs / 8)
   if (pair >= p.N * p.H) return;
   const int n = pair / p.H, h = pair - n * p.H;
   int cbeg, cend;

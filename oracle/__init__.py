@@ -106,6 +106,8 @@ def _load():
                                         dp, dp, dp, dp, dp, dp, dp, dp, dp]
     lib.kda_oracle_num_threads.restype = ctypes.c_int
     lib.kda_oracle_num_threads.argtypes = []
+    lib.kda_oracle_set_num_threads.restype = None
+    lib.kda_oracle_set_num_threads.argtypes = [ctypes.c_int]
     _lib = lib
     return lib
 
@@ -309,3 +311,9 @@ def kda_backward(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, dout, scale=
 
 def num_threads() -> int:
     return int(_load().kda_oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads used by the following oracle calls (timing only: each (sequence,
+    head) pair is computed by one thread, so results do not depend on it)."""
+    _load().kda_oracle_set_num_threads(int(n))

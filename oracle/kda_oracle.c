@@ -699,6 +699,16 @@ int kda_oracle_bwd_rect(const double* q, const double* k, const double* v, const
 }
 
 /* Number of threads the OpenMP runtime will use (reported by the benchmark). */
+/* Thread count for the OpenMP loops that follow (timing only; results do
+ * not depend on it: every (sequence, head) pair is computed by one thread). */
+void kda_oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 int kda_oracle_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -127,6 +127,34 @@ def test_backward_argument_errors_before_launch():
     assert 600e3 < b[-1] / (256 * 64) < 660e3
 
 
+def test_grid_limits_rejected_before_launch():
+    """A dispatch counts each grid dimension in work-items with a 32-bit field.
+    Sizes whose grids would not fit return KDA_ERR_UNSUPPORTED from the host
+    checks, before any HIP call (this runs on a machine without a GPU)."""
+    from chunked_gated_delta_07_amd import kda
+
+    lib = kda.load_library()
+    p = ctypes.c_void_p(16)  # never dereferenced: the checks fail first
+    big = ctypes.c_size_t(-1).value  # any workspace is large enough
+    # forward: the intra grid's head dimension is H x 256 work-items
+    H = (1 << 24) + 1
+    assert lib.kda_chunk_fwd(*([p] * 8), 1, 1, H, 128, 0, p, p, big, None) == \
+        kda.KDA_ERR_UNSUPPORTED
+    # backward: chunks x 512 work-items; 2^24 one-token sequences are 2^24 chunks
+    n = 1 << 24
+    assert lib.kda_chunk_bwd(*([p] * 8), n, n, 1, 128, 1, None, p, None, p, p, p, p, p, p, p, None,
+                             p, big, None) == kda.KDA_ERR_UNSUPPORTED
+    # just inside the limit the same call reaches the workspace check instead
+    n = (1 << 23) - 1
+    assert lib.kda_chunk_bwd(*([p] * 8), n, n, 1, 128, 1, None, p, None, p, p, p, p, p, p, p, None,
+                             p, 1, None) == kda.KDA_ERR_WORKSPACE
+    # token-serial: one workgroup of 64 ceil(max(dk, dv) / 64) threads per (sequence, head)
+    rr = lambda N, dk, dv: lib.kda_recurrent_fwd_rect(*([p] * 8), N, 10, 1, dk, dv, 0, p, None,
+                                                      None, None)
+    assert rr((1 << 23) + 1, 16, 512) == kda.KDA_ERR_UNSUPPORTED
+    assert rr((1 << 25) + 1, 128, 128) == kda.KDA_ERR_UNSUPPORTED
+
+
 def test_workspace_query():
     from chunked_gated_delta_07_amd import kda
 

@@ -1,7 +1,9 @@
 """GPU parity: libkda (through its C ABI) against the FP64 oracle.
 
 Tolerances (whole-tensor relative L2, per-element max abs): FP32-intermediate
-mode <= 1e-4 / <= 1e-3 on a float32 output; BF16-intermediate mode <= 1e-2.
+mode <= 1e-4 / <= 1e-3 on a float32 output; BF16-intermediate mode <= 1e-2,
+checked both on a float32 output and on the bf16 output the benchmark times
+(that output has its own pack-and-store code in the state pass).
 Large workloads are compared on a sample of heads that the oracle computes in
 seconds (heads are independent, so every sampled head is a full-size check).
 """
@@ -31,20 +33,34 @@ def _gpu():
     yield
 
 
-def _check(inp, fp32, heads=None, out_fp32=True, label=""):
-    out = U.out_to_f64(U.run_gpu(inp, fp32, out_fp32))
+def _check(inp, fp32, heads=None, out_fp32=True, label="", bf16_out=None):
+    """GPU output vs the FP64 oracle on the given heads.  ``bf16_out`` (default:
+    in BF16-intermediate mode) also runs the same call with the output cast to
+    bf16 (the benched form of the path) and holds it to the same bar against
+    the unrounded oracle."""
     heads = list(range(inp.H)) if heads is None else list(heads)
     ref = U.oracle_heads(inp, heads)
-    got = out[:, heads]
-    rel, mab = U.rel_l2(got, ref), U.max_abs(got, ref)
-    print(f"[{label}] mode={'fp32' if fp32 else 'bf16'} heads={len(heads)} rel_l2={rel:.3e} "
-          f"max_abs={mab:.3e}", flush=True)
-    assert np.all(np.isfinite(out))
-    if fp32:
-        assert rel <= U.TOL_FP32_REL and mab <= U.TOL_FP32_MAXABS, (rel, mab)
-    else:
-        assert rel <= U.TOL_BF16_REL, rel
-    return out, ref
+    if bf16_out is None:
+        bf16_out = not fp32 and inp.act == "bf16"
+    args = U.to_device(inp, "cuda:0")
+    variants = [out_fp32] + ([False] if bf16_out and out_fp32 else [])
+    result = None
+    for o32 in variants:
+        out = U.out_to_f64(U.run_gpu(inp, fp32, o32, args=args))
+        got = out[:, heads]
+        rel, mab = U.rel_l2(got, ref), U.max_abs(got, ref)
+        print(f"[{label}] mode={'fp32' if fp32 else 'bf16'} out={'fp32' if o32 else 'bf16'} "
+              f"heads={len(heads)} rel_l2={rel:.3e} max_abs={mab:.3e}", flush=True)
+        assert np.all(np.isfinite(out))
+        if fp32 and o32:
+            assert rel <= U.TOL_FP32_REL and mab <= U.TOL_FP32_MAXABS, (rel, mab)
+        else:
+            # BF16 intermediates, or a bf16 output (whose rounding alone costs
+            # ~1.7e-3 relative L2): the BF16 bar
+            assert rel <= U.TOL_BF16_REL, rel
+        if result is None:
+            result = (out, ref)
+    return result
 
 
 def test_cfg0_129_tokens_fp32():
@@ -79,12 +95,13 @@ def test_cfg2_2048_tokens(fp32):
 @pytest.mark.parametrize("fp32", [False, True], ids=["bf16", "fp32"])
 def test_cfg3_16384_tokens_sampled_heads(fp32):
     inp = synth.config_inputs(3)
-    _check(inp, fp32=fp32, heads=[5, 38], label="cfg3")
+    _check(inp, fp32=fp32, heads=[2, 13, 38, 51, 63], label="cfg3")
 
 
-def test_cfg4_ragged_65536_tokens_sampled_heads():
+@pytest.mark.parametrize("fp32", [False, True], ids=["bf16", "fp32"])
+def test_cfg4_ragged_65536_tokens_sampled_heads(fp32):
     inp = synth.config_inputs(4)
-    _check(inp, fp32=True, heads=[17], label="cfg4")
+    _check(inp, fp32=fp32, heads=[4, 17, 42, 63], label="cfg4")
 
 
 @pytest.mark.parametrize("cu", [

@@ -2,6 +2,8 @@
 library through its C ABI, run the oracle on a subset of heads, compare."""
 from __future__ import annotations
 
+import functools
+
 import numpy as np
 
 import oracle
@@ -11,6 +13,14 @@ from chunked_gated_delta_07_amd import synth
 TOL_FP32_REL = 1e-4
 TOL_FP32_MAXABS = 1e-3
 TOL_BF16_REL = 1e-2
+
+
+@functools.lru_cache(maxsize=2)
+def config_inputs(i: int) -> synth.KdaInputs:
+    """synth.config_inputs(i), kept for the next test that asks (the ragged
+    65,536-token batch takes most of a minute to draw).  Callers must not
+    modify the arrays."""
+    return synth.config_inputs(i)
 
 
 def to_device(inp: synth.KdaInputs, dev):

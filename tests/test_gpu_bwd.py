@@ -195,7 +195,7 @@ def test_bwd_headline_size_sampled_heads():
     oracle (heads are independent, so the oracle runs on those two alone)."""
     import torch
 
-    inp = synth.config_inputs(3)
+    inp = U.config_inputs(3)
     T, H = inp.T, inp.H
     rng = np.random.default_rng(77)
     dout = synth.bf16_bits_to_f32(
@@ -220,7 +220,7 @@ def test_bwd_ragged_65536_sampled_head():
     gradients, with the final-state gradient of every sequence."""
     import torch
 
-    inp = synth.config_inputs(4)
+    inp = U.config_inputs(4)
     T, H = inp.T, inp.H
     N = len(inp.cu_seqlens) - 1
     rng = np.random.default_rng(78)

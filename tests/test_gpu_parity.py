@@ -88,19 +88,19 @@ def test_cfg1_fp32_mode_bf16_output():
 
 @pytest.mark.parametrize("fp32", [False, True], ids=["bf16", "fp32"])
 def test_cfg2_2048_tokens(fp32):
-    inp = synth.config_inputs(2)
+    inp = U.config_inputs(2)
     _check(inp, fp32=fp32, heads=[0, 9, 22, 31, 40, 47, 58, 63], label="cfg2")
 
 
 @pytest.mark.parametrize("fp32", [False, True], ids=["bf16", "fp32"])
 def test_cfg3_16384_tokens_sampled_heads(fp32):
-    inp = synth.config_inputs(3)
+    inp = U.config_inputs(3)
     _check(inp, fp32=fp32, heads=[2, 13, 38, 51, 63], label="cfg3")
 
 
 @pytest.mark.parametrize("fp32", [False, True], ids=["bf16", "fp32"])
 def test_cfg4_ragged_65536_tokens_sampled_heads(fp32):
-    inp = synth.config_inputs(4)
+    inp = U.config_inputs(4)
     _check(inp, fp32=fp32, heads=[4, 17, 42, 63], label="cfg4")
 
 
@@ -150,7 +150,7 @@ def test_zero_tokens_is_noop():
 def test_deterministic_bitwise():
     import torch
 
-    inp = synth.config_inputs(2)
+    inp = U.config_inputs(2)
     args = U.to_device(inp, "cuda:0")
     for fp32 in (False, True):
         a = U.run_gpu(inp, fp32, False, args=args)
@@ -184,7 +184,7 @@ def test_single_sequence_without_chunk_table_matches_table_path():
 def test_negative_control_dropped_carry_fails():
     """A planted mistake (state reset every 64 tokens, planted in the oracle on
     the CPU) must be rejected by the same tolerance the real check passes."""
-    inp = synth.config_inputs(2)
+    inp = U.config_inputs(2)
     heads = [0, 9]
     out = U.out_to_f64(U.run_gpu(inp, True, True))[:, heads]
     good = U.oracle_heads(inp, heads)

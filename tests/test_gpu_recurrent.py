@@ -96,7 +96,7 @@ def test_recurrent_agrees_with_chunked_2048_tokens():
 
     from chunked_gated_delta_07_amd import kda
 
-    inp = synth.config_inputs(2)
+    inp = U.config_inputs(2)
     args = U.to_device(inp, "cuda:0")
     o_rec, f_rec = _rec(args, out_fp32=True, return_final_state=True)
     o_chk, f_chk = kda.chunk_fwd(*args, fp32_intermediate=True, out_fp32=True,

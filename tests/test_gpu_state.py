@@ -128,7 +128,7 @@ def test_split_handoff_16384_tokens(fp32):
     against the oracle over the whole sequence."""
     import torch
 
-    inp = synth.config_inputs(3)
+    inp = U.config_inputs(3)
     full = U.to_device(inp, "cuda:0")
     out, fin = _run(full, fp32)
     cut = 5000

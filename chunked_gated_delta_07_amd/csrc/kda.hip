@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/kda.h"
 #include "kda_common.hpp"
 #include "kda_intra.hpp"
@@ -310,6 +312,73 @@ extern "C" int kda_chunk_fwd(const void* q, const void* k, const void* v, const 
   return fwd_impl(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, num_seqs, total_tokens, H, d,
                   mode, out, workspace, workspace_bytes, nullptr, nullptr, nullptr, nullptr, 0, stream,
                   nullptr, 0);
+}
+
+// ------------------------------------------------------------ no-allocation forward
+// The workspace of kda_chunk_fwd_noalloc: a device array of the library's own
+// (every GPU the library runs on holds one until the process ends).  In host
+// code `scratch` names a host-side stand-in, not device memory, so kernels get
+// the address hipGetSymbolAddress returns for the current device instead.
+static __device__ __align__(256) char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // per device, set once
+
+// Device address of `scratch` on device dev (made current for the lookup).
+int scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return KDA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return KDA_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return KDA_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || p == nullptr) return KDA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KDA_OK;
+}
+}  // namespace
+
+extern "C" int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                                     const void* f_raw, const void* b_raw, const float* A_log,
+                                     const float* dt_bias, const int32_t* cu_seqlens,
+                                     int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t d,
+                                     uint32_t mode, void* out, void* stream) {
+  // every size check comes before the first HIP call; a workspace larger than
+  // the library's array is refused
+  const size_t need = kda_chunk_fwd_workspace_bytes(total_tokens, num_seqs, H, d, mode);
+  if (need == (size_t)-1) {
+    if (mode & ~KDA_MODE_ALL_BITS) return KDA_ERR_INVALID_ARG;
+    if (num_seqs < 1 || total_tokens < 0 || H < 1) return KDA_ERR_INVALID_ARG;
+    return KDA_ERR_UNSUPPORTED;
+  }
+  if (need > (size_t)KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE;
+  if (total_tokens == 0)
+    return check_args(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, num_seqs, 0, H, d, mode,
+                      out, nullptr, 0);
+  // argument errors before the device lookup (the workspace is ours and large enough)
+  int st = check_args(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, num_seqs, total_tokens, H,
+                      d, mode, out, reinterpret_cast<void*>(256), (size_t)KDA_NOALLOC_SCRATCH_BYTES);
+  if (st != KDA_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int dev = -1;
+  if (s != nullptr) {
+    if (hipStreamGetDevice(s, &dev) != hipSuccess) return KDA_ERR_HIP;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return KDA_ERR_HIP;
+  }
+  void* ws = nullptr;
+  st = scratch_address(dev, &ws);
+  if (st != KDA_OK) return st;
+  return fwd_impl(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, num_seqs, total_tokens, H, d,
+                  mode, out, ws, (size_t)KDA_NOALLOC_SCRATCH_BYTES, nullptr, nullptr, nullptr,
+                  nullptr, 0, stream, nullptr, 0);
 }
 
 extern "C" int kda_chunk_fwd_state(const void* q, const void* k, const void* v, const void* f_raw,

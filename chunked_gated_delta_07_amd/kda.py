@@ -25,8 +25,11 @@ KDA_OUT_FP32 = 0x4
 # Exported symbols, in declaration order of include/kda.h.
 SYMBOLS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_state",
            "kda_chunk_fwd_conv", "kda_recurrent_fwd", "kda_recurrent_fwd_rect",
-           "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_chunk_fwd_num_stages",
-           "kda_chunk_fwd_timed", "kda_status_string")
+           "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_chunk_fwd_noalloc",
+           "kda_chunk_fwd_num_stages", "kda_chunk_fwd_timed", "kda_status_string")
+
+# Size of the library-owned workspace of kda_chunk_fwd_noalloc (kda.h).
+NOALLOC_SCRATCH_BYTES = 256 << 20
 
 _lib = None
 
@@ -77,6 +80,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_bwd.argtypes = ([vp] * 8 + [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                               ctypes.c_int32, ctypes.c_uint32]
                                   + [vp] * 11 + [vp, ctypes.c_size_t, vp])
+    lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
+    lib.kda_chunk_fwd_noalloc.argtypes = fwd_args[:14] + [vp]
     lib.kda_chunk_fwd_timed.restype = ctypes.c_int
     lib.kda_chunk_fwd_timed.argtypes = fwd_args + [ctypes.POINTER(vp), ctypes.c_int32]
     lib.kda_chunk_fwd_num_stages.restype = ctypes.c_int
@@ -115,7 +120,7 @@ def _ptr(t):
 def chunk_fwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, fp32_intermediate=False,
               out_fp32=False, out=None, workspace=None, stream=None, events=None,
               initial_state=None, final_state=None, return_final_state=False,
-              conv_weight=None, conv_bias=None, conv_silu=True):
+              conv_weight=None, conv_bias=None, conv_silu=True, noalloc=False):
     """KDA chunked forward through libkda.
 
     q, k, v, f_raw: [T, H, 128] bfloat16 or float32 (one dtype for all);
@@ -130,7 +135,10 @@ def chunk_fwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, fp32_intermedia
     kda_chunk_fwd_state and makes the result (out, final_state).
     ``conv_weight`` [3, H, 128, 4] float32 (optional ``conv_bias`` [3, H, 128],
     ``conv_silu``) selects kda_chunk_fwd_conv: the short causal convolution on
-    q, k, v fused in front of the core."""
+    q, k, v fused in front of the core.
+    ``noalloc=True`` selects kda_chunk_fwd_noalloc: no workspace is allocated
+    or passed (the library's own device array serves), for shapes whose
+    workspace fits NOALLOC_SCRATCH_BYTES; pass ``out`` to allocate nothing."""
     import torch
 
     lib = load_library()
@@ -159,12 +167,22 @@ def chunk_fwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, fp32_intermedia
         out = torch.empty((T, H, d), dtype=out_dtype, device=q.device)
     elif out.dtype != out_dtype or out.shape != (T, H, d) or not out.is_contiguous():
         raise ValueError("out has the wrong dtype, shape or layout")
-    nbytes = workspace_bytes(T, max(num_seqs, 1), H, d, mode) if num_seqs >= 1 else 0
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     sp = ctypes.c_void_p(stream.cuda_stream)
+    if noalloc:
+        if (workspace is not None or events is not None or conv_weight is not None
+                or initial_state is not None or final_state is not None or return_final_state):
+            raise ValueError("noalloc takes no workspace, events, states or convolution")
+        st = lib.kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(f_raw), _ptr(b_raw),
+                                       _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens), num_seqs, T,
+                                       H, d, mode, _ptr(out), sp)
+        if st != KDA_OK:
+            raise KdaError(st, "kda_chunk_fwd_noalloc")
+        return out
+    nbytes = workspace_bytes(T, max(num_seqs, 1), H, d, mode) if num_seqs >= 1 else 0
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(f_raw), _ptr(b_raw), _ptr(A_log), _ptr(dt_bias),
             _ptr(cu_seqlens), num_seqs, T, H, d, mode, _ptr(out), _ptr(workspace),
             workspace.numel(), sp)

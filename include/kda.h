@@ -234,6 +234,28 @@ KDA_API int kda_chunk_bwd(const void* q, const void* k, const void* v, const voi
                   void* db_raw, float* dA_log, float* ddt_bias, float* dinitial_state,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* Size of the device array that kda_chunk_fwd_noalloc uses as its workspace
+ * (256 MiB, on every GPU the library runs on, held until the process ends). */
+#define KDA_NOALLOC_SCRATCH_BYTES (256u << 20)
+
+/* kda_chunk_fwd without a workspace argument and without any allocation:
+ * for callers that cannot allocate device memory (code being captured into
+ * a HIP graph, tight serving loops, harnesses that forbid hipMalloc).  The
+ * workspace is a library-owned device array of KDA_NOALLOC_SCRATCH_BYTES per
+ * GPU; shapes whose kda_chunk_fwd_workspace_bytes exceeds it return
+ * KDA_ERR_WORKSPACE before anything is launched (at 64 heads: up to 56 chunks
+ * of 64 tokens with BF16 intermediates, 28 with FP32 intermediates).  Every
+ * byte of the array that a call reads it has written earlier in the same
+ * call, so nothing needs clearing between calls.  Calls that overlap in time
+ * on one GPU (two streams, two host threads) share the one array and race:
+ * serialise them.  The first call on a device looks the array's address up
+ * once (hipGetSymbolAddress); no call allocates or frees memory.
+ * Arguments, results and errors otherwise as for kda_chunk_fwd. */
+KDA_API int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* f_raw,
+                          const void* b_raw, const float* A_log, const float* dt_bias,
+                          const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                          int32_t H, int32_t d, uint32_t mode, void* out, void* stream);
+
 /* Number of kernels kda_chunk_fwd launches for this mode (the stages timed by
  * kda_chunk_fwd_timed). */
 KDA_API int kda_chunk_fwd_num_stages(uint32_t mode);

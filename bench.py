@@ -116,21 +116,33 @@ def copy_calibration(nbytes: int):
     print(json.dumps({"copy_calibration_bytes": nbytes}))
 
 
-def time_mode(args_dev, fp32: bool, steps: int, warmup: int):
+WIN_CHUNKS = 24  # chunks per window of the windowed schedule (libkda)
+
+
+def stage_names(nst: int):
+    """Stages kda_chunk_fwd_timed separates: two passes, or the windowed
+    pipeline (its launches each run the intra-chunk work of one window and the
+    state pass over the window before)."""
+    return ["chunk_table", "intra", "state_pass"] if nst == 3 else ["chunk_table", "windows"]
+
+
+def time_mode(args_dev, fp32: bool, steps: int, warmup: int, windowed: bool = False):
     import torch
 
     from chunked_gated_delta_07_amd import kda
 
     q = args_dev[0]
     T, H, d = q.shape
-    mode = kda.make_mode(fp32, False, False)
-    ws = torch.empty(kda.workspace_bytes(T, args_dev[7].numel() - 1, H, d, mode),
-                     dtype=torch.uint8, device=q.device)
+    N = args_dev[7].numel() - 1
+    mode = kda.make_mode(fp32, False, False, windowed)
+    ws = torch.empty(kda.workspace_bytes(T, N, H, d, mode), dtype=torch.uint8, device=q.device)
     out = torch.empty((T, H, d), dtype=q.dtype, device=q.device)
     stream = torch.cuda.current_stream()
-    nst = kda.num_stages(mode)
+    nst = kda.num_stages(T, N, H, mode)
+    run = lambda ev=None: kda.chunk_fwd(*args_dev, fp32_intermediate=fp32, out=out, workspace=ws,
+                                        events=ev, windowed=windowed)
     for _ in range(warmup):
-        kda.chunk_fwd(*args_dev, fp32_intermediate=fp32, out=out, workspace=ws)
+        run()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(steps)]
     for e in evs:  # create the events outside the timed region
@@ -139,16 +151,21 @@ def time_mode(args_dev, fp32: bool, steps: int, warmup: int):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        kda.chunk_fwd(*args_dev, fp32_intermediate=fp32, out=out, workspace=ws, events=evs[i])
+        run(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per_step_us = [evs[i][0].elapsed_time(evs[i][nst]) * 1e3 for i in range(steps)]
     stage_us = [[evs[i][s].elapsed_time(evs[i][s + 1]) * 1e3 for i in range(steps)] for s in range(nst)]
+    chunks = -(-T // 64)
     return {
         "ms_per_step": wall * 1e3 / steps,
         "p50_us": statistics.median(per_step_us),
         "max_us": max(per_step_us),
         "stage_avg_us": [sum(s) / len(s) for s in stage_us],
+        "stage_names": stage_names(nst),
+        "workspace_bytes": ws.numel(),
+        "launches": ({"windows": -(-chunks // WIN_CHUNKS) + 1} if nst == 2 else
+                     {"intra": 1, "state_pass": 1}),
     }
 
 
@@ -372,9 +389,10 @@ def roofline_for(mode_name: str, T: int, H: int, res: dict, workload: str):
     the instructions it runs (intra: FP32 matrix cores and VALU, 157.3 TFLOP/s;
     state pass: six bf16 products per FP32 product, 2500 / 6 TFLOP/s); the
     whole step against the sum of both kernels' bounds (`path_frac`)."""
-    names = ["chunk_table", "intra", "state_pass"]
+    names = res["stage_names"]
     st = res["stage_avg_us"]
     dom = max(range(len(st)), key=lambda i: st[i])
+    windowed = names[dom] == "windows"
     act = 2  # bf16 activations
     th = T * H
     t = st[dom] * 1e-6
@@ -387,6 +405,13 @@ def roofline_for(mode_name: str, T: int, H: int, res: dict, workload: str):
         bound_us = path_bytes / (HBM_PEAK_GBS * 1e9) * 1e6
         roof["path_bound_us"] = round(bound_us, 1)
         roof["path_frac"] = round(bound_us / res["p50_us"], 4)
+        if windowed:
+            # the window launches carry the whole path (intra-chunk work and
+            # state pass): per launch, its share of the token-heads over the
+            # average launch time, which is the same ratio
+            nl = res["launches"]["windows"]
+            roof["launches"] = nl
+            roof["launch_avg_us"] = round(st[dom] / nl, 2)
     else:
         peak_of = {1: MFMA_FP32_TFLOPS, 2: MFMA_BF16_TFLOPS / SPLIT_PASSES}
         flop_of = {1: FLOP_INTRA_PER_TH, 2: FLOP_STATE_PER_TH}
@@ -404,11 +429,12 @@ def roofline_for(mode_name: str, T: int, H: int, res: dict, workload: str):
         roof["path_bound_parts_us"] = {"intra_fp32": round(b_intra, 1),
                                        "state_pass_bf16x6": round(b_state, 1)}
         roof["path_frac"] = round((b_intra + b_state) / res["p50_us"], 4)
-        sfl = FLOP_STATE_PER_TH * th / (st[2] * 1e-6) / 1e12
+        sfl = FLOP_STATE_PER_TH * th / (st[names.index("state_pass")] * 1e-6) / 1e12
         speak = MFMA_BF16_TFLOPS / SPLIT_PASSES
         roof["state_pass_split"] = {"achieved": round(sfl, 2), "peak": round(speak, 1),
                                     "unit": "TFLOP/s", "frac": round(sfl / speak, 4),
-                                    "passes": SPLIT_PASSES, "kernel_avg_us": round(st[2], 2)}
+                                    "passes": SPLIT_PASSES,
+                                    "kernel_avg_us": round(st[names.index("state_pass")], 2)}
     roof["kernel"] = names[dom]
     roof["kernel_avg_us"] = round(st[dom], 2)
     roof["traffic"] = load_traffic(names[dom], workload, mode_name)
@@ -578,8 +604,8 @@ def main():
                    "global_batch": 1, "parallelism": "none"},
         "p50_us": round(r["p50_us"], 2),
         "max_us": round(r["max_us"], 2),
-        "stage_avg_us": {n: round(x, 2) for n, x in
-                         zip(["chunk_table", "intra", "state_pass"], r["stage_avg_us"])},
+        "stage_avg_us": {n: round(x, 2) for n, x in zip(r["stage_names"], r["stage_avg_us"])},
+        "workspace_bytes": r["workspace_bytes"],
         "roofline": roofline_for(head, T, H, r, cfg["name"]),
     }
     if head in graph:
@@ -590,12 +616,20 @@ def main():
             "value": round(T / (rm["ms_per_step"] * 1e-3), 1), "unit": "tokens/s",
             "ms_per_step": round(rm["ms_per_step"], 4), "p50_us": round(rm["p50_us"], 2),
             "max_us": round(rm["max_us"], 2),
-            "stage_avg_us": {n: round(x, 2) for n, x in
-                             zip(["chunk_table", "intra", "state_pass"], rm["stage_avg_us"])},
+            "stage_avg_us": {n: round(x, 2) for n, x in zip(rm["stage_names"], rm["stage_avg_us"])},
+            "workspace_bytes": rm["workspace_bytes"],
             "roofline": roofline_for(m, T, H, rm, cfg["name"]),
         }
         if m in graph:
             line[f"{m}_mode"]["graph_replay"] = graph[m]
+    if args.only_mode in (None, "bf16"):
+        # the same BF16-intermediate arithmetic in the windowed schedule
+        # (KDA_MODE_WINDOWED: workspace independent of the length)
+        tp = time_mode(args_dev, False, args.steps, args.warmup, windowed=True)
+        line["bf16_windowed"] = {
+            "value": round(T / (tp["ms_per_step"] * 1e-3), 1), "unit": "tokens/s",
+            "p50_us": round(tp["p50_us"], 2), "workspace_bytes": tp["workspace_bytes"],
+            "stage_avg_us": {n: round(x, 2) for n, x in zip(tp["stage_names"], tp["stage_avg_us"])}}
     if args.only_mode is None:
         line["conv_fused"] = time_conv(args_dev, max(args.steps, 10), max(args.warmup, 2))
     if not args.no_bwd and args.only_mode is None:

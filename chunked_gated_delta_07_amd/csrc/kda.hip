@@ -9,6 +9,7 @@
 #include "kda_common.hpp"
 #include "kda_intra.hpp"
 #include "kda_scan.hpp"
+#include "kda_window.hpp"
 #include "kda_recurrent.hpp"
 #include "kda_bwd.hpp"
 
@@ -61,18 +62,35 @@ static inline int64_t max_chunks(int64_t T, int64_t N) {
   return (T + 63 * ne) / 64;
 }
 
+// The windowed schedule (kda_window.hpp) when asked for, with BF16
+// intermediates and at most WIN_MAX_SEQS sequences (the state-pass role of a
+// window has one grid row per sequence); otherwise two passes.
+static inline bool use_windows(int32_t N, uint32_t mode) {
+  return (mode & KDA_MODE_WINDOWED) && !(mode & KDA_MODE_FP32_INTERMEDIATE) && N <= WIN_MAX_SEQS;
+}
+
+// Record slots: every chunk (two passes), or a ring of two windows.
+static inline int64_t ring_chunks(int64_t T, int32_t N) {
+  const int64_t C = max_chunks(T, N);
+  return C < 2 * WIN_CHUNKS ? C : 2 * WIN_CHUNKS;
+}
+
 struct WsLayout {
-  size_t off_cfirst, off_gam, off_rec, total;
+  size_t off_cfirst, off_gam, off_rec, off_carry, total;
 };
 
+// two passes: [cfirst][gam: chunks x H x 128 f32][rec: chunks x H x REC]
+// windowed:   [cfirst][gam: ring x H x 128 f32][rec: ring x H x RECW bf16][carry: 2 x H x 128 x 128 f32]
 static inline WsLayout ws_layout(int64_t T, int32_t N, int32_t H, uint32_t mode) {
   const size_t mt = (mode & KDA_MODE_FP32_INTERMEDIATE) ? 4 : 2;
-  const int64_t C = max_chunks(T, N);
+  const bool win = use_windows(N, mode);
+  const int64_t C = win ? ring_chunks(T, N) : max_chunks(T, N);
   WsLayout L;
   L.off_cfirst = 0;
   L.off_gam = align256(sizeof(int32_t) * (size_t)(N + 1));
   L.off_rec = L.off_gam + align256(sizeof(float) * (size_t)C * H * DH);
-  L.total = L.off_rec + align256(mt * (size_t)C * H * REC);
+  L.off_carry = L.off_rec + align256(mt * (size_t)C * H * (win ? RECW : REC));
+  L.total = L.off_carry + (win ? align256(sizeof(float) * 2 * (size_t)H * DH * DH) : 0);
   return L;
 }
 
@@ -107,7 +125,7 @@ static int launch_all(const void* q, const void* k, const void* v, const void* f
   ia.A_log = A_log; ia.dt_bias = dt_bias; ia.cu = cu; ia.cfirst = cfirst;
   ia.N = N; ia.H = H; ia.eps = 1e-6f; ia.gam = gam; ia.rec = rec;
   ia.conv_w = conv_w; ia.conv_b = conv_b; ia.conv_silu = conv_silu;
-  ia.tmat = nullptr; ia.bw = nullptr; ia.wt = nullptr; ia.kbr = nullptr;
+  ia.tmat = nullptr; ia.bw = nullptr; ia.wt = nullptr; ia.kbr = nullptr; ia.ring = 0;
   const dim3 gintra((unsigned)H, (unsigned)C);  // heads x chunks (sizes checked by the caller)
   if (conv_w)
     hipLaunchKernelGGL((kda_intra_kernel<TA, MT, true>), gintra, dim3(256), 0, stream, ia);
@@ -131,6 +149,59 @@ static int launch_all(const void* q, const void* k, const void* v, const void* f
   return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+// The windowed forward: the chunk table, then launch k = 0 .. nwin of
+// kda_window_kernel (intra work of window k, state pass over window k-1).
+template <typename TA, typename TO>
+static int launch_windows(const void* q, const void* k, const void* v, const void* f, const void* b,
+                          const float* A_log, const float* dt_bias, const int32_t* cu, int32_t N,
+                          int64_t T, int32_t H, uint32_t mode, void* out, void* ws,
+                          const float* init, float* fin, const float* conv_w, const float* conv_b,
+                          int conv_silu, hipStream_t stream, hipEvent_t const* ev) {
+  const WsLayout L = ws_layout(T, N, H, mode);
+  char* base = reinterpret_cast<char*>(ws);
+  int32_t* cfirst = reinterpret_cast<int32_t*>(base + L.off_cfirst);
+  const int64_t C = max_chunks(T, N);  // upper bound; the kernels know the real count
+  const int W = WIN_CHUNKS;
+  const int64_t nwin = (C + W - 1) / W;
+
+  if (ev) (void)hipEventRecord(ev[0], stream);
+  if (N == 1) cfirst = nullptr;
+  else hipLaunchKernelGGL(kda_chunk_table_kernel, dim3(1), dim3(1024), 0, stream, cu, (int)N, cfirst);
+  if (ev) (void)hipEventRecord(ev[1], stream);
+
+  WinArgs wa;
+  IntraArgs& ia = wa.ia;
+  ia.q = q; ia.k = k; ia.v = v; ia.f = f; ia.b = b;
+  ia.A_log = A_log; ia.dt_bias = dt_bias; ia.cu = cu; ia.cfirst = cfirst;
+  ia.N = N; ia.H = H; ia.eps = 1e-6f;
+  ia.gam = reinterpret_cast<float*>(base + L.off_gam);
+  ia.rec = base + L.off_rec;
+  ia.ring = (int)ring_chunks(T, N);
+  ia.conv_w = conv_w; ia.conv_b = conv_b; ia.conv_silu = conv_silu;
+  ia.tmat = nullptr; ia.bw = nullptr; ia.wt = nullptr; ia.kbr = nullptr;
+  wa.nseg = N; wa.W = W;
+  wa.cu = cu; wa.cfirst = cfirst; wa.N = N; wa.H = H;
+  wa.scale = 0.08838834764831845f;  // 1/sqrt(128)
+  wa.gam = ia.gam;
+  wa.rec = reinterpret_cast<const bf16*>(ia.rec);
+  wa.ring = ia.ring;
+  wa.out = out; wa.init = init; wa.fin = fin;
+  wa.carry = reinterpret_cast<float*>(base + L.off_carry);
+  for (int64_t kw = 0; kw <= nwin; ++kw) {
+    wa.scan_win = kw >= 1 ? (int)(kw - 1) : -1;
+    wa.intra_c0 = kw < nwin ? (int)(kw * W) : -1;
+    const unsigned rows = (unsigned)((kw >= 1 ? N : 0) + (kw < nwin ? W : 0));
+    if (conv_w)
+      hipLaunchKernelGGL((kda_window_kernel<TA, TO, true>), dim3((unsigned)H, rows), dim3(256), 0,
+                         stream, wa);
+    else
+      hipLaunchKernelGGL((kda_window_kernel<TA, TO, false>), dim3((unsigned)H, rows), dim3(256), 0,
+                         stream, wa);
+  }
+  if (ev) (void)hipEventRecord(ev[2], stream);
+  return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 static int dispatch(const void* q, const void* k, const void* v, const void* f, const void* b,
                     const float* A_log, const float* dt_bias, const int32_t* cu, int32_t N,
                     int64_t T, int32_t H, uint32_t mode, void* out, void* ws, const float* init,
@@ -139,6 +210,15 @@ static int dispatch(const void* q, const void* k, const void* v, const void* f, 
   const bool f32i = mode & KDA_MODE_FP32_INTERMEDIATE;
   const bool a32 = mode & KDA_ACT_FP32;
   const bool o32 = (mode & KDA_OUT_FP32) || a32;
+  if (use_windows(N, mode)) {
+#define KDA_WIN(TA, TO)                                                                             \
+  return launch_windows<TA, TO>(q, k, v, f, b, A_log, dt_bias, cu, N, T, H, mode, out, ws, init, \
+                                fin, conv_w, conv_b, conv_silu, s, ev)
+    if (a32) KDA_WIN(float, float);
+    if (o32) KDA_WIN(bf16, float);
+    KDA_WIN(bf16, bf16);
+#undef KDA_WIN
+  }
 #define KDA_GO(TA, MT, TO) \
   return launch_all<TA, MT, TO>(q, k, v, f, b, A_log, dt_bias, cu, N, T, H, mode, out, ws, init, \
                                 fin, conv_w, conv_b, conv_silu, s, ev)
@@ -210,7 +290,7 @@ static int launch_bwd(const void* q, const void* k, const void* v, const void* f
   ia.A_log = A_log; ia.dt_bias = dt_bias; ia.cu = cu; ia.cfirst = cfirst;
   ia.N = N; ia.H = H; ia.eps = 1e-6f; ia.gam = fp(L.off_gam); ia.rec = fp(L.off_rec);
   ia.conv_w = nullptr; ia.conv_b = nullptr; ia.conv_silu = 0;
-  ia.tmat = fp(L.off_t); ia.bw = fp(L.off_bw); ia.wt = fp(L.off_wt); ia.kbr = fp(L.off_kbr);
+  ia.tmat = fp(L.off_t); ia.bw = fp(L.off_bw); ia.wt = fp(L.off_wt); ia.kbr = fp(L.off_kbr); ia.ring = 0;
   const dim3 gch((unsigned)C, (unsigned)H);
   hipLaunchKernelGGL((kda_intra_kernel<TA, float, false, PlainRec<float>, true>), gch, dim3(256), 0,
                      stream, ia);
@@ -273,9 +353,12 @@ extern "C" size_t kda_chunk_fwd_workspace_bytes(int64_t total_tokens, int32_t nu
   return kda::ws_layout(total_tokens, num_seqs, H, mode).total;
 }
 
-extern "C" int kda_chunk_fwd_num_stages(uint32_t mode) {
-  (void)mode;
-  return 3;
+extern "C" int kda_chunk_fwd_num_stages(int64_t total_tokens, int32_t num_seqs, int32_t H,
+                                        uint32_t mode) {
+  (void)total_tokens;
+  (void)H;
+  if ((mode & ~KDA_MODE_ALL_BITS) || num_seqs < 1) return -1;
+  return kda::use_windows(num_seqs, mode) ? 2 : 3;
 }
 
 static int fwd_impl(const void* q, const void* k, const void* v, const void* f_raw, const void* b_raw,
@@ -294,7 +377,7 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* f_r
                        reinterpret_cast<hipStream_t>(stream), init, fin, n);
     return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
   }
-  if (events && num_events != kda_chunk_fwd_num_stages(mode) + 1) return KDA_ERR_INVALID_ARG;
+  if (events && num_events != kda_chunk_fwd_num_stages(T, N, H, mode) + 1) return KDA_ERR_INVALID_ARG;
   if (events)
     for (int i = 0; i < num_events; ++i)
       if (!events[i]) return KDA_ERR_INVALID_ARG;

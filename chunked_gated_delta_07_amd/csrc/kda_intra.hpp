@@ -54,6 +54,8 @@ constexpr int REC = 4 * CHUNK * DH + CHUNK * CHUNK;
 template <typename MT> struct Frag {
   static constexpr int FE = 16 / (int)sizeof(MT);
   static constexpr bool TRANSPOSED_QT_P = false;
+  static constexpr bool P_LOWER_TILES = false;  // P stored whole (see FragW)
+  static constexpr int REC_ELEMS = REC;
   // W / Qt element (token r, key channel c): A operand of [W;Qt] S0, contracted
   // over key channels, half g = c/64.
   __host__ __device__ static constexpr int a(int r, int c) {
@@ -84,11 +86,58 @@ template <typename MT> struct Frag {
 template <typename MT> struct PlainRec {
   static constexpr int FE = 16 / (int)sizeof(MT);
   static constexpr bool TRANSPOSED_QT_P = true;
+  static constexpr bool P_LOWER_TILES = false;
+  static constexpr int REC_ELEMS = REC;
   __host__ __device__ static constexpr int a(int r, int c) { return r * DH + c; }
   __host__ __device__ static constexpr int qt(int r, int c) { return c * CHUNK + r; }
   __host__ __device__ static constexpr int kb(int c, int t) { return c * CHUNK + t; }
   __host__ __device__ static constexpr int pm(int r, int i) { return i * CHUNK + r; }
   __host__ __device__ static constexpr int u(int t, int v) { return v * CHUNK + t; }
+};
+
+// The record in the order of the windowed state pass (kda_window.hpp), bf16
+// only.  There every matrix is a 32x32x16 bf16 MFMA operand fragment read by
+// one wave: 64 lanes x 8 elements, 1 KB contiguous.  The contracted index is
+// permuted inside each step of 16: lane group g (lanes 32g..32g+31) element p
+// holds index kappa(g, p) = 4g + (p & 3) + 8 (p >> 2).  With that order the
+// rows held by one lane of a 32x32 accumulator (rows 8j + 4g + i of lane
+// group g) are, two j at a time, exactly one operand fragment, so the state
+// and the corrected values D feed the next products straight from their
+// accumulators.  Fragments:
+//   W, Qt  (token r, key c):    (key step c/16, token tile r/32), lane r%32 + 32 g
+//   Kb^T   (key c, token t):    (token step t/16, key tile c/32), lane c%32 + 32 g
+//   P      (row r, column i):   only the tiles on or below the diagonal at
+//                               32-token granularity: (0,0) (0,1) (1,0) .. (1,3)
+//   U      (token t, value v):  accumulator order, 16 values per lane:
+//                               (value block v/32, token tile t/32), lane v%32 + 32 g
+//                               element 4 (m/8) + m%4, m = t%32, g = (m/4)%2
+constexpr int OFFW_P = 4 * CHUNK * DH;  // = OFF_P
+constexpr int RECW = 4 * CHUNK * DH + 6 * 512;  // 35,840 elements
+template <typename MT> struct FragW {
+  static_assert(sizeof(MT) == 2, "bf16 records only");
+  static constexpr int FE = 8;
+  static constexpr bool TRANSPOSED_QT_P = false;
+  static constexpr bool P_LOWER_TILES = true;
+  static constexpr int REC_ELEMS = RECW;
+  // element p of lane group g for contracted index k (within its step of 16)
+  __host__ __device__ static constexpr int kg(int k) { return (k >> 2) & 1; }
+  __host__ __device__ static constexpr int kp(int k) { return 4 * ((k & 15) >> 3) + (k & 3); }
+  __host__ __device__ static constexpr int a(int r, int c) {
+    return (((c >> 4) * 2 + (r >> 5)) * 64 + (r & 31) + 32 * kg(c)) * 8 + kp(c);
+  }
+  __host__ __device__ static constexpr int qt(int r, int c) { return a(r, c); }
+  __host__ __device__ static constexpr int kb(int c, int t) {
+    return (((t >> 4) * 4 + (c >> 5)) * 64 + (c & 31) + 32 * kg(t)) * 8 + kp(t);
+  }
+  // P (row r, column i), i < 32 (r / 32 + 1); the record holds these only.
+  // Offset inside the P region, which starts at OFF_P (= OFFW_P).
+  __host__ __device__ static constexpr int pm(int r, int i) {
+    return ((((r >> 5) == 0 ? 0 : 2) + (i >> 4)) * 64 + (r & 31) + 32 * kg(i)) * 8 + kp(i);
+  }
+  __host__ __device__ static constexpr int u(int t, int v) {
+    return ((((v >> 5) * 2 + (t >> 5)) * 64 + (v & 31) + 32 * (((t & 31) >> 2) & 1)) * 16 +
+            4 * ((t & 31) >> 3) + (t & 3));
+  }
 };
 
 struct IntraArgs {
@@ -105,7 +154,8 @@ struct IntraArgs {
   int H;
   float eps;
   float* gam;  // [chunks][H][128]
-  void* rec;   // [chunks][H][REC] of MT
+  void* rec;   // [chunks][H][LY::REC_ELEMS] of MT (or [ring][H][..])
+  int ring;    // > 0: records and gam of chunk c live in slot c % ring
   // optional short causal convolution on q, k, v (used when the kernel's
   // CONV parameter is set): weights [3][H*128][4] (tap 3 = current token),
   // bias [3][H*128] or null, SiLU after it when conv_silu != 0
@@ -309,13 +359,13 @@ template <int N> __device__ __forceinline__ float wave_sum_many(const float (&v)
 // Index of cross-block combination (R, I), R > I, in 0..5.
 __device__ __forceinline__ constexpr int combo(int R, int I) { return (R * (R - 1)) / 2 + I; }
 
-// LY: record layout (Frag for the forward's state pass, PlainRec for the
-// backward).  BWD: also store T and the W product's right-hand operand.
-template <typename TA, typename MT, bool CONV, typename LY = Frag<MT>, bool BWD = false>
-__global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
+// The work of one (chunk, head): a workgroup of 256 threads; smem is the
+// workgroup's LDS buffer of IntraLds<MT>::BYTES bytes, 16-byte aligned.
+// Template parameters as for kda_intra_kernel below.
+template <typename TA, typename MT, bool CONV, typename LY, bool BWD>
+__device__ __forceinline__ void intra_chunk(const IntraArgs& p, int chunk, int h, char* smem) {
   typedef IntraLds<MT> L;
   constexpr int ROWL = L::ROWL, TL = L::TL, AL = L::AL;
-  __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
   float* sBeta = reinterpret_cast<float*>(smem + L::O_BETA);
   float* sRk = reinterpret_cast<float*>(smem + L::O_RK);
   float* sRq = reinterpret_cast<float*>(smem + L::O_RQ);
@@ -324,20 +374,6 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
   float* sA = reinterpret_cast<float*>(smem + L::O_A);
   char* sU = smem + L::O_U;
 
-  // Forward: a grid of heads x chunks, chunk-major with the last chunk
-  // first, so that the records the state pass reads first (every head's first
-  // chunks) are the most recently written ones, still in the memory-side
-  // cache; consecutive workgroups read neighbouring heads of the same tokens.
-  // Backward recomputation: the (chunk, head) grid of the other kernels.
-  int chunk, h;
-  if constexpr (BWD) {
-    chunk = blockIdx.x;
-    h = blockIdx.y;
-  } else {
-    // grid (H, chunks): x = head, y = chunk counted from the last
-    chunk = (int)gridDim.y - 1 - (int)blockIdx.y;
-    h = (int)blockIdx.x;
-  }
   int t0, len, tseq;
   if (!locate_chunk(p.cu, p.cfirst, p.N, chunk, t0, len, tseq)) return;  // uniform over the block
 
@@ -349,7 +385,9 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
   const TA* __restrict__ gv = reinterpret_cast<const TA*>(p.v);
   const TA* __restrict__ gf = reinterpret_cast<const TA*>(p.f);
   const TA* __restrict__ gb = reinterpret_cast<const TA*>(p.b);
-  const size_t rec_off = ((size_t)chunk * H + h) * REC;
+  // record slot: chunk modulo the ring length when the records live in a ring
+  const int slot = p.ring > 0 ? chunk % p.ring : chunk;
+  const size_t rec_off = ((size_t)slot * H + h) * LY::REC_ELEMS;
   MT* __restrict__ gW = reinterpret_cast<MT*>(p.rec) + rec_off + OFF_W;
   MT* __restrict__ gQt = reinterpret_cast<MT*>(p.rec) + rec_off + OFF_QT;
   MT* __restrict__ gKbT = reinterpret_cast<MT*>(p.rec) + rec_off + OFF_KBT;
@@ -773,7 +811,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
       float g0 = 1.0f, g1 = 1.0f;
 #pragma unroll
       for (int x = 0; x < 4; ++x) { g0 *= sTot[x * DH + c0]; g1 *= sTot[x * DH + c0 + 1]; }
-      *reinterpret_cast<f32x2*>(p.gam + ((size_t)chunk * H + h) * DH + c0) = f32x2{g0, g1};
+      *reinterpret_cast<f32x2*>(p.gam + ((size_t)slot * H + h) * DH + c0) = f32x2{g0, g1};
     }
   }
   // Cross-block operands.  A-side (rows of block R = w >= 1, reference = the
@@ -912,6 +950,12 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
   if constexpr (LY::TRANSPOSED_QT_P) {
     for (int f = tid; f < CHUNK * CHUNK; f += 256) {
       const int r = f & 63, i = f >> 6;  // consecutive threads: consecutive addresses
+      if (i > r) gP[LY::pm(r, i)] = from_f32<MT>(0.0f);
+    }
+  } else if constexpr (LY::P_LOWER_TILES) {
+    // only the stored tiles: the upper part of the two diagonal 32 x 32 tiles
+    for (int f = tid; f < 2 * 32 * 32; f += 256) {
+      const int r = 32 * (f >> 10) + ((f >> 5) & 31), i = 32 * (f >> 10) + (f & 31);
       if (i > r) gP[LY::pm(r, i)] = from_f32<MT>(0.0f);
     }
   } else {
@@ -1135,6 +1179,24 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
     }
     if (ps + 1 < NP) __syncthreads();
   }
+}
+
+// LY: record layout (Frag for the two-pass forward's state pass, FragW for the
+// windowed one, PlainRec for the backward).  BWD: also store T and the W
+// product's right-hand operand.
+//   Forward: a grid of heads x chunks, chunk-major with the last chunk first,
+//   so that the records the state pass reads first (every head's first
+//   chunks) are the most recently written ones, still in the memory-side
+//   cache; consecutive workgroups read neighbouring heads of the same tokens.
+//   Backward recomputation: the (chunk, head) grid of the other kernels.
+template <typename TA, typename MT, bool CONV, typename LY = Frag<MT>, bool BWD = false>
+__global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
+  __shared__ __attribute__((aligned(16))) char smem[IntraLds<MT>::BYTES];
+  if constexpr (BWD)
+    intra_chunk<TA, MT, CONV, LY, BWD>(p, (int)blockIdx.x, (int)blockIdx.y, smem);
+  else  // grid (H, chunks): x = head, y = chunk counted from the last
+    intra_chunk<TA, MT, CONV, LY, BWD>(p, (int)gridDim.y - 1 - (int)blockIdx.y, (int)blockIdx.x,
+                                       smem);
 }
 
 }  // namespace kda

@@ -21,6 +21,7 @@ KDA_ERR_HIP = 4
 KDA_MODE_FP32_INTERMEDIATE = 0x1
 KDA_ACT_FP32 = 0x2
 KDA_OUT_FP32 = 0x4
+KDA_MODE_WINDOWED = 0x8
 
 # Exported symbols, in declaration order of include/kda.h.
 SYMBOLS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_state",
@@ -85,7 +86,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd_timed.restype = ctypes.c_int
     lib.kda_chunk_fwd_timed.argtypes = fwd_args + [ctypes.POINTER(vp), ctypes.c_int32]
     lib.kda_chunk_fwd_num_stages.restype = ctypes.c_int
-    lib.kda_chunk_fwd_num_stages.argtypes = [ctypes.c_uint32]
+    lib.kda_chunk_fwd_num_stages.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_uint32]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_status_string.argtypes = [ctypes.c_int]
     _lib = lib
@@ -104,13 +106,19 @@ def workspace_bytes(total_tokens: int, num_seqs: int, H: int, d: int, mode: int)
     return int(n)
 
 
-def num_stages(mode: int) -> int:
-    return int(load_library().kda_chunk_fwd_num_stages(int(mode)))
+def num_stages(total_tokens: int, num_seqs: int, H: int, mode: int) -> int:
+    n = int(load_library().kda_chunk_fwd_num_stages(int(total_tokens), int(num_seqs), int(H),
+                                                    int(mode)))
+    if n < 0:
+        raise KdaError(KDA_ERR_INVALID_ARG, "kda_chunk_fwd_num_stages")
+    return n
 
 
-def make_mode(fp32_intermediate: bool, act_fp32: bool = False, out_fp32: bool = False) -> int:
+def make_mode(fp32_intermediate: bool, act_fp32: bool = False, out_fp32: bool = False,
+              windowed: bool = False) -> int:
     return ((KDA_MODE_FP32_INTERMEDIATE if fp32_intermediate else 0)
-            | (KDA_ACT_FP32 if act_fp32 else 0) | (KDA_OUT_FP32 if out_fp32 else 0))
+            | (KDA_ACT_FP32 if act_fp32 else 0) | (KDA_OUT_FP32 if out_fp32 else 0)
+            | (KDA_MODE_WINDOWED if windowed else 0))
 
 
 def _ptr(t):
@@ -120,15 +128,18 @@ def _ptr(t):
 def chunk_fwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, fp32_intermediate=False,
               out_fp32=False, out=None, workspace=None, stream=None, events=None,
               initial_state=None, final_state=None, return_final_state=False,
-              conv_weight=None, conv_bias=None, conv_silu=True, noalloc=False):
+              conv_weight=None, conv_bias=None, conv_silu=True, noalloc=False,
+              windowed=False):
     """KDA chunked forward through libkda.
 
     q, k, v, f_raw: [T, H, 128] bfloat16 or float32 (one dtype for all);
     b_raw: [T, H] same dtype; A_log: [H] float32; dt_bias: [H, 128] float32;
     cu_seqlens: [N+1] int32.  All CUDA (HIP) tensors, contiguous.  Returns
     out [T, H, 128] (activation dtype, or float32 when out_fp32).
-    ``events``: optional list of num_stages(mode)+1 torch.cuda.Event objects
-    recorded between the kernels (kda_chunk_fwd_timed).
+    ``events``: optional list of num_stages(T, N, H, mode)+1 torch.cuda.Event
+    objects recorded between the stages (kda_chunk_fwd_timed).
+    ``windowed=True`` sets KDA_MODE_WINDOWED (schedule only: the pipeline of
+    24-chunk windows whose workspace does not grow with the length).
     ``initial_state``: optional [N, H, 128, 128] float32 start states (key,
     value); ``final_state`` (a tensor of that shape to fill, may be the
     initial_state tensor) or ``return_final_state=True`` (allocated) selects
@@ -161,7 +172,7 @@ def chunk_fwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, fp32_intermedia
     if b_raw.shape != (T, H) or A_log.shape != (H,) or dt_bias.shape != (H, d):
         raise ValueError("b_raw [T,H], A_log [H], dt_bias [H,d] expected")
     num_seqs = cu_seqlens.numel() - 1
-    mode = make_mode(fp32_intermediate, act_fp32, out_fp32)
+    mode = make_mode(fp32_intermediate, act_fp32, out_fp32, windowed)
     out_dtype = torch.float32 if (out_fp32 or act_fp32) else q.dtype
     if out is None:
         out = torch.empty((T, H, d), dtype=out_dtype, device=q.device)

@@ -71,16 +71,30 @@ extern "C" {
  *   the running state are FP32.
  * KDA_ACT_FP32: activation dtype of q, k, v, f_raw, b_raw: 0 = bfloat16,
  *   1 = float32.
- * KDA_OUT_FP32: dtype of out: 0 = the activation dtype, 1 = float32. */
+ * KDA_OUT_FP32: dtype of out: 0 = the activation dtype, 1 = float32.
+ * KDA_MODE_WINDOWED: schedule only, same arithmetic.  By default the
+ *   forward makes two passes over every chunk (intra-chunk kernel, then state
+ *   pass), with a record per chunk and head in the workspace.  With this bit,
+ *   BF16 intermediates and at most 64 sequences it runs as a pipeline of
+ *   windows of 24 chunks instead: each launch does the intra-chunk work of one
+ *   window and the state pass over the window before, and the records live in
+ *   a ring of two windows, so the workspace stops growing with the sequence
+ *   length (230 MB instead of 1.2 GB at 16384 tokens x 64 heads).  Ignored
+ *   with FP32 intermediates or more than 64 sequences. */
 #define KDA_MODE_FP32_INTERMEDIATE 0x1u
 #define KDA_ACT_FP32 0x2u
 #define KDA_OUT_FP32 0x4u
-#define KDA_MODE_ALL_BITS 0x7u
+#define KDA_MODE_WINDOWED 0x8u
+#define KDA_MODE_ALL_BITS 0xFu
 
 /* Bytes of caller-provided scratch that kda_chunk_fwd needs for this shape.
- * Depends only on the arguments; monotone non-decreasing in total_tokens and
- * num_seqs.  Returns 0 when total_tokens == 0, and (size_t)-1 when the
- * arguments are invalid (negative sizes, d != 128, unknown mode bits). */
+ * Depends only on the arguments; non-decreasing in total_tokens.  Two
+ * passes need about 74 KB (BF16) or 148 KB (FP32) per 64-token chunk and
+ * head.  The windowed schedule (KDA_MODE_WINDOWED with BF16 intermediates and
+ * at most 64 sequences) stops growing at 48 chunks: about 3.6 MB per head
+ * (the BF16 records of two 24-chunk windows and two 64 KB boundary states).  Returns 0 when total_tokens == 0, and
+ * (size_t)-1 when the arguments are invalid (negative sizes, d != 128,
+ * unknown mode bits). */
 KDA_API size_t kda_chunk_fwd_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t d,
                                      uint32_t mode);
 
@@ -243,8 +257,10 @@ KDA_API int kda_chunk_bwd(const void* q, const void* k, const void* v, const voi
  * a HIP graph, tight serving loops, harnesses that forbid hipMalloc).  The
  * workspace is a library-owned device array of KDA_NOALLOC_SCRATCH_BYTES per
  * GPU; shapes whose kda_chunk_fwd_workspace_bytes exceeds it return
- * KDA_ERR_WORKSPACE before anything is launched (at 64 heads: up to 56 chunks
- * of 64 tokens with BF16 intermediates, 28 with FP32 intermediates).  Every
+ * KDA_ERR_WORKSPACE before anything is launched.  With KDA_MODE_WINDOWED
+ * (BF16 intermediates, at most 64 sequences) that is any length up to 74
+ * heads; two passes fit up to 56 chunks of 64 tokens at 64 heads with BF16
+ * intermediates and 28 with FP32 intermediates.  Every
  * byte of the array that a call reads it has written earlier in the same
  * call, so nothing needs clearing between calls.  Calls that overlap in time
  * on one GPU (two streams, two host threads) share the one array and race:
@@ -256,13 +272,18 @@ KDA_API int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, c
                           const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
                           int32_t H, int32_t d, uint32_t mode, void* out, void* stream);
 
-/* Number of kernels kda_chunk_fwd launches for this mode (the stages timed by
- * kda_chunk_fwd_timed). */
-KDA_API int kda_chunk_fwd_num_stages(uint32_t mode);
+/* Number of stages kda_chunk_fwd_timed separates for this shape and mode:
+ * 3 for two passes (chunk table, intra-chunk kernel, state pass), 2 for the
+ * windowed schedule (chunk table, all window launches); -1 for invalid
+ * arguments.  The chunk table is launched only when num_seqs > 1 (the stage
+ * is then empty). */
+KDA_API int kda_chunk_fwd_num_stages(int64_t total_tokens, int32_t num_seqs, int32_t H,
+                                     uint32_t mode);
 
 /* Same as kda_chunk_fwd, and additionally records events[i] (hipEvent_t,
  * created by the caller) on `stream` before stage i and events[n] after the
- * last stage, n = kda_chunk_fwd_num_stages(mode); num_events must be n + 1.
+ * last stage, n = kda_chunk_fwd_num_stages(total_tokens, num_seqs, H, mode);
+ * num_events must be n + 1.
  * Used by the benchmark to time each kernel on the stream it runs on. */
 KDA_API int kda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void* f_raw,
                         const void* b_raw, const float* A_log, const float* dt_bias,

@@ -59,14 +59,18 @@ def test_argument_errors_before_launch():
     assert _call(lib, H=0) == kda.KDA_ERR_INVALID_ARG                 # H < 1
     assert _call(lib, N=0) == kda.KDA_ERR_INVALID_ARG                 # num_seqs < 1
     assert _call(lib, T=-1) == kda.KDA_ERR_INVALID_ARG                # negative T
-    assert _call(lib, mode=0x8) == kda.KDA_ERR_INVALID_ARG            # unknown mode bit
+    assert _call(lib, mode=0x10) == kda.KDA_ERR_INVALID_ARG           # unknown mode bit
     assert _call(lib, d=64) == kda.KDA_ERR_UNSUPPORTED                # d != 128
     assert _call(lib, ws_bytes=1) == kda.KDA_ERR_WORKSPACE            # workspace too small
     assert _call(lib, T=0, ptrs=False) == kda.KDA_OK                  # empty batch: no-op
     # timed variant needs n+1 non-null events
     p = ctypes.c_void_p(16)
     ev = (ctypes.c_void_p * 2)(None, None)
-    n = kda.num_stages(0)
+    n = kda.num_stages(10, 1, 4, 0)
+    W = kda.KDA_MODE_WINDOWED
+    assert n == 3 and kda.num_stages(10, 1, 4, W) == 2
+    assert kda.num_stages(10, 1, 4, W | kda.KDA_MODE_FP32_INTERMEDIATE) == 3
+    assert kda.num_stages(10, 65, 4, W) == 3  # many sequences: two passes
     assert lib.kda_chunk_fwd_timed(p, p, p, p, p, p, p, p, 1, 10, 4, 128, 0, p, p, 1 << 40, None,
                                    ev, 2) == kda.KDA_ERR_INVALID_ARG
     assert n >= 1
@@ -114,7 +118,7 @@ def test_backward_argument_errors_before_launch():
     assert bw(N=0) == kda.KDA_ERR_INVALID_ARG
     assert bw(H=0) == kda.KDA_ERR_INVALID_ARG
     assert bw(T=-1) == kda.KDA_ERR_INVALID_ARG
-    assert bw(mode=0x8) == kda.KDA_ERR_INVALID_ARG
+    assert bw(mode=0x10) == kda.KDA_ERR_INVALID_ARG
     assert bw(d=64) == kda.KDA_ERR_UNSUPPORTED
     assert bw(ws=1) == kda.KDA_ERR_WORKSPACE
     assert bw(T=0, par=None) == kda.KDA_ERR_INVALID_ARG  # still required for an empty batch
@@ -169,8 +173,13 @@ def test_workspace_query():
             if N > T:
                 continue
             b = kda.workspace_bytes(T, N, 64, 128, 0)
+            bw = kda.workspace_bytes(T, N, 64, 128, kda.KDA_MODE_WINDOWED)
             b32 = kda.workspace_bytes(T, N, 64, 128, 1)
-            assert b > 0 and b32 > b and b % 256 == 0
+            assert b > 0 and bw > 0 and b32 > b and b % 256 == 0 and bw % 256 == 0
+    # the windowed schedule keeps a ring of two 24-chunk windows: its workspace
+    # stops growing with the sequence length
+    w = [kda.workspace_bytes(T, 1, 64, 128, kda.KDA_MODE_WINDOWED) for T in (48 * 64, 16384, 1 << 20)]
+    assert w[0] == w[1] == w[2] < kda.workspace_bytes(16384, 1, 64, 128, 0)
     for T in range(1, 400, 7):
         b = kda.workspace_bytes(T, 3, 8, 128, 0)
         assert b >= prev

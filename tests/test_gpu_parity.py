@@ -247,3 +247,76 @@ def test_intra_records_match_chunk_oracle():
         rel = U.rel_l2(got.astype(np.float64), ref)
         print(f"[records] {name}: rel_l2={rel:.3e}", flush=True)
         assert rel < 1e-5, (name, rel)
+
+
+@pytest.mark.parametrize("cu", [[0, 3000], [0, 1700, 1700, 1701, 4000, 4100]],
+                         ids=["one_seq_3000", "packed_with_empty"])
+def test_windowed_and_two_pass_schedules(cu):
+    """BF16 intermediates run as two passes by default and as a pipeline of
+    24-chunk windows with KDA_MODE_WINDOWED: both against the oracle, with
+    start and end states, on sequences that cross window boundaries (the
+    windowed state pass hands the state over between launches), an empty
+    sequence and a one-token sequence."""
+    import torch
+
+    from chunked_gated_delta_07_amd import kda
+
+    inp = synth.make_inputs(cu, H=6, d=128, act="bf16", seed=61)
+    args = U.to_device(inp, "cuda:0")
+    N = len(cu) - 1
+    S0 = (0.3 * np.random.default_rng(62).standard_normal((N, 6, 128, 128))).astype(np.float32)
+    ref, fin_ref = oracle.kda_forward(**inp.as_f64(), initial_state=S0.astype(np.float64),
+                                      return_final_state=True)
+    S0d = torch.from_numpy(S0).to("cuda:0")
+    assert kda.num_stages(inp.T, N, 6, kda.KDA_MODE_WINDOWED) == 2
+    outs = {}
+    for windowed in (True, False):
+        for o32 in (True, False):
+            o, f = kda.chunk_fwd(*args, out_fp32=o32, initial_state=S0d, return_final_state=True,
+                                 windowed=windowed)
+            torch.cuda.synchronize()
+            o = U.out_to_f64(o)
+            f = f.double().cpu().numpy()
+            ro, rf = U.rel_l2(o, ref), U.rel_l2(f, fin_ref)
+            print(f"[schedules {cu}] windowed={windowed} out={'fp32' if o32 else 'bf16'} "
+                  f"out rel_l2={ro:.3e} final rel_l2={rf:.3e}", flush=True)
+            assert ro <= U.TOL_BF16_REL and rf <= U.TOL_BF16_REL
+            outs[(windowed, o32)] = o
+    # the schedules share the arithmetic up to summation order
+    assert U.rel_l2(outs[(True, True)], outs[(False, True)]) <= 2e-3
+
+
+@pytest.mark.parametrize("fp32", [False, True], ids=["bf16", "fp32"])
+def test_windowed_headline_and_conv(fp32):
+    """The windowed schedule at the headline size (16384 tokens x 64 heads,
+    sampled heads against the oracle) and with the fused convolution; with
+    FP32 intermediates the bit is ignored (two passes, bitwise the default)."""
+    import torch
+
+    from chunked_gated_delta_07_amd import kda
+
+    inp = U.config_inputs(3)
+    args = U.to_device(inp, "cuda:0")
+    heads = [3, 60]
+    a = kda.chunk_fwd(*args, fp32_intermediate=fp32, out_fp32=True, windowed=True)
+    b = kda.chunk_fwd(*args, fp32_intermediate=fp32, out_fp32=True)
+    torch.cuda.synchronize()
+    if fp32:
+        assert torch.equal(a, b)
+        return
+    ref = U.oracle_heads(inp, heads)
+    got = U.out_to_f64(a)[:, heads]
+    rel = U.rel_l2(got, ref)
+    print(f"[windowed 16384x64] rel_l2={rel:.3e} vs two passes "
+          f"{U.rel_l2(U.out_to_f64(a), U.out_to_f64(b)):.3e}", flush=True)
+    assert rel <= U.TOL_BF16_REL
+    # convolution fused into the windowed intra role: same as the two passes
+    g = torch.Generator().manual_seed(63)
+    w = (0.5 * torch.randn((3, 64, 128, 4), generator=g)).to("cuda:0")
+    cb = (0.1 * torch.randn((3, 64, 128), generator=g)).to("cuda:0")
+    sub = [x[:3000].contiguous() for x in args[:5]] + list(args[5:7]) + [
+        torch.tensor([0, 3000], dtype=torch.int32, device="cuda:0")]
+    cw = kda.chunk_fwd(*sub, out_fp32=True, conv_weight=w, conv_bias=cb, windowed=True)
+    c2 = kda.chunk_fwd(*sub, out_fp32=True, conv_weight=w, conv_bias=cb)
+    torch.cuda.synchronize()
+    assert U.rel_l2(U.out_to_f64(cw), U.out_to_f64(c2)) <= 2e-3

@@ -37,22 +37,27 @@ def test_noalloc_matches_workspace_entry_point(fp32, out_fp32):
 
     from chunked_gated_delta_07_amd import kda
 
-    # a larger call, then a smaller one with a different packing
-    cases = [([0, 700, 1500, 1792], 32, 41), ([0, 37, 65, 300], 8, 42)]
-    for cu, H, seed in cases:
+    # a larger call, then a smaller one with a different packing; the
+    # windowed schedule's workspace does not grow with the length, so with it
+    # the 16384-token, 64-head shape fits too
+    cases = [([0, 700, 1500, 1792], 32, 41, False), ([0, 37, 65, 300], 8, 42, False)]
+    if not fp32:
+        cases = [([0, 16384], 64, 43, True), ([0, 700, 1500, 1792], 32, 41, True)] + cases
+    for cu, H, seed, win in cases:
         inp = synth.make_inputs(cu, H=H, d=128, act="bf16", seed=seed)
         args = U.to_device(inp, "cuda:0")
         T = inp.T
-        mode = kda.make_mode(fp32, False, out_fp32)
+        mode = kda.make_mode(fp32, False, out_fp32, win)
         assert kda.workspace_bytes(T, len(cu) - 1, H, 128, mode) <= kda.NOALLOC_SCRATCH_BYTES
         odt = torch.float32 if out_fp32 else torch.bfloat16
-        ref = kda.chunk_fwd(*args, fp32_intermediate=fp32, out_fp32=out_fp32)
+        ref = kda.chunk_fwd(*args, fp32_intermediate=fp32, out_fp32=out_fp32, windowed=win)
         # poison the output buffer: every element must be written
         got = torch.full((T, H, 128), float("nan"), dtype=odt, device="cuda:0")
-        kda.chunk_fwd(*args, fp32_intermediate=fp32, out_fp32=out_fp32, out=got, noalloc=True)
+        kda.chunk_fwd(*args, fp32_intermediate=fp32, out_fp32=out_fp32, out=got, noalloc=True,
+                      windowed=win)
         torch.cuda.synchronize()
         print(f"[noalloc] cu={cu} H={H} mode={'fp32' if fp32 else 'bf16'} "
-              f"out={'fp32' if out_fp32 else 'bf16'}", flush=True)
+              f"out={'fp32' if out_fp32 else 'bf16'} windowed={win}", flush=True)
         assert torch.equal(ref.view(torch.int16) if not out_fp32 else ref.view(torch.int32),
                            got.view(torch.int16) if not out_fp32 else got.view(torch.int32))
         # and against the oracle on a few heads, at the mode's bar
@@ -71,9 +76,14 @@ def test_noalloc_rejects_shapes_beyond_its_array():
     lib = kda.load_library()
     p = ctypes.c_void_p(16)  # never dereferenced: the size check fails first
     T = 16384
+    m32 = kda.KDA_MODE_FP32_INTERMEDIATE  # two passes: records for every chunk
+    assert kda.workspace_bytes(T, 1, 64, 128, m32) > kda.NOALLOC_SCRATCH_BYTES
+    assert lib.kda_chunk_fwd_noalloc(*([p] * 8), 1, T, 64, 128, m32, p, None) == \
+        kda.KDA_ERR_WORKSPACE
     assert kda.workspace_bytes(T, 1, 64, 128, 0) > kda.NOALLOC_SCRATCH_BYTES
     assert lib.kda_chunk_fwd_noalloc(*([p] * 8), 1, T, 64, 128, 0, p, None) == \
         kda.KDA_ERR_WORKSPACE
+    assert kda.workspace_bytes(T, 1, 64, 128, kda.KDA_MODE_WINDOWED) <= kda.NOALLOC_SCRATCH_BYTES
     assert lib.kda_chunk_fwd_noalloc(*([p] * 8), 1, 10, 64, 96, 0, p, None) == \
         kda.KDA_ERR_UNSUPPORTED
     assert lib.kda_chunk_fwd_noalloc(*([p] * 8), 0, 10, 64, 128, 0, p, None) == \

@@ -101,12 +101,13 @@ __global__ __launch_bounds__(256) void kda_state_copy_kernel(const float* __rest
     fin[i] = init ? init[i] : 0.0f;
 }
 
-template <typename TA, typename MT, typename TO>
+template <typename TA, typename MT, typename TO, bool RECT = false>
 static int launch_all(const void* q, const void* k, const void* v, const void* f, const void* b,
                       const float* A_log, const float* dt_bias, const int32_t* cu, int32_t N,
                       int64_t T, int32_t H, uint32_t mode, void* out, void* ws,
                       const float* init, float* fin, const float* conv_w, const float* conv_b,
-                      int conv_silu, hipStream_t stream, hipEvent_t const* ev) {
+                      int conv_silu, hipStream_t stream, hipEvent_t const* ev, int dk = DH,
+                      int dv = DH) {
   const WsLayout W = ws_layout(T, N, H, mode);
   char* base = reinterpret_cast<char*>(ws);
   int32_t* cfirst = reinterpret_cast<int32_t*>(base + W.off_cfirst);
@@ -126,8 +127,12 @@ static int launch_all(const void* q, const void* k, const void* v, const void* f
   ia.N = N; ia.H = H; ia.eps = 1e-6f; ia.gam = gam; ia.rec = rec;
   ia.conv_w = conv_w; ia.conv_b = conv_b; ia.conv_silu = conv_silu;
   ia.tmat = nullptr; ia.bw = nullptr; ia.wt = nullptr; ia.kbr = nullptr; ia.ring = 0;
+  ia.dk = dk; ia.dv = dv;
   const dim3 gintra((unsigned)H, (unsigned)C);  // heads x chunks (sizes checked by the caller)
-  if (conv_w)
+  if constexpr (RECT)
+    hipLaunchKernelGGL((kda_intra_kernel<TA, MT, false, Frag<MT>, false, true>), gintra, dim3(256),
+                       0, stream, ia);
+  else if (conv_w)
     hipLaunchKernelGGL((kda_intra_kernel<TA, MT, true>), gintra, dim3(256), 0, stream, ia);
   else
     hipLaunchKernelGGL((kda_intra_kernel<TA, MT, false>), gintra, dim3(256), 0, stream, ia);
@@ -135,16 +140,17 @@ static int launch_all(const void* q, const void* k, const void* v, const void* f
 
   ScanArgs sa;
   sa.cu = cu; sa.cfirst = cfirst; sa.N = N; sa.H = H;
-  sa.scale = 0.08838834764831845f;  // 1/sqrt(128)
+  sa.scale = (float)(1.0 / sqrt((double)dk));  // 1/sqrt(d_k), correctly rounded
   sa.gam = gam; sa.rec = rec; sa.out = out; sa.init = init; sa.fin = fin;
+  sa.dk = dk; sa.dv = dv;
   // 32 workgroups (four value blocks of eight (sequence, head) pairs) per
   // grid row; workgroup id = x + 32 y
   const int64_t pairs = (int64_t)N * H;
   const dim3 gscan(32, (unsigned)((pairs + 7) / 8));
   if constexpr (sizeof(MT) == 2)
-    hipLaunchKernelGGL((kda_scan_ring_kernel<TO>), gscan, dim3(512), 0, stream, sa);
+    hipLaunchKernelGGL((kda_scan_ring_kernel<TO, RECT>), gscan, dim3(512), 0, stream, sa);
   else
-    hipLaunchKernelGGL((kda_scan_ring32_kernel<TO>), gscan, dim3(512), 0, stream, sa);
+    hipLaunchKernelGGL((kda_scan_ring32_kernel<TO, RECT>), gscan, dim3(512), 0, stream, sa);
   if (ev) (void)hipEventRecord(ev[3], stream);
   return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
@@ -485,6 +491,50 @@ extern "C" int kda_chunk_fwd_timed(const void* q, const void* k, const void* v, 
   return fwd_impl(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, num_seqs, total_tokens, H, d,
                   mode, out, workspace, workspace_bytes, nullptr, nullptr, nullptr, nullptr, 0, stream,
                   events, num_events);
+}
+
+extern "C" int kda_chunk_fwd_rect(const void* q, const void* k, const void* v, const void* f_raw,
+                                  const void* b_raw, const float* A_log, const float* dt_bias,
+                                  const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                                  int32_t H, int32_t dk, int32_t dv, uint32_t mode, void* out,
+                                  void* workspace, size_t workspace_bytes,
+                                  const float* initial_state, float* final_state, void* stream) {
+  if (dk < 1 || dv < 1) return KDA_ERR_INVALID_ARG;
+  if (dk > kda::DH || dv > kda::DH) return KDA_ERR_UNSUPPORTED;
+  const uint32_t m = (mode & ~KDA_MODE_ALL_BITS) ? mode : (mode & ~KDA_MODE_WINDOWED);
+  if (dk == kda::DH && dv == kda::DH)
+    return fwd_impl(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, num_seqs, total_tokens, H,
+                    kda::DH, m, out, workspace, workspace_bytes, initial_state, final_state,
+                    nullptr, nullptr, 0, stream, nullptr, 0);
+  // the host checks of the square call (its workspace layout serves here)
+  int st = check_args(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, num_seqs, total_tokens,
+                      H, kda::DH, m, out, workspace, workspace_bytes);
+  if (st != KDA_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (total_tokens == 0) {
+    if (!final_state) return KDA_OK;
+    const int64_t n = (int64_t)num_seqs * H * dk * dv;
+    const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+    hipLaunchKernelGGL(kda::kda_state_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       initial_state, final_state, n);
+    return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  }
+  const bool f32i = m & KDA_MODE_FP32_INTERMEDIATE;
+  const bool a32 = m & KDA_ACT_FP32;
+  const bool o32 = (m & KDA_OUT_FP32) || a32;
+#define KDA_RECT(TA, MT, TO)                                                                   \
+  return kda::launch_all<TA, MT, TO, true>(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, \
+                                           num_seqs, total_tokens, H, m, out, workspace,      \
+                                           initial_state, final_state, nullptr, nullptr, 0, s, \
+                                           nullptr, dk, dv)
+  if (!a32 && !f32i && !o32) KDA_RECT(kda::bf16, kda::bf16, kda::bf16);
+  if (!a32 && !f32i && o32) KDA_RECT(kda::bf16, kda::bf16, float);
+  if (!a32 && f32i && !o32) KDA_RECT(kda::bf16, float, kda::bf16);
+  if (!a32 && f32i && o32) KDA_RECT(kda::bf16, float, float);
+  if (a32 && !f32i) KDA_RECT(float, kda::bf16, float);
+  KDA_RECT(float, float, float);
+#undef KDA_RECT
 }
 
 extern "C" int kda_chunk_fwd_conv(const void* q, const void* k, const void* v, const void* f_raw,

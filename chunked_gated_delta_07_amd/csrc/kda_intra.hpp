@@ -169,6 +169,10 @@ struct IntraArgs {
   // and W^T [128][64], Kb [64][128] (the backward's reverse state scan)
   float* wt;
   float* kbr;
+  // key and value widths of the inputs when the kernel's RECT parameter is
+  // set (q, k, f_raw [T][H][dk], dt_bias [H][dk], v [T][H][dv], each <= 128);
+  // the chunk algebra runs at 128 with the missing channels taken as zero
+  int dk, dv;
 };
 
 // Chunks [cbeg, cend) of sequence n.  A null cfirst means a single sequence
@@ -362,8 +366,9 @@ __device__ __forceinline__ constexpr int combo(int R, int I) { return (R * (R - 
 // The work of one (chunk, head): a workgroup of 256 threads; smem is the
 // workgroup's LDS buffer of IntraLds<MT>::BYTES bytes, 16-byte aligned.
 // Template parameters as for kda_intra_kernel below.
-template <typename TA, typename MT, bool CONV, typename LY, bool BWD>
+template <typename TA, typename MT, bool CONV, typename LY, bool BWD, bool RECT = false>
 __device__ __forceinline__ void intra_chunk(const IntraArgs& p, int chunk, int h, char* smem) {
+  static_assert(!(RECT && (CONV || BWD)), "rectangular widths: forward without convolution only");
   typedef IntraLds<MT> L;
   constexpr int ROWL = L::ROWL, TL = L::TL, AL = L::AL;
   float* sBeta = reinterpret_cast<float*>(smem + L::O_BETA);
@@ -401,11 +406,23 @@ __device__ __forceinline__ void intra_chunk(const IntraArgs& p, int chunk, int h
   // All row loads are issued before any use (rows past the end re-read the
   // chunk's first row and are masked), so their latencies overlap.
   const float lam = expf(p.A_log[h]);  // exp(-inf) = 0 gives g = 0 exactly
-  const f32x2 dtb = *reinterpret_cast<const f32x2*>(p.dt_bias + (size_t)h * DH + c0);
+  // RECT: channel c of a row of width dim; missing channels (c >= dim) read as
+  // zero, which leaves q, k, v zero there (and the decay finite)
+  auto ld2 = [&](const TA* __restrict__ gx, int tok, int dim) -> f32x2 {
+    const TA* row = gx + ((size_t)tok * p.H + h) * dim;
+    return f32x2{c0 < dim ? to_f32(row[c0]) : 0.0f, c0 + 1 < dim ? to_f32(row[c0 + 1]) : 0.0f};
+  };
+  f32x2 dtb;
+  if constexpr (RECT) {
+    const float* db = p.dt_bias + (size_t)h * p.dk;
+    dtb = f32x2{c0 < p.dk ? db[c0] : 0.0f, c0 + 1 < p.dk ? db[c0 + 1] : 0.0f};
+  } else {
+    dtb = *reinterpret_cast<const f32x2*>(p.dt_bias + (size_t)h * DH + c0);
+  }
   float qa[16][2], ka[16][2], aa[16][2];
   // Full chunks (all but a sequence's last) load their rows from one
   // wave-uniform base with scalar row offsets and need no masks.
-  const bool full = len == CHUNK;  // uniform over the block
+  const bool full = !RECT && len == CHUNK;  // uniform over the block
   const size_t rstride = (size_t)H * DH;  // elements from one token to the next
   // the three tokens before this wave's first row, for the convolution: zero
   // before the sequence start (and past the chunk's end, where every row of
@@ -441,8 +458,13 @@ __device__ __forceinline__ void intra_chunk(const IntraArgs& p, int chunk, int h
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int r = 16 * w + j;
-        const size_t o = ((size_t)(t0 + (r < len ? r : 0)) * H + h) * DH + c0;
-        xq[j] = load2(gq + o); xk[j] = load2(gk + o); xf[j] = load2(gf + o);
+        if constexpr (RECT) {
+          const int tok = t0 + (r < len ? r : 0);
+          xq[j] = ld2(gq, tok, p.dk); xk[j] = ld2(gk, tok, p.dk); xf[j] = ld2(gf, tok, p.dk);
+        } else {
+          const size_t o = ((size_t)(t0 + (r < len ? r : 0)) * H + h) * DH + c0;
+          xq[j] = load2(gq + o); xk[j] = load2(gk + o); xf[j] = load2(gf + o);
+        }
       }
     }
     if constexpr (CONV) {
@@ -1010,7 +1032,8 @@ __device__ __forceinline__ void intra_chunk(const IntraArgs& p, int chunk, int h
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int r = 16 * w + j;
-      const f32x2 xv = load2(gv + ((size_t)(t0 + (r < len ? r : 0)) * H + h) * DH + c0);
+      const f32x2 xv = RECT ? ld2(gv, t0 + (r < len ? r : 0), p.dv)
+                            : load2(gv + ((size_t)(t0 + (r < len ? r : 0)) * H + h) * DH + c0);
       v0[j] = r < len ? xv[0] : 0.0f;
       v1[j] = r < len ? xv[1] : 0.0f;
     }
@@ -1183,20 +1206,22 @@ __device__ __forceinline__ void intra_chunk(const IntraArgs& p, int chunk, int h
 
 // LY: record layout (Frag for the two-pass forward's state pass, FragW for the
 // windowed one, PlainRec for the backward).  BWD: also store T and the W
-// product's right-hand operand.
+// product's right-hand operand.  RECT: inputs of key / value widths p.dk,
+// p.dv below 128 (zero-padded on load).
 //   Forward: a grid of heads x chunks, chunk-major with the last chunk first,
 //   so that the records the state pass reads first (every head's first
 //   chunks) are the most recently written ones, still in the memory-side
 //   cache; consecutive workgroups read neighbouring heads of the same tokens.
 //   Backward recomputation: the (chunk, head) grid of the other kernels.
-template <typename TA, typename MT, bool CONV, typename LY = Frag<MT>, bool BWD = false>
+template <typename TA, typename MT, bool CONV, typename LY = Frag<MT>, bool BWD = false,
+          bool RECT = false>
 __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
   __shared__ __attribute__((aligned(16))) char smem[IntraLds<MT>::BYTES];
   if constexpr (BWD)
-    intra_chunk<TA, MT, CONV, LY, BWD>(p, (int)blockIdx.x, (int)blockIdx.y, smem);
+    intra_chunk<TA, MT, CONV, LY, BWD, RECT>(p, (int)blockIdx.x, (int)blockIdx.y, smem);
   else  // grid (H, chunks): x = head, y = chunk counted from the last
-    intra_chunk<TA, MT, CONV, LY, BWD>(p, (int)gridDim.y - 1 - (int)blockIdx.y, (int)blockIdx.x,
-                                       smem);
+    intra_chunk<TA, MT, CONV, LY, BWD, RECT>(p, (int)gridDim.y - 1 - (int)blockIdx.y,
+                                             (int)blockIdx.x, smem);
 }
 
 }  // namespace kda

@@ -37,7 +37,22 @@ struct ScanArgs {
   void* out;         // [T][H][128]
   const float* init; // [N][H][128 key][128 value] start states, or null (zero)
   float* fin;        // [N][H][128][128] end states, or null (not written)
+  // with the kernels' RECT parameter: key / value widths (<= 128) of out
+  // [T][H][dv] and of the states [N][H][dk][dv]
+  int dk, dv;
 };
+
+// State entry (key, value) of (sequence, head) pair `pair` in a [..][dk][dv]
+// array, or -1 when the pair of widths leaves it out.
+template <bool RECT>
+__device__ __forceinline__ int64_t state_index(const ScanArgs& p, int pair, int key, int value) {
+  if constexpr (RECT) {
+    if (key >= p.dk || value >= p.dv) return -1;
+    return ((int64_t)pair * p.dk + key) * p.dv + value;
+  } else {
+    return ((int64_t)pair * DH + key) * DH + value;
+  }
+}
 
 constexpr int DVB = 32;  // value channels per workgroup
 
@@ -57,6 +72,45 @@ constexpr int DVB = 32;  // value channels per workgroup
 typedef unsigned u32;
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Output of one lane after the lane-half exchange: for q = 0, 1 the words
+// wd[2q][..] hold values rowp[16q .. 16q+3] and wd[2q+1][..] values
+// rowp[16q+4 .. 16q+7] (packed pairs for bf16); rowp is value column v0 of
+// the token's output row.  RECT: values at or past column dv are not written
+// (element stores).
+template <typename TO, bool RECT>
+__device__ __forceinline__ void store_out8(TO* rowp, int v0, int dv, const u32 (&wd)[4][sizeof(TO)]) {
+  constexpr int NW = (int)sizeof(TO);
+  if constexpr (!RECT) {
+    u32x4* o = reinterpret_cast<u32x4*>(rowp);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if constexpr (NW == 2) {
+        o[2 * q] = u32x4{wd[2 * q][0], wd[2 * q][1], wd[2 * q + 1][0], wd[2 * q + 1][1]};
+      } else {
+        o[4 * q] = u32x4{wd[2 * q][0], wd[2 * q][1], wd[2 * q][2], wd[2 * q][3]};
+        o[4 * q + 1] = u32x4{wd[2 * q + 1][0], wd[2 * q + 1][1], wd[2 * q + 1][2], wd[2 * q + 1][3]};
+      }
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int v = 16 * q + 4 * half + i;  // offset from v0
+          if (v0 + v < dv) {
+            const u32 word = wd[2 * q + half][NW == 2 ? i / 2 : i];
+            if constexpr (NW == 2)
+              reinterpret_cast<uint16_t*>(rowp)[v] = (uint16_t)(i & 1 ? word >> 16 : word & 0xffff);
+            else
+              reinterpret_cast<u32*>(rowp)[v] = word;
+          }
+        }
+  }
+}
+
 // the two bf16 of a packed pair as FP32 (exact)
 __device__ __forceinline__ f32x2 bf16x2_as_f32(u32 v) {
   return f32x2{__builtin_bit_cast(float, v << 16), __builtin_bit_cast(float, v & 0xffff0000u)};
@@ -229,7 +283,7 @@ __device__ __forceinline__ void ring_copy_late(const char* rc, const char* gc, c
 }
 
 // One chunk for one compute wave; operands come from ring slot `slot`.
-template <typename TO, int ROLE, bool FULL>
+template <typename TO, int ROLE, bool FULL, bool RECT>
 __device__ __forceinline__ void ring_step(const ScanArgs& p, const char* slot, f32x16& S, bf16* sS,
                                           bf16* sD, int h, int ctok, int len, int vb, int w, int l) {
   typedef RingLds L;
@@ -304,16 +358,9 @@ __device__ __forceinline__ void ring_step(const ScanArgs& p, const char* slot, f
       }
     const int tk = 32 * wp + col;
     if (FULL || tk < len) {
-      u32x4* o = reinterpret_cast<u32x4*>(out + ((size_t)(ctok + tk) * p.H + h) * DH + DVB * vb + 8 * g);
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        if constexpr (sizeof(TO) == 2) {
-          o[2 * q] = u32x4{wd[2 * q][0], wd[2 * q][1], wd[2 * q + 1][0], wd[2 * q + 1][1]};
-        } else {
-          o[4 * q] = u32x4{wd[2 * q][0], wd[2 * q][1], wd[2 * q][2], wd[2 * q][3]};
-          o[4 * q + 1] = u32x4{wd[2 * q + 1][0], wd[2 * q + 1][1], wd[2 * q + 1][2], wd[2 * q + 1][3]};
-        }
-      }
+      const int dvo = RECT ? p.dv : DH;  // output row width
+      store_out8<TO, RECT>(out + ((size_t)(ctok + tk) * p.H + h) * dvo + DVB * vb + 8 * g,
+                           DVB * vb + 8 * g, dvo, wd);
     }
   }
   // S_next = Diag(Gam) S0 + Kb^T D
@@ -328,7 +375,7 @@ __device__ __forceinline__ void ring_step(const ScanArgs& p, const char* slot, f
   ring_barrier();  // new S0 complete; D may be overwritten
 }
 
-template <typename TO>
+template <typename TO, bool RECT = false>
 __global__ __launch_bounds__(512) void kda_scan_ring_kernel(ScanArgs p) {
   typedef RingLds L;
   constexpr int SL = L::SL;
@@ -340,13 +387,15 @@ __global__ __launch_bounds__(512) void kda_scan_ring_kernel(ScanArgs p) {
   int pair, vb;
   scan_unit(blockIdx.x + 32 * blockIdx.y, pair, vb);  // grid (32, pairs / 8)
   if (pair >= p.N * p.H) return;
+  if (RECT && DVB * vb >= p.dv) return;  // a value block past the value width
   const int n = pair / p.H, h = pair - n * p.H;
   int cbeg, cend;
   chunk_range(p.cu, p.cfirst, n, cbeg, cend);
   const int tseq = p.cu[n], tend = p.cu[n + 1];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int col = l & 31, g = l >> 5;
-  const size_t sbase = (size_t)pair * DH * DH + (size_t)(32 * (w & 3)) * DH + DVB * vb + col;
+  // state entry e of this lane: key 32 (w & 3) + row32(e, l), value 32 vb + col
+  auto sidx = [&](int e) { return state_index<RECT>(p, pair, 32 * (w & 3) + row32(e, l), DVB * vb + col); };
   const int H = p.H;
   const char* recb = reinterpret_cast<const char*>(p.rec);
   const char* gamb = reinterpret_cast<const char*>(p.gam);
@@ -377,11 +426,15 @@ __global__ __launch_bounds__(512) void kda_scan_ring_kernel(ScanArgs p) {
   // -------------------------------------------------------------- compute
   f32x16 S;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) S[e] = p.init ? p.init[sbase + (size_t)row32(e, l) * DH] : 0.0f;
+  for (int e = 0; e < 16; ++e) {
+    const int64_t i = sidx(e);
+    S[e] = (p.init && i >= 0) ? p.init[i] : 0.0f;
+  }
   if (cbeg == cend) {
     if (p.fin) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) p.fin[sbase + (size_t)row32(e, l) * DH] = S[e];
+      for (int e = 0; e < 16; ++e)
+        if (sidx(e) >= 0) p.fin[sidx(e)] = S[e];
     }
     return;
   }
@@ -396,16 +449,17 @@ __global__ __launch_bounds__(512) void kda_scan_ring_kernel(ScanArgs p) {
     const char* slot = ring + ((c - cbeg) & 1) * RG_SLOT;
     const int ctok = tseq + (c - cbeg) * CHUNK;
     if (c < cfull) {
-      if (w < 2) ring_step<TO, 0, true>(p, slot, S, sS, sD, h, ctok, CHUNK, vb, w, l);
-      else ring_step<TO, 1, true>(p, slot, S, sS, sD, h, ctok, CHUNK, vb, w, l);
+      if (w < 2) ring_step<TO, 0, true, RECT>(p, slot, S, sS, sD, h, ctok, CHUNK, vb, w, l);
+      else ring_step<TO, 1, true, RECT>(p, slot, S, sS, sD, h, ctok, CHUNK, vb, w, l);
     } else {
-      if (w < 2) ring_step<TO, 0, false>(p, slot, S, sS, sD, h, ctok, tend - ctok, vb, w, l);
-      else ring_step<TO, 1, false>(p, slot, S, sS, sD, h, ctok, tend - ctok, vb, w, l);
+      if (w < 2) ring_step<TO, 0, false, RECT>(p, slot, S, sS, sD, h, ctok, tend - ctok, vb, w, l);
+      else ring_step<TO, 1, false, RECT>(p, slot, S, sS, sD, h, ctok, tend - ctok, vb, w, l);
     }
   }
   if (p.fin) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) p.fin[sbase + (size_t)row32(e, l) * DH] = S[e];
+    for (int e = 0; e < 16; ++e)
+      if (sidx(e) >= 0) p.fin[sidx(e)] = S[e];
   }
 }
 
@@ -499,7 +553,7 @@ __device__ __forceinline__ f32x16 mma_x6_pipe(const bf16x8 (&r)[3], const bf16x8
 // One chunk for one compute wave of the FP32 ring.  Every FP32 record fragment
 // is one 16-byte LDS read per lane from the slot, issued two steps before its
 // products, and split into pieces during the previous step's products.
-template <typename TO, int ROLE, bool FULL>
+template <typename TO, int ROLE, bool FULL, bool RECT>
 __device__ __forceinline__ void ring32_step(const ScanArgs& p, const char* slot, f32x16& S,
                                             bf16* sS, bf16* sD, int h, int ctok, int len, int vb,
                                             int w, int l) {
@@ -620,23 +674,16 @@ __device__ __forceinline__ void ring32_step(const ScanArgs& p, const char* slot,
       }
     const int tk = 32 * wp + col;
     if (FULL || tk < len) {
-      u32x4* o = reinterpret_cast<u32x4*>(out + ((size_t)(ctok + tk) * p.H + h) * DH + DVB * vb + 8 * g);
-#pragma unroll
-      for (int pr = 0; pr < 2; ++pr) {
-        if constexpr (sizeof(TO) == 2) {
-          o[2 * pr] = u32x4{wd[2 * pr][0], wd[2 * pr][1], wd[2 * pr + 1][0], wd[2 * pr + 1][1]};
-        } else {
-          o[4 * pr] = u32x4{wd[2 * pr][0], wd[2 * pr][1], wd[2 * pr][2], wd[2 * pr][3]};
-          o[4 * pr + 1] = u32x4{wd[2 * pr + 1][0], wd[2 * pr + 1][1], wd[2 * pr + 1][2], wd[2 * pr + 1][3]};
-        }
-      }
+      const int dvo = RECT ? p.dv : DH;  // output row width
+      store_out8<TO, RECT>(out + ((size_t)(ctok + tk) * p.H + h) * dvo + DVB * vb + 8 * g,
+                           DVB * vb + 8 * g, dvo, wd);
     }
   }
   wait_lds();
   ring_barrier();  // new S0 complete; D and the late operands may be overwritten
 }
 
-template <typename TO>
+template <typename TO, bool RECT = false>
 __global__ __launch_bounds__(512) void kda_scan_ring32_kernel(ScanArgs p) {
   typedef Ring32Lds L;
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
@@ -647,6 +694,7 @@ __global__ __launch_bounds__(512) void kda_scan_ring32_kernel(ScanArgs p) {
   int pair, vb;
   scan_unit(blockIdx.x + 32 * blockIdx.y, pair, vb);  // grid (32, pairs / 8)
   if (pair >= p.N * p.H) return;
+  if (RECT && DVB * vb >= p.dv) return;  // a value block past the value width
   const int n = pair / p.H, h = pair - n * p.H;
   int cbeg, cend;
   chunk_range(p.cu, p.cfirst, n, cbeg, cend);
@@ -679,14 +727,18 @@ __global__ __launch_bounds__(512) void kda_scan_ring32_kernel(ScanArgs p) {
     return;
   }
   // -------------------------------------------------------------- compute
-  const size_t sbase = (size_t)pair * DH * DH + (size_t)(32 * w) * DH + DVB * vb + col;
+  auto sidx = [&](int e) { return state_index<RECT>(p, pair, 32 * w + row32(e, l), DVB * vb + col); };
   f32x16 S;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) S[e] = p.init ? p.init[sbase + (size_t)row32(e, l) * DH] : 0.0f;
+  for (int e = 0; e < 16; ++e) {
+    const int64_t i = sidx(e);
+    S[e] = (p.init && i >= 0) ? p.init[i] : 0.0f;
+  }
   if (cbeg == cend) {
     if (p.fin) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) p.fin[sbase + (size_t)row32(e, l) * DH] = S[e];
+      for (int e = 0; e < 16; ++e)
+        if (sidx(e) >= 0) p.fin[sidx(e)] = S[e];
     }
     return;
   }
@@ -700,16 +752,17 @@ __global__ __launch_bounds__(512) void kda_scan_ring32_kernel(ScanArgs p) {
   for (int c = cbeg; c < cend; ++c) {
     const int ctok = tseq + (c - cbeg) * CHUNK;
     if (c < cfull) {
-      if (w < 2) ring32_step<TO, 0, true>(p, slot, S, sS, sD, h, ctok, CHUNK, vb, w, l);
-      else ring32_step<TO, 1, true>(p, slot, S, sS, sD, h, ctok, CHUNK, vb, w, l);
+      if (w < 2) ring32_step<TO, 0, true, RECT>(p, slot, S, sS, sD, h, ctok, CHUNK, vb, w, l);
+      else ring32_step<TO, 1, true, RECT>(p, slot, S, sS, sD, h, ctok, CHUNK, vb, w, l);
     } else {
-      if (w < 2) ring32_step<TO, 0, false>(p, slot, S, sS, sD, h, ctok, tend - ctok, vb, w, l);
-      else ring32_step<TO, 1, false>(p, slot, S, sS, sD, h, ctok, tend - ctok, vb, w, l);
+      if (w < 2) ring32_step<TO, 0, false, RECT>(p, slot, S, sS, sD, h, ctok, tend - ctok, vb, w, l);
+      else ring32_step<TO, 1, false, RECT>(p, slot, S, sS, sD, h, ctok, tend - ctok, vb, w, l);
     }
   }
   if (p.fin) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) p.fin[sbase + (size_t)row32(e, l) * DH] = S[e];
+    for (int e = 0; e < 16; ++e)
+      if (sidx(e) >= 0) p.fin[sidx(e)] = S[e];
   }
 }
 

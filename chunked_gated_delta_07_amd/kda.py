@@ -25,7 +25,7 @@ KDA_MODE_WINDOWED = 0x8
 
 # Exported symbols, in declaration order of include/kda.h.
 SYMBOLS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_state",
-           "kda_chunk_fwd_conv", "kda_recurrent_fwd", "kda_recurrent_fwd_rect",
+           "kda_chunk_fwd_conv", "kda_chunk_fwd_rect", "kda_recurrent_fwd", "kda_recurrent_fwd_rect",
            "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_chunk_fwd_noalloc",
            "kda_chunk_fwd_num_stages", "kda_chunk_fwd_timed", "kda_status_string")
 
@@ -67,6 +67,10 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd_conv.restype = ctypes.c_int
     lib.kda_chunk_fwd_conv.argtypes = (fwd_args[:13] + [vp, vp, ctypes.c_int32] + fwd_args[13:16]
                                        + [vp, vp, vp])
+    lib.kda_chunk_fwd_rect.restype = ctypes.c_int
+    lib.kda_chunk_fwd_rect.argtypes = (fwd_args[:11] + [ctypes.c_int32, ctypes.c_int32,
+                                                        ctypes.c_uint32, vp, vp, ctypes.c_size_t,
+                                                        vp, vp, vp])
     lib.kda_recurrent_fwd.restype = ctypes.c_int
     lib.kda_recurrent_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32,
                                       ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
@@ -136,6 +140,9 @@ def chunk_fwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, fp32_intermedia
     b_raw: [T, H] same dtype; A_log: [H] float32; dt_bias: [H, 128] float32;
     cu_seqlens: [N+1] int32.  All CUDA (HIP) tensors, contiguous.  Returns
     out [T, H, 128] (activation dtype, or float32 when out_fp32).
+    A rectangular state (q, k, f_raw [T, H, dk], dt_bias [H, dk], v [T, H, dv],
+    dk, dv <= 128, not both 128) selects kda_chunk_fwd_rect: out [T, H, dv],
+    states [N, H, dk, dv].
     ``events``: optional list of num_stages(T, N, H, mode)+1 torch.cuda.Event
     objects recorded between the stages (kda_chunk_fwd_timed).
     ``windowed=True`` sets KDA_MODE_WINDOWED (schedule only: the pipeline of
@@ -164,20 +171,46 @@ def chunk_fwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, fp32_intermedia
     if cu_seqlens.dtype != torch.int32:
         raise TypeError("cu_seqlens must be int32")
     T, H, d = q.shape
+    dv = v.shape[2] if v.dim() == 3 else -1
     for t in (q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens):
         if not t.is_contiguous() or not t.is_cuda:
             raise ValueError("all tensors must be contiguous device tensors")
-    if k.shape != q.shape or v.shape != q.shape or f_raw.shape != q.shape:
-        raise ValueError("q, k, v, f_raw must have one shape [T, H, d]")
+    if k.shape != q.shape or f_raw.shape != q.shape or v.shape != (T, H, dv):
+        raise ValueError("q, k, f_raw must have one shape [T, H, dk] and v [T, H, dv]")
     if b_raw.shape != (T, H) or A_log.shape != (H,) or dt_bias.shape != (H, d):
-        raise ValueError("b_raw [T,H], A_log [H], dt_bias [H,d] expected")
+        raise ValueError("b_raw [T,H], A_log [H], dt_bias [H,dk] expected")
     num_seqs = cu_seqlens.numel() - 1
     mode = make_mode(fp32_intermediate, act_fp32, out_fp32, windowed)
     out_dtype = torch.float32 if (out_fp32 or act_fp32) else q.dtype
     if out is None:
-        out = torch.empty((T, H, d), dtype=out_dtype, device=q.device)
-    elif out.dtype != out_dtype or out.shape != (T, H, d) or not out.is_contiguous():
+        out = torch.empty((T, H, dv), dtype=out_dtype, device=q.device)
+    elif out.dtype != out_dtype or out.shape != (T, H, dv) or not out.is_contiguous():
         raise ValueError("out has the wrong dtype, shape or layout")
+    if (d, dv) != (128, 128):
+        # rectangular state: kda_chunk_fwd_rect (workspace of the 128 x 128 call)
+        if conv_weight is not None or events is not None or noalloc:
+            raise ValueError("rectangular widths take no convolution, events or noalloc")
+        sshape = (num_seqs, H, d, dv)
+        for t in (initial_state, final_state):
+            if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != sshape
+                                  or not t.is_contiguous() or not t.is_cuda):
+                raise ValueError("states must be contiguous float32 [N, H, dk, dv] device tensors")
+        if final_state is None and return_final_state:
+            final_state = torch.empty(sshape, dtype=torch.float32, device=q.device)
+        m = mode & ~KDA_MODE_WINDOWED
+        nbytes = workspace_bytes(T, max(num_seqs, 1), H, 128, m) if num_seqs >= 1 else 0
+        if workspace is None:
+            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        st = lib.kda_chunk_fwd_rect(_ptr(q), _ptr(k), _ptr(v), _ptr(f_raw), _ptr(b_raw),
+                                    _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens), num_seqs, T, H,
+                                    d, dv, m, _ptr(out), _ptr(workspace), workspace.numel(),
+                                    _ptr(initial_state), _ptr(final_state),
+                                    ctypes.c_void_p(stream.cuda_stream))
+        if st != KDA_OK:
+            raise KdaError(st, "kda_chunk_fwd_rect")
+        return (out, final_state) if final_state is not None else out
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     sp = ctypes.c_void_p(stream.cuda_stream)

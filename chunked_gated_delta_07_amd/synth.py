@@ -115,6 +115,29 @@ def make_inputs(cu_seqlens, H=H_DEFAULT, d=D_DEFAULT, act="bf16", seed=0,
     return KdaInputs(q, k, v, f, b, A_log, dt_bias, cu, act)
 
 
+def rect_inputs(cu_seqlens, H, dk, dv, seed, act="bf16") -> dict:
+    """Inputs with a rectangular state: q, k, f_raw [T,H,dk], v [T,H,dv],
+    b_raw [T,H], A_log [H], dt_bias [H,dk], all float32 (activations rounded
+    to bf16 values when act == 'bf16'), drawn in that order with the
+    distributions of make_inputs."""
+    cu = np.asarray(cu_seqlens, dtype=np.int32)
+    T = int(cu[-1])
+    r = np.random.default_rng(seed)
+
+    def act_round(a):
+        a = a.astype(np.float32)
+        return bf16_bits_to_f32(f32_to_bf16_bits(a)) if act == "bf16" else a
+
+    return dict(q=act_round(r.standard_normal((T, H, dk))),
+                k=act_round(r.standard_normal((T, H, dk))),
+                v=act_round(r.standard_normal((T, H, dv))),
+                f_raw=act_round(r.standard_normal((T, H, dk))),
+                b_raw=act_round(r.standard_normal((T, H))),
+                A_log=r.uniform(0, np.log(16), H).astype(np.float32),
+                dt_bias=(0.5 * r.standard_normal((H, dk))).astype(np.float32),
+                cu_seqlens=cu)
+
+
 # The five workloads.  cfg 0/1 are small parity cases, 2 a scaling point, 3 the
 # headline 16K-token case, 4 a ragged packed batch.
 CONFIGS = {

@@ -173,6 +173,26 @@ KDA_API int kda_chunk_fwd_conv(const void* q, const void* k, const void* v, cons
                        size_t workspace_bytes, const float* initial_state, float* final_state,
                        void* stream);
 
+/* kda_chunk_fwd_state with a rectangular state: dk key channels (q, k, f_raw
+ * [T][H][dk], dt_bias [H][dk]) and dv value channels (v, out [T][H][dv]),
+ * 1 <= dk, dv <= 128 (larger: KDA_ERR_UNSUPPORTED); states [num_seqs][H][dk]
+ * [dv] (NULL allowed, as for kda_chunk_fwd_state); the output scale is
+ * 1/sqrt(dk).  The pages record the rectangular case dk = 16, dv = 24 failing
+ * to compile in their TileLang chunk kernels (xtuner PR #2301, section
+ * Validation).  Here the chunked kernels run on the 128 x 128 layout with the
+ * missing key and value channels read as zero (they stay zero in every
+ * intermediate and in the state), and only the dk x dv part is written: the
+ * cost is that of a 128 x 128 call, less the value blocks of 32 channels
+ * that lie wholly past dv.  Workspace: kda_chunk_fwd_workspace_bytes(T,
+ * num_seqs, H, 128, mode); KDA_MODE_WINDOWED is ignored (two passes).
+ * Everything else as for kda_chunk_fwd_state; dk = dv = 128 is that call. */
+KDA_API int kda_chunk_fwd_rect(const void* q, const void* k, const void* v, const void* f_raw,
+                       const void* b_raw, const float* A_log, const float* dt_bias,
+                       const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                       int32_t H, int32_t dk, int32_t dv, uint32_t mode, void* out,
+                       void* workspace, size_t workspace_bytes, const float* initial_state,
+                       float* final_state, void* stream);
+
 /* Token-serial KDA forward: the same operator as kda_chunk_fwd_state, taken
  * one token at a time with the state in FP32 (the serving-side FP32
  * recurrence that xtuner PR #2301 validates its chunked path against,

@@ -136,19 +136,7 @@ def test_recurrent_in_place_and_empty():
 
 
 def _rect_inputs(cu, H, dk, dv, seed, act):
-    r = np.random.default_rng(seed)
-    T = cu[-1]
-
-    def act_round(a):
-        a = a.astype(np.float32)
-        return synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(a)) if act == "bf16" else a
-    x = dict(q=act_round(r.standard_normal((T, H, dk))), k=act_round(r.standard_normal((T, H, dk))),
-             v=act_round(r.standard_normal((T, H, dv))), f_raw=act_round(r.standard_normal((T, H, dk))),
-             b_raw=act_round(r.standard_normal((T, H))),
-             A_log=r.uniform(0, np.log(16), H).astype(np.float32),
-             dt_bias=(0.5 * r.standard_normal((H, dk))).astype(np.float32),
-             cu_seqlens=np.asarray(cu, dtype=np.int32))
-    return x
+    return synth.rect_inputs(cu, H, dk, dv, seed, act)
 
 
 @pytest.mark.parametrize("dk,dv", [(16, 24), (32, 16), (64, 100), (128, 64), (16, 512)])

@@ -533,7 +533,7 @@ __device__ __forceinline__ void intra_chunk(const IntraArgs& p, int chunk, int h
         va += *sa;
         vp += *sp;
         *sa = sBeta[ru] * sRk[ru] * sRk[ri] * va;
-        gP[LY::pm(ru, ri)] = from_f32<MT>(sRq[ru] * sRk[ri] * vp);
+        *sp = sRq[ru] * sRk[ri] * vp;
       }
     };
     // norms (sums of squares) and the plain q.k diagonal on the VALU: 48
@@ -560,7 +560,7 @@ __device__ __forceinline__ void intra_chunk(const IntraArgs& p, int chunk, int h
         const float rq = rsqrt_hw(sRq[r] + p.eps);
         sRk[r] = rk;
         sRq[r] = rq;
-        gP[LY::pm(r, r)] = from_f32<MT>(rq * rk * sA[r * AL + r]);  // P[r][r], decay 1
+        sA[r * AL + r] = rq * rk * sA[r * AL + r];  // P[r][r], decay 1
       }
       wsync();
     }
@@ -645,7 +645,7 @@ __device__ __forceinline__ void intra_chunk(const IntraArgs& p, int chunk, int h
           const int pp = 16 * bt + 8 * sd.h32 + 4 * sd.h16 + 2 * b3 + b2;
           if (pp < NPAIR) {
             const int ru = 16 * w + pair_u(pp), ri = 16 * w + pair_i(pp);
-            if (b1) gP[LY::pm(ru, ri)] = from_f32<MT>(sRq[ru] * sRk[ri] * tot);
+            if (b1) sA[ri * AL + ru] = sRq[ru] * sRk[ri] * tot;
             else sA[ru * AL + ri] = sBeta[ru] * sRk[ru] * sRk[ri] * tot;
           }
         }
@@ -690,7 +690,7 @@ __device__ __forceinline__ void intra_chunk(const IntraArgs& p, int chunk, int h
         const float rq = rsqrt_hw(cqq[e] + p.eps);
         sRk[r] = rk;
         sRq[r] = rq;
-        gP[LY::pm(r, r)] = from_f32<MT>(rq * rk * cqk[e]);  // P[r][r], decay 1
+        sA[r * AL + r] = rq * rk * cqk[e];  // P[r][r], decay 1
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -735,7 +735,7 @@ __device__ __forceinline__ void intra_chunk(const IntraArgs& p, int chunk, int h
         for (int e = 0; e < 4; ++e) {
           const int ru = 16 * w + m0 + e;
           sA[ru * AL + ri] = sBeta[ru] * sRk[ru] * rki * ca[e];
-          gP[LY::pm(ru, ri)] = from_f32<MT>(sRq[ru] * rki * cp[e]);
+          sA[ri * AL + ru] = sRq[ru] * rki * cp[e];
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -775,7 +775,7 @@ __device__ __forceinline__ void intra_chunk(const IntraArgs& p, int chunk, int h
               const float vp = e == 0 ? cp[0] : e == 1 ? cp[1] : e == 2 ? cp[2] : cp[3];
               const int ru = 16 * w + u, ri = 16 * w + i;
               sA[ru * AL + ri] = sBeta[ru] * sRk[ru] * sRk[ri] * va;
-              gP[LY::pm(ru, ri)] = from_f32<MT>(sRq[ru] * sRk[ri] * vp);
+              sA[ri * AL + ru] = sRq[ru] * sRk[ri] * vp;
             }
           }
         }
@@ -901,8 +901,7 @@ __device__ __forceinline__ void intra_chunk(const IntraArgs& p, int chunk, int h
             *slot = cx[e];
           } else {
             const float v = *slot + cx[e];
-            if (isq) gP[LY::pm(ru, ri)] = from_f32<MT>(sRq[ru] * sRk[ri] * v);
-            else *slot = sBeta[ru] * sRk[ru] * sRk[ri] * v;
+            *slot = isq ? sRq[ru] * sRk[ri] * v : sBeta[ru] * sRk[ru] * sRk[ri] * v;
           }
         }
       }
@@ -960,42 +959,49 @@ __device__ __forceinline__ void intra_chunk(const IntraArgs& p, int chunk, int h
   #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ru = 16 * R + m0 + e;
-        if (isq) gP[LY::pm(ru, ri)] = from_f32<MT>(sRq[ru] * sRk[ri] * c[e]);
+        if (isq) sA[ri * AL + ru] = sRq[ru] * sRk[ri] * c[e];
         else sA[ru * AL + ri] = sBeta[ru] * sRk[ru] * sRk[ri] * c[e];
       }
     }
   }
-  // Upper triangle of P is zero.  In the forward's stored order a 16-byte
-  // fragment holds FE consecutive columns of one row: fragments wholly above
-  // the diagonal are written as one vector, the one straddling it element by
-  // element.  The transposed (backward) layout is zeroed element by element.
-  if constexpr (LY::TRANSPOSED_QT_P) {
-    for (int f = tid; f < CHUNK * CHUNK; f += 256) {
-      const int r = f & 63, i = f >> 6;  // consecutive threads: consecutive addresses
-      if (i > r) gP[LY::pm(r, i)] = from_f32<MT>(0.0f);
-    }
-  } else if constexpr (LY::P_LOWER_TILES) {
-    // only the stored tiles: the upper part of the two diagonal 32 x 32 tiles
-    for (int f = tid; f < 2 * 32 * 32; f += 256) {
-      const int r = 32 * (f >> 10) + ((f >> 5) & 31), i = 32 * (f >> 10) + (f & 31);
-      if (i > r) gP[LY::pm(r, i)] = from_f32<MT>(0.0f);
-    }
-  } else {
-    constexpr int FE = LY::FE;
-    typedef typename std::conditional<sizeof(MT) == 2, bf16x8, f32x4>::type v16;
-    for (int f = tid; f < CHUNK * CHUNK / FE; f += 256) {
-      const int r = f / (CHUNK / FE), i0 = (f % (CHUNK / FE)) * FE;
-      if (i0 > r) {
-        v16 z;
+  if constexpr (L::NP == 1) __syncthreads();  // (the two-pass FP32 loop ends with one)
+  // P to the record.  Every entry P[r][i] (i <= r) was left in LDS at
+  // sA[i][r], the upper triangle of the A buffer (A is strictly lower); here
+  // it is written in the layout's order, zeros above the diagonal, one 16-byte
+  // store per fragment (consecutive lanes: consecutive rows r, so the LDS reads
+  // fall in consecutive banks).  The T solve below reads only A's lower part.
+  {
+    auto pval = [&](int r, int i) { return i <= r ? sA[i * AL + r] : 0.0f; };
+    if constexpr (LY::TRANSPOSED_QT_P) {
+      // P^T [i][r] (FP32 records): four consecutive rows r per store
+      static_assert(sizeof(MT) == 4, "transposed records are FP32");
+      for (int f = tid; f < CHUNK * CHUNK / 4; f += 256) {
+        const int i = f >> 4, r0 = 4 * (f & 15);
+        store4(gP + LY::pm(r0, i), f32x4{pval(r0, i), pval(r0 + 1, i), pval(r0 + 2, i), pval(r0 + 3, i)});
+      }
+    } else if constexpr (LY::P_LOWER_TILES) {
+      // the six stored fragments: lane (r % 32, g) of fragment (r / 32, step s)
+      for (int f = tid; f < 6 * 64; f += 256) {
+        const int idx = f >> 6, lane = f & 63, g = lane >> 5;
+        const int r = (idx >= 2 ? 32 : 0) + (lane & 31), s = idx >= 2 ? idx - 2 : idx;
+        bf16x8 x;
 #pragma unroll
-        for (int e = 0; e < FE; ++e) z[e] = from_f32<MT>(0.0f);
-        *reinterpret_cast<v16*>(gP + LY::pm(r, i0)) = z;
-      } else {
-        for (int i = r + 1; i < i0 + FE; ++i) gP[LY::pm(r, i)] = from_f32<MT>(0.0f);
+        for (int q = 0; q < 8; ++q) x[q] = (bf16)pval(r, 16 * s + 4 * g + (q & 3) + 8 * (q >> 2));
+        *reinterpret_cast<bf16x8*>(gP + LY::pm(r, 16 * s + 4 * g)) = x;
+      }
+    } else {
+      // FE consecutive columns of one row per 16 bytes
+      constexpr int FE = LY::FE;
+      typedef typename std::conditional<sizeof(MT) == 2, bf16x8, f32x4>::type v16;
+      for (int f = tid; f < CHUNK * CHUNK / FE; f += 256) {
+        const int r = f & 63, i0 = FE * (f >> 6);
+        v16 x;
+#pragma unroll
+        for (int e = 0; e < FE; ++e) x[e] = from_f32<MT>(pval(r, i0 + e));
+        *reinterpret_cast<v16*>(gP + LY::pm(r, i0)) = x;
       }
     }
   }
-  __syncthreads();
 
   // ------------------------------------------------- phase 3: T = (I + A)^{-1}
   // Forward substitution, blocked: 4x4 diagonal blocks explicitly, then

@@ -1058,15 +1058,19 @@ __device__ __forceinline__ void intra_chunk(const IntraArgs& p, int chunk, int h
     float t3v = c4 == 3 ? 1.0f : -(n30 * t0v + n31 * t1v + n32 * t2v);
     const float mine = r4 == 0 ? t0v : r4 == 1 ? t1v : r4 == 2 ? t2v : t3v;
     sT[(base + r4) * AL + base + c4] = mine;
-    // zero the rest of this wave's 16x16 diagonal block above the 4x4 diagonal
-    // and every block above the 16x16 diagonal
+    // zero the rest of this wave's 16x16 diagonal block above the 4x4 diagonal,
+    // and with FP32 operands (T is then the W/U operand itself) every block
+    // above the 16x16 diagonal; a bf16 operand is converted with those blocks
+    // masked instead
     for (int x = l; x < 16 * 16; x += 64) {
       const int rr = x >> 4, cc = x & 15;
       if ((cc >> 2) > (rr >> 2)) sT[(16 * w + rr) * AL + 16 * w + cc] = 0.0f;
     }
-    for (int x = tid; x < CHUNK * CHUNK; x += 256) {
-      const int rr = x >> 6, cc = x & 63;
-      if ((cc >> 4) > (rr >> 4)) sT[rr * AL + cc] = 0.0f;
+    if constexpr (L::TS_ALIAS) {
+      for (int x = tid; x < CHUNK * CHUNK; x += 256) {
+        const int rr = x >> 6, cc = x & 63;
+        if ((cc >> 4) > (rr >> 4)) sT[rr * AL + cc] = 0.0f;
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -1129,10 +1133,13 @@ __device__ __forceinline__ void intra_chunk(const IntraArgs& p, int chunk, int h
   MT* sXt = reinterpret_cast<MT*>(sU + L::O_XT);  // transposed operand [128 / NP][TL]
   // W = T (Diag(beta rk) (k * E)),  U = T (Diag(beta) v): the row scales go
   // on the right-hand operands, T is converted once (FP32: T is used as is).
+  // (T is lower triangular: entries above the 16x16 block diagonal were not
+  // written and read as zero here)
   for (int x = tid; x < CHUNK * CHUNK; x += 256) {
     const int r = x >> 6, i = x & 63;
-    if constexpr (!L::TS_ALIAS) sTs[r * TL + i] = from_f32<MT>(sT[r * AL + i]);
-    if constexpr (BWD) p.tmat[((size_t)chunk * H + h) * CHUNK * CHUNK + x] = sT[r * AL + i];
+    const float tv = (i >> 4) > (r >> 4) ? 0.0f : sT[r * AL + i];
+    if constexpr (!L::TS_ALIAS) sTs[r * TL + i] = from_f32<MT>(tv);
+    if constexpr (BWD) p.tmat[((size_t)chunk * H + h) * CHUNK * CHUNK + x] = tv;
   }
 #pragma unroll
   for (int j = 0; j < 16; ++j) {

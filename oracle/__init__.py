@@ -54,6 +54,11 @@ CONV_PLANT = {
     "conv_no_reset": 1 << 15,
     "conv_taps_reversed": 1 << 16,
 }
+# Deliberate mistakes of its backward (kda_oracle_short_conv_vjp).
+CONVB_PLANT = {
+    "convb_no_silu_deriv": 1 << 21,
+    "convb_taps_forward": 1 << 22,
+}
 
 
 def build(force: bool = False) -> str:
@@ -99,6 +104,10 @@ def _load():
     lib.kda_oracle_short_conv.argtypes = [dp, ip, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
                                           ctypes.c_int, dp, dp, ctypes.c_int, ctypes.c_int,
                                           ctypes.c_int, ctypes.c_uint]
+    lib.kda_oracle_short_conv_vjp.restype = ctypes.c_int
+    lib.kda_oracle_short_conv_vjp.argtypes = [dp, dp, ip, ctypes.c_int, ctypes.c_int64,
+                                              ctypes.c_int, ctypes.c_int, dp, dp, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_uint, dp, dp, dp]
     lib.kda_oracle_bwd_rect.restype = ctypes.c_int
     lib.kda_oracle_bwd_rect.argtypes = [dp, dp, dp, dp, dp, dp, dp, ip, ctypes.c_int,
                                         ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -268,6 +277,30 @@ def short_conv(x, cu_seqlens, weight, bias=None, silu=True, round_bf16=False, pl
     if rc != 0:
         raise ValueError("kda_oracle_short_conv rejected its arguments")
     return y
+
+
+def short_conv_vjp(x, dy, cu_seqlens, weight, bias=None, silu=True, plant=0):
+    """Vector-Jacobian product of short_conv (without rounding): for
+    L = <dy, short_conv(x)>, returns (dx [T, H, d], dweight [H*d, K],
+    dbias [H*d]), FP64.  See kda_oracle_short_conv_vjp."""
+    lib = _load()
+    x = _f64(x)
+    dy = _f64(dy)
+    T, H, d = x.shape
+    assert dy.shape == x.shape
+    w = _f64(weight).reshape(H * d, -1)
+    K = w.shape[1]
+    b = None if bias is None else _f64(bias).reshape(H * d)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    dx = np.zeros_like(x)
+    dw = np.zeros_like(w)
+    db = np.zeros(H * d)
+    rc = lib.kda_oracle_short_conv_vjp(_ptr(x), _ptr(dy), _ptr(cu, ctypes.c_int32), len(cu) - 1, T,
+                                       H, d, _ptr(w), _ptr(b) if b is not None else None, K,
+                                       int(bool(silu)), int(plant), _ptr(dx), _ptr(dw), _ptr(db))
+    if rc != 0:
+        raise ValueError("kda_oracle_short_conv_vjp rejected its arguments")
+    return dx, dw, db
 
 
 def kda_backward(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, dout, scale=None, eps=1e-6,

@@ -82,6 +82,8 @@ enum {
   PLANT_FINAL_EARLY = 1u << 14,      /* final state taken before the last token */
   PLANT_CONV_NO_RESET = 1u << 15,    /* convolution history crosses sequences   */
   PLANT_CONV_TAPS_REVERSED = 1u << 16, /* taps applied in reverse order          */
+  PLANT_CONVB_NO_SILU_DERIV = 1u << 21, /* backward: SiLU derivative taken as 1     */
+  PLANT_CONVB_TAPS_FORWARD = 1u << 22,  /* backward: dx correlates the taps forward */
   /* mistakes of the backward (kda_oracle_bwd_rect) */
   PLANT_BWD_BETA_SCALE = 1u << 17,   /* beta gradient scaled by 1.25            */
   PLANT_BWD_NO_STATE_DECAY = 1u << 18, /* dS passed back without Diag(exp g)    */
@@ -504,6 +506,63 @@ int kda_oracle_short_conv(double* x, const int32_t* cu_seqlens, int N, int64_t T
       }
     }
     free(hist);
+  }
+  return 0;
+}
+
+/* Vector-Jacobian product of kda_oracle_short_conv (the convolution in front
+ * of the core, xtuner PR #2153, KDA module description: FP32 weight and bias
+ * gradients).  The rounding of the output to the activation dtype is taken as
+ * the identity (the backward differentiates the FP64 convolution).  For
+ * L = <dy, y>, per channel ch and sequence, with x = 0 before its start:
+ *   z_t  = bias + sum_i w_i x_{t-K+1+i}
+ *   dz_t = dy_t * act'(z_t),  act'(z) = s (1 + z (1 - s)), s = 1/(1+e^-z) for
+ *          SiLU, 1 without
+ *   dx_u = sum_i w_i dz_{u+K-1-i}  over the tokens u+K-1-i of the same sequence
+ *   dw_i = sum_t dz_t x_{t-K+1+i},  dbias = sum_t dz_t  (over every sequence)
+ * x, dy, dx: [T][H*d]; w, dw: [H*d][K]; bias (may be NULL), dbias: [H*d].
+ * Every output is overwritten.  Returns 0, or -1 for invalid arguments. */
+int kda_oracle_short_conv_vjp(const double* x, const double* dy, const int32_t* cu_seqlens, int N,
+                              int64_t T, int H, int d, const double* w, const double* bias, int K,
+                              int silu, unsigned plant, double* dx, double* dw, double* dbias) {
+  if (N < 1 || H < 1 || d < 1 || K < 1) return -1;
+  if (cu_seqlens[0] != 0 || cu_seqlens[N] != T) return -1;
+  const int64_t HD = (int64_t)H * d;
+#pragma omp parallel for schedule(static)
+  for (int64_t ch = 0; ch < HD; ++ch) {
+    double* dz = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+    for (int i = 0; i < K; ++i) dw[ch * K + i] = 0.0;
+    dbias[ch] = 0.0;
+    for (int n = 0; n < N; ++n) {
+      const int64_t s0 = cu_seqlens[n], s1 = cu_seqlens[n + 1];
+      for (int64_t t = s0; t < s1; ++t) {
+        double z = bias ? bias[ch] : 0.0;
+        for (int i = 0; i < K; ++i) {
+          const int64_t u = t - K + 1 + i;
+          if (u >= s0) z += w[ch * K + i] * x[u * HD + ch];
+        }
+        double g = 1.0;
+        if (silu && !(plant & PLANT_CONVB_NO_SILU_DERIV)) {
+          const double sg = 1.0 / (1.0 + exp(-z));
+          g = sg * (1.0 + z * (1.0 - sg));
+        }
+        dz[t] = dy[t * HD + ch] * g;
+        dbias[ch] += dz[t];
+        for (int i = 0; i < K; ++i) {
+          const int64_t u = t - K + 1 + i;
+          if (u >= s0) dw[ch * K + i] += dz[t] * x[u * HD + ch];
+        }
+      }
+      for (int64_t u = s0; u < s1; ++u) {
+        double acc = 0.0;
+        for (int i = 0; i < K; ++i) {
+          const int64_t t = (plant & PLANT_CONVB_TAPS_FORWARD) ? u - K + 1 + i : u + K - 1 - i;
+          if (t >= s0 && t < s1) acc += w[ch * K + i] * dz[t];
+        }
+        dx[u * HD + ch] = acc;
+      }
+    }
+    free(dz);
   }
   return 0;
 }

@@ -88,3 +88,91 @@ def test_conv_planted_mistake_is_caught(plant):
     def bad(*a, **kw):
         return oracle.short_conv(*a, plant=oracle.CONV_PLANT[plant], **kw)
     assert [p.__name__ for p in CONV_PINS if not p(bad)], plant
+
+
+# ----------------------------------------------------------------- backward
+def _conv_loss(x, cu, w, b, dy, silu):
+    return float(np.sum(dy * oracle.short_conv(x, cu, w, bias=b, silu=silu)))
+
+
+def pin_vjp_finite_differences(vjp):
+    """Central differences of L = <dy, short_conv(x)> for every element of x,
+    the taps and the bias (packed sequences with an empty one, with and
+    without SiLU)."""
+    r = np.random.default_rng(11)
+    cu = np.asarray([0, 5, 5, 12], dtype=np.int32)
+    x = r.standard_normal((12, 1, 2))
+    w = r.standard_normal((2, 4))
+    b = r.standard_normal(2)
+    dy = r.standard_normal((12, 1, 2))
+    ok = True
+    for silu in (False, True):
+        dx, dw, db = vjp(x, dy, cu, w, b, silu)
+        h = 1e-6
+        for arr, grad in ((x, dx), (w, dw), (b, db)):
+            flat = arr.reshape(-1)
+            for j in range(flat.size):
+                keep = flat[j]
+                flat[j] = keep + h
+                lp = _conv_loss(x, cu, w, b, dy, silu)
+                flat[j] = keep - h
+                lm = _conv_loss(x, cu, w, b, dy, silu)
+                flat[j] = keep
+                ok &= abs((lp - lm) / (2 * h) - grad.reshape(-1)[j]) <= 1e-7 * (1 + abs(grad.reshape(-1)[j]))
+    return bool(ok)
+
+
+def pin_vjp_identity_taps(vjp):
+    """Taps (0, 0, 0, 1), no bias, no SiLU: dx = dy exactly; the gradient of
+    tap i is the sum of dy_t x_{t-3+i} over tokens with that history inside
+    the sequence; the bias gradient is the sum of dy."""
+    r = np.random.default_rng(12)
+    cu = np.asarray([0, 7, 20], dtype=np.int32)
+    x = r.standard_normal((20, 2, 3))
+    dy = r.standard_normal((20, 2, 3))
+    ident = np.tile([0.0, 0.0, 0.0, 1.0], (6, 1))
+    dx, dw, db = vjp(x, dy, cu, ident, None, False)
+    ok = np.array_equal(dx, dy)
+    xf, dyf = x.reshape(20, 6), dy.reshape(20, 6)
+    for i in range(4):
+        exp = np.zeros(6)
+        for a, bnd in ((0, 7), (7, 20)):
+            for t in range(a, bnd):
+                u = t - 3 + i
+                if u >= a:
+                    exp += dyf[t] * xf[u]
+        ok &= np.allclose(dw[:, i], exp, rtol=1e-13, atol=1e-13)
+    ok &= np.allclose(db, dyf.sum(0), rtol=1e-13, atol=1e-13)
+    return bool(ok)
+
+
+def pin_vjp_sequence_isolation(vjp):
+    """A gradient that reaches only the second sequence leaves the first
+    sequence's input gradient exactly zero."""
+    r = np.random.default_rng(13)
+    cu = np.asarray([0, 9, 25], dtype=np.int32)
+    x = r.standard_normal((25, 1, 4))
+    w = r.standard_normal((4, 4))
+    dy = r.standard_normal((25, 1, 4))
+    dy[:9] = 0.0
+    dx, _, _ = vjp(x, dy, cu, w, r.standard_normal(4), True)
+    return bool(np.count_nonzero(dx[:9]) == 0 and np.count_nonzero(dx[9:]) > 0)
+
+
+CONV_VJP_PINS = [pin_vjp_finite_differences, pin_vjp_identity_taps, pin_vjp_sequence_isolation]
+
+
+def _vjp(plant=0):
+    return lambda x, dy, cu, w, b, silu: oracle.short_conv_vjp(x, dy, cu, w, bias=b, silu=silu,
+                                                               plant=plant)
+
+
+@pytest.mark.parametrize("pin", CONV_VJP_PINS, ids=lambda p: p.__name__)
+def test_conv_vjp_pin(pin):
+    assert pin(_vjp())
+
+
+@pytest.mark.parametrize("plant", sorted(oracle.CONVB_PLANT), ids=str)
+def test_conv_vjp_planted_mistake_is_caught(plant):
+    bad = _vjp(oracle.CONVB_PLANT[plant])
+    assert [p.__name__ for p in CONV_VJP_PINS if not p(bad)], plant

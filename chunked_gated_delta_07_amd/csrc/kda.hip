@@ -12,6 +12,7 @@
 #include "kda_window.hpp"
 #include "kda_recurrent.hpp"
 #include "kda_bwd.hpp"
+#include "kda_conv_bwd.hpp"
 
 namespace kda {
 
@@ -325,6 +326,84 @@ static int launch_bwd(const void* q, const void* k, const void* v, const void* f
   hipLaunchKernelGGL((kda_bwd_gate_kernel<TA>), gch, dim3(512), 0, stream, a);
   hipLaunchKernelGGL((kda_bwd_final_kernel<TA, TR>), gch, dim3(256), 0, stream, a);
   hipLaunchKernelGGL(kda_bwd_param_kernel, dim3((unsigned)H), dim3(DH), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+// Backward through the fused convolution: the backward's own workspace, then
+// the convolution outputs (activation dtype), their FP32 gradients, FP32
+// gradients of f_raw and b_raw (cast at the end when the gradients are bf16)
+// and the per-chunk tap / bias partials.
+struct ConvBwdLayout {
+  BwdLayout core;
+  size_t off_y, off_dy, off_df, off_db, off_part, total;
+};
+
+static inline ConvBwdLayout conv_bwd_layout(int64_t T, int32_t N, int32_t H, uint32_t mode) {
+  ConvBwdLayout L;
+  L.core = bwd_layout(T, N, H);
+  const size_t act = (mode & KDA_ACT_FP32) ? 4 : 2;
+  const size_t n = (size_t)T * H * DH;
+  size_t o = L.core.total;
+  auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
+  L.off_y = take(3 * n * act);
+  L.off_dy = take(3 * n * 4);
+  L.off_df = take(n * 4);
+  L.off_db = take((size_t)T * H * 4);
+  L.off_part = take((size_t)max_chunks(T, N) * H * 3 * DH * 5 * 4);
+  L.total = o;
+  return L;
+}
+
+template <typename TA, typename TG, typename TR>
+static int launch_bwd_conv(const void* q, const void* k, const void* v, const void* f, const void* b,
+                           const float* A_log, const float* dt_bias, const int32_t* cu, int32_t N,
+                           int64_t T, int32_t H, uint32_t mode, const float* conv_w,
+                           const float* conv_b, int conv_silu, const float* init, const void* dout,
+                           const float* dfin, void* dq, void* dk, void* dv, void* df, void* db,
+                           float* dA_log, float* ddt, float* dinit, float* dconv_w, float* dconv_b,
+                           void* ws, hipStream_t stream) {
+  const ConvBwdLayout L = conv_bwd_layout(T, N, H, mode);
+  char* base = reinterpret_cast<char*>(ws);
+  const size_t n = (size_t)T * H * DH;
+  const size_t act = sizeof(TA);
+  const int64_t C = max_chunks(T, N);
+  ConvBwdArgs a;
+  a.cu = cu;
+  a.cfirst = reinterpret_cast<int32_t*>(base + L.core.off_cfirst);
+  a.N = N; a.H = H;
+  a.x[0] = q; a.x[1] = k; a.x[2] = v;
+  for (int i = 0; i < 3; ++i) {
+    a.y[i] = base + L.off_y + i * n * act;
+    a.dy[i] = reinterpret_cast<float*>(base + L.off_dy) + i * n;
+  }
+  a.dx[0] = dq; a.dx[1] = dk; a.dx[2] = dv;
+  a.w = conv_w; a.b = conv_b; a.silu = conv_silu;
+  a.part = reinterpret_cast<float*>(base + L.off_part);
+  a.dw = dconv_w; a.db = dconv_b;
+  // chunk table (the core's backward rebuilds the same one), convolution outputs
+  hipLaunchKernelGGL(kda_chunk_table_kernel, dim3(1), dim3(1024), 0, stream, cu, (int)N,
+                     const_cast<int32_t*>(a.cfirst));
+  const dim3 gconv((unsigned)C, (unsigned)H, 3);
+  hipLaunchKernelGGL((kda_conv_apply_kernel<TA>), gconv, dim3(128), 0, stream, a);
+  // the core's backward on the convolution outputs, FP32 gradients
+  const bool cast = sizeof(TR) != 4;
+  float* df32 = reinterpret_cast<float*>(base + L.off_df);
+  float* db32 = reinterpret_cast<float*>(base + L.off_db);
+  const int st = launch_bwd<TA, TG, float>(
+      a.y[0], a.y[1], a.y[2], f, b, A_log, dt_bias, cu, N, T, H, init, dout, dfin,
+      const_cast<float*>(a.dy[0]), const_cast<float*>(a.dy[1]), const_cast<float*>(a.dy[2]),
+      cast ? (void*)df32 : df, cast ? (void*)db32 : db, dA_log, ddt, dinit, ws, stream);
+  if (st != KDA_OK) return st;
+  // input gradients through the convolution, tap and bias gradients
+  hipLaunchKernelGGL((kda_conv_bwd_kernel<TA, TR>), gconv, dim3(128), 0, stream, a);
+  hipLaunchKernelGGL(kda_conv_param_kernel, dim3((unsigned)H, 3), dim3(128), 0, stream, a);
+  if (cast) {
+    const int64_t blocks = ((int64_t)n + 255) / 256 < 8192 ? ((int64_t)n + 255) / 256 : 8192;
+    hipLaunchKernelGGL((kda_cast_kernel<TR>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const float*)df32, df, (int64_t)n);
+    hipLaunchKernelGGL((kda_cast_kernel<TR>), dim3(1024), dim3(256), 0, stream,
+                       (const float*)db32, db, (int64_t)T * H);
+  }
   return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -679,6 +758,71 @@ extern "C" int kda_chunk_bwd(const void* q, const void* k, const void* v, const 
   if (o32) KDA_BWD(kda::bf16, float, float);
   KDA_BWD(kda::bf16, kda::bf16, kda::bf16);
 #undef KDA_BWD
+}
+
+extern "C" size_t kda_chunk_bwd_conv_workspace_bytes(int64_t total_tokens, int32_t num_seqs,
+                                                     int32_t H, int32_t d, uint32_t mode) {
+  if ((mode & ~KDA_MODE_ALL_BITS) || total_tokens < 0 || num_seqs < 1 || H < 1 || d != kda::DH)
+    return (size_t)-1;
+  if (total_tokens == 0) return 0;
+  return kda::conv_bwd_layout(total_tokens, num_seqs, H, mode).total;
+}
+
+extern "C" int kda_chunk_bwd_conv(const void* q, const void* k, const void* v, const void* f_raw,
+                                  const void* b_raw, const float* A_log, const float* dt_bias,
+                                  const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                                  int32_t H, int32_t d, uint32_t mode, const float* conv_weight,
+                                  const float* conv_bias, int32_t conv_silu,
+                                  const float* initial_state, const void* dout,
+                                  const float* dfinal_state, void* dq, void* dk, void* dv,
+                                  void* df_raw, void* db_raw, float* dA_log, float* ddt_bias,
+                                  float* dinitial_state, float* dconv_weight, float* dconv_bias,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  // every host-side check comes before the first HIP call
+  if (mode & ~KDA_MODE_ALL_BITS) return KDA_ERR_INVALID_ARG;
+  if (num_seqs < 1 || total_tokens < 0 || H < 1) return KDA_ERR_INVALID_ARG;
+  if (d != kda::DH) return KDA_ERR_UNSUPPORTED;
+  if (!dA_log || !ddt_bias || !dconv_weight) return KDA_ERR_INVALID_ARG;
+  if (total_tokens > 0) {
+    if (!q || !k || !v || !f_raw || !b_raw || !A_log || !dt_bias || !cu_seqlens || !dout || !dq ||
+        !dk || !dv || !df_raw || !db_raw || !workspace || !conv_weight)
+      return KDA_ERR_INVALID_ARG;
+    if (total_tokens > (int64_t)INT32_MAX / 64 || (int64_t)num_seqs * H > (int64_t)INT32_MAX / 64)
+      return KDA_ERR_UNSUPPORTED;
+    if (!kda::grid_fits(kda::max_chunks(total_tokens, num_seqs), 512) ||
+        !kda::grid_fits(((int64_t)num_seqs * H + 7) / 8, 1))
+      return KDA_ERR_UNSUPPORTED;
+    if (workspace_bytes < kda::conv_bwd_layout(total_tokens, num_seqs, H, mode).total)
+      return KDA_ERR_WORKSPACE;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (total_tokens == 0) {
+    // the core's empty case (dA_log, ddt_bias zeroed, dinitial_state = dfinal_state or 0)
+    // and zero tap / bias gradients
+    const int st = kda_chunk_bwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, num_seqs, 0, H,
+                                 d, mode, initial_state, dout, dfinal_state, dq, dk, dv, df_raw,
+                                 db_raw, dA_log, ddt_bias, dinitial_state, workspace,
+                                 workspace_bytes, stream);
+    if (st != KDA_OK) return st;
+    hipLaunchKernelGGL(kda::kda_state_copy_kernel, dim3(64), dim3(256), 0, s, (const float*)nullptr,
+                       dconv_weight, (int64_t)3 * H * kda::DH * 4);
+    if (dconv_bias)
+      hipLaunchKernelGGL(kda::kda_state_copy_kernel, dim3(16), dim3(256), 0, s,
+                         (const float*)nullptr, dconv_bias, (int64_t)3 * H * kda::DH);
+    return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  }
+  const bool a32 = mode & KDA_ACT_FP32;
+  const bool o32 = (mode & KDA_OUT_FP32) || a32;
+#define KDA_BWDC(TA, TG, TR)                                                                   \
+  return kda::launch_bwd_conv<TA, TG, TR>(                                                    \
+      q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, num_seqs, total_tokens, H, mode,      \
+      conv_weight, conv_bias, conv_silu, initial_state, dout, dfinal_state, dq, dk, dv, df_raw, \
+      db_raw, dA_log, ddt_bias, dinitial_state, dconv_weight, dconv_bias, workspace, s)
+  if (a32) KDA_BWDC(float, float, float);
+  if (o32) KDA_BWDC(kda::bf16, float, float);
+  KDA_BWDC(kda::bf16, kda::bf16, kda::bf16);
+#undef KDA_BWDC
 }
 
 extern "C" const char* kda_status_string(int status) {

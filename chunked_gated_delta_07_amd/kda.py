@@ -26,7 +26,8 @@ KDA_MODE_WINDOWED = 0x8
 # Exported symbols, in declaration order of include/kda.h.
 SYMBOLS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_state",
            "kda_chunk_fwd_conv", "kda_chunk_fwd_rect", "kda_recurrent_fwd", "kda_recurrent_fwd_rect",
-           "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_chunk_fwd_noalloc",
+           "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_chunk_bwd_conv_workspace_bytes",
+           "kda_chunk_bwd_conv", "kda_chunk_fwd_noalloc",
            "kda_chunk_fwd_num_stages", "kda_chunk_fwd_timed", "kda_status_string")
 
 # Size of the library-owned workspace of kda_chunk_fwd_noalloc (kda.h).
@@ -85,6 +86,13 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_bwd.argtypes = ([vp] * 8 + [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                               ctypes.c_int32, ctypes.c_uint32]
                                   + [vp] * 11 + [vp, ctypes.c_size_t, vp])
+    lib.kda_chunk_bwd_conv_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_chunk_bwd_conv_workspace_bytes.argtypes = lib.kda_chunk_fwd_workspace_bytes.argtypes
+    lib.kda_chunk_bwd_conv.restype = ctypes.c_int
+    lib.kda_chunk_bwd_conv.argtypes = ([vp] * 8 + [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                                   ctypes.c_int32, ctypes.c_uint32]
+                                       + [vp, vp, ctypes.c_int32] + [vp] * 13
+                                       + [vp, ctypes.c_size_t, vp])
     lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.kda_chunk_fwd_noalloc.argtypes = fwd_args[:14] + [vp]
     lib.kda_chunk_fwd_timed.restype = ctypes.c_int
@@ -350,11 +358,20 @@ def bwd_workspace_bytes(total_tokens: int, num_seqs: int, H: int, d: int, mode: 
     return int(n)
 
 
+def bwd_conv_workspace_bytes(total_tokens: int, num_seqs: int, H: int, d: int, mode: int) -> int:
+    n = load_library().kda_chunk_bwd_conv_workspace_bytes(int(total_tokens), int(num_seqs),
+                                                          int(H), int(d), int(mode))
+    if n == ctypes.c_size_t(-1).value:
+        raise KdaError(KDA_ERR_INVALID_ARG, "kda_chunk_bwd_conv_workspace_bytes")
+    return int(n)
+
+
 def chunk_bwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, dout, out_fp32=False,
               initial_state=None, dfinal_state=None, return_dinitial_state=False,
-              workspace=None, stream=None):
+              conv_weight=None, conv_bias=None, conv_silu=True, workspace=None, stream=None):
     """Backward (vector-Jacobian product) of the KDA chunked forward through
-    libkda, recomputed in FP32 (kda_chunk_bwd).
+    libkda, recomputed in FP32 (kda_chunk_bwd; kda_chunk_bwd_conv when
+    conv_weight is given).
 
     Inputs as for chunk_fwd, plus dout [T, H, 128] = dL/dout in the forward's
     output dtype (float32 when out_fp32 or float32 activations, else the
@@ -362,7 +379,12 @@ def chunk_bwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, dout, out_fp32=
     Returns a dict: dq, dk, dv, df (= dL/df_raw), db (= dL/db_raw) in dout's
     dtype, dA_log [H] and ddt_bias [H, 128] float32, and dinit [N, H, 128,
     128] float32 when initial_state, dfinal_state or return_dinitial_state is
-    given (the gradient of the start state; zero start if none was given)."""
+    given (the gradient of the start state; zero start if none was given).
+    With conv_weight [3, H, 128, 4] (and optionally conv_bias [3, H, 128],
+    conv_silu) the forward was chunk_fwd with that convolution: dq, dk, dv are
+    then the gradients of the convolution's raw inputs, and the dict also
+    holds dconv_weight [3, H, 128, 4] and dconv_bias [3, H, 128] (when
+    conv_bias is given) in float32."""
     import torch
 
     lib = load_library()
@@ -393,6 +415,16 @@ def chunk_bwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, dout, out_fp32=
         if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != sshape
                               or not t.is_contiguous() or not t.is_cuda):
             raise ValueError("states must be contiguous float32 [N, H, d, d] device tensors")
+    if conv_weight is not None:
+        if (conv_weight.dtype != torch.float32 or tuple(conv_weight.shape) != (3, H, d, 4)
+                or not conv_weight.is_contiguous() or not conv_weight.is_cuda):
+            raise ValueError("conv_weight must be a contiguous float32 [3, H, d, 4] device tensor")
+        if conv_bias is not None and (conv_bias.dtype != torch.float32
+                                      or tuple(conv_bias.shape) != (3, H, d)
+                                      or not conv_bias.is_contiguous() or not conv_bias.is_cuda):
+            raise ValueError("conv_bias must be a contiguous float32 [3, H, d] device tensor")
+    elif conv_bias is not None:
+        raise ValueError("conv_bias needs conv_weight")
     mode = make_mode(True, act_fp32, out_fp32)
     dev = q.device
     g = {"dq": torch.empty((T, H, d), dtype=gdtype, device=dev),
@@ -405,11 +437,27 @@ def chunk_bwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, dout, out_fp32=
     want_dinit = initial_state is not None or dfinal_state is not None or return_dinitial_state
     if want_dinit:
         g["dinit"] = torch.empty(sshape, dtype=torch.float32, device=dev)
-    nbytes = bwd_workspace_bytes(T, max(num_seqs, 1), H, d, mode) if num_seqs >= 1 else 0
+    wsq = bwd_conv_workspace_bytes if conv_weight is not None else bwd_workspace_bytes
+    nbytes = wsq(T, max(num_seqs, 1), H, d, mode) if num_seqs >= 1 else 0
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    if conv_weight is not None:
+        g["dconv_weight"] = torch.empty((3, H, d, 4), dtype=torch.float32, device=dev)
+        if conv_bias is not None:
+            g["dconv_bias"] = torch.empty((3, H, d), dtype=torch.float32, device=dev)
+        st = lib.kda_chunk_bwd_conv(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(f_raw), _ptr(b_raw), _ptr(A_log), _ptr(dt_bias),
+            _ptr(cu_seqlens), num_seqs, T, H, d, mode, _ptr(conv_weight), _ptr(conv_bias),
+            1 if conv_silu else 0, _ptr(initial_state), _ptr(dout), _ptr(dfinal_state),
+            _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["df"]), _ptr(g["db"]),
+            _ptr(g["dA_log"]), _ptr(g["ddt_bias"]), _ptr(g.get("dinit")),
+            _ptr(g["dconv_weight"]), _ptr(g.get("dconv_bias")), _ptr(workspace),
+            workspace.numel(), ctypes.c_void_p(stream.cuda_stream))
+        if st != KDA_OK:
+            raise KdaError(st, "kda_chunk_bwd_conv")
+        return g
     st = lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(f_raw), _ptr(b_raw), _ptr(A_log),
                            _ptr(dt_bias), _ptr(cu_seqlens), num_seqs, T, H, d, mode,
                            _ptr(initial_state), _ptr(dout), _ptr(dfinal_state), _ptr(g["dq"]),

@@ -125,8 +125,8 @@ KDA_API int kda_chunk_fwd(const void* q, const void* k, const void* v, const voi
                   void* stream);
 
 /* kda_chunk_fwd with a start state and an end state per sequence and head.
- * The pages' wrapper has neither (xtuner PR #2301, section Change: "does not
- * add initial/final state"); the sequence-parallel design of xtuner PR #2153
+ * The pages' wrapper takes neither (xtuner PR #2301, section Change: no start
+ * or end state is added); the sequence-parallel design of xtuner PR #2153
  * (contiguous shards exchanging recurrent boundary states) is what needs
  * them: a sequence run in two calls, the second starting from the first
  * call's final state, gives the outputs of one call over the whole sequence.
@@ -267,6 +267,44 @@ KDA_API int kda_chunk_bwd(const void* q, const void* k, const void* v, const voi
                   const float* dfinal_state, void* dq, void* dk, void* dv, void* df_raw,
                   void* db_raw, float* dA_log, float* ddt_bias, float* dinitial_state,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes needed by kda_chunk_bwd_conv (same arguments and failure
+ * value as kda_chunk_fwd_workspace_bytes; the mode decides the activation
+ * dtype of the stored convolution outputs).  kda_chunk_bwd's workspace plus
+ * the three convolution outputs, their FP32 gradients, FP32 gradients of
+ * f_raw and b_raw and per-chunk tap partial sums: about 810 KB per (64-token
+ * chunk, head) with bf16 activations, e.g. 13.3 GB for 16384 tokens x 64
+ * heads. */
+KDA_API size_t kda_chunk_bwd_conv_workspace_bytes(int64_t total_tokens, int32_t num_seqs,
+                                          int32_t H, int32_t d, uint32_t mode);
+
+/* Backward of kda_chunk_fwd_conv: kda_chunk_bwd through the core, then
+ * through the q/k/v short causal convolutions, whose weight and bias
+ * gradients are FP32 (xtuner PR #2153, KDA module description: separate
+ * q/k/v causal convolutions with FP32 master parameters).  With z the
+ * pre-activation of x'_t = act(z_t) and dz_t = dL/dx'_t * act'(z_t):
+ *   dx_u = sum_{i<4} w[i] dz_{u+3-i}   (tokens of u's own sequence),
+ *   dw[i] = sum_t dz_t x_{t-3+i},  dbias = sum_t dz_t   (over all sequences).
+ * The forward rounds x' to the activation dtype; the backward recomputes x'
+ * the same way for the core's backward and takes that rounding as the
+ * identity (its derivative is 1).  Arguments as for kda_chunk_bwd (q, k, v
+ * are the convolution's raw inputs, dq, dk, dv the gradients with respect to
+ * them), plus those of kda_chunk_fwd_conv and:
+ *  dconv_weight : device, [3][H][d][4] float32, required; overwritten.
+ *  dconv_bias   : device, [3][H][d] float32, or NULL (not written).
+ * The tap and bias sums are reduced in a fixed order (deterministic).
+ * total_tokens == 0: as kda_chunk_bwd, and dconv_weight (dconv_bias when
+ * given) is zeroed.  Workspace of kda_chunk_bwd_conv_workspace_bytes bytes;
+ * errors, aliasing and asynchrony as for kda_chunk_bwd. */
+KDA_API int kda_chunk_bwd_conv(const void* q, const void* k, const void* v, const void* f_raw,
+                       const void* b_raw, const float* A_log, const float* dt_bias,
+                       const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                       int32_t H, int32_t d, uint32_t mode, const float* conv_weight,
+                       const float* conv_bias, int32_t conv_silu, const float* initial_state,
+                       const void* dout, const float* dfinal_state, void* dq, void* dk, void* dv,
+                       void* df_raw, void* db_raw, float* dA_log, float* ddt_bias,
+                       float* dinitial_state, float* dconv_weight, float* dconv_bias,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Size of the device array that kda_chunk_fwd_noalloc uses as its workspace
  * (256 MiB, on every GPU the library runs on, held until the process ends). */

@@ -131,6 +131,40 @@ def test_backward_argument_errors_before_launch():
     assert 600e3 < b[-1] / (256 * 64) < 660e3
 
 
+def test_conv_backward_argument_errors_before_launch():
+    """kda_chunk_bwd_conv rejects bad arguments before any HIP call (this runs
+    on a machine without a GPU); its workspace adds the convolution's buffers
+    to the core backward's."""
+    from chunked_gated_delta_07_amd import kda
+
+    lib = kda.load_library()
+    p = ctypes.c_void_p(16)  # never dereferenced: the checks fail first
+
+    def bw(N=1, T=10, H=4, d=128, mode=1, x=p, par=p, cw=p, dcw=p, ws=1 << 40):
+        return lib.kda_chunk_bwd_conv(*([x] * 8), N, T, H, d, mode, cw, None, 1, None, x, None,
+                                      x, x, x, x, x, par, par, None, dcw, None, x, ws, None)
+
+    assert bw(x=None) == kda.KDA_ERR_INVALID_ARG
+    assert bw(par=None) == kda.KDA_ERR_INVALID_ARG
+    assert bw(cw=None) == kda.KDA_ERR_INVALID_ARG     # the convolution's weights are required
+    assert bw(dcw=None) == kda.KDA_ERR_INVALID_ARG    # and so is their gradient
+    assert bw(T=0, dcw=None) == kda.KDA_ERR_INVALID_ARG
+    assert bw(N=0) == kda.KDA_ERR_INVALID_ARG
+    assert bw(mode=0x10) == kda.KDA_ERR_INVALID_ARG
+    assert bw(d=64) == kda.KDA_ERR_UNSUPPORTED
+    assert bw(ws=1) == kda.KDA_ERR_WORKSPACE
+    n = (1 << 23) - 1
+    assert bw(N=n, T=n, H=1, ws=1) == kda.KDA_ERR_WORKSPACE
+    assert bw(N=1 << 24, T=1 << 24, H=1) == kda.KDA_ERR_UNSUPPORTED
+    assert kda.bwd_conv_workspace_bytes(0, 1, 64, 128, 1) == 0
+    for T in (1, 64, 65, 16384):
+        for mode in (1, 1 | kda.KDA_ACT_FP32):
+            c = kda.bwd_conv_workspace_bytes(T, 1, 64, 128, mode)
+            assert c % 256 == 0 and c > kda.bwd_workspace_bytes(T, 1, 64, 128, mode)
+    c = kda.bwd_conv_workspace_bytes(16384, 1, 64, 128, 1)
+    assert 780e3 < c / (256 * 64) < 850e3
+
+
 def test_grid_limits_rejected_before_launch():
     """A dispatch counts each grid dimension in work-items with a 32-bit field.
     Sizes whose grids would not fit return KDA_ERR_UNSUPPORTED from the host

@@ -322,8 +322,14 @@ def time_conv(args_dev, steps: int, warmup: int):
             "tokens_per_s": round(T / (p50 * 1e-6), 1)}
 
 
+def progress(msg: str):
+    """One progress line on stderr (stdout carries only the result line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def time_bwd(args_dev, steps: int, warmup: int):
-    """kda_chunk_bwd on the headline workload: the FP32-recomputed backward
+    """kda_chunk_bwd (and kda_chunk_bwd_conv, the q/k/v convolution in front)
+    on the headline workload: the FP32-recomputed backward
     with bf16 activations, bf16 output gradient and bf16 input gradients
     (the pages' training path casts input gradients back to the activation
     dtype), a random dout.  Step time from HIP events on the launch stream."""
@@ -336,22 +342,37 @@ def time_bwd(args_dev, steps: int, warmup: int):
     g = torch.Generator().manual_seed(4245)
     dout = torch.randn((T, H, d), generator=g).to(torch.bfloat16).to(q.device)
     N = args_dev[7].numel() - 1
-    ws = torch.empty(kda.bwd_workspace_bytes(T, N, H, d, kda.make_mode(True)), dtype=torch.uint8,
-                     device=q.device)
-    for _ in range(warmup):
-        kda.chunk_bwd(*args_dev, dout, workspace=ws)
-    stream = torch.cuda.current_stream()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    torch.cuda.synchronize()
-    for a, e in evs:
-        a.record(stream)
-        kda.chunk_bwd(*args_dev, dout, workspace=ws)
-        e.record(stream)
-    torch.cuda.synchronize()
-    us = sorted(a.elapsed_time(e) * 1e3 for a, e in evs)
+    mode = kda.make_mode(True)
+
+    def timed(call):
+        for _ in range(warmup):
+            call()
+        stream = torch.cuda.current_stream()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        torch.cuda.synchronize()
+        for a, e in evs:
+            a.record(stream)
+            call()
+            e.record(stream)
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(e) * 1e3 for a, e in evs)
+
+    ws = torch.empty(kda.bwd_workspace_bytes(T, N, H, d, mode), dtype=torch.uint8, device=q.device)
+    us = timed(lambda: kda.chunk_bwd(*args_dev, dout, workspace=ws))
     p50 = statistics.median(us)
     del ws
+    # the same with the q/k/v short convolution in front (kda_chunk_bwd_conv)
+    gw = torch.Generator().manual_seed(4244)
+    cw = (0.5 * torch.randn((3, H, d, 4), generator=gw)).to(q.device)
+    cb = (0.1 * torch.randn((3, H, d), generator=gw)).to(q.device)
+    wsc = torch.empty(kda.bwd_conv_workspace_bytes(T, N, H, d, mode), dtype=torch.uint8,
+                      device=q.device)
+    usc = timed(lambda: kda.chunk_bwd(*args_dev, dout, conv_weight=cw, conv_bias=cb,
+                                      conv_silu=True, workspace=wsc))
+    conv = {"entry_point": "kda_chunk_bwd_conv", "p50_us": round(statistics.median(usc), 2),
+            "max_us": round(usc[-1], 2), "workspace_bytes": wsc.numel()}
+    del wsc
     # algorithmic FLOP of a vector-Jacobian product: twice the forward's
     # (every product of the forward has two adjoint products)
     flop = 2 * FLOP_PER_TH * T * H
@@ -359,6 +380,8 @@ def time_bwd(args_dev, steps: int, warmup: int):
     return {"entry_point": "kda_chunk_bwd", "workload": "headline, dout bf16, gradients bf16",
             "intermediates": "fp32", "p50_us": round(p50, 2), "max_us": round(us[-1], 2),
             "tokens_per_s": round(T / (p50 * 1e-6), 1),
+            "workspace_bytes": kda.bwd_workspace_bytes(T, N, H, d, mode),
+            "with_conv": conv,
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_FP32_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / MFMA_FP32_TFLOPS, 4),
                          "flop_per_token_head": 2 * FLOP_PER_TH}}
@@ -615,12 +638,14 @@ def main():
     torch.cuda.synchronize()
     modes = ["bf16", "fp32"] if args.only_mode is None else [args.only_mode]
     res = {m: time_mode(args_dev, m == "fp32", args.steps, args.warmup) for m in modes}
+    progress("launched steps timed")
     graph = {m: time_graph(args_dev, m == "fp32") for m in modes} if args.only_mode is None else {}
     # the headline ms_per_step: K graph-replayed steps (stage times above come
     # from the event-instrumented launches of time_mode)
     for m in modes:
         res[m]["ms_per_step_launched"] = res[m]["ms_per_step"]
         res[m]["ms_per_step"] = time_steps_graph(args_dev, m == "fp32", args.steps, args.warmup)
+    progress("graph-replayed steps timed")
     head = modes[0]
     r = res[head]
     line = {
@@ -674,10 +699,13 @@ def main():
             "stage_avg_us": {n: round(x, 2) for n, x in zip(tp["stage_names"], tp["stage_avg_us"])}}
     if args.only_mode is None:
         line["conv_fused"] = time_conv(args_dev, max(args.steps, 10), max(args.warmup, 2))
+        progress("fused convolution timed")
     if not args.no_bwd and args.only_mode is None:
         line["backward"] = time_bwd(args_dev, max(args.steps // 2, 5), max(args.warmup, 2))
+        progress("backward timed")
     if not args.no_decode and args.only_mode is None:
         line["decode"] = time_decode(256, H, max(args.steps, 10), max(args.warmup, 2))
+        progress("decode timed")
     if not args.no_peaks:
         mp = measured_peaks()
         line["measured_peaks"] = mp

@@ -98,7 +98,7 @@ def cpu_baseline(T: int, budget_s: float):
         oracle.kda_forward(**f64)
         dt += time.perf_counter() - t0
         reps += 1
-    return {"value": T * nh * reps / H_total / dt, "unit": "tokens/s", "cores": threads,
+    return {"value": T * nh * reps / H_total / dt, "unit": "tokens/s", "cores": min(threads, nh),
             "kind": "oracle",
             "sample": f"{T} tokens x {nh} of {H_total} heads (bf16 inputs, FP64 token-serial "
                       f"recurrence, OpenMP over heads) x {reps} runs, {dt:.1f} s; scaled to 64 heads"}
@@ -528,7 +528,8 @@ def cpu_oracle_timing(inp, heads, threads=None):
     if threads:
         oracle.set_num_threads(threads)
     try:
-        used = oracle.num_threads()
+        # the oracle parallelises over (sequence, head) pairs
+        used = min(oracle.num_threads(), (len(inp.cu_seqlens) - 1) * len(heads))
         t0 = time.perf_counter()
         oracle.kda_forward(**sub)
         dt = time.perf_counter() - t0
@@ -577,7 +578,8 @@ def time_configs(no_cpu: bool):
         del args_dev
         torch.cuda.empty_cache()
         if not no_cpu:
-            nh = {0: 64, 1: 64, 2: 16, 3: 4, 4: 4}[i]
+            # enough heads that every (sequence, head) thread of the oracle has work
+            nh = {0: 64, 1: 64, 2: 16, 3: 16, 4: 16}[i]
             heads = list(np.linspace(0, inp.H - 1, nh).astype(int))
             rec["cpu_oracle"] = cpu_oracle_timing(inp, heads)
             if i <= 2:

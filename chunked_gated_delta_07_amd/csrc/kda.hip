@@ -21,12 +21,35 @@ namespace kda {
 // at every sequence start: packed offsets, xtuner PR #2301 section Change).
 // One workgroup of 1024 threads; each thread owns a contiguous slice of
 // sequences.  Also writes cfirst[N] = total chunks.
+// With a status pointer (KDA_MODE_CHECK_CU) the offsets are checked first:
+// bit 0 cu[0] != 0, bit 1 a decrease, bit 2 cu[N] != T.  The code is stored at
+// *status (0: valid); when it is not 0 the table says every sequence is empty,
+// so no later kernel touches token data (every token range is derived from it).
 __global__ __launch_bounds__(1024) void kda_chunk_table_kernel(const int32_t* __restrict__ cu, int N,
-                                                                int32_t* __restrict__ cfirst) {
+                                                                int32_t* __restrict__ cfirst,
+                                                                int64_t T, int32_t* __restrict__ status) {
   __shared__ int32_t part[1024];
+  __shared__ int32_t bad;
   const int tid = threadIdx.x;
   const int per = (N + 1023) / 1024;
   const int lo = min(N, tid * per), hi = min(N, lo + per);
+  if (status) {
+    if (tid == 0) bad = 0;
+    __syncthreads();
+    int code = 0;
+    for (int n = lo; n < hi; ++n)
+      if (cu[n + 1] < cu[n]) code |= 2;
+    if (tid == 0 && cu[0] != 0) code |= 1;
+    if (tid == 0 && (int64_t)cu[N] != T) code |= 4;
+    if (code) atomicOr(&bad, code);
+    __syncthreads();
+    if (bad) {
+      for (int n = tid; n <= N; n += 1024) cfirst[n] = 0;
+      if (tid == 0) *status = bad;
+      return;
+    }
+    if (tid == 0) *status = 0;
+  }
   int32_t s = 0;
   for (int n = lo; n < hi; ++n) s += (cu[n + 1] - cu[n] + CHUNK - 1) / CHUNK;
   part[tid] = s;
@@ -50,6 +73,16 @@ __global__ __launch_bounds__(1024) void kda_chunk_table_kernel(const int32_t* __
 // blocks x threads must stay below 2^32 in every dimension.
 static inline bool grid_fits(int64_t blocks, int64_t threads) {
   return blocks >= 0 && blocks * threads <= (int64_t)UINT32_MAX;
+}
+
+// The chunk table (checked when `check`); a single unchecked sequence needs
+// none (its chunk c starts at token 64 c) and gets a null table.
+static inline int32_t* launch_table(const int32_t* cu, int32_t N, int64_t T, int32_t* cfirst,
+                                    void* ws, bool check, hipStream_t stream) {
+  if (N == 1 && !check) return nullptr;
+  hipLaunchKernelGGL(kda_chunk_table_kernel, dim3(1), dim3(1024), 0, stream, cu, (int)N, cfirst, T,
+                     check ? reinterpret_cast<int32_t*>(ws) : (int32_t*)nullptr);
+  return cfirst;
 }
 
 // ------------------------------------------------------------ workspace
@@ -87,8 +120,8 @@ static inline WsLayout ws_layout(int64_t T, int32_t N, int32_t H, uint32_t mode)
   const bool win = use_windows(N, mode);
   const int64_t C = win ? ring_chunks(T, N) : max_chunks(T, N);
   WsLayout L;
-  L.off_cfirst = 0;
-  L.off_gam = align256(sizeof(int32_t) * (size_t)(N + 1));
+  L.off_cfirst = 256;  // [0, 4): status word of KDA_MODE_CHECK_CU
+  L.off_gam = L.off_cfirst + align256(sizeof(int32_t) * (size_t)(N + 1));
   L.off_rec = L.off_gam + align256(sizeof(float) * (size_t)C * H * DH);
   L.off_carry = L.off_rec + align256(mt * (size_t)C * H * (win ? RECW : REC));
   L.total = L.off_carry + (win ? align256(sizeof(float) * 2 * (size_t)H * DH * DH) : 0);
@@ -117,9 +150,7 @@ static int launch_all(const void* q, const void* k, const void* v, const void* f
   const int64_t C = max_chunks(T, N);
 
   if (ev) (void)hipEventRecord(ev[0], stream);
-  // a single sequence needs no table: its chunk c starts at token 64 c
-  if (N == 1) cfirst = nullptr;
-  else hipLaunchKernelGGL(kda_chunk_table_kernel, dim3(1), dim3(1024), 0, stream, cu, (int)N, cfirst);
+  cfirst = launch_table(cu, N, T, cfirst, ws, mode & KDA_MODE_CHECK_CU, stream);
   if (ev) (void)hipEventRecord(ev[1], stream);
 
   IntraArgs ia;
@@ -172,8 +203,7 @@ static int launch_windows(const void* q, const void* k, const void* v, const voi
   const int64_t nwin = (C + W - 1) / W;
 
   if (ev) (void)hipEventRecord(ev[0], stream);
-  if (N == 1) cfirst = nullptr;
-  else hipLaunchKernelGGL(kda_chunk_table_kernel, dim3(1), dim3(1024), 0, stream, cu, (int)N, cfirst);
+  cfirst = launch_table(cu, N, T, cfirst, ws, mode & KDA_MODE_CHECK_CU, stream);
   if (ev) (void)hipEventRecord(ev[1], stream);
 
   WinArgs wa;
@@ -252,7 +282,7 @@ struct BwdLayout {
 static inline BwdLayout bwd_layout(int64_t T, int32_t N, int32_t H) {
   const size_t CH = (size_t)max_chunks(T, N) * H;
   BwdLayout L;
-  size_t o = 0;
+  size_t o = 256;  // [0, 4): status word of KDA_MODE_CHECK_CU
   auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
   L.off_cfirst = take(sizeof(int32_t) * (size_t)(N + 1));
   L.off_gam = take(4 * CH * DH);
@@ -284,13 +314,15 @@ static int launch_bwd(const void* q, const void* k, const void* v, const void* f
                       const float* A_log, const float* dt_bias, const int32_t* cu, int32_t N,
                       int64_t T, int32_t H, const float* init, const void* dout, const float* dfin,
                       void* dq, void* dk, void* dv, void* df, void* db, float* dA_log, float* ddt,
-                      float* dinit, void* ws, hipStream_t stream) {
+                      float* dinit, void* ws, hipStream_t stream, bool check) {
   const BwdLayout L = bwd_layout(T, N, H);
   char* base = reinterpret_cast<char*>(ws);
   auto fp = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
   int32_t* cfirst = reinterpret_cast<int32_t*>(base + L.off_cfirst);
   const int64_t C = max_chunks(T, N);
-  hipLaunchKernelGGL(kda_chunk_table_kernel, dim3(1), dim3(1024), 0, stream, cu, (int)N, cfirst);
+  // the backward's kernels always take a table
+  hipLaunchKernelGGL(kda_chunk_table_kernel, dim3(1), dim3(1024), 0, stream, cu, (int)N, cfirst, T,
+                     check ? reinterpret_cast<int32_t*>(ws) : (int32_t*)nullptr);
 
   IntraArgs ia;
   ia.q = q; ia.k = k; ia.v = v; ia.f = f; ia.b = b;
@@ -381,8 +413,10 @@ static int launch_bwd_conv(const void* q, const void* k, const void* v, const vo
   a.part = reinterpret_cast<float*>(base + L.off_part);
   a.dw = dconv_w; a.db = dconv_b;
   // chunk table (the core's backward rebuilds the same one), convolution outputs
+  const bool check = mode & KDA_MODE_CHECK_CU;
   hipLaunchKernelGGL(kda_chunk_table_kernel, dim3(1), dim3(1024), 0, stream, cu, (int)N,
-                     const_cast<int32_t*>(a.cfirst));
+                     const_cast<int32_t*>(a.cfirst), T,
+                     check ? reinterpret_cast<int32_t*>(ws) : (int32_t*)nullptr);
   const dim3 gconv((unsigned)C, (unsigned)H, 3);
   hipLaunchKernelGGL((kda_conv_apply_kernel<TA>), gconv, dim3(128), 0, stream, a);
   // the core's backward on the convolution outputs, FP32 gradients
@@ -392,7 +426,7 @@ static int launch_bwd_conv(const void* q, const void* k, const void* v, const vo
   const int st = launch_bwd<TA, TG, float>(
       a.y[0], a.y[1], a.y[2], f, b, A_log, dt_bias, cu, N, T, H, init, dout, dfin,
       const_cast<float*>(a.dy[0]), const_cast<float*>(a.dy[1]), const_cast<float*>(a.dy[2]),
-      cast ? (void*)df32 : df, cast ? (void*)db32 : db, dA_log, ddt, dinit, ws, stream);
+      cast ? (void*)df32 : df, cast ? (void*)db32 : db, dA_log, ddt, dinit, ws, stream, check);
   if (st != KDA_OK) return st;
   // input gradients through the convolution, tap and bias gradients
   hipLaunchKernelGGL((kda_conv_bwd_kernel<TA, TR>), gconv, dim3(128), 0, stream, a);
@@ -520,6 +554,7 @@ extern "C" int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v
                                      uint32_t mode, void* out, void* stream) {
   // every size check comes before the first HIP call; a workspace larger than
   // the library's array is refused
+  if (mode & KDA_MODE_CHECK_CU) return (mode & ~KDA_MODE_ALL_BITS) ? KDA_ERR_INVALID_ARG : KDA_ERR_UNSUPPORTED;
   const size_t need = kda_chunk_fwd_workspace_bytes(total_tokens, num_seqs, H, d, mode);
   if (need == (size_t)-1) {
     if (mode & ~KDA_MODE_ALL_BITS) return KDA_ERR_INVALID_ARG;
@@ -647,6 +682,7 @@ static int recurrent_impl(const void* q, const void* k, const void* v, const voi
                           int32_t H, int32_t dk, int32_t dv, uint32_t mode, void* out,
                           const float* initial_state, float* final_state, void* stream) {
   if (mode & ~KDA_MODE_ALL_BITS) return KDA_ERR_INVALID_ARG;
+  if (mode & KDA_MODE_CHECK_CU) return KDA_ERR_UNSUPPORTED;  // no workspace to report into
   if (num_seqs < 1 || total_tokens < 0 || H < 1 || dk < 1 || dv < 1) return KDA_ERR_INVALID_ARG;
   if ((dk != 16 && dk != 32 && dk != 64 && dk != 128) || dv > kda::rec_max_threads(dk))
     return KDA_ERR_UNSUPPORTED;
@@ -753,7 +789,7 @@ extern "C" int kda_chunk_bwd(const void* q, const void* k, const void* v, const 
   return kda::launch_bwd<TA, TG, TR>(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, num_seqs, \
                                      total_tokens, H, initial_state, dout, dfinal_state, dq, dk, \
                                      dv, df_raw, db_raw, dA_log, ddt_bias, dinitial_state,       \
-                                     workspace, s)
+                                     workspace, s, (mode & KDA_MODE_CHECK_CU) != 0)
   if (a32) KDA_BWD(float, float, float);
   if (o32) KDA_BWD(kda::bf16, float, float);
   KDA_BWD(kda::bf16, kda::bf16, kda::bf16);

@@ -309,7 +309,9 @@ __device__ __forceinline__ void win_scan(const WinArgs& p, int seg, int h, char*
   if (cb == ce) {
     // an empty sequence: its end state is its start state, written once (by
     // the window its position falls in, or the last one)
-    const int nwin = (Ctot + p.W - 1) / p.W;
+    // (at least one window: with no chunks at all, as after a failed
+    // cu_seqlens check, every sequence is empty and window 0 writes them)
+    const int nwin = max(1, (Ctot + p.W - 1) / p.W);
     if (min(cb / p.W, nwin - 1) != win || !p.fin) return;
 #pragma unroll
     for (int t = 0; t < 4; ++t)

@@ -22,6 +22,7 @@ KDA_MODE_FP32_INTERMEDIATE = 0x1
 KDA_ACT_FP32 = 0x2
 KDA_OUT_FP32 = 0x4
 KDA_MODE_WINDOWED = 0x8
+KDA_MODE_CHECK_CU = 0x10
 
 # Exported symbols, in declaration order of include/kda.h.
 SYMBOLS = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_state",
@@ -127,10 +128,18 @@ def num_stages(total_tokens: int, num_seqs: int, H: int, mode: int) -> int:
 
 
 def make_mode(fp32_intermediate: bool, act_fp32: bool = False, out_fp32: bool = False,
-              windowed: bool = False) -> int:
+              windowed: bool = False, check_cu: bool = False) -> int:
     return ((KDA_MODE_FP32_INTERMEDIATE if fp32_intermediate else 0)
             | (KDA_ACT_FP32 if act_fp32 else 0) | (KDA_OUT_FP32 if out_fp32 else 0)
-            | (KDA_MODE_WINDOWED if windowed else 0))
+            | (KDA_MODE_WINDOWED if windowed else 0) | (KDA_MODE_CHECK_CU if check_cu else 0))
+
+
+def check_status(workspace) -> int:
+    """The code a call with check_cu=True left in its workspace (read after
+    the call has completed; this synchronises on the workspace's device):
+    0 when cu_seqlens was valid, else bit 0 (cu_seqlens[0] != 0), bit 1 (a
+    decrease), bit 2 (the last offset differs from the token count)."""
+    return int(workspace[:4].view(__import__("torch").int32).item())
 
 
 def _ptr(t):
@@ -141,7 +150,7 @@ def chunk_fwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, fp32_intermedia
               out_fp32=False, out=None, workspace=None, stream=None, events=None,
               initial_state=None, final_state=None, return_final_state=False,
               conv_weight=None, conv_bias=None, conv_silu=True, noalloc=False,
-              windowed=False):
+              windowed=False, check_cu=False):
     """KDA chunked forward through libkda.
 
     q, k, v, f_raw: [T, H, 128] bfloat16 or float32 (one dtype for all);
@@ -155,6 +164,9 @@ def chunk_fwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, fp32_intermedia
     objects recorded between the stages (kda_chunk_fwd_timed).
     ``windowed=True`` sets KDA_MODE_WINDOWED (schedule only: the pipeline of
     24-chunk windows whose workspace does not grow with the length).
+    ``check_cu=True`` sets KDA_MODE_CHECK_CU: the device validates cu_seqlens
+    first and, if invalid, touches no token data; pass a ``workspace`` and
+    read the code with check_status(workspace) afterwards.
     ``initial_state``: optional [N, H, 128, 128] float32 start states (key,
     value); ``final_state`` (a tensor of that shape to fill, may be the
     initial_state tensor) or ``return_final_state=True`` (allocated) selects
@@ -188,7 +200,7 @@ def chunk_fwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, fp32_intermedia
     if b_raw.shape != (T, H) or A_log.shape != (H,) or dt_bias.shape != (H, d):
         raise ValueError("b_raw [T,H], A_log [H], dt_bias [H,dk] expected")
     num_seqs = cu_seqlens.numel() - 1
-    mode = make_mode(fp32_intermediate, act_fp32, out_fp32, windowed)
+    mode = make_mode(fp32_intermediate, act_fp32, out_fp32, windowed, check_cu)
     out_dtype = torch.float32 if (out_fp32 or act_fp32) else q.dtype
     if out is None:
         out = torch.empty((T, H, dv), dtype=out_dtype, device=q.device)
@@ -368,7 +380,8 @@ def bwd_conv_workspace_bytes(total_tokens: int, num_seqs: int, H: int, d: int, m
 
 def chunk_bwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, dout, out_fp32=False,
               initial_state=None, dfinal_state=None, return_dinitial_state=False,
-              conv_weight=None, conv_bias=None, conv_silu=True, workspace=None, stream=None):
+              conv_weight=None, conv_bias=None, conv_silu=True, workspace=None, stream=None,
+              check_cu=False):
     """Backward (vector-Jacobian product) of the KDA chunked forward through
     libkda, recomputed in FP32 (kda_chunk_bwd; kda_chunk_bwd_conv when
     conv_weight is given).
@@ -384,7 +397,7 @@ def chunk_bwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, dout, out_fp32=
     conv_silu) the forward was chunk_fwd with that convolution: dq, dk, dv are
     then the gradients of the convolution's raw inputs, and the dict also
     holds dconv_weight [3, H, 128, 4] and dconv_bias [3, H, 128] (when
-    conv_bias is given) in float32."""
+    conv_bias is given) in float32.  ``check_cu`` as for chunk_fwd."""
     import torch
 
     lib = load_library()
@@ -425,7 +438,7 @@ def chunk_bwd(q, k, v, f_raw, b_raw, A_log, dt_bias, cu_seqlens, dout, out_fp32=
             raise ValueError("conv_bias must be a contiguous float32 [3, H, d] device tensor")
     elif conv_bias is not None:
         raise ValueError("conv_bias needs conv_weight")
-    mode = make_mode(True, act_fp32, out_fp32)
+    mode = make_mode(True, act_fp32, out_fp32, check_cu=check_cu)
     dev = q.device
     g = {"dq": torch.empty((T, H, d), dtype=gdtype, device=dev),
          "dk": torch.empty((T, H, d), dtype=gdtype, device=dev),

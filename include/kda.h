@@ -80,12 +80,28 @@ extern "C" {
  *   window and the state pass over the window before, and the records live in
  *   a ring of two windows, so the workspace stops growing with the sequence
  *   length (230 MB instead of 1.2 GB at 16384 tokens x 64 heads).  Ignored
- *   with FP32 intermediates or more than 64 sequences. */
+ *   with FP32 intermediates or more than 64 sequences.
+ * KDA_MODE_CHECK_CU: debugging aid.  The device checks cu_seqlens before any
+ *   kernel reads token data: cu_seqlens[0] == 0, non-decreasing,
+ *   cu_seqlens[num_seqs] == total_tokens.  It stores a code in the first 4
+ *   bytes of the workspace (int32, readable once the call has completed):
+ *   0 when valid, else bit 0 (cu_seqlens[0] != 0) | bit 1 (a decrease) |
+ *   bit 2 (last offset != total_tokens).  When the code is not 0 every
+ *   sequence is treated as empty: no token data is read or written (out and
+ *   the input gradients are left as they were), end states are the start
+ *   states (zero without), the parameter gradients are zero and the start-state
+ *   gradient is the end-state gradient.  Cost: one small launch.  Taken by the chunked forward entry points
+ *   and the backward ones when total_tokens > 0 (with total_tokens == 0
+ *   nothing is launched and no code is written); kda_chunk_fwd_noalloc and the
+ *   token-serial entry points, which have no workspace to report into, return
+ *   KDA_ERR_UNSUPPORTED for it.  Without the bit the offsets are a
+ *   precondition and are not checked. */
 #define KDA_MODE_FP32_INTERMEDIATE 0x1u
 #define KDA_ACT_FP32 0x2u
 #define KDA_OUT_FP32 0x4u
 #define KDA_MODE_WINDOWED 0x8u
-#define KDA_MODE_ALL_BITS 0xFu
+#define KDA_MODE_CHECK_CU 0x10u
+#define KDA_MODE_ALL_BITS 0x1Fu
 
 /* Bytes of caller-provided scratch that kda_chunk_fwd needs for this shape.
  * Depends only on the arguments; non-decreasing in total_tokens.  Two

@@ -59,7 +59,7 @@ def test_argument_errors_before_launch():
     assert _call(lib, H=0) == kda.KDA_ERR_INVALID_ARG                 # H < 1
     assert _call(lib, N=0) == kda.KDA_ERR_INVALID_ARG                 # num_seqs < 1
     assert _call(lib, T=-1) == kda.KDA_ERR_INVALID_ARG                # negative T
-    assert _call(lib, mode=0x10) == kda.KDA_ERR_INVALID_ARG           # unknown mode bit
+    assert _call(lib, mode=0x20) == kda.KDA_ERR_INVALID_ARG           # unknown mode bit
     assert _call(lib, d=64) == kda.KDA_ERR_UNSUPPORTED                # d != 128
     assert _call(lib, ws_bytes=1) == kda.KDA_ERR_WORKSPACE            # workspace too small
     assert _call(lib, T=0, ptrs=False) == kda.KDA_OK                  # empty batch: no-op
@@ -90,8 +90,9 @@ def test_argument_errors_before_launch():
     assert rc(p=None) == kda.KDA_ERR_INVALID_ARG
     assert rc(N=0) == kda.KDA_ERR_INVALID_ARG
     assert rc(H=0) == kda.KDA_ERR_INVALID_ARG
-    assert rc(mode=0x10) == kda.KDA_ERR_INVALID_ARG
+    assert rc(mode=0x20) == kda.KDA_ERR_INVALID_ARG
     assert rc(d=64) == kda.KDA_ERR_UNSUPPORTED
+    assert rc(mode=kda.KDA_MODE_CHECK_CU) == kda.KDA_ERR_UNSUPPORTED  # no workspace to report into
     assert rc(T=0, p=None) == kda.KDA_OK  # nothing to compute or copy
     rr = lambda dk, dv: lib.kda_recurrent_fwd_rect(*([p] * 8), 1, 10, 4, dk, dv, 0, p, None, None,
                                                    None)
@@ -118,7 +119,7 @@ def test_backward_argument_errors_before_launch():
     assert bw(N=0) == kda.KDA_ERR_INVALID_ARG
     assert bw(H=0) == kda.KDA_ERR_INVALID_ARG
     assert bw(T=-1) == kda.KDA_ERR_INVALID_ARG
-    assert bw(mode=0x10) == kda.KDA_ERR_INVALID_ARG
+    assert bw(mode=0x20) == kda.KDA_ERR_INVALID_ARG
     assert bw(d=64) == kda.KDA_ERR_UNSUPPORTED
     assert bw(ws=1) == kda.KDA_ERR_WORKSPACE
     assert bw(T=0, par=None) == kda.KDA_ERR_INVALID_ARG  # still required for an empty batch
@@ -150,7 +151,7 @@ def test_conv_backward_argument_errors_before_launch():
     assert bw(dcw=None) == kda.KDA_ERR_INVALID_ARG    # and so is their gradient
     assert bw(T=0, dcw=None) == kda.KDA_ERR_INVALID_ARG
     assert bw(N=0) == kda.KDA_ERR_INVALID_ARG
-    assert bw(mode=0x10) == kda.KDA_ERR_INVALID_ARG
+    assert bw(mode=0x20) == kda.KDA_ERR_INVALID_ARG
     assert bw(d=64) == kda.KDA_ERR_UNSUPPORTED
     assert bw(ws=1) == kda.KDA_ERR_WORKSPACE
     n = (1 << 23) - 1
@@ -163,6 +164,27 @@ def test_conv_backward_argument_errors_before_launch():
             assert c % 256 == 0 and c > kda.bwd_workspace_bytes(T, 1, 64, 128, mode)
     c = kda.bwd_conv_workspace_bytes(16384, 1, 64, 128, 1)
     assert 780e3 < c / (256 * 64) < 850e3
+
+
+def test_check_cu_bit_before_launch():
+    """KDA_MODE_CHECK_CU (device-side cu_seqlens check) changes no workspace
+    size, and the entry points without a workspace refuse it before any HIP
+    call (this runs on a machine without a GPU)."""
+    from chunked_gated_delta_07_amd import kda
+
+    lib = kda.load_library()
+    C = kda.KDA_MODE_CHECK_CU
+    for T, N in ((1, 1), (16384, 1), (5000, 7)):
+        for m in (0, 1, kda.KDA_MODE_WINDOWED):
+            assert kda.workspace_bytes(T, N, 64, 128, m | C) == kda.workspace_bytes(T, N, 64, 128, m)
+        assert kda.bwd_workspace_bytes(T, N, 64, 128, 1 | C) == kda.bwd_workspace_bytes(T, N, 64, 128, 1)
+        assert kda.num_stages(T, N, 64, C) == kda.num_stages(T, N, 64, 0)
+    p = ctypes.c_void_p(16)  # never dereferenced: the checks fail first
+    assert lib.kda_chunk_fwd_noalloc(*([p] * 8), 1, 10, 4, 128, C, p, None) == kda.KDA_ERR_UNSUPPORTED
+    assert lib.kda_chunk_fwd_noalloc(*([p] * 8), 1, 10, 4, 128, C | 0x20, p, None) == \
+        kda.KDA_ERR_INVALID_ARG
+    assert lib.kda_recurrent_fwd_rect(*([p] * 8), 1, 10, 4, 16, 24, C, p, None, None, None) == \
+        kda.KDA_ERR_UNSUPPORTED
 
 
 def test_grid_limits_rejected_before_launch():
@@ -200,7 +222,7 @@ def test_workspace_query():
     with pytest.raises(kda.KdaError):
         kda.workspace_bytes(10, 1, 64, 64, 0)
     with pytest.raises(kda.KdaError):
-        kda.workspace_bytes(10, 1, 64, 128, 0x10)
+        kda.workspace_bytes(10, 1, 64, 128, 0x20)
     prev = 0
     for T in (1, 63, 64, 65, 1000, 16384):
         for N in (1, 2, 7):

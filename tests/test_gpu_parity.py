@@ -207,12 +207,14 @@ def test_intra_records_match_chunk_oracle():
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda:0")
     U.run_gpu(inp, True, True, workspace=ws)
     wsb = ws.cpu().numpy()
-    # layout: cfirst [(N+1) int32] | gam [C][H][128] f32 | rec [C][H][REC] f32 (256-aligned parts)
+    # layout: status word (256 B) | cfirst [(N+1) int32] | gam [C][H][128] f32 |
+    # rec [C][H][REC] f32 (256-aligned parts)
     al = lambda x: (x + 255) // 256 * 256
     Cmax = (T + 63 * min(N, T)) // 64
-    off_gam = al(4 * (N + 1))
+    off_cfirst = 256
+    off_gam = off_cfirst + al(4 * (N + 1))
     off_rec = off_gam + al(4 * Cmax * H * 128)
-    cfirst = wsb[:4 * (N + 1)].view(np.int32)
+    cfirst = wsb[off_cfirst:off_cfirst + 4 * (N + 1)].view(np.int32)
     nc = int(cfirst[-1])
     REC = 4 * 64 * 128 + 64 * 64
     gam = wsb[off_gam:off_gam + 4 * nc * H * 128].view(np.float32).reshape(nc, H, 128)

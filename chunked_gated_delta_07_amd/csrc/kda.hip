@@ -417,8 +417,8 @@ static int launch_bwd_conv(const void* q, const void* k, const void* v, const vo
   hipLaunchKernelGGL(kda_chunk_table_kernel, dim3(1), dim3(1024), 0, stream, cu, (int)N,
                      const_cast<int32_t*>(a.cfirst), T,
                      check ? reinterpret_cast<int32_t*>(ws) : (int32_t*)nullptr);
-  const dim3 gconv((unsigned)C, (unsigned)H, 3);
-  hipLaunchKernelGGL((kda_conv_apply_kernel<TA>), gconv, dim3(128), 0, stream, a);
+  const dim3 gconv((unsigned)C, (unsigned)((H + CONV_HEADS_PER_BLOCK - 1) / CONV_HEADS_PER_BLOCK), 3);
+  hipLaunchKernelGGL((kda_conv_apply_kernel<TA>), gconv, dim3(256), 0, stream, a);
   // the core's backward on the convolution outputs, FP32 gradients
   const bool cast = sizeof(TR) != 4;
   float* df32 = reinterpret_cast<float*>(base + L.off_df);
@@ -429,7 +429,7 @@ static int launch_bwd_conv(const void* q, const void* k, const void* v, const vo
       cast ? (void*)df32 : df, cast ? (void*)db32 : db, dA_log, ddt, dinit, ws, stream, check);
   if (st != KDA_OK) return st;
   // input gradients through the convolution, tap and bias gradients
-  hipLaunchKernelGGL((kda_conv_bwd_kernel<TA, TR>), gconv, dim3(128), 0, stream, a);
+  hipLaunchKernelGGL((kda_conv_bwd_kernel<TA, TR>), gconv, dim3(256), 0, stream, a);
   hipLaunchKernelGGL(kda_conv_param_kernel, dim3((unsigned)H, 3), dim3(128), 0, stream, a);
   if (cast) {
     const int64_t blocks = ((int64_t)n + 255) / 256 < 8192 ? ((int64_t)n + 255) / 256 : 8192;

@@ -120,10 +120,13 @@ WIN_CHUNKS = 24  # chunks per window of the windowed schedule (libkda)
 
 
 def stage_names(nst: int):
-    """Stages kda_chunk_fwd_timed separates: two passes, or the windowed
-    pipeline (its launches each run the intra-chunk work of one window and the
-    state pass over the window before)."""
-    return ["chunk_table", "intra", "state_pass"] if nst == 3 else ["chunk_table", "windows"]
+    """Stages kda_chunk_fwd_timed separates: the chunk table, then the
+    intra-chunk and state-pass launches of each segment (two passes), or all
+    launches of the windowed pipeline (each runs the intra-chunk work of one
+    window and the state pass over the window before)."""
+    if nst == 2:
+        return ["chunk_table", "windows"]
+    return ["chunk_table"] + [k for _ in range((nst - 1) // 2) for k in ("intra", "state_pass")]
 
 
 def time_mode(args_dev, fp32: bool, steps: int, warmup: int, windowed: bool = False):
@@ -157,15 +160,24 @@ def time_mode(args_dev, fp32: bool, steps: int, warmup: int, windowed: bool = Fa
     per_step_us = [evs[i][0].elapsed_time(evs[i][nst]) * 1e3 for i in range(steps)]
     stage_us = [[evs[i][s].elapsed_time(evs[i][s + 1]) * 1e3 for i in range(steps)] for s in range(nst)]
     chunks = -(-T // 64)
+    # per kernel: its launches' time per step (summed over segments) and count
+    names, tot, launches = [], {}, {}
+    for nm, su in zip(stage_names(nst), stage_us):
+        if nm not in tot:
+            names.append(nm)
+            tot[nm], launches[nm] = 0.0, 0
+        tot[nm] += sum(su) / len(su)
+        launches[nm] += 1
+    if nst == 2:
+        launches["windows"] = -(-chunks // WIN_CHUNKS) + 1
     return {
         "ms_per_step": wall * 1e3 / steps,
         "p50_us": statistics.median(per_step_us),
         "max_us": max(per_step_us),
-        "stage_avg_us": [sum(s) / len(s) for s in stage_us],
-        "stage_names": stage_names(nst),
+        "stage_avg_us": [tot[nm] for nm in names],
+        "stage_names": names,
         "workspace_bytes": ws.numel(),
-        "launches": ({"windows": -(-chunks // WIN_CHUNKS) + 1} if nst == 2 else
-                     {"intra": 1, "state_pass": 1}),
+        "launches": launches,
     }
 
 
@@ -446,11 +458,16 @@ def roofline_for(mode_name: str, T: int, H: int, res: dict, workload: str):
     state pass: six bf16 products per FP32 product, 2500 / 6 TFLOP/s); the
     whole step against the sum of both kernels' bounds (`path_frac`)."""
     names = res["stage_names"]
-    st = res["stage_avg_us"]
+    st = res["stage_avg_us"]  # per step, each kernel's launches summed
+    # the whole step: the headline's graph-replayed time when known, else the
+    # event-instrumented launches' p50
+    step_us = res["ms_per_step"] * 1e3 if res.get("graph_timed") else res["p50_us"]
     dom = max(range(len(st)), key=lambda i: st[i])
-    windowed = names[dom] == "windows"
+    nl = res["launches"][names[dom]]
     act = 2  # bf16 activations
     th = T * H
+    # per launch: its share of the token-heads over its average duration,
+    # i.e. the step's token-heads over the kernel's time per step
     t = st[dom] * 1e-6
     path_bytes = th * (BYTES_IN_PER_TH(act) + BYTES_OUT_PER_TH(act))
     if mode_name == "bf16":
@@ -460,23 +477,18 @@ def roofline_for(mode_name: str, T: int, H: int, res: dict, workload: str):
                 "alg_bytes_per_launch": path_bytes, "alg_bytes_per_token_head": 1282}
         bound_us = path_bytes / (HBM_PEAK_GBS * 1e9) * 1e6
         roof["path_bound_us"] = round(bound_us, 1)
-        roof["path_frac"] = round(bound_us / res["p50_us"], 4)
-        if windowed:
-            # the window launches carry the whole path (intra-chunk work and
-            # state pass): per launch, its share of the token-heads over the
-            # average launch time, which is the same ratio
-            nl = res["launches"]["windows"]
-            roof["launches"] = nl
-            roof["launch_avg_us"] = round(st[dom] / nl, 2)
+        roof["path_frac"] = round(bound_us / step_us, 4)
     else:
-        peak_of = {1: MFMA_FP32_TFLOPS, 2: MFMA_BF16_TFLOPS / SPLIT_PASSES}
-        flop_of = {1: FLOP_INTRA_PER_TH, 2: FLOP_STATE_PER_TH}
+        peak_of = {"intra": MFMA_FP32_TFLOPS, "state_pass": MFMA_BF16_TFLOPS / SPLIT_PASSES}
+        flop_of = {"intra": FLOP_INTRA_PER_TH, "state_pass": FLOP_STATE_PER_TH}
+        dom = names[dom]
         kpeak = peak_of.get(dom, MFMA_FP32_TFLOPS)
         kfl = flop_of.get(dom, 0) * th / t / 1e12
+        dom = names.index(dom)
         roof = {"bound": "mfma", "achieved": round(kfl, 2), "peak": round(kpeak, 1),
                 "unit": "TFLOP/s", "frac": round(kfl / kpeak, 4),
-                "alg_flop_per_launch": flop_of.get(dom, 0) * th,
-                "alg_flop_per_token_head": flop_of.get(dom, 0)}
+                "alg_flop_per_launch": flop_of.get(names[dom], 0) * th // nl,
+                "alg_flop_per_token_head": flop_of.get(names[dom], 0)}
         # split-aware bound of the whole step: each kernel's FLOP at the peak
         # of the instructions it runs
         b_intra = FLOP_INTRA_PER_TH * th / (MFMA_FP32_TFLOPS * 1e12) * 1e6
@@ -484,15 +496,19 @@ def roofline_for(mode_name: str, T: int, H: int, res: dict, workload: str):
         roof["path_bound_us"] = round(b_intra + b_state, 1)
         roof["path_bound_parts_us"] = {"intra_fp32": round(b_intra, 1),
                                        "state_pass_bf16x6": round(b_state, 1)}
-        roof["path_frac"] = round((b_intra + b_state) / res["p50_us"], 4)
+        roof["path_frac"] = round((b_intra + b_state) / step_us, 4)
         sfl = FLOP_STATE_PER_TH * th / (st[names.index("state_pass")] * 1e-6) / 1e12
         speak = MFMA_BF16_TFLOPS / SPLIT_PASSES
         roof["state_pass_split"] = {"achieved": round(sfl, 2), "peak": round(speak, 1),
                                     "unit": "TFLOP/s", "frac": round(sfl / speak, 4),
                                     "passes": SPLIT_PASSES,
                                     "kernel_avg_us": round(st[names.index("state_pass")], 2)}
+    if mode_name == "bf16":
+        roof["alg_bytes_per_launch"] = path_bytes // nl
     roof["kernel"] = names[dom]
-    roof["kernel_avg_us"] = round(st[dom], 2)
+    roof["launches_per_step"] = nl
+    roof["kernel_avg_us"] = round(st[dom] / nl, 2)  # per launch, as rocprofv3 averages
+    roof["kernel_us_per_step"] = round(st[dom], 2)
     roof["traffic"] = load_traffic(names[dom], workload, mode_name)
     roof["traffic_source"] = (
         f"profiles/counters_{names[dom]}_{workload}_{mode_name}.json: rocprofv3 --pmc FETCH_SIZE "
@@ -505,7 +521,7 @@ def roofline_for(mode_name: str, T: int, H: int, res: dict, workload: str):
     if mode_name == "fp32":
         bounds["mfma_split_aware"] = roof["path_bound_us"]
     roof["path_bounds_us"] = {k: round(v, 1) for k, v in bounds.items()}
-    roof["path_frac_vs_max_bound"] = round(max(bounds.values()) / res["p50_us"], 4)
+    roof["path_frac_vs_max_bound"] = round(max(bounds.values()) / step_us, 4)
     return roof
 
 
@@ -647,6 +663,7 @@ def main():
     for m in modes:
         res[m]["ms_per_step_launched"] = res[m]["ms_per_step"]
         res[m]["ms_per_step"] = time_steps_graph(args_dev, m == "fp32", args.steps, args.warmup)
+        res[m]["graph_timed"] = True
     progress("graph-replayed steps timed")
     head = modes[0]
     r = res[head]

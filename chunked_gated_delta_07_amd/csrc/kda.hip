@@ -103,6 +103,20 @@ static inline bool use_windows(int32_t N, uint32_t mode) {
   return (mode & KDA_MODE_WINDOWED) && !(mode & KDA_MODE_FP32_INTERMEDIATE) && N <= WIN_MAX_SEQS;
 }
 
+// Segments of the two-pass schedule: with BF16 intermediates a long batch
+// runs as segments of SEG_CHUNKS chunks, each an intra-chunk launch followed
+// by a state-pass launch over the same chunks, the records in a ring of one
+// segment and the state of a sequence crossing a boundary carried in FP32
+// (the results are those of one pass over everything, bit for bit).  A
+// segment's records (about 150 MB at 64 heads) stay in the memory-side cache
+// until the state pass reads them.  FP32 records are twice the size and
+// gain nothing from it: one segment.
+static inline int64_t seg_count(int64_t T, int32_t N, uint32_t mode) {
+  const int64_t C = max_chunks(T, N);
+  if ((mode & KDA_MODE_FP32_INTERMEDIATE) || C <= SEG_CHUNKS) return 1;
+  return (C + SEG_CHUNKS - 1) / SEG_CHUNKS;
+}
+
 // Record slots: every chunk (two passes), or a ring of two windows.
 static inline int64_t ring_chunks(int64_t T, int32_t N) {
   const int64_t C = max_chunks(T, N);
@@ -114,17 +128,18 @@ struct WsLayout {
 };
 
 // two passes: [cfirst][gam: chunks x H x 128 f32][rec: chunks x H x REC]
+// segmented:  [cfirst][gam: 32 x H x 128 f32][rec: 32 x H x REC bf16][carry: 2 x H x 128 x 128 f32]
 // windowed:   [cfirst][gam: ring x H x 128 f32][rec: ring x H x RECW bf16][carry: 2 x H x 128 x 128 f32]
 static inline WsLayout ws_layout(int64_t T, int32_t N, int32_t H, uint32_t mode) {
   const size_t mt = (mode & KDA_MODE_FP32_INTERMEDIATE) ? 4 : 2;
-  const bool win = use_windows(N, mode);
-  const int64_t C = win ? ring_chunks(T, N) : max_chunks(T, N);
+  const bool win = use_windows(N, mode), seg = !win && seg_count(T, N, mode) > 1;
+  const int64_t C = win ? ring_chunks(T, N) : seg ? SEG_CHUNKS : max_chunks(T, N);
   WsLayout L;
   L.off_cfirst = 256;  // [0, 4): status word of KDA_MODE_CHECK_CU
   L.off_gam = L.off_cfirst + align256(sizeof(int32_t) * (size_t)(N + 1));
   L.off_rec = L.off_gam + align256(sizeof(float) * (size_t)C * H * DH);
   L.off_carry = L.off_rec + align256(mt * (size_t)C * H * (win ? RECW : REC));
-  L.total = L.off_carry + (win ? align256(sizeof(float) * 2 * (size_t)H * DH * DH) : 0);
+  L.total = L.off_carry + (win || seg ? align256(sizeof(float) * 2 * (size_t)H * DH * DH) : 0);
   return L;
 }
 
@@ -153,37 +168,54 @@ static int launch_all(const void* q, const void* k, const void* v, const void* f
   cfirst = launch_table(cu, N, T, cfirst, ws, mode & KDA_MODE_CHECK_CU, stream);
   if (ev) (void)hipEventRecord(ev[1], stream);
 
+  // one segment, or segments of SEG_CHUNKS chunks (BF16 intermediates only)
+  const int64_t nseg = seg_count(T, N, mode);
+  const int64_t per = nseg > 1 ? SEG_CHUNKS : C;
+  float* carry = nseg > 1 ? reinterpret_cast<float*>(base + W.off_carry) : nullptr;
+
   IntraArgs ia;
   ia.q = q; ia.k = k; ia.v = v; ia.f = f; ia.b = b;
   ia.A_log = A_log; ia.dt_bias = dt_bias; ia.cu = cu; ia.cfirst = cfirst;
   ia.N = N; ia.H = H; ia.eps = 1e-6f; ia.gam = gam; ia.rec = rec;
   ia.conv_w = conv_w; ia.conv_b = conv_b; ia.conv_silu = conv_silu;
-  ia.tmat = nullptr; ia.bw = nullptr; ia.wt = nullptr; ia.kbr = nullptr; ia.ring = 0;
+  ia.tmat = nullptr; ia.bw = nullptr; ia.wt = nullptr; ia.kbr = nullptr;
+  ia.ring = nseg > 1 ? SEG_CHUNKS : 0;
   ia.dk = dk; ia.dv = dv;
-  const dim3 gintra((unsigned)H, (unsigned)C);  // heads x chunks (sizes checked by the caller)
-  if constexpr (RECT)
-    hipLaunchKernelGGL((kda_intra_kernel<TA, MT, false, Frag<MT>, false, true>), gintra, dim3(256),
-                       0, stream, ia);
-  else if (conv_w)
-    hipLaunchKernelGGL((kda_intra_kernel<TA, MT, true>), gintra, dim3(256), 0, stream, ia);
-  else
-    hipLaunchKernelGGL((kda_intra_kernel<TA, MT, false>), gintra, dim3(256), 0, stream, ia);
-  if (ev) (void)hipEventRecord(ev[2], stream);
 
   ScanArgs sa;
   sa.cu = cu; sa.cfirst = cfirst; sa.N = N; sa.H = H;
   sa.scale = (float)(1.0 / sqrt((double)dk));  // 1/sqrt(d_k), correctly rounded
   sa.gam = gam; sa.rec = rec; sa.out = out; sa.init = init; sa.fin = fin;
   sa.dk = dk; sa.dv = dv;
+  sa.ring = ia.ring;
   // 32 workgroups (four value blocks of eight (sequence, head) pairs) per
   // grid row; workgroup id = x + 32 y
   const int64_t pairs = (int64_t)N * H;
   const dim3 gscan(32, (unsigned)((pairs + 7) / 8));
-  if constexpr (sizeof(MT) == 2)
-    hipLaunchKernelGGL((kda_scan_ring_kernel<TO, RECT>), gscan, dim3(512), 0, stream, sa);
-  else
-    hipLaunchKernelGGL((kda_scan_ring32_kernel<TO, RECT>), gscan, dim3(512), 0, stream, sa);
-  if (ev) (void)hipEventRecord(ev[3], stream);
+  const size_t cstride = (size_t)H * DH * DH;
+  for (int64_t sg = 0; sg < nseg; ++sg) {
+    const int64_t c0 = sg * per, rows = (C - c0 < per) ? C - c0 : per;
+    ia.c0 = (int)c0;
+    const dim3 gintra((unsigned)H, (unsigned)rows);  // heads x chunks (sizes checked by the caller)
+    if constexpr (RECT)
+      hipLaunchKernelGGL((kda_intra_kernel<TA, MT, false, Frag<MT>, false, true>), gintra, dim3(256),
+                         0, stream, ia);
+    else if (conv_w)
+      hipLaunchKernelGGL((kda_intra_kernel<TA, MT, true>), gintra, dim3(256), 0, stream, ia);
+    else
+      hipLaunchKernelGGL((kda_intra_kernel<TA, MT, false>), gintra, dim3(256), 0, stream, ia);
+    if (ev) (void)hipEventRecord(ev[2 + 2 * sg], stream);
+
+    sa.c0 = (int)c0;
+    sa.c1 = sg + 1 < nseg ? (int)(c0 + per) : INT32_MAX;  // the last one takes everything after
+    sa.carry_in = carry ? carry + ((sg + 1) & 1) * cstride : nullptr;
+    sa.carry_out = carry ? carry + (sg & 1) * cstride : nullptr;
+    if constexpr (sizeof(MT) == 2)
+      hipLaunchKernelGGL((kda_scan_ring_kernel<TO, RECT>), gscan, dim3(512), 0, stream, sa);
+    else
+      hipLaunchKernelGGL((kda_scan_ring32_kernel<TO, RECT>), gscan, dim3(512), 0, stream, sa);
+    if (ev) (void)hipEventRecord(ev[3 + 2 * sg], stream);
+  }
   return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -214,6 +246,7 @@ static int launch_windows(const void* q, const void* k, const void* v, const voi
   ia.gam = reinterpret_cast<float*>(base + L.off_gam);
   ia.rec = base + L.off_rec;
   ia.ring = (int)ring_chunks(T, N);
+  ia.c0 = 0;
   ia.conv_w = conv_w; ia.conv_b = conv_b; ia.conv_silu = conv_silu;
   ia.tmat = nullptr; ia.bw = nullptr; ia.wt = nullptr; ia.kbr = nullptr;
   wa.nseg = N; wa.W = W;
@@ -330,6 +363,7 @@ static int launch_bwd(const void* q, const void* k, const void* v, const void* f
   ia.N = N; ia.H = H; ia.eps = 1e-6f; ia.gam = fp(L.off_gam); ia.rec = fp(L.off_rec);
   ia.conv_w = nullptr; ia.conv_b = nullptr; ia.conv_silu = 0;
   ia.tmat = fp(L.off_t); ia.bw = fp(L.off_bw); ia.wt = fp(L.off_wt); ia.kbr = fp(L.off_kbr); ia.ring = 0;
+  ia.c0 = 0;
   const dim3 gch((unsigned)C, (unsigned)H);
   hipLaunchKernelGGL((kda_intra_kernel<TA, float, false, PlainRec<float>, true>), gch, dim3(256), 0,
                      stream, ia);
@@ -474,10 +508,10 @@ extern "C" size_t kda_chunk_fwd_workspace_bytes(int64_t total_tokens, int32_t nu
 
 extern "C" int kda_chunk_fwd_num_stages(int64_t total_tokens, int32_t num_seqs, int32_t H,
                                         uint32_t mode) {
-  (void)total_tokens;
   (void)H;
-  if ((mode & ~KDA_MODE_ALL_BITS) || num_seqs < 1) return -1;
-  return kda::use_windows(num_seqs, mode) ? 2 : 3;
+  if ((mode & ~KDA_MODE_ALL_BITS) || num_seqs < 1 || total_tokens < 0) return -1;
+  // windowed: table, windows; two passes: table, then intra and state pass per segment
+  return kda::use_windows(num_seqs, mode) ? 2 : (int)(1 + 2 * kda::seg_count(total_tokens, num_seqs, mode));
 }
 
 static int fwd_impl(const void* q, const void* k, const void* v, const void* f_raw, const void* b_raw,

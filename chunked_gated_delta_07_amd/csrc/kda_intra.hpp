@@ -156,6 +156,7 @@ struct IntraArgs {
   float* gam;  // [chunks][H][128]
   void* rec;   // [chunks][H][LY::REC_ELEMS] of MT (or [ring][H][..])
   int ring;    // > 0: records and gam of chunk c live in slot c % ring
+  int c0;      // forward kernel: first chunk of this launch's grid rows
   // optional short causal convolution on q, k, v (used when the kernel's
   // CONV parameter is set): weights [3][H*128][4] (tap 3 = current token),
   // bias [3][H*128] or null, SiLU after it when conv_silu != 0
@@ -1232,8 +1233,8 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(IntraArgs p) {
   __shared__ __attribute__((aligned(16))) char smem[IntraLds<MT>::BYTES];
   if constexpr (BWD)
     intra_chunk<TA, MT, CONV, LY, BWD, RECT>(p, (int)blockIdx.x, (int)blockIdx.y, smem);
-  else  // grid (H, chunks): x = head, y = chunk counted from the last
-    intra_chunk<TA, MT, CONV, LY, BWD, RECT>(p, (int)gridDim.y - 1 - (int)blockIdx.y,
+  else  // grid (H, chunks): x = head, y = chunk counted from the last one of the launch
+    intra_chunk<TA, MT, CONV, LY, BWD, RECT>(p, p.c0 + (int)gridDim.y - 1 - (int)blockIdx.y,
                                              (int)blockIdx.x, smem);
 }
 

@@ -40,7 +40,18 @@ struct ScanArgs {
   // with the kernels' RECT parameter: key / value widths (<= 128) of out
   // [T][H][dv] and of the states [N][H][dk][dv]
   int dk, dv;
+  // Segmented schedule (BF16 intermediates): this launch walks the chunks in
+  // [c0, c1) only; records and Gam of chunk c sit in slot c % ring (ring = 0:
+  // slot c).  A sequence that starts before c0 takes its state from carry_in,
+  // one that continues past c1 leaves it in carry_out ([H][128][128] each; at
+  // most one sequence crosses a segment boundary).  Whole-sequence launches
+  // use c0 = 0, c1 = INT_MAX.  Only kda_scan_ring_kernel reads these.
+  int c0, c1, ring;
+  const float* carry_in;
+  float* carry_out;
 };
+
+constexpr int SEG_CHUNKS = 32;  // chunks per segment of the segmented schedule
 
 // State entry (key, value) of (sequence, head) pair `pair` in a [..][dk][dv]
 // array, or -1 when the pair of widths leaves it out.
@@ -391,28 +402,35 @@ __global__ __launch_bounds__(512) void kda_scan_ring_kernel(ScanArgs p) {
   const int n = pair / p.H, h = pair - n * p.H;
   int cbeg, cend;
   chunk_range(p.cu, p.cfirst, n, cbeg, cend);
+  // this launch's chunks of the sequence; an empty sequence is handled by the
+  // launch whose range holds its position
+  const int lo = max(cbeg, p.c0), hi = min(cend, p.c1);
+  if (cbeg < cend ? lo >= hi : (cbeg < p.c0 || cbeg >= p.c1)) return;  // uniform over the block
   const int tseq = p.cu[n], tend = p.cu[n + 1];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int col = l & 31, g = l >> 5;
   // state entry e of this lane: key 32 (w & 3) + row32(e, l), value 32 vb + col
   auto sidx = [&](int e) { return state_index<RECT>(p, pair, 32 * (w & 3) + row32(e, l), DVB * vb + col); };
+  // the same entry in a per-head carry buffer [H][128][128]
+  auto cidx = [&](int e) { return ((size_t)h * DH + 32 * (w & 3) + row32(e, l)) * DH + DVB * vb + col; };
   const int H = p.H;
   const char* recb = reinterpret_cast<const char*>(p.rec);
   const char* gamb = reinterpret_cast<const char*>(p.gam);
-  auto rec_of = [&](int c) { return recb + ((size_t)c * H + h) * (size_t)REC * 2; };
-  auto gam_of = [&](int c) { return gamb + ((size_t)c * H + h) * DH * 4; };
+  auto slot_of = [&](int c) { return (size_t)(p.ring ? c % p.ring : c); };
+  auto rec_of = [&](int c) { return recb + (slot_of(c) * H + h) * (size_t)REC * 2; };
+  auto gam_of = [&](int c) { return gamb + (slot_of(c) * H + h) * DH * 4; };
 
   if (w >= 4) {
     // ------------------------------------------------------------ loaders
     if (cbeg == cend) return;
-    const int lw = w - 4, clast = cend - 1;
-    ring_copy_early(rec_of(cbeg), ring, vb, lw, l);
-    ring_copy_late(rec_of(cbeg), gam_of(cbeg), ring, lw, l);
+    const int lw = w - 4, clast = hi - 1;
+    ring_copy_early(rec_of(lo), ring, vb, lw, l);
+    ring_copy_late(rec_of(lo), gam_of(lo), ring, lw, l);
     wait_vm<0>();
-    ring_barrier();  // chunk cbeg in slot 0; start state in sS
-    for (int c = cbeg; c < cend; ++c) {
+    ring_barrier();  // chunk lo in slot 0; start state in sS
+    for (int c = lo; c < hi; ++c) {
       const int nx = min(c + 1, clast);
-      char* nslot = ring + ((c - cbeg + 1) & 1) * RG_SLOT;
+      char* nslot = ring + ((c - lo + 1) & 1) * RG_SLOT;
       ring_copy_early(rec_of(nx), nslot, vb, lw, l);
       wait_vm<RG_EARLY_PER_LOADER>();  // late operands of chunk c are in
       ring_barrier();
@@ -425,10 +443,15 @@ __global__ __launch_bounds__(512) void kda_scan_ring_kernel(ScanArgs p) {
   }
   // -------------------------------------------------------------- compute
   f32x16 S;
+  if (lo > cbeg) {  // continued from the previous segment
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int64_t i = sidx(e);
-    S[e] = (p.init && i >= 0) ? p.init[i] : 0.0f;
+    for (int e = 0; e < 16; ++e) S[e] = p.carry_in[cidx(e)];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t i = sidx(e);
+      S[e] = (p.init && i >= 0) ? p.init[i] : 0.0f;
+    }
   }
   if (cbeg == cend) {
     if (p.fin) {
@@ -445,8 +468,8 @@ __global__ __launch_bounds__(512) void kda_scan_ring_kernel(ScanArgs p) {
   wait_lds();
   ring_barrier();
   const int cfull = cbeg + (tend - tseq) / CHUNK;
-  for (int c = cbeg; c < cend; ++c) {
-    const char* slot = ring + ((c - cbeg) & 1) * RG_SLOT;
+  for (int c = lo; c < hi; ++c) {
+    const char* slot = ring + ((c - lo) & 1) * RG_SLOT;
     const int ctok = tseq + (c - cbeg) * CHUNK;
     if (c < cfull) {
       if (w < 2) ring_step<TO, 0, true, RECT>(p, slot, S, sS, sD, h, ctok, CHUNK, vb, w, l);
@@ -456,7 +479,10 @@ __global__ __launch_bounds__(512) void kda_scan_ring_kernel(ScanArgs p) {
       else ring_step<TO, 1, false, RECT>(p, slot, S, sS, sD, h, ctok, tend - ctok, vb, w, l);
     }
   }
-  if (p.fin) {
+  if (hi < cend) {  // the sequence continues in the next segment
+#pragma unroll
+    for (int e = 0; e < 16; ++e) p.carry_out[cidx(e)] = S[e];
+  } else if (p.fin) {
 #pragma unroll
     for (int e = 0; e < 16; ++e)
       if (sidx(e) >= 0) p.fin[sidx(e)] = S[e];

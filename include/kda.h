@@ -73,14 +73,18 @@ extern "C" {
  *   1 = float32.
  * KDA_OUT_FP32: dtype of out: 0 = the activation dtype, 1 = float32.
  * KDA_MODE_WINDOWED: schedule only, same arithmetic.  By default the
- *   forward makes two passes over every chunk (intra-chunk kernel, then state
- *   pass), with a record per chunk and head in the workspace.  With this bit,
- *   BF16 intermediates and at most 64 sequences it runs as a pipeline of
+ *   forward makes two passes (intra-chunk kernel, then state pass): with FP32
+ *   intermediates over all chunks at once, with a record per chunk and head in
+ *   the workspace; with BF16 intermediates over segments of 32 chunks (per
+ *   segment one intra-chunk launch and one state-pass launch, the records in a
+ *   ring of one segment: 160 MB at 64 heads, whatever the length; the results
+ *   are bit for bit those of one pass over all chunks).  With this bit, BF16
+ *   intermediates and at most 64 sequences the forward runs as a pipeline of
  *   windows of 24 chunks instead: each launch does the intra-chunk work of one
- *   window and the state pass over the window before, and the records live in
- *   a ring of two windows, so the workspace stops growing with the sequence
- *   length (230 MB instead of 1.2 GB at 16384 tokens x 64 heads).  Ignored
- *   with FP32 intermediates or more than 64 sequences.
+ *   window and the state pass over the window before, the records in a ring of
+ *   two windows (230 MB at 64 heads).  Slower than the default segments; kept
+ *   as the alternative schedule it measures against.  Ignored with FP32
+ *   intermediates or more than 64 sequences.
  * KDA_MODE_CHECK_CU: debugging aid.  The device checks cu_seqlens before any
  *   kernel reads token data: cu_seqlens[0] == 0, non-decreasing,
  *   cu_seqlens[num_seqs] == total_tokens.  It stores a code in the first 4
@@ -104,11 +108,13 @@ extern "C" {
 #define KDA_MODE_ALL_BITS 0x1Fu
 
 /* Bytes of caller-provided scratch that kda_chunk_fwd needs for this shape.
- * Depends only on the arguments; non-decreasing in total_tokens.  Two
- * passes need about 74 KB (BF16) or 148 KB (FP32) per 64-token chunk and
- * head.  The windowed schedule (KDA_MODE_WINDOWED with BF16 intermediates and
- * at most 64 sequences) stops growing at 48 chunks: about 3.6 MB per head
- * (the BF16 records of two 24-chunk windows and two 64 KB boundary states).  Returns 0 when total_tokens == 0, and
+ * Depends only on the arguments; non-decreasing in total_tokens.  FP32
+ * intermediates need about 148 KB per 64-token chunk and head.  BF16
+ * intermediates need about 74 KB per chunk and head up to 32 chunks and stop
+ * growing there: about 2.5 MB per head (the records of one 32-chunk segment and
+ * two 64 KB boundary states).  The windowed schedule (KDA_MODE_WINDOWED with
+ * BF16 intermediates and at most 64 sequences) stops growing at 48 chunks:
+ * about 3.6 MB per head (two 24-chunk windows).  Returns 0 when total_tokens == 0, and
  * (size_t)-1 when the arguments are invalid (negative sizes, d != 128,
  * unknown mode bits). */
 KDA_API size_t kda_chunk_fwd_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t d,
@@ -331,10 +337,9 @@ KDA_API int kda_chunk_bwd_conv(const void* q, const void* k, const void* v, cons
  * a HIP graph, tight serving loops, harnesses that forbid hipMalloc).  The
  * workspace is a library-owned device array of KDA_NOALLOC_SCRATCH_BYTES per
  * GPU; shapes whose kda_chunk_fwd_workspace_bytes exceeds it return
- * KDA_ERR_WORKSPACE before anything is launched.  With KDA_MODE_WINDOWED
- * (BF16 intermediates, at most 64 sequences) that is any length up to 74
- * heads; two passes fit up to 56 chunks of 64 tokens at 64 heads with BF16
- * intermediates and 28 with FP32 intermediates.  Every
+ * KDA_ERR_WORKSPACE before anything is launched.  With BF16 intermediates
+ * that is any length up to 107 heads (74 with KDA_MODE_WINDOWED); with FP32
+ * intermediates up to 28 chunks of 64 tokens at 64 heads.  Every
  * byte of the array that a call reads it has written earlier in the same
  * call, so nothing needs clearing between calls.  Calls that overlap in time
  * on one GPU (two streams, two host threads) share the one array and race:
@@ -347,10 +352,13 @@ KDA_API int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, c
                           int32_t H, int32_t d, uint32_t mode, void* out, void* stream);
 
 /* Number of stages kda_chunk_fwd_timed separates for this shape and mode:
- * 3 for two passes (chunk table, intra-chunk kernel, state pass), 2 for the
- * windowed schedule (chunk table, all window launches); -1 for invalid
- * arguments.  The chunk table is launched only when num_seqs > 1 (the stage
- * is then empty). */
+ * 1 + 2 s for two passes in s segments (the chunk table, then for each
+ * segment its intra-chunk launch and its state-pass launch; s = 1 with FP32
+ * intermediates or up to 32 chunks, else ceil(chunks / 32) with chunks the
+ * workspace query's upper bound), 2 for the windowed schedule (chunk table,
+ * all window launches); -1 for invalid arguments.  The chunk table is
+ * launched only when num_seqs > 1 or the cu_seqlens check is asked for (the
+ * stage is otherwise empty). */
 KDA_API int kda_chunk_fwd_num_stages(int64_t total_tokens, int32_t num_seqs, int32_t H,
                                      uint32_t mode);
 

@@ -66,7 +66,7 @@ int main(void) {
   EXPECT(kda_chunk_fwd_rect(p, p, p, p, p, fp, fp, ip, 1, 10, 4, 0, 24, 0, p, p, big, NULL, NULL, NULL), KDA_ERR_INVALID_ARG);
   EXPECT(kda_chunk_fwd_rect(p, p, p, p, p, fp, fp, ip, 1, 10, 4, 16, 24, 0, p, p, 1, NULL, NULL, NULL), KDA_ERR_WORKSPACE);
   EXPECT(kda_chunk_fwd_noalloc(p, p, p, p, p, fp, fp, ip, 1, 10, 4, 128, KDA_MODE_CHECK_CU, p, NULL), KDA_ERR_UNSUPPORTED);
-  EXPECT(kda_chunk_fwd_noalloc(p, p, p, p, p, fp, fp, ip, 1, 1 << 20, 64, 128, 0, p, NULL), KDA_ERR_WORKSPACE);
+  EXPECT(kda_chunk_fwd_noalloc(p, p, p, p, p, fp, fp, ip, 1, 1 << 20, 64, 128, KDA_MODE_FP32_INTERMEDIATE, p, NULL), KDA_ERR_WORKSPACE);
   EXPECT(kda_chunk_fwd_noalloc(p, p, p, p, p, fp, fp, ip, 1, 10, 4, 96, 0, p, NULL), KDA_ERR_UNSUPPORTED);
   {
     void* ev[4] = {p, p, p, p};

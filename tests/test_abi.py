@@ -232,10 +232,17 @@ def test_workspace_query():
             bw = kda.workspace_bytes(T, N, 64, 128, kda.KDA_MODE_WINDOWED)
             b32 = kda.workspace_bytes(T, N, 64, 128, 1)
             assert b > 0 and bw > 0 and b32 > b and b % 256 == 0 and bw % 256 == 0
-    # the windowed schedule keeps a ring of two 24-chunk windows: its workspace
-    # stops growing with the sequence length
+    # with BF16 intermediates the records live in a ring: one 32-chunk segment
+    # (two passes, segmented) or two 24-chunk windows (windowed schedule); the
+    # workspace stops growing with the length.  FP32 records cover every chunk.
     w = [kda.workspace_bytes(T, 1, 64, 128, kda.KDA_MODE_WINDOWED) for T in (48 * 64, 16384, 1 << 20)]
-    assert w[0] == w[1] == w[2] < kda.workspace_bytes(16384, 1, 64, 128, 0)
+    sg = [kda.workspace_bytes(T, 1, 64, 128, 0) for T in (33 * 64, 16384, 1 << 20)]
+    assert w[0] == w[1] == w[2] and sg[0] == sg[1] == sg[2] < 200e6
+    assert kda.workspace_bytes(32 * 64, 1, 64, 128, 0) < sg[0]  # one segment: no carry buffers
+    assert kda.workspace_bytes(16384, 1, 64, 128, 1) > 2e9
+    # stages: the table, then intra and state pass per segment (32 chunks)
+    assert kda.num_stages(16384, 1, 64, 0) == 1 + 2 * 8
+    assert kda.num_stages(2048, 1, 64, 0) == 3 and kda.num_stages(16384, 1, 64, 1) == 3
     for T in range(1, 400, 7):
         b = kda.workspace_bytes(T, 3, 8, 128, 0)
         assert b >= prev

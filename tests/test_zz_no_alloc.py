@@ -37,12 +37,13 @@ def test_noalloc_matches_workspace_entry_point(fp32, out_fp32):
 
     from chunked_gated_delta_07_amd import kda
 
-    # a larger call, then a smaller one with a different packing; the
-    # windowed schedule's workspace does not grow with the length, so with it
-    # the 16384-token, 64-head shape fits too
+    # a larger call, then a smaller one with a different packing; with BF16
+    # intermediates the records live in a ring (one 32-chunk segment, or two
+    # windows with KDA_MODE_WINDOWED), so the 16384-token, 64-head shape fits
     cases = [([0, 700, 1500, 1792], 32, 41, False), ([0, 37, 65, 300], 8, 42, False)]
     if not fp32:
-        cases = [([0, 16384], 64, 43, True), ([0, 700, 1500, 1792], 32, 41, True)] + cases
+        cases = [([0, 16384], 64, 43, False), ([0, 16384], 64, 43, True),
+                 ([0, 700, 1500, 1792], 32, 41, True)] + cases
     for cu, H, seed, win in cases:
         inp = synth.make_inputs(cu, H=H, d=128, act="bf16", seed=seed)
         args = U.to_device(inp, "cuda:0")
@@ -80,8 +81,10 @@ def test_noalloc_rejects_shapes_beyond_its_array():
     assert kda.workspace_bytes(T, 1, 64, 128, m32) > kda.NOALLOC_SCRATCH_BYTES
     assert lib.kda_chunk_fwd_noalloc(*([p] * 8), 1, T, 64, 128, m32, p, None) == \
         kda.KDA_ERR_WORKSPACE
-    assert kda.workspace_bytes(T, 1, 64, 128, 0) > kda.NOALLOC_SCRATCH_BYTES
-    assert lib.kda_chunk_fwd_noalloc(*([p] * 8), 1, T, 64, 128, 0, p, None) == \
+    # BF16: a ring of one 32-chunk segment, about 2.5 MB per head
+    assert kda.workspace_bytes(T, 1, 64, 128, 0) <= kda.NOALLOC_SCRATCH_BYTES
+    assert kda.workspace_bytes(T, 1, 128, 128, 0) > kda.NOALLOC_SCRATCH_BYTES
+    assert lib.kda_chunk_fwd_noalloc(*([p] * 8), 1, T, 128, 128, 0, p, None) == \
         kda.KDA_ERR_WORKSPACE
     assert kda.workspace_bytes(T, 1, 64, 128, kda.KDA_MODE_WINDOWED) <= kda.NOALLOC_SCRATCH_BYTES
     assert lib.kda_chunk_fwd_noalloc(*([p] * 8), 1, 10, 64, 96, 0, p, None) == \

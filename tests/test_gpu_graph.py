@@ -26,13 +26,17 @@ def _gpu():
     yield
 
 
+@pytest.mark.parametrize("cu", [[0, 100, 100, 357, 1000], [0, 2500, 2500, 4300]],
+                         ids=["short", "three_segments"])
 @pytest.mark.parametrize("fp32", [False, True], ids=["bf16", "fp32"])
-def test_graph_replay_matches_eager(fp32):
+def test_graph_replay_matches_eager(fp32, cu):
+    """A captured forward replays bit for bit, also when the BF16 forward runs
+    as several 32-chunk segments (the second case: 70 chunks)."""
     import torch
 
     from chunked_gated_delta_07_amd import kda
 
-    inp = synth.make_inputs([0, 100, 100, 357, 1000], H=8, d=128, act="bf16", seed=55)
+    inp = synth.make_inputs(cu, H=8, d=128, act="bf16", seed=55)
     args = U.to_device(inp, "cuda:0")
     T, H, N = inp.T, inp.H, len(inp.cu_seqlens) - 1
     mode = kda.make_mode(fp32, False, False)

@@ -89,19 +89,23 @@ def test_cfg1_fp32_mode_bf16_output():
 @pytest.mark.parametrize("fp32", [False, True], ids=["bf16", "fp32"])
 def test_cfg2_2048_tokens(fp32):
     inp = U.config_inputs(2)
-    _check(inp, fp32=fp32, heads=[0, 9, 22, 31, 40, 47, 58, 63], label="cfg2")
+    _check(inp, fp32=fp32, label="cfg2")
 
 
 @pytest.mark.parametrize("fp32", [False, True], ids=["bf16", "fp32"])
-def test_cfg3_16384_tokens_sampled_heads(fp32):
+def test_cfg3_16384_tokens_all_heads(fp32):
+    """The headline workload, every head, in the launch configuration the
+    benchmark times (BF16: eight 32-chunk segments, bf16 output too)."""
     inp = U.config_inputs(3)
-    _check(inp, fp32=fp32, heads=[2, 13, 38, 51, 63], label="cfg3")
+    _check(inp, fp32=fp32, label="cfg3")
 
 
 @pytest.mark.parametrize("fp32", [False, True], ids=["bf16", "fp32"])
 def test_cfg4_ragged_65536_tokens_sampled_heads(fp32):
+    """19 ragged sequences (33 segments in BF16 mode, most boundaries inside
+    a sequence); 16 heads spread over the workgroup-to-XCD mapping."""
     inp = U.config_inputs(4)
-    _check(inp, fp32=fp32, heads=[4, 17, 42, 63], label="cfg4")
+    _check(inp, fp32=fp32, heads=list(range(1, 64, 4)), label="cfg4")
 
 
 @pytest.mark.parametrize("cu", [

@@ -304,12 +304,10 @@ static int dispatch(const void* q, const void* k, const void* v, const void* f, 
 
 // ------------------------------------------------------------ backward
 // Workspace of the backward, FP32 arrays per (chunk, head) after the chunk
-// table.  Arrays written by the last three kernels reuse ones whose readers
-// have finished: alpha/pi/rho take D/dD/dW, q^/k^ take S0, G takes dSn.
+// table.
 struct BwdLayout {
   size_t off_cfirst, off_gam, off_rec, off_t, off_bw, off_wt, off_kbr, off_s0, off_dsn, off_d,
-      off_dd, off_dqt, off_dkb, off_dw, off_dbw, off_dp, off_da, off_dgam, off_db1, off_rqk, off_pp,
-      total;
+      off_dd, off_dqt, off_dkb, off_dw, off_dbw, off_dp, off_da, off_dgam, off_db1, off_pp, total;
 };
 
 static inline BwdLayout bwd_layout(int64_t T, int32_t N, int32_t H) {
@@ -336,7 +334,6 @@ static inline BwdLayout bwd_layout(int64_t T, int32_t N, int32_t H) {
   L.off_da = take(4 * CH * SQM);
   L.off_dgam = take(4 * CH * DH);
   L.off_db1 = take(4 * CH * CHUNK);
-  L.off_rqk = take(4 * CH * 2 * CHUNK);
   L.off_pp = take(4 * CH * PPART);
   L.total = o;
   return L;
@@ -378,9 +375,7 @@ static int launch_bwd(const void* q, const void* k, const void* v, const void* f
   a.s0 = fp(L.off_s0); a.dsn = fp(L.off_dsn); a.dmat = fp(L.off_d); a.ddmat = fp(L.off_dd);
   a.dqt = fp(L.off_dqt); a.dkb = fp(L.off_dkb); a.dw = fp(L.off_dw); a.dbw = fp(L.off_dbw);
   a.dpm = fp(L.off_dp); a.dam = fp(L.off_da); a.dgam = fp(L.off_dgam); a.db1 = fp(L.off_db1);
-  a.rqk = fp(L.off_rqk); a.ppart = fp(L.off_pp);
-  a.al = a.dmat; a.pi = a.ddmat; a.rho = a.dw;  // read-once arrays reused
-  a.qn = a.s0; a.kn = a.s0 + (size_t)C * H * MAT; a.g2 = a.dsn;
+  a.ppart = fp(L.off_pp);
   a.dq = dq; a.dk = dk; a.dv = dv; a.df = df; a.db = db;
   a.dinit = dinit; a.dA_log = dA_log; a.ddt_bias = ddt;
   const int64_t pairs = (int64_t)N * H;
@@ -389,8 +384,7 @@ static int launch_bwd(const void* q, const void* k, const void* v, const void* f
   hipLaunchKernelGGL((kda_bwd_bscan_kernel<TG>), gscan, dim3(SCAN_THREADS), 0, stream, a);
   hipLaunchKernelGGL((kda_bwd_jprod_kernel<TG>), gch, dim3(256), 0, stream, a);
   hipLaunchKernelGGL((kda_bwd_tprod_kernel<TA, TR>), gch, dim3(256), 0, stream, a);
-  hipLaunchKernelGGL((kda_bwd_gate_kernel<TA>), gch, dim3(512), 0, stream, a);
-  hipLaunchKernelGGL((kda_bwd_final_kernel<TA, TR>), gch, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((kda_bwd_gate_kernel<TA, TR>), gch, dim3(512), 0, stream, a);
   hipLaunchKernelGGL(kda_bwd_param_kernel, dim3((unsigned)H), dim3(DH), 0, stream, a);
   return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

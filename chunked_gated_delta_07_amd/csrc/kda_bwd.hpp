@@ -32,8 +32,8 @@
 //   dA_log += sum dg g,  db = dbeta beta (1 - beta),
 //   dq = (dq^ - q^ (q^.dq^)) rq,  dk likewise.
 // Every exponential of a difference of G has a non-positive exponent
-// (diagonal blocks per element; off-diagonal 8x8 blocks factorised about the
-// first row of the row block), so no gate strength can overflow it.
+// (4x4 diagonal blocks per element; every other pair factorised about a row
+// between the two), so no gate strength can overflow it.
 //
 // Kernel sequence (all intermediates FP32 in the workspace):
 //   1. kda_intra_kernel<.., PlainRec, BWD>: records W, Qt^T, Kb^T, U^T, P^T, Gam, T, Bw,
@@ -42,9 +42,9 @@
 //   3. kda_bwd_bscan_kernel: dSn of every chunk, dD, dS_init   (same, chunks in reverse)
 //   4. kda_bwd_jprod_kernel: dQt, dP, dKb, dW, dGam            (per chunk, head)
 //   5. kda_bwd_tprod_kernel: dv, dbeta part, dBw, dA          (per chunk, head)
-//   6. kda_bwd_gate_kernel:  q^, k^, G, alpha, pi, rho         (per chunk, head)
-//   7. kda_bwd_final_kernel: dq, dk, df, db, parameter parts   (per chunk, head)
-//   8. kda_bwd_param_kernel: dA_log, dt_bias gradient          (per head, fixed order)
+//   6. kda_bwd_gate_kernel:  q^, k^, G, alpha, pi, rho, then dq, dk, df, db and the
+//      parameter parts                                        (per chunk, head)
+//   7. kda_bwd_param_kernel: dA_log, dt_bias gradient          (per head, fixed order)
 #pragma once
 
 #include "kda_common.hpp"
@@ -93,13 +93,6 @@ struct BwdArgs {
   float* dam;              // dA [64][64]
   float* dgam;             // dGam [128]
   float* db1;              // v . dBu per row [64]
-  float* qn;               // q^ [64][128]
-  float* kn;               // k^ [64][128]
-  float* g2;               // G log2(e) [64][128]
-  float* rqk;              // [64] rq, [64] rk
-  float* al;               // alpha [64][128]
-  float* pi;               // pi [64][128]
-  float* rho;              // rho [64][128]
   float* ppart;            // [PPART]
   // outputs
   void* dq;
@@ -710,298 +703,501 @@ __device__ __forceinline__ float gate_log2(float x, float lam) {
   return -lam * (fmaxf(x, 0.0f) * LOG2E + log2_hw(1.0f + t));
 }
 
-// ------------------------------------------------------------ 6. decay-weighted sums
-// Recomputes q^, k^ and G (stored for kernel 7), then
-//   waves 0-3 (one thread per channel): alpha, pi (sums over i <= r per row r)
-//   waves 4-7 (one thread per channel): rho (sums over r >= i per column i)
-// in 8x8 token blocks: off-diagonal blocks (R > I) factorised about row 8R,
-//   e^{G_r - G_i} = e^{G_r - G_8R} e^{G_8R - G_i}  (both exponents <= 0),
-// diagonal blocks per element.
-template <typename TA>
-__global__ __launch_bounds__(512) void kda_bwd_gate_kernel(BwdArgs p) {
-  __shared__ __attribute__((aligned(16))) float sQ[CHUNK * DH];
-  __shared__ __attribute__((aligned(16))) float sK[CHUNK * DH];
-  __shared__ __attribute__((aligned(16))) float sG[CHUNK * DH];
-  __shared__ __attribute__((aligned(16))) float sA[SQM];
-  __shared__ __attribute__((aligned(16))) float sP[SQM];
-  __shared__ float sBeta[CHUNK];
-  const int cidx = blockIdx.x, h = blockIdx.y;
-  int t0, len;
-  if (!bwd_chunk(p, cidx, t0, len)) return;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const size_t ch = (size_t)cidx * p.H + h;
-  const TA* __restrict__ gq = reinterpret_cast<const TA*>(p.q);
-  const TA* __restrict__ gk = reinterpret_cast<const TA*>(p.k);
-  const TA* __restrict__ gf = reinterpret_cast<const TA*>(p.f);
-  const TA* __restrict__ gb = reinterpret_cast<const TA*>(p.b);
-  const float lam = expf(p.A_log[h]);
-  const int c0 = 2 * l;
-  const f32x2 dtb = *reinterpret_cast<const f32x2*>(p.dt_bias + (size_t)h * DH + c0);
-  // prep: wave w (of 8) rows 8w..8w+7, lane channels c0, c0+1; rows past the
-  // end are zero (q^ = k^ = 0, g = 0).  All row loads are issued before any use.
-  f32x2 qv[8], kv[8], fv[8];
-  float bv[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 8 * w + j;
-    const int rr = r < len ? r : 0;
-    const size_t o = ((size_t)(t0 + rr) * p.H + h) * DH + c0;
-    qv[j] = load2(gq + o);
-    kv[j] = load2(gk + o);
-    fv[j] = load2(gf + o);
-    bv[j] = to_f32(gb[(size_t)(t0 + rr) * p.H + h]);
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 8 * w + j;
-    const bool ok = r < len;
-    if (!ok) qv[j] = kv[j] = fv[j] = f32x2{0, 0};
-    const float sq = wave_sum(qv[j][0] * qv[j][0] + qv[j][1] * qv[j][1]);
-    const float sk = wave_sum(kv[j][0] * kv[j][0] + kv[j][1] * kv[j][1]);
-    const float rq = rsqrt_hw(sq + p.eps), rk = rsqrt_hw(sk + p.eps);
-    sQ[r * DH + c0] = qv[j][0] * rq; sQ[r * DH + c0 + 1] = qv[j][1] * rq;
-    sK[r * DH + c0] = kv[j][0] * rk; sK[r * DH + c0 + 1] = kv[j][1] * rk;
-    sG[r * DH + c0] = ok ? gate_log2(fv[j][0] + dtb[0], lam) : 0.0f;
-    sG[r * DH + c0 + 1] = ok ? gate_log2(fv[j][1] + dtb[1], lam) : 0.0f;
-    if (l == 0) {
-      sBeta[r] = ok ? sigmoid_f(bv[j]) : 0.0f;
-      p.rqk[ch * 2 * CHUNK + r] = rq;
-      p.rqk[ch * 2 * CHUNK + CHUNK + r] = rk;
-    }
-  }
-  __syncthreads();
-  if (tid < DH) {
-    float acc = 0.0f;
-    for (int r = 0; r < CHUNK; ++r) {
-      acc += sG[r * DH + tid];
-      sG[r * DH + tid] = acc;
-    }
-  } else {
-    for (int x = tid - DH; x < SQM / 4; x += 384) {
-      reinterpret_cast<f32x4*>(sA)[x] = reinterpret_cast<const f32x4*>(p.dam + ch * SQM)[x];
-      reinterpret_cast<f32x4*>(sP)[x] = reinterpret_cast<const f32x4*>(p.dpm + ch * SQM)[x];
-    }
-  }
-  __syncthreads();
-  for (int x = tid; x < MAT / 4; x += 512) {
-    reinterpret_cast<f32x4*>(p.qn + ch * MAT)[x] = reinterpret_cast<const f32x4*>(sQ)[x];
-    reinterpret_cast<f32x4*>(p.kn + ch * MAT)[x] = reinterpret_cast<const f32x4*>(sK)[x];
-    reinterpret_cast<f32x4*>(p.g2 + ch * MAT)[x] = reinterpret_cast<const f32x4*>(sG)[x];
-  }
-  // Four roles of 128 threads (one per channel): rows of blocks {7,6,1,0},
-  // rows of {5,4,3,2}, columns of blocks {0,1,6,7}, columns of {2,3,4,5}
-  // (18 of the 36 block pairs each).
-  const int c = tid & (DH - 1), role = tid >> 7;
-  const int set = role & 1;
-  if (role < 2) {
-    // rows: alpha_r = sum_{i<r} dA_ri k^_i e^{G_r-G_i}, pi_r = sum_{i<=r} dP_ri k^_i e^{..}
-    for (int k4 = 0; k4 < 4; ++k4) {
-      const int R = set == 0 ? (k4 < 2 ? 7 - k4 : 3 - k4) : 5 - k4;
-      const int m = 8 * R;
-      const float gm = sG[m * DH + c];
-      float ao[8], po[8];
-#pragma unroll
-      for (int a = 0; a < 8; ++a) ao[a] = po[a] = 0.0f;
-      for (int I = 0; I < R; ++I) {
-        float kt[8];
-#pragma unroll
-        for (int bb = 0; bb < 8; ++bb) {
-          const int i = 8 * I + bb;
-          kt[bb] = sK[i * DH + c] * exp2_hw(gm - sG[i * DH + c]);
-        }
-#pragma unroll
-        for (int a = 0; a < 8; ++a) {
-          const float* ar = sA + (m + a) * CHUNK + 8 * I;
-          const float* pr = sP + (m + a) * CHUNK + 8 * I;
-#pragma unroll
-          for (int bb = 0; bb < 8; ++bb) {
-            ao[a] = fmaf(ar[bb], kt[bb], ao[a]);
-            po[a] = fmaf(pr[bb], kt[bb], po[a]);
-          }
-        }
-      }
-#pragma unroll
-      for (int a = 0; a < 8; ++a) {
-        const int r = m + a;
-        const float gr = sG[r * DH + c];
-        const float fa = exp2_hw(gr - gm);
-        float al = ao[a] * fa, pv = po[a] * fa;
-#pragma unroll
-        for (int bb = 0; bb <= a; ++bb) {
-          const int i = m + bb;
-          const float kte = sK[i * DH + c] * exp2_hw(gr - sG[i * DH + c]);
-          al = fmaf(sA[r * CHUNK + i], kte, al);
-          pv = fmaf(sP[r * CHUNK + i], kte, pv);
-        }
-        p.al[ch * MAT + r * DH + c] = al;
-        p.pi[ch * MAT + r * DH + c] = pv;
-      }
-    }
-  } else {
-    // columns: rho_i = sum_{r>=i} (beta_r dA_ri k^_r + dP_ri q^_r) e^{G_r-G_i}
-    for (int k4 = 0; k4 < 4; ++k4) {
-      const int I = set == 0 ? (k4 < 2 ? k4 : 4 + k4) : 2 + k4;
-      float ro[8];
-#pragma unroll
-      for (int bb = 0; bb < 8; ++bb) ro[bb] = 0.0f;
-      for (int R = I + 1; R < 8; ++R) {
-        const int m = 8 * R;
-        const float gm = sG[m * DH + c];
-        float bk[8], qq[8], part[8];
-#pragma unroll
-        for (int a = 0; a < 8; ++a) {
-          const int r = m + a;
-          const float fa = exp2_hw(sG[r * DH + c] - gm);
-          bk[a] = sBeta[r] * sK[r * DH + c] * fa;
-          qq[a] = sQ[r * DH + c] * fa;
-        }
-#pragma unroll
-        for (int bb = 0; bb < 8; ++bb) part[bb] = 0.0f;
-#pragma unroll
-        for (int a = 0; a < 8; ++a) {
-          const float* ar = sA + (m + a) * CHUNK + 8 * I;
-          const float* pr = sP + (m + a) * CHUNK + 8 * I;
-#pragma unroll
-          for (int bb = 0; bb < 8; ++bb) part[bb] = fmaf(ar[bb], bk[a], fmaf(pr[bb], qq[a], part[bb]));
-        }
-#pragma unroll
-        for (int bb = 0; bb < 8; ++bb) {
-          const int i = 8 * I + bb;
-          ro[bb] = fmaf(exp2_hw(gm - sG[i * DH + c]), part[bb], ro[bb]);
-        }
-      }
-#pragma unroll
-      for (int bb = 0; bb < 8; ++bb) {
-        const int i = 8 * I + bb;
-        const float gi = sG[i * DH + c];
-        float rv = ro[bb];
-#pragma unroll
-        for (int a = bb; a < 8; ++a) {
-          const int r = 8 * I + a;
-          const float e = exp2_hw(sG[r * DH + c] - gi);
-          rv = fmaf(fmaf(sA[r * CHUNK + i], sBeta[r] * sK[r * DH + c], sP[r * CHUNK + i] * sQ[r * DH + c]), e, rv);
-        }
-        p.rho[ch * MAT + i * DH + c] = rv;
-      }
-    }
-  }
+// ------------------------------------------------------------ 6. decay-weighted sums and the chain
+// One workgroup of 8 waves per (chunk, head).
+//
+// Prep (wave w: rows 8w..8w+7, lane channels 2l, 2l+1): the norms'
+// reciprocals, the gate in log2 units and beta; then G, the prefix of the gate
+// over the chunk's rows (128 channels x 4 segments of 16 rows).  dA and dP go
+// to LDS in both orientations.
+//
+// Sums (wave w: channels 16w..16w+15; lane (n, g) = (l & 15, l >> 4) holds
+// channel 16w+n of its group's own rows 16R+4g+j, R, j = 0..3 -- the result
+// layout of a 16x16x4 FP32 MFMA tile):
+//   alpha_r = sum_{i<r} dA_ri k^_i e^{G_r-G_i},  pi_r = sum_{i<=r} dP_ri k^_i e^{..}
+//   rho_i   = sum_{r>=i} (beta_r dA_ri k^_r + dP_ri q^_r) e^{G_r-G_i}
+// Each exponential is split about a row m between the pair,
+// e^{G_r-G_i} = e^{G_r-G_m} e^{G_m-G_i}, both exponents <= 0:
+//   * a 16-row block against the earlier blocks: m = its first row (alpha, pi)
+//     or the first row after the column block (rho);
+//   * inside a block, rows 8..15 against columns 0..7: m = 8; rows 4..7
+//     against 0..3 and rows 12..15 against 8..11: m = 4, 12.
+// Each family is one MFMA accumulator, the factor of the contracted index on
+// the B operand and the other on the result.  The contracted index of step s
+// is, in lane group g, the group's own row 16R'+4g+s, so every B operand
+// (k^ or q^ times its factor) comes from registers and every A operand is one
+// 16-byte LDS read per four steps (dA rows for alpha, pi; dA^T rows for rho).
+// The 4x4 diagonal blocks (a lane group's own rows against each other) are
+// summed per element on the VALU.  Then the elementwise chain in the same
+// layout: the row sums over channels (16 lanes by DPP, 8 waves through LDS),
+// dq, dk, db, dG; the reverse prefix of dG per channel (in-lane over rows and
+// blocks, across the four lane groups by shuffles); df and the per-chunk
+// parameter partials.
+constexpr int GA_LD = 68;  // padded dA / dP row: 16-byte row reads of 8 lanes hit distinct banks
+// LDS layout of the gate kernel (floats)
+constexpr int GS_G = 0, GS_A = GS_G + CHUNK * DH, GS_P = GS_A + CHUNK * GA_LD,
+              GS_AT = GS_P + CHUNK * GA_LD, GS_PT = GS_AT + CHUNK * GA_LD, GS_RED = GS_PT + CHUNK * GA_LD,
+              GS_SUM = GS_RED + 3 * 8 * CHUNK, GS_BETA = GS_SUM + 3 * CHUNK, GS_RQ = GS_BETA + CHUNK,
+              GS_RK = GS_RQ + CHUNK, GS_SEG = GS_RK + CHUNK, GS_PA = GS_SEG + 4 * DH, GS_TOTAL = GS_PA + 8;
+constexpr int OP = GS_P - GS_A;  // dA -> dP, dA^T -> dP^T
+
+// G [64][128] in LDS with bits 4-5 of the channel XORed by (r ^ r/4) & 3, so
+// that the four lane groups reading their own rows 16R+4g+j hit four
+// different 16-bank ranges.
+__device__ __forceinline__ int gsw(int r, int c) { return r * DH + (c ^ (((r ^ (r >> 2)) & 3) << 4)); }
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// ------------------------------------------------------------ 7. elementwise chain
-// Wave w: rows 16w..16w+15, lane channels c0, c0+1.  Row-local parts (dq, dk,
-// db, dG) row by row; dG goes to LDS.  Then the reverse
-// prefix of dG over the chunk: inside the wave over its 16 rows from LDS,
-// across waves one carry (column totals of the later waves plus the last
-// row's d(G_last) terms), giving df and the per-chunk parameter partials.
+// Sums over the 16 lanes of a row of 4 values: two DPP halving steps leave
+// value 2 b3 + b2 in each lane (summed over four lanes), two butterfly steps
+// inside the quad finish the sum.
+__device__ __forceinline__ float row16_sum4(const float (&v)[4], int l) {
+  constexpr int DPP_MIRROR = 0x140, DPP_HALF_MIRROR = 0x141, DPP_XOR2 = 0x4E, DPP_XOR1 = 0xB1;
+  const bool b3 = (l >> 3) & 1, b2 = (l >> 2) & 1;
+  const float v1[2] = {dpp_halve<DPP_MIRROR>(v[0], v[2], b3), dpp_halve<DPP_MIRROR>(v[1], v[3], b3)};
+  float t = dpp_halve<DPP_HALF_MIRROR>(v1[0], v1[1], b2);
+  t += dpp_f<DPP_XOR2>(t);
+  return t + dpp_f<DPP_XOR1>(t);
+}
+
+// Sum over the 16 lanes of a row; every lane of the row gets the total.
+__device__ __forceinline__ float row16_sum(float x) {
+  constexpr int DPP_MIRROR = 0x140, DPP_HALF_MIRROR = 0x141, DPP_XOR2 = 0x4E, DPP_XOR1 = 0xB1;
+  x += dpp_f<DPP_MIRROR>(x);
+  x += dpp_f<DPP_HALF_MIRROR>(x);
+  x += dpp_f<DPP_XOR2>(x);
+  return x + dpp_f<DPP_XOR1>(x);
+}
+
 template <typename TA, typename TR>
-__global__ __launch_bounds__(256) void kda_bwd_final_kernel(BwdArgs p) {
-  __shared__ __attribute__((aligned(16))) float sDG[CHUNK * DH];
-  __shared__ float sTot[4][DH];
-  __shared__ float sCol[4][DH];
-  __shared__ float sPdt[4][DH];
-  __shared__ float sPa[4];
+__global__ __launch_bounds__(512) void kda_bwd_gate_kernel(BwdArgs p) {
+  __shared__ __attribute__((aligned(16))) float smem[GS_TOTAL];
+  float* const sG = smem + GS_G;
+  float* const sA = smem + GS_A;
+  float* const sAT = smem + GS_AT;
+  float (*const sRed)[8][CHUNK] = reinterpret_cast<float (*)[8][CHUNK]>(smem + GS_RED);
+  float (*const sSum)[CHUNK] = reinterpret_cast<float (*)[CHUNK]>(smem + GS_SUM);
+  float* const sBeta = smem + GS_BETA;
+  float* const sRq = smem + GS_RQ;
+  float* const sRk = smem + GS_RK;
+  float (*const sSeg)[DH] = reinterpret_cast<float (*)[DH]>(smem + GS_SEG);
+  float* const sPa = smem + GS_PA;
   const int cidx = blockIdx.x, h = blockIdx.y;
   int t0, len;
   if (!bwd_chunk(p, cidx, t0, len)) return;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const size_t ch = (size_t)cidx * p.H + h;
+  const size_t mb = ch * MAT;
+  const TA* __restrict__ gq = reinterpret_cast<const TA*>(p.q);
+  const TA* __restrict__ gk = reinterpret_cast<const TA*>(p.k);
   const TA* __restrict__ gf = reinterpret_cast<const TA*>(p.f);
   const TA* __restrict__ gb = reinterpret_cast<const TA*>(p.b);
   TR* __restrict__ gdq = reinterpret_cast<TR*>(p.dq);
   TR* __restrict__ gdk = reinterpret_cast<TR*>(p.dk);
   TR* __restrict__ gdf = reinterpret_cast<TR*>(p.df);
   TR* __restrict__ gdb = reinterpret_cast<TR*>(p.db);
-  const int c0 = 2 * l;
-  const size_t mb = ch * MAT;
   const float lam = expf(p.A_log[h]);
-  const f32x2 dtb = *reinterpret_cast<const f32x2*>(p.dt_bias + (size_t)h * DH + c0);
-  const f32x2 gL = load2(p.g2 + mb + (CHUNK - 1) * DH + c0);  // G_last (rows past the end keep it)
-  float tot0 = 0.0f, tot1 = 0.0f, col0 = 0.0f, col1 = 0.0f;
-#pragma unroll 2
-  for (int j = 0; j < 16; ++j) {
-    const int r = 16 * w + j;
-    const bool ok = r < len;
-    const int rr = ok ? r : 0;
-    const size_t o = mb + r * DH + c0;
-    const f32x2 qn = load2(p.qn + o), kn = load2(p.kn + o), g2 = load2(p.g2 + o);
-    const f32x2 al = load2(p.al + o), pv = load2(p.pi + o), rh = load2(p.rho + o);
-    const f32x2 dqt = load2(p.dqt + o), dkb = load2(p.dkb + o), dbw = load2(p.dbw + o);
-    const float bv = to_f32(gb[(size_t)(t0 + rr) * p.H + h]);
-    const float beta = ok ? sigmoid_f(bv) : 0.0f;
-    float dqn[2], dkn[2], dG[2], kbf[2], sb = 0.0f;
+  const int HD = p.H * DH;
+
+  // ---- loads: the prep's rows (wave w: rows 8w + 4u + l/16, u = 0, 1; lane
+  // channels 8 (l % 16) .. +7; rows past the end read row 0 and are zeroed),
+  // dA and dP, and at the lane's own rows of the sums' layout the raw q, k and
+  // the chain's inputs
+  const int c8 = 8 * (l & 15);
+  float qv[2][8], kv[2][8], fv[2][8];
+  float bv[2];
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const float E = exp2_hw(g2[x]), F = exp2_hw(gL[x] - g2[x]);
-      dqn[x] = pv[x] + dqt[x] * E;
-      dkn[x] = beta * al[x] + rh[x] + beta * dbw[x] * E + dkb[x] * F;
-      kbf[x] = ok ? dkb[x] * kn[x] * F : 0.0f;
-      dG[x] = ok ? beta * kn[x] * al[x] + qn[x] * pv[x] - kn[x] * rh[x] + dqt[x] * qn[x] * E +
-                       beta * dbw[x] * kn[x] * E - kbf[x]
-                 : 0.0f;
-      sb += kn[x] * al[x] + dbw[x] * kn[x] * E;
+  for (int u = 0; u < 2; ++u) {
+    const int r = 8 * w + 4 * u + (l >> 4);
+    const int rr = r < len ? r : 0;
+    const size_t o = ((size_t)(t0 + rr) * p.H + h) * DH + c8;
+    load8_scaled(gq + o, 1.0f, qv[u]);
+    load8_scaled(gk + o, 1.0f, kv[u]);
+    load8_scaled(gf + o, 1.0f, fv[u]);
+    bv[u] = to_f32(gb[(size_t)(t0 + rr) * p.H + h]);
+  }
+  f32x4 da4[2], dp4[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    da4[u] = reinterpret_cast<const f32x4*>(p.dam + ch * SQM)[tid + 512 * u];
+    dp4[u] = reinterpret_cast<const f32x4*>(p.dpm + ch * SQM)[tid + 512 * u];
+  }
+  const int n = l & 15, g = l >> 4, c = 16 * w + n;
+  // row 16R + 4g + j of a [64][128] workspace matrix: a wave-uniform row
+  // (16R + j) plus the lane's offset 4g * 128 + c; of a [T][H][128] tensor:
+  // token t0 + 16R + j plus 4g * H * 128 + c
+  const int lo_ws = 4 * g * DH + c;
+  const int lo_tok = 4 * g * HD + c;
+  float qo[4][4], ko[4][4];
+  {
+    const TA* q0 = gq + ((size_t)t0 * p.H + h) * DH;
+    const TA* k0 = gk + ((size_t)t0 * p.H + h) * DH;
+#pragma unroll
+    for (int R = 0; R < 4; ++R)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * R + 4 * g + j, o = (r < len ? r : 0) * HD + c;
+        qo[R][j] = to_f32(q0[o]);
+        ko[R][j] = to_f32(k0[o]);
+      }
+  }
+  // the chain's inputs of block R, loaded one block ahead of their use
+  float xdqt[4][4], xdkb[4][4], xdbw[4][4];
+  auto load_chain = [&](int R) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const size_t o = mb + (size_t)(16 * R + j) * DH;
+      xdqt[R][j] = (p.dqt + o)[lo_ws];
+      xdkb[R][j] = (p.dkb + o)[lo_ws];
+      xdbw[R][j] = (p.dbw + o)[lo_ws];
     }
-    tot0 += dG[0]; tot1 += dG[1];
-    col0 += kbf[0]; col1 += kbf[1];
-    *reinterpret_cast<f32x2*>(sDG + r * DH + c0) = f32x2{dG[0], dG[1]};
-    const float s_b = wave_sum(sb);
-    const float s_q = wave_sum(qn[0] * dqn[0] + qn[1] * dqn[1]);
-    const float s_k = wave_sum(kn[0] * dkn[0] + kn[1] * dkn[1]);
-    if (ok) {
-      const float rq = p.rqk[ch * 2 * CHUNK + r], rk = p.rqk[ch * 2 * CHUNK + CHUNK + r];
-      const size_t go = ((size_t)(t0 + r) * p.H + h) * DH + c0;
-      store2(gdq + go, rq * (dqn[0] - qn[0] * s_q), rq * (dqn[1] - qn[1] * s_q));
-      store2(gdk + go, rk * (dkn[0] - kn[0] * s_k), rk * (dkn[1] - kn[1] * s_k));
-      if (l == 0)
-        gdb[(size_t)(t0 + r) * p.H + h] =
-            from_f32<TR>((p.db1[ch * CHUNK + r] + s_b) * beta * (1.0f - beta));
+  };
+  load_chain(0);
+  // per-channel and per-row inputs of the chain's end
+  const float dgam_c = p.dgam[ch * DH + c];
+  const float dtb = p.dt_bias[(size_t)h * DH + c];
+  const float db1_r = tid < CHUNK ? p.db1[ch * CHUNK + tid] : 0.0f;
+
+  // ---- prep: norms by a sum over the row's 16 lanes, the gate, beta
+  {
+    const f32x4 dtb_lo = *reinterpret_cast<const f32x4*>(p.dt_bias + (size_t)h * DH + c8);
+    const f32x4 dtb_hi = *reinterpret_cast<const f32x4*>(p.dt_bias + (size_t)h * DH + c8 + 4);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int r = 8 * w + 4 * u + (l >> 4);
+      const bool ok = r < len;
+      float sq = 0.0f, sk = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sq = fmaf(qv[u][e], qv[u][e], sq);
+        sk = fmaf(kv[u][e], kv[u][e], sk);
+      }
+      sq = row16_sum(sq);
+      sk = row16_sum(sk);
+      f32x4 g_lo, g_hi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        g_lo[e] = ok ? gate_log2(fv[u][e] + dtb_lo[e], lam) : 0.0f;
+        g_hi[e] = ok ? gate_log2(fv[u][e + 4] + dtb_hi[e], lam) : 0.0f;
+      }
+      // eight adjacent channels stay adjacent under the swizzle
+      *reinterpret_cast<f32x4*>(sG + gsw(r, c8)) = g_lo;
+      *reinterpret_cast<f32x4*>(sG + gsw(r, c8) + 4) = g_hi;
+      if ((l & 15) == 0) {
+        sBeta[r] = ok ? sigmoid_f(bv[u]) : 0.0f;
+        sRq[r] = ok ? rsqrt_hw(sq + p.eps) : 0.0f;
+        sRk[r] = ok ? rsqrt_hw(sk + p.eps) : 0.0f;
+      }
     }
   }
-  sTot[w][c0] = tot0; sTot[w][c0 + 1] = tot1;
-  sCol[w][c0] = col0; sCol[w][c0 + 1] = col1;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int x = tid + 512 * u, r = x >> 4, c4 = 4 * (x & 15);
+    *reinterpret_cast<f32x4*>(sA + r * GA_LD + c4) = da4[u];
+    *reinterpret_cast<f32x4*>(sA + OP + r * GA_LD + c4) = dp4[u];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sAT[(c4 + e) * GA_LD + r] = da4[u][e];
+      sAT[OP + (c4 + e) * GA_LD + r] = dp4[u][e];
+    }
+  }
   __syncthreads();
-  // dg_r = sum_{j >= r} dG_j plus, on every valid row, the last row's extra
-  // terms sum_r dKb k^ F + dGam Gam (they belong to G_last)
-  float carry[2];
+  {
+    // G: running sums over 16-row segments, then the totals of the earlier segments
+    const int cc = tid & (DH - 1), seg = tid >> 7;
+    float gs[16];
+    float run = 0.0f;
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int c = c0 + x;
-    float a = sCol[0][c] + sCol[1][c] + sCol[2][c] + sCol[3][c] + p.dgam[ch * DH + c] * exp2_hw(gL[x]);
-    for (int w2 = w + 1; w2 < 4; ++w2) a += sTot[w2][c];
-    carry[x] = a;
-  }
-  float pdt0 = 0.0f, pdt1 = 0.0f, pa = 0.0f;
-  // x = f + dt_bias of the wave's 16 rows, loaded together (second read, cached)
-  f32x2 xs[16];
+    for (int j = 0; j < 16; ++j) {
+      run += sG[gsw(16 * seg + j, cc)];
+      gs[j] = run;
+    }
+    sSeg[seg][cc] = run;
+    __syncthreads();
+    float off = 0.0f;
+    for (int s = 0; s < seg; ++s) off += sSeg[s][cc];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int r = 16 * w + j;
-    xs[j] = load2(gf + ((size_t)(t0 + (r < len ? r : 0)) * p.H + h) * DH + c0) + dtb;
+    for (int j = 0; j < 16; ++j) sG[gsw(16 * seg + j, cc)] = gs[j] + off;
   }
+  __syncthreads();
+
+  // ---- sums, and the chain's row-local part block by block
+  // Lane addresses (every per-step address below is one of them plus a
+  // constant): ob[j] G at the group's own rows 16R + 4g + j; rb[u] G at rows
+  // m with m % 4 == 0, (m / 4) % 4 == u; rg4 G at row 16R + 4g + 4; aR the dA
+  // row 16R + n from column 16I + 4g; aC the dA^T row 16I + n from column
+  // 16R' + 4g; aD the group's diagonal 4x4 block of dA.
+  const float* ob[4];
+  const float* rb[4];
 #pragma unroll
-  for (int j = 15; j >= 0; --j) {
-    const int r = 16 * w + j;
-    if (r >= len) continue;  // uniform over the wave
-    const f32x2 dg = *reinterpret_cast<const f32x2*>(sDG + r * DH + c0);
-    const f32x2 xx = xs[j];
-    carry[0] += dg[0];
-    carry[1] += dg[1];
-    const float dx0 = lam == 0.0f ? 0.0f : -lam * sigmoid_f(xx[0]) * carry[0];
-    const float dx1 = lam == 0.0f ? 0.0f : -lam * sigmoid_f(xx[1]) * carry[1];
-    pdt0 += dx0;
-    pdt1 += dx1;
-    pa = fmaf(carry[0], gate_log2(xx[0], lam) * (1.0f / LOG2E), pa);
-    pa = fmaf(carry[1], gate_log2(xx[1], lam) * (1.0f / LOG2E), pa);
-    store2(gdf + ((size_t)(t0 + r) * p.H + h) * DH + c0, dx0, dx1);
+  for (int u = 0; u < 4; ++u) {
+    ob[u] = sG + (4 * g + u) * DH + (c ^ (((u ^ g) & 3) << 4));
+    rb[u] = sG + (c ^ (u << 4));
   }
-  sPdt[w][c0] = pdt0; sPdt[w][c0 + 1] = pdt1;
+  const float* rg4 = sG + (4 * g + 4) * DH + (c ^ (((g + 1) & 3) << 4));
+  const float* aR = sA + n * GA_LD + 4 * g;
+  const float* aC = sAT + n * GA_LD + 4 * g;
+  const float* aD = sA + 4 * g * GA_LD + 4 * g;
+  const float* bB = sBeta + 4 * g;
+  auto gref = [&](int m) { return rb[(m >> 2) & 3][m * DH]; };  // G at row m (m % 4 == 0)
+
+  // own rows: q^, k^ (zero past the end), G
+  float Ko[4][4], Qo[4][4], Go[4][4];
+#pragma unroll
+  for (int R = 0; R < 4; ++R)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * R + 4 * g + j;
+      const bool ok = r < len;
+      Ko[R][j] = ok ? ko[R][j] * sRk[r] : 0.0f;
+      Qo[R][j] = ok ? qo[R][j] * sRq[r] : 0.0f;
+      Go[R][j] = ob[j][16 * R * DH];
+    }
+  const float GL = sG[gsw(CHUNK - 1, c)];
+  // f at the lane's rows (for df), loaded while dq and dk are stored
+  float xf[4][4];
+  auto load_f = [&]() {
+    const TA* f0 = gf + ((size_t)t0 * p.H + h) * DH;
+#pragma unroll
+    for (int R = 0; R < 4; ++R)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * R + 4 * g + j;
+        xf[R][j] = to_f32(f0[(r < len ? r : 0) * HD + c]);
+      }
+  };
+  float dqn[4][4], dkn[4][4], dG[4][4];
+  float kbf_sum = 0.0f;
+#pragma unroll
+  for (int R = 0; R < 4; ++R) {
+    if (R < 3) load_chain(R + 1);
+    // ex[j][jj] = e^{G_j - G_jj}, jj <= j, inside the lane group's rows
+    float ex[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) ex[j][jj] = jj < j ? exp2_hw(Go[R][j] - Go[R][jj]) : 1.0f;
+    const float gm0 = gref(16 * R), gm8 = gref(16 * R + 8);
+    // G at row 16R + 4g + 4: reference of the 4-row families (groups 0, 2)
+    const float g4 = (R < 3 || g < 3) ? rg4[16 * R * DH] : 0.0f;
+    // the lane group's diagonal 4x4 blocks of dA and dP (row 16R+4g+j, column 16R+4g+jj)
+    f32x4 dAd[4], dPd[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      dAd[j] = *reinterpret_cast<const f32x4*>(aD + (16 * R + j) * GA_LD + 16 * R);
+      dPd[j] = *reinterpret_cast<const f32x4*>(aD + OP + (16 * R + j) * GA_LD + 16 * R);
+    }
+    float al[4], pv[4], rh[4];
+
+    // alpha, pi of the rows of block R (A: dA row 16R + n, columns 16I + 4g + s)
+    {
+      f32x4 oA = {0, 0, 0, 0}, oP = oA, eA = oA, eP = oA, fA = oA, fP = oA;
+#pragma unroll
+      for (int I = 0; I < R; ++I) {
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(aR + 16 * R * GA_LD + 16 * I);
+        const f32x4 p4 = *reinterpret_cast<const f32x4*>(aR + OP + 16 * R * GA_LD + 16 * I);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const float b = Ko[I][s] * exp2_hw(gm0 - Go[I][s]);
+          oA = mfma4(a4[s], b, oA);
+          oP = mfma4(p4[s], b, oP);
+        }
+      }
+      const f32x4 a4 = *reinterpret_cast<const f32x4*>(aR + 16 * R * GA_LD + 16 * R);
+      const f32x4 p4 = *reinterpret_cast<const f32x4*>(aR + OP + 16 * R * GA_LD + 16 * R);
+      // rows 8..15 against columns 0..7 (groups 0, 1); rows 4..7 against
+      // columns 0..3 (group 0) and rows 12..15 against 8..11 (group 2)
+      const bool on8 = n >= 8 && g < 2;
+      const bool on4 = (g == 0 && (n >> 2) == 1) || (g == 2 && (n >> 2) == 3);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const float b8 = Ko[R][s] * exp2_hw(fminf(gm8 - Go[R][s], 0.0f));
+        eA = mfma4(on8 ? a4[s] : 0.0f, b8, eA);
+        eP = mfma4(on8 ? p4[s] : 0.0f, b8, eP);
+        const float b4 = Ko[R][s] * exp2_hw(fminf(g4 - Go[R][s], 0.0f));
+        fA = mfma4(on4 ? a4[s] : 0.0f, b4, fA);
+        fP = mfma4(on4 ? p4[s] : 0.0f, b4, fP);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float gr = Go[R][j];
+        float a = 0.0f, q = 0.0f;
+        if (R > 0) {
+          const float e = exp2_hw(gr - gm0);
+          a = oA[j] * e;
+          q = oP[j] * e;
+        }
+        const float e8 = exp2_hw(fminf(gr - gm8, 0.0f));  // eA, eP are zero where it is clamped
+        a = fmaf(eA[j], e8, a);
+        q = fmaf(eP[j], e8, q);
+        a = fmaf(fA[j], ex[j][0], a);  // reference row 16R + 4g, the group's first row
+        q = fmaf(fP[j], ex[j][0], q);
+#pragma unroll
+        for (int jj = 0; jj <= j; ++jj) {
+          const float kte = Ko[R][jj] * ex[j][jj];
+          if (jj < j) a = fmaf(dAd[j][jj], kte, a);
+          q = fmaf(dPd[j][jj], kte, q);
+        }
+        al[j] = a;
+        pv[j] = q;
+      }
+    }
+
+    // rho of the columns of block I = R (A: dA^T row 16I + n, columns 16R' + 4g + s)
+    {
+      const int I = R;
+      f32x4 o = {0, 0, 0, 0}, e8 = o, f4 = o;
+      const float gm = I < 3 ? gref(16 * (I + 1)) : 0.0f;
+#pragma unroll
+      for (int R2 = I + 1; R2 < 4; ++R2) {
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(aC + 16 * I * GA_LD + 16 * R2);
+        const f32x4 p4 = *reinterpret_cast<const f32x4*>(aC + OP + 16 * I * GA_LD + 16 * R2);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const float e = exp2_hw(Go[R2][s] - gm);
+          o = mfma4(a4[s], bB[16 * R2 + s] * Ko[R2][s] * e, o);
+          o = mfma4(p4[s], Qo[R2][s] * e, o);
+        }
+      }
+      const f32x4 a4 = *reinterpret_cast<const f32x4*>(aC + 16 * I * GA_LD + 16 * I);
+      const f32x4 p4 = *reinterpret_cast<const f32x4*>(aC + OP + 16 * I * GA_LD + 16 * I);
+      // rows 8..15 (groups 2, 3) against columns 0..7; rows 4..7 (group 1)
+      // against columns 0..3 and rows 12..15 (group 3) against 8..11
+      const bool on8 = g >= 2 && n < 8;
+      const bool on4 = (g == 1 && n < 4) || (g == 3 && (n >> 2) == 2);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const float e = exp2_hw(fminf(Go[I][s] - gm8, 0.0f));
+        e8 = mfma4(on8 ? a4[s] : 0.0f, bB[16 * I + s] * Ko[I][s] * e, e8);
+        e8 = mfma4(on8 ? p4[s] : 0.0f, Qo[I][s] * e, e8);
+        // reference row 16I + 4g, the contributing group's first row
+        f4 = mfma4(on4 ? a4[s] : 0.0f, bB[16 * I + s] * Ko[I][s] * ex[s][0], f4);
+        f4 = mfma4(on4 ? p4[s] : 0.0f, Qo[I][s] * ex[s][0], f4);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float gi = Go[I][j];
+        float rv = I < 3 ? o[j] * exp2_hw(gm - gi) : 0.0f;
+        rv = fmaf(e8[j], exp2_hw(fminf(gm8 - gi, 0.0f)), rv);
+        // f4 reaches this lane's columns for g = 0, 2 (reference row 16I + 4g + 4)
+        rv = fmaf(f4[j], exp2_hw(fminf(g4 - gi, 0.0f)), rv);
+#pragma unroll
+        for (int jj = j; jj < 4; ++jj)
+          rv = fmaf(fmaf(dAd[jj][j], bB[16 * I + jj] * Ko[I][jj], dPd[jj][j] * Qo[I][jj]), ex[jj][j], rv);
+        rh[j] = rv;
+      }
+    }
+
+    // the chain's row-local part for rows 16R + 4g + j
+    float vq[4], vk[4], vb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * R + 4 * g + j;
+      const bool ok = r < len;
+      const float E = exp2_hw(Go[R][j]), F = exp2_hw(GL - Go[R][j]);
+      const float beta = bB[16 * R + j], kn = Ko[R][j], qn = Qo[R][j];
+      const float a = al[j], pp = pv[j], rr = rh[j];
+      const float dqt = xdqt[R][j], dkb = xdkb[R][j], dbw = xdbw[R][j];
+      dqn[R][j] = pp + dqt * E;
+      dkn[R][j] = beta * a + rr + beta * dbw * E + dkb * F;
+      const float kbf = ok ? dkb * kn * F : 0.0f;
+      dG[R][j] = ok ? beta * kn * a + qn * pp - kn * rr + dqt * qn * E + beta * dbw * kn * E - kbf : 0.0f;
+      kbf_sum += kbf;
+      vq[j] = qn * dqn[R][j];
+      vk[j] = kn * dkn[R][j];
+      vb[j] = kn * a + dbw * kn * E;
+    }
+    // row sums over this wave's 16 channels: the lanes of a quad end with the
+    // total of row 16R + 4g + (2 b3 + b2)
+    const float tq = row16_sum4(vq, l), tk = row16_sum4(vk, l), tb = row16_sum4(vb, l);
+    if ((n & 3) == 0) {
+      const int r = 16 * R + 4 * g + (n >> 2);
+      sRed[0][w][r] = tq;
+      sRed[1][w][r] = tk;
+      sRed[2][w][r] = tb;
+    }
+  }
+  __syncthreads();
+  if (tid < 3 * CHUNK) {
+    const int qi = tid >> 6, r = tid & (CHUNK - 1);
+    float s = 0.0f;
+#pragma unroll
+    for (int w2 = 0; w2 < 8; ++w2) s += sRed[qi][w2][r];
+    sSum[qi][r] = s;
+  }
+  __syncthreads();
+  load_f();
+#pragma unroll
+  for (int R = 0; R < 4; ++R) {
+    const f32x4 sq4 = *reinterpret_cast<const f32x4*>(&sSum[0][16 * R + 4 * g]);
+    const f32x4 sk4 = *reinterpret_cast<const f32x4*>(&sSum[1][16 * R + 4 * g]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * R + 4 * g + j;
+      if (r < len) {
+        const size_t go = ((size_t)(t0 + 16 * R + j) * p.H + h) * DH;
+        (gdq + go)[lo_tok] = from_f32<TR>(sRq[r] * (dqn[R][j] - Qo[R][j] * sq4[j]));
+        (gdk + go)[lo_tok] = from_f32<TR>(sRk[r] * (dkn[R][j] - Ko[R][j] * sk4[j]));
+      }
+    }
+  }
+  if (tid < len && tid < CHUNK) {
+    const float beta = sBeta[tid];
+    gdb[(size_t)(t0 + tid) * p.H + h] =
+        from_f32<TR>((db1_r + sSum[2][tid]) * beta * (1.0f - beta));
+  }
+
+  // dg_r = sum_{j >= r} dG_j plus, on every valid row, the terms of G_last:
+  // sum_r dKb k^ F + dGam Gam
+  float kt = kbf_sum;
+  kt += __shfl_xor(kt, 16, 64);
+  kt += __shfl_xor(kt, 32, 64);
+  const float carry0 = kt + dgam_c * exp2_hw(GL);
+  float suf[4], tot[4];
+#pragma unroll
+  for (int R = 0; R < 4; ++R) {
+    const float bs = (dG[R][0] + dG[R][1]) + (dG[R][2] + dG[R][3]);
+    const float y1 = __shfl_xor(bs, 16, 64);  // group g ^ 1
+    const float pair = bs + y1;
+    const float y2 = __shfl_xor(pair, 32, 64);  // the other pair of groups
+    tot[R] = pair + y2;
+    suf[R] = ((g & 1) == 0 ? y1 : 0.0f) + (g < 2 ? y2 : 0.0f);  // groups after g
+  }
+  float later = 0.0f, pdt = 0.0f, pa = 0.0f;
+#pragma unroll
+  for (int R = 3; R >= 0; --R) {
+    float run = carry0 + later + suf[R];
+#pragma unroll
+    for (int j = 3; j >= 0; --j) {
+      const int r = 16 * R + 4 * g + j;
+      run += dG[R][j];
+      if (r < len) {
+        const float x = xf[R][j] + dtb;
+        const float dx = lam == 0.0f ? 0.0f : -lam * sigmoid_f(x) * run;
+        pdt += dx;
+        pa = fmaf(run, gate_log2(x, lam) * (1.0f / LOG2E), pa);
+        (gdf + ((size_t)(t0 + 16 * R + j) * p.H + h) * DH)[lo_tok] = from_f32<TR>(dx);
+      }
+    }
+    later += tot[R];
+  }
+  pdt += __shfl_xor(pdt, 16, 64);
+  pdt += __shfl_xor(pdt, 32, 64);
+  if (g == 0) p.ppart[ch * PPART + c] = pdt;
   pa = wave_sum(pa);
   if (l == 0) sPa[w] = pa;
   __syncthreads();
-  if (tid < DH) p.ppart[ch * PPART + tid] = sPdt[0][tid] + sPdt[1][tid] + sPdt[2][tid] + sPdt[3][tid];
-  if (tid == 0) p.ppart[ch * PPART + DH] = sPa[0] + sPa[1] + sPa[2] + sPa[3];
+  if (tid == 0) {
+    float s = 0.0f;
+#pragma unroll
+    for (int w2 = 0; w2 < 8; ++w2) s += sPa[w2];
+    p.ppart[ch * PPART + DH] = s;
+  }
 }
 
-// ------------------------------------------------------------ 8. parameter gradients
+// ------------------------------------------------------------ 7. parameter gradients
 // dt_bias and A_log gradients of head h: per-chunk partials summed in chunk
 // order (FP32, deterministic).
 __global__ __launch_bounds__(DH) void kda_bwd_param_kernel(BwdArgs p) {

@@ -304,7 +304,9 @@ static int dispatch(const void* q, const void* k, const void* v, const void* f, 
 
 // ------------------------------------------------------------ backward
 // Workspace of the backward, FP32 arrays per (chunk, head) after the chunk
-// table.
+// table.  The outputs of the value and T products take the space of arrays
+// whose only readers are the two scans, which have finished by then: dQt,
+// dKb, dW and dP the records, dBw W^T, dA the Kb copy, dGam Gam.
 struct BwdLayout {
   size_t off_cfirst, off_gam, off_rec, off_t, off_bw, off_wt, off_kbr, off_s0, off_dsn, off_d,
       off_dd, off_dqt, off_dkb, off_dw, off_dbw, off_dp, off_da, off_dgam, off_db1, off_pp, total;
@@ -326,13 +328,14 @@ static inline BwdLayout bwd_layout(int64_t T, int32_t N, int32_t H) {
   L.off_dsn = take(4 * CH * STM);
   L.off_d = take(4 * CH * MAT);
   L.off_dd = take(4 * CH * MAT);
-  L.off_dqt = take(4 * CH * MAT);
-  L.off_dkb = take(4 * CH * MAT);
-  L.off_dw = take(4 * CH * MAT);
-  L.off_dbw = take(4 * CH * MAT);
-  L.off_dp = take(4 * CH * SQM);
-  L.off_da = take(4 * CH * SQM);
-  L.off_dgam = take(4 * CH * DH);
+  static_assert(3 * MAT + SQM <= REC, "dQt, dKb, dW and dP fit in the records");
+  L.off_dqt = L.off_rec;
+  L.off_dkb = L.off_dqt + 4 * CH * MAT;
+  L.off_dw = L.off_dkb + 4 * CH * MAT;
+  L.off_dp = L.off_dw + 4 * CH * MAT;
+  L.off_dbw = L.off_wt;
+  L.off_da = L.off_kbr;
+  L.off_dgam = L.off_gam;
   L.off_db1 = take(4 * CH * CHUNK);
   L.off_pp = take(4 * CH * PPART);
   L.total = o;

@@ -252,8 +252,8 @@ KDA_API int kda_recurrent_fwd_rect(const void* q, const void* k, const void* v, 
                            const float* initial_state, float* final_state, void* stream);
 
 /* Workspace bytes needed by kda_chunk_bwd (same arguments and failure value
- * as kda_chunk_fwd_workspace_bytes).  FP32 throughout: about 620 KB per
- * (64-token chunk, head), e.g. 10.2 GB for 16384 tokens x 64 heads. */
+ * as kda_chunk_fwd_workspace_bytes).  FP32 throughout: about 460 KB per
+ * (64-token chunk, head), e.g. 7.5 GB for 16384 tokens x 64 heads. */
 KDA_API size_t kda_chunk_bwd_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t H,
                                      int32_t d, uint32_t mode);
 
@@ -294,8 +294,8 @@ KDA_API int kda_chunk_bwd(const void* q, const void* k, const void* v, const voi
  * value as kda_chunk_fwd_workspace_bytes; the mode decides the activation
  * dtype of the stored convolution outputs).  kda_chunk_bwd's workspace plus
  * the three convolution outputs, their FP32 gradients, FP32 gradients of
- * f_raw and b_raw and per-chunk tap partial sums: about 810 KB per (64-token
- * chunk, head) with bf16 activations, e.g. 13.3 GB for 16384 tokens x 64
+ * f_raw and b_raw and per-chunk tap partial sums: about 650 KB per (64-token
+ * chunk, head) with bf16 activations, e.g. 10.7 GB for 16384 tokens x 64
  * heads. */
 KDA_API size_t kda_chunk_bwd_conv_workspace_bytes(int64_t total_tokens, int32_t num_seqs,
                                           int32_t H, int32_t d, uint32_t mode);

@@ -304,12 +304,12 @@ static int dispatch(const void* q, const void* k, const void* v, const void* f, 
 
 // ------------------------------------------------------------ backward
 // Workspace of the backward, FP32 arrays per (chunk, head) after the chunk
-// table.  The outputs of the value and T products take the space of arrays
-// whose only readers are the two scans, which have finished by then: dQt,
-// dKb, dW and dP the records, dBw W^T, dA the Kb copy, dGam Gam.
+// table.  The outputs of the products kernel take the space of arrays whose
+// only readers are the two scans, which have finished by then: dQt, dKb and
+// dP the records, dBw W^T, dA the Kb copy, dGam Gam (dW never leaves it).
 struct BwdLayout {
   size_t off_cfirst, off_gam, off_rec, off_t, off_bw, off_wt, off_kbr, off_s0, off_dsn, off_d,
-      off_dd, off_dqt, off_dkb, off_dw, off_dbw, off_dp, off_da, off_dgam, off_db1, off_pp, total;
+      off_dd, off_dqt, off_dkb, off_dbw, off_dp, off_da, off_dgam, off_db1, off_pp, total;
 };
 
 static inline BwdLayout bwd_layout(int64_t T, int32_t N, int32_t H) {
@@ -328,11 +328,10 @@ static inline BwdLayout bwd_layout(int64_t T, int32_t N, int32_t H) {
   L.off_dsn = take(4 * CH * STM);
   L.off_d = take(4 * CH * MAT);
   L.off_dd = take(4 * CH * MAT);
-  static_assert(3 * MAT + SQM <= REC, "dQt, dKb, dW and dP fit in the records");
+  static_assert(2 * MAT + SQM <= REC, "dQt, dKb and dP fit in the records");
   L.off_dqt = L.off_rec;
   L.off_dkb = L.off_dqt + 4 * CH * MAT;
-  L.off_dw = L.off_dkb + 4 * CH * MAT;
-  L.off_dp = L.off_dw + 4 * CH * MAT;
+  L.off_dp = L.off_dkb + 4 * CH * MAT;
   L.off_dbw = L.off_wt;
   L.off_da = L.off_kbr;
   L.off_dgam = L.off_gam;
@@ -376,7 +375,7 @@ static int launch_bwd(const void* q, const void* k, const void* v, const void* f
   a.rec = fp(L.off_rec); a.gam = fp(L.off_gam); a.tmat = fp(L.off_t); a.bw = fp(L.off_bw);
   a.wt = fp(L.off_wt); a.kbr = fp(L.off_kbr);
   a.s0 = fp(L.off_s0); a.dsn = fp(L.off_dsn); a.dmat = fp(L.off_d); a.ddmat = fp(L.off_dd);
-  a.dqt = fp(L.off_dqt); a.dkb = fp(L.off_dkb); a.dw = fp(L.off_dw); a.dbw = fp(L.off_dbw);
+  a.dqt = fp(L.off_dqt); a.dkb = fp(L.off_dkb); a.dbw = fp(L.off_dbw);
   a.dpm = fp(L.off_dp); a.dam = fp(L.off_da); a.dgam = fp(L.off_dgam); a.db1 = fp(L.off_db1);
   a.ppart = fp(L.off_pp);
   a.dq = dq; a.dk = dk; a.dv = dv; a.df = df; a.db = db;
@@ -385,8 +384,7 @@ static int launch_bwd(const void* q, const void* k, const void* v, const void* f
   const dim3 gscan(32, (unsigned)((pairs + 7) / 8));  // workgroup id = x + 32 y
   hipLaunchKernelGGL(kda_bwd_fscan_kernel, gscan, dim3(SCAN_THREADS), 0, stream, a);
   hipLaunchKernelGGL((kda_bwd_bscan_kernel<TG>), gscan, dim3(SCAN_THREADS), 0, stream, a);
-  hipLaunchKernelGGL((kda_bwd_jprod_kernel<TG>), gch, dim3(256), 0, stream, a);
-  hipLaunchKernelGGL((kda_bwd_tprod_kernel<TA, TR>), gch, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((kda_bwd_prod_kernel<TA, TG, TR>), gch, dim3(256), 0, stream, a);
   hipLaunchKernelGGL((kda_bwd_gate_kernel<TA, TR>), gch, dim3(512), 0, stream, a);
   hipLaunchKernelGGL(kda_bwd_param_kernel, dim3((unsigned)H), dim3(DH), 0, stream, a);
   return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;

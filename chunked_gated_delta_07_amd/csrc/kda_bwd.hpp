@@ -40,11 +40,11 @@
 //      W^T, Kb
 //   2. kda_bwd_fscan_kernel: S0 of every chunk and D           (per sequence, head, 32 values)
 //   3. kda_bwd_bscan_kernel: dSn of every chunk, dD, dS_init   (same, chunks in reverse)
-//   4. kda_bwd_jprod_kernel: dQt, dP, dKb, dW, dGam            (per chunk, head)
-//   5. kda_bwd_tprod_kernel: dv, dbeta part, dBw, dA          (per chunk, head)
-//   6. kda_bwd_gate_kernel:  q^, k^, G, alpha, pi, rho, then dq, dk, df, db and the
+//   4. kda_bwd_prod_kernel:  dQt, dP, dKb, dW, dGam, then dv, dbeta part, dBw, dA
+//                                                              (per chunk, head)
+//   5. kda_bwd_gate_kernel:  q^, k^, G, alpha, pi, rho, then dq, dk, df, db and the
 //      parameter parts                                        (per chunk, head)
-//   7. kda_bwd_param_kernel: dA_log, dt_bias gradient          (per head, fixed order)
+//   6. kda_bwd_param_kernel: dA_log, dt_bias gradient          (per head, fixed order)
 #pragma once
 
 #include "kda_common.hpp"
@@ -87,7 +87,6 @@ struct BwdArgs {
   float* ddmat;            // dD [64][128]
   float* dqt;              // dQt [64][128]
   float* dkb;              // dKb [64][128]
-  float* dw;               // dW [64][128]
   float* dbw;              // dBw [64][128]
   float* dpm;              // dP [64][64]
   float* dam;              // dA [64][64]
@@ -406,24 +405,79 @@ __device__ __forceinline__ bool bwd_chunk(const BwdArgs& p, int c, int& t0, int&
   return locate_chunk(p.cu, p.cfirst, p.N, c, t0, len, tseq);
 }
 
-// ------------------------------------------------------------ 4. products over values
-// dQt = scale dO S0^T, dP = scale dO D^T (i <= r), dKb = D dSn^T, dW = -dD S0^T,
-// dGam = rowsum(dSn * S0); contracted over the 128 value channels in four
-// slabs of 32.  Wave w owns token rows 16w..16w+15 of every output.
-template <typename TG>
-__global__ __launch_bounds__(256, 2) void kda_bwd_jprod_kernel(BwdArgs p) {
+// ------------------------------------------------------------ 4. products
+// One workgroup of 4 waves per (chunk, head); wave w owns token rows
+// 16w..16w+15 of every output.
+//  (a) over the 128 value channels, in four slabs of 32:
+//      dQt = scale dO S0^T, dP = scale dO D^T (i <= r), dKb = D dSn^T,
+//      dW = -dD S0^T, dGam = rowsum(dSn * S0);
+//  (b) with T: dBu = T^T dD -> dv = beta dBu and db1 = v . dBu per row;
+//      dBw = T^T dW; dT = dD Bu^T + dW Bw^T; dA = -(T^T dT) T^T, strictly lower.
+// dW stays in the accumulators of (a) until (b) stores it in LDS; T and dD
+// are loaded during the last slab of (a).  (a) and (b) share one 80 KB LDS
+// block, two workgroups per CU; in (b) the matrices are unpadded with their
+// 16-byte chunks XOR-swizzled by row.
+template <int LC>
+__device__ __forceinline__ int swz(int r, int c) {
+  return r * LC + ((((c >> 2) ^ (r & (LC / 4 - 1)))) << 2) + (c & 3);
+}
+// C[m][n] += sum_k A[m0+m][k] B[n0+n][k], both swizzled rows of K (16-byte reads)
+template <int LCA, int LCB, int K>
+__device__ __forceinline__ f32x4 mma16_rows_swz(const float* A, int m0, const float* B, int n0,
+                                                f32x4 c, int lane) {
+  constexpr int KG = K / 4;
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < KG / 4; ++s) {
+    const int k = g * KG + 4 * s;
+    const f32x4 a4 = *reinterpret_cast<const f32x4*>(A + swz<LCA>(m0 + r, k));
+    const f32x4 b4 = *reinterpret_cast<const f32x4*>(B + swz<LCB>(n0 + r, k));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[e], b4[e], c, 0, 0, 0);
+  }
+  return c;
+}
+// C[m][n] += sum_k At[k][m0+m] B[k][n0+n], both swizzled, k-major
+template <int LCA, int LCB, int K>
+__device__ __forceinline__ f32x4 mma16_tn_swz(const float* At, int m0, const float* B, int n0,
+                                              f32x4 c, int lane) {
+  constexpr int KG = K / 4;
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < KG; ++s) {
+    const int k = g * KG + s;
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(At[swz<LCA>(k, m0 + r)], B[swz<LCB>(k, n0 + r)], c, 0,
+                                             0, 0);
+  }
+  return c;
+}
+
+template <typename TA, typename TG, typename TR>
+__global__ __launch_bounds__(256, 2) void kda_bwd_prod_kernel(BwdArgs p) {
   constexpr int LS = 36;
-  __shared__ __attribute__((aligned(16))) float sO[CHUNK * LS];
-  __shared__ __attribute__((aligned(16))) float sDm[CHUNK * LS];
-  __shared__ __attribute__((aligned(16))) float sDD[CHUNK * LS];
-  __shared__ __attribute__((aligned(16))) float sS0[DH * LS];
-  __shared__ __attribute__((aligned(16))) float sDS[DH * LS];
+  __shared__ __attribute__((aligned(16))) float smem[SQM + 2 * MAT];
+  // (a): slabs of 32 value channels, rows padded to 36
+  float* const sO = smem;
+  float* const sDm = sO + CHUNK * LS;
+  float* const sDD = sDm + CHUNK * LS;
+  float* const sS0 = sDD + CHUNK * LS;
+  float* const sDS = sS0 + DH * LS;
+  static_assert(3 * CHUNK * LS + 2 * DH * LS <= SQM + 2 * MAT, "slabs fit the block");
+  // (b)
+  float* const sT = smem;
+  float* const sR1 = smem + SQM;
+  float* const sR2 = sR1 + MAT;
   const int c = blockIdx.x, h = blockIdx.y;
   int t0, len;
   if (!bwd_chunk(p, c, t0, len)) return;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const size_t ch = (size_t)c * p.H + h;
   const TG* __restrict__ gO = reinterpret_cast<const TG*>(p.dout);
+  const TA* __restrict__ gv = reinterpret_cast<const TA*>(p.v);
+  const TA* __restrict__ gb = reinterpret_cast<const TA*>(p.b);
+  TR* __restrict__ gdv = reinterpret_cast<TR*>(p.dv);
+
+  // ---- (a)
   f32x4 aq[8], ak[8], aw[8], ap[4];
 #pragma unroll
   for (int x = 0; x < 8; ++x) aq[x] = ak[x] = aw[x] = f32x4{0, 0, 0, 0};
@@ -473,11 +527,21 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_jprod_kernel(BwdArgs p) {
       store4(sDS + i * LS + j4, rDS[u]);
     }
   };
+  // T and dD for (b), loaded during the last slab
+  f32x4 rT[4], rDf[8];
   fetch(0);
   stage();
   __syncthreads();
+#pragma unroll
   for (int sl = 0; sl < 4; ++sl) {
-    if (sl < 3) fetch(sl + 1);
+    if (sl < 3) {
+      fetch(sl + 1);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) rT[u] = *reinterpret_cast<const f32x4*>(p.tmat + ch * SQM + 4 * (tid + 256 * u));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) rDf[u] = *reinterpret_cast<const f32x4*>(p.ddmat + ch * MAT + 4 * (tid + 256 * u));
+    }
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) {
       aq[cb] = mma16_rows<float, 32>(sO + 16 * w * LS, LS, sS0 + 16 * cb * LS, LS, aq[cb], l);
@@ -505,7 +569,6 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_jprod_kernel(BwdArgs p) {
       const int r = 16 * w + 4 * (l >> 4) + e;
       p.dqt[ch * MAT + r * DH + col] = aq[cb][e];
       p.dkb[ch * MAT + r * DH + col] = ak[cb][e];
-      p.dw[ch * MAT + r * DH + col] = -aw[cb][e];
     }
   }
 #pragma unroll
@@ -518,76 +581,20 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_jprod_kernel(BwdArgs p) {
     }
   }
   if (tid < DH) p.dgam[ch * DH + tid] = gacc;
-}
 
-// ------------------------------------------------------------ 5. products with T
-// dBu = T^T dD -> dv = beta dBu and db1 = v . dBu per row; dBw = T^T dW;
-// dT = dD Bu^T + dW Bw^T;  dA = -(T^T dT) T^T, strictly lower.
-// LDS holds unpadded matrices whose 16-byte chunks are XOR-swizzled by row
-// (T [64][64], two [64][128] operands; 80 KB in all, two workgroups per CU).
-template <int LC>
-__device__ __forceinline__ int swz(int r, int c) {
-  return r * LC + ((((c >> 2) ^ (r & (LC / 4 - 1)))) << 2) + (c & 3);
-}
-// C[m][n] += sum_k A[m0+m][k] B[n0+n][k], both swizzled rows of K (16-byte reads)
-template <int LCA, int LCB, int K>
-__device__ __forceinline__ f32x4 mma16_rows_swz(const float* A, int m0, const float* B, int n0,
-                                                f32x4 c, int lane) {
-  constexpr int KG = K / 4;
-  const int r = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int s = 0; s < KG / 4; ++s) {
-    const int k = g * KG + 4 * s;
-    const f32x4 a4 = *reinterpret_cast<const f32x4*>(A + swz<LCA>(m0 + r, k));
-    const f32x4 b4 = *reinterpret_cast<const f32x4*>(B + swz<LCB>(n0 + r, k));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[e], b4[e], c, 0, 0, 0);
-  }
-  return c;
-}
-// C[m][n] += sum_k At[k][m0+m] B[k][n0+n], both swizzled, k-major
-template <int LCA, int LCB, int K>
-__device__ __forceinline__ f32x4 mma16_tn_swz(const float* At, int m0, const float* B, int n0,
-                                              f32x4 c, int lane) {
-  constexpr int KG = K / 4;
-  const int r = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int s = 0; s < KG; ++s) {
-    const int k = g * KG + s;
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(At[swz<LCA>(k, m0 + r)], B[swz<LCB>(k, n0 + r)], c, 0,
-                                             0, 0);
-  }
-  return c;
-}
-
-template <typename TA, typename TR>
-__global__ __launch_bounds__(256, 2) void kda_bwd_tprod_kernel(BwdArgs p) {
-  __shared__ __attribute__((aligned(16))) float sT[CHUNK * CHUNK];
-  __shared__ __attribute__((aligned(16))) float sR1[CHUNK * DH];
-  __shared__ __attribute__((aligned(16))) float sR2[CHUNK * DH];
-  const int c = blockIdx.x, h = blockIdx.y;
-  int t0, len;
-  if (!bwd_chunk(p, c, t0, len)) return;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const size_t ch = (size_t)c * p.H + h;
-  const TA* __restrict__ gv = reinterpret_cast<const TA*>(p.v);
-  const TA* __restrict__ gb = reinterpret_cast<const TA*>(p.b);
-  TR* __restrict__ gdv = reinterpret_cast<TR*>(p.dv);
+  // ---- (b) phase 1: T, dD, raw v (rows past the end zero); the slabs are done
   auto beta_of = [&](int i) {
     return i < len ? sigmoid_f(to_f32(gb[(size_t)(t0 + i) * p.H + h])) : 0.0f;
   };
-  // phase 1: T, dD, raw v (rows past the end zero)
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int x = tid + 256 * u, r = x >> 4, i4 = 4 * (x & 15);
-    *reinterpret_cast<f32x4*>(sT + swz<CHUNK>(r, i4)) =
-        *reinterpret_cast<const f32x4*>(p.tmat + ch * SQM + 4 * x);
+    *reinterpret_cast<f32x4*>(sT + swz<CHUNK>(r, i4)) = rT[u];
   }
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int x = tid + 256 * u, r = x >> 5, c4 = 4 * (x & 31);
-    *reinterpret_cast<f32x4*>(sR1 + swz<DH>(r, c4)) =
-        *reinterpret_cast<const f32x4*>(p.ddmat + ch * MAT + 4 * x);
+    *reinterpret_cast<f32x4*>(sR1 + swz<DH>(r, c4)) = rDf[u];
   }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -644,12 +651,15 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_tprod_kernel(BwdArgs p) {
     dt[ib] = acc * bcol[ib];
   }
   __syncthreads();
-  // phase 2: dW -> sR1, Bw -> sR2 (the other workgroup on the CU covers the latency)
+  // phase 2: dW (from the accumulators of (a)) -> sR1, Bw -> sR2
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      sR1[swz<DH>(16 * w + 4 * (l >> 4) + e, 16 * cb + (l & 15))] = -aw[cb][e];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int x = tid + 256 * u, r = x >> 5, c4 = 4 * (x & 31);
-    *reinterpret_cast<f32x4*>(sR1 + swz<DH>(r, c4)) =
-        *reinterpret_cast<const f32x4*>(p.dw + ch * MAT + 4 * x);
     *reinterpret_cast<f32x4*>(sR2 + swz<DH>(r, c4)) =
         *reinterpret_cast<const f32x4*>(p.bw + ch * MAT + 4 * x);
   }
@@ -703,7 +713,7 @@ __device__ __forceinline__ float gate_log2(float x, float lam) {
   return -lam * (fmaxf(x, 0.0f) * LOG2E + log2_hw(1.0f + t));
 }
 
-// ------------------------------------------------------------ 6. decay-weighted sums and the chain
+// ------------------------------------------------------------ 5. decay-weighted sums and the chain
 // One workgroup of 8 waves per (chunk, head).
 //
 // Prep (wave w: rows 8w..8w+7, lane channels 2l, 2l+1): the norms'
@@ -1197,7 +1207,7 @@ __global__ __launch_bounds__(512) void kda_bwd_gate_kernel(BwdArgs p) {
   }
 }
 
-// ------------------------------------------------------------ 7. parameter gradients
+// ------------------------------------------------------------ 6. parameter gradients
 // dt_bias and A_log gradients of head h: per-chunk partials summed in chunk
 // order (FP32, deterministic).
 __global__ __launch_bounds__(DH) void kda_bwd_param_kernel(BwdArgs p) {

@@ -49,6 +49,7 @@
 
 #include "kda_common.hpp"
 #include "kda_intra.hpp"
+#include "kda_scan.hpp"
 
 namespace kda {
 
@@ -452,6 +453,30 @@ __device__ __forceinline__ f32x4 mma16_tn_swz(const float* At, int m0, const flo
   return c;
 }
 
+// bf16 slab rows of 32 values (64 B) whose 16-byte chunks are XOR-swizzled
+// by row, so that the 16-byte operand reads of 8 consecutive lanes (rows
+// r..r+7, one chunk) hit distinct banks.
+__device__ __forceinline__ int sw32(int r, int k) {
+  return r * 32 + ((((k >> 3) ^ (r >> 2)) & 3) << 3) + (k & 7);
+}
+// C += A B over 32 contracted values, A exact in bf16 (one piece), B as its
+// three pieces (smallest terms first)
+__device__ __forceinline__ f32x4 mma_x3(const bf16x8& a, const bf16x8 (&b)[3], f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[2], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[1], c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[0], c, 0, 0, 0);
+}
+// C += A B over 32 contracted values from the pieces of both (the six terms
+// of order >= 2^-16, smallest first; see the bf16x6 note of the state pass)
+__device__ __forceinline__ f32x4 mma_x6_16(const bf16x8 (&a)[3], const bf16x8 (&b)[3], f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], b[0], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b[1], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[2], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b[0], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[1], c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[0], c, 0, 0, 0);
+}
+
 template <typename TA, typename TG, typename TR>
 __global__ __launch_bounds__(256, 2) void kda_bwd_prod_kernel(BwdArgs p) {
   constexpr int LS = 36;
@@ -484,82 +509,191 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_prod_kernel(BwdArgs p) {
 #pragma unroll
   for (int x = 0; x < 4; ++x) ap[x] = f32x4{0, 0, 0, 0};
   float gacc = 0.0f;
-  // slab sl + 1 is loaded into registers while slab sl is multiplied; dout
-  // stays in its own dtype (raw 16 or 32 bytes) until it is written to LDS
-  constexpr int OW = sizeof(TG) == 2 ? 1 : 2;
-  f32x4 rO[OW];
-  f32x4 rD[2], rDD[2], rS0[4], rDS[4];
-  auto fetch = [&](int sl) {
-    const int v0 = 32 * sl;
-    const int r = tid >> 2, j8 = 8 * (tid & 3);
-    const f32x4* src = reinterpret_cast<const f32x4*>(gO + ((size_t)(t0 + (r < len ? r : 0)) * p.H + h) * DH + v0 + j8);
-#pragma unroll
-    for (int u = 0; u < OW; ++u) rO[u] = r < len ? src[u] : f32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int x = tid + 256 * u, rr = x >> 3, j4 = 4 * (x & 7);
-      rD[u] = *reinterpret_cast<const f32x4*>(p.dmat + ch * MAT + rr * DH + v0 + j4);
-      rDD[u] = *reinterpret_cast<const f32x4*>(p.ddmat + ch * MAT + rr * DH + v0 + j4);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int x = tid + 256 * u, i = x >> 3, j4 = 4 * (x & 7);
-      rS0[u] = *reinterpret_cast<const f32x4*>(p.s0 + ch * STM + i * DH + v0 + j4);
-      rDS[u] = *reinterpret_cast<const f32x4*>(p.dsn + ch * STM + i * DH + v0 + j4);
-    }
-  };
-  auto stage = [&]() {
-    const int r = tid >> 2, j8 = 8 * (tid & 3);
-    float o[8];
-    load8_scaled(reinterpret_cast<const TG*>(rO), p.scale, o);  // from registers
-    store4(sO + r * LS + j8, f32x4{o[0], o[1], o[2], o[3]});
-    store4(sO + r * LS + j8 + 4, f32x4{o[4], o[5], o[6], o[7]});
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int x = tid + 256 * u, rr = x >> 3, j4 = 4 * (x & 7);
-      store4(sDm + rr * LS + j4, rD[u]);
-      store4(sDD + rr * LS + j4, rDD[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int x = tid + 256 * u, i = x >> 3, j4 = 4 * (x & 7);
-      store4(sS0 + i * LS + j4, rS0[u]);
-      store4(sDS + i * LS + j4, rDS[u]);
-    }
-  };
-  // T and dD for (b), loaded during the last slab
+  // T and dD for (b)
   f32x4 rT[4], rDf[8];
-  fetch(0);
-  stage();
-  __syncthreads();
-#pragma unroll
-  for (int sl = 0; sl < 4; ++sl) {
-    if (sl < 3) {
-      fetch(sl + 1);
-    } else {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) rT[u] = *reinterpret_cast<const f32x4*>(p.tmat + ch * SQM + 4 * (tid + 256 * u));
-#pragma unroll
-      for (int u = 0; u < 8; ++u) rDf[u] = *reinterpret_cast<const f32x4*>(p.ddmat + ch * MAT + 4 * (tid + 256 * u));
-    }
-#pragma unroll
-    for (int cb = 0; cb < 8; ++cb) {
-      aq[cb] = mma16_rows<float, 32>(sO + 16 * w * LS, LS, sS0 + 16 * cb * LS, LS, aq[cb], l);
-      ak[cb] = mma16_rows<float, 32>(sDm + 16 * w * LS, LS, sDS + 16 * cb * LS, LS, ak[cb], l);
-      aw[cb] = mma16_rows<float, 32>(sDD + 16 * w * LS, LS, sS0 + 16 * cb * LS, LS, aw[cb], l);
-    }
-#pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
-      ap[ib] = mma16_rows<float, 32>(sO + 16 * w * LS, LS, sDm + 16 * ib * LS, LS, ap[ib], l);
-    if (tid < DH) {
-#pragma unroll 8
-      for (int j = 0; j < 32; ++j) gacc = fmaf(sDS[tid * LS + j], sS0[tid * LS + j], gacc);
-    }
+  if constexpr (sizeof(TG) == 4) {
+    // FP32 dout: FP32 products over FP32 slabs; T and dD are loaded during
+    // the last slab
+    // slab sl + 1 is loaded into registers while slab sl is multiplied; dout
+    // stays in its own dtype (raw 16 or 32 bytes) until it is written to LDS
+    constexpr int OW = sizeof(TG) == 2 ? 1 : 2;
+    f32x4 rO[OW];
+    f32x4 rD[2], rDD[2], rS0[4], rDS[4];
+    auto fetch = [&](int sl) {
+      const int v0 = 32 * sl;
+      const int r = tid >> 2, j8 = 8 * (tid & 3);
+      const f32x4* src = reinterpret_cast<const f32x4*>(gO + ((size_t)(t0 + (r < len ? r : 0)) * p.H + h) * DH + v0 + j8);
+  #pragma unroll
+      for (int u = 0; u < OW; ++u) rO[u] = r < len ? src[u] : f32x4{0, 0, 0, 0};
+  #pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int x = tid + 256 * u, rr = x >> 3, j4 = 4 * (x & 7);
+        rD[u] = *reinterpret_cast<const f32x4*>(p.dmat + ch * MAT + rr * DH + v0 + j4);
+        rDD[u] = *reinterpret_cast<const f32x4*>(p.ddmat + ch * MAT + rr * DH + v0 + j4);
+      }
+  #pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int x = tid + 256 * u, i = x >> 3, j4 = 4 * (x & 7);
+        rS0[u] = *reinterpret_cast<const f32x4*>(p.s0 + ch * STM + i * DH + v0 + j4);
+        rDS[u] = *reinterpret_cast<const f32x4*>(p.dsn + ch * STM + i * DH + v0 + j4);
+      }
+    };
+    auto stage = [&]() {
+      const int r = tid >> 2, j8 = 8 * (tid & 3);
+      float o[8];
+      load8_scaled(reinterpret_cast<const TG*>(rO), p.scale, o);  // from registers
+      store4(sO + r * LS + j8, f32x4{o[0], o[1], o[2], o[3]});
+      store4(sO + r * LS + j8 + 4, f32x4{o[4], o[5], o[6], o[7]});
+  #pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int x = tid + 256 * u, rr = x >> 3, j4 = 4 * (x & 7);
+        store4(sDm + rr * LS + j4, rD[u]);
+        store4(sDD + rr * LS + j4, rDD[u]);
+      }
+  #pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int x = tid + 256 * u, i = x >> 3, j4 = 4 * (x & 7);
+        store4(sS0 + i * LS + j4, rS0[u]);
+        store4(sDS + i * LS + j4, rDS[u]);
+      }
+    };
+    fetch(0);
+    stage();
     __syncthreads();
-    if (sl < 3) {
-      stage();
+  #pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      if (sl < 3) {
+        fetch(sl + 1);
+      } else {
+  #pragma unroll
+        for (int u = 0; u < 4; ++u) rT[u] = *reinterpret_cast<const f32x4*>(p.tmat + ch * SQM + 4 * (tid + 256 * u));
+  #pragma unroll
+        for (int u = 0; u < 8; ++u) rDf[u] = *reinterpret_cast<const f32x4*>(p.ddmat + ch * MAT + 4 * (tid + 256 * u));
+      }
+  #pragma unroll
+      for (int cb = 0; cb < 8; ++cb) {
+        aq[cb] = mma16_rows<float, 32>(sO + 16 * w * LS, LS, sS0 + 16 * cb * LS, LS, aq[cb], l);
+        ak[cb] = mma16_rows<float, 32>(sDm + 16 * w * LS, LS, sDS + 16 * cb * LS, LS, ak[cb], l);
+        aw[cb] = mma16_rows<float, 32>(sDD + 16 * w * LS, LS, sS0 + 16 * cb * LS, LS, aw[cb], l);
+      }
+  #pragma unroll
+      for (int ib = 0; ib < 4; ++ib)
+        ap[ib] = mma16_rows<float, 32>(sO + 16 * w * LS, LS, sDm + 16 * ib * LS, LS, ap[ib], l);
+      if (tid < DH) {
+  #pragma unroll 8
+        for (int j = 0; j < 32; ++j) gacc = fmaf(sDS[tid * LS + j], sS0[tid * LS + j], gacc);
+      }
       __syncthreads();
+      if (sl < 3) {
+        stage();
+        __syncthreads();
+      }
     }
+    if (tid < DH) p.dgam[ch * DH + tid] = gacc;
+  } else {
+    // bf16 dout: dO is exact as one bf16 piece (its products take three
+    // terms; the scale is applied to the results), D, dD, S0 and dSn are split
+    // into three pieces once, as they are staged; slab rows of 32 values
+    bf16* const pO = reinterpret_cast<bf16*>(smem);  // [64][32]
+    bf16* const pD = pO + CHUNK * 32;                 // 3 planes [64][32]
+    bf16* const pDD = pD + 3 * CHUNK * 32;            // 3 planes [64][32]
+    bf16* const pS = pDD + 3 * CHUNK * 32;            // 3 planes [128][32]
+    bf16* const pDS = pS + 3 * DH * 32;               // 3 planes [128][32]
+    constexpr int PR = CHUNK * 32, PK = DH * 32;      // plane strides
+    static_assert((7 * CHUNK * 32 + 6 * DH * 32) * 2 <= (SQM + 2 * MAT) * 4, "pieces fit the block");
+    f32x4 rO;  // 8 raw bf16 of dout
+    f32x4 rD[2], rDD[2], rS0[4], rDS[4];
+    float gq[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // dGam partials of rows (tid + 256 u) / 8
+    auto fetch = [&](int sl) {
+      const int v0 = 32 * sl;
+      const int r = tid >> 2, j8 = 8 * (tid & 3);
+      const f32x4* src = reinterpret_cast<const f32x4*>(gO + ((size_t)(t0 + (r < len ? r : 0)) * p.H + h) * DH + v0 + j8);
+      rO = r < len ? src[0] : f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int x = tid + 256 * u, rr = x >> 3, j4 = 4 * (x & 7);
+        rD[u] = *reinterpret_cast<const f32x4*>(p.dmat + ch * MAT + rr * DH + v0 + j4);
+        rDD[u] = *reinterpret_cast<const f32x4*>(p.ddmat + ch * MAT + rr * DH + v0 + j4);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int x = tid + 256 * u, i = x >> 3, j4 = 4 * (x & 7);
+        rS0[u] = *reinterpret_cast<const f32x4*>(p.s0 + ch * STM + i * DH + v0 + j4);
+        rDS[u] = *reinterpret_cast<const f32x4*>(p.dsn + ch * STM + i * DH + v0 + j4);
+      }
+    };
+    auto stage = [&]() {
+      const int r = tid >> 2, j8 = 8 * (tid & 3);
+      *reinterpret_cast<f32x4*>(pO + sw32(r, j8)) = rO;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int x = tid + 256 * u, rr = x >> 3, j4 = 4 * (x & 7);
+        store_pieces4(pD + sw32(rr, j4), PR, rD[u]);
+        store_pieces4(pDD + sw32(rr, j4), PR, rDD[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int x = tid + 256 * u, i = x >> 3, j4 = 4 * (x & 7);
+        store_pieces4(pS + sw32(i, j4), PK, rS0[u]);
+        store_pieces4(pDS + sw32(i, j4), PK, rDS[u]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gq[u] = fmaf(rDS[u][e], rS0[u][e], gq[u]);
+      }
+    };
+    // the three pieces of row `row` of a slab, this lane's 8 values
+    auto pieces = [&](const bf16* base, int stride, int row, bf16x8 (&o)[3]) {
+      const int off = sw32(row, 8 * (l >> 4));
+#pragma unroll
+      for (int q = 0; q < 3; ++q) o[q] = *reinterpret_cast<const bf16x8*>(base + q * stride + off);
+    };
+    fetch(0);
+    stage();
+    __syncthreads();
+    for (int sl = 0; sl < 4; ++sl) {
+      if (sl < 3) fetch(sl + 1);
+      const int ra = 16 * w + (l & 15);
+      const bf16x8 aO = *reinterpret_cast<const bf16x8*>(pO + sw32(ra, 8 * (l >> 4)));
+      bf16x8 aD[3], aDD[3];
+      pieces(pD, PR, ra, aD);
+      pieces(pDD, PR, ra, aDD);
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) {
+        bf16x8 bS[3], bDS[3];
+        pieces(pS, PK, 16 * cb + (l & 15), bS);
+        pieces(pDS, PK, 16 * cb + (l & 15), bDS);
+        aq[cb] = mma_x3(aO, bS, aq[cb]);
+        aw[cb] = mma_x6_16(aDD, bS, aw[cb]);
+        ak[cb] = mma_x6_16(aD, bDS, ak[cb]);
+      }
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) {
+        bf16x8 bD[3];
+        pieces(pD, PR, 16 * ib + (l & 15), bD);
+        ap[ib] = mma_x3(aO, bD, ap[ib]);
+      }
+      __syncthreads();
+      if (sl < 3) {
+        stage();
+        __syncthreads();
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < 8; ++x) aq[x] *= p.scale;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) ap[x] *= p.scale;
+    // dGam: the 8 lanes of a row sum their partials
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float v = gq[u];
+      v += __shfl_xor(v, 1, 64);
+      v += __shfl_xor(v, 2, 64);
+      v += __shfl_xor(v, 4, 64);
+      if ((tid & 7) == 0) p.dgam[ch * DH + ((tid + 256 * u) >> 3)] = v;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) rT[u] = *reinterpret_cast<const f32x4*>(p.tmat + ch * SQM + 4 * (tid + 256 * u));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) rDf[u] = *reinterpret_cast<const f32x4*>(p.ddmat + ch * MAT + 4 * (tid + 256 * u));
   }
 #pragma unroll
   for (int cb = 0; cb < 8; ++cb) {
@@ -580,7 +714,6 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_prod_kernel(BwdArgs p) {
       p.dpm[ch * SQM + r * CHUNK + i] = i <= r ? ap[ib][e] : 0.0f;
     }
   }
-  if (tid < DH) p.dgam[ch * DH + tid] = gacc;
 
   // ---- (b) phase 1: T, dD, raw v (rows past the end zero); the slabs are done
   auto beta_of = [&](int i) {

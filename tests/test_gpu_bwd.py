@@ -144,6 +144,38 @@ def test_bwd_production_geometry_65_tokens():
     _check(_gpu_bwd(inp, dout, None, None, False), ref, TOL_BF16, "H64 bf16-grad")
 
 
+def test_bwd_bf16_dout_split_products_match_fp32_dout():
+    """With bf16 dout the value products run on bf16 matrix cores from split
+    operands (dout exact as one bf16 piece, D, dD, S0, dSn as three); with
+    FP32 dout the same products run in FP32.  On one bf16-exact dout the two
+    paths agree to FP32 accuracy: the FP32 outputs (dA_log, dt_bias, dS_init)
+    to 1e-5 relative, and each bf16 gradient is within one bf16 rounding step
+    (2^-8, relative L2) of the FP32 path's gradient rounded to bf16.  (df is
+    a running sum over the chunk, so where it nearly cancels, differences of
+    FP32 size in larger terms flip its bf16 rounding; dA_log and dt_bias,
+    which sum df's FP32 values, agree to ~3e-6.)  Against the oracle the
+    split path's FP32 outputs meet the FP32 bars and its bf16 gradients the
+    pages' BF16 budget."""
+    inp, dout, init, dfin = _case([300, 1, 0, 64, 130, 65], 3, "bf16", seed=13, grad_fp32=False)
+    got16 = _gpu_bwd(inp, dout, init, dfin, False)
+    got32 = _gpu_bwd(inp, dout, init, dfin, True)
+    ref = _oracle_bwd(inp, dout, init, dfin)
+    for k in ("dinit",) + PARAMS:
+        e_ref = U.rel_l2(got16[k], ref[k])
+        e_fp32 = U.rel_l2(got16[k], got32[k])
+        print("split", k, f"oracle {e_ref:.2e} fp32-path {e_fp32:.2e}", flush=True)
+        assert e_ref < (TOL_PARAM if k in PARAMS else TOL_FP32), (k, e_ref)
+        assert e_fp32 < 1e-5, (k, e_fp32)
+    for k in ("dq", "dk", "dv", "df", "db"):
+        b = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(got32[k].astype(np.float32)))
+        e_path = U.rel_l2(got16[k], b)
+        e_ref = U.rel_l2(got16[k], ref[k])
+        print("split", k, f"equal {np.mean(got16[k] == b):.6f} vs fp32 path {e_path:.2e} "
+              f"oracle {e_ref:.2e}", flush=True)
+        assert e_path < 2.0 ** -8, (k, e_path)
+        assert e_ref < TOL_BF16, (k, e_ref)
+
+
 def test_bwd_planted_scale_error_fails():
     """The pages' negative control: a 25 % scaling of one gradient (in the
     oracle) is far outside the bar the GPU result meets."""

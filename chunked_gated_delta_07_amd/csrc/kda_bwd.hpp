@@ -49,7 +49,6 @@
 
 #include "kda_common.hpp"
 #include "kda_intra.hpp"
-#include "kda_scan.hpp"
 
 namespace kda {
 
@@ -459,24 +458,6 @@ __device__ __forceinline__ f32x4 mma16_tn_swz(const float* At, int m0, const flo
 __device__ __forceinline__ int sw32(int r, int k) {
   return r * 32 + ((((k >> 3) ^ (r >> 2)) & 3) << 3) + (k & 7);
 }
-// C += A B over 32 contracted values, A exact in bf16 (one piece), B as its
-// three pieces (smallest terms first)
-__device__ __forceinline__ f32x4 mma_x3(const bf16x8& a, const bf16x8 (&b)[3], f32x4 c) {
-  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[2], c, 0, 0, 0);
-  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[1], c, 0, 0, 0);
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[0], c, 0, 0, 0);
-}
-// C += A B over 32 contracted values from the pieces of both (the six terms
-// of order >= 2^-16, smallest first; see the bf16x6 note of the state pass)
-__device__ __forceinline__ f32x4 mma_x6_16(const bf16x8 (&a)[3], const bf16x8 (&b)[3], f32x4 c) {
-  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], b[0], c, 0, 0, 0);
-  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b[1], c, 0, 0, 0);
-  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[2], c, 0, 0, 0);
-  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b[0], c, 0, 0, 0);
-  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[1], c, 0, 0, 0);
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[0], c, 0, 0, 0);
-}
-
 template <typename TA, typename TG, typename TR>
 __global__ __launch_bounds__(256, 2) void kda_bwd_prod_kernel(BwdArgs p) {
   constexpr int LS = 36;

@@ -192,4 +192,73 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+
+// ---------------------------------------------------------------- split products
+// FP32 operands on bf16 matrix cores.  Each FP32 value x is split into three
+// bf16 pieces x = h + m + l: h is x rounded to nearest even, m the same for
+// x - h, l for x - h - m (both remainders are exact in FP32, and for a normal
+// x the three pieces hold all 24 significand bits, so the split is exact).  A
+// product x y is the sum of the six piece products of order >= 2^-16,
+//   h h' + (h m' + m h') + (h l' + m m' + l h'),
+// the "bf16x6" scheme of Henry, Tang and Heinecke ("Leveraging the bfloat16
+// artificial intelligence datatype for higher-precision computations", ARITH
+// 2019).  The omitted terms m l' + l m' + l l' stay below 2^-23 |x y| and the
+// matrix core accumulates in FP32, so a contraction agrees with an FP32 one to
+// within FP32 rounding.  Cost per 16 contracted values of a 32x32 tile: six
+// v_mfma_f32_32x32x16_bf16 (32 cycles each) instead of eight
+// v_mfma_f32_32x32x2f32 (64 cycles each).  A factor exact in bf16 (one piece)
+// needs only the three products with the other factor's pieces.
+typedef unsigned u32;
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// the two bf16 of a packed pair as FP32 (exact)
+__device__ __forceinline__ f32x2 bf16x2_as_f32(u32 v) {
+  return f32x2{__builtin_bit_cast(float, v << 16), __builtin_bit_cast(float, v & 0xffff0000u)};
+}
+__device__ __forceinline__ u32 cvt_pair(f32x2 x) {
+  return __builtin_bit_cast(u32, __builtin_convertvector(x, bf16x2));  // RNE, one instruction
+}
+// pieces of two FP32 values, each piece packed as a bf16 pair
+struct Pieces2 { u32 h, m, l; };
+__device__ __forceinline__ Pieces2 split2(f32x2 x) {
+  Pieces2 o;
+  o.h = cvt_pair(x);
+  const f32x2 r = x - bf16x2_as_f32(o.h);
+  o.m = cvt_pair(r);
+  o.l = cvt_pair(r - bf16x2_as_f32(o.m));
+  return o;
+}
+// four FP32 values -> their pieces at p, p + stride, p + 2 stride
+__device__ __forceinline__ void store_pieces4(bf16* p, int stride, const f32x4& v) {
+  const Pieces2 p0 = split2(f32x2{v[0], v[1]}), p1 = split2(f32x2{v[2], v[3]});
+  *reinterpret_cast<u32x2*>(p) = u32x2{p0.h, p1.h};
+  *reinterpret_cast<u32x2*>(p + stride) = u32x2{p0.m, p1.m};
+  *reinterpret_cast<u32x2*>(p + 2 * stride) = u32x2{p0.l, p1.l};
+}
+// C += A B over 32 contracted values, A exact in bf16 (one piece), B as its
+// three pieces (smallest terms first)
+__device__ __forceinline__ f32x4 mma_x3(const bf16x8& a, const bf16x8 (&b)[3], f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[2], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[1], c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[0], c, 0, 0, 0);
+}
+// C += A B over 32 contracted values from the pieces of both (the six terms
+// of order >= 2^-16, smallest first)
+__device__ __forceinline__ f32x4 mma_x6_16(const bf16x8 (&a)[3], const bf16x8 (&b)[3], f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], b[0], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b[1], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[2], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b[0], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[1], c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[0], c, 0, 0, 0);
+}
+
+// C += A B over 32 contracted values, A as its three pieces, B exact in bf16
+__device__ __forceinline__ f32x4 mma_x3b(const bf16x8 (&a)[3], const bf16x8& b, f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], b, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b, c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b, c, 0, 0, 0);
+}
+
 }  // namespace kda

@@ -1130,91 +1130,216 @@ __device__ __forceinline__ void intra_chunk(const IntraArgs& p, int chunk, int h
   }
 
   // ------------------------------------------------------ phase 4: W and U
-  MT* sTs = reinterpret_cast<MT*>(sU + L::O_TS);  // scaled T, row-major [64][TL]
-  MT* sXt = reinterpret_cast<MT*>(sU + L::O_XT);  // transposed operand [128 / NP][TL]
-  // W = T (Diag(beta rk) (k * E)),  U = T (Diag(beta) v): the row scales go
-  // on the right-hand operands, T is converted once (FP32: T is used as is).
-  // (T is lower triangular: entries above the 16x16 block diagonal were not
-  // written and read as zero here)
-  for (int x = tid; x < CHUNK * CHUNK; x += 256) {
-    const int r = x >> 6, i = x & 63;
-    const float tv = (i >> 4) > (r >> 4) ? 0.0f : sT[r * AL + i];
-    if constexpr (!L::TS_ALIAS) sTs[r * TL + i] = from_f32<MT>(tv);
-    if constexpr (BWD) p.tmat[((size_t)chunk * H + h) * CHUNK * CHUNK + x] = tv;
-  }
+  if constexpr (sizeof(MT) == 4) {
+    // FP32 operands on bf16 matrix cores: W = T' (Diag(rk) (k * E)) and
+    // U = T' v with T' = T Diag(beta), each product from three-piece splits
+    // (bf16x6; v from bf16 activations is exact in one piece and takes three
+    // terms).  T' and one 64-channel half of the right-hand operand,
+    // transposed to [channel][token], are bf16 planes of 64-element rows
+    // whose 16-byte chunks are XOR-swizzled by row.
+    constexpr int PP = CHUNK * CHUNK;                         // plane stride
+    bf16* pX = reinterpret_cast<bf16*>(sU);                   // right-hand planes
+    bf16* pT = reinterpret_cast<bf16*>(sU + 3 * PP * 2);      // T' planes
+    static_assert(6 * PP * 2 <= L::U_BYTES, "W/U planes fit the union region");
+    static_assert(CHUNK * AL * 4 <= 3 * PP * 2, "the FP32 T lies below the T' planes");
+    auto sw64 = [](int r, int k) { return r * 64 + ((((k >> 3) ^ r) & 7) << 3) + (k & 7); };
+    // (T is lower triangular, its blocks above the 16x16 diagonal zeroed)
+    for (int x4 = tid; x4 < PP / 4; x4 += 256) {
+      const int r = x4 >> 4, i4 = 4 * (x4 & 15);
+      const f32x4 tv = *reinterpret_cast<const f32x4*>(sT + r * AL + i4);
+      if constexpr (BWD)
+        *reinterpret_cast<f32x4*>(p.tmat + ((size_t)chunk * H + h) * PP + r * CHUNK + i4) = tv;
+      f32x4 tb;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const float bj = sBeta[16 * w + j];
-    v0[j] *= bj; v1[j] *= bj;
-  }
-  // Each product in NP passes over channel halves (NP = 1 for bf16): the
-  // transposed operand holds 128 / NP channels; lanes whose channels fall in
-  // the pass form and write them.
-  constexpr int NP = L::NP, CB = 8 / NP;  // channel blocks of 16 per pass
-#pragma unroll 1
-  for (int ps = 0; ps < NP; ++ps) {
-    const int cl = c0 - 64 * ps;
-    if (NP == 1 || (l >> 5) == ps) {
-      float kg0[16], kg1[16];
-      float e0 = pb[0], e1 = pb[1];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        e0 *= aa[j][0]; e1 *= aa[j][1];
-        const float sc = sBeta[16 * w + j] * sRk[16 * w + j];
-        kg0[j] = ka[j][0] * e0 * sc; kg1[j] = ka[j][1] * e1 * sc;
-      }
-      if constexpr (BWD) {
-        float* gb = p.bw + ((size_t)chunk * H + h) * CHUNK * DH;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) store2(gb + (16 * w + j) * DH + c0, kg0[j], kg1[j]);
-      }
-#pragma unroll
-      for (int j = 0; j < 16; j += 4) {
-        store4(sXt + cl * TL + 16 * w + j, f32x4{kg0[j], kg0[j + 1], kg0[j + 2], kg0[j + 3]});
-        store4(sXt + (cl + 1) * TL + 16 * w + j, f32x4{kg1[j], kg1[j + 1], kg1[j + 2], kg1[j + 3]});
-      }
+      for (int e = 0; e < 4; ++e) tb[e] = tv[e] * sBeta[i4 + e];
+      store_pieces4(pT + sw64(r, i4), PP, tb);
     }
-    __syncthreads();
-    // output tiles of W^T: (channel block mt) x (token block nt 0..3); 8 / NP per wave
-#pragma unroll
-    for (int t = 0; t < 2 * CB / 2; ++t) {
-      const int tile = CB * w + t, mtl = tile >> 2, nt = tile & 3, mt = CB * ps + mtl;
+    __syncthreads();  // the FP32 T is no longer read; the right-hand planes may overwrite it
+    // one product: tiles of 16 x 16 over the 64 tokens (two steps of 32),
+    // rows ra of the planes at A, rows rb at B; B in one piece when exact
+    auto tile = [&](const bf16* A, int ra, const bf16* B, int rb, bool b_exact) {
       f32x4 c = {0, 0, 0, 0};
-      c = mma16_rows<MT, CHUNK>(sXt + 16 * mtl * TL, TL, sTs + 16 * nt * TL, TL, c, l);
-      // c[e] = W^T[16mt + 4(l/16) + e][16nt + l%16] = W[tok][ch..ch+3]
-      const int tok = 16 * nt + (l & 15), ch = 16 * mt + 4 * (l >> 4);
-      store4(gW + LY::a(tok, ch), c);
-      if constexpr (BWD) {
-        float* gwt = p.wt + ((size_t)chunk * H + h) * DH * CHUNK;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) gwt[(ch + e) * CHUNK + tok] = c[e];
+      for (int st = 0; st < 2; ++st) {
+        const int k = 32 * st + 8 * (l >> 4);
+        bf16x8 a[3], bb[3];
+#pragma unroll
+        for (int q = 0; q < 3; ++q) a[q] = *reinterpret_cast<const bf16x8*>(A + q * PP + sw64(ra, k));
+        bb[0] = *reinterpret_cast<const bf16x8*>(B + sw64(rb, k));
+        if (b_exact) {
+          c = mma_x3b(a, bb[0], c);
+        } else {
+          bb[1] = *reinterpret_cast<const bf16x8*>(B + PP + sw64(rb, k));
+          bb[2] = *reinterpret_cast<const bf16x8*>(B + 2 * PP + sw64(rb, k));
+          c = mma_x6_16(a, bb, c);
+        }
       }
-    }
-    __syncthreads();
-  }
-  // U = T (Diag(beta) v)
+      return c;
+    };
+    // W, per channel half: the lanes owning the half store (rk k E) transposed
 #pragma unroll 1
-  for (int ps = 0; ps < NP; ++ps) {
-    const int cl = c0 - 64 * ps;
-    if (NP == 1 || (l >> 5) == ps) {
+    for (int ps = 0; ps < 2; ++ps) {
+      const int cl = c0 - 64 * ps;
+      if ((l >> 5) == ps) {
+        float kg0[16], kg1[16];
+        float e0 = pb[0], e1 = pb[1];
 #pragma unroll
-      for (int j = 0; j < 16; j += 4) {
-        store4(sXt + cl * TL + 16 * w + j, f32x4{v0[j], v0[j + 1], v0[j + 2], v0[j + 3]});
-        store4(sXt + (cl + 1) * TL + 16 * w + j, f32x4{v1[j], v1[j + 1], v1[j + 2], v1[j + 3]});
+        for (int j = 0; j < 16; ++j) {
+          e0 *= aa[j][0]; e1 *= aa[j][1];
+          const float rk = sRk[16 * w + j];
+          kg0[j] = ka[j][0] * e0 * rk; kg1[j] = ka[j][1] * e1 * rk;
+        }
+        if constexpr (BWD) {
+          float* gb = p.bw + ((size_t)chunk * H + h) * CHUNK * DH;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const float bj = sBeta[16 * w + j];
+            store2(gb + (16 * w + j) * DH + c0, kg0[j] * bj, kg1[j] * bj);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 16; j += 4) {
+          store_pieces4(pX + sw64(cl, 16 * w + j), PP, f32x4{kg0[j], kg0[j + 1], kg0[j + 2], kg0[j + 3]});
+          store_pieces4(pX + sw64(cl + 1, 16 * w + j), PP, f32x4{kg1[j], kg1[j + 1], kg1[j + 2], kg1[j + 3]});
+        }
       }
-    }
-    __syncthreads();
-    // output tiles of U: (token block mt 0..3) x (value block nt); 8 / NP per wave
+      __syncthreads();
+      // W^T tiles (channel block mtl of the half, token block nt), four per wave
 #pragma unroll
-    for (int t = 0; t < CB; ++t) {
-      const int tile = CB * w + t, mt = tile / CB, ntl = tile % CB, nt = CB * ps + ntl;
-      f32x4 c = {0, 0, 0, 0};
-      c = mma16_rows<MT, CHUNK>(sTs + 16 * mt * TL, TL, sXt + 16 * ntl * TL, TL, c, l);
-      // c[e] = U[16mt + 4(l/16) + e][16nt + l%16]: four consecutive tokens
-      const int dv = 16 * nt + (l & 15), tok = 16 * mt + 4 * (l >> 4);
-      store4(gUT + LY::u(tok, dv), c);
+      for (int t = 0; t < 4; ++t) {
+        const int tl = 4 * w + t, mtl = tl >> 2, nt = tl & 3, mt = 4 * ps + mtl;
+        const f32x4 c = tile(pX, 16 * mtl + (l & 15), pT, 16 * nt + (l & 15), false);
+        // c[e] = W^T[16mt + 4(l/16) + e][16nt + l%16] = W[tok][ch..ch+3]
+        const int tok = 16 * nt + (l & 15), ch = 16 * mt + 4 * (l >> 4);
+        store4(gW + LY::a(tok, ch), c);
+        if constexpr (BWD) {
+          float* gwt = p.wt + ((size_t)chunk * H + h) * DH * CHUNK;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) gwt[(ch + e) * CHUNK + tok] = c[e];
+        }
+      }
+      __syncthreads();
     }
-    if (ps + 1 < NP) __syncthreads();
+    // U = T' v, per value half (beta is in T')
+    constexpr bool V_EXACT = sizeof(TA) == 2;  // v from bf16 activations (or their convolution)
+#pragma unroll 1
+    for (int ps = 0; ps < 2; ++ps) {
+      const int cl = c0 - 64 * ps;
+      if ((l >> 5) == ps) {
+#pragma unroll
+        for (int j = 0; j < 16; j += 4) {
+          const f32x4 a0 = f32x4{v0[j], v0[j + 1], v0[j + 2], v0[j + 3]};
+          const f32x4 a1 = f32x4{v1[j], v1[j + 1], v1[j + 2], v1[j + 3]};
+          if constexpr (V_EXACT) {
+            *reinterpret_cast<u32x2*>(pX + sw64(cl, 16 * w + j)) =
+                u32x2{cvt_pair(f32x2{a0[0], a0[1]}), cvt_pair(f32x2{a0[2], a0[3]})};
+            *reinterpret_cast<u32x2*>(pX + sw64(cl + 1, 16 * w + j)) =
+                u32x2{cvt_pair(f32x2{a1[0], a1[1]}), cvt_pair(f32x2{a1[2], a1[3]})};
+          } else {
+            store_pieces4(pX + sw64(cl, 16 * w + j), PP, a0);
+            store_pieces4(pX + sw64(cl + 1, 16 * w + j), PP, a1);
+          }
+        }
+      }
+      __syncthreads();
+      // U tiles (token block w, value block t of the half)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int nt = 4 * ps + t;
+        const f32x4 c = tile(pT, 16 * w + (l & 15), pX, 16 * t + (l & 15), V_EXACT);
+        // c[e] = U[16w + 4(l/16) + e][16nt + l%16]: four consecutive tokens
+        const int dv = 16 * nt + (l & 15), tok = 16 * w + 4 * (l >> 4);
+        store4(gUT + LY::u(tok, dv), c);
+      }
+      if (ps == 0) __syncthreads();
+    }
+  } else {
+    MT* sTs = reinterpret_cast<MT*>(sU + L::O_TS);  // scaled T, row-major [64][TL]
+    MT* sXt = reinterpret_cast<MT*>(sU + L::O_XT);  // transposed operand [128 / NP][TL]
+    // W = T (Diag(beta rk) (k * E)),  U = T (Diag(beta) v): the row scales go
+    // on the right-hand operands, T is converted once (FP32: T is used as is).
+    // (T is lower triangular: entries above the 16x16 block diagonal were not
+    // written and read as zero here)
+    for (int x = tid; x < CHUNK * CHUNK; x += 256) {
+      const int r = x >> 6, i = x & 63;
+      const float tv = (i >> 4) > (r >> 4) ? 0.0f : sT[r * AL + i];
+      if constexpr (!L::TS_ALIAS) sTs[r * TL + i] = from_f32<MT>(tv);
+      if constexpr (BWD) p.tmat[((size_t)chunk * H + h) * CHUNK * CHUNK + x] = tv;
+    }
+  #pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float bj = sBeta[16 * w + j];
+      v0[j] *= bj; v1[j] *= bj;
+    }
+    // Each product in NP passes over channel halves (NP = 1 for bf16): the
+    // transposed operand holds 128 / NP channels; lanes whose channels fall in
+    // the pass form and write them.
+    constexpr int NP = L::NP, CB = 8 / NP;  // channel blocks of 16 per pass
+  #pragma unroll 1
+    for (int ps = 0; ps < NP; ++ps) {
+      const int cl = c0 - 64 * ps;
+      if (NP == 1 || (l >> 5) == ps) {
+        float kg0[16], kg1[16];
+        float e0 = pb[0], e1 = pb[1];
+  #pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          e0 *= aa[j][0]; e1 *= aa[j][1];
+          const float sc = sBeta[16 * w + j] * sRk[16 * w + j];
+          kg0[j] = ka[j][0] * e0 * sc; kg1[j] = ka[j][1] * e1 * sc;
+        }
+        if constexpr (BWD) {
+          float* gb = p.bw + ((size_t)chunk * H + h) * CHUNK * DH;
+  #pragma unroll
+          for (int j = 0; j < 16; ++j) store2(gb + (16 * w + j) * DH + c0, kg0[j], kg1[j]);
+        }
+  #pragma unroll
+        for (int j = 0; j < 16; j += 4) {
+          store4(sXt + cl * TL + 16 * w + j, f32x4{kg0[j], kg0[j + 1], kg0[j + 2], kg0[j + 3]});
+          store4(sXt + (cl + 1) * TL + 16 * w + j, f32x4{kg1[j], kg1[j + 1], kg1[j + 2], kg1[j + 3]});
+        }
+      }
+      __syncthreads();
+      // output tiles of W^T: (channel block mt) x (token block nt 0..3); 8 / NP per wave
+  #pragma unroll
+      for (int t = 0; t < 2 * CB / 2; ++t) {
+        const int tile = CB * w + t, mtl = tile >> 2, nt = tile & 3, mt = CB * ps + mtl;
+        f32x4 c = {0, 0, 0, 0};
+        c = mma16_rows<MT, CHUNK>(sXt + 16 * mtl * TL, TL, sTs + 16 * nt * TL, TL, c, l);
+        // c[e] = W^T[16mt + 4(l/16) + e][16nt + l%16] = W[tok][ch..ch+3]
+        const int tok = 16 * nt + (l & 15), ch = 16 * mt + 4 * (l >> 4);
+        store4(gW + LY::a(tok, ch), c);
+        if constexpr (BWD) {
+          float* gwt = p.wt + ((size_t)chunk * H + h) * DH * CHUNK;
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) gwt[(ch + e) * CHUNK + tok] = c[e];
+        }
+      }
+      __syncthreads();
+    }
+    // U = T (Diag(beta) v)
+  #pragma unroll 1
+    for (int ps = 0; ps < NP; ++ps) {
+      const int cl = c0 - 64 * ps;
+      if (NP == 1 || (l >> 5) == ps) {
+  #pragma unroll
+        for (int j = 0; j < 16; j += 4) {
+          store4(sXt + cl * TL + 16 * w + j, f32x4{v0[j], v0[j + 1], v0[j + 2], v0[j + 3]});
+          store4(sXt + (cl + 1) * TL + 16 * w + j, f32x4{v1[j], v1[j + 1], v1[j + 2], v1[j + 3]});
+        }
+      }
+      __syncthreads();
+      // output tiles of U: (token block mt 0..3) x (value block nt); 8 / NP per wave
+  #pragma unroll
+      for (int t = 0; t < CB; ++t) {
+        const int tile = CB * w + t, mt = tile / CB, ntl = tile % CB, nt = CB * ps + ntl;
+        f32x4 c = {0, 0, 0, 0};
+        c = mma16_rows<MT, CHUNK>(sTs + 16 * mt * TL, TL, sXt + 16 * ntl * TL, TL, c, l);
+        // c[e] = U[16mt + 4(l/16) + e][16nt + l%16]: four consecutive tokens
+        const int dv = 16 * nt + (l & 15), tok = 16 * mt + 4 * (l >> 4);
+        store4(gUT + LY::u(tok, dv), c);
+      }
+      if (ps + 1 < NP) __syncthreads();
+    }
   }
 }
 

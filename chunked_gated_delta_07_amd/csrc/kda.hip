@@ -69,6 +69,10 @@ __global__ __launch_bounds__(1024) void kda_chunk_table_kernel(const int32_t* __
   if (tid == 1023) cfirst[N] = part[1023];
 }
 
+// The backward's per-chunk kernels address a chunk's rows of a [T][H][128]
+// tensor with 32-bit offsets from the chunk's first token (up to 64 H 128).
+static inline bool bwd_heads_fit(int64_t H) { return H * DH * CHUNK <= (int64_t)INT32_MAX; }
+
 // A dispatch counts each grid dimension in work-items with a 32-bit field:
 // blocks x threads must stay below 2^32 in every dimension.
 static inline bool grid_fits(int64_t blocks, int64_t threads) {
@@ -794,7 +798,8 @@ extern "C" int kda_chunk_bwd(const void* q, const void* k, const void* v, const 
     if (!q || !k || !v || !f_raw || !b_raw || !A_log || !dt_bias || !cu_seqlens || !dout || !dq ||
         !dk || !dv || !df_raw || !db_raw || !workspace)
       return KDA_ERR_INVALID_ARG;
-    if (total_tokens > (int64_t)INT32_MAX / 64 || (int64_t)num_seqs * H > (int64_t)INT32_MAX / 64)
+    if (total_tokens > (int64_t)INT32_MAX / 64 || (int64_t)num_seqs * H > (int64_t)INT32_MAX / 64 ||
+        !kda::bwd_heads_fit(H))
       return KDA_ERR_UNSUPPORTED;
     // grids: (chunks x up to 512 threads, H) per chunk; (32 x 512, N H / 8) scans
     if (!kda::grid_fits(kda::max_chunks(total_tokens, num_seqs), 512) ||
@@ -852,7 +857,8 @@ extern "C" int kda_chunk_bwd_conv(const void* q, const void* k, const void* v, c
     if (!q || !k || !v || !f_raw || !b_raw || !A_log || !dt_bias || !cu_seqlens || !dout || !dq ||
         !dk || !dv || !df_raw || !db_raw || !workspace || !conv_weight)
       return KDA_ERR_INVALID_ARG;
-    if (total_tokens > (int64_t)INT32_MAX / 64 || (int64_t)num_seqs * H > (int64_t)INT32_MAX / 64)
+    if (total_tokens > (int64_t)INT32_MAX / 64 || (int64_t)num_seqs * H > (int64_t)INT32_MAX / 64 ||
+        !kda::bwd_heads_fit(H))
       return KDA_ERR_UNSUPPORTED;
     if (!kda::grid_fits(kda::max_chunks(total_tokens, num_seqs), 512) ||
         !kda::grid_fits(((int64_t)num_seqs * H + 7) / 8, 1))

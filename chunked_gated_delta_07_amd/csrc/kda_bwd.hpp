@@ -830,10 +830,12 @@ __device__ __forceinline__ float gate_log2(float x, float lam) {
 // ------------------------------------------------------------ 5. decay-weighted sums and the chain
 // One workgroup of 8 waves per (chunk, head).
 //
-// Prep (wave w: rows 8w..8w+7, lane channels 2l, 2l+1): the norms'
-// reciprocals, the gate in log2 units and beta; then G, the prefix of the gate
-// over the chunk's rows (128 channels x 4 segments of 16 rows).  dA and dP go
-// to LDS in both orientations.
+// Prep (wave w: rows 8w..8w+7, one row per 16 lanes, eight channels per
+// lane): the norms' reciprocals (sums over the row's 16 lanes by DPP), the
+// gate in log2 units and beta; then G, the prefix of the gate over the
+// chunk's rows (128 channels x 4 segments of 16 rows).  dA and dP go to LDS
+// in both orientations; q^ and k^ of the lane's own rows of the sums' layout
+// come from the raw inputs and the norms.
 //
 // Sums (wave w: channels 16w..16w+15; lane (n, g) = (l & 15, l >> 4) holds
 // channel 16w+n of its group's own rows 16R+4g+j, R, j = 0..3 -- the result

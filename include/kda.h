@@ -281,7 +281,8 @@ KDA_API size_t kda_chunk_bwd_workspace_bytes(int64_t total_tokens, int32_t num_s
  * (= dfinal_state, or zero) are written; the other pointers are not read.
  * No output may alias an input.  Asynchronous on `stream`, no allocation, no
  * host synchronisation.  Errors as for kda_chunk_fwd (dA_log and ddt_bias
- * are required). */
+ * are required); besides, H > 262143 gives KDA_ERR_UNSUPPORTED (the kernels
+ * address a chunk's 64 rows of an activation with 32-bit offsets). */
 KDA_API int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* f_raw,
                   const void* b_raw, const float* A_log, const float* dt_bias,
                   const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens, int32_t H,

@@ -121,6 +121,7 @@ def test_backward_argument_errors_before_launch():
     assert bw(T=-1) == kda.KDA_ERR_INVALID_ARG
     assert bw(mode=0x20) == kda.KDA_ERR_INVALID_ARG
     assert bw(d=64) == kda.KDA_ERR_UNSUPPORTED
+    assert bw(H=262144) == kda.KDA_ERR_UNSUPPORTED   # 32-bit row offsets: 64 x H x 128 < 2^31
     assert bw(ws=1) == kda.KDA_ERR_WORKSPACE
     assert bw(T=0, par=None) == kda.KDA_ERR_INVALID_ARG  # still required for an empty batch
     assert kda.bwd_workspace_bytes(0, 1, 64, 128, 1) == 0
@@ -153,6 +154,7 @@ def test_conv_backward_argument_errors_before_launch():
     assert bw(N=0) == kda.KDA_ERR_INVALID_ARG
     assert bw(mode=0x20) == kda.KDA_ERR_INVALID_ARG
     assert bw(d=64) == kda.KDA_ERR_UNSUPPORTED
+    assert bw(H=262144) == kda.KDA_ERR_UNSUPPORTED
     assert bw(ws=1) == kda.KDA_ERR_WORKSPACE
     n = (1 << 23) - 1
     assert bw(N=n, T=n, H=1, ws=1) == kda.KDA_ERR_WORKSPACE

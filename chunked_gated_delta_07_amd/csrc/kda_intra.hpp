@@ -227,6 +227,17 @@ __host__ __device__ constexpr int pair_u(int p) {
 }
 constexpr int NPAIR = 56;
 constexpr int NBATCH = 4;  // ceil(56 / 16)
+// Pairs (u, i), i < u, inside one 4-row group of a 16-row diagonal block,
+// ordered by group, then i, then u (six per group: (0,1) (0,2) (0,3) (1,2)
+// (1,3) (2,3) relative to the group's first row).
+__host__ __device__ constexpr int pair4_i(int p) {
+  return 4 * (p / 6) + (p % 6 < 3 ? 0 : p % 6 < 5 ? 1 : 2);
+}
+__host__ __device__ constexpr int pair4_u(int p) {
+  return 4 * (p / 6) + (p % 6 < 3 ? p % 6 + 1 : p % 6 < 5 ? p % 6 - 1 : 3);
+}
+constexpr int NPAIR4 = 24;
+constexpr int NBATCH4 = 2;  // ceil(24 / 16)
 
 template <typename MT> struct IntraLds {
   static constexpr int ROWL = sizeof(MT) == 2 ? 136 : 132;  // padded row of 128 channels
@@ -742,17 +753,71 @@ __device__ __forceinline__ void intra_chunk(const IntraArgs& p, int chunk, int h
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
       __builtin_amdgcn_wave_barrier();
     }
-    // Inside each 8-row half: pair vectors kd_(u,i)[c] = k_i[c] prod_{i<j<=u} a_j[c],
+    // Rows 4..7 x columns 0..3 and rows 12..15 x columns 8..11: factorised
+    // about rows 4 and 12 in the same way, both blocks from one tile: X8 rows
+    // 0..3 and 8..11 hold the column factors, rows 4..7 and 12..15 the row
+    // factors of k (then of q for P).
+    {
+      float ra0[8], ra1[8];
+  #pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int m = 8 * hf + 4;  // reference row
+        float x0 = 1.0f, x1 = 1.0f;
+  #pragma unroll
+        for (int j = m; j < m + 4; ++j) {
+          if (j > m) { x0 *= aa[j][0]; x1 *= aa[j][1]; }
+          ra0[4 * hf + j - m] = x0; ra1[4 * hf + j - m] = x1;
+          store2(pD + j * ROWL + c0, ka[j][0] * x0, ka[j][1] * x1);
+        }
+        float y0 = aa[m][0], y1 = aa[m][1];
+  #pragma unroll
+        for (int j = m - 1; j >= m - 4; --j) {
+          store2(pD + j * ROWL + c0, ka[j][0] * y0, ka[j][1] * y1);
+          y0 *= aa[j][0]; y1 *= aa[j][1];
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      f32x4 ca = {0, 0, 0, 0};
+      ca = mma16_rows<MT, DH>(pD, ROWL, pD, ROWL, ca, l);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+  #pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 8 * hf + 4 + j;
+          store2(pD + r * ROWL + c0, qa[r][0] * ra0[4 * hf + j], qa[r][1] * ra1[4 * hf + j]);
+        }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      f32x4 cp = {0, 0, 0, 0};
+      cp = mma16_rows<MT, DH>(pD, ROWL, pD, ROWL, cp, l);
+      const int n = l & 15, g = l >> 4;
+      if ((g == 1 && n < 4) || (g == 3 && n >= 8 && n < 12)) {
+        const int ri = 16 * w + n;
+        const float rki = sRk[ri];
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ru = 16 * w + 4 * g + e;
+          sA[ru * AL + ri] = sBeta[ru] * sRk[ru] * rki * ca[e];
+          sA[ri * AL + ru] = sRq[ru] * rki * cp[e];
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    }
+    // Inside each 4-row group: pair vectors kd_(u,i)[c] = k_i[c] prod_{i<j<=u} a_j[c],
     // 16 per batch; MFMA k.kd and q.kd; keep the (u, column) entry.
     {
       float d0 = 1.0f, d1 = 1.0f;
   #pragma unroll
-      for (int bt = 0; bt < NBATCH; ++bt) {
+      for (int bt = 0; bt < NBATCH4; ++bt) {
   #pragma unroll
         for (int n = 0; n < 16; ++n) {
           const int pp = 16 * bt + n;
-          if (pp < NPAIR) {
-            const int i = pair_i(pp), u = pair_u(pp);
+          if (pp < NPAIR4) {
+            const int i = pair4_i(pp), u = pair4_u(pp);
             if (u == i + 1) { d0 = aa[u][0]; d1 = aa[u][1]; }
             else { d0 *= aa[u][0]; d1 *= aa[u][1]; }
             store2(pD + n * ROWL + c0, ka[i][0] * d0, ka[i][1] * d1);
@@ -767,8 +832,8 @@ __device__ __forceinline__ void intra_chunk(const IntraArgs& p, int chunk, int h
         cp = mma16_rows<MT, DH>(pQ, ROWL, pD, ROWL, cp, l);
         {
           const int n = l & 15, pp = 16 * bt + n;
-          if (pp < NPAIR) {
-            const int i = pair_i(pp), u = pair_u(pp);
+          if (pp < NPAIR4) {
+            const int i = pair4_i(pp), u = pair4_u(pp);
             const int m0 = 4 * (l >> 4);
             if (u >= m0 && u < m0 + 4) {
               const int e = u - m0;

@@ -260,7 +260,11 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_bwd_fscan_kernel(BwdArgs p) 
 // LDS (rows of K): P^T [64 r][64 i], Kb [64 r][128 c], Qt^T [128 i][64 r],
 // W^T [128][64], (scale dO)^T block [32 j][64 r], dS^T block [32][128],
 // dD^T [32][64], Gam.  Eight waves as in the forward scan: dD tiles one per
-// wave, dS0 tiles two per wave.
+// wave, dS0 tiles two per wave.  With bf16 dout the two products with dO run
+// on bf16 matrix cores: dO is exact as one bf16 piece (stored unscaled, as
+// bf16, in the dO block), P^T and Qt^T are split into three pieces as they
+// are read (three products per 32 contracted values, the scale applied to
+// the result); the products with dS and dD stay FP32.
 template <typename TG>
 __global__ __launch_bounds__(SCAN_THREADS) void kda_bwd_bscan_kernel(BwdArgs p) {
   constexpr int LL = SL_LONG, LS = SL_SHORT, NT = SCAN_THREADS;
@@ -268,7 +272,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_bwd_bscan_kernel(BwdArgs p) 
   __shared__ __attribute__((aligned(16))) float sKb[CHUNK * LL];
   __shared__ __attribute__((aligned(16))) float sQtT[DH * LS];
   __shared__ __attribute__((aligned(16))) float sWT[DH * LS];
-  __shared__ __attribute__((aligned(16))) float sOT[32 * LS];
+  __shared__ __attribute__((aligned(16))) float sOT[32 * LS];  // bf16 dout: bf16 [32][LSB]
   __shared__ __attribute__((aligned(16))) float sST[32 * LL];
   __shared__ __attribute__((aligned(16))) float sDT[32 * LS];
   __shared__ __attribute__((aligned(16))) float sGam[DH];
@@ -281,6 +285,9 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_bwd_bscan_kernel(BwdArgs p) 
   const TG* __restrict__ gO = reinterpret_cast<const TG*>(p.dout);
   const int c_lo = p.cfirst[n], c_hi = p.cfirst[n + 1];
   const int tseq = p.cu[n], tend = p.cu[n + 1];
+  constexpr bool SPLIT = sizeof(TG) == 2;  // dO exact in bf16: split products
+  constexpr int LSB = 72;                   // bf16 row of 64 tokens (16-byte rows)
+  bf16* sOTb = reinterpret_cast<bf16*>(sOT);
   // dSn of each chunk is snapshotted from registers as it is formed; the
   // last chunk's (= dS_final) here
   for (int x = tid; x < DH * 32; x += NT) {
@@ -310,7 +317,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_bwd_bscan_kernel(BwdArgs p) 
     const int t0 = tseq + (c - c_lo) * CHUNK, len = min(CHUNK, tend - t0);
     const int r = tid >> 3, j4 = 4 * (tid & 7);
     if (r < len) {
-      load4_scaled(gO + ((size_t)(t0 + r) * p.H + h) * DH + v0 + j4, p.scale, rO);
+      load4_scaled(gO + ((size_t)(t0 + r) * p.H + h) * DH + v0 + j4, SPLIT ? 1.0f : p.scale, rO);
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) rO[e] = 0.0f;
@@ -333,7 +340,10 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_bwd_bscan_kernel(BwdArgs p) 
     {
       const int r = tid >> 3, j4 = 4 * (tid & 7);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sOT[(j4 + e) * LS + r] = rO[e];
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (SPLIT) sOTb[(j4 + e) * LSB + r] = (bf16)rO[e];  // exact
+        else sOT[(j4 + e) * LS + r] = rO[e];
+      }
     }
     if (tid < 32) *reinterpret_cast<f32x4*>(sGam + 4 * tid) = rG;
   };
@@ -348,8 +358,26 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_bwd_bscan_kernel(BwdArgs p) 
     // dD[r][j] = sum_i P^T[r][i] dO^T[j][i] + sum_c Kb[r][c] dS^T[j][c]: rows 16 rb.., values 16 cbw..
     {
       f32x4 acc = {0, 0, 0, 0};
-      acc = mma16_rows<float, CHUNK>(sPT + 16 * rb * LS, LS, sOT + 16 * cbw * LS, LS, acc, l);
-      acc = mma16_rows<float, DH>(sKb + 16 * rb * LL, LL, sST + 16 * cbw * LL, LL, acc, l);
+      if constexpr (SPLIT) {
+        // P^T dO: lane (m, g) takes contracted tokens 16 g + 8 s .. + 7 of A
+        // row m and of B column m (the FP32 path's lane split)
+        const int m = l & 15, g = l >> 4;
+        f32x4 po = {0, 0, 0, 0};
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const float* pa = sPT + (16 * rb + m) * LS + 16 * g + 8 * s;
+          bf16x8 ap[3];
+          split8(*reinterpret_cast<const f32x4*>(pa), *reinterpret_cast<const f32x4*>(pa + 4), ap);
+          const bf16x8 bo = *reinterpret_cast<const bf16x8*>(sOTb + (16 * cbw + m) * LSB + 16 * g + 8 * s);
+          po = mma_x3b(ap, bo, po);
+        }
+        acc = mma16_rows<float, DH>(sKb + 16 * rb * LL, LL, sST + 16 * cbw * LL, LL, acc, l);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = fmaf(p.scale, po[e], acc[e]);
+      } else {
+        acc = mma16_rows<float, CHUNK>(sPT + 16 * rb * LS, LS, sOT + 16 * cbw * LS, LS, acc, l);
+        acc = mma16_rows<float, DH>(sKb + 16 * rb * LL, LL, sST + 16 * cbw * LL, LL, acc, l);
+      }
       const int j = 16 * cbw + (l & 15);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -364,6 +392,16 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_bwd_bscan_kernel(BwdArgs p) 
     // dS0[i][j] = Gam_i dSn[i][j] + sum_r Qt^T[i][r] dO^T[j][r] - sum_r W^T[i][r] dD^T[j][r]:
     // key rows 16w..16w+15
     f32x4 ns[2];
+    // bf16 dout: the pieces of this wave's Qt^T rows (A operand of both tiles)
+    bf16x8 aq[SPLIT ? 2 : 1][3];
+    if constexpr (SPLIT) {
+      const int m = l & 15, g = l >> 4;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const float* pa = sQtT + (16 * w + m) * LS + 16 * g + 8 * s;
+        split8(*reinterpret_cast<const f32x4*>(pa), *reinterpret_cast<const f32x4*>(pa + 4), aq[s]);
+      }
+    }
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       f32x4 acc, neg = {0, 0, 0, 0};
@@ -373,7 +411,19 @@ __global__ __launch_bounds__(SCAN_THREADS) void kda_bwd_bscan_kernel(BwdArgs p) 
         const int i = 16 * w + 4 * (l >> 4) + e;
         acc[e] = sGam[i] * sST[j * LL + i];
       }
-      acc = mma16_rows<float, CHUNK>(sQtT + 16 * w * LS, LS, sOT + 16 * cb * LS, LS, acc, l);
+      if constexpr (SPLIT) {
+        const int m = l & 15, g = l >> 4;
+        f32x4 qo = {0, 0, 0, 0};
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const bf16x8 bo = *reinterpret_cast<const bf16x8*>(sOTb + (16 * cb + m) * LSB + 16 * g + 8 * s);
+          qo = mma_x3b(aq[s], bo, qo);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = fmaf(p.scale, qo[e], acc[e]);
+      } else {
+        acc = mma16_rows<float, CHUNK>(sQtT + 16 * w * LS, LS, sOT + 16 * cb * LS, LS, acc, l);
+      }
       neg = mma16_rows<float, CHUNK>(sWT + 16 * w * LS, LS, sDT + 16 * cb * LS, LS, neg, l);
       ns[cb] = acc - neg;
       if (more) {

@@ -106,14 +106,6 @@ __device__ __forceinline__ void store_out8(TO* rowp, int v0, int dv, const u32 (
   }
 }
 
-// pieces of eight FP32 values (a then b), one bf16x8 per piece
-__device__ __forceinline__ void split8(const f32x4& a, const f32x4& b, bf16x8 (&o)[3]) {
-  const Pieces2 p0 = split2(f32x2{a[0], a[1]}), p1 = split2(f32x2{a[2], a[3]});
-  const Pieces2 p2 = split2(f32x2{b[0], b[1]}), p3 = split2(f32x2{b[2], b[3]});
-  o[0] = __builtin_bit_cast(bf16x8, u32x4{p0.h, p1.h, p2.h, p3.h});
-  o[1] = __builtin_bit_cast(bf16x8, u32x4{p0.m, p1.m, p2.m, p3.m});
-  o[2] = __builtin_bit_cast(bf16x8, u32x4{p0.l, p1.l, p2.l, p3.l});
-}
 // C += A B over 16 contracted values from their pieces (smallest terms first)
 __device__ __forceinline__ f32x16 mma_x6(const bf16x8 (&a)[3], const bf16x8 (&b)[3], f32x16 c) {
   c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], b[0], c, 0, 0, 0);

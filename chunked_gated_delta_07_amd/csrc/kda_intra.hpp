@@ -20,9 +20,12 @@
 //
 // Off-diagonal 16x16 blocks (row block R > column block I) are products
 // (k^_r * prod_{16R<j<=r} a_j) . (k^_i * prod_{i<j<=16R} a_j): both factors
-// <= 1, one MFMA tile each.  Inside a diagonal block the decay of each pair is
-// formed per pair and channel on the VALU and the channel sum is done by an
-// MFMA (one useful pair per output column).
+// <= 1, one MFMA tile each.  Inside a diagonal block the same split about a
+// row between the two covers rows 8..15 x columns 0..7 (about row 8) and, with
+// bf16 operands, rows 4..7 x 0..3 and 12..15 x 8..11 (about rows 4 and 12, one
+// tile for both); for the remaining pairs the decay is formed per pair and
+// channel on the VALU and the channel sum is done by an MFMA (one useful pair
+// per output column), or with FP32 operands by a sum over the wave.
 //
 // Layout choices: one workgroup (4 waves) per (chunk, head).  For the VALU
 // work each wave owns 16 token rows and each lane two adjacent channels, so

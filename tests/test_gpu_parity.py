@@ -125,6 +125,14 @@ def test_fp32_activations_bf16_intermediates():
     _check(inp, fp32=False, label="act fp32 / bf16 inter")
 
 
+@pytest.mark.parametrize("fp32", [False, True], ids=["bf16", "fp32"])
+def test_fp32_activations_long_packed(fp32):
+    """FP32 activations over 2,500 + 1,100 tokens (57 chunks: two segments of
+    the BF16 schedule, one pass in FP32 mode), three heads."""
+    inp = synth.make_inputs([0, 2500, 3600], H=3, d=128, act="fp32", seed=6)
+    _check(inp, fp32=fp32, label="act fp32 long")
+
+
 def test_special_values():
     """A_log = -inf (no decay) on one head; b_raw = +-inf (beta exactly 1 / 0)
     on some tokens; large |f_raw| (gate saturation both ways)."""

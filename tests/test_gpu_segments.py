@@ -133,3 +133,35 @@ def test_segmented_rectangular_and_convolution():
         oo = kda.chunk_fwd(*sub, out_fp32=True, conv_weight=w)
         torch.cuda.synchronize()
         assert torch.equal(o[s0:s1], oo)
+
+
+@pytest.mark.parametrize("H", [3, 5])
+def test_segments_many_sequences_odd_heads(H):
+    """Seven packed sequences (4500, 0, 65, 2100, 1, 3000 and 64 tokens: 153
+    chunks, five segments; the first sequence crosses two segment boundaries)
+    with a head count that leaves the state pass's last grid row partly
+    empty (7 H pairs, not a multiple of 8), start states on: every sequence
+    equals its run alone bit for bit, and the batch meets the BF16 bar
+    against the oracle (output and end states)."""
+    import torch
+
+    lens = [4500, 0, 65, 2100, 1, 3000, 64]
+    cu = [0] + np.cumsum(lens).tolist()
+    inp = synth.make_inputs(cu, H=H, d=128, act="bf16", seed=98 + H)
+    args = U.to_device(inp, "cuda:0")
+    N = len(lens)
+    S0 = (0.3 * torch.randn((N, H, 128, 128), generator=torch.Generator().manual_seed(H))).cuda()
+    out, fin = _call(args, cu, S0, True)
+    for n in range(N):
+        a, b = cu[n], cu[n + 1]
+        sub = [x[a:b].contiguous() for x in args[:5]] + list(args[5:7])
+        o, f = _call(sub, [0, b - a], S0[n:n + 1].contiguous(), True)
+        torch.cuda.synchronize()
+        assert torch.equal(out[a:b], o), n
+        assert torch.equal(fin[n:n + 1], f), n
+    ref, fref = oracle.kda_forward(**inp.as_f64(), initial_state=S0.double().cpu().numpy(),
+                                   return_final_state=True)
+    ro = U.rel_l2(U.out_to_f64(out), ref)
+    rf = U.rel_l2(fin.double().cpu().numpy(), fref)
+    print(f"[segments odd heads H={H}] rel={ro:.3e} final={rf:.3e}", flush=True)
+    assert ro <= U.TOL_BF16_REL and rf <= U.TOL_BF16_REL

@@ -887,15 +887,33 @@ __device__ __forceinline__ void intra_chunk(const IntraArgs& p, int chunk, int h
       kb1[j] = ka[j][1] * rk * s1;
       s0 *= aa[j][0]; s1 *= aa[j][1];
     }
+    if constexpr (sizeof(MT) == 2 && std::is_same<LY, Frag<MT>>::value) {
+      // a 16-byte unit of Kb^T is 8 consecutive tokens of one channel: this
+      // lane holds four whole units (channels c0, c0 + 1; tokens 16w .. 16w+7
+      // and 16w+8 .. 16w+15), written with one 16-byte store each (8-byte
+      // half-unit stores took about 1 % longer over the kernel)
 #pragma unroll
-    for (int j = 0; j < 16; j += 4) {
-      store4(gKbT + LY::kb(c0, 16 * w + j), f32x4{kb0[j], kb0[j + 1], kb0[j + 2], kb0[j + 3]});
-      store4(gKbT + LY::kb(c0 + 1, 16 * w + j),
-             f32x4{kb1[j], kb1[j + 1], kb1[j + 2], kb1[j + 3]});
-      if constexpr (BWD) {
-        float* gk = p.kbr + ((size_t)chunk * H + h) * CHUNK * DH;
+      for (int hh = 0; hh < 2; ++hh) {
+        u32x4 x0, x1;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) store2(gk + (16 * w + j + e) * DH + c0, kb0[j + e], kb1[j + e]);
+        for (int i = 0; i < 4; ++i) {
+          x0[i] = cvt_pair(f32x2{kb0[8 * hh + 2 * i], kb0[8 * hh + 2 * i + 1]});
+          x1[i] = cvt_pair(f32x2{kb1[8 * hh + 2 * i], kb1[8 * hh + 2 * i + 1]});
+        }
+        *reinterpret_cast<u32x4*>(gKbT + LY::kb(c0, 16 * w + 8 * hh)) = x0;
+        *reinterpret_cast<u32x4*>(gKbT + LY::kb(c0 + 1, 16 * w + 8 * hh)) = x1;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; j += 4) {
+        store4(gKbT + LY::kb(c0, 16 * w + j), f32x4{kb0[j], kb0[j + 1], kb0[j + 2], kb0[j + 3]});
+        store4(gKbT + LY::kb(c0 + 1, 16 * w + j),
+               f32x4{kb1[j], kb1[j + 1], kb1[j + 2], kb1[j + 3]});
+        if constexpr (BWD) {
+          float* gk = p.kbr + ((size_t)chunk * H + h) * CHUNK * DH;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) store2(gk + (16 * w + j + e) * DH + c0, kb0[j + e], kb1[j + e]);
+        }
       }
     }
     if (w == 0) {

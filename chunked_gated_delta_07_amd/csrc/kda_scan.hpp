@@ -255,8 +255,16 @@ __device__ __forceinline__ void ring_step(const ScanArgs& p, const char* slot, f
   TO* __restrict__ out = reinterpret_cast<TO*>(p.out);
   auto frag = [&](int off) { return *reinterpret_cast<const bf16x8*>(slot + off + 16 * l); };
   bf16x8 a[8];
+  if constexpr (ROLE == 0) {
 #pragma unroll
-  for (int s = 0; s < 8; ++s) a[s] = frag((ROLE == 0 ? RG_W : RG_QT) + wp * 8192 + s * 1024);
+    for (int s = 0; s < 8; ++s) a[s] = frag(RG_W + wp * 8192 + s * 1024);
+  } else {
+    // Qt in its own order (Frag::qt): token 32 wp + col, channels 64 g + 8 s
+    // .. + 7, the same values as a W fragment
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      a[s] = *reinterpret_cast<const bf16x8*>(slot + RG_QT + 2 * Frag<bf16>::qt(32 * wp + col, 64 * g + 8 * s));
+  }
   f32x16 X;
 #pragma unroll
   for (int e = 0; e < 16; ++e) X[e] = 0.0f;

@@ -44,8 +44,8 @@ namespace kda {
 //   U [64 tok][128 value ch], P [64][64]
 // plus Gam [128] float in a separate array.  Each matrix is stored in the
 // order in which the state pass reads it: one state-pass load instruction
-// (64 lanes x 16 bytes) covers 1 KB of contiguous memory (bf16 Qt: one
-// 16-byte unit per lane from a row-major layout, see qt).  The state pass uses
+// (64 lanes x 16 bytes) covers 1 KB of contiguous memory (Qt: one 16-byte
+// unit per lane from a row-major layout, see qt).  The state pass uses
 // 32x32 MFMA tiles; lane L = 32 g + col holds tile row/column col and the
 // contracted-index half g (see kda_scan.hpp).  FE = elements per 16 bytes.
 constexpr int OFF_W = 0;
@@ -65,14 +65,14 @@ template <typename MT> struct Frag {
   __host__ __device__ static constexpr int a(int r, int c) {
     return (((r >> 5) * (64 / FE) + (c & 63) / FE) * 64 + 32 * (c >> 6) + (r & 31)) * FE + (c & 63) % FE;
   }
-  // Qt element (token r, key channel c).  FP32: as W.  bf16: row-major, the
-  // 16-byte chunks of row r permuted by chunk ^ (r % 16), so that the intra
-  // kernel writes whole 256-byte rows (four lanes per chunk) and the state
-  // pass reads the same fragments as for W (lane: token, 8 channels) from 16
-  // rows per 16 lanes with no bank conflicts.
+  // Qt element (token r, key channel c): row-major, the 16-byte chunks of row
+  // r permuted by chunk ^ (r % 16), so that the intra kernel writes whole rows
+  // per store (two or four lanes per chunk; as W's order a chunk would hold
+  // values of lanes 1 KB apart) and the state pass reads the values of a W
+  // fragment (lane: token, 8 or 4 channels) from 16 rows per 16 lanes with no
+  // bank conflicts.
   __host__ __device__ static constexpr int qt(int r, int c) {
-    if constexpr (FE == 8) return r * DH + 8 * ((c >> 3) ^ (r & 15)) + (c & 7);
-    else return a(r, c);
+    return r * DH + FE * ((c / FE) ^ (r & 15)) + c % FE;
   }
   // Kb^T element (key channel c, token t): A operand of Kb^T D, contracted over
   // tokens, half g = t/32.

@@ -552,16 +552,23 @@ __device__ __forceinline__ void ring32_step(const ScanArgs& p, const char* slot,
 #pragma unroll
   for (int e = 0; e < 16; ++e) X[e] = 0.0f;
   // X = W S0 (role 0) or S0^T Qt^T (role 1); fragments 2s, 2s+1 of the row
-  // pair with S0^T entries 64g + 8s .. 64g + 8s + 7
+  // pair with S0^T entries 64g + 8s .. 64g + 8s + 7 (Qt in its own row-major
+  // order, Frag::qt: the same values, token 32 wp + col)
   {
-    const int abase = (ROLE == 0 ? RF_W : RF_QT) + wp * 16384;
+    const int abase = RF_W + wp * 16384;
+    auto afrag = [&](int s, int d) {
+      if constexpr (ROLE == 0) return frag(abase + (2 * s + d) * 1024);
+      else
+        return *reinterpret_cast<const f32x4*>(
+            slot + RF_QT + 4 * Frag<float>::qt(32 * wp + col, 64 * g + 8 * s + 4 * d));
+    };
     const bf16* ps = sS + col * SL + 64 * g;
     f32x4 raw[8][2];
     bf16x8 rr[8][3], oo[8][3];
-    raw[0][0] = frag(abase);
-    raw[0][1] = frag(abase + 1024);
-    raw[1][0] = frag(abase + 2048);
-    raw[1][1] = frag(abase + 3072);
+    raw[0][0] = afrag(0, 0);
+    raw[0][1] = afrag(0, 1);
+    raw[1][0] = afrag(1, 0);
+    raw[1][1] = afrag(1, 1);
     load_pieces8(ps, PS, oo[0]);
     f32x4 u[4];
     if constexpr (ROLE == 0) {
@@ -572,8 +579,8 @@ __device__ __forceinline__ void ring32_step(const ScanArgs& p, const char* slot,
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       if (s + 2 < 8) {
-        raw[s + 2][0] = frag(abase + 2 * (s + 2) * 1024);
-        raw[s + 2][1] = frag(abase + (2 * (s + 2) + 1) * 1024);
+        raw[s + 2][0] = afrag(s + 2, 0);
+        raw[s + 2][1] = afrag(s + 2, 1);
       }
       if (s + 1 < 8) load_pieces8(ps + 8 * (s + 1), PS, oo[s + 1]);
       __builtin_amdgcn_sched_barrier(0);

@@ -249,9 +249,11 @@ def test_intra_records_match_chunk_oracle():
     rr, ii = np.meshgrid(np.arange(64), np.arange(64), indexing="ij")
     ip = ((((rr >> 5) * (32 // FE) + (ii & 31) // FE) * 64 + 32 * (ii >> 5) + (rr & 31)) * FE
           + (ii & 31) % FE)
+    # Qt: row-major, 16-byte chunk index permuted by row: chunk ^ (r % 16)
+    iq = r * 128 + FE * ((c // FE) ^ (r & 15)) + c % FE
     checks = {
         "W": (rec[:, :, 0:8192][:, :, ia], R["W"]),
-        "Qt": (rec[:, :, 8192:16384][:, :, ia], R["Qt"]),
+        "Qt": (rec[:, :, 8192:16384][:, :, iq], R["Qt"]),
         "KbT": (rec[:, :, 16384:24576][:, :, ikb], np.swapaxes(R["Kb"], 2, 3)),
         "U": (rec[:, :, 24576:32768][:, :, iu], R["U"]),
         "P": (rec[:, :, 32768:][:, :, ip], R["P"]),

@@ -245,6 +245,45 @@ __device__ __forceinline__ void ring_copy_late(const char* rc, const char* gc, c
   if (lw == 0 && l < 32) copy_1k(gc, slot + RG_GM, l);  // 512 bytes of Gam
 }
 
+// Output of one chunk from an output wave's accumulator X (lane (col, g):
+// token 32 wp + col, values 8 e4 + 4 g + (0..3)): scaled, converted, one
+// exchange between the lane halves per pair of e4 (8 consecutive values per
+// lane), 16-byte stores of the tokens below len.
+template <typename TO, bool RECT>
+__device__ __forceinline__ void ring_out_store(const ScanArgs& p, const f32x16& X, int ctok, int len,
+                                               int h, int vb, int w, int l) {
+  const int col = l & 31, g = l >> 5, wp = w & 1;
+  TO* __restrict__ out = reinterpret_cast<TO*>(p.out);
+  constexpr int NW = (int)sizeof(TO);  // 32-bit words per four output values
+  u32 wd[4][NW];
+#pragma unroll
+  for (int e4 = 0; e4 < 4; ++e4) {
+    if constexpr (sizeof(TO) == 2) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        wd[e4][j] = __builtin_bit_cast(u32, bf16x2{(bf16)(p.scale * X[4 * e4 + 2 * j]),
+                                                   (bf16)(p.scale * X[4 * e4 + 2 * j + 1])});
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wd[e4][j] = __builtin_bit_cast(u32, p.scale * X[4 * e4 + j]);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      const auto r = __builtin_amdgcn_permlane32_swap(wd[2 * q][j], wd[2 * q + 1][j], false, false);
+      wd[2 * q][j] = r[0];
+      wd[2 * q + 1][j] = r[1];
+    }
+  const int tk = 32 * wp + col;
+  if (tk < len) {
+    const int dvo = RECT ? p.dv : DH;  // output row width
+    store_out8<TO, RECT>(out + ((size_t)(ctok + tk) * p.H + h) * dvo + DVB * vb + 8 * g,
+                         DVB * vb + 8 * g, dvo, wd);
+  }
+}
+
 // One chunk for one compute wave; operands come from ring slot `slot`.
 template <typename TO, int ROLE, bool FULL, bool RECT>
 __device__ __forceinline__ void ring_step(const ScanArgs& p, const char* slot, f32x16& S, bf16* sS,
@@ -301,38 +340,7 @@ __device__ __forceinline__ void ring_step(const ScanArgs& p, const char* slot, f
 #pragma unroll
     for (int s = 0; s < 4; ++s) pr[s] = frag(RG_P + wp * 4096 + s * 1024);
     X = mma32_rr<32>(dfr, pr, X);
-    // lane (col, g): token 32wp + col, values 8 e4 + 4g + (0..3); one exchange
-    // between the lane halves per pair of e4 gives 8 consecutive values
-    typedef unsigned u32;
-    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-    constexpr int NW = (int)sizeof(TO);
-    u32 wd[4][NW];
-#pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      if constexpr (sizeof(TO) == 2) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          wd[e4][j] = __builtin_bit_cast(u32, bf16x2{(bf16)(p.scale * X[4 * e4 + 2 * j]),
-                                                     (bf16)(p.scale * X[4 * e4 + 2 * j + 1])});
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) wd[e4][j] = __builtin_bit_cast(u32, p.scale * X[4 * e4 + j]);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int j = 0; j < NW; ++j) {
-        const auto r = __builtin_amdgcn_permlane32_swap(wd[2 * q][j], wd[2 * q + 1][j], false, false);
-        wd[2 * q][j] = r[0];
-        wd[2 * q + 1][j] = r[1];
-      }
-    const int tk = 32 * wp + col;
-    if (FULL || tk < len) {
-      const int dvo = RECT ? p.dv : DH;  // output row width
-      store_out8<TO, RECT>(out + ((size_t)(ctok + tk) * p.H + h) * dvo + DVB * vb + 8 * g,
-                           DVB * vb + 8 * g, dvo, wd);
-    }
+    ring_out_store<TO, RECT>(p, X, ctok, FULL ? CHUNK : len, h, vb, w, l);
   }
   // S_next = Diag(Gam) S0 + Kb^T D
 #pragma unroll
@@ -539,10 +547,23 @@ __device__ __forceinline__ f32x16 mma_x6_pipe(const bf16x8 (&r)[3], const bf16x8
 // One chunk for one compute wave of the FP32 ring.  Every FP32 record fragment
 // is one 16-byte LDS read per lane from the slot, issued two steps before its
 // products, and split into pieces during the previous step's products.
+// A finished output tile waiting for its store (FP32 state pass): the output
+// waves store it at the start of the next step, in the first phase, where
+// they wait for the other waves' D anyway, instead of at the end of the
+// second phase, which ends the step.
+struct Ring32Out {
+  f32x16 X;
+  int ctok, len;
+  bool valid;
+};
+
 template <typename TO, int ROLE, bool FULL, bool RECT>
 __device__ __forceinline__ void ring32_step(const ScanArgs& p, const char* slot, f32x16& S,
                                             bf16* sS, bf16* sD, int h, int ctok, int len, int vb,
-                                            int w, int l) {
+                                            int w, int l, Ring32Out& ro) {
+  if constexpr (ROLE == 1) {
+    if (ro.valid) ring_out_store<TO, RECT>(p, ro.X, ro.ctok, ro.len, h, vb, w, l);
+  }
   typedef Ring32Lds L;
   constexpr int SL = L::SL, DL = L::DL, PS = L::PS, PD = L::PD;
   const int col = l & 31, g = l >> 5, wp = w & 1;
@@ -642,35 +663,10 @@ __device__ __forceinline__ void ring32_step(const ScanArgs& p, const char* slot,
     store_pieces4(sS + col * SL + 32 * w + 8 * e4 + 4 * g, PS,
                   f32x4{S[4 * e4], S[4 * e4 + 1], S[4 * e4 + 2], S[4 * e4 + 3]});
   if constexpr (ROLE == 1) {
-    // output of this chunk while the state pieces are written
-    constexpr int NW = (int)sizeof(TO);  // 32-bit words per four output values
-    u32 wd[4][NW];
-#pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      if constexpr (sizeof(TO) == 2) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          wd[e4][j] = __builtin_bit_cast(u32, bf16x2{(bf16)(p.scale * X[4 * e4 + 2 * j]),
-                                                     (bf16)(p.scale * X[4 * e4 + 2 * j + 1])});
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) wd[e4][j] = __builtin_bit_cast(u32, p.scale * X[4 * e4 + j]);
-      }
-    }
-#pragma unroll
-    for (int pr = 0; pr < 2; ++pr)
-#pragma unroll
-      for (int j = 0; j < NW; ++j) {
-        const auto r = __builtin_amdgcn_permlane32_swap(wd[2 * pr][j], wd[2 * pr + 1][j], false, false);
-        wd[2 * pr][j] = r[0];
-        wd[2 * pr + 1][j] = r[1];
-      }
-    const int tk = 32 * wp + col;
-    if (FULL || tk < len) {
-      const int dvo = RECT ? p.dv : DH;  // output row width
-      store_out8<TO, RECT>(out + ((size_t)(ctok + tk) * p.H + h) * dvo + DVB * vb + 8 * g,
-                           DVB * vb + 8 * g, dvo, wd);
-    }
+    ro.X = X;
+    ro.ctok = ctok;
+    ro.len = FULL ? CHUNK : len;
+    ro.valid = true;
   }
   wait_lds();
   ring_barrier();  // new S0 complete; D and the late operands may be overwritten
@@ -742,16 +738,19 @@ __global__ __launch_bounds__(512) void kda_scan_ring32_kernel(ScanArgs p) {
   wait_lds();
   ring_barrier();
   const int cfull = cbeg + (tend - tseq) / CHUNK;
+  Ring32Out ro;
+  ro.valid = false;
   for (int c = cbeg; c < cend; ++c) {
     const int ctok = tseq + (c - cbeg) * CHUNK;
     if (c < cfull) {
-      if (w < 2) ring32_step<TO, 0, true, RECT>(p, slot, S, sS, sD, h, ctok, CHUNK, vb, w, l);
-      else ring32_step<TO, 1, true, RECT>(p, slot, S, sS, sD, h, ctok, CHUNK, vb, w, l);
+      if (w < 2) ring32_step<TO, 0, true, RECT>(p, slot, S, sS, sD, h, ctok, CHUNK, vb, w, l, ro);
+      else ring32_step<TO, 1, true, RECT>(p, slot, S, sS, sD, h, ctok, CHUNK, vb, w, l, ro);
     } else {
-      if (w < 2) ring32_step<TO, 0, false, RECT>(p, slot, S, sS, sD, h, ctok, tend - ctok, vb, w, l);
-      else ring32_step<TO, 1, false, RECT>(p, slot, S, sS, sD, h, ctok, tend - ctok, vb, w, l);
+      if (w < 2) ring32_step<TO, 0, false, RECT>(p, slot, S, sS, sD, h, ctok, tend - ctok, vb, w, l, ro);
+      else ring32_step<TO, 1, false, RECT>(p, slot, S, sS, sD, h, ctok, tend - ctok, vb, w, l, ro);
     }
   }
+  if (w >= 2 && ro.valid) ring_out_store<TO, RECT>(p, ro.X, ro.ctok, ro.len, h, vb, w, l);  // last chunk
   if (p.fin) {
 #pragma unroll
     for (int e = 0; e < 16; ++e)

@@ -131,8 +131,8 @@ struct WsLayout {
   size_t off_cfirst, off_gam, off_rec, off_carry, total;
 };
 
-// two passes: [cfirst][gam: chunks x H x 128 f32][rec: chunks x H x REC]
-// segmented:  [cfirst][gam: 32 x H x 128 f32][rec: 32 x H x REC bf16][carry: 2 x H x 128 x 128 f32]
+// two passes: [cfirst][gam: chunks x H x 128 f32][rec: chunks x H x Frag<MT> record]
+// segmented:  [cfirst][gam: 32 x H x 128 f32][rec: 32 x H x Frag<bf16> record][carry: 2 x H x 128 x 128 f32]
 // windowed:   [cfirst][gam: ring x H x 128 f32][rec: ring x H x RECW bf16][carry: 2 x H x 128 x 128 f32]
 static inline WsLayout ws_layout(int64_t T, int32_t N, int32_t H, uint32_t mode) {
   const size_t mt = (mode & KDA_MODE_FP32_INTERMEDIATE) ? 4 : 2;
@@ -142,7 +142,8 @@ static inline WsLayout ws_layout(int64_t T, int32_t N, int32_t H, uint32_t mode)
   L.off_cfirst = 256;  // [0, 4): status word of KDA_MODE_CHECK_CU
   L.off_gam = L.off_cfirst + align256(sizeof(int32_t) * (size_t)(N + 1));
   L.off_rec = L.off_gam + align256(sizeof(float) * (size_t)C * H * DH);
-  L.off_carry = L.off_rec + align256(mt * (size_t)C * H * (win ? RECW : REC));
+  const size_t rec_elems = win ? RECW : mt == 2 ? Frag<bf16>::REC_ELEMS : Frag<float>::REC_ELEMS;
+  L.off_carry = L.off_rec + align256(mt * (size_t)C * H * rec_elems);
   L.total = L.off_carry + (win || seg ? align256(sizeof(float) * 2 * (size_t)H * DH * DH) : 0);
   return L;
 }

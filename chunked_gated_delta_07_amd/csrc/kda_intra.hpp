@@ -41,7 +41,8 @@ namespace kda {
 
 // Per-(chunk, head) record in the workspace, element type MT, holding
 //   W [64 tok][128 key ch], Qt [64][128], Kb^T [128 key ch][64 tok],
-//   U [64 tok][128 value ch], P [64][64]
+//   U [64 tok][128 value ch], P [64][64] (bf16: its three 32x32 tiles on or
+//   below the diagonal)
 // plus Gam [128] float in a separate array.  Each matrix is stored in the
 // order in which the state pass reads it: one state-pass load instruction
 // (64 lanes x 16 bytes) covers 1 KB of contiguous memory (Qt: one 16-byte
@@ -54,12 +55,17 @@ constexpr int OFF_KBT = 2 * CHUNK * DH;
 constexpr int OFF_UT = 3 * CHUNK * DH;
 constexpr int OFF_P = 4 * CHUNK * DH;
 constexpr int REC = 4 * CHUNK * DH + CHUNK * CHUNK;
+// P as its three 32x32 tiles on or below the diagonal (the fourth is zero):
+// the bf16 records of the two-pass and windowed forwards
+constexpr int REC_LP = 4 * CHUNK * DH + 3 * CHUNK * CHUNK / 4;
 
 template <typename MT> struct Frag {
   static constexpr int FE = 16 / (int)sizeof(MT);
   static constexpr bool TRANSPOSED_QT_P = false;
-  static constexpr bool P_LOWER_TILES = false;  // P stored whole (see FragW)
-  static constexpr int REC_ELEMS = REC;
+  // bf16: P without its zero tile, and the token-contracted operands (Kb^T,
+  // P) in steps of 16 tokens (see kb); FP32 keeps P whole.
+  static constexpr bool P_LOWER_TILES = sizeof(MT) == 2;
+  static constexpr int REC_ELEMS = P_LOWER_TILES ? REC_LP : REC;
   // W / Qt element (token r, key channel c): A operand of [W;Qt] S0, contracted
   // over key channels, half g = c/64.
   __host__ __device__ static constexpr int a(int r, int c) {
@@ -75,14 +81,23 @@ template <typename MT> struct Frag {
     return r * DH + FE * ((c / FE) ^ (r & 15)) + c % FE;
   }
   // Kb^T element (key channel c, token t): A operand of Kb^T D, contracted over
-  // tokens, half g = t/32.
+  // tokens.  bf16: fragment (c/32, step t/16), lane half g = (t/8) % 2, so a
+  // step of the contraction covers 16 consecutive tokens; FP32: half g = t/32.
   __host__ __device__ static constexpr int kb(int c, int t) {
+    if (FE == 8) return (((c >> 5) * 4 + (t >> 4)) * 64 + 32 * ((t >> 3) & 1) + (c & 31)) * 8 + (t & 7);
     return (((c >> 5) * (32 / FE) + (t & 31) / FE) * 64 + 32 * (t >> 5) + (c & 31)) * FE + (t & 31) % FE;
   }
-  // P element (token r, token i): A operand of P D, rows 32..63 -> waves 2,3.
+  // P element (token r, token i): A operand of P D, contracted over i in the
+  // order of Kb^T's tokens.  bf16: only i < 32 (r / 32 + 1) is stored, rows
+  // 0..31 in fragments 0, 1 (i < 32), rows 32..63 in fragments 2..5.  FP32:
+  // whole, half g = i/32.
   __host__ __device__ static constexpr int pm(int r, int i) {
+    if (FE == 8)
+      return ((((r >> 5) == 0 ? 0 : 2) + (i >> 4)) * 64 + 32 * ((i >> 3) & 1) + (r & 31)) * 8 + (i & 7);
     return (((r >> 5) * (32 / FE) + (i & 31) / FE) * 64 + 32 * (i >> 5) + (r & 31)) * FE + (i & 31) % FE;
   }
+  // column i of element q of lane half g in P fragment step s (lower tiles)
+  __host__ __device__ static constexpr int pcol(int s, int g, int q) { return 16 * s + 8 * g + q; }
   // U element (token t, value channel v): lane (g, col = v%32) of wave t/32 in
   // value block v/32 holds the 16 tokens 32w + 8e + 4g + i as q = 4e + i.
   __host__ __device__ static constexpr int u(int t, int v) {
@@ -124,7 +139,7 @@ template <typename MT> struct PlainRec {
 //                               (value block v/32, token tile t/32), lane v%32 + 32 g
 //                               element 4 (m/8) + m%4, m = t%32, g = (m/4)%2
 constexpr int OFFW_P = 4 * CHUNK * DH;  // = OFF_P
-constexpr int RECW = 4 * CHUNK * DH + 6 * 512;  // 35,840 elements
+constexpr int RECW = REC_LP;  // 35,840 elements
 template <typename MT> struct FragW {
   static_assert(sizeof(MT) == 2, "bf16 records only");
   static constexpr int FE = 8;
@@ -146,6 +161,8 @@ template <typename MT> struct FragW {
   __host__ __device__ static constexpr int pm(int r, int i) {
     return ((((r >> 5) == 0 ? 0 : 2) + (i >> 4)) * 64 + (r & 31) + 32 * kg(i)) * 8 + kp(i);
   }
+  // column i of element q of lane half g in P fragment step s
+  __host__ __device__ static constexpr int pcol(int s, int g, int q) { return 16 * s + 4 * g + (q & 3) + 8 * (q >> 2); }
   __host__ __device__ static constexpr int u(int t, int v) {
     return ((((v >> 5) * 2 + (t >> 5)) * 64 + (v & 31) + 32 * (((t & 31) >> 2) & 1)) * 16 +
             4 * ((t & 31) >> 3) + (t & 3));
@@ -1082,8 +1099,8 @@ __device__ __forceinline__ void intra_chunk(const IntraArgs& p, int chunk, int h
         const int r = (idx >= 2 ? 32 : 0) + (lane & 31), s = idx >= 2 ? idx - 2 : idx;
         bf16x8 x;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) x[q] = (bf16)pval(r, 16 * s + 4 * g + (q & 3) + 8 * (q >> 2));
-        *reinterpret_cast<bf16x8*>(gP + LY::pm(r, 16 * s + 4 * g)) = x;
+        for (int q = 0; q < 8; ++q) x[q] = (bf16)pval(r, LY::pcol(s, g, q));
+        *reinterpret_cast<bf16x8*>(gP + LY::pm(r, LY::pcol(s, g, 0))) = x;
       }
     } else {
       // FE consecutive columns of one row per 16 bytes

@@ -33,7 +33,7 @@ struct ScanArgs {
   int H;
   float scale;
   const float* gam;  // [chunks][H][128]
-  const void* rec;   // [chunks][H][REC]
+  const void* rec;   // [chunks][H][record elements] (Frag layout)
   void* out;         // [T][H][128]
   const float* init; // [N][H][128 key][128 value] start states, or null (zero)
   float* fin;        // [N][H][128][128] end states, or null (not written)
@@ -186,7 +186,8 @@ template <typename V> __device__ __forceinline__ float val_at(const V* f, int q)
 // so every copy is 1 KB contiguous on both sides.
 //
 // Slot layout (bytes): W [0,16K) | Qt [16K,32K) | Kb^T [32K,48K) | U of this
-// value block [48K,52K) | P [52K,60K) | Gam [60K, 60K+512).  "Early" operands
+// value block [48K,52K) | P's lower tiles [52K,58K) | Gam [58K, 58K+512).
+// "Early" operands
 // (W, Qt, U) are read before the first barrier of a step, "late" ones (Kb^T,
 // P, Gam) after it.  In step c the loaders copy chunk c+1's early operands at
 // the start and its late operands after the first barrier, each into the slot
@@ -194,8 +195,8 @@ template <typename V> __device__ __forceinline__ float val_at(const V* f, int q)
 // right before the barrier that publishes them.  The barriers here are plain
 // s_barrier with explicit waits: a workgroup-scope fence would make every
 // loader wait for all of its copies in flight.
-constexpr int RG_W = 0, RG_QT = 16384, RG_KBT = 32768, RG_U = 49152, RG_P = 53248, RG_GM = 61440;
-constexpr int RG_SLOT = 61952;
+constexpr int RG_W = 0, RG_QT = 16384, RG_KBT = 32768, RG_U = 49152, RG_P = 53248, RG_GM = 59392;
+constexpr int RG_SLOT = 59904;
 struct RingLds {
   static constexpr int SL = 136, DL = 72;  // bf16 row lengths of S0^T and D^T
   static constexpr int O_RING = 0;
@@ -231,7 +232,8 @@ __device__ __forceinline__ void ring_barrier() {
 
 // Loader wave lw (0..3): copies of chunk record rc (bytes) and gamma gc.
 constexpr int RG_EARLY_PER_LOADER = 9;  // 32 KB of W, Qt + 4 KB of U over 4 loaders
-constexpr int RG_LATE_MIN = 6;          // 24 KB of Kb^T, P over 4 loaders (+ Gam on loader 0)
+// 22 KB of Kb^T, P and Gam over 4 loaders: 5 copies on loader 0, 6 on the others
+template <int LW> constexpr int rg_late_copies() { return LW == 0 ? 5 : 6; }
 __device__ __forceinline__ void ring_copy_early(const char* rc, char* slot, int vb, int lw, int l) {
 #pragma unroll
   for (int k = 0; k < 8; ++k) copy_1k(rc + (lw + 4 * k) * 1024, slot + RG_W + (lw + 4 * k) * 1024, l);
@@ -240,9 +242,14 @@ __device__ __forceinline__ void ring_copy_early(const char* rc, char* slot, int 
 __device__ __forceinline__ void ring_copy_late(const char* rc, const char* gc, char* slot, int lw, int l) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) copy_1k(rc + 2 * OFF_KBT + (lw + 4 * k) * 1024, slot + RG_KBT + (lw + 4 * k) * 1024, l);
-#pragma unroll
-  for (int k = 0; k < 2; ++k) copy_1k(rc + 2 * OFF_P + (lw + 4 * k) * 1024, slot + RG_P + (lw + 4 * k) * 1024, l);
-  if (lw == 0 && l < 32) copy_1k(gc, slot + RG_GM, l);  // 512 bytes of Gam
+  copy_1k(rc + 2 * OFF_P + lw * 1024, slot + RG_P + lw * 1024, l);  // P: six fragments
+  if (lw >= 2) copy_1k(rc + 2 * OFF_P + (lw + 2) * 1024, slot + RG_P + (lw + 2) * 1024, l);
+  if (lw == 1 && l < 32) copy_1k(gc, slot + RG_GM, l);  // 512 bytes of Gam
+}
+// Wait until only this loader's late copies are in flight.
+__device__ __forceinline__ void ring_wait_early(int lw) {
+  if (lw == 0) wait_vm<rg_late_copies<0>()>();
+  else wait_vm<rg_late_copies<1>()>();
 }
 
 // Output of one chunk from an output wave's accumulator X (lane (col, g):
@@ -333,13 +340,20 @@ __device__ __forceinline__ void ring_step(const ScanArgs& p, const char* slot, f
   f32x4 gm[4];
 #pragma unroll
   for (int e4 = 0; e4 < 4; ++e4) gm[e4] = gmp[(32 * w + 8 * e4 + 4 * g) / 4];
+  // D^T fragments, tokens 16 s + 8 g .. + 7 (the records' token order)
 #pragma unroll
-  for (int s = 0; s < 4; ++s) dfr[s] = *reinterpret_cast<const bf16x8*>(sD + col * DL + 32 * g + 8 * s);
+  for (int s = 0; s < 4; ++s) dfr[s] = *reinterpret_cast<const bf16x8*>(sD + col * DL + 16 * s + 8 * g);
   if constexpr (ROLE == 1) {
     bf16x8 pr[4];
+    if (wp == 0) {  // tokens 0..31: P's columns below 32 only
 #pragma unroll
-    for (int s = 0; s < 4; ++s) pr[s] = frag(RG_P + wp * 4096 + s * 1024);
-    X = mma32_rr<32>(dfr, pr, X);
+      for (int s = 0; s < 2; ++s) pr[s] = frag(RG_P + s * 1024);
+      X = mma32_rr<16>(dfr, pr, X);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) pr[s] = frag(RG_P + 2048 + s * 1024);
+      X = mma32_rr<32>(dfr, pr, X);
+    }
     ring_out_store<TO, RECT>(p, X, ctok, FULL ? CHUNK : len, h, vb, w, l);
   }
   // S_next = Diag(Gam) S0 + Kb^T D
@@ -385,7 +399,7 @@ __global__ __launch_bounds__(512) void kda_scan_ring_kernel(ScanArgs p) {
   const char* recb = reinterpret_cast<const char*>(p.rec);
   const char* gamb = reinterpret_cast<const char*>(p.gam);
   auto slot_of = [&](int c) { return (size_t)(p.ring ? c % p.ring : c); };
-  auto rec_of = [&](int c) { return recb + (slot_of(c) * H + h) * (size_t)REC * 2; };
+  auto rec_of = [&](int c) { return recb + (slot_of(c) * H + h) * (size_t)Frag<bf16>::REC_ELEMS * 2; };
   auto gam_of = [&](int c) { return gamb + (slot_of(c) * H + h) * DH * 4; };
 
   if (w >= 4) {
@@ -403,7 +417,7 @@ __global__ __launch_bounds__(512) void kda_scan_ring_kernel(ScanArgs p) {
       wait_vm<RG_EARLY_PER_LOADER>();  // late operands of chunk c are in
       ring_barrier();
       ring_copy_late(rec_of(nx), gam_of(nx), nslot, lw, l);
-      wait_vm<RG_LATE_MIN>();  // early operands of chunk c+1 are in
+      ring_wait_early(lw);  // early operands of chunk c+1 are in
       ring_barrier();
     }
     wait_vm<0>();  // nothing left in flight when the wave ends

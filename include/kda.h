@@ -110,8 +110,8 @@ extern "C" {
 /* Bytes of caller-provided scratch that kda_chunk_fwd needs for this shape.
  * Depends only on the arguments; non-decreasing in total_tokens.  FP32
  * intermediates need about 148 KB per 64-token chunk and head.  BF16
- * intermediates need about 74 KB per chunk and head up to 32 chunks and stop
- * growing there: about 2.5 MB per head (the records of one 32-chunk segment and
+ * intermediates need about 72 KB per chunk and head up to 32 chunks and stop
+ * growing there: about 2.4 MB per head (the records of one 32-chunk segment and
  * two 64 KB boundary states).  The windowed schedule (KDA_MODE_WINDOWED with
  * BF16 intermediates and at most 64 sequences) stops growing at 48 chunks:
  * about 3.6 MB per head (two 24-chunk windows).  Returns 0 when total_tokens == 0, and

@@ -56,16 +56,16 @@ constexpr int OFF_UT = 3 * CHUNK * DH;
 constexpr int OFF_P = 4 * CHUNK * DH;
 constexpr int REC = 4 * CHUNK * DH + CHUNK * CHUNK;
 // P as its three 32x32 tiles on or below the diagonal (the fourth is zero):
-// the bf16 records of the two-pass and windowed forwards
+// the records of the forward (Frag, FragW)
 constexpr int REC_LP = 4 * CHUNK * DH + 3 * CHUNK * CHUNK / 4;
 
 template <typename MT> struct Frag {
   static constexpr int FE = 16 / (int)sizeof(MT);
   static constexpr bool TRANSPOSED_QT_P = false;
-  // bf16: P without its zero tile, and the token-contracted operands (Kb^T,
-  // P) in steps of 16 tokens (see kb); FP32 keeps P whole.
-  static constexpr bool P_LOWER_TILES = sizeof(MT) == 2;
-  static constexpr int REC_ELEMS = P_LOWER_TILES ? REC_LP : REC;
+  // P without its zero tile, and the token-contracted operands (Kb^T, P) in
+  // steps of 16 consecutive tokens (see kb).
+  static constexpr bool P_LOWER_TILES = true;
+  static constexpr int REC_ELEMS = REC_LP;
   // W / Qt element (token r, key channel c): A operand of [W;Qt] S0, contracted
   // over key channels, half g = c/64.
   __host__ __device__ static constexpr int a(int r, int c) {
@@ -81,23 +81,24 @@ template <typename MT> struct Frag {
     return r * DH + FE * ((c / FE) ^ (r & 15)) + c % FE;
   }
   // Kb^T element (key channel c, token t): A operand of Kb^T D, contracted over
-  // tokens.  bf16: fragment (c/32, step t/16), lane half g = (t/8) % 2, so a
-  // step of the contraction covers 16 consecutive tokens; FP32: half g = t/32.
+  // tokens in steps of 16: the 8 tokens 16 s + 8 g .. + 7 of step s sit in
+  // lane half g (one 16-byte unit in bf16, the units of fragments 2 s and
+  // 2 s + 1 in FP32).
   __host__ __device__ static constexpr int kb(int c, int t) {
-    if (FE == 8) return (((c >> 5) * 4 + (t >> 4)) * 64 + 32 * ((t >> 3) & 1) + (c & 31)) * 8 + (t & 7);
-    return (((c >> 5) * (32 / FE) + (t & 31) / FE) * 64 + 32 * (t >> 5) + (c & 31)) * FE + (t & 31) % FE;
+    return (((c >> 5) * (32 / FE) + (t >> 4) * (8 / FE) + (t & 7) / FE) * 64 + 32 * ((t >> 3) & 1) +
+            (c & 31)) * FE + t % FE;
   }
   // P element (token r, token i): A operand of P D, contracted over i in the
-  // order of Kb^T's tokens.  bf16: only i < 32 (r / 32 + 1) is stored, rows
-  // 0..31 in fragments 0, 1 (i < 32), rows 32..63 in fragments 2..5.  FP32:
-  // whole, half g = i/32.
+  // order of Kb^T's tokens.  Only i < 32 (r / 32 + 1) is stored: rows 0..31
+  // in the first 16 / FE fragments (i < 32), rows 32..63 in the next 32 / FE.
   __host__ __device__ static constexpr int pm(int r, int i) {
-    if (FE == 8)
-      return ((((r >> 5) == 0 ? 0 : 2) + (i >> 4)) * 64 + 32 * ((i >> 3) & 1) + (r & 31)) * 8 + (i & 7);
-    return (((r >> 5) * (32 / FE) + (i & 31) / FE) * 64 + 32 * (i >> 5) + (r & 31)) * FE + (i & 31) % FE;
+    return ((((r >> 5) == 0 ? 0 : 16 / FE) + (i >> 4) * (8 / FE) + (i & 7) / FE) * 64 +
+            32 * ((i >> 3) & 1) + (r & 31)) * FE + i % FE;
   }
-  // column i of element q of lane half g in P fragment step s (lower tiles)
-  __host__ __device__ static constexpr int pcol(int s, int g, int q) { return 16 * s + 8 * g + q; }
+  // column i of element q of lane half g in P fragment u of its row tile
+  __host__ __device__ static constexpr int pcol(int u, int g, int q) {
+    return 16 * (u / (8 / FE)) + 8 * g + FE * (u % (8 / FE)) + q;
+  }
   // U element (token t, value channel v): lane (g, col = v%32) of wave t/32 in
   // value block v/32 holds the 16 tokens 32w + 8e + 4g + i as q = 4e + i.
   __host__ __device__ static constexpr int u(int t, int v) {
@@ -1080,8 +1081,8 @@ __device__ __forceinline__ void intra_chunk(const IntraArgs& p, int chunk, int h
   if constexpr (L::NP == 1) __syncthreads();  // (the two-pass FP32 loop ends with one)
   // P to the record.  Every entry P[r][i] (i <= r) was left in LDS at
   // sA[i][r], the upper triangle of the A buffer (A is strictly lower); here
-  // it is written in the layout's order, zeros above the diagonal, one 16-byte
-  // store per fragment (consecutive lanes: consecutive rows r, so the LDS reads
+  // it is written in the layout's order (its tiles on or below the diagonal;
+  // zeros above the diagonal inside them), 16-byte stores, one fragment per 64 (consecutive lanes: consecutive rows r, so the LDS reads
   // fall in consecutive banks).  The T solve below reads only A's lower part.
   {
     auto pval = [&](int r, int i) { return i <= r ? sA[i * AL + r] : 0.0f; };
@@ -1092,26 +1093,19 @@ __device__ __forceinline__ void intra_chunk(const IntraArgs& p, int chunk, int h
         const int i = f >> 4, r0 = 4 * (f & 15);
         store4(gP + LY::pm(r0, i), f32x4{pval(r0, i), pval(r0 + 1, i), pval(r0 + 2, i), pval(r0 + 3, i)});
       }
-    } else if constexpr (LY::P_LOWER_TILES) {
-      // the six stored fragments: lane (r % 32, g) of fragment (r / 32, step s)
-      for (int f = tid; f < 6 * 64; f += 256) {
-        const int idx = f >> 6, lane = f & 63, g = lane >> 5;
-        const int r = (idx >= 2 ? 32 : 0) + (lane & 31), s = idx >= 2 ? idx - 2 : idx;
-        bf16x8 x;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) x[q] = (bf16)pval(r, LY::pcol(s, g, q));
-        *reinterpret_cast<bf16x8*>(gP + LY::pm(r, LY::pcol(s, g, 0))) = x;
-      }
     } else {
-      // FE consecutive columns of one row per 16 bytes
-      constexpr int FE = LY::FE;
+      static_assert(LY::P_LOWER_TILES, "forward records hold P's lower tiles");
+      // the stored fragments (16 / FE for rows 0..31, then 32 / FE for rows
+      // 32..63): lane (r % 32, g) of fragment u of its row tile
+      constexpr int FE = LY::FE, F0 = 16 / FE;
       typedef typename std::conditional<sizeof(MT) == 2, bf16x8, f32x4>::type v16;
-      for (int f = tid; f < CHUNK * CHUNK / FE; f += 256) {
-        const int r = f & 63, i0 = FE * (f >> 6);
+      for (int f = tid; f < 3 * F0 * 64; f += 256) {
+        const int idx = f >> 6, lane = f & 63, g = lane >> 5;
+        const int r = (idx >= F0 ? 32 : 0) + (lane & 31), u = idx >= F0 ? idx - F0 : idx;
         v16 x;
 #pragma unroll
-        for (int e = 0; e < FE; ++e) x[e] = from_f32<MT>(pval(r, i0 + e));
-        *reinterpret_cast<v16*>(gP + LY::pm(r, i0)) = x;
+        for (int q = 0; q < FE; ++q) x[q] = from_f32<MT>(pval(r, LY::pcol(u, g, q)));
+        *reinterpret_cast<v16*>(gP + LY::pm(r, LY::pcol(u, g, 0))) = x;
       }
     }
   }

@@ -475,7 +475,7 @@ __global__ __launch_bounds__(512) void kda_scan_ring_kernel(ScanArgs p) {
 // State pass with loader waves, FP32 intermediates.
 //
 // The same division of labour as above, with one LDS slot: a chunk's FP32
-// operands (120.5 KB) and the pieces of S0 and D (39 KB) fill the 160 KB of a
+// operands (116.5 KB) and the pieces of S0 and D (39 KB) fill the 160 KB of a
 // CU, so there is no second slot.  The slot is refilled in halves instead:
 // the early operands (W, Qt, U; read before the first barrier of a step) of
 // chunk c+1 are copied while the compute waves work on chunk c's late
@@ -486,15 +486,16 @@ __global__ __launch_bounds__(512) void kda_scan_ring_kernel(ScanArgs p) {
 // the register file to the splitting of the operands into bf16 pieces.
 //
 // Slot layout (bytes): W [0,32K) | Qt [32K,64K) | Kb^T [64K,96K) | U of this
-// value block [96K,104K) | P [104K,120K) | Gam [120K, 120K+512).
-constexpr int RF_W = 0, RF_QT = 32768, RF_KBT = 65536, RF_U = 98304, RF_P = 106496, RF_GM = 122880;
-constexpr int RF_SLOT = 123392;
+// value block [96K,104K) | P's lower tiles [104K,116K) | Gam [116K, 116K+512).
+constexpr int RF_W = 0, RF_QT = 32768, RF_KBT = 65536, RF_U = 98304, RF_P = 106496, RF_GM = 118784;
+constexpr int RF_SLOT = 119296;
 struct Ring32Lds {
   static constexpr int SL = ScanLds::SL, DL = ScanLds::DL, PS = ScanLds::PS, PD = ScanLds::PD;
   static constexpr int O_SLOT = 0;
   static constexpr int O_S = RF_SLOT;               // S0^T pieces [3][32][SL]
   static constexpr int O_D = O_S + 3 * PS * 2;      // D^T pieces  [3][32][DL]
-  static constexpr int BYTES = O_D + 3 * PD * 2;
+  static constexpr int O_Z = O_D + 3 * PD * 2;      // 1 KB of zeros: P of rows 0..31, columns 32..63
+  static constexpr int BYTES = O_Z + 1024;
 };
 static_assert(Ring32Lds::BYTES <= 160 * 1024, "one slot plus the pieces fit in a CU's LDS");
 
@@ -513,7 +514,7 @@ __device__ __forceinline__ void ring32_copy_late(const char* rc, const char* gc,
   for (int k = 0; k < 8; ++k)  // Kb^T: 32 KB
     copy_1k(rc + 4 * OFF_KBT + (lw + 4 * k) * 1024, slot + RF_KBT + (lw + 4 * k) * 1024, l);
 #pragma unroll
-  for (int k = 0; k < 4; ++k)  // P: 16 KB
+  for (int k = 0; k < 3; ++k)  // P: 12 KB
     copy_1k(rc + 4 * OFF_P + (lw + 4 * k) * 1024, slot + RF_P + (lw + 4 * k) * 1024, l);
   if (lw == 0 && l < 32) copy_1k(gc, slot + RF_GM, l);  // 512 bytes of Gam
 }
@@ -634,22 +635,26 @@ __device__ __forceinline__ void ring32_step(const ScanArgs& p, const char* slot,
   wait_lds();
   ring_barrier();  // D complete; every wave is done reading S0 and the early operands
   // Phase 2, one pipelined sequence of steps: role 1 runs D^T P^T into X
-  // (steps 0..3) and then Kb^T D into S (steps 4..7); role 0 only the latter.
-  constexpr int FIRST = ROLE == 1 ? 0 : 4;
+  // (4 steps of 16 tokens; for tokens 0..31, whose P columns stop at 31, the
+  // last two read a zero fragment) and then Kb^T D into S (4 steps); role 0
+  // only the latter.
+  constexpr int NPS = ROLE == 1 ? 4 : 0, NST = NPS + 4;
   bf16x8 dp[4][3];
-  f32x4 raw[8][2];
-  bf16x8 rr[8][3];
-  auto rec_off = [&](int s, int half) {
-    return s < 4 ? RF_P + wp * 8192 + (2 * s + half) * 1024
-                 : RF_KBT + w * 8192 + (2 * (s - 4) + half) * 1024;
+  f32x4 raw[NST][2];
+  bf16x8 rr[NST][3];
+  auto rec_off = [&](int j, int half) {
+    if (j < NPS)
+      return wp ? RF_P + 4096 + (2 * j + half) * 1024 : j < 2 ? RF_P + (2 * j + half) * 1024 : L::O_Z;
+    return RF_KBT + w * 8192 + (2 * (j - NPS) + half) * 1024;
   };
 #pragma unroll
-  for (int s = FIRST; s < 8 && s < FIRST + 2; ++s) {
-    raw[s][0] = frag(rec_off(s, 0));
-    raw[s][1] = frag(rec_off(s, 1));
+  for (int j = 0; j < 2; ++j) {
+    raw[j][0] = frag(rec_off(j, 0));
+    raw[j][1] = frag(rec_off(j, 1));
   }
+  // D^T pieces, tokens 16 s + 8 g .. + 7 (the records' token order)
 #pragma unroll
-  for (int s = 0; s < 4; ++s) load_pieces8(sD + col * DL + 32 * g + 8 * s, PD, dp[s]);
+  for (int s = 0; s < 4; ++s) load_pieces8(sD + col * DL + 16 * s + 8 * g, PD, dp[s]);
   // Diag(Gam) S0 first: the state tile is free until the Kb^T products
   const f32x4* gmp = reinterpret_cast<const f32x4*>(slot + RF_GM);
 #pragma unroll
@@ -658,19 +663,19 @@ __device__ __forceinline__ void ring32_step(const ScanArgs& p, const char* slot,
 #pragma unroll
     for (int i = 0; i < 4; ++i) S[4 * e4 + i] *= gm[i];
   }
-  split8(raw[FIRST][0], raw[FIRST][1], rr[FIRST]);
+  split8(raw[0][0], raw[0][1], rr[0]);
 #pragma unroll
-  for (int s = FIRST; s < 8; ++s) {
-    if (s + 2 < 8) {
-      raw[s + 2][0] = frag(rec_off(s + 2, 0));
-      raw[s + 2][1] = frag(rec_off(s + 2, 1));
+  for (int j = 0; j < NST; ++j) {
+    if (j + 2 < NST) {
+      raw[j + 2][0] = frag(rec_off(j + 2, 0));
+      raw[j + 2][1] = frag(rec_off(j + 2, 1));
     }
     __builtin_amdgcn_sched_barrier(0);
-    const int sn = s + 1 < 8 ? s + 1 : s;
-    if (s < 4)  // out^T += D^T P^T: P rows 32wp.. are the columns
-      X = mma_x6_pipe<false>(rr[s], dp[s], X, true, raw[sn][0], raw[sn][1], rr[sn]);
+    const int jn = j + 1 < NST ? j + 1 : j;
+    if (j < NPS)  // out^T += D^T P^T: P rows 32wp.. are the columns
+      X = mma_x6_pipe<false>(rr[j], dp[j], X, true, raw[jn][0], raw[jn][1], rr[jn]);
     else  // S_next = Diag(Gam) S0 + Kb^T D, rows 32w.. of Kb^T, 64 tokens contracted
-      S = mma_x6_pipe<true>(rr[s], dp[s - 4], S, s + 1 < 8, raw[sn][0], raw[sn][1], rr[sn]);
+      S = mma_x6_pipe<true>(rr[j], dp[j - NPS], S, j + 1 < NST, raw[jn][0], raw[jn][1], rr[jn]);
   }
 #pragma unroll
   for (int e4 = 0; e4 < 4; ++e4)
@@ -707,7 +712,7 @@ __global__ __launch_bounds__(512) void kda_scan_ring32_kernel(ScanArgs p) {
   const int H = p.H;
   const char* recb = reinterpret_cast<const char*>(p.rec);
   const char* gamb = reinterpret_cast<const char*>(p.gam);
-  auto rec_of = [&](int c) { return recb + ((size_t)c * H + h) * (size_t)REC * 4; };
+  auto rec_of = [&](int c) { return recb + ((size_t)c * H + h) * (size_t)Frag<float>::REC_ELEMS * 4; };
   auto gam_of = [&](int c) { return gamb + ((size_t)c * H + h) * DH * 4; };
 
   if (w >= 4) {
@@ -749,6 +754,7 @@ __global__ __launch_bounds__(512) void kda_scan_ring32_kernel(ScanArgs p) {
   for (int e4 = 0; e4 < 4; ++e4)
     store_pieces4(sS + col * L::SL + 32 * w + 8 * e4 + 4 * g, L::PS,
                   f32x4{S[4 * e4], S[4 * e4 + 1], S[4 * e4 + 2], S[4 * e4 + 3]});
+  if (w == 2) *reinterpret_cast<f32x4*>(smem + L::O_Z + 16 * l) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   wait_lds();
   ring_barrier();
   const int cfull = cbeg + (tend - tseq) / CHUNK;

@@ -109,7 +109,7 @@ extern "C" {
 
 /* Bytes of caller-provided scratch that kda_chunk_fwd needs for this shape.
  * Depends only on the arguments; non-decreasing in total_tokens.  FP32
- * intermediates need about 148 KB per 64-token chunk and head.  BF16
+ * intermediates need about 144 KB per 64-token chunk and head.  BF16
  * intermediates need about 72 KB per chunk and head up to 32 chunks and stop
  * growing there: about 2.4 MB per head (the records of one 32-chunk segment and
  * two 64 KB boundary states).  The windowed schedule (KDA_MODE_WINDOWED with

@@ -223,7 +223,7 @@ def test_intra_records_match_chunk_oracle(fp32):
     U.run_gpu(inp, fp32, True, workspace=ws)
     wsb = ws.cpu().numpy()
     # layout: status word (256 B) | cfirst [(N+1) int32] | gam [C][H][128] f32 |
-    # rec [C][H][REC] (256-aligned parts); bf16 records hold P's three lower
+    # rec [C][H][REC] (256-aligned parts); a record holds P's three lower
     # 32x32 tiles only
     al = lambda x: (x + 255) // 256 * 256
     Cmax = (T + 63 * min(N, T)) // 64
@@ -232,7 +232,7 @@ def test_intra_records_match_chunk_oracle(fp32):
     off_rec = off_gam + al(4 * Cmax * H * 128)
     cfirst = wsb[off_cfirst:off_cfirst + 4 * (N + 1)].view(np.int32)
     nc = int(cfirst[-1])
-    REC = 4 * 64 * 128 + (64 * 64 if fp32 else 3 * 32 * 32)
+    REC = 4 * 64 * 128 + 3 * 32 * 32
     gam = wsb[off_gam:off_gam + 4 * nc * H * 128].view(np.float32).reshape(nc, H, 128)
     if fp32:
         rec = wsb[off_rec:off_rec + 4 * nc * H * REC].view(np.float32).reshape(nc, H, REC)
@@ -253,21 +253,15 @@ def test_intra_records_match_chunk_oracle(fp32):
     iu = (((((c >> 5) * 2 + (r >> 5)) * (16 // FE) + q16 // FE) * 64 + 32 * ((r >> 2) & 1)
            + (c & 31)) * FE + q16 % FE)
     rr, ii = np.meshgrid(np.arange(64), np.arange(64), indexing="ij")
-    if fp32:
-        # token-contracted operands: lane half = token / 32
-        ikb = ((((ch >> 5) * (32 // FE) + (t & 31) // FE) * 64 + 32 * (t >> 5) + (ch & 31)) * FE
-               + (t & 31) % FE)
-        ip = ((((rr >> 5) * (32 // FE) + (ii & 31) // FE) * 64 + 32 * (ii >> 5) + (rr & 31)) * FE
-              + (ii & 31) % FE)
-        stored = np.ones((64, 64), dtype=bool)
-    else:
-        # steps of 16 tokens, lane half = (token / 8) % 2; P: rows 0..31 keep
-        # columns 0..31 (fragments 0, 1), rows 32..63 all (fragments 2..5)
-        ikb = (((ch >> 5) * 4 + (t >> 4)) * 64 + 32 * ((t >> 3) & 1) + (ch & 31)) * 8 + (t & 7)
-        stored = ii < 32 * ((rr >> 5) + 1)
-        ip = (((np.where(rr >> 5 == 0, 0, 2) + (ii >> 4)) * 64 + 32 * ((ii >> 3) & 1)
-               + (rr & 31)) * 8 + (ii & 7))
-        ip = np.where(stored, ip, 0)
+    # token-contracted operands in steps of 16 tokens: tokens 16 s + 8 g .. + 7
+    # in lane half g; P: rows 0..31 keep columns 0..31 (the first 16 / FE
+    # fragments), rows 32..63 all columns (the next 32 / FE)
+    ikb = ((((ch >> 5) * (32 // FE) + (t >> 4) * (8 // FE) + (t & 7) // FE) * 64
+            + 32 * ((t >> 3) & 1) + (ch & 31)) * FE + t % FE)
+    stored = ii < 32 * ((rr >> 5) + 1)
+    ip = (((np.where(rr >> 5 == 0, 0, 16 // FE) + (ii >> 4) * (8 // FE) + (ii & 7) // FE) * 64
+           + 32 * ((ii >> 3) & 1) + (rr & 31)) * FE + ii % FE)
+    ip = np.where(stored, ip, 0)
     # Qt: row-major, 16-byte chunk index permuted by row: chunk ^ (r % 16)
     iq = r * 128 + FE * ((c // FE) ^ (r & 15)) + c % FE
     P = np.where(stored, rec[:, :, 32768:][:, :, ip], 0.0)

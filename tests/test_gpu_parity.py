@@ -111,11 +111,14 @@ def test_cfg4_ragged_65536_tokens_sampled_heads(fp32):
 @pytest.mark.parametrize("cu", [
     [0, 1], [0, 64], [0, 65], [0, 63, 64, 127], [0, 0, 5, 5, 70, 70],
     [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 200], [0, 128, 129, 257, 300],
+    [0, 15, 31, 48, 79, 111, 144, 191, 239, 288],
 ], ids=lambda c: "cu" + "_".join(map(str, c)))
 @pytest.mark.parametrize("fp32", [False, True], ids=["bf16", "fp32"])
 def test_edge_lengths(cu, fp32):
     """1-token sequences, exact chunk multiples, a ragged tail, empty sequences,
-    many short sequences; H = 3 exercises an odd head count."""
+    many short sequences, lengths on either side of the 16-token contraction
+    steps and the 32-token tiles of P (15, 16, 17, 31, 32, 33, 47, 48, 49);
+    H = 3 exercises an odd head count."""
     inp = synth.make_inputs(cu, H=3, d=128, act="bf16", seed=sum(cu))
     _check(inp, fp32=fp32, label=f"edge {cu}")
 

@@ -178,7 +178,7 @@ template <typename V> __device__ __forceinline__ float val_at(const V* f, int q)
 // State pass with loader waves (bf16 intermediates).
 //
 // The state pass is bound by how fast one CU can bring in each chunk's
-// operands (about 60 KB per workgroup) while the compute waves also have to
+// operands (about 58 KB per workgroup) while the compute waves also have to
 // issue those loads in order with their matrix work.  Here four extra waves do
 // nothing but copy each chunk's operands straight from global memory into a
 // two-slot LDS ring with 16-byte direct-to-LDS loads; the four compute waves
@@ -298,7 +298,6 @@ __device__ __forceinline__ void ring_step(const ScanArgs& p, const char* slot, f
   typedef RingLds L;
   constexpr int SL = L::SL, DL = L::DL;
   const int col = l & 31, g = l >> 5, wp = w & 1;
-  TO* __restrict__ out = reinterpret_cast<TO*>(p.out);
   auto frag = [&](int off) { return *reinterpret_cast<const bf16x8*>(slot + off + 16 * l); };
   bf16x8 a[8];
   if constexpr (ROLE == 0) {
@@ -582,7 +581,6 @@ __device__ __forceinline__ void ring32_step(const ScanArgs& p, const char* slot,
   typedef Ring32Lds L;
   constexpr int SL = L::SL, DL = L::DL, PS = L::PS, PD = L::PD;
   const int col = l & 31, g = l >> 5, wp = w & 1;
-  TO* __restrict__ out = reinterpret_cast<TO*>(p.out);
   auto frag = [&](int off) { return *reinterpret_cast<const f32x4*>(slot + off + 16 * l); };
   f32x16 X;
 #pragma unroll

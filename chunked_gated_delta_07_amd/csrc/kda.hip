@@ -115,8 +115,8 @@ static inline bool use_windows(int32_t N, uint32_t mode) {
 // segment's records (about 150 MB at 64 heads) stay in the memory-side cache
 // until the state pass reads them.  FP32 intermediates run as one segment:
 // their state pass is bound by its split products, not by the record reads
-// (with every read an L2 hit it ran only 4 % faster), so the cache would save
-// less than the extra launches' tails cost.
+// (with every read an L2 hit it ran only 4 % faster), which bounds what the
+// memory-side cache could save against the extra launches' tails.
 static inline int64_t seg_count(int64_t T, int32_t N, uint32_t mode) {
   const int64_t C = max_chunks(T, N);
   if ((mode & KDA_MODE_FP32_INTERMEDIATE) || C <= SEG_CHUNKS) return 1;

@@ -114,9 +114,9 @@ static inline bool use_windows(int32_t N, uint32_t mode) {
 // (the results are those of one pass over everything, bit for bit).  A
 // segment's records (about 150 MB at 64 heads) stay in the memory-side cache
 // until the state pass reads them.  FP32 intermediates run as one segment:
-// their state pass is bound by its split products, not by the record reads
-// (with every read an L2 hit it ran only 4 % faster), which bounds what the
-// memory-side cache could save against the extra launches' tails.
+// their records are twice the size, and segments made that forward slower
+// (2.07 -> 2.13 ms with four); its state pass is bound by its split products
+// rather than by the record reads.
 static inline int64_t seg_count(int64_t T, int32_t N, uint32_t mode) {
   const int64_t C = max_chunks(T, N);
   if ((mode & KDA_MODE_FP32_INTERMEDIATE) || C <= SEG_CHUNKS) return 1;

@@ -41,8 +41,8 @@ namespace kda {
 
 // Per-(chunk, head) record in the workspace, element type MT, holding
 //   W [64 tok][128 key ch], Qt [64][128], Kb^T [128 key ch][64 tok],
-//   U [64 tok][128 value ch], P [64][64] (bf16: its three 32x32 tiles on or
-//   below the diagonal)
+//   U [64 tok][128 value ch], P [64][64] (its three 32x32 tiles on or below
+//   the diagonal)
 // plus Gam [128] float in a separate array.  Each matrix is stored in the
 // order in which the state pass reads it: one state-pass load instruction
 // (64 lanes x 16 bytes) covers 1 KB of contiguous memory (Qt: one 16-byte
